@@ -1,0 +1,395 @@
+"""Pins for the fp64 oracle (CPU only).
+
+Every check here compares the oracle with something other than itself: a
+hand-worked example, the unrolled closed-form solution of the linear
+recurrence (products of transition matrices, in numpy and at 50 digits in
+mpmath), closed forms for special inputs (one token, beta = 0 with exact
+decays, one-hot keys, orthogonal keys with g = 0 and beta = 1) and
+invariants that any correct implementation satisfies (state hand-off,
+packing, scaling, linearity, head permutation, grouped heads, decode).
+Library routines (numpy.logaddexp for softplus, scipy.special.expit for the
+sigmoid, numpy.linalg.norm) stand in for the prologue functions.
+"""
+
+import json
+import math
+import os
+
+import numpy as np
+import pytest
+from scipy.special import expit
+
+import oracle
+from chunked_gated_delta_10_amd.inputs import bf16_bits, make_inputs, varlen_lengths, cu_seqlens_from_lengths
+
+GOLDEN = os.path.join(os.path.dirname(__file__), "golden")
+EPS = 1e-6
+
+
+def _f64(x):
+    return oracle.widen(x)
+
+
+def _normalise(x):
+    return x / np.sqrt(np.sum(x * x, axis=-1, keepdims=True) + EPS)
+
+
+def unrolled_reference(inp, H_qk, H, gate_per_channel=True):
+    """Closed-form solution of the linear recurrence for one dense batch.
+
+    Phi_t = (I - b_t k_t k_t^T) Diag(exp(g_t));
+    S_t = Phi_t ... Phi_1 S_0 + sum_{i<=t} Phi_t ... Phi_{i+1} b_i k_i v_i^T;
+    o_t = scale * S_t^T q_t.  Built from explicit matrix products.
+    """
+    q, k, v, g_raw = (_f64(inp[n]) for n in ("q", "k", "v", "g_raw"))
+    b = _f64(inp["b"])
+    A_log = _f64(inp["A_log"])
+    scale = inp["scale"]
+    B, T, _, K = q.shape
+    V = v.shape[-1]
+    G = H // H_qk
+    out = np.zeros((B, T, H, V))
+    final = np.zeros((B, H, V, K))
+    s0 = inp.get("initial_state")
+    for bb in range(B):
+        for h in range(H):
+            hq = h // G
+            qn = _normalise(q[bb, :, hq])
+            kn = _normalise(k[bb, :, hq])
+            sp = np.logaddexp(0.0, g_raw[bb, :, h])  # softplus
+            g = -np.exp(A_log[h]) * sp
+            if not gate_per_channel:
+                g = np.repeat(g[:, None], K, axis=1)
+            beta = expit(b[bb, :, h])
+            phis = [(np.eye(K) - beta[t] * np.outer(kn[t], kn[t])) @ np.diag(np.exp(g[t])) for t in range(T)]
+            S0 = np.zeros((K, V)) if s0 is None else _f64(s0)[bb, h].T
+            for t in range(T):
+                P = np.eye(K)
+                for j in range(t, -1, -1):
+                    P = P @ phis[j]
+                S = P @ S0
+                for i in range(t + 1):
+                    Pi = np.eye(K)
+                    for j in range(t, i, -1):
+                        Pi = Pi @ phis[j]
+                    S = S + Pi @ (beta[i] * np.outer(kn[i], v[bb, i, h]))
+                out[bb, t, h] = scale * S.T @ qn[t]
+            final[bb, h] = S.T
+    return out, final
+
+
+def _run(inp, **kw):
+    return oracle.kda_fwd(inp["q"], inp["k"], inp["v"], inp["g_raw"], inp["b"], inp["A_log"], inp["scale"],
+                          gate_per_channel=inp["gate_per_channel"], initial_state=inp.get("initial_state"),
+                          cu_seqlens=inp.get("cu_seqlens"), **kw)
+
+
+def test_worked_example():
+    with open(os.path.join(GOLDEN, "worked_example_k2_t3.json")) as f:
+        ex = json.load(f)
+    T, K = len(ex["q"]), len(ex["q"][0])
+    q = np.array(ex["q"]).reshape(1, T, 1, K)
+    k = np.array(ex["k"]).reshape(1, T, 1, K)
+    v = np.array(ex["v"]).reshape(1, T, 1, -1)
+    g = np.array(ex["g_raw"]).reshape(1, T, 1, K)
+    b = np.array(ex["beta_logit"]).reshape(1, T, 1)
+    out, fin = oracle.kda_fwd(q, k, v, g, b, np.array(ex["A_log"]), ex["scale"])
+    np.testing.assert_allclose(out[0, :, 0], np.array(ex["out"]), rtol=ex["rtol"], atol=ex["atol"])
+    np.testing.assert_allclose(fin[0, 0], np.array(ex["final_state"]), rtol=ex["rtol"], atol=ex["atol"])
+
+
+@pytest.mark.parametrize("K,V,T,H,H_qk,per_channel,state", [
+    (4, 4, 9, 2, 2, True, None), (8, 8, 12, 2, 1, True, 0.3), (4, 8, 7, 4, 2, False, 0.5),
+    (8, 4, 11, 1, 1, True, 1.0)])
+def test_matches_unrolled_products(K, V, T, H, H_qk, per_channel, state):
+    inp = make_inputs(2, T, H, H_qk, gate_per_channel=per_channel, state_std=state, seed=11 + K + T, K=K, V=V,
+                      A_log=(-2.0, 0.5))
+    out, fin = _run(inp)
+    ref_out, ref_fin = unrolled_reference(inp, H_qk, H, per_channel)
+    np.testing.assert_allclose(out, ref_out, rtol=1e-11, atol=1e-13)
+    np.testing.assert_allclose(fin, ref_fin, rtol=1e-11, atol=1e-13)
+
+
+def test_fp64_error_vs_50_digit_unrolled():
+    """The oracle's own rounding error, measured against 50-digit arithmetic."""
+    mpmath = pytest.importorskip("mpmath")
+    mp = mpmath.mp
+    mp.dps = 50
+    K = V = 4
+    T = 8
+    inp = make_inputs(1, T, 1, 1, state_std=0.5, seed=5, K=K, V=V, A_log=(-1.0, 1.0))
+    out, fin = _run(inp)
+    q, k, v, g_raw = (_f64(inp[n])[0, :, 0] for n in ("q", "k", "v", "g_raw"))
+    b = _f64(inp["b"])[0, :, 0]
+    a = mp.exp(mp.mpf(float(inp["A_log"][0])))
+    S = mp.matrix(K, V)
+    s0 = _f64(inp["initial_state"])[0, 0]
+    for i in range(K):
+        for j in range(V):
+            S[i, j] = mp.mpf(float(s0[j, i]))
+    for t in range(T):
+        def nrm(x):
+            x = [mp.mpf(float(e)) for e in x]
+            n = mp.sqrt(sum(e * e for e in x) + mp.mpf("1e-6"))
+            return mp.matrix([e / n for e in x])
+        qn, kn = nrm(q[t]), nrm(k[t])
+        dec = [mp.exp(-a * mp.log(1 + mp.exp(mp.mpf(float(x))))) for x in g_raw[t]]
+        beta = 1 / (1 + mp.exp(-mp.mpf(float(b[t]))))
+        Phi = (mp.eye(K) - beta * kn * kn.T) * mp.diag(dec)
+        S = Phi * S + beta * kn * mp.matrix([[mp.mpf(float(e)) for e in v[t]]])
+        o = (S.T * qn) * mp.mpf(float(inp["scale"]))
+        for j in range(V):
+            assert abs(float(o[j]) - out[0, t, 0, j]) <= 1e-13 * (1 + abs(float(o[j])))
+    for i in range(K):
+        for j in range(V):
+            assert abs(float(S[i, j]) - fin[0, 0, j, i]) <= 1e-13 * (1 + abs(float(S[i, j])))
+
+
+def test_single_token_closed_form():
+    """T = 1 from a zero state: o = scale * b (q.k) v and S = b k v^T."""
+    inp = make_inputs(3, 1, 4, 2, seed=21)
+    out, fin = _run(inp)
+    q, k, v = (_f64(inp[n]) for n in ("q", "k", "v"))
+    b = expit(_f64(inp["b"]))
+    for bb in range(3):
+        for h in range(4):
+            qn = q[bb, 0, h // 2] / np.linalg.norm(np.append(q[bb, 0, h // 2], math.sqrt(EPS)))
+            kn = k[bb, 0, h // 2] / np.linalg.norm(np.append(k[bb, 0, h // 2], math.sqrt(EPS)))
+            exp_o = inp["scale"] * b[bb, 0, h] * (qn @ kn) * v[bb, 0, h]
+            np.testing.assert_allclose(out[bb, 0, h], exp_o, rtol=1e-12, atol=1e-15)
+            np.testing.assert_allclose(fin[bb, h], b[bb, 0, h] * np.outer(v[bb, 0, h], kn), rtol=1e-12, atol=1e-15)
+
+
+def test_zero_beta_exact_decays():
+    """beta ~ 0 (logit -200) with g_raw in {0, -100} and A_log = 0.
+
+    softplus(0) = ln 2, so those channels decay by exactly 1/2 per token;
+    softplus(-100) ~ 4e-44, so those channels keep their value.  With no
+    writes, S_t = Diag(d^t) S_0 and o_t = scale * S_t^T q_t.
+    """
+    K = V = 128
+    T, H = 40, 2
+    inp = make_inputs(1, T, H, H, state_std=1.0, seed=31, A_log=0.0)
+    rng = np.random.default_rng(3)
+    keep = rng.random(K) < 0.5
+    g = np.where(keep, -100.0, 0.0)
+    inp["g_raw"] = bf16_bits(np.broadcast_to(g, (1, T, H, K)))
+    inp["b"] = np.full((1, T, H), -200.0, dtype=np.float32)
+    out, fin = _run(inp)
+    d = np.where(keep, 1.0, 0.5)
+    S0 = _f64(inp["initial_state"])[0]  # [H, V, K]
+    q = _f64(inp["q"])[0]
+    for h in range(H):
+        for t in range(T):
+            St = S0[h] * (d ** (t + 1))[None, :]          # [V, K]
+            qn = q[t, h] / np.linalg.norm(np.append(q[t, h], math.sqrt(EPS)))
+            np.testing.assert_allclose(out[0, t, h], inp["scale"] * St @ qn, rtol=1e-12, atol=1e-14)
+        np.testing.assert_allclose(fin[0, h], S0[h] * (d ** T)[None, :], rtol=1e-12, atol=1e-300)
+
+
+def test_one_hot_keys_give_gated_linear_attention():
+    """Distinct one-hot keys from a zero state never overlap, so the erase term
+    vanishes and o_t = scale * sum_{i<=t} b_i c exp(G_t - G_i)[c_i] q_t[c_i] v_i,
+    where G is the running sum of g and c = 1/sqrt(1 + eps) is the norm of a
+    normalised one-hot key."""
+    K = V = 128
+    T, H = 96, 2
+    inp = make_inputs(1, T, H, H, seed=41, A_log=(-1.0, 1.0))
+    rng = np.random.default_rng(4)
+    chans = rng.permutation(K)[:T]
+    kk = np.zeros((1, T, H, K), dtype=np.float32)
+    kk[0, np.arange(T), :, chans] = 1.0
+    inp["k"] = bf16_bits(kk)
+    out, _ = _run(inp)
+    q = _f64(inp["q"])[0]
+    v = _f64(inp["v"])[0]
+    g = -np.exp(_f64(inp["A_log"]))[None, :, None] * np.logaddexp(0.0, _f64(inp["g_raw"])[0])  # [T, H, K]
+    G = np.cumsum(g, axis=0)
+    beta = expit(_f64(inp["b"])[0])
+    c = 1.0 / math.sqrt(1.0 + EPS)
+    for h in range(H):
+        for t in range(T):
+            qn = q[t, h] / np.linalg.norm(np.append(q[t, h], math.sqrt(EPS)))
+            acc = np.zeros(V)
+            for i in range(t + 1):
+                ci = chans[i]
+                acc += beta[i, h] * c * math.exp(G[t, h, ci] - G[i, h, ci]) * qn[ci] * v[i, h]
+            np.testing.assert_allclose(out[0, t, h], inp["scale"] * acc, rtol=1e-10, atol=1e-13)
+
+
+def _sylvester(n):
+    Hm = np.array([[1.0]])
+    while Hm.shape[0] < n:
+        Hm = np.block([[Hm, Hm], [Hm, -Hm]])
+    return Hm
+
+
+def test_orthogonal_keys_overwrite():
+    """g = 0 (A_log = -60) and beta = 1 (logit +200) with orthogonal +-1 keys:
+    writing v to key j replaces what key j held, and querying with key j
+    returns scale * (latest value written to j) up to the eps of the norm."""
+    K = V = 128
+    T = 48
+    Hm = _sylvester(K)
+    rng = np.random.default_rng(7)
+    wkeys = rng.integers(0, 6, size=T)       # few keys, so they get overwritten
+    qkeys = rng.integers(0, 6, size=T)
+    inp = make_inputs(1, T, 1, 1, seed=51, A_log=-60.0)
+    inp["k"] = bf16_bits(Hm[wkeys][None, :, None, :])
+    inp["q"] = bf16_bits(Hm[qkeys][None, :, None, :])
+    inp["b"] = np.full((1, T, 1), 200.0, dtype=np.float32)
+    out, _ = _run(inp)
+    v = _f64(inp["v"])[0, :, 0]
+    latest = {}
+    for t in range(T):
+        latest[wkeys[t]] = v[t]
+        exp_o = inp["scale"] * latest.get(qkeys[t], np.zeros(V))
+        np.testing.assert_allclose(out[0, t, 0], exp_o, rtol=0, atol=1e-7)
+
+
+@pytest.mark.parametrize("split", [1, 63, 64, 65, 100, 250])
+def test_state_handoff_is_exact(split):
+    T = 300
+    inp = make_inputs(2, T, 3, 3, state_std=0.02, seed=61, A_log=(-6.0, -4.0))
+    full_out, full_fin = _run(inp)
+    a = {n: (x[:, :split] if n in ("q", "k", "v", "g_raw", "b") else x) for n, x in inp.items()}
+    b = {n: (x[:, split:] if n in ("q", "k", "v", "g_raw", "b") else x) for n, x in inp.items()}
+    o1, f1 = _run(a)
+    b["initial_state"] = f1
+    o2, f2 = _run(b)
+    assert np.array_equal(np.concatenate([o1, o2], axis=1), full_out)
+    assert np.array_equal(f2, full_fin)
+
+
+def test_varlen_equals_separate_calls():
+    lens = [19, 64, 1, 130, 0, 77]
+    T = sum(lens)
+    cu = cu_seqlens_from_lengths(lens)
+    N = len(lens)
+    inp = make_inputs(1, T, 2, 2, state_std=0.05, N=N, lengths=lens, seed=71, A_log=(-6.0, -4.0))
+    out, fin = _run(inp)
+    for n in range(N):
+        s, e = cu[n], cu[n + 1]
+        one = {x: (inp[x][:, s:e] if x in ("q", "k", "v", "g_raw", "b") else inp[x]) for x in inp}
+        one["cu_seqlens"] = None
+        one["initial_state"] = inp["initial_state"][n:n + 1]
+        o, f = _run(one)
+        assert np.array_equal(out[:, s:e], o)
+        assert np.array_equal(fin[n:n + 1], f)
+    # a zero-length sequence hands its initial state straight through
+    assert np.array_equal(fin[4], inp["initial_state"][4].astype(np.float64))
+
+
+def test_dense_batch_equals_two_packed_sequences():
+    T = 150
+    inp = make_inputs(2, T, 2, 2, state_std=0.02, seed=81)
+    out, fin = _run(inp)
+    packed = {x: (inp[x].reshape((1, 2 * T) + inp[x].shape[2:]) if x in ("q", "k", "v", "g_raw", "b") else inp[x])
+              for x in inp}
+    packed["cu_seqlens"] = np.array([0, T, 2 * T], dtype=np.int32)
+    o2, f2 = _run(packed)
+    assert np.array_equal(o2.reshape(out.shape), out)
+    assert np.array_equal(f2, fin)
+
+
+def test_qk_scale_invariance():
+    inp = make_inputs(1, 70, 2, 2, state_std=0.02, seed=91)
+    out, fin = _run(inp)
+    for n in ("q", "k"):
+        x = oracle.widen(inp[n]).astype(np.float32) * 2  # exact in bf16
+        inp[n] = bf16_bits(x)
+    out2, fin2 = _run(inp)
+    # eps under the norm's square root moves q, k by ~eps / |x|^2 ~ 1e-8 relative
+    np.testing.assert_allclose(out2, out, rtol=0, atol=1e-7 * np.abs(out).max())
+    np.testing.assert_allclose(fin2, fin, rtol=0, atol=1e-7 * np.abs(fin).max())
+
+
+def test_linear_in_values_and_state():
+    inp = make_inputs(1, 90, 2, 1, state_std=0.1, seed=101)
+    out, fin = _run(inp)
+    inp["v"] = bf16_bits(oracle.widen(inp["v"]).astype(np.float32) * 2)
+    inp["initial_state"] = inp["initial_state"] * 2
+    out2, fin2 = _run(inp)
+    assert np.array_equal(out2, 2 * out) and np.array_equal(fin2, 2 * fin)
+
+
+def test_head_permutation():
+    H = 4
+    inp = make_inputs(1, 80, H, H, state_std=0.02, seed=111)
+    out, fin = _run(inp)
+    perm = np.array([2, 0, 3, 1])
+    p = dict(inp)
+    for n in ("q", "k", "v", "g_raw"):
+        p[n] = inp[n][:, :, perm]
+    p["b"] = inp["b"][:, :, perm]
+    p["A_log"] = inp["A_log"][perm]
+    p["initial_state"] = inp["initial_state"][:, perm]
+    out2, fin2 = _run(p)
+    assert np.array_equal(out2, out[:, :, perm]) and np.array_equal(fin2, fin[:, perm])
+
+
+def test_grouped_heads_equal_repeated_heads_with_broadcast_gate():
+    """Scalar-gate grouped mode == per-channel mode on repeat-interleaved q/k
+    and a gate broadcast over the key channels (value head j uses q/k head j // G)."""
+    G, H_qk = 4, 2
+    H = G * H_qk
+    inp = make_inputs(1, 75, H, H_qk, gate_per_channel=False, state_std=0.02, seed=121, A_log=(-1.0, 1.0))
+    out, fin = _run(inp)
+    rep = dict(inp)
+    rep["q"] = np.repeat(inp["q"], G, axis=2)
+    rep["k"] = np.repeat(inp["k"], G, axis=2)
+    rep["g_raw"] = np.repeat(inp["g_raw"][..., None], 128, axis=-1)
+    rep["gate_per_channel"] = True
+    out2, fin2 = _run(rep)
+    assert np.array_equal(out2, out) and np.array_equal(fin2, fin)
+    # and the grouping is contiguous: swapping the two q/k heads changes the result
+    sw = dict(inp)
+    sw["q"] = inp["q"][:, :, ::-1].copy()
+    sw["k"] = inp["k"][:, :, ::-1].copy()
+    out3, _ = _run(sw)
+    assert not np.allclose(out3, out)
+
+
+def test_decode_steps_equal_one_forward():
+    B, T, H = 3, 20, 2
+    inp = make_inputs(B, T, H, H, state_std=0.05, seed=131)
+    out, fin = _run(inp)
+    st = inp["initial_state"]
+    for t in range(T):
+        o, st = oracle.kda_decode(inp["q"][:, t], inp["k"][:, t], inp["v"][:, t], inp["g_raw"][:, t],
+                                  inp["b"][:, t], inp["A_log"], inp["scale"], st)
+        assert np.array_equal(o, out[:, t])
+    assert np.array_equal(st, fin)
+
+
+def test_zero_query_gives_zero_output():
+    inp = make_inputs(1, 10, 1, 1, state_std=0.1, seed=141)
+    q = np.zeros((1, 10, 1, 128), dtype=np.float32)
+    inp["q"] = bf16_bits(q)
+    out, _ = _run(inp)
+    assert np.all(out == 0.0)
+
+
+def test_chain_mask_computes_subset():
+    inp = make_inputs(2, 40, 3, 3, state_std=0.02, seed=151)
+    out, fin = _run(inp)
+    mask = np.zeros((2, 3), dtype=bool)
+    mask[1, 2] = True
+    o2, f2 = _run(inp, chain_mask=mask)
+    assert np.array_equal(o2[1, :, 2], out[1, :, 2]) and np.array_equal(f2[1, 2], fin[1, 2])
+    assert np.isnan(o2[0]).all()
+
+
+def test_varlen_length_recipe():
+    rng = np.random.default_rng(1002)
+    lens = varlen_lengths(rng)
+    assert lens.sum() == 16384 and lens.min() == 19 and lens.max() == 3147 and len(lens) == 20
+
+
+def test_bf16_rounding_is_nearest_even():
+    x = np.array([1.0, 1.00390625, 1.01171875, -3.0e-3, 65504.0, 1e-30], dtype=np.float32)
+    bits = bf16_bits(x)
+    back = oracle.widen(bits)
+    # 1 + 2^-8 is a tie between 1 and 1 + 2^-7: even mantissa wins (1.0)
+    assert back[0] == 1.0 and back[1] == 1.0 and back[2] == 1.015625
+    np.testing.assert_allclose(back, x, rtol=2 ** -8)
