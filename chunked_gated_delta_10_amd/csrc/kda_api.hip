@@ -1,0 +1,259 @@
+// kda_api.hip -- the C ABI of libkda.so (declared in include/kda.h).
+//
+// Host side only: argument validation (before anything touches the device),
+// workspace layout, and the launch sequence
+//   schedule (kda_table) -> chunk-local (kda_chunk) -> recurrence (kda_recur)
+// for the chunked forward pass, and the single decode kernel for decode.
+#include <hip/hip_runtime.h>
+
+#include <cstdarg>
+#include <cstdio>
+#include <cstdlib>
+#include <cstring>
+#include <string>
+#include <vector>
+
+#include "kda.h"
+#include "kda_device.h"
+#include "kda_kernels.h"
+
+namespace {
+
+thread_local std::string g_last_error;
+
+kda_status fail(kda_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_last_error = buf;
+  return st;
+}
+
+kda_status ok() {
+  g_last_error.clear();
+  return KDA_OK;
+}
+
+bool env_flag(const char* name) {
+  const char* v = std::getenv(name);
+  return v && v[0] == '1';
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+constexpr size_t ALIGN = 256;
+size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
+
+struct Layout {
+  size_t rec, seqs, chunks, order, total;
+  int n_entries;
+};
+
+// Workspace: chunk records, then the schedule (sequence table, chunk table, order).
+Layout layout(int n_seqs, int n_entries, int H) {
+  Layout L;
+  L.n_entries = n_entries;
+  L.rec = 0;
+  L.seqs = round_up((size_t)n_entries * H * kda::REC_BYTES);
+  L.chunks = L.seqs + round_up((size_t)n_seqs * sizeof(int4));
+  L.order = L.chunks + round_up((size_t)n_entries * sizeof(int4));
+  L.total = L.order + round_up((size_t)n_seqs * sizeof(int));
+  return L;
+}
+
+int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
+
+kda_status check_state_dtypes(const void* init, kda_state_dtype idt, const void* fin, kda_state_dtype fdt,
+                               bool* bf16) {
+  auto valid = [](kda_state_dtype d) { return d == KDA_STATE_BF16 || d == KDA_STATE_FP32; };
+  if (init && !valid(idt)) return fail(KDA_ERR_DTYPE, "initial_state dtype %d is not bf16 (1) or fp32 (2)", (int)idt);
+  if (fin && !valid(fdt)) return fail(KDA_ERR_DTYPE, "final_state dtype %d is not bf16 (1) or fp32 (2)", (int)fdt);
+  if (init && fin && idt != fdt)
+    return fail(KDA_ERR_STATE_DTYPE_MISMATCH, "initial_state and final_state dtypes differ (%d vs %d)", (int)idt,
+                (int)fdt);
+  *bf16 = (init ? idt : fdt) == KDA_STATE_BF16;
+  return KDA_OK;
+}
+
+struct FwdArgs {
+  const void *q, *k, *v, *g_raw;
+  const float *beta, *A_log;
+  float scale;
+  int gate_per_channel;
+  const void* s0;
+  kda_state_dtype s0_dt;
+  void* out;
+  void* s1;
+  kda_state_dtype s1_dt;
+  const int32_t* cu;  // null for dense
+  int n_seqs;         // B (dense) or N (packed)
+  int T;              // tokens per row (dense) or total tokens
+  int rows;           // B for dense, 1 for packed
+  int H_qk, H, K, V;
+  void* ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+
+kda_status validate_common(const FwdArgs& a) {
+  if (a.n_seqs < 0 || a.T < 0 || a.H_qk <= 0 || a.H <= 0)
+    return fail(KDA_ERR_SHAPE, "sizes must be non-negative with H, H_qk > 0 (got seqs=%d T=%d H_qk=%d H=%d)",
+                a.n_seqs, a.T, a.H_qk, a.H);
+  if (a.K != kda::HD || a.V != kda::HD)
+    return fail(KDA_ERR_SHAPE, "only K = V = 128 is supported (got K=%d V=%d)", a.K, a.V);
+  if (a.H % a.H_qk != 0) return fail(KDA_ERR_SHAPE, "H (%d) must be a multiple of H_qk (%d)", a.H, a.H_qk);
+  if (a.gate_per_channel != 0 && a.gate_per_channel != 1)
+    return fail(KDA_ERR_SHAPE, "gate_per_channel must be 0 or 1 (got %d)", a.gate_per_channel);
+  if ((long)a.rows * a.T >= (1L << 31) || (long)a.n_seqs * a.H >= (1L << 31))
+    return fail(KDA_ERR_SHAPE, "problem too large (tokens and sequences x heads must fit in int32)");
+  return KDA_OK;
+}
+
+kda_status run_forward(const FwdArgs& a) {
+  kda_status st = validate_common(a);
+  if (st != KDA_OK) return st;
+  bool bf16_state = false;
+  st = check_state_dtypes(a.s0, a.s0_dt, a.s1, a.s1_dt, &bf16_state);
+  if (st != KDA_OK) return st;
+  if (a.n_seqs == 0) return ok();
+  const long tokens = (long)a.rows * a.T;
+  if (tokens > 0) {
+    const void* req[] = {a.q, a.k, a.v, a.g_raw, a.beta, a.A_log, a.out};
+    const char* names[] = {"q", "k", "v", "g_raw", "beta_logits", "A_log", "out"};
+    for (int i = 0; i < 7; ++i)
+      if (!req[i]) return fail(KDA_ERR_NULL, "%s is NULL", names[i]);
+    for (int i = 0; i < 7; ++i)
+      if (!aligned16(req[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  if (a.s0 && !aligned16(a.s0)) return fail(KDA_ERR_ALIGN, "initial_state is not 16-byte aligned");
+  if (a.s1 && !aligned16(a.s1)) return fail(KDA_ERR_ALIGN, "final_state is not 16-byte aligned");
+  if (a.cu && (reinterpret_cast<uintptr_t>(a.cu) & 3u)) return fail(KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+  const int n_entries = a.cu ? cdiv(a.T, kda::CH) + a.n_seqs : a.n_seqs * cdiv(a.T, kda::CH);
+  const Layout L = layout(a.n_seqs, n_entries, a.H);
+  if (!a.ws) return fail(KDA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
+  if (a.ws_bytes < L.total)
+    return fail(KDA_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", a.ws_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(a.ws) & (ALIGN - 1)) return fail(KDA_ERR_ALIGN, "workspace is not 256-byte aligned");
+
+  if (a.cu && env_flag("KDA_DEBUG")) {
+    std::vector<int32_t> h(a.n_seqs + 1);
+    if (hipMemcpyAsync(h.data(), a.cu, h.size() * sizeof(int32_t), hipMemcpyDeviceToHost, a.stream) != hipSuccess ||
+        hipStreamSynchronize(a.stream) != hipSuccess)
+      return fail(KDA_ERR_HIP, "KDA_DEBUG: could not read cu_seqlens: %s", hipGetErrorString(hipGetLastError()));
+    if (h[0] != 0) return fail(KDA_ERR_SHAPE, "KDA_DEBUG: cu_seqlens[0] = %d, expected 0", h[0]);
+    for (int n = 0; n < a.n_seqs; ++n)
+      if (h[n + 1] < h[n]) return fail(KDA_ERR_SHAPE, "KDA_DEBUG: cu_seqlens decreases at %d", n);
+    if (h[a.n_seqs] != a.T) return fail(KDA_ERR_SHAPE, "KDA_DEBUG: cu_seqlens[N] = %d, expected T = %d", h[a.n_seqs], a.T);
+  }
+
+  uint8_t* ws = static_cast<uint8_t*>(a.ws);
+  int4* seqs = reinterpret_cast<int4*>(ws + L.seqs);
+  int4* chunks = reinterpret_cast<int4*>(ws + L.chunks);
+  int* order = reinterpret_cast<int*>(ws + L.order);
+
+  (void)hipGetLastError();  // clear any stale error before launching
+  kda::TableParams tp{a.cu, a.n_seqs, a.T, n_entries, seqs, chunks, order};
+  kda::launch_table(tp, a.stream);
+  if (n_entries > 0 && tokens > 0) {
+    kda::ChunkParams cp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                        static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log, chunks, a.H, a.H_qk, ws + L.rec};
+    kda::launch_chunk_local(cp, n_entries, a.gate_per_channel == 1, a.stream);
+  }
+  kda::RecurParams rp{ws + L.rec, seqs, order, a.n_seqs * a.H, n_entries, a.H, static_cast<const uint16_t*>(a.v),
+                      static_cast<uint16_t*>(a.out), a.s0, a.s1, a.scale};
+  kda::launch_recur(rp, bf16_state, a.stream);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  if (env_flag("KDA_LOG"))
+    std::fprintf(stderr, "[kda] fwd seqs=%d T=%d H=%d H_qk=%d entries=%d chunk-grid=%dx%d recur-grid=%d state=%s\n",
+                 a.n_seqs, a.T, a.H, a.H_qk, n_entries, n_entries, a.H, kda::recur_grid(a.n_seqs * a.H),
+                 bf16_state ? "bf16" : "fp32");
+  return ok();
+}
+
+}  // namespace
+
+extern "C" {
+
+size_t kda_fwd_workspace_bytes(int B, int T, int H_qk, int H, int N) {
+  if (B < 0 || T < 0 || H_qk <= 0 || H <= 0 || N < 0 || H % H_qk != 0) return 0;
+  if (N > 0 && B != 1) return 0;
+  const int n_seqs = N > 0 ? N : B;
+  const int n_entries = N > 0 ? cdiv(T, kda::CH) + N : B * cdiv(T, kda::CH);
+  return layout(n_seqs, n_entries, H).total;
+}
+
+kda_status kda_fwd(const void* q, const void* k, const void* v, const void* g_raw, const float* beta_logits,
+                   const float* A_log, float scale, int gate_per_channel, const void* initial_state,
+                   kda_state_dtype init_dtype, void* out, void* final_state, kda_state_dtype final_dtype, int B,
+                   int T, int H_qk, int H, int K, int V, void* workspace, size_t workspace_bytes, void* stream) {
+  FwdArgs a{q, k, v, g_raw, beta_logits, A_log, scale, gate_per_channel, initial_state, init_dtype, out,
+            final_state, final_dtype, nullptr, B, T, B, H_qk, H, K, V, workspace, workspace_bytes,
+            static_cast<hipStream_t>(stream)};
+  return run_forward(a);
+}
+
+kda_status kda_fwd_varlen(const void* q, const void* k, const void* v, const void* g_raw, const float* beta_logits,
+                          const float* A_log, float scale, int gate_per_channel, const void* initial_state,
+                          kda_state_dtype init_dtype, void* out, void* final_state, kda_state_dtype final_dtype,
+                          const int32_t* cu_seqlens, int N, int T, int H_qk, int H, int K, int V, void* workspace,
+                          size_t workspace_bytes, void* stream) {
+  if (N > 0 && !cu_seqlens) return fail(KDA_ERR_NULL, "cu_seqlens is NULL");
+  FwdArgs a{q, k, v, g_raw, beta_logits, A_log, scale, gate_per_channel, initial_state, init_dtype, out,
+            final_state, final_dtype, cu_seqlens, N, T, 1, H_qk, H, K, V, workspace, workspace_bytes,
+            static_cast<hipStream_t>(stream)};
+  return run_forward(a);
+}
+
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* g_raw, const float* beta_logits,
+                           const float* A_log, float scale, int gate_per_channel, void* state,
+                           kda_state_dtype state_dtype, void* out, int B, int H_qk, int H, int K, int V,
+                           void* stream) {
+  if (B < 0 || H_qk <= 0 || H <= 0)
+    return fail(KDA_ERR_SHAPE, "sizes must be non-negative with H, H_qk > 0 (got B=%d H_qk=%d H=%d)", B, H_qk, H);
+  if (K != kda::HD || V != kda::HD) return fail(KDA_ERR_SHAPE, "only K = V = 128 is supported (got K=%d V=%d)", K, V);
+  if (H % H_qk != 0) return fail(KDA_ERR_SHAPE, "H (%d) must be a multiple of H_qk (%d)", H, H_qk);
+  if (gate_per_channel != 0 && gate_per_channel != 1)
+    return fail(KDA_ERR_SHAPE, "gate_per_channel must be 0 or 1 (got %d)", gate_per_channel);
+  if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP32)
+    return fail(KDA_ERR_DTYPE, "state dtype %d is not bf16 (1) or fp32 (2)", (int)state_dtype);
+  if ((long)B * H >= (1L << 31)) return fail(KDA_ERR_SHAPE, "problem too large");
+  if (B == 0) return ok();
+  const void* req[] = {q, k, v, g_raw, beta_logits, A_log, state, out};
+  const char* names[] = {"q", "k", "v", "g_raw", "beta_logits", "A_log", "state", "out"};
+  for (int i = 0; i < 8; ++i)
+    if (!req[i]) return fail(KDA_ERR_NULL, "%s is NULL", names[i]);
+  for (int i = 0; i < 8; ++i)
+    if (!aligned16(req[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  (void)hipGetLastError();
+  kda::DecodeParams p{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(g_raw), beta_logits, A_log,
+                      state, static_cast<uint16_t*>(out), H, H_qk, scale};
+  kda::launch_decode(p, B, state_dtype == KDA_STATE_BF16, gate_per_channel == 1, static_cast<hipStream_t>(stream));
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  if (env_flag("KDA_LOG"))
+    std::fprintf(stderr, "[kda] decode B=%d H=%d H_qk=%d grid=%d state=%s\n", B, H, H_qk, B * H,
+                 state_dtype == KDA_STATE_BF16 ? "bf16" : "fp32");
+  return ok();
+}
+
+const char* kda_status_string(kda_status s) {
+  switch (s) {
+    case KDA_OK: return "KDA_OK";
+    case KDA_ERR_NULL: return "KDA_ERR_NULL";
+    case KDA_ERR_SHAPE: return "KDA_ERR_SHAPE";
+    case KDA_ERR_DTYPE: return "KDA_ERR_DTYPE";
+    case KDA_ERR_STATE_DTYPE_MISMATCH: return "KDA_ERR_STATE_DTYPE_MISMATCH";
+    case KDA_ERR_WORKSPACE: return "KDA_ERR_WORKSPACE";
+    case KDA_ERR_ALIGN: return "KDA_ERR_ALIGN";
+    case KDA_ERR_HIP: return "KDA_ERR_HIP";
+  }
+  return "KDA_UNKNOWN_STATUS";
+}
+
+const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+}  // extern "C"

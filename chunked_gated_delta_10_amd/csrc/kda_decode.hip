@@ -1,0 +1,150 @@
+// kda_decode.hip -- one decode step for every (batch row, value head).
+//
+// With the state stored [V, K] (row v is the 128-float key vector s_v), one
+// token advances each row independently:
+//   s'_v = exp(g) . s_v                 (per key channel)
+//   a_v  = kn . s'_v,   c_v = qn . s'_v  (one fused pass, two dot products)
+//   u_v  = b (v_v - a_v)
+//   o_v  = scale (c_v + u_v (qn . kn))   (since S_t^T qn = S'^T qn + (qn.kn) u)
+//   s_v  = s'_v + u_v kn
+// so the state streams through once: read 512 B, write 512 B per row.
+//
+// Workgroup = one (batch row, head), 256 threads; a group of 16 lanes owns
+// one state row per step (8 key channels per lane, two 16-byte accesses),
+// 16 rows are in flight per pass and each lane walks 8 rows.  All loads of a
+// lane are issued before any arithmetic so 16 x 16-byte requests per lane
+// are outstanding.
+#include "kda_device.h"
+#include "kda_kernels.h"
+
+namespace kda {
+
+namespace {
+
+template <typename StT>
+struct RowIO;
+
+template <>
+struct RowIO<float> {
+  __device__ static void load(const void* base, size_t off, float* x) {
+    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + off);
+    const f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      x[j] = a[j];
+      x[4 + j] = b[j];
+    }
+  }
+  __device__ static void store(void* base, size_t off, const float* x) {
+    f32x4* p = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + off);
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, p);
+    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, p + 1);
+  }
+};
+
+template <>
+struct RowIO<uint16_t> {
+  __device__ static void load(const void* base, size_t off, float* x) {
+    const u32x4 w = __builtin_nontemporal_load(
+        reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + off));
+    unpack_bf16x8(make_uint4(w[0], w[1], w[2], w[3]), x);
+  }
+  __device__ static void store(void* base, size_t off, const float* x) {
+    u32x4 w;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) w[j] = (uint32_t)f32_to_bf16(x[2 * j]) | ((uint32_t)f32_to_bf16(x[2 * j + 1]) << 16);
+    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(base) + off));
+  }
+};
+
+}  // namespace
+
+template <typename StT, bool PER_CHANNEL>
+__global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
+  constexpr int ROWS = 8;  // rows per lane
+  const int tid = threadIdx.x;
+  const int ks = tid & 15;   // key slice: channels 8*ks .. 8*ks+7
+  const int rg = tid >> 4;   // row group: rows rg + 16 i
+  const int bh = blockIdx.x;
+  const int b = bh / p.H, h = bh - b * p.H;
+  const int hq = h / (p.H / p.H_qk);
+  const size_t sbase = (size_t)bh * HD * HD + 8 * ks;
+
+  float s[ROWS][8];
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) RowIO<StT>::load(p.state, sbase + (size_t)(rg + 16 * i) * HD, s[i]);
+
+  float qv[8], kv[8], d[8];
+  {
+    const size_t qoff = ((size_t)b * p.H_qk + hq) * HD + 8 * ks;
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.q + qoff), qv);
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.k + qoff), kv);
+    const float a = __expf(p.A_log[h]);
+    if (PER_CHANNEL) {
+      float gr[8];
+      unpack_bf16x8(*reinterpret_cast<const uint4*>(p.g_raw + ((size_t)bh * HD + 8 * ks)), gr);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        float g;
+        gate_decay(gr[j], a, d[j], g);
+      }
+    } else {
+      float dd, g;
+      gate_decay(bf16_to_f32(p.g_raw[bh]), a, dd, g);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) d[j] = dd;
+    }
+  }
+  float sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    sq += qv[j] * qv[j];
+    sk += kv[j] * kv[j];
+  }
+  sq = sum16(sq);
+  sk = sum16(sk);
+  const float rq = 1.f / sqrtf(sq + 1e-6f), rk = 1.f / sqrtf(sk + 1e-6f);
+  float qk = 0.f;
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    qv[j] *= rq;
+    kv[j] *= rk;
+    qk += qv[j] * kv[j];
+  }
+  qk = sum16(qk);
+  const float beta = sigmoidf_(p.beta[bh]);
+  float vrow[ROWS];
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) vrow[i] = bf16_to_f32(p.v[(size_t)bh * HD + rg + 16 * i]);
+
+#pragma unroll
+  for (int i = 0; i < ROWS; ++i) {
+    float a = 0.f, c = 0.f;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      s[i][j] *= d[j];
+      a += kv[j] * s[i][j];
+      c += qv[j] * s[i][j];
+    }
+    a = sum16(a);
+    c = sum16(c);
+    const float u = beta * (vrow[i] - a);
+#pragma unroll
+    for (int j = 0; j < 8; ++j) s[i][j] += u * kv[j];
+    RowIO<StT>::store(p.state, sbase + (size_t)(rg + 16 * i) * HD, s[i]);
+    if (ks == 0) p.out[(size_t)bh * HD + rg + 16 * i] = f32_to_bf16(p.scale * (c + u * qk));
+  }
+}
+
+void launch_decode(const DecodeParams& p, int B, bool bf16_state, bool per_channel, hipStream_t stream) {
+  dim3 grid((unsigned)(B * p.H));
+  if (bf16_state) {
+    if (per_channel) decode_kernel<uint16_t, true><<<grid, 256, 0, stream>>>(p);
+    else decode_kernel<uint16_t, false><<<grid, 256, 0, stream>>>(p);
+  } else {
+    if (per_channel) decode_kernel<float, true><<<grid, 256, 0, stream>>>(p);
+    else decode_kernel<float, false><<<grid, 256, 0, stream>>>(p);
+  }
+}
+
+}  // namespace kda

@@ -1,0 +1,67 @@
+// kda_kernels.h -- launch interface between the host library and the kernels.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace kda {
+
+// Chunk-local kernel (kda_chunk.hip): one workgroup per (schedule entry, head).
+struct ChunkParams {
+  const uint16_t* q;      // bf16 [tokens, H_qk, 128]
+  const uint16_t* k;      // bf16 [tokens, H_qk, 128]
+  const uint16_t* g_raw;  // bf16 [tokens, H, 128] or [tokens, H]
+  const float* beta;      // fp32 [tokens, H] (logits)
+  const float* A_log;     // fp32 [H]
+  const int4* chunks;     // schedule entries
+  int H, H_qk;
+  uint8_t* rec;           // [entries][H] chunk records
+};
+
+// Recurrence kernel (kda_recur.hip): one workgroup per (chain, value tile).
+struct RecurParams {
+  const uint8_t* rec;
+  const int4* seqs;       // per sequence: first token, length, first schedule entry
+  const int* order;       // sequences in processing order (longest first)
+  int n_chains;           // sequences * H
+  int n_entries;          // schedule entries (records per head)
+  int H;
+  const uint16_t* v;      // bf16 [tokens, H, 128]
+  uint16_t* out;          // bf16 [tokens, H, 128]
+  const void* s0;         // [seqs, H, 128, 128] fp32 or bf16, or null
+  void* s1;               // same layout, or null
+  float scale;
+};
+
+// Decode kernel (kda_decode.hip): one workgroup per (batch row, head).
+struct DecodeParams {
+  const uint16_t* q;      // bf16 [B, H_qk, 128]
+  const uint16_t* k;
+  const uint16_t* v;      // bf16 [B, H, 128]
+  const uint16_t* g_raw;  // bf16 [B, H, 128] or [B, H]
+  const float* beta;      // fp32 [B, H]
+  const float* A_log;     // fp32 [H]
+  void* state;            // [B, H, 128, 128], in place
+  uint16_t* out;          // bf16 [B, H, 128]
+  int H, H_qk;
+  float scale;
+};
+
+// Schedule kernel (kda_table.hip): one workgroup.
+struct TableParams {
+  const int32_t* cu;      // device offsets [N + 1], or null for B rows of T tokens
+  int N;                  // sequences (B when cu is null)
+  int T;                  // tokens per row (dense) or total tokens (packed)
+  int n_entries;          // capacity of `chunks`
+  int4* seqs;             // [N]
+  int4* chunks;           // [n_entries]
+  int* order;             // [N]
+};
+
+void launch_table(const TableParams& p, hipStream_t stream);
+void launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, hipStream_t stream);
+void launch_recur(const RecurParams& p, bool bf16_state, hipStream_t stream);
+int recur_grid(int n_chains);
+void launch_decode(const DecodeParams& p, int B, bool bf16_state, bool per_channel, hipStream_t stream);
+
+}  // namespace kda

@@ -1,0 +1,219 @@
+// kda_recur.hip -- the sequential part of the chunked forward pass.
+//
+// One workgroup owns one (sequence, value head, 16-column value tile): the
+// columns of the state evolve independently, so a chain's 128 value columns
+// are spread over 8 workgroups that never communicate.  Per chunk, with the
+// chunk record produced by the chunk-local kernel and the 128 x 16 state tile
+// S (fp32, held in registers in matrix-core C layout):
+//   U  = T diag(b) V - W S
+//   O  = scale * (Qhat S + M U)          -> out (bf16)
+//   S <- Diag(exp(Gamma_L)) S + Kbar^T U
+// Wave w owns token tile w of U and O and key tiles 2w, 2w+1 of S; the fp16
+// copies of S and U travel between waves through LDS (4 KiB + 2 KiB).
+//
+// Workgroups of one chain are given ids congruent mod 8 so they land on the
+// same XCD and share its L2 for the chunk records.
+#include "kda_device.h"
+#include "kda_kernels.h"
+
+namespace kda {
+
+namespace {
+
+constexpr int VT = 16;        // value columns per workgroup
+constexpr int NVT = HD / VT;  // value tiles per chain
+constexpr int VS = CH + 8;    // row stride (fp16) of the transposed value tile
+
+struct Frags {
+  f16x8 w[4], q[4], k[4], m[2], t[2];
+  float4 gl[2];
+  uint2 v;  // 4 bf16 of the value tile (token tid/4, columns 4*(tid%4)..)
+};
+
+template <typename StT>
+struct StateIO;
+
+template <>
+struct StateIO<float> {
+  __device__ static f32x4 load(const void* base, size_t off) {
+    const float4 x = *reinterpret_cast<const float4*>(reinterpret_cast<const float*>(base) + off);
+    return f32x4{x.x, x.y, x.z, x.w};
+  }
+  __device__ static void store(void* base, size_t off, f32x4 v) {
+    *reinterpret_cast<float4*>(reinterpret_cast<float*>(base) + off) = make_float4(v[0], v[1], v[2], v[3]);
+  }
+};
+
+template <>
+struct StateIO<uint16_t> {  // bf16 state
+  __device__ static f32x4 load(const void* base, size_t off) {
+    const uint2 x = *reinterpret_cast<const uint2*>(reinterpret_cast<const uint16_t*>(base) + off);
+    return f32x4{__uint_as_float(x.x << 16), __uint_as_float(x.x & 0xFFFF0000u),
+                 __uint_as_float(x.y << 16), __uint_as_float(x.y & 0xFFFF0000u)};
+  }
+  __device__ static void store(void* base, size_t off, f32x4 v) {
+    uint2 x;
+    x.x = (uint32_t)f32_to_bf16(v[0]) | ((uint32_t)f32_to_bf16(v[1]) << 16);
+    x.y = (uint32_t)f32_to_bf16(v[2]) | ((uint32_t)f32_to_bf16(v[3]) << 16);
+    *reinterpret_cast<uint2*>(reinterpret_cast<uint16_t*>(base) + off) = x;
+  }
+};
+
+__device__ __forceinline__ f16x8 ldfrag(const uint8_t* rec, int off, int frag, int lane) {
+  return *reinterpret_cast<const f16x8*>(rec + off + frag * FRAG_BYTES + lane * 16);
+}
+
+__device__ __forceinline__ void load_frags(Frags& F, const uint8_t* R, int wave, int lane, int tid,
+                                           const uint16_t* vsrc, int L, size_t vstride) {
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    F.w[s] = ldfrag(R, REC_WNEG, wave * 4 + s, lane);
+    F.q[s] = ldfrag(R, REC_QHAT, wave * 4 + s, lane);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i) F.k[i] = ldfrag(R, REC_KBAR, (2 * wave + (i >> 1)) * 2 + (i & 1), lane);
+  F.m[0] = ldfrag(R, REC_M, wave * 2, lane);
+  F.t[0] = ldfrag(R, REC_TB, wave * 2, lane);
+  if (wave >= 2) {
+    F.m[1] = ldfrag(R, REC_M, wave * 2 + 1, lane);
+    F.t[1] = ldfrag(R, REC_TB, wave * 2 + 1, lane);
+  }
+  const int lg = lane >> 4;
+#pragma unroll
+  for (int i = 0; i < 2; ++i)
+    F.gl[i] = *reinterpret_cast<const float4*>(R + REC_GL + 4 * (SUB * (2 * wave + i) + 4 * lg));
+  const int r = tid >> 2;
+  F.v = (r < L) ? *reinterpret_cast<const uint2*>(vsrc + (size_t)r * vstride) : make_uint2(0u, 0u);
+}
+
+}  // namespace
+
+template <typename StT>
+__global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
+  __shared__ __attribute__((aligned(16))) f16x8 sbuf[4 * 64];  // S slices (B operand)
+  __shared__ __attribute__((aligned(16))) f16x4 ubuf[4 * 64];  // U tiles (C layout)
+  __shared__ __attribute__((aligned(16))) f16 vsT[VT * VS];    // value tile, [column][token]
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int x = blockIdx.x, xcd = x & 7, y = x >> 3;
+  const int vt = y % NVT, ch = (y / NVT) * 8 + xcd;
+  if (ch >= p.n_chains) return;
+  const int n = p.order[ch / p.H], h = ch % p.H;
+  const int4 sq = p.seqs[n];
+  const int tok0 = sq.x, len = sq.y, chunk0 = sq.z;
+  // never walk past the schedule, whatever cu_seqlens held
+  const int nch = max(0, min((len + CH - 1) / CH, p.n_entries - chunk0));
+  const int v0 = vt * VT;
+
+  // state tile: wave holds key tiles 2w, 2w+1; lane (column l16, key rows 4lg..4lg+3)
+  const size_t sbase = ((size_t)n * p.H + h) * HD * HD + (size_t)(v0 + l16) * HD;
+  f32x4 S[2];
+#pragma unroll
+  for (int i = 0; i < 2; ++i) {
+    const int k0 = SUB * (2 * wave + i) + 4 * lg;
+    S[i] = p.s0 ? StateIO<StT>::load(p.s0, sbase + k0) : zero4();
+  }
+
+  const size_t vstride = (size_t)p.H * HD;
+  const int vcol = v0 + 4 * (tid & 3);
+  Frags cur, nxt;
+  if (nch > 0) {
+    const uint8_t* R = p.rec + ((size_t)chunk0 * p.H + h) * REC_BYTES;
+    load_frags(cur, R, wave, lane, tid, p.v + ((size_t)tok0 * p.H + h) * HD + vcol, min(CH, len), vstride);
+  }
+  for (int c = 0; c < nch; ++c) {
+    const int L = min(CH, len - c * CH);
+    if (c + 1 < nch) {
+      const uint8_t* R = p.rec + ((size_t)(chunk0 + c + 1) * p.H + h) * REC_BYTES;
+      const int Ln = min(CH, len - (c + 1) * CH);
+      load_frags(nxt, R, wave, lane, tid, p.v + ((size_t)(tok0 + (c + 1) * CH) * p.H + h) * HD + vcol, Ln,
+                 vstride);
+    }
+    // 1. publish this wave's fp16 slice of S and the value tile
+    {
+      f16x8 sb;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sb[j] = (f16)S[0][j];
+        sb[4 + j] = (f16)S[1][j];
+      }
+      sbuf[wave * 64 + lane] = sb;
+      const int r = tid >> 2, c4 = 4 * (tid & 3);
+      vsT[(c4 + 0) * VS + r] = (f16)__uint_as_float(cur.v.x << 16);
+      vsT[(c4 + 1) * VS + r] = (f16)__uint_as_float(cur.v.x & 0xFFFF0000u);
+      vsT[(c4 + 2) * VS + r] = (f16)__uint_as_float(cur.v.y << 16);
+      vsT[(c4 + 3) * VS + r] = (f16)__uint_as_float(cur.v.y & 0xFFFF0000u);
+    }
+    __syncthreads();
+    // 2. U = T diag(b) V - W S ;  OQ = Qhat S      (token tile `wave`)
+    f16x8 sB[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sB[s] = sbuf[s * 64 + lane];
+    f32x4 U = zero4(), OQ = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      if (s <= (wave >> 1)) {
+        const f16x4 lo = *reinterpret_cast<const f16x4*>(&vsT[l16 * VS + 32 * s + 4 * lg]);
+        const f16x4 hi = *reinterpret_cast<const f16x4*>(&vsT[l16 * VS + 32 * s + 16 + 4 * lg]);
+        const f16x8 vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+        U = mma_f16(cur.t[s], vb, U);
+      }
+    }
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      U = mma_f16(cur.w[s], sB[s], U);
+      OQ = mma_f16(cur.q[s], sB[s], OQ);
+    }
+    // 3. publish U (fp16, C layout of token tile `wave`)
+    {
+      const f16x4 u4 = {(f16)U[0], (f16)U[1], (f16)U[2], (f16)U[3]};
+      ubuf[wave * 64 + lane] = u4;
+    }
+    __syncthreads();
+    // 4. O = scale (OQ + M U) ; S <- Diag(exp(Gamma_L)) S + Kbar^T U
+    f16x8 uB[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f16x4 a = ubuf[(2 * s) * 64 + lane], b = ubuf[(2 * s + 1) * 64 + lane];
+      uB[s] = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+    }
+    f32x4 O = OQ;
+    O = mma_f16(cur.m[0], uB[0], O);
+    if (wave >= 2) O = mma_f16(cur.m[1], uB[1], O);
+    {
+      const size_t orow0 = (size_t)(tok0 + c * CH) * p.H + h;
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int r = SUB * wave + 4 * lg + j;
+        if (r < L) p.out[(orow0 + (size_t)r * p.H) * HD + v0 + l16] = f32_to_bf16(p.scale * O[j]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const float4 gl = cur.gl[i];
+      f32x4 acc = {gl.x * S[i][0], gl.y * S[i][1], gl.z * S[i][2], gl.w * S[i][3]};
+      acc = mma_f16(cur.k[2 * i], uB[0], acc);
+      acc = mma_f16(cur.k[2 * i + 1], uB[1], acc);
+      S[i] = acc;
+    }
+    if (c + 1 < nch) cur = nxt;
+  }
+  if (p.s1) {
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int k0 = SUB * (2 * wave + i) + 4 * lg;
+      StateIO<StT>::store(p.s1, sbase + k0, S[i]);
+    }
+  }
+}
+
+int recur_grid(int n_chains) { return ((n_chains + 7) / 8) * 8 * NVT; }
+
+void launch_recur(const RecurParams& p, bool bf16_state, hipStream_t stream) {
+  dim3 grid(recur_grid(p.n_chains));
+  if (bf16_state) recur_kernel<uint16_t><<<grid, 256, 0, stream>>>(p);
+  else recur_kernel<float><<<grid, 256, 0, stream>>>(p);
+}
+
+}  // namespace kda

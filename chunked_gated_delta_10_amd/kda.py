@@ -1,0 +1,220 @@
+"""Thin Python binding of libkda.so (argument marshalling only).
+
+Every step of the computation runs in the library's HIP kernels; this module
+checks tensor dtypes/shapes, allocates outputs and workspace with torch (the
+only thing torch is used for, together with the current stream) and passes
+raw device pointers through the C ABI declared in ``include/kda.h``.
+
+There is no fallback: if ``libkda.so`` is missing every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+import re
+from typing import Optional, Tuple
+
+import torch
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "libkda.so")
+HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "kda.h")
+
+KDA_STATE_NONE, KDA_STATE_BF16, KDA_STATE_FP32 = 0, 1, 2
+STATUS = {0: "KDA_OK", 1: "KDA_ERR_NULL", 2: "KDA_ERR_SHAPE", 3: "KDA_ERR_DTYPE",
+          4: "KDA_ERR_STATE_DTYPE_MISMATCH", 5: "KDA_ERR_WORKSPACE", 6: "KDA_ERR_ALIGN", 7: "KDA_ERR_HIP"}
+
+_lib = None
+
+
+class KdaError(RuntimeError):
+    def __init__(self, status: int, detail: str):
+        super().__init__("%s: %s" % (STATUS.get(status, str(status)), detail))
+        self.status = status
+        self.detail = detail
+
+
+def header_functions():
+    """Names of the functions include/kda.h declares."""
+    with open(HEADER_PATH) as f:
+        text = f.read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(kda_[a-z_]+)\s*\(", text)))
+
+
+def load():
+    """Load libkda.so (raises if it has not been built)."""
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(LIB_PATH):
+        raise RuntimeError("libkda.so is not built (%s); run __graft_entry__.build() first" % LIB_PATH)
+    lib = ctypes.CDLL(LIB_PATH)
+    P, I, F, Z = ctypes.c_void_p, ctypes.c_int, ctypes.c_float, ctypes.c_size_t
+    lib.kda_fwd_workspace_bytes.restype = Z
+    lib.kda_fwd_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.kda_fwd.restype = I
+    lib.kda_fwd.argtypes = [P, P, P, P, P, P, F, I, P, I, P, P, I, I, I, I, I, I, I, P, Z, P]
+    lib.kda_fwd_varlen.restype = I
+    lib.kda_fwd_varlen.argtypes = [P, P, P, P, P, P, F, I, P, I, P, P, I, P, I, I, I, I, I, I, P, Z, P]
+    lib.kda_decode_step.restype = I
+    lib.kda_decode_step.argtypes = [P, P, P, P, P, P, F, I, P, I, P, I, I, I, I, I, P]
+    lib.kda_status_string.restype = ctypes.c_char_p
+    lib.kda_status_string.argtypes = [I]
+    lib.kda_last_error.restype = ctypes.c_char_p
+    lib.kda_last_error.argtypes = []
+    _lib = lib
+    return lib
+
+
+def _check(status: int):
+    if status != 0:
+        raise KdaError(status, load().kda_last_error().decode())
+
+
+def _ptr(t: Optional[torch.Tensor]):
+    return None if t is None else ctypes.c_void_p(t.data_ptr())
+
+
+def _stream(stream) -> ctypes.c_void_p:
+    s = torch.cuda.current_stream() if stream is None else stream
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _state_code(t: Optional[torch.Tensor]) -> int:
+    if t is None:
+        return KDA_STATE_NONE
+    if t.dtype == torch.float32:
+        return KDA_STATE_FP32
+    if t.dtype == torch.bfloat16:
+        return KDA_STATE_BF16
+    raise TypeError("state must be float32 or bfloat16, got %s" % t.dtype)
+
+
+def _need(t: torch.Tensor, name: str, dtype: torch.dtype):
+    if t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if not t.is_cuda:
+        raise ValueError("%s must be a device tensor" % name)
+    if not t.is_contiguous():
+        raise ValueError("%s must be contiguous" % name)
+
+
+def workspace_bytes(B: int, T: int, H_qk: int, H: int, N: int = 0) -> int:
+    return int(load().kda_fwd_workspace_bytes(B, T, H_qk, H, N))
+
+
+def _workspace(nbytes: int, device) -> torch.Tensor:
+    return torch.empty(max(nbytes, 256), dtype=torch.uint8, device=device)
+
+
+def _prep(q, k, v, g_raw, beta_logits, A_log):
+    _need(q, "q", torch.bfloat16)
+    _need(k, "k", torch.bfloat16)
+    _need(v, "v", torch.bfloat16)
+    _need(g_raw, "g_raw", torch.bfloat16)
+    _need(beta_logits, "beta_logits", torch.float32)
+    _need(A_log, "A_log", torch.float32)
+    if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
+        raise ValueError("q, k must be [B, T, H_qk, K] and v [B, T, H, V]")
+    B, T, H_qk, K = q.shape
+    H, V = v.shape[2], v.shape[3]
+    if g_raw.shape == (B, T, H, K):
+        per_channel = 1
+    elif g_raw.shape == (B, T, H):
+        per_channel = 0
+    else:
+        raise ValueError("g_raw must be [B, T, H, K] (per channel) or [B, T, H] (scalar)")
+    if beta_logits.shape != (B, T, H) or A_log.shape != (H,):
+        raise ValueError("beta_logits must be [B, T, H] and A_log [H]")
+    return B, T, H_qk, H, K, V, per_channel
+
+
+def fwd(q, k, v, g_raw, beta_logits, A_log, scale: Optional[float] = None,
+        initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+        final_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None, state_dtype: Optional[torch.dtype] = None,
+        stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked KDA forward over B rows of T tokens.  Returns (out, final_state)."""
+    lib = load()
+    B, T, H_qk, H, K, V, per_channel = _prep(q, k, v, g_raw, beta_logits, A_log)
+    scale = K ** -0.5 if scale is None else float(scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
+    if final_state is None and output_final_state:
+        sd = state_dtype or (initial_state.dtype if initial_state is not None else torch.float32)
+        final_state = torch.empty((B, H, V, K), dtype=sd, device=dev)
+    for t, n in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None and (tuple(t.shape) != (B, H, V, K) or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous [B, H, V, K] tensor" % n)
+    nbytes = workspace_bytes(B, T, H_qk, H, 0)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _workspace(nbytes, dev)
+    _check(lib.kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale,
+                       per_channel, _ptr(initial_state), _state_code(initial_state), _ptr(out),
+                       _ptr(final_state), _state_code(final_state), B, T, H_qk, H, K, V, _ptr(workspace),
+                       workspace.numel(), _stream(stream)))
+    return out, final_state
+
+
+def fwd_varlen(q, k, v, g_raw, beta_logits, A_log, cu_seqlens: torch.Tensor, scale: Optional[float] = None,
+               initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+               final_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+               workspace: Optional[torch.Tensor] = None, state_dtype: Optional[torch.dtype] = None,
+               stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked KDA forward over packed sequences (B = 1).  Returns (out, final_state [N, H, V, K])."""
+    lib = load()
+    B, T, H_qk, H, K, V, per_channel = _prep(q, k, v, g_raw, beta_logits, A_log)
+    if B != 1:
+        raise ValueError("packed sequences need B == 1")
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    N = cu_seqlens.numel() - 1
+    scale = K ** -0.5 if scale is None else float(scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty((1, T, H, V), dtype=torch.bfloat16, device=dev)
+    if final_state is None and output_final_state:
+        sd = state_dtype or (initial_state.dtype if initial_state is not None else torch.float32)
+        final_state = torch.empty((N, H, V, K), dtype=sd, device=dev)
+    for t, n in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None and (tuple(t.shape) != (N, H, V, K) or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous [N, H, V, K] tensor" % n)
+    nbytes = workspace_bytes(1, T, H_qk, H, max(N, 0))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _workspace(nbytes, dev)
+    _check(lib.kda_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale,
+                              per_channel, _ptr(initial_state), _state_code(initial_state), _ptr(out),
+                              _ptr(final_state), _state_code(final_state), _ptr(cu_seqlens), N, T, H_qk, H, K, V,
+                              _ptr(workspace), workspace.numel(), _stream(stream)))
+    return out, final_state
+
+
+def decode_step(q, k, v, g_raw, beta_logits, A_log, state: torch.Tensor, scale: Optional[float] = None,
+                out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decode step; `state` [B, H, V, K] is updated in place.  Returns out [B, H, V]."""
+    lib = load()
+    for t, n, dt in ((q, "q", torch.bfloat16), (k, "k", torch.bfloat16), (v, "v", torch.bfloat16),
+                     (g_raw, "g_raw", torch.bfloat16), (beta_logits, "beta_logits", torch.float32),
+                     (A_log, "A_log", torch.float32)):
+        _need(t, n, dt)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3:
+        raise ValueError("q, k must be [B, H_qk, K] and v [B, H, V]")
+    B, H_qk, K = q.shape
+    H, V = v.shape[1], v.shape[2]
+    if g_raw.shape == (B, H, K):
+        per_channel = 1
+    elif g_raw.shape == (B, H):
+        per_channel = 0
+    else:
+        raise ValueError("g_raw must be [B, H, K] or [B, H]")
+    if tuple(state.shape) != (B, H, V, K) or not state.is_contiguous():
+        raise ValueError("state must be a contiguous [B, H, V, K] tensor")
+    scale = K ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, V), dtype=torch.bfloat16, device=q.device)
+    _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale,
+                               per_channel, _ptr(state), _state_code(state), _ptr(out), B, H_qk, H, K, V,
+                               _stream(stream)))
+    return out

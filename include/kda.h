@@ -1,0 +1,135 @@
+/*
+ * kda.h -- C ABI of libkda.so: Kimi Delta Attention (KDA) forward pass on
+ * AMD MI355X (gfx950).
+ *
+ * The operator (a gated delta rule; interface constraints from the refft.com
+ * "FlashKDA: High-performance KDA CUDA kernels for SM90+ GPUs" summary,
+ * sections "How does FlashKDA's stateful/streaming (chunked) support work?"
+ * and "How to seamlessly replace flash-linear-attention's chunk_kda"):
+ * per chain (a batch row, or one packed sequence) and value head h, with a
+ * state S in R^{K x V} and for each token t
+ *
+ *     qn = q_t / sqrt(|q_t|^2 + 1e-6),  kn = k_t / sqrt(|k_t|^2 + 1e-6)
+ *     g_t = -exp(A_log[h]) * softplus(g_raw_t)      (<= 0; per key channel,
+ *                                                    or one value per token
+ *                                                    and head)
+ *     b_t = sigmoid(beta_logit_t)
+ *     S_t = (I - b_t kn kn^T) Diag(exp(g_t)) S_{t-1} + b_t kn v_t^T
+ *     o_t = scale * S_t^T qn
+ *
+ * The gate activation, the sigmoid and the q/k L2 normalisation all run
+ * inside the kernels; callers pass raw values.  K = V = 128 only (the
+ * FlashKDA summary: the implementation assumes K = V = 128).
+ *
+ * Conventions shared by every entry point
+ * ----------------------------------------
+ * - Every tensor pointer is a caller-owned DEVICE pointer to contiguous
+ *   row-major memory, 16-byte aligned.  The library never allocates, frees
+ *   or retains device memory, creates no streams and keeps no device state.
+ * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
+ *   default stream).  Nothing synchronises the host.
+ * - Arguments are validated on the host before anything is enqueued; on a
+ *   validation failure nothing is enqueued, a status is returned and
+ *   kda_last_error() describes the problem.  Launch failures return
+ *   KDA_ERR_HIP.  Faults inside a kernel surface at the caller's next
+ *   synchronisation.  No C++ exception crosses this ABI.
+ * - Token layout: q, k are [B, T, H_qk, 128]; v and out are [B, T, H, 128];
+ *   value head h reads q/k head h / (H / H_qk) (contiguous groups, so
+ *   H % H_qk == 0).  bf16 tensors hold IEEE bfloat16.
+ * - g_raw is bf16 [B, T, H, 128] when gate_per_channel = 1 (KDA), or
+ *   bf16 [B, T, H] when gate_per_channel = 0 (one decay per token and head:
+ *   the gated delta rule with grouped value heads benchmarked on the
+ *   FlashQLA H200 page, "FORWARD BENCHMARKS" table).
+ * - beta_logits is fp32 [B, T, H]; A_log is fp32 [H].
+ * - State layout is [C, H, V, K] with state[c][h][v][k] = S[k][v], where
+ *   C = B (dense) or N (packed sequences).  A state is fp32 or bf16; when
+ *   both an initial and a final state are given their dtypes must match.
+ *   initial_state = NULL means a zero state; final_state = NULL means the
+ *   final state is not written.  initial_state may equal final_state (the
+ *   state is read before it is overwritten).
+ */
+#ifndef KDA_H
+#define KDA_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+  KDA_OK = 0,
+  KDA_ERR_NULL = 1,                  /* a required pointer is NULL */
+  KDA_ERR_SHAPE = 2,                 /* a size is negative, K or V != 128, H % H_qk != 0, ... */
+  KDA_ERR_DTYPE = 3,                 /* unknown state dtype */
+  KDA_ERR_STATE_DTYPE_MISMATCH = 4,  /* initial and final state dtypes differ */
+  KDA_ERR_WORKSPACE = 5,             /* workspace NULL or smaller than kda_fwd_workspace_bytes() */
+  KDA_ERR_ALIGN = 6,                 /* a pointer is not 16-byte aligned */
+  KDA_ERR_HIP = 7                    /* the HIP runtime reported an error */
+} kda_status;
+
+typedef enum { KDA_STATE_NONE = 0, KDA_STATE_BF16 = 1, KDA_STATE_FP32 = 2 } kda_state_dtype;
+
+/*
+ * Bytes of device workspace kda_fwd (N = 0) or kda_fwd_varlen (N > 0
+ * packed sequences, B = 1) needs for these sizes.  Returns 0 for invalid
+ * sizes.  The workspace holds per-chunk intermediates and the chunk
+ * schedule; its contents need not be initialised and are garbage afterwards.
+ */
+size_t kda_fwd_workspace_bytes(int B, int T, int H_qk, int H, int N);
+
+/*
+ * Chunked forward pass over B independent rows of T tokens (the cuLA KDA
+ * fixed-length table's B x T workload).  States are [B, H, V, K].
+ * B * T == 0 is a successful no-op.
+ */
+kda_status kda_fwd(const void* q, const void* k, const void* v, const void* g_raw,
+                   const float* beta_logits, const float* A_log, float scale,
+                   int gate_per_channel, const void* initial_state, kda_state_dtype init_dtype,
+                   void* out, void* final_state, kda_state_dtype final_dtype, int B, int T,
+                   int H_qk, int H, int K, int V, void* workspace, size_t workspace_bytes,
+                   void* stream);
+
+/*
+ * Chunked forward pass over N packed sequences (the FlashKDA summary: with
+ * cu_seqlens, B must be 1 and the state is [N, H, V, K]; the cuLA KDA varlen
+ * table's workload).  The token tensors have B = 1 and T = total tokens.
+ * cu_seqlens is a DEVICE int32 array of N + 1 offsets with cu_seqlens[0] = 0,
+ * non-decreasing, cu_seqlens[N] = T; it is read on the device (no host
+ * copy).  Its contents are a precondition: they are only checked when the
+ * environment variable KDA_DEBUG=1 is set, which synchronises the stream.
+ * Zero-length sequences are allowed (their final state equals their initial
+ * state).  N == 0 or T == 0 is a successful no-op (no state is written).
+ */
+kda_status kda_fwd_varlen(const void* q, const void* k, const void* v, const void* g_raw,
+                          const float* beta_logits, const float* A_log, float scale,
+                          int gate_per_channel, const void* initial_state,
+                          kda_state_dtype init_dtype, void* out, void* final_state,
+                          kda_state_dtype final_dtype, const int32_t* cu_seqlens, int N, int T,
+                          int H_qk, int H, int K, int V, void* workspace, size_t workspace_bytes,
+                          void* stream);
+
+/*
+ * One decode step: every batch row advances by exactly one token (the cuLA
+ * single-token decode table's workload shape: batch up to 256, 64 heads,
+ * head dim 128).  q, k: bf16 [B, H_qk, 128]; v: bf16 [B, H, 128]; g_raw:
+ * bf16 [B, H, 128] or [B, H]; beta_logits: fp32 [B, H]; state: [B, H, V, K]
+ * updated in place; out: bf16 [B, H, 128].  B == 0 is a successful no-op.
+ */
+kda_status kda_decode_step(const void* q, const void* k, const void* v, const void* g_raw,
+                           const float* beta_logits, const float* A_log, float scale,
+                           int gate_per_channel, void* state, kda_state_dtype state_dtype,
+                           void* out, int B, int H_qk, int H, int K, int V, void* stream);
+
+/* Static, human-readable name of a status code. */
+const char* kda_status_string(kda_status status);
+
+/* Detail of the last non-OK status returned on the calling thread ("" if none). */
+const char* kda_last_error(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KDA_H */
