@@ -1,0 +1,210 @@
+#!/usr/bin/env python3
+"""KDA chunked forward throughput on one MI355X.
+
+A step is one kda_fwd call (schedule, chunk-local and recurrence kernels:
+the whole chunked hot path) over one batch of the dense KDA workload
+B=2, T=16384, H=16, K=V=128 with fp32 initial/final state, inputs already
+resident in HBM.  Prints ONE JSON line (see the design doc for the fields).
+
+    python bench.py [--gpus 1] [--steps 100] [--warmup 10]
+
+Only one GPU is used; --gpus above 1 exits with an explanation.
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
+MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix throughput, published
+D, C = 128, 64                 # head dim, chunk length
+FLOP_PER_TOKEN_HEAD = 6 * D * D + 5 * C * D   # 139,264 (algorithmic, per token and head)
+KERNEL_SOURCES = ["chunked_gated_delta_10_amd/csrc/kda_chunk.hip", "chunked_gated_delta_10_amd/csrc/kda_recur.hip",
+                  "chunked_gated_delta_10_amd/csrc/kda_decode.hip", "chunked_gated_delta_10_amd/csrc/kda_device.h"]
+
+
+def algorithmic_bytes(w, with_state=True):
+    """Each input read once and each output written once (bytes), split by kernel."""
+    tok = w.B * w.T
+    qk = 2 * tok * w.H_qk * D * 2
+    g = tok * w.H * (D if w.gate_per_channel else 1) * 2
+    beta = tok * w.H * 4
+    v = tok * w.H * D * 2
+    out = tok * w.H * D * 2
+    C_ = w.N if w.N else w.B
+    state = C_ * w.H * D * D * 4
+    s_in = state if w.state_std is not None else 0
+    s_out = state if with_state else 0
+    return {"kda_chunk_local": qk + g + beta + w.H * 4, "kda_recur": v + out + s_in + s_out}
+
+
+def sources_hash():
+    h = hashlib.sha256()
+    for p in KERNEL_SOURCES:
+        with open(os.path.join(ROOT, p), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def load_traffic(kernel, workload):
+    """HBM bytes per launch measured with rocprofv3 counters, if taken on the current kernel sources."""
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        data = json.load(f)
+    rec = data.get(workload, {}).get(kernel)
+    if not rec or rec.get("sources_hash") != sources_hash():
+        return None
+    return rec.get("hbm_bytes_per_launch")
+
+
+def cpu_baseline(inp, w, tokens):
+    """The fp64 oracle, untuned, on the first `tokens` tokens of every row of the same workload."""
+    import numpy as np
+    import oracle
+    sub = {}
+    for n in ("q", "k", "v", "g_raw", "b"):
+        sub[n] = np.ascontiguousarray(inp[n][:, :tokens])
+    cores = min(os.cpu_count() or 1, w.B * w.H)
+    t0 = time.perf_counter()
+    oracle.kda_fwd(sub["q"], sub["k"], sub["v"], sub["g_raw"], sub["b"], inp["A_log"], inp["scale"],
+                   gate_per_channel=w.gate_per_channel, initial_state=inp["initial_state"], nthreads=cores)
+    dt = time.perf_counter() - t0
+    return {"value": w.B * tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
+            "sample": "%s: all %d chains (B=%d x H=%d), first %d of %d tokens per row, fp32 initial state; %.1f s"
+                      % (w.name, w.B * w.H, w.B, w.H, tokens, w.T, dt)}
+
+
+def time_workload(name, steps, warmup):
+    """Returns (ms per step, per-kernel {name: avg ms}, inputs, workload)."""
+    import torch
+    from chunked_gated_delta_10_amd import kda
+    from chunked_gated_delta_10_amd.inputs import WORKLOADS, workload_inputs
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import kda_util as U
+    w = WORKLOADS[name]
+    inp = workload_inputs(name)
+    d = U.to_device(inp)
+    if w.decode:
+        st = d["initial_state"]
+        out = torch.empty((w.B, w.H, D), dtype=torch.bfloat16, device="cuda")
+
+        def step():
+            kda.decode_step(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], st, scale=inp["scale"], out=out)
+    else:
+        C_ = w.N if w.N else w.B
+        out = torch.empty((w.B, w.T, w.H, D), dtype=torch.bfloat16, device="cuda")
+        fin = torch.empty((C_, w.H, D, D), dtype=torch.float32, device="cuda")
+        ws = torch.empty(kda.workspace_bytes(w.B, w.T, w.H_qk, w.H, w.N), dtype=torch.uint8, device="cuda")
+        if w.N:
+            def step():
+                kda.fwd_varlen(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], d["cu_seqlens"],
+                               scale=inp["scale"], initial_state=d["initial_state"], final_state=fin, out=out,
+                               workspace=ws)
+        else:
+            def step():
+                kda.fwd(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], scale=inp["scale"],
+                        initial_state=d["initial_state"], final_state=fin, out=out, workspace=ws)
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    kda.kernel_timing(True)
+    kda.kernel_timing_read()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record()
+    for _ in range(steps):
+        step()
+    ev1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kt = kda.kernel_timing_read()
+    kda.kernel_timing(False)
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms = max(wall * 1000.0, gpu_ms) / steps
+    per_kernel = {k: v[0] / v[1] for k, v in kt.items()}
+    return ms, per_kernel, inp, w
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=100)
+    ap.add_argument("--warmup", type=int, default=10)
+    ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens per row in the oracle's timed sample")
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    args = ap.parse_args()
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py runs on exactly one GPU: the KDA path here is built and measured on a single MI355X "
+              "(sharding across GPUs is by batch, sequence and head with no exchange; see DESIGN.md). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    assert torch.cuda.is_available(), "bench.py needs a GPU"
+    from chunked_gated_delta_10_amd import kda
+    kda.load()
+
+    name = "kda_dense"
+    ms, per_kernel, inp, w = time_workload(name, args.steps, args.warmup)
+    tokens = w.B * w.T
+    value = tokens / (ms / 1000.0)
+    alg = algorithmic_bytes(w)
+    alg_total = sum(alg.values())
+    flops = FLOP_PER_TOKEN_HEAD * tokens * w.H
+    kernels = {}
+    for k, avg in per_kernel.items():
+        b = alg.get(k, 0)
+        kernels[k] = {"avg_ms": round(avg, 4), "algorithmic_bytes": b,
+                      "hbm_gbs": round(b / (avg * 1e-3) / 1e9, 1) if b else None,
+                      "hbm_frac": round(b / (avg * 1e-3) / 1e9 / HBM_PEAK_GBS, 4) if b else None}
+    dom = max((k for k in per_kernel if k in alg), key=lambda k: per_kernel[k])
+    dom_gbs = alg[dom] / (per_kernel[dom] * 1e-3) / 1e9
+    roofline = {"bound": "hbm", "achieved": round(dom_gbs, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom_gbs / HBM_PEAK_GBS, 4), "traffic": load_traffic(dom, name), "kernel": dom,
+                "algorithmic_bytes_per_launch": alg[dom], "avg_launch_ms": round(per_kernel[dom], 4),
+                "step": {"algorithmic_bytes": alg_total,
+                         "hbm_frac": round(alg_total / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                         "algorithmic_flop": flops,
+                         "mfma_frac": round(flops / (ms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}}
+    result = {
+        "metric": "KDA fwd tokens/s (B=2,T=16384,H=16,K=V=128) + % of MFMA/HBM roofline",
+        "value": round(value, 1), "unit": "tokens/s", "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
+        "ms_per_step": round(ms, 4), "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
+        "dtype": "bf16", "data": "synthetic",
+        "config": {"workload": name, "B": w.B, "T": w.T, "H": w.H, "H_qk": w.H_qk, "K": D, "V": D,
+                   "state": "fp32 in/out", "seed": w.seed},
+        "roofline": roofline,
+        "kernels": kernels,
+    }
+    if not args.no_extra:
+        extra = {}
+        for other in ("kda_varlen", "gdn_gva", "kda_decode"):
+            oms, opk, _, ow = time_workload(other, max(10, args.steps // 5), 3)
+            ab = algorithmic_bytes(ow)
+            tok = ow.B if ow.decode else ow.B * ow.T
+            tot = sum(ab.values())
+            extra[other] = {"ms_per_step": round(oms, 4), "tokens_per_s": round(tok / (oms * 1e-3), 1),
+                            "algorithmic_bytes": tot,
+                            "hbm_frac": round(tot / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                            "kernels_avg_ms": {k: round(v, 4) for k, v in opk.items()}}
+        result["other_workloads"] = extra
+    if not args.no_cpu_baseline:
+        result["cpu_baseline"] = cpu_baseline(inp, w, min(args.cpu_tokens, w.T))
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()

@@ -65,6 +65,46 @@ Layout layout(int n_seqs, int n_entries, int H) {
 
 int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
+// ---- per-kernel event timing (diagnostics) --------------------------------
+enum { K_TABLE = 0, K_CHUNK = 1, K_RECUR = 2, K_DECODE = 3, K_COUNT = 4 };
+const char* const kKernelNames[K_COUNT] = {"kda_table", "kda_chunk_local", "kda_recur", "kda_decode"};
+
+struct Timing {
+  bool on = false;
+  struct Rec { int id; hipEvent_t a, b; };
+  std::vector<Rec> pending;
+  std::vector<hipEvent_t> pool;
+  hipEvent_t get() {
+    if (!pool.empty()) {
+      hipEvent_t e = pool.back();
+      pool.pop_back();
+      return e;
+    }
+    hipEvent_t e = nullptr;
+    if (hipEventCreate(&e) != hipSuccess) return nullptr;
+    return e;
+  }
+};
+thread_local Timing g_timing;
+
+// Brackets one launch with events when timing is on.
+struct Timed {
+  int id;
+  hipStream_t s;
+  hipEvent_t a = nullptr, b = nullptr;
+  Timed(int id_, hipStream_t s_) : id(id_), s(s_) {
+    if (!g_timing.on) return;
+    a = g_timing.get();
+    b = g_timing.get();
+    if (a && b) (void)hipEventRecord(a, s);
+  }
+  ~Timed() {
+    if (!a || !b) return;
+    (void)hipEventRecord(b, s);
+    g_timing.pending.push_back({id, a, b});
+  }
+};
+
 kda_status check_state_dtypes(const void* init, kda_state_dtype idt, const void* fin, kda_state_dtype fdt,
                                bool* bf16) {
   auto valid = [](kda_state_dtype d) { return d == KDA_STATE_BF16 || d == KDA_STATE_FP32; };
@@ -155,15 +195,22 @@ kda_status run_forward(const FwdArgs& a) {
 
   (void)hipGetLastError();  // clear any stale error before launching
   kda::TableParams tp{a.cu, a.n_seqs, a.T, n_entries, seqs, chunks, order};
-  kda::launch_table(tp, a.stream);
+  {
+    Timed t(K_TABLE, a.stream);
+    kda::launch_table(tp, a.stream);
+  }
   if (n_entries > 0 && tokens > 0) {
     kda::ChunkParams cp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                         static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log, chunks, a.H, a.H_qk, ws + L.rec};
+    Timed t(K_CHUNK, a.stream);
     kda::launch_chunk_local(cp, n_entries, a.gate_per_channel == 1, a.stream);
   }
   kda::RecurParams rp{ws + L.rec, seqs, order, a.n_seqs * a.H, n_entries, a.H, static_cast<const uint16_t*>(a.v),
                       static_cast<uint16_t*>(a.out), a.s0, a.s1, a.scale};
-  kda::launch_recur(rp, bf16_state, a.stream);
+  {
+    Timed t(K_RECUR, a.stream);
+    kda::launch_recur(rp, bf16_state, a.stream);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   if (env_flag("KDA_LOG"))
@@ -231,7 +278,10 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
   kda::DecodeParams p{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
                       static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(g_raw), beta_logits, A_log,
                       state, static_cast<uint16_t*>(out), H, H_qk, scale};
-  kda::launch_decode(p, B, state_dtype == KDA_STATE_BF16, gate_per_channel == 1, static_cast<hipStream_t>(stream));
+  {
+    Timed t(K_DECODE, static_cast<hipStream_t>(stream));
+    kda::launch_decode(p, B, state_dtype == KDA_STATE_BF16, gate_per_channel == 1, static_cast<hipStream_t>(stream));
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   if (env_flag("KDA_LOG"))
@@ -255,5 +305,29 @@ const char* kda_status_string(kda_status s) {
 }
 
 const char* kda_last_error(void) { return g_last_error.c_str(); }
+
+void kda_kernel_timing_enable(int enable) { g_timing.on = enable != 0; }
+
+int kda_kernel_timing_read(double* total_ms, int* launches, int max_kernels) {
+  for (int i = 0; i < max_kernels && i < K_COUNT; ++i) {
+    if (total_ms) total_ms[i] = 0.0;
+    if (launches) launches[i] = 0;
+  }
+  int rc = K_COUNT;
+  for (auto& r : g_timing.pending) {
+    float ms = 0.f;
+    if (hipEventSynchronize(r.b) != hipSuccess || hipEventElapsedTime(&ms, r.a, r.b) != hipSuccess) rc = -1;
+    if (r.id < max_kernels) {
+      if (total_ms) total_ms[r.id] += ms;
+      if (launches) launches[r.id] += 1;
+    }
+    g_timing.pool.push_back(r.a);
+    g_timing.pool.push_back(r.b);
+  }
+  g_timing.pending.clear();
+  return rc;
+}
+
+const char* kda_kernel_name(int id) { return (id >= 0 && id < K_COUNT) ? kKernelNames[id] : ""; }
 
 }  // extern "C"

@@ -64,10 +64,8 @@ constexpr int REC_BYTES = REC_GL + HD * 4;            // 66048
 __device__ __forceinline__ float bf16_to_f32(uint16_t h) { return __uint_as_float((uint32_t)h << 16); }
 
 __device__ __forceinline__ uint16_t f32_to_bf16(float f) {
-  // round to nearest even (inputs are finite)
-  uint32_t u = __float_as_uint(f);
-  u += 0x7FFFu + ((u >> 16) & 1u);
-  return (uint16_t)(u >> 16);
+  // round to nearest even (one v_cvt_pk_bf16_f32 on gfx950)
+  return __builtin_bit_cast(uint16_t, (__bf16)f);
 }
 
 __device__ __forceinline__ void unpack_bf16x8(const uint4& w, float* out) {
@@ -89,7 +87,7 @@ __device__ __forceinline__ f16x8 to_f16x8(const float* x) {
 __device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
   bf16x8 r;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) r[i] = __builtin_bit_cast(__bf16, f32_to_bf16(x[i]));
+  for (int i = 0; i < 8; ++i) r[i] = (__bf16)x[i];
   return r;
 }
 
@@ -97,9 +95,9 @@ __device__ __forceinline__ bf16x8 to_bf16x8(const float* x) {
 __device__ __forceinline__ void split_bf16x8(const float* x, bf16x8& hi, bf16x8& lo) {
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
-    const uint16_t h = f32_to_bf16(x[i]);
-    hi[i] = __builtin_bit_cast(__bf16, h);
-    lo[i] = __builtin_bit_cast(__bf16, f32_to_bf16(x[i] - bf16_to_f32(h)));
+    const __bf16 h = (__bf16)x[i];
+    hi[i] = h;
+    lo[i] = (__bf16)(x[i] - (float)h);
   }
 }
 
@@ -146,10 +144,12 @@ __device__ __forceinline__ float sum64(float x) {
 __device__ __forceinline__ void gate_decay(float x, float a, float& d, float& g) {
   constexpr float LOG2E = 1.4426950408889634f;
   constexpr float LN2 = 0.6931471805599453f;
+  // v_exp_f32 / v_log_f32 directly (no denormal range handling is needed:
+  // 1 + 2^y >= 1, and a decay below 2^-126 may flush to zero)
   float t2;  // softplus(x) / ln 2
   if (x > 20.f) t2 = x * LOG2E;
-  else t2 = __log2f(1.f + exp2f(x * LOG2E));
-  d = exp2f(-a * t2);
+  else t2 = __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(x * LOG2E));
+  d = __builtin_amdgcn_exp2f(-a * t2);
   g = -a * LN2 * t2;
 }
 

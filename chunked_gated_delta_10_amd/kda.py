@@ -64,6 +64,12 @@ def load():
     lib.kda_status_string.argtypes = [I]
     lib.kda_last_error.restype = ctypes.c_char_p
     lib.kda_last_error.argtypes = []
+    lib.kda_kernel_timing_enable.restype = None
+    lib.kda_kernel_timing_enable.argtypes = [I]
+    lib.kda_kernel_timing_read.restype = I
+    lib.kda_kernel_timing_read.argtypes = [ctypes.POINTER(ctypes.c_double), ctypes.POINTER(ctypes.c_int), I]
+    lib.kda_kernel_name.restype = ctypes.c_char_p
+    lib.kda_kernel_name.argtypes = [I]
     _lib = lib
     return lib
 
@@ -99,6 +105,23 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype):
         raise ValueError("%s must be a device tensor" % name)
     if not t.is_contiguous():
         raise ValueError("%s must be contiguous" % name)
+
+
+def kernel_timing(enable: bool) -> None:
+    """Turn per-kernel HIP-event timing of this thread's launches on or off."""
+    load().kda_kernel_timing_enable(1 if enable else 0)
+
+
+def kernel_timing_read() -> dict:
+    """{kernel name: (total ms, launches)} since the last read (waits for the events)."""
+    lib = load()
+    n = 8
+    ms = (ctypes.c_double * n)()
+    cnt = (ctypes.c_int * n)()
+    k = lib.kda_kernel_timing_read(ms, cnt, n)
+    if k < 0:
+        raise RuntimeError("kda_kernel_timing_read failed")
+    return {lib.kda_kernel_name(i).decode(): (ms[i], cnt[i]) for i in range(k) if cnt[i] > 0}
 
 
 def workspace_bytes(B: int, T: int, H_qk: int, H: int, N: int = 0) -> int:

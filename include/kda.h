@@ -122,6 +122,20 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
                            int gate_per_channel, void* state, kda_state_dtype state_dtype,
                            void* out, int B, int H_qk, int H, int K, int V, void* stream);
 
+/*
+ * Diagnostics: per-kernel timing with HIP events (used by the benchmark).
+ * While enabled on the calling thread, each kernel launched by the entry
+ * points above is bracketed by two hipEventRecord calls on the caller's
+ * stream.  kda_kernel_timing_read() waits for those events, writes the total
+ * milliseconds and launch count per kernel id into the caller's arrays
+ * (up to max_kernels entries), forgets them, and returns the number of
+ * kernel ids (or -1 on a HIP error).  Kernel ids: 0 schedule, 1 chunk-local,
+ * 2 recurrence, 3 decode.  The events are created by the library and reused.
+ */
+void kda_kernel_timing_enable(int enable);
+int kda_kernel_timing_read(double* total_ms, int* launches, int max_kernels);
+const char* kda_kernel_name(int id);
+
 /* Static, human-readable name of a status code. */
 const char* kda_status_string(kda_status status);
 
