@@ -101,8 +101,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     sq += qv[j] * qv[j];
     sk += kv[j] * kv[j];
   }
-  sq = sum16(sq);
-  sk = sum16(sk);
+  sq = rowsum16(sq);
+  sk = rowsum16(sk);
   const float rq = 1.f / sqrtf(sq + 1e-6f), rk = 1.f / sqrtf(sk + 1e-6f);
   float qk = 0.f;
 #pragma unroll
@@ -111,7 +111,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     kv[j] *= rk;
     qk += qv[j] * kv[j];
   }
-  qk = sum16(qk);
+  qk = rowsum16(qk);
   const float beta = sigmoidf_(p.beta[bh]);
   float vrow[ROWS];
 #pragma unroll
@@ -126,8 +126,8 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
       a += kv[j] * s[i][j];
       c += qv[j] * s[i][j];
     }
-    a = sum16(a);
-    c = sum16(c);
+    a = rowsum16(a);
+    c = rowsum16(c);
     const float u = beta * (vrow[i] - a);
 #pragma unroll
     for (int j = 0; j < 8; ++j) s[i][j] += u * kv[j];

@@ -123,6 +123,25 @@ __device__ __forceinline__ float sum4(float x) {
   x += __shfl_xor(x, 2);
   return x;
 }
+// Sum over an aligned row of 16 lanes with DPP row rotations (no LDS traffic):
+// after rotating by 8, 4, 2, 1 every lane of the row holds the row sum.
+__device__ __forceinline__ float dpp_ror(float x, int n) {
+  // DPP control 0x120 + n: row_ror:n (rotate right within a row of 16 lanes)
+  switch (n) {
+    case 8: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x128, 0xF, 0xF, false));
+    case 4: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x124, 0xF, 0xF, false));
+    case 2: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x122, 0xF, 0xF, false));
+    default: return __builtin_bit_cast(float, __builtin_amdgcn_mov_dpp(__builtin_bit_cast(int, x), 0x121, 0xF, 0xF, false));
+  }
+}
+__device__ __forceinline__ float rowsum16(float x) {
+  x += dpp_ror(x, 8);
+  x += dpp_ror(x, 4);
+  x += dpp_ror(x, 2);
+  x += dpp_ror(x, 1);
+  return x;
+}
+
 // Sum over aligned groups of 16 lanes.
 __device__ __forceinline__ float sum16(float x) {
   x += __shfl_xor(x, 1);

@@ -82,7 +82,9 @@ size_t kda_fwd_workspace_bytes(int B, int T, int H_qk, int H, int N);
 /*
  * Chunked forward pass over B independent rows of T tokens (the cuLA KDA
  * fixed-length table's B x T workload).  States are [B, H, V, K].
- * B * T == 0 is a successful no-op.
+ * B == 0 is a successful no-op.  T == 0 writes no output and sets
+ * final_state (if given) to initial_state, or to zero when initial_state is
+ * NULL.
  */
 kda_status kda_fwd(const void* q, const void* k, const void* v, const void* g_raw,
                    const float* beta_logits, const float* A_log, float scale,
@@ -100,7 +102,9 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const void* g_ra
  * copy).  Its contents are a precondition: they are only checked when the
  * environment variable KDA_DEBUG=1 is set, which synchronises the stream.
  * Zero-length sequences are allowed (their final state equals their initial
- * state).  N == 0 or T == 0 is a successful no-op (no state is written).
+ * state).  N == 0 is a successful no-op.  T == 0 (all sequences empty)
+ * writes no output and sets each final state to its initial state, or to
+ * zero when initial_state is NULL.
  */
 kda_status kda_fwd_varlen(const void* q, const void* k, const void* v, const void* g_raw,
                           const float* beta_logits, const float* A_log, float scale,

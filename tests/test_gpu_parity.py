@@ -132,6 +132,20 @@ def test_zero_tokens_copy_state():
     np.testing.assert_array_equal(fin, inp["initial_state"].astype(np.float64))
 
 
+def test_zero_tokens_without_state_gives_zero_state():
+    inp = make_inputs(2, 0, 2, 2, seed=22)
+    out, fin = U.run_gpu(inp)
+    assert out.shape[1] == 0 and fin.shape == (2, 2, 128, 128)
+    assert not np.any(fin)
+
+
+def test_packed_all_sequences_empty():
+    inp = make_inputs(1, 0, 2, 1, N=3, lengths=[0, 0, 0], state_std=0.05, seed=23)
+    out, fin = U.run_gpu(inp)
+    assert out.shape[1] == 0
+    np.testing.assert_array_equal(fin, inp["initial_state"].astype(np.float64))
+
+
 def test_run_to_run_bitwise_determinism():
     inp = make_inputs(2, 333, 4, 2, state_std=0.02, seed=21)
     o1, f1 = U.run_gpu(inp)
