@@ -82,8 +82,9 @@ __device__ __forceinline__ void load_frags(Frags& F, const uint8_t* R, int wave,
 #pragma unroll
   for (int i = 0; i < 2; ++i)
     F.gl[i] = *reinterpret_cast<const float4*>(R + REC_GL + 4 * (SUB * (2 * wave + i) + 4 * lg));
-  const int r = tid >> 2;
-  F.v = (r < L) ? *reinterpret_cast<const uint2*>(vsrc + (size_t)r * vstride) : make_uint2(0u, 0u);
+  // rows past the chunk's end are clamped here (L >= 1) and zeroed at use, so
+  // the load is unconditional
+  F.v = *reinterpret_cast<const uint2*>(vsrc + (size_t)min(tid >> 2, L - 1) * vstride);
 }
 
 }  // namespace
@@ -117,19 +118,15 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
 
   const size_t vstride = (size_t)p.H * HD;
   const int vcol = v0 + 4 * (tid & 3);
-  Frags cur, nxt;
-  if (nch > 0) {
-    const uint8_t* R = p.rec + ((size_t)chunk0 * p.H + h) * REC_BYTES;
-    load_frags(cur, R, wave, lane, tid, p.v + ((size_t)tok0 * p.H + h) * HD + vcol, min(CH, len), vstride);
-  }
-  for (int c = 0; c < nch; ++c) {
+  const uint16_t* vchain = p.v + ((size_t)tok0 * p.H + h) * HD + vcol;
+  auto load_chunk = [&](Frags& F, int c) {
+    const uint8_t* R = p.rec + ((size_t)(chunk0 + c) * p.H + h) * REC_BYTES;
+    load_frags(F, R, wave, lane, tid, vchain + (size_t)c * CH * vstride, min(CH, len - c * CH), vstride);
+  };
+
+  // one chunk of the recurrence on fragments F
+  auto step = [&](const Frags& F, int c) {
     const int L = min(CH, len - c * CH);
-    if (c + 1 < nch) {
-      const uint8_t* R = p.rec + ((size_t)(chunk0 + c + 1) * p.H + h) * REC_BYTES;
-      const int Ln = min(CH, len - (c + 1) * CH);
-      load_frags(nxt, R, wave, lane, tid, p.v + ((size_t)(tok0 + (c + 1) * CH) * p.H + h) * HD + vcol, Ln,
-                 vstride);
-    }
     // 1. publish this wave's fp16 slice of S and the value tile
     {
       f16x8 sb;
@@ -140,10 +137,11 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
       }
       sbuf[wave * 64 + lane] = sb;
       const int r = tid >> 2, c4 = 4 * (tid & 3);
-      vsT[(c4 + 0) * VS + r] = (f16)__uint_as_float(cur.v.x << 16);
-      vsT[(c4 + 1) * VS + r] = (f16)__uint_as_float(cur.v.x & 0xFFFF0000u);
-      vsT[(c4 + 2) * VS + r] = (f16)__uint_as_float(cur.v.y << 16);
-      vsT[(c4 + 3) * VS + r] = (f16)__uint_as_float(cur.v.y & 0xFFFF0000u);
+      const uint2 vv = r < L ? F.v : make_uint2(0u, 0u);
+      vsT[(c4 + 0) * VS + r] = (f16)__uint_as_float(vv.x << 16);
+      vsT[(c4 + 1) * VS + r] = (f16)__uint_as_float(vv.x & 0xFFFF0000u);
+      vsT[(c4 + 2) * VS + r] = (f16)__uint_as_float(vv.y << 16);
+      vsT[(c4 + 3) * VS + r] = (f16)__uint_as_float(vv.y & 0xFFFF0000u);
     }
     __syncthreads();
     // 2. U = T diag(b) V - W S ;  OQ = Qhat S      (token tile `wave`)
@@ -157,13 +155,13 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
         const f16x4 lo = *reinterpret_cast<const f16x4*>(&vsT[l16 * VS + 32 * s + 4 * lg]);
         const f16x4 hi = *reinterpret_cast<const f16x4*>(&vsT[l16 * VS + 32 * s + 16 + 4 * lg]);
         const f16x8 vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        U = mma_f16(cur.t[s], vb, U);
+        U = mma_f16(F.t[s], vb, U);
       }
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      U = mma_f16(cur.w[s], sB[s], U);
-      OQ = mma_f16(cur.q[s], sB[s], OQ);
+      U = mma_f16(F.w[s], sB[s], U);
+      OQ = mma_f16(F.q[s], sB[s], OQ);
     }
     // 3. publish U (fp16, C layout of token tile `wave`)
     {
@@ -179,8 +177,8 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
       uB[s] = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
     f32x4 O = OQ;
-    O = mma_f16(cur.m[0], uB[0], O);
-    if (wave >= 2) O = mma_f16(cur.m[1], uB[1], O);
+    O = mma_f16(F.m[0], uB[0], O);
+    if (wave >= 2) O = mma_f16(F.m[1], uB[1], O);
     {
       const size_t orow0 = (size_t)(tok0 + c * CH) * p.H + h;
 #pragma unroll
@@ -191,13 +189,27 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
     }
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
-      const float4 gl = cur.gl[i];
+      const float4 gl = F.gl[i];
       f32x4 acc = {gl.x * S[i][0], gl.y * S[i][1], gl.z * S[i][2], gl.w * S[i][3]};
-      acc = mma_f16(cur.k[2 * i], uB[0], acc);
-      acc = mma_f16(cur.k[2 * i + 1], uB[1], acc);
+      acc = mma_f16(F.k[2 * i], uB[0], acc);
+      acc = mma_f16(F.k[2 * i + 1], uB[1], acc);
       S[i] = acc;
     }
-    if (c + 1 < nch) cur = nxt;
+  };
+
+  // ping-pong over two fragment sets: chunk c+1 loads while chunk c computes
+  Frags fa, fb;
+  if (nch > 0) load_chunk(fa, 0);
+  // Drain the first chunk's loads here, so the loop header carries no
+  // pending-load state on the fragments and the waits inside the loop only
+  // cover the older of the two fragment sets.
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int c = 0; c < nch; c += 2) {
+    if (c + 1 < nch) load_chunk(fb, c + 1);
+    step(fa, c);
+    if (c + 1 >= nch) break;
+    if (c + 2 < nch) load_chunk(fa, c + 2);
+    step(fb, c + 1);
   }
   if (p.s1) {
 #pragma unroll

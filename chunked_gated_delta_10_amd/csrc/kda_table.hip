@@ -16,7 +16,9 @@ constexpr int TB = 1024;
 constexpr int MAX_RANKED = 4096;
 
 __global__ __launch_bounds__(TB) void table_kernel(TableParams p) {
-  __shared__ int scan[TB];
+  __shared__ int scan[TB];   // inclusive scan of chunk counts within the current block of sequences
+  __shared__ int tok0s[TB];
+  __shared__ int lens_blk[TB];
   __shared__ int carry;
   __shared__ int lens[MAX_RANKED];
   const int tid = threadIdx.x;
@@ -37,6 +39,8 @@ __global__ __launch_bounds__(TB) void table_kernel(TableParams p) {
     }
     const int nch = (len + CH - 1) / CH;
     scan[tid] = nch;
+    tok0s[tid] = tok0;
+    lens_blk[tid] = len;
     __syncthreads();
     for (int off = 1; off < TB; off <<= 1) {
       const int y = tid >= off ? scan[tid - off] : 0;
@@ -44,17 +48,28 @@ __global__ __launch_bounds__(TB) void table_kernel(TableParams p) {
       scan[tid] += y;
       __syncthreads();
     }
-    const int first = carry + scan[tid] - nch;
+    const int c0 = carry;
     if (n < p.N) {
-      p.seqs[n] = make_int4(tok0, len, first, 0);
+      p.seqs[n] = make_int4(tok0, len, c0 + scan[tid] - nch, 0);
       if (n < MAX_RANKED) lens[n] = len;
-      for (int c = 0; c < nch; ++c) {
-        const int e = first + c;
-        if (e < p.n_entries) p.chunks[e] = make_int4(n, tok0 + c * CH, min(CH, len - c * CH), c);
+    }
+    // chunk entries of this block, written cooperatively: entry j belongs to
+    // the first sequence i of the block whose inclusive scan exceeds j
+    const int blk_total = scan[TB - 1];
+    for (int j = tid; j < blk_total; j += TB) {
+      int lo = 0, hi = TB - 1;
+      while (lo < hi) {
+        const int mid = (lo + hi) >> 1;
+        if (scan[mid] > j) hi = mid;
+        else lo = mid + 1;
       }
+      const int c = j - (scan[lo] - (lens_blk[lo] + CH - 1) / CH);
+      const int e = c0 + j;
+      if (e < p.n_entries)
+        p.chunks[e] = make_int4(base + lo, tok0s[lo] + c * CH, min(CH, lens_blk[lo] - c * CH), c);
     }
     __syncthreads();
-    if (tid == TB - 1) carry += scan[TB - 1];
+    if (tid == 0) carry = c0 + blk_total;
     __syncthreads();
   }
   for (int e = carry + tid; e < p.n_entries; e += TB) p.chunks[e] = make_int4(0, 0, 0, 0);
