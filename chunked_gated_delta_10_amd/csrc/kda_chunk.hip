@@ -21,18 +21,26 @@
 // For r in sub-chunk b and i in sub-chunk a < b:
 //   exp(Gamma_r - Gamma_i) = rho_r * (prod_{a<m<b} D_m) * kappa_i, every factor <= 1,
 // so those blocks use fp16 operands without overflow.  Diagonal blocks use
-//   exp(Gamma_r - Gamma_i) = (rho_r / D_b) * kappa_i
-// whose first factor can reach 1/D_b; they run with split-bf16 operands
-// (three bf16 products, ~16 significant bits) while D_b >= 2^-100, and fall
+//   exp(Gamma_r - Gamma_i) = (kn_r / kappa_r) . (kn_i kappa_i)
+// whose first factor can reach 1/D_b.
+// The per-token log2-decays are scanned along the sub-chunk (prefix and
+// suffix sums) and every factor is one exp2 of a scan value.  Diagonal blocks
+// run on fp32 matrix cores (exact fp32 products) while D_b >= 2^-100 and fall
 // back to an exact per-channel evaluation in the log domain otherwise.
 // In scalar-gate mode exp(Gamma_r - Gamma_i) is one number per (r, i) and is
 // applied after the Gram products.
 //
-// Work layout: 512 threads (8 waves, two per SIMD so one wave's LDS and
-// transcendental latency hides behind the other's work).  The kernel is
-// persistent: each workgroup walks (chunk, head) jobs with a stride of the
-// grid size and prefetches the next job's q, k, gate and beta into
-// registers while it computes the current one.
+// Work layout: 4 waves, wave n owns sub-chunk n.  Lane (l16, g) of wave n
+// holds token 16n + l16 and the 32 key channels
+//   32s + 4g + e (e < 4),  32s + 16 + 4g + (e - 4) (e >= 4),   s = 0..3,
+// i.e. exactly the A-operand order of the record fragments, so the Gram
+// products, Qhat and the decay scans (DPP shifts along the 16 token lanes of
+// a row) all run on registers loaded straight from memory.  Transposed
+// (key-major) operands Khat^T and Kbar^T come out of matrix-core products
+// with 0/1 selection matrices.  Only the fp16 Y operands, the sub-chunk decay
+// products and the 64 x 64 matrices A and T go through LDS (~69 KB), so two
+// workgroups share a CU and hide each other's latencies (one waits on its
+// loads while the other computes).  One workgroup per (chunk, head).
 #include "kda_device.h"
 #include "kda_kernels.h"
 
@@ -40,174 +48,134 @@ namespace kda {
 
 namespace {
 
-constexpr int NT = 512;  // threads per workgroup
-constexpr int LS = 132;  // row stride (floats) of the [64][128] operand arrays
-constexpr int MS = 68;   // row stride (floats) of the [64][64] matrices
+constexpr int NT = 256;  // threads per workgroup (4 waves)
+constexpr int MS = 68;   // row stride (floats) of the 64 x 64 matrices
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr float TINY_D = 0x1p-100f;  // smallest sub-chunk decay the fast diagonal path takes
+constexpr float TINY_LOG2 = -100.f;  // log2 of the smallest sub-chunk decay the fast diagonal path takes
 
 // LDS layout (bytes)
-constexpr int L_KR = 0;                          // kn*rho (kn in scalar mode), fp32 [64][LS]
-constexpr int L_QR = L_KR + CH * LS * 4;         // qn*rho (qn)
-constexpr int L_YS = L_QR + CH * LS * 4;         // raw gates, then kn*kappa (unused in scalar mode)
-constexpr int L_AM = L_YS + CH * LS * 4;         // A [64][MS]; after the inverse: Khat^T fragments
-constexpr int L_TM = L_AM + CH * MS * 4;         // T [64][MS]; before the inverse: fallback scratch
-constexpr int L_EP = L_TM + CH * MS * 4;         // exp(Gamma before sub-chunk n)[c]      [4][128]
-constexpr int L_EG = L_EP + NSUB * HD * 4;       // exp(Gamma_L - Gamma_end(n))[c]         [4][128]
-constexpr int L_LAM = L_EG + NSUB * HD * 4;      // pair factors for blocks (b, a <= b)    [10][128]
-constexpr int L_DS = L_LAM + 10 * HD * 4;        // D_n[c]                                 [4][128]
-constexpr int L_MX = L_DS + NSUB * HD * 4;       // M fragment halves handed between waves [2][64] f16x4
-constexpr int L_ROW = L_MX + 2 * 64 * 8;         // beta, exp(Gamma), exp(Gamma_L-Gamma), Gamma, 1/|k|, 1/|q|
-constexpr int L_FLAG = L_ROW + 6 * CH * 4;       // unsafe[4], any
+constexpr int L_YB = 0;                          // Y = kn*kappa (fp16) of sub-chunks 0..2 [3][4 slices][64] f16x8
+constexpr int L_KH = L_YB + 3 * 4 * 64 * 16;     // Khat^T fragments [8 key tiles][2 token slices][64] f16x8
+constexpr int L_AM = L_KH + 16 * 64 * 16;        // A [64][MS] fp32 (upper blocks: exact diagonal M scratch)
+constexpr int L_TM = L_AM + CH * MS * 4;         // T [64][MS] fp32 (upper blocks: exact diagonal A scratch)
+constexpr int L_AT = L_TM + CH * MS * 4;         // diagonal blocks of A, column-major [4][16][16]
+constexpr int L_DS = L_AT + NSUB * 256 * 4;      // D_n[key] [4][128]
+constexpr int L_ROW = L_DS + NSUB * HD * 4;      // per-token values, see R_*
+constexpr int L_FLAG = L_ROW + (5 * CH + 8) * 4;  // exact-fallback flags of the 4 sub-chunks
 constexpr int LDS_BYTES = L_FLAG + 8 * 4;
-static_assert(16 * 64 * 16 <= CH * MS * 4, "Khat^T fragments must fit in the A region");
-static_assert(3328 * 4 <= CH * MS * 4, "fallback scratch must fit in the T region");
-static_assert(LDS_BYTES <= 160 * 1024, "LDS budget");
+static_assert(3 * 16 * 64 * 4 <= 16 * 64 * 16, "fallback scratch must fit in the Khat^T region");
+static_assert(2 * LDS_BYTES <= 160 * 1024, "two workgroups per CU");
 
-// ROW sub-arrays
-constexpr int R_BETA = 0, R_EG = CH, R_EGL = 2 * CH, R_G = 3 * CH, R_RK = 4 * CH, R_RQ = 5 * CH;
+// ROW sub-arrays (floats)
+constexpr int R_BETA = 0, R_RK = CH, R_RQ = 2 * CH, R_GP = 3 * CH, R_GS = 5 * CH;
 
-__device__ __forceinline__ int pair_index(int b, int a) { return b * (b + 1) / 2 + a; }
+// Upper (never used) 16x16 blocks of A and T that hold the exact diagonal
+// blocks of sub-chunk b when the fallback runs.
+__device__ __forceinline__ int upper_block(int b) { return b < 3 ? b + 1 : 6; }  // (0,1) (0,2) (0,3) (1,2)
+__device__ __forceinline__ int upper_off(int b) {
+  const int rb = b < 3 ? 0 : 1, cb = b < 3 ? b + 1 : 2;
+  return (SUB * rb) * MS + SUB * cb;
+}
+
+// Sums along the 16 token lanes of a DPP row.  Lanes whose source lies
+// outside the row read 0 (bound_ctrl), so each step is one v_add_f32_dpp.
+template <int CTRL>
+__device__ __forceinline__ float dpp0(float x) {
+  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), CTRL, 0xF, 0xF, true));
+}
+// inclusive prefix sum over the lanes up to this one
+__device__ __forceinline__ float row_prefix_sum(float x) {
+  x += dpp0<0x111>(x);  // row_shr:1
+  x += dpp0<0x112>(x);
+  x += dpp0<0x114>(x);
+  x += dpp0<0x118>(x);
+  return x;
+}
+// sum over the lanes after this one (0 for the last lane of the row)
+__device__ __forceinline__ float row_suffix_sum_excl(float x) {
+  float y = dpp0<0x101>(x);  // row_shl:1
+  y += dpp0<0x101>(y);
+  y += dpp0<0x102>(y);
+  y += dpp0<0x104>(y);
+  y += dpp0<0x108>(y);
+  return y;
+}
+
+__device__ __forceinline__ void unpack4(uint2 w, float* out) {
+  out[0] = __uint_as_float(w.x << 16);
+  out[1] = __uint_as_float(w.x & 0xFFFF0000u);
+  out[2] = __uint_as_float(w.y << 16);
+  out[3] = __uint_as_float(w.y & 0xFFFF0000u);
+}
 
 __device__ __forceinline__ void store_frag(uint8_t* rec, int off, int frag, int lane, const float* v) {
   *reinterpret_cast<f16x8*>(rec + off + frag * FRAG_BYTES + lane * 16) = to_f16x8(v);
 }
 
-__device__ __forceinline__ void ld8(const float* p, float* x) {
-  *reinterpret_cast<float4*>(x) = *reinterpret_cast<const float4*>(p);
-  *reinterpret_cast<float4*>(x + 4) = *reinterpret_cast<const float4*>(p + 4);
-}
-__device__ __forceinline__ void ld4(const float* p, float* x) {
-  *reinterpret_cast<float4*>(x) = *reinterpret_cast<const float4*>(p);
-}
-
-// Registers prefetched for one job: row tid/8, channels 16*(tid%8) .. +15.
+// One job's inputs for this lane: token 16*wave + lane%16, key channels of
+// slice s: 32s + 4g .. +3 (half 0) and 32s + 16 + 4g .. +3 (half 1).
 struct Pref {
-  uint4 q[2], k[2], g[2];  // bf16; g only in per-channel mode
-  uint32_t gs;             // scalar gate of row tid%64, bf16 in the low half
-  float beta;              // logit of row tid/8
+  uint2 q[8], k[8], g[8];  // [2s + half], bf16; g only in per-channel mode
+  uint32_t gs;             // scalar gate of the token, bf16 in the low half
+  float beta;              // logit of the token
 };
 
 template <bool PER_CHANNEL>
-__device__ __forceinline__ void prefetch(Pref& P, const ChunkParams& p, int4 ce, int h, int tid) {
+__device__ __forceinline__ void load_rows(Pref& P, const ChunkParams& p, int4 ce, int h, int wave, int lane) {
   // Loads are unconditional (rows past the chunk end are clamped to its last
   // row and zeroed when used) so they issue back to back without waits.
   const int len = ce.z, tok0 = ce.y;
   if (len <= 0) return;
   const int hq = h / (p.H / p.H_qk);
-  const int last = len - 1;
-  const int r = min(tid >> 3, last), c0 = (tid & 7) * 16;
-  const size_t base = ((size_t)(tok0 + r) * p.H_qk + hq) * HD + c0;
-  const uint4* qp = reinterpret_cast<const uint4*>(p.q + base);
-  const uint4* kp = reinterpret_cast<const uint4*>(p.k + base);
-  P.q[0] = qp[0];
-  P.q[1] = qp[1];
-  P.k[0] = kp[0];
-  P.k[1] = kp[1];
-  P.beta = p.beta[(size_t)(tok0 + r) * p.H + h];
+  const int r = min(SUB * wave + (lane & 15), len - 1), g4 = 4 * (lane >> 4);
+  const size_t t = (size_t)(tok0 + r);
+  const uint16_t* qp = p.q + (t * p.H_qk + hq) * HD + g4;
+  const uint16_t* kp = p.k + (t * p.H_qk + hq) * HD + g4;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    const int off = 32 * (i >> 1) + 16 * (i & 1);
+    P.q[i] = *reinterpret_cast<const uint2*>(qp + off);
+    P.k[i] = *reinterpret_cast<const uint2*>(kp + off);
+  }
+  P.beta = p.beta[t * p.H + h];
   if (PER_CHANNEL) {
-    const uint4* gp = reinterpret_cast<const uint4*>(p.g_raw + ((size_t)(tok0 + r) * p.H + h) * HD + c0);
-    P.g[0] = gp[0];
-    P.g[1] = gp[1];
+    const uint16_t* gp = p.g_raw + (t * p.H + h) * HD + g4;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) P.g[i] = *reinterpret_cast<const uint2*>(gp + 32 * (i >> 1) + 16 * (i & 1));
   } else {
-    P.gs = p.g_raw[(size_t)(tok0 + min(tid & 63, last)) * p.H + h];
-  }
-}
-
-// One A block (b, a) (fp32, to LDS) and its M^T block (returned in C layout:
-// lane holds M[16b + l16][16a + 4lg + j]).  K = 128 key channels, 4 slices.
-template <bool PER_CHANNEL>
-__device__ __forceinline__ void ablock(int b, int a, const float* KR, const float* QR, const float* YSrc,
-                                       const float* LAM, const float* ROW, float* AM, int l16, int lg,
-                                       f32x4& accM) {
-  const int r = SUB * b + l16, i = SUB * a + l16;
-  const bool diag = (a == b);
-  f32x4 accA = zero4();
-  accM = zero4();
-#pragma unroll 1
-  for (int s = 0; s < 4; ++s) {
-    const int c0 = 32 * s + 8 * lg;
-    float xk[8], xq[8], y[8];
-    ld8(&KR[r * LS + c0], xk);
-    ld8(&QR[r * LS + c0], xq);
-    ld8(&YSrc[i * LS + c0], y);
-    if (PER_CHANNEL) {
-      float lam[8];
-      ld8(&LAM[pair_index(b, a) * HD + c0], lam);
-#pragma unroll
-      for (int q = 0; q < 8; ++q) {
-        xk[q] *= lam[q];
-        xq[q] *= lam[q];
-      }
-    }
-    if (PER_CHANNEL && diag) {
-      bf16x8 xkh, xkl, xqh, xql, yh, yl;
-      split_bf16x8(xk, xkh, xkl);
-      split_bf16x8(xq, xqh, xql);
-      split_bf16x8(y, yh, yl);
-      accA = mma_bf16(xkh, yh, accA);
-      accA = mma_bf16(xkh, yl, accA);
-      accA = mma_bf16(xkl, yh, accA);
-      accM = mma_bf16(yh, xqh, accM);
-      accM = mma_bf16(yl, xqh, accM);
-      accM = mma_bf16(yh, xql, accM);
-    } else {
-      const f16x8 yf = to_f16x8(y);
-      accA = mma_f16(to_f16x8(xk), yf, accA);
-      accM = mma_f16(yf, to_f16x8(xq), accM);
-    }
-  }
-  // A block: lane holds A[16b + 4lg + j][16a + l16]
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rr = SUB * b + 4 * lg + j, ii = SUB * a + l16;
-    float v = 0.f;
-    if (ii < rr) {
-      v = accA[j];
-      if (!PER_CHANNEL) v *= exp2f((ROW[R_G + rr] - ROW[R_G + ii]) * LOG2E);
-      v *= ROW[R_BETA + rr];
-    }
-    AM[rr * MS + ii] = v;
-  }
-#pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const int rr = SUB * b + l16, ii = SUB * a + 4 * lg + j;
-    float v = 0.f;
-    if (ii <= rr) {
-      v = accM[j];
-      if (!PER_CHANNEL) v *= exp2f((ROW[R_G + rr] - ROW[R_G + ii]) * LOG2E);
-    }
-    accM[j] = v;
+    P.gs = p.g_raw[t * p.H + h];
   }
 }
 
 }  // namespace
 
 template <bool PER_CHANNEL>
-__global__ __launch_bounds__(NT) void chunk_local_kernel(const ChunkParams p, const int n_jobs) {
+__global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p, const int n_jobs) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  float* KR = reinterpret_cast<float*>(smem + L_KR);
-  float* QR = reinterpret_cast<float*>(smem + L_QR);
-  float* YS = reinterpret_cast<float*>(smem + L_YS);
+  f16x8* YB = reinterpret_cast<f16x8*>(smem + L_YB);
+  uint8_t* KHb = smem + L_KH;
+  const f16x8* KH = reinterpret_cast<const f16x8*>(smem + L_KH);
   float* AM = reinterpret_cast<float*>(smem + L_AM);
-  f16x8* KH = reinterpret_cast<f16x8*>(smem + L_AM);
   float* TM = reinterpret_cast<float*>(smem + L_TM);
-  float* EP = reinterpret_cast<float*>(smem + L_EP);
-  float* EG = reinterpret_cast<float*>(smem + L_EG);
-  float* LAM = reinterpret_cast<float*>(smem + L_LAM);
+  float* AT = reinterpret_cast<float*>(smem + L_AT);
   float* DS = reinterpret_cast<float*>(smem + L_DS);
-  f16x4* MX = reinterpret_cast<f16x4*>(smem + L_MX);
   float* ROW = reinterpret_cast<float*>(smem + L_ROW);
   int* FLAG = reinterpret_cast<int*>(smem + L_FLAG);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
   const int l16 = lane & 15, lg = lane >> 4;
-  const float* YSrc = PER_CHANNEL ? YS : KR;
+  const int n = wave;              // sub-chunk of this wave
+  const int r = SUB * n + l16;     // this lane's token row in the chunk
+
+  // 0/1 selection operands: sel[h] picks key 32s + 16h + l16 out of slice s
+  f16x8 sel[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[hh][e] = ((e >> 2) == hh && (e & 3) == l16 - 4 * lg) ? (f16)1.f : (f16)0.f;
 
   // Job indices are wave-uniform; the schedule and A_log are read through
-  // the constant address space so these loads go to the scalar unit and
-  // waiting for them never waits on the vector-memory counter that the
-  // prefetch and the record stores share.
+  // the constant address space so these loads go to the scalar unit.
   const int H = p.H;
   typedef __attribute__((address_space(4))) const int cint;
   typedef __attribute__((address_space(4))) const float cfloat;
@@ -216,197 +184,153 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(const ChunkParams p, co
   auto entry = [&](int i) {
     return make_int4(chunks[4 * i], chunks[4 * i + 1], chunks[4 * i + 2], chunks[4 * i + 3]);
   };
-  int job = __builtin_amdgcn_readfirstlane(blockIdx.x);
-  if (job >= n_jobs) return;
-  int4 ce = entry(__builtin_amdgcn_readfirstlane(job / H));
-  float alog = A_log[__builtin_amdgcn_readfirstlane(job % H)];
-  Pref nxt;
-  prefetch<PER_CHANNEL>(nxt, p, ce, job % H, tid);
-
-  for (;;) {
-    const Pref cur = nxt;
-    const int4 ce_cur = ce;
-    const float alog_cur = alog;
+  {
+    const int job = blockIdx.x;
     const int e = __builtin_amdgcn_readfirstlane(job / H), h = __builtin_amdgcn_readfirstlane(job % H);
-    const int nj = __builtin_amdgcn_readfirstlane(job + (int)gridDim.x);
-    if (nj < n_jobs) {
-      ce = entry(__builtin_amdgcn_readfirstlane(nj / H));
-      alog = A_log[__builtin_amdgcn_readfirstlane(nj % H)];
-      prefetch<PER_CHANNEL>(nxt, p, ce, nj % H, tid);
-    }
+    const int4 ce_cur = entry(e);
     const int len = ce_cur.z;
     if (len > 0) {  // uniform over the workgroup
+      Pref cur;
+      load_rows<PER_CHANNEL>(cur, p, ce_cur, h, wave, lane);
+      const float alog_cur = A_log[h];
       uint8_t* rec = p.rec + ((size_t)e * p.H + h) * REC_BYTES;
-      if (tid < 8) FLAG[tid] = 0;
-
-      // ---- A: L2-normalise q, k rows; beta; stage raw gates -----------------
-      {
-        const int r = tid >> 3, c0 = (tid & 7) * 16;
-        const bool live = r < len;
-        float qv[16], kv[16];
-        unpack_bf16x8(cur.q[0], qv);
-        unpack_bf16x8(cur.q[1], qv + 8);
-        unpack_bf16x8(cur.k[0], kv);
-        unpack_bf16x8(cur.k[1], kv + 8);
-        float sq = 0.f, sk = 0.f;
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-          qv[i] = live ? qv[i] : 0.f;
-          kv[i] = live ? kv[i] : 0.f;
-          sq += qv[i] * qv[i];
-          sk += kv[i] * kv[i];
-        }
-        sq += __shfl_xor(sq, 1);
-        sk += __shfl_xor(sk, 1);
-        sq += __shfl_xor(sq, 2);
-        sk += __shfl_xor(sk, 2);
-        sq += __shfl_xor(sq, 4);
-        sk += __shfl_xor(sk, 4);
-        const float rq = 1.f / sqrtf(sq + 1e-6f), rk = 1.f / sqrtf(sk + 1e-6f);
-#pragma unroll
-        for (int i = 0; i < 16; i += 4) {
-          *reinterpret_cast<float4*>(&QR[r * LS + c0 + i]) =
-              make_float4(qv[i] * rq, qv[i + 1] * rq, qv[i + 2] * rq, qv[i + 3] * rq);
-          *reinterpret_cast<float4*>(&KR[r * LS + c0 + i]) =
-              make_float4(kv[i] * rk, kv[i + 1] * rk, kv[i + 2] * rk, kv[i + 3] * rk);
-        }
-        if (PER_CHANNEL) {
-          float gv[16];
-          unpack_bf16x8(cur.g[0], gv);
-          unpack_bf16x8(cur.g[1], gv + 8);
-#pragma unroll
-          for (int i = 0; i < 16; i += 4)
-            *reinterpret_cast<float4*>(&YS[r * LS + c0 + i]) = make_float4(gv[i], gv[i + 1], gv[i + 2], gv[i + 3]);
-        }
-        if ((tid & 7) == 0) {
-          ROW[R_BETA + r] = live ? sigmoidf_(cur.beta) : 0.f;
-          ROW[R_RK + r] = rk;
-          ROW[R_RQ + r] = rq;
-        }
-      }
-      __syncthreads();
-
-      // ---- B: gates -> decay factors ----------------------------------------
+      const bool live = r < len;
       const float a_h = __expf(alog_cur);
-      if (PER_CHANNEL) {
-        // thread (key channel c, sub-chunk n)
-        const int c = tid & 127, n = tid >> 7;
-        float d[SUB];
-#pragma unroll
-        for (int i = 0; i < SUB; ++i) {
-          const int r = n * SUB + i;
-          float dd, g;
-          gate_decay(YS[r * LS + c], a_h, dd, g);
-          d[i] = (r < len) ? dd : 1.f;
-        }
-        float kap = 1.f;
-#pragma unroll
-        for (int i = SUB - 1; i >= 0; --i) {
-          const int r = n * SUB + i;
-          YS[r * LS + c] = KR[r * LS + c] * kap;
-          kap *= d[i];
-        }
-        float rho = 1.f;
-#pragma unroll
-        for (int i = 0; i < SUB; ++i) {
-          const int r = n * SUB + i;
-          rho *= d[i];
-          KR[r * LS + c] *= rho;
-          QR[r * LS + c] *= rho;
-        }
-        DS[n * HD + c] = rho;
-        if (!(rho >= TINY_D)) {
-          FLAG[n] = 1;
-          FLAG[4] = 1;
-        }
-      } else if (wave == 0) {
-        float d = 1.f, g = 0.f;
-        if (lane < len) gate_decay(bf16_to_f32((uint16_t)cur.gs), a_h, d, g);
-        float G = g;  // inclusive prefix sum over the 64 tokens
-#pragma unroll
-        for (int off = 1; off < 64; off <<= 1) {
-          const float y = __shfl_up(G, off);
-          if (lane >= off) G += y;
-        }
-        const float GL = __shfl(G, 63);
-        ROW[R_EG + lane] = exp2f(G * LOG2E);
-        ROW[R_EGL + lane] = exp2f((GL - G) * LOG2E);
-        ROW[R_G + lane] = G;
-      }
-      __syncthreads();
 
-      // ---- B2: per-channel factor vectors; exp(Gamma_L) ----------------------
+      // ---- 1. normalise; gates -> decay scans; diagonal block ---------------
+      float sq = 0.f, sk = 0.f;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        float x[4], y[4];
+        unpack4(cur.q[i], x);
+        unpack4(cur.k[i], y);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sq += x[j] * x[j];
+          sk += y[j] * y[j];
+        }
+      }
+      sq += __shfl_xor(sq, 16);
+      sk += __shfl_xor(sk, 16);
+      sq += __shfl_xor(sq, 32);
+      sk += __shfl_xor(sk, 32);
+      const float rq = live ? 1.f / sqrtf(sq + 1e-6f) : 0.f;
+      const float rk = live ? 1.f / sqrtf(sk + 1e-6f) : 0.f;
+      const float beta = live ? sigmoidf_(cur.beta) : 0.f;
+      if (lg == 0) {
+        ROW[R_BETA + r] = beta;
+        ROW[R_RK + r] = rk;
+        ROW[R_RQ + r] = rq;
+      }
+
+      float X[32], Q[32], Y[32];  // kn*rho, qn*rho, kn*kappa (scalar mode: kn, qn, -)
+      f32x4 accA_d = zero4(), accM_d = zero4();
+      float Gloc = 0.f;           // scalar mode: gate prefix within the sub-chunk
       if (PER_CHANNEL) {
-        if (tid < HD) {
-          const int c = tid;
-          const float Dn[4] = {DS[c], DS[HD + c], DS[2 * HD + c], DS[3 * HD + c]};
-          EP[c] = 1.f;
-          EP[HD + c] = Dn[0];
-          EP[2 * HD + c] = Dn[0] * Dn[1];
-          EP[3 * HD + c] = Dn[0] * Dn[1] * Dn[2];
-          EG[c] = Dn[1] * Dn[2] * Dn[3];
-          EG[HD + c] = Dn[2] * Dn[3];
-          EG[2 * HD + c] = Dn[3];
-          EG[3 * HD + c] = 1.f;
+        bool tiny = false;
+        f32x4 accA2 = zero4(), accM2 = zero4();
 #pragma unroll
-          for (int b = 0; b < NSUB; ++b) {
+        for (int s = 0; s < 4; ++s) {
+          float kn[8], qn[8], gx[8];
+          unpack4(cur.k[2 * s], kn);
+          unpack4(cur.k[2 * s + 1], kn + 4);
+          unpack4(cur.q[2 * s], qn);
+          unpack4(cur.q[2 * s + 1], qn + 4);
+          unpack4(cur.g[2 * s], gx);
+          unpack4(cur.g[2 * s + 1], gx + 4);
+          float P[8], S[8];
 #pragma unroll
-            for (int a = 0; a <= b; ++a) {
-              float f = 1.f;
-              if (a == b) f = Dn[b] >= TINY_D ? 1.f / Dn[b] : 0.f;
-              else {
+          for (int q = 0; q < 8; ++q) {
+            kn[q] *= rk;
+            qn[q] *= rq;
+            const float l2d = gate_log2(gx[q], a_h);  // log2 of the token's decay
+            P[q] = live ? l2d : 0.f;
+          }
 #pragma unroll
-                for (int m = a + 1; m < b; ++m) f *= Dn[m];
-              }
-              LAM[pair_index(b, a) * HD + c] = f;
+          for (int q = 0; q < 8; ++q) {
+            S[q] = row_suffix_sum_excl(P[q]);  // log2 kappa
+            P[q] = row_prefix_sum(P[q]);       // log2 rho
+          }
+          float Dv[8];
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            const float rho = __builtin_amdgcn_exp2f(P[q]);
+            const float kap = __builtin_amdgcn_exp2f(S[q]);
+            const float ikap = __builtin_amdgcn_exp2f(-S[q]);
+            const int v = 8 * s + q;
+            X[v] = kn[q] * rho;
+            Q[v] = qn[q] * rho;
+            Y[v] = kn[q] * kap;
+            Dv[q] = rho * kap;
+            tiny |= !(P[q] + S[q] >= TINY_LOG2);
+            // diagonal block on fp32 matrix cores: the lane's value is the
+            // A/B operand of the 16x16x4 product for key (s, q)
+            if (q & 1) {
+              accA2 = mma_f32(kn[q] * ikap, Y[v], accA2);
+              accM2 = mma_f32(Y[v], qn[q] * ikap, accM2);
+            } else {
+              accA_d = mma_f32(kn[q] * ikap, Y[v], accA_d);
+              accM_d = mma_f32(Y[v], qn[q] * ikap, accM_d);
             }
           }
-          *reinterpret_cast<float*>(rec + REC_GL + 4 * c) = Dn[0] * Dn[1] * Dn[2] * Dn[3];
+          if (l16 == 0) {  // D_n of this lane group's 8 keys
+            *reinterpret_cast<float4*>(&DS[n * HD + 32 * s + 4 * lg]) = make_float4(Dv[0], Dv[1], Dv[2], Dv[3]);
+            *reinterpret_cast<float4*>(&DS[n * HD + 32 * s + 16 + 4 * lg]) = make_float4(Dv[4], Dv[5], Dv[6], Dv[7]);
+          }
+          if (n < 3) {
+            f16x8 yh;
+#pragma unroll
+            for (int q = 0; q < 8; ++q) yh[q] = (f16)Y[8 * s + q];
+            YB[(n * 4 + s) * 64 + lane] = yh;
+          }
         }
-        __syncthreads();
-      } else if (tid < HD) {
-        *reinterpret_cast<float*>(rec + REC_GL + 4 * tid) = ROW[R_EG + CH - 1];
-      }
-
-      // ---- D: A and M blocks on the matrix cores -----------------------------
-      // Waves 0..3 take the diagonal blocks (b, b) (split-bf16, the costliest);
-      // waves 4..7 the off-diagonal ones.  M fragment (t, s) covers blocks
-      // (t, 2s) and (t, 2s+1); halves computed by different waves meet in MX.
-      //   w0 (0,0) -> M(0,0)        w4 (1,0) + half from w1 -> M(1,0)
-      //   w1 (1,1) -> MX[0]         w5 (3,2) + half from w3 -> M(3,1)
-      //   w2 (2,2) -> M(2,1)        w6 (2,0),(2,1) -> M(2,0)
-      //   w3 (3,3) -> MX[1]         w7 (3,0),(3,1) -> M(3,0)
-      f32x4 m0 = zero4(), m1 = zero4();
-      if (wave < 4) {
-        ablock<PER_CHANNEL>(wave, wave, KR, QR, YSrc, LAM, ROW, AM, l16, lg, m0);
-      } else if (wave == 4) {
-        ablock<PER_CHANNEL>(1, 0, KR, QR, YSrc, LAM, ROW, AM, l16, lg, m0);
-      } else if (wave == 5) {
-        ablock<PER_CHANNEL>(3, 2, KR, QR, YSrc, LAM, ROW, AM, l16, lg, m0);
-      } else if (wave == 6) {
-        ablock<PER_CHANNEL>(2, 0, KR, QR, YSrc, LAM, ROW, AM, l16, lg, m0);
-        ablock<PER_CHANNEL>(2, 1, KR, QR, YSrc, LAM, ROW, AM, l16, lg, m1);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          accA_d[j] += accA2[j];
+          accM_d[j] += accM2[j];
+        }
+        const bool any_tiny = __ballot(tiny && l16 == 0) != 0;
+        if (lane == 0) FLAG[n] = any_tiny ? 1 : 0;
       } else {
-        ablock<PER_CHANNEL>(3, 0, KR, QR, YSrc, LAM, ROW, AM, l16, lg, m0);
-        ablock<PER_CHANNEL>(3, 1, KR, QR, YSrc, LAM, ROW, AM, l16, lg, m1);
+        float g = 0.f;
+        if (live) {
+          float d;
+          gate_decay(bf16_to_f32((uint16_t)cur.gs), a_h, d, g);
+        }
+        Gloc = row_prefix_sum(g);
+        if (lg == 0) ROW[R_GP + r] = Gloc;
+        if (lane == 15) ROW[R_GS + n] = Gloc;
+#pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          float kn[8], qn[8];
+          unpack4(cur.k[2 * s], kn);
+          unpack4(cur.k[2 * s + 1], kn + 4);
+          unpack4(cur.q[2 * s], qn);
+          unpack4(cur.q[2 * s + 1], qn + 4);
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            X[8 * s + q] = kn[q] * rk;
+            Q[8 * s + q] = qn[q] * rq;
+          }
+          if (n < 3) YB[(n * 4 + s) * 64 + lane] = to_f16x8(&X[8 * s]);
+        }
       }
+      __syncthreads();  // Y operands, D_n, per-token values and flags visible
 
-      // ---- D': exact diagonal blocks when a sub-chunk's decay span is huge ---
-      // Rare (a channel decays by more than 2^-100 within 16 tokens).  Runs
-      // before anything consumes A or M: the unsafe diagonal blocks of A are
-      // overwritten and the affected M values replaced in m0 of waves 0..3.
-      // Scratch lives in the (not yet used) T region: normalised k, q rows of
-      // the sub-chunk and the running log-decay for 64 key channels at a time.
-      if (PER_CHANNEL && FLAG[4]) {
+      // ---- 1'. exact diagonal blocks when a sub-chunk's decay span is huge -----
+      // Rare (a channel decays by more than 2^-100 within 16 tokens).  Results
+      // go to upper (unused) blocks of T (A values) and A (M values); scratch
+      // lives in the Khat^T region, which is written only afterwards.
+      const bool flagged = PER_CHANNEL && FLAG[n];
+      if (PER_CHANNEL && (FLAG[0] | FLAG[1] | FLAG[2] | FLAG[3])) {
         const int hq = h / (p.H / p.H_qk);
-        float* SK = TM;         // [16][64]
-        float* SQ = TM + 1024;  // [16][64]
-        float* SG = TM + 2048;  // [16][64]
-        float* FM = TM + 3072;  // [16][16] M sums
+        float* SK = reinterpret_cast<float*>(KHb);  // [16][64]
+        float* SQ = SK + 1024;                      // [16][64]
+        float* SG = SK + 2048;                      // [16][64]
+        const int rr = tid >> 4, ii = tid & 15;
 #pragma unroll 1
         for (int b = 0; b < NSUB; ++b) {
           if (!FLAG[b]) continue;
-          const int rr = (tid >> 4) & 15, ii = tid & 15;
           float accA = 0.f, accM = 0.f;
 #pragma unroll 1
           for (int half = 0; half < 2; ++half) {
@@ -416,12 +340,12 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(const ChunkParams p, co
               float run = 0.f;
 #pragma unroll 1
               for (int i = 0; i < SUB; ++i) {
-                const int r = SUB * b + i;
+                const int rw = SUB * b + i;
                 float kk = 0.f, qq = 0.f, g = 0.f, dd;
-                if (r < len) {
-                  const size_t t = (size_t)(ce_cur.y + r);
-                  kk = bf16_to_f32(p.k[(t * p.H_qk + hq) * HD + c]) * ROW[R_RK + r];
-                  qq = bf16_to_f32(p.q[(t * p.H_qk + hq) * HD + c]) * ROW[R_RQ + r];
+                if (rw < len) {
+                  const size_t t = (size_t)(ce_cur.y + rw);
+                  kk = bf16_to_f32(p.k[(t * p.H_qk + hq) * HD + c]) * ROW[R_RK + rw];
+                  qq = bf16_to_f32(p.q[(t * p.H_qk + hq) * HD + c]) * ROW[R_RQ + rw];
                   gate_decay(bf16_to_f32(p.g_raw[(t * p.H + h) * HD + c]), a_h, dd, g);
                 }
                 run += g;
@@ -431,7 +355,7 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(const ChunkParams p, co
               }
             }
             __syncthreads();
-            if (tid < SUB * SUB && ii <= rr) {
+            if (ii <= rr) {
 #pragma unroll 4
               for (int c = 0; c < 64; ++c) {
                 const float dec = exp2f((SG[rr * 64 + c] - SG[ii * 64 + c]) * LOG2E);
@@ -440,208 +364,307 @@ __global__ __launch_bounds__(NT) void chunk_local_kernel(const ChunkParams p, co
               }
             }
           }
-          if (tid < SUB * SUB) {
-            AM[(SUB * b + rr) * MS + SUB * b + ii] = ii < rr ? accA * ROW[R_BETA + SUB * b + rr] : 0.f;
-            FM[rr * SUB + ii] = ii <= rr ? accM : 0.f;
-          }
-          __syncthreads();
-          if (wave == b) {
-#pragma unroll
-            for (int j = 0; j < 4; ++j) m0[j] = FM[l16 * SUB + 4 * lg + j];
-          }
+          TM[upper_off(b) + rr * MS + ii] = ii < rr ? accA * ROW[R_BETA + SUB * b + rr] : 0.f;
+          AM[upper_off(b) + rr * MS + ii] = ii <= rr ? accM : 0.f;
         }
-        __syncthreads();
+        __syncthreads();  // scratch free for Khat^T; exact blocks visible
       }
 
-      // hand over M halves computed by waves 1 and 3
-      if (wave == 1) MX[lane] = f16x4{(f16)m0[0], (f16)m0[1], (f16)m0[2], (f16)m0[3]};
-      if (wave == 3) MX[64 + lane] = f16x4{(f16)m0[0], (f16)m0[1], (f16)m0[2], (f16)m0[3]};
-      __syncthreads();  // A complete, M halves visible
-
-      // ---- E1 (waves 0..3): inverse of diagonal block w of I + A ---------------
-      // ---- G  (waves 4..7): M, Qhat and Kbar^T fragments -----------------------
-      if (wave < 4) {
-        if (wave == 0 || wave == 2) {  // complete M fragments (0,0) and (2,1)
-          float v[8];
+      // ---- 2. off-diagonal blocks; Qhat, Kbar^T (record) and Khat^T (LDS) -----
+      f32x4 accA[3], accM[3];
 #pragma unroll
-          for (int j = 0; j < 4; ++j) {
-            v[j] = m0[j];
-            v[4 + j] = 0.f;
-          }
-          store_frag(rec, REC_M, wave == 0 ? 0 : 5, lane, v);
+      for (int a = 0; a < 3; ++a) {
+        accA[a] = zero4();
+        accM[a] = zero4();
+      }
+      float Gr = 0.f, GL = 0.f;  // scalar mode: Gamma of this token, Gamma_L
+      if (!PER_CHANNEL) {
+        float below = 0.f;
+#pragma unroll
+        for (int m = 0; m < NSUB; ++m) {
+          const float gs = ROW[R_GS + m];
+          if (m < n) below += gs;
+          GL += gs;
         }
-        if (lane < SUB) {
-          const int b = wave, c = lane;
-          float x[SUB];
+        Gr = Gloc + below;
+      }
+      const float EGr = PER_CHANNEL ? 0.f : exp2f(Gr * LOG2E);
+      const float EGLr = PER_CHANNEL ? 0.f : exp2f((GL - Gr) * LOG2E);
 #pragma unroll
-          for (int i = 0; i < SUB; ++i) {
-            float acc = (i == c) ? 1.f : 0.f;
+      for (int s = 0; s < 4; ++s) {
+        float ep[8], eg[8], lam[8];
+        float Dm[4][8];
+        if (PER_CHANNEL) {
 #pragma unroll
-            for (int j = 0; j < i; ++j) acc -= AM[(SUB * b + i) * MS + SUB * b + j] * x[j];
-            x[i] = acc;
+          for (int m = 0; m < NSUB; ++m) {
+            const float4 lo = *reinterpret_cast<const float4*>(&DS[m * HD + 32 * s + 4 * lg]);
+            const float4 hi = *reinterpret_cast<const float4*>(&DS[m * HD + 32 * s + 16 + 4 * lg]);
+            Dm[m][0] = lo.x; Dm[m][1] = lo.y; Dm[m][2] = lo.z; Dm[m][3] = lo.w;
+            Dm[m][4] = hi.x; Dm[m][5] = hi.y; Dm[m][6] = hi.z; Dm[m][7] = hi.w;
           }
 #pragma unroll
-          for (int i = 0; i < SUB; ++i) TM[(SUB * b + i) * MS + SUB * b + c] = x[i];
+          for (int q = 0; q < 8; ++q) {
+            float a1 = 1.f, a2 = 1.f;
+#pragma unroll
+            for (int m = 0; m < NSUB; ++m) {
+              if (m < n) a1 *= Dm[m][q];
+              if (m > n) a2 *= Dm[m][q];
+            }
+            ep[q] = a1;
+            eg[q] = a2;
+            lam[q] = 1.f;
+          }
+        } else {
+#pragma unroll
+          for (int q = 0; q < 8; ++q) {
+            ep[q] = EGr;
+            eg[q] = EGLr;
+            lam[q] = 1.f;
+          }
         }
-      } else {
+        // Qhat fragment (n, s) straight from registers
         {
           float v[8];
-          if (wave == 4 || wave == 5) {  // (1,0) or (3,1): own half + handed half
-            const f16x4 hx = MX[(wave == 4 ? 0 : 64) + lane];
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              v[j] = m0[j];
-              v[4 + j] = (float)hx[j];
-            }
-            store_frag(rec, REC_M, wave == 4 ? 2 : 7, lane, v);
-          } else {  // (2,0) or (3,0): both halves computed here
+          for (int q = 0; q < 8; ++q) v[q] = Q[8 * s + q] * ep[q];
+          store_frag(rec, REC_QHAT, n * 4 + s, lane, v);
+        }
+        // Khat and Kbar of this sub-chunk, transposed by selection products
+        {
+          f16x8 kh, kb;
 #pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              v[j] = m0[j];
-              v[4 + j] = m1[j];
-            }
-            store_frag(rec, REC_M, wave == 6 ? 4 : 6, lane, v);
+          for (int q = 0; q < 8; ++q) {
+            kh[q] = (f16)(X[8 * s + q] * ep[q]);
+            kb[q] = (f16)((PER_CHANNEL ? Y[8 * s + q] : X[8 * s + q]) * eg[q]);
+          }
+#pragma unroll
+          for (int hh = 0; hh < 2; ++hh) {
+            const int kt = 2 * s + hh;  // key tile
+            const f32x4 th = mma_f16(kh, sel[hh], zero4());
+            const f32x4 tb = mma_f16(kb, sel[hh], zero4());
+            const f16x4 th4 = {(f16)th[0], (f16)th[1], (f16)th[2], (f16)th[3]};
+            const f16x4 tb4 = {(f16)tb[0], (f16)tb[1], (f16)tb[2], (f16)tb[3]};
+            *reinterpret_cast<f16x4*>(KHb + ((kt * 2 + (n >> 1)) * 64 + lane) * 16 + (n & 1) * 8) = th4;
+            *reinterpret_cast<f16x4*>(rec + REC_KBAR + (kt * 2 + (n >> 1)) * FRAG_BYTES + lane * 16 + (n & 1) * 8) = tb4;
           }
         }
-#pragma unroll 1
-        for (int job2 = wave - 4; job2 < 32; job2 += 4) {
-          float v[8];
-          if (job2 < 16) {  // Qhat (t, s): lane (row r, key channels perm(s, lg))
-            const int t = job2 >> 2, s = job2 & 3;
-            const int r = SUB * t + l16, n = t;
-            const int c0 = 32 * s + 4 * lg, c1 = c0 + 16;
-            ld4(&QR[r * LS + c0], v);
-            ld4(&QR[r * LS + c1], v + 4);
-            float f[8];
-            if (PER_CHANNEL) {
-              ld4(&EP[n * HD + c0], f);
-              ld4(&EP[n * HD + c1], f + 4);
-            } else {
+        // blocks (n, a), a < n: (X lam) Y_a^T and Y_a (Q lam)^T
 #pragma unroll
-              for (int q = 0; q < 8; ++q) f[q] = ROW[R_EG + r];
+        for (int a = 2; a >= 0; --a) {
+          if (a < n) {
+            if (PER_CHANNEL && a + 1 < n) {
+#pragma unroll
+              for (int q = 0; q < 8; ++q) lam[q] *= Dm[a + 1][q];
             }
+            f16x8 xl, ql;
 #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] *= f[q];
-            store_frag(rec, REC_QHAT, job2, lane, v);
-          } else {  // Kbar^T (kb, s): lane (key channel k, tokens perm(s, lg))
-            const int f = job2 - 16, kb = f >> 1, s = f & 1;
-            const int k = SUB * kb + l16;
-            const int j0 = 32 * s + 4 * lg, j1 = j0 + 16;
-            const float f0 = PER_CHANNEL ? EG[(j0 / SUB) * HD + k] : 0.f;
-            const float f1 = PER_CHANNEL ? EG[(j1 / SUB) * HD + k] : 0.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              v[q] = YSrc[(j0 + q) * LS + k] * (PER_CHANNEL ? f0 : ROW[R_EGL + j0 + q]);
-              v[4 + q] = YSrc[(j1 + q) * LS + k] * (PER_CHANNEL ? f1 : ROW[R_EGL + j1 + q]);
+            for (int q = 0; q < 8; ++q) {
+              xl[q] = (f16)(X[8 * s + q] * lam[q]);
+              ql[q] = (f16)(Q[8 * s + q] * lam[q]);
             }
-            store_frag(rec, REC_KBAR, f, lane, v);
+            const f16x8 ya = YB[(a * 4 + s) * 64 + lane];
+            accA[a] = mma_f16(xl, ya, accA[a]);
+            accM[a] = mma_f16(ya, ql, accM[a]);
           }
+        }
+        if (!PER_CHANNEL) {  // scalar mode: the diagonal block is an fp16 Gram block too
+          const f16x8 xh = to_f16x8(&X[8 * s]);
+          accA_d = mma_f16(xh, xh, accA_d);
+          accM_d = mma_f16(xh, to_f16x8(&Q[8 * s]), accM_d);
         }
       }
-      __syncthreads();
+      if (tid < HD) {  // exp(Gamma_L) per key
+        const float gl = PER_CHANNEL ? DS[tid] * DS[HD + tid] * DS[2 * HD + tid] * DS[3 * HD + tid]
+                                     : exp2f(GL * LOG2E);
+        *reinterpret_cast<float*>(rec + REC_GL + 4 * tid) = gl;
+      }
 
-      // ---- E2: off-diagonal blocks of T, level by level (fp32 matrix cores) --
+      // ---- 3. A rows of this sub-chunk -> LDS; M fragments -> record ----------
+      {
+        // scalar mode: Gamma_x from the per-token prefix within its sub-chunk
+        // plus the totals of the sub-chunks before it
+        float gbase[NSUB];
+        if (!PER_CHANNEL) {
+          float acc = 0.f;
+#pragma unroll
+          for (int m = 0; m < NSUB; ++m) {
+            gbase[m] = acc;
+            acc += ROW[R_GS + m];
+          }
+        }
+        auto gam = [&](int x) { return ROW[R_GP + x] + gbase[x >> 4]; };
+        float brow[4], grow[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rr = SUB * n + 4 * lg + j;
+          brow[j] = ROW[R_BETA + rr];
+          grow[j] = PER_CHANNEL ? 0.f : gam(rr);
+        }
+        // diagonal block: lane holds A[16n + 4lg + j][16n + l16]
+        float dv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rl = 4 * lg + j, il = l16;
+          float v = 0.f;
+          if (il < rl) {
+            if (flagged) v = TM[upper_off(n) + rl * MS + il];
+            else {
+              v = accA_d[j] * brow[j];
+              if (!PER_CHANNEL) v *= exp2f((grow[j] - gam(SUB * n + il)) * LOG2E);
+            }
+          }
+          dv[j] = v;
+          AM[(SUB * n + rl) * MS + SUB * n + il] = v;
+        }
+        *reinterpret_cast<float4*>(&AT[n * 256 + l16 * 16 + 4 * lg]) = make_float4(dv[0], dv[1], dv[2], dv[3]);
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+          if (a < n) {
+            const float gi = PER_CHANNEL ? 0.f : gam(SUB * a + l16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float v = accA[a][j] * brow[j];
+              if (!PER_CHANNEL) v *= exp2f((grow[j] - gi) * LOG2E);
+              AM[(SUB * n + 4 * lg + j) * MS + SUB * a + l16] = v;
+            }
+          }
+        }
+        // M^T blocks: lane holds M[16n + l16][16a + 4lg + j]
+        const float gr = PER_CHANNEL ? 0.f : gam(r);
+        float md[4], mo[3][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int il = 4 * lg + j;
+          float v = 0.f;
+          if (il <= l16) {
+            if (flagged) v = AM[upper_off(n) + l16 * MS + il];
+            else {
+              v = accM_d[j];
+              if (!PER_CHANNEL) v *= exp2f((gr - gam(SUB * n + il)) * LOG2E);
+            }
+          }
+          md[j] = v;
+        }
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            float v = accM[a][j];
+            if (!PER_CHANNEL && a < n) v *= exp2f((gr - gam(SUB * a + 4 * lg + j)) * LOG2E);
+            mo[a][j] = v;
+          }
+        float v[8];
+        // fragment (n, 0): blocks (n, 0), (n, 1)
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          v[j] = n == 0 ? md[j] : mo[0][j];
+          v[4 + j] = n == 0 ? 0.f : (n == 1 ? md[j] : mo[1][j]);
+        }
+        store_frag(rec, REC_M, n * 2, lane, v);
+        if (n >= 2) {  // fragment (n, 1): blocks (n, 2), (n, 3)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[j] = n == 2 ? md[j] : mo[2][j];
+            v[4 + j] = n == 3 ? md[j] : 0.f;
+          }
+          store_frag(rec, REC_M, n * 2 + 1, lane, v);
+        }
+      }
+
+      // ---- 4. T_nn = (I + A_nn)^-1 by column-oriented substitution -----------
+      // Lane c < 16 owns column c; A_nn's columns come from AT (written by this
+      // wave just above, so no barrier is needed).
+      if (lane < SUB) {
+        const float* ATn = AT + n * 256;
+        float acc[SUB];
+#pragma unroll
+        for (int i = 0; i < SUB; ++i) acc[i] = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+        for (int j = 0; j < SUB - 1; ++j) {
+          float col[SUB];
+#pragma unroll
+          for (int q = 0; q < SUB; q += 4) *reinterpret_cast<float4*>(&col[q]) = *reinterpret_cast<const float4*>(&ATn[j * SUB + q]);
+          const float xj = acc[j];
+#pragma unroll
+          for (int i = j + 1; i < SUB; ++i) acc[i] -= col[i] * xj;
+        }
+#pragma unroll
+        for (int i = 0; i < SUB; ++i) TM[(SUB * n + i) * MS + SUB * n + lane] = acc[i];
+      }
+      __syncthreads();  // A rows, diagonal T blocks and Khat^T visible
+
+      // ---- 5. off-diagonal blocks of T, level by level (fp32 matrix cores) ----
       //   T_ba = -T_bb * sum_{a<=j<b} A_bj T_ja
 #pragma unroll
       for (int lev = 1; lev < NSUB; ++lev) {
         if (wave < NSUB - lev) {
           const int a = wave, b = wave + lev;
-          f32x4 X = zero4();
+          f32x4 Xs = zero4();
           for (int j = a; j < b; ++j) {
 #pragma unroll
             for (int s = 0; s < 4; ++s) {
               const float av = AM[(SUB * b + l16) * MS + SUB * j + 4 * s + lg];
               const float tv = TM[(SUB * j + 4 * s + lg) * MS + SUB * a + l16];
-              X = mma_f32(av, tv, X);
+              Xs = mma_f32(av, tv, Xs);
             }
           }
-          // contraction order permuted so that X's own C layout is the B operand
-          f32x4 Y = zero4();
+          // contraction order permuted so that Xs's own C layout is the B operand
+          f32x4 Ys = zero4();
 #pragma unroll
-          for (int s = 0; s < 4; ++s) Y = mma_f32(TM[(SUB * b + l16) * MS + SUB * b + 4 * lg + s], X[s], Y);
+          for (int s = 0; s < 4; ++s) Ys = mma_f32(TM[(SUB * b + l16) * MS + SUB * b + 4 * lg + s], Xs[s], Ys);
 #pragma unroll
-          for (int j = 0; j < 4; ++j) TM[(SUB * b + 4 * lg + j) * MS + SUB * a + l16] = -Y[j];
+          for (int j = 0; j < 4; ++j) TM[(SUB * b + 4 * lg + j) * MS + SUB * a + l16] = -Ys[j];
         }
         __syncthreads();
       }
 
-      // ---- F0: Khat^T fragments into LDS (A is dead now) ----------------------
-#pragma unroll
-      for (int q2 = 0; q2 < 2; ++q2) {
-        const int f = wave * 2 + q2, kb = f >> 1, s = f & 1;
-        const int k = SUB * kb + l16;
-        const int j0 = 32 * s + 8 * lg;
-        const float fe = PER_CHANNEL ? EP[(j0 / SUB) * HD + k] : 0.f;
-        float v[8];
-#pragma unroll
-        for (int q = 0; q < 8; ++q) v[q] = KR[(j0 + q) * LS + k] * (PER_CHANNEL ? fe : ROW[R_EG + j0 + q]);
-        KH[f * 64 + lane] = to_f16x8(v);
-      }
-      __syncthreads();
-
-      // ---- F: W^T = Khat^T (T diag(b))^T; T diag(b) fragments -----------------
-      // wave w: token tile t = w % 4, key slices sp = 2 (w / 4) .. +1
+      // ---- 6. -W^T = -Khat^T (T diag(b))^T and T diag(b) fragments -----------
       {
-        const int t = wave & 3;
-        const int r = SUB * t + l16;
+        const int t = wave, rt = SUB * t + l16;
         const int ns = (t >> 1) + 1;  // token slices with nonzero T entries for this tile
         f16x8 tbB[2];
 #pragma unroll
         for (int s = 0; s < 2; ++s) {
-          float v[8], bb[8];
-          ld8(&TM[r * MS + 32 * s + 8 * lg], v);
-          ld8(&ROW[R_BETA + 32 * s + 8 * lg], bb);
+          float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+          if (s < ns) {
+            const int j0 = 32 * s + 4 * lg, j1 = j0 + 16;
+            float tv[8], bb[8];
+            *reinterpret_cast<float4*>(&tv[0]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j0]);
+            *reinterpret_cast<float4*>(&tv[4]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j1]);
+            *reinterpret_cast<float4*>(&bb[0]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j0]);
+            *reinterpret_cast<float4*>(&bb[4]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j1]);
 #pragma unroll
-          for (int q = 0; q < 8; ++q) v[q] = (32 * s + 8 * lg + q <= r) ? v[q] * bb[q] : 0.f;
+            for (int q = 0; q < 4; ++q) {
+              v[q] = (j0 + q <= rt) ? tv[q] * bb[q] : 0.f;
+              v[4 + q] = (j1 + q <= rt) ? tv[4 + q] * bb[4 + q] : 0.f;
+            }
+            store_frag(rec, REC_TB, t * 2 + s, lane, v);
+          }
           tbB[s] = to_f16x8(v);
         }
 #pragma unroll
-        for (int sq = 0; sq < 2; ++sq) {
-          const int sp = 2 * (wave >> 2) + sq;
+        for (int sp = 0; sp < 4; ++sp) {
           float v[8];
 #pragma unroll
           for (int hh = 0; hh < 2; ++hh) {
-            const int kb = 2 * sp + hh;
+            const int kt = 2 * sp + hh;
             f32x4 acc = zero4();
-            acc = mma_f16(KH[(kb * 2) * 64 + lane], tbB[0], acc);
-            if (ns > 1) acc = mma_f16(KH[(kb * 2 + 1) * 64 + lane], tbB[1], acc);
+            acc = mma_f16(KH[(kt * 2) * 64 + lane], tbB[0], acc);
+            if (ns > 1) acc = mma_f16(KH[(kt * 2 + 1) * 64 + lane], tbB[1], acc);
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[hh * 4 + j] = -acc[j];
           }
           store_frag(rec, REC_WNEG, t * 4 + sp, lane, v);
         }
-        const int s = wave >> 2;  // T diag(b) fragment (t, s), if nonzero
-        if (s < ns) {
-          const int j0 = 32 * s + 4 * lg, j1 = j0 + 16;
-          float v[8], bb[8];
-          ld4(&TM[r * MS + j0], v);
-          ld4(&TM[r * MS + j1], v + 4);
-          ld4(&ROW[R_BETA + j0], bb);
-          ld4(&ROW[R_BETA + j1], bb + 4);
-#pragma unroll
-          for (int q = 0; q < 4; ++q) {
-            v[q] = (j0 + q <= r) ? v[q] * bb[q] : 0.f;
-            v[4 + q] = (j1 + q <= r) ? v[4 + q] * bb[4 + q] : 0.f;
-          }
-          store_frag(rec, REC_TB, t * 2 + s, lane, v);
-        }
       }
-      __syncthreads();  // LDS is reused by the next job
     }
-    job = nj;
-    if (job >= n_jobs) break;
   }
 }
 
 void launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, hipStream_t stream) {
   const int n_jobs = n_entries * p.H;
   if (n_jobs <= 0) return;
-  int dev = 0, cus = 256;
-  if (hipGetDevice(&dev) == hipSuccess) {
-    int v = 0;
-    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) cus = v;
-  }
-  const int grid = n_jobs < cus ? n_jobs : cus;  // one resident workgroup per CU (LDS-bound)
+  const int grid = n_jobs;  // one job per workgroup; two are resident per CU (LDS-bound)
   static bool attr_set[2] = {false, false};
   if (per_channel) {
     if (!attr_set[1]) {

@@ -172,6 +172,15 @@ __device__ __forceinline__ void gate_decay(float x, float a, float& d, float& g)
   g = -a * LN2 * t2;
 }
 
+// log2 of the decay factor: -a * softplus(x) / ln 2 (same evaluation as
+// above, without a branch: the clamped exponent keeps the unused side finite).
+__device__ __forceinline__ float gate_log2(float x, float a) {
+  constexpr float LOG2E = 1.4426950408889634f;
+  const float y = x * LOG2E;
+  const float t = __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(fminf(y, 64.f)));
+  return -a * (x > 20.f ? y : t);
+}
+
 __device__ __forceinline__ float sigmoidf_(float x) { return 1.f / (1.f + __expf(-x)); }
 
 }  // namespace kda
