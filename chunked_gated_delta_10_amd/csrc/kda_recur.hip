@@ -9,7 +9,8 @@
 //   O  = scale * (Qhat S + M U)          -> out (bf16)
 //   S <- Diag(exp(Gamma_L)) S + Kbar^T U
 // Wave w owns token tile w of U and O and key tiles 2w, 2w+1 of S; the fp16
-// copies of S and U travel between waves through LDS (4 KiB + 2 KiB).
+// copies of S and U travel between waves through LDS (4 KiB + 2 KiB).  The
+// chunk records stream through two or three register sets.
 //
 // Workgroups of one chain are given ids congruent mod 8 so they land on the
 // same XCD and share its L2 for the chunk records.
@@ -89,7 +90,7 @@ __device__ __forceinline__ void load_frags(Frags& F, const uint8_t* R, int wave,
 
 }  // namespace
 
-template <typename StT>
+template <typename StT, int NSTAGE>
 __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
   __shared__ __attribute__((aligned(16))) f16x8 sbuf[4 * 64];  // S slices (B operand)
   __shared__ __attribute__((aligned(16))) f16x4 ubuf[4 * 64];  // U tiles (C layout)
@@ -145,23 +146,35 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
     }
     __syncthreads();
     // 2. U = T diag(b) V - W S ;  OQ = Qhat S      (token tile `wave`)
+    //    (two accumulators each, halving the dependent matrix-core chains)
     f16x8 sB[4];
 #pragma unroll
     for (int s = 0; s < 4; ++s) sB[s] = sbuf[s * 64 + lane];
-    f32x4 U = zero4(), OQ = zero4();
+    f32x4 U = zero4(), U2 = zero4(), OQ = zero4(), OQ2 = zero4();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       if (s <= (wave >> 1)) {
         const f16x4 lo = *reinterpret_cast<const f16x4*>(&vsT[l16 * VS + 32 * s + 4 * lg]);
         const f16x4 hi = *reinterpret_cast<const f16x4*>(&vsT[l16 * VS + 32 * s + 16 + 4 * lg]);
         const f16x8 vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        U = mma_f16(F.t[s], vb, U);
+        if (s == 0) U = mma_f16(F.t[s], vb, U);
+        else U2 = mma_f16(F.t[s], vb, U2);
       }
     }
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
-      U = mma_f16(F.w[s], sB[s], U);
-      OQ = mma_f16(F.q[s], sB[s], OQ);
+      if (s & 1) {
+        U2 = mma_f16(F.w[s], sB[s], U2);
+        OQ2 = mma_f16(F.q[s], sB[s], OQ2);
+      } else {
+        U = mma_f16(F.w[s], sB[s], U);
+        OQ = mma_f16(F.q[s], sB[s], OQ);
+      }
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      U[j] += U2[j];
+      OQ[j] += OQ2[j];
     }
     // 3. publish U (fp16, C layout of token tile `wave`)
     {
@@ -197,19 +210,44 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
     }
   };
 
-  // ping-pong over two fragment sets: chunk c+1 loads while chunk c computes
-  Frags fa, fb;
-  if (nch > 0) load_chunk(fa, 0);
-  // Drain the first chunk's loads here, so the loop header carries no
-  // pending-load state on the fragments and the waits inside the loop only
-  // cover the older of the two fragment sets.
-  __builtin_amdgcn_s_waitcnt(0);
-  for (int c = 0; c < nch; c += 2) {
-    if (c + 1 < nch) load_chunk(fb, c + 1);
-    step(fa, c);
-    if (c + 1 >= nch) break;
-    if (c + 2 < nch) load_chunk(fa, c + 2);
-    step(fb, c + 1);
+  // NSTAGE fragment sets in rotation: chunk c + NSTAGE - 1 loads while chunk
+  // c computes.  Loads past the last chunk re-read the last chunk (clamped),
+  // so every load is unconditional and the wait counts inside the loop are
+  // exact.  Three sets give a record two chunk steps to arrive but take ~300
+  // registers (one workgroup per CU); two sets fit two workgroups per CU,
+  // which suits grids with many short chains.
+  const int last = nch - 1;
+  if (NSTAGE == 3) {
+    Frags f0, f1, f2;
+    if (nch > 0) {
+      load_chunk(f0, 0);
+      load_chunk(f1, min(1, last));
+    }
+    // Drain the first loads here, so the loop header carries no pending-load
+    // state on the fragments and each wait inside the loop only covers the
+    // oldest set.
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int c = 0; c < nch; c += 3) {
+      load_chunk(f2, min(c + 2, last));
+      step(f0, c);
+      if (c + 1 >= nch) break;
+      load_chunk(f0, min(c + 3, last));
+      step(f1, c + 1);
+      if (c + 2 >= nch) break;
+      load_chunk(f1, min(c + 4, last));
+      step(f2, c + 2);
+    }
+  } else {
+    Frags f0, f1;
+    if (nch > 0) load_chunk(f0, 0);
+    __builtin_amdgcn_s_waitcnt(0);
+    for (int c = 0; c < nch; c += 2) {
+      load_chunk(f1, min(c + 1, last));
+      step(f0, c);
+      if (c + 1 >= nch) break;
+      load_chunk(f0, min(c + 2, last));
+      step(f1, c + 1);
+    }
   }
   if (p.s1) {
 #pragma unroll
@@ -223,9 +261,22 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
 int recur_grid(int n_chains) { return ((n_chains + 7) / 8) * 8 * NVT; }
 
 void launch_recur(const RecurParams& p, bool bf16_state, hipStream_t stream) {
-  dim3 grid(recur_grid(p.n_chains));
-  if (bf16_state) recur_kernel<uint16_t><<<grid, 256, 0, stream>>>(p);
-  else recur_kernel<float><<<grid, 256, 0, stream>>>(p);
+  static int cus = 0;
+  if (cus == 0) {
+    int dev = 0, v = 0;
+    cus = (hipGetDevice(&dev) == hipSuccess &&
+           hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ? v : 256;
+  }
+  const int g = recur_grid(p.n_chains);
+  const bool deep = g <= 4 * cus;  // few chains: latency per chain matters most
+  dim3 grid(g);
+  if (bf16_state) {
+    if (deep) recur_kernel<uint16_t, 3><<<grid, 256, 0, stream>>>(p);
+    else recur_kernel<uint16_t, 2><<<grid, 256, 0, stream>>>(p);
+  } else {
+    if (deep) recur_kernel<float, 3><<<grid, 256, 0, stream>>>(p);
+    else recur_kernel<float, 2><<<grid, 256, 0, stream>>>(p);
+  }
 }
 
 }  // namespace kda
