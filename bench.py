@@ -27,8 +27,8 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix throughput, published
 D, C = 128, 64                 # head dim, chunk length
 FLOP_PER_TOKEN_HEAD = 6 * D * D + 5 * C * D   # 139,264 (algorithmic, per token and head)
-KERNEL_SOURCES = ["chunked_gated_delta_10_amd/csrc/kda_chunk.hip", "chunked_gated_delta_10_amd/csrc/kda_recur.hip",
-                  "chunked_gated_delta_10_amd/csrc/kda_decode.hip", "chunked_gated_delta_10_amd/csrc/kda_device.h"]
+KERNEL_SOURCES = ["chunked_gated_delta_10_amd/csrc/" + f for f in
+                  ("kda_chunk.hip", "kda_recur.hip", "kda_table.hip", "kda_decode.hip", "kda_device.h", "kda_kernels.h")]
 
 
 def algorithmic_bytes(w, with_state=True):
@@ -65,6 +65,72 @@ def load_traffic(kernel, workload):
     if not rec or rec.get("sources_hash") != sources_hash():
         return None
     return rec.get("hbm_bytes_per_launch")
+
+
+def copy_calibration(mib):
+    """A plain device-to-device copy of `mib` MiB, five times: the reference
+    kernel whose FETCH_SIZE / WRITE_SIZE counters calibrate HBM byte counts."""
+    import torch
+    n = mib * 1024 * 1024
+    src = torch.empty(n, dtype=torch.uint8, device="cuda")
+    src.fill_(1)
+    dst = torch.empty_like(src)
+    torch.cuda.synchronize()
+    for _ in range(5):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes": n}), flush=True)
+
+
+def _counter_rows(directory):
+    """(kernel name, counter name, value) from every rocprofv3 counter CSV under `directory`."""
+    import csv
+    import glob
+    rows = []
+    for path in glob.glob(os.path.join(directory, "**", "*counter_collection.csv"), recursive=True):
+        with open(path) as f:
+            for r in csv.DictReader(f):
+                rows.append((r.get("Kernel_Name", ""), r.get("Counter_Name", ""), float(r.get("Counter_Value", 0))))
+    return rows
+
+
+def _per_dispatch_kib(rows, counter, match):
+    vals = [v for k, c, v in rows if c == counter and match(k)]
+    return sum(vals) / len(vals) if vals else None
+
+
+def traffic_from(root, copy_bytes, workload="kda_dense"):
+    """Turn four rocprofv3 --pmc runs into profiles/traffic.json.
+
+    Expects under `root`: pmc_fetch/ and pmc_write/ (FETCH_SIZE, WRITE_SIZE of
+    the bench run) and cal_fetch/, cal_write/ (the same counters over
+    --copy-calibration).  Each counter is scaled by ideal/measured of the copy
+    (a copy of N bytes fetches N and writes N bytes)."""
+    cal_f = _counter_rows(os.path.join(root, "cal_fetch"))
+    cal_w = _counter_rows(os.path.join(root, "cal_write"))
+    copy_f = max(v for _, c, v in cal_f if c == "FETCH_SIZE")
+    copy_w = max(v for _, c, v in cal_w if c == "WRITE_SIZE")
+    kf = copy_bytes / (copy_f * 1024.0)
+    kw = copy_bytes / (copy_w * 1024.0)
+    run_f = _counter_rows(os.path.join(root, "pmc_fetch"))
+    run_w = _counter_rows(os.path.join(root, "pmc_write"))
+    out = {"_calibration": {"copy_bytes": copy_bytes, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+                            "fetch_factor": kf, "write_factor": kw}}
+    rec = {}
+    for kern, tag in (("kda_chunk_local", "chunk_local_kernel"), ("kda_recur", "recur_kernel"),
+                      ("kda_table", "table_kernel")):
+        f = _per_dispatch_kib(run_f, "FETCH_SIZE", lambda k, t=tag: t in k)
+        w = _per_dispatch_kib(run_w, "WRITE_SIZE", lambda k, t=tag: t in k)
+        if f is None or w is None:
+            continue
+        rec[kern] = {"fetch_kib": f, "write_kib": w, "hbm_read_bytes": f * 1024 * kf,
+                     "hbm_write_bytes": w * 1024 * kw, "hbm_bytes_per_launch": f * 1024 * kf + w * 1024 * kw,
+                     "sources_hash": sources_hash()}
+    out[workload] = rec
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    with open(path, "w") as fh:
+        json.dump(out, fh, indent=1)
+    print(json.dumps(out, indent=1))
 
 
 def cpu_baseline(inp, w, tokens):
@@ -144,7 +210,16 @@ def main():
     ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens per row in the oracle's timed sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
+    ap.add_argument("--copy-calibration", type=int, metavar="MIB",
+                    help="only run a plain device copy of MIB MiB (counter calibration)")
+    ap.add_argument("--traffic-from", metavar="DIR",
+                    help="write profiles/traffic.json from rocprofv3 counter runs under DIR (no GPU needed)")
+    ap.add_argument("--copy-bytes", type=int, default=1024 * 1024 * 1024,
+                    help="size of the calibration copy used with --traffic-from")
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from, args.copy_bytes)
+        return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: the KDA path here is built and measured on a single MI355X "
@@ -154,6 +229,9 @@ def main():
 
     import torch
     assert torch.cuda.is_available(), "bench.py needs a GPU"
+    if args.copy_calibration:
+        copy_calibration(args.copy_calibration)
+        return
     from chunked_gated_delta_10_amd import kda
     kda.load()
 
