@@ -25,10 +25,18 @@ constexpr int VT = 16;        // value columns per workgroup
 constexpr int NVT = HD / VT;  // value tiles per chain
 constexpr int VS = CH + 8;    // row stride (fp16) of the transposed value tile
 
+constexpr int PF_AHEAD = 3;                          // chunks the L2 touches run ahead of the loads
+constexpr int LINE = 128;                            // L2 line bytes
+constexpr int REC_LINES = (REC_BYTES + LINE - 1) / LINE;
+constexpr int TOUCH_REC = (REC_LINES + NVT - 1) / NVT;  // record lines touched per value tile (65)
+constexpr int TOUCH_V = 2 * CH / NVT;                // value-row lines touched per value tile (16)
+static_assert(TOUCH_REC + TOUCH_V <= 256, "one touch per thread");
+
 struct Frags {
   f16x8 w[4], q[4], k[4], m[2], t[2];
   float4 gl[2];
-  uint2 v;  // 4 bf16 of the value tile (token tid/4, columns 4*(tid%4)..)
+  uint2 v;         // 4 bf16 of the value tile (token tid/4, columns 4*(tid%4)..)
+  uint32_t touch;  // word of a later chunk's record or value row, loaded only to pull its line into L2
 };
 
 template <typename StT>
@@ -120,13 +128,34 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
   const size_t vstride = (size_t)p.H * HD;
   const int vcol = v0 + 4 * (tid & 3);
   const uint16_t* vchain = p.v + ((size_t)tok0 * p.H + h) * HD + vcol;
+  // L2 warm-up: value tile vt's workgroup touches record lines
+  // [vt*TOUCH_REC, ...) and value-row lines [vt*TOUCH_V, ...) of chunk
+  // c + PF_AHEAD, so the eight workgroups of a chain together bring each
+  // record into their XCD's L2 before any of them loads it.  Threads past
+  // the share repeat a valid address.
+  const int tl = tid < TOUCH_REC + TOUCH_V ? tid : 0;
+  const bool trec = tl < TOUCH_REC;
+  const int rec_line = min(vt * TOUCH_REC + (trec ? tl : 0), REC_LINES - 1);
+  const int vrow = (vt * TOUCH_V + (trec ? 0 : tl - TOUCH_REC)) >> 1, vhalf = (tl - TOUCH_REC) & 1;
   auto load_chunk = [&](Frags& F, int c) {
     const uint8_t* R = p.rec + ((size_t)(chunk0 + c) * p.H + h) * REC_BYTES;
     load_frags(F, R, wave, lane, tid, vchain + (size_t)c * CH * vstride, min(CH, len - c * CH), vstride);
+    const int ct = min(c + PF_AHEAD, nch - 1);
+    const uint32_t* tp;
+    if (trec) {
+      tp = reinterpret_cast<const uint32_t*>(p.rec + ((size_t)(chunk0 + ct) * p.H + h) * REC_BYTES + (size_t)rec_line * LINE);
+    } else {
+      const int L = min(CH, len - ct * CH);
+      tp = reinterpret_cast<const uint32_t*>(p.v + ((size_t)(tok0 + ct * CH + min(vrow, L - 1)) * p.H + h) * HD +
+                                             vhalf * (LINE / 2));
+    }
+    F.touch = *tp;
   };
 
+  uint32_t sink = 0;  // keeps the L2 touches alive; consumed NSTAGE-1 steps after issue
   // one chunk of the recurrence on fragments F
   auto step = [&](const Frags& F, int c) {
+    sink ^= F.touch;
     const int L = min(CH, len - c * CH);
     // 1. publish this wave's fp16 slice of S and the value tile
     {
@@ -249,6 +278,7 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
       step(f1, c + 1);
     }
   }
+  asm volatile("" ::"v"(sink));
   if (p.s1) {
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
