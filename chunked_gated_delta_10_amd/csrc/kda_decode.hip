@@ -10,7 +10,8 @@
 // so the state streams through once: read 512 B, write 512 B per row.
 //
 // Workgroup = one (batch row, head), 256 threads; a group of 16 lanes owns
-// one state row per step (8 key channels per lane, two 16-byte accesses),
+// one state row per step (8 key channels per lane, two 16-byte accesses that
+// each cover half a row contiguously across the 16 lanes),
 // 16 rows are in flight per pass and each lane walks 8 rows.  All loads of a
 // lane are issued before any arithmetic so 16 x 16-byte requests per lane
 // are outstanding.
@@ -21,41 +22,56 @@ namespace kda {
 
 namespace {
 
+// A lane holds key channels 4ks .. 4ks+3 and 64+4ks .. 64+4ks+3 of a row, so
+// each 16-byte access instruction of 16 lanes covers 256 contiguous bytes.
 template <typename StT>
 struct RowIO;
 
 template <>
 struct RowIO<float> {
-  __device__ static void load(const void* base, size_t off, float* x) {
-    const f32x4* p = reinterpret_cast<const f32x4*>(reinterpret_cast<const float*>(base) + off);
-    const f32x4 a = __builtin_nontemporal_load(p), b = __builtin_nontemporal_load(p + 1);
+  __device__ static void load(const void* base, size_t row, int ks, float* x) {
+    const float* r = reinterpret_cast<const float*>(base) + row;
+    const f32x4 a = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + 4 * ks));
+    const f32x4 b = __builtin_nontemporal_load(reinterpret_cast<const f32x4*>(r + 64 + 4 * ks));
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
       x[j] = a[j];
       x[4 + j] = b[j];
     }
   }
-  __device__ static void store(void* base, size_t off, const float* x) {
-    f32x4* p = reinterpret_cast<f32x4*>(reinterpret_cast<float*>(base) + off);
-    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, p);
-    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, p + 1);
+  __device__ static void store(void* base, size_t row, int ks, const float* x) {
+    float* r = reinterpret_cast<float*>(base) + row;
+    __builtin_nontemporal_store(f32x4{x[0], x[1], x[2], x[3]}, reinterpret_cast<f32x4*>(r + 4 * ks));
+    __builtin_nontemporal_store(f32x4{x[4], x[5], x[6], x[7]}, reinterpret_cast<f32x4*>(r + 64 + 4 * ks));
   }
 };
 
 template <>
 struct RowIO<uint16_t> {
-  __device__ static void load(const void* base, size_t off, float* x) {
-    const u32x4 w = __builtin_nontemporal_load(
-        reinterpret_cast<const u32x4*>(reinterpret_cast<const uint16_t*>(base) + off));
-    unpack_bf16x8(make_uint4(w[0], w[1], w[2], w[3]), x);
+  __device__ static void load(const void* base, size_t row, int ks, float* x) {
+    const uint16_t* r = reinterpret_cast<const uint16_t*>(base) + row;
+    const uint2 a = *reinterpret_cast<const uint2*>(r + 4 * ks);
+    const uint2 b = *reinterpret_cast<const uint2*>(r + 64 + 4 * ks);
+    unpack_bf16x8(make_uint4(a.x, a.y, b.x, b.y), x);
   }
-  __device__ static void store(void* base, size_t off, const float* x) {
-    u32x4 w;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) w[j] = (uint32_t)f32_to_bf16(x[2 * j]) | ((uint32_t)f32_to_bf16(x[2 * j + 1]) << 16);
-    __builtin_nontemporal_store(w, reinterpret_cast<u32x4*>(reinterpret_cast<uint16_t*>(base) + off));
+  __device__ static void store(void* base, size_t row, int ks, const float* x) {
+    uint16_t* r = reinterpret_cast<uint16_t*>(base) + row;
+    uint2 a, b;
+    a.x = (uint32_t)f32_to_bf16(x[0]) | ((uint32_t)f32_to_bf16(x[1]) << 16);
+    a.y = (uint32_t)f32_to_bf16(x[2]) | ((uint32_t)f32_to_bf16(x[3]) << 16);
+    b.x = (uint32_t)f32_to_bf16(x[4]) | ((uint32_t)f32_to_bf16(x[5]) << 16);
+    b.y = (uint32_t)f32_to_bf16(x[6]) | ((uint32_t)f32_to_bf16(x[7]) << 16);
+    *reinterpret_cast<uint2*>(r + 4 * ks) = a;
+    *reinterpret_cast<uint2*>(r + 64 + 4 * ks) = b;
   }
 };
+
+// 8 bf16 values of a vector at this lane's channels
+__device__ __forceinline__ void load_vec8(const uint16_t* base, int ks, float* x) {
+  const uint2 a = *reinterpret_cast<const uint2*>(base + 4 * ks);
+  const uint2 b = *reinterpret_cast<const uint2*>(base + 64 + 4 * ks);
+  unpack_bf16x8(make_uint4(a.x, a.y, b.x, b.y), x);
+}
 
 }  // namespace
 
@@ -63,26 +79,26 @@ template <typename StT, bool PER_CHANNEL>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr int ROWS = 8;  // rows per lane
   const int tid = threadIdx.x;
-  const int ks = tid & 15;   // key slice: channels 8*ks .. 8*ks+7
+  const int ks = tid & 15;   // key slice: channels 4ks .. 4ks+3 and 64+4ks .. 64+4ks+3
   const int rg = tid >> 4;   // row group: rows rg + 16 i
   const int bh = blockIdx.x;
   const int b = bh / p.H, h = bh - b * p.H;
   const int hq = h / (p.H / p.H_qk);
-  const size_t sbase = (size_t)bh * HD * HD + 8 * ks;
+  const size_t sbase = (size_t)bh * HD * HD;
 
   float s[ROWS][8];
 #pragma unroll
-  for (int i = 0; i < ROWS; ++i) RowIO<StT>::load(p.state, sbase + (size_t)(rg + 16 * i) * HD, s[i]);
+  for (int i = 0; i < ROWS; ++i) RowIO<StT>::load(p.state, sbase + (size_t)(rg + 16 * i) * HD, ks, s[i]);
 
   float qv[8], kv[8], d[8];
   {
-    const size_t qoff = ((size_t)b * p.H_qk + hq) * HD + 8 * ks;
-    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.q + qoff), qv);
-    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.k + qoff), kv);
+    const size_t qoff = ((size_t)b * p.H_qk + hq) * HD;
+    load_vec8(p.q + qoff, ks, qv);
+    load_vec8(p.k + qoff, ks, kv);
     const float a = __expf(p.A_log[h]);
     if (PER_CHANNEL) {
       float gr[8];
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(p.g_raw + ((size_t)bh * HD + 8 * ks)), gr);
+      load_vec8(p.g_raw + (size_t)bh * HD, ks, gr);
 #pragma unroll
       for (int j = 0; j < 8; ++j) {
         float g;
@@ -131,7 +147,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     const float u = beta * (vrow[i] - a);
 #pragma unroll
     for (int j = 0; j < 8; ++j) s[i][j] += u * kv[j];
-    RowIO<StT>::store(p.state, sbase + (size_t)(rg + 16 * i) * HD, s[i]);
+    RowIO<StT>::store(p.state, sbase + (size_t)(rg + 16 * i) * HD, ks, s[i]);
     if (ks == 0) p.out[(size_t)bh * HD + rg + 16 * i] = f32_to_bf16(p.scale * (c + u * qk));
   }
 }
