@@ -67,6 +67,27 @@ def load_traffic(kernel, workload):
     return rec.get("hbm_bytes_per_launch")
 
 
+def copy_bandwidth(mib=1024, reps=10):
+    """Achieved GB/s (read + write) of a plain 1 GiB device-to-device copy: what
+    this HBM delivers in practice, next to the 8 TB/s specification."""
+    import torch
+    n = mib * 1024 * 1024
+    src = torch.ones(n, dtype=torch.uint8, device="cuda")
+    dst = torch.empty_like(src)
+    dst.copy_(src)
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    e0.record()
+    for _ in range(reps):
+        dst.copy_(src)
+    e1.record()
+    torch.cuda.synchronize()
+    gbs = 2.0 * n * reps / (e0.elapsed_time(e1) * 1e-3) / 1e9
+    del src, dst
+    torch.cuda.empty_cache()
+    return round(gbs, 1)
+
+
 def copy_calibration(mib):
     """A plain device-to-device copy of `mib` MiB, five times: the reference
     kernel whose FETCH_SIZE / WRITE_SIZE counters calibrate HBM byte counts."""
@@ -185,21 +206,24 @@ def time_workload(name, steps, warmup):
     torch.cuda.synchronize()
     kda.kernel_timing(True)
     kda.kernel_timing_read()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
-    ev0.record()
-    for _ in range(steps):
+    evs[0].record()
+    for i in range(steps):
         step()
-    ev1.record()
+        evs[i + 1].record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
     kt = kda.kernel_timing_read()
     kda.kernel_timing(False)
-    gpu_ms = ev0.elapsed_time(ev1)
+    gpu_ms = evs[0].elapsed_time(evs[-1])
     ms = max(wall * 1000.0, gpu_ms) / steps
+    per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
+    pct = {"p10": round(per_step[int(0.1 * (steps - 1))], 4), "p50": round(per_step[int(0.5 * (steps - 1))], 4),
+           "p90": round(per_step[int(0.9 * (steps - 1))], 4)}
     per_kernel = {k: v[0] / v[1] for k, v in kt.items()}
-    return ms, per_kernel, inp, w
+    return ms, per_kernel, inp, w, pct
 
 
 def main():
@@ -236,7 +260,7 @@ def main():
     kda.load()
 
     name = "kda_dense"
-    ms, per_kernel, inp, w = time_workload(name, args.steps, args.warmup)
+    ms, per_kernel, inp, w, pct = time_workload(name, args.steps, args.warmup)
     tokens = w.B * w.T
     value = tokens / (ms / 1000.0)
     alg = algorithmic_bytes(w)
@@ -266,11 +290,13 @@ def main():
                    "state": "fp32 in/out", "seed": w.seed},
         "roofline": roofline,
         "kernels": kernels,
+        "step_ms_percentiles": pct,
+        "hbm_copy_gbs": copy_bandwidth(),
     }
     if not args.no_extra:
         extra = {}
         for other in ("kda_varlen", "gdn_gva", "kda_decode"):
-            oms, opk, _, ow = time_workload(other, max(10, args.steps // 5), 3)
+            oms, opk, _, ow, _ = time_workload(other, max(10, args.steps // 5), 3)
             ab = algorithmic_bytes(ow)
             tok = ow.B if ow.decode else ow.B * ow.T
             tot = sum(ab.values())

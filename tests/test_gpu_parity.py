@@ -72,6 +72,14 @@ def test_bf16_state():
     check(inp, state_dtype=torch.bfloat16, what="bf16 state")
 
 
+@pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16])
+def test_many_chains_shallow_pipeline(state_dtype):
+    # 40 rows x 8 heads = 320 chains -> 2560 value-tile workgroups, past the
+    # grid size where the recurrence switches to its two-stage fragment ring
+    inp = make_inputs(40, 150, 8, 4, state_std=0.05, seed=24, A_log=(-4.0, -1.0))
+    check(inp, state_dtype=state_dtype, what="many chains %s" % state_dtype)
+
+
 def test_packed_sequences_edge_lengths():
     lens = [19, 64, 1, 130, 0, 77, 65, 63]
     inp = make_inputs(1, sum(lens), 3, 3, state_std=0.02, N=len(lens), lengths=lens, seed=15)
