@@ -47,11 +47,12 @@ constexpr size_t ALIGN = 256;
 size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-  size_t rec, seqs, chunks, order, total;
+  size_t rec, seqs, chunks, order, sink, total;
   int n_entries;
 };
 
-// Workspace: chunk records, then the schedule (sequence table, chunk table, order).
+// Workspace: chunk records, then the schedule (sequence table, chunk table,
+// order) and a small sink for output rows past a chunk's end.
 Layout layout(int n_seqs, int n_entries, int H) {
   Layout L;
   L.n_entries = n_entries;
@@ -59,7 +60,8 @@ Layout layout(int n_seqs, int n_entries, int H) {
   L.seqs = round_up((size_t)n_entries * H * kda::REC_BYTES);
   L.chunks = L.seqs + round_up((size_t)n_seqs * sizeof(int4));
   L.order = L.chunks + round_up((size_t)n_entries * sizeof(int4));
-  L.total = L.order + round_up((size_t)n_seqs * sizeof(int));
+  L.sink = L.order + round_up((size_t)n_seqs * sizeof(int));
+  L.total = L.sink + round_up(64 * sizeof(uint16_t));
   return L;
 }
 
@@ -206,7 +208,8 @@ kda_status run_forward(const FwdArgs& a) {
     kda::launch_chunk_local(cp, n_entries, a.gate_per_channel == 1, a.stream);
   }
   kda::RecurParams rp{ws + L.rec, seqs, order, a.n_seqs * a.H, n_entries, a.H, static_cast<const uint16_t*>(a.v),
-                      static_cast<uint16_t*>(a.out), a.s0, a.s1, a.scale};
+                      static_cast<uint16_t*>(a.out), a.s0, a.s1, a.scale,
+                      reinterpret_cast<uint16_t*>(ws + L.sink)};
   {
     Timed t(K_RECUR, a.stream);
     kda::launch_recur(rp, bf16_state, a.stream);

@@ -31,6 +31,7 @@ struct RecurParams {
   const void* s0;         // [seqs, H, 128, 128] fp32 or bf16, or null
   void* s1;               // same layout, or null
   float scale;
+  uint16_t* sink;         // 64 scratch values: destination of output rows past a chunk's end
 };
 
 // Decode kernel (kda_decode.hip): one workgroup per (batch row, head).
