@@ -10,10 +10,13 @@
 //   S <- Diag(exp(Gamma_L)) S + Kbar^T U
 // Wave w owns token tile w of U and O and key tiles 2w, 2w+1 of S; the fp16
 // copies of S and U travel between waves through LDS (4 KiB + 2 KiB).  The
-// chunk records stream through two or three register sets.
+// chunk records stream through two or three register sets.  Grids of at most
+// one workgroup per CU use an eight-wave variant that gives the chain
+// S -> U -> S' and the output products to different waves.
 //
 // Workgroups of one chain are given ids congruent mod 8 so they land on the
-// same XCD and share its L2 for the chunk records.
+// same XCD and share its L2 for the chunk records, and each of them warms a
+// later record's eighth in that L2.
 #include "kda_device.h"
 #include "kda_kernels.h"
 
@@ -292,40 +295,34 @@ __global__ __launch_bounds__(256) void recur_kernel(RecurParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// Variant for grids of at most one workgroup per CU (few chains, e.g. the
-// dense shape): two extra loader waves copy each chunk record into a
-// two-slot LDS ring with direct-to-LDS 16-byte loads, so the four compute
-// waves never stall behind their own bursts of fragment loads (a wave whose
-// loads wait for room in the texture unit cannot issue anything else).  Per
-// chunk c: the loaders make sure slot c%2 holds chunk c before barrier A;
-// the compute waves read all of chunk c's fragments from LDS before barrier
-// B; after barrier B the loaders refill slot c%2 with chunk c+2.  Each loader
-// copies half of a record (at most 35 loads in flight per chunk, within the
-// 63 the counter can track) and touches its half of the L2 warm-up lines.
+// Split-role variant (eight waves) for one-workgroup-per-CU grids.  The
+// chunk-to-chunk chain is S -> U -> S'; the output products (Qhat S, M U) and
+// the stores hang off it.  Waves 0..3 run only the chain (token tile w of U,
+// key tiles 2w, 2w+1 of S) and waves 4..7 only the output (token tile w-4),
+// so the output work of chunk c overlaps the chain of chunk c+1.  Each role
+// streams its own fragments through three register sets, two chunks ahead;
+// the chain waves also issue the L2 touches.  Both roles meet at the same two
+// barriers per chunk.
 // ---------------------------------------------------------------------------
-constexpr int LR_THREADS = 384;                       // 4 compute + 2 loader waves
-constexpr int LR_SBUF = 2 * REC_BYTES;                // after the two record slots
-constexpr int LR_UBUF = LR_SBUF + 4 * 64 * 16;
-constexpr int LR_VST = LR_UBUF + 4 * 64 * 8;
-constexpr int LR_SINK = LR_VST + VT * VS * 2;         // landing area of the L2 touches (never read)
-constexpr int LR_LDS = LR_SINK + 64 * 4;
-static_assert(LR_LDS <= 160 * 1024, "LDS budget");
-constexpr int LR_FRAGS = REC_GL / FRAG_BYTES;         // 64 fragments, then exp(Gamma_L)
-
-// s_waitcnt immediate for "at most n vector-memory operations outstanding"
-// (gfx9 encoding: vmcnt bits [3:0] and [15:14]; expcnt and lgkmcnt left at max)
-template <int N>
-constexpr int vmcnt_imm() { return (N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8); }
+struct ChainFrags {
+  f16x8 w[4], t[2], k[4];
+  float4 gl[2];
+  uint2 v;
+  uint32_t touch;
+};
+struct OutFrags {
+  f16x8 q[4], m[2];
+};
 
 template <typename StT>
-__global__ __launch_bounds__(LR_THREADS) void recur_lds_kernel(RecurParams p) {
-  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  f16x8* sbuf = reinterpret_cast<f16x8*>(smem + LR_SBUF);
-  f16x4* ubuf = reinterpret_cast<f16x4*>(smem + LR_UBUF);
-  f16* vsT = reinterpret_cast<f16*>(smem + LR_VST);
+__global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
+  __shared__ __attribute__((aligned(16))) f16x8 sbuf[4 * 64];  // S slices (B operand)
+  __shared__ __attribute__((aligned(16))) f16x4 ubuf[4 * 64];  // U tiles (C layout)
+  __shared__ __attribute__((aligned(16))) f16 vsT[VT * VS];    // value tile, [column][token]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
+  const int tw = wave & 3;
   const int x = blockIdx.x, xcd = x & 7, y = x >> 3;
   const int vt = y % NVT, ch = (y / NVT) * 8 + xcd;
   if (ch >= p.n_chains) return;
@@ -334,215 +331,187 @@ __global__ __launch_bounds__(LR_THREADS) void recur_lds_kernel(RecurParams p) {
   const int tok0 = sq.x, len = sq.y, chunk0 = sq.z;
   // never walk past the schedule, whatever cu_seqlens held
   const int nch = max(0, min((len + CH - 1) / CH, p.n_entries - chunk0));
+  const int last = nch - 1;
   const int v0 = vt * VT;
   auto record = [&](int c) { return p.rec + ((size_t)(chunk0 + c) * p.H + h) * REC_BYTES; };
 
-  if (wave >= 4) {
-    // ---- loader waves ------------------------------------------------------
-    const int L = wave - 4;  // half of the record: fragments [32L, 32L+32); L = 1 also copies exp(Gamma_L)
-    // L2 warm-up share of this tile, split over the two loaders: loader 0
-    // touches 33 record lines, loader 1 the other 32 and the 16 value-row lines
-    const int tl = L == 0 ? min(lane, 32) : 33 + min(lane, TOUCH_REC + TOUCH_V - 34);
+  if (wave < 4) {
+    // ---- chain waves ---------------------------------------------------------
+    const size_t sbase = ((size_t)n * p.H + h) * HD * HD + (size_t)(v0 + l16) * HD;
+    f32x4 S[2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      const int k0 = SUB * (2 * tw + i) + 4 * lg;
+      S[i] = p.s0 ? StateIO<StT>::load(p.s0, sbase + k0) : zero4();
+    }
+    const size_t vstride = (size_t)p.H * HD;
+    const uint16_t* vchain = p.v + ((size_t)tok0 * p.H + h) * HD + v0 + 4 * (tid & 3);
+    const int tl = tid < TOUCH_REC + TOUCH_V ? tid : 0;
     const bool trec = tl < TOUCH_REC;
     const int rec_line = min(vt * TOUCH_REC + (trec ? tl : 0), REC_LINES - 1);
-    const int vi = trec ? 0 : tl - TOUCH_REC;
-    const int vrow = (vt * TOUCH_V + vi) >> 1, vhalf = vi & 1;
-    auto copy = [&](int c) {
+    const int vrow = (vt * TOUCH_V + (trec ? 0 : tl - TOUCH_REC)) >> 1, vhalf = (tl - TOUCH_REC) & 1;
+    auto load = [&](ChainFrags& F, int c) {
       const uint8_t* R = record(c);
-      uint8_t* slot = smem + (c & 1) * REC_BYTES;
-#pragma unroll 8
-      for (int f = 32 * L; f < 32 * L + 32; ++f)
-        __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(R + f * FRAG_BYTES + lane * 16),
-                                         (void __attribute__((address_space(3)))*)(slot + f * FRAG_BYTES), 16, 0, 0);
-      if (L == 1) {  // exp(Gamma_L): 512 bytes, lanes 0..31
-        const int ln = lane & 31;
-        if (lane < 32)
-          __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)(R + REC_GL + ln * 16),
-                                           (void __attribute__((address_space(3)))*)(slot + REC_GL), 16, 0, 0);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        F.w[s2] = ldfrag(R, REC_WNEG, tw * 4 + s2, lane);
+        F.k[s2] = ldfrag(R, REC_KBAR, (2 * tw + (s2 >> 1)) * 2 + (s2 & 1), lane);
       }
-    };
-    // the touch lands in LDS too (a never-read area), so no register waits on it
-    auto touch = [&](int c) {
-      const int ct = min(c + PF_AHEAD, nch - 1);
-      const uint8_t* src;
+      F.t[0] = ldfrag(R, REC_TB, tw * 2, lane);
+      F.t[1] = ldfrag(R, REC_TB, tw * 2 + (tw >= 2 ? 1 : 0), lane);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        F.gl[i] = *reinterpret_cast<const float4*>(R + REC_GL + 4 * (SUB * (2 * tw + i) + 4 * lg));
+      const int Lc = min(CH, len - c * CH);
+      F.v = *reinterpret_cast<const uint2*>(vchain + (size_t)c * CH * vstride + (size_t)min(tid >> 2, Lc - 1) * vstride);
+      const int ct = min(c + PF_AHEAD, last);
+      const uint32_t* tp;
       if (trec) {
-        src = record(ct) + (size_t)rec_line * LINE;
+        tp = reinterpret_cast<const uint32_t*>(record(ct) + (size_t)rec_line * LINE);
       } else {
         const int Lt = min(CH, len - ct * CH);
-        src = reinterpret_cast<const uint8_t*>(p.v + ((size_t)(tok0 + ct * CH + min(vrow, Lt - 1)) * p.H + h) * HD +
+        tp = reinterpret_cast<const uint32_t*>(p.v + ((size_t)(tok0 + ct * CH + min(vrow, Lt - 1)) * p.H + h) * HD +
                                                vhalf * (LINE / 2));
       }
-      __builtin_amdgcn_global_load_lds((const void __attribute__((address_space(1)))*)src,
-                                       (void __attribute__((address_space(3)))*)(smem + LR_SINK), 4, 0, 0);
+      F.touch = *tp;
     };
+    uint32_t sink = 0;
+    auto step = [&](const ChainFrags& F, int c) {
+      sink ^= F.touch;
+      const int L = min(CH, len - c * CH);
+      {
+        f16x8 sb;
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          sb[j] = (f16)S[0][j];
+          sb[4 + j] = (f16)S[1][j];
+        }
+        sbuf[tw * 64 + lane] = sb;
+        const int r = tid >> 2, c4 = 4 * (tid & 3);
+        const uint2 vv = r < L ? F.v : make_uint2(0u, 0u);
+        vsT[(c4 + 0) * VS + r] = (f16)__uint_as_float(vv.x << 16);
+        vsT[(c4 + 1) * VS + r] = (f16)__uint_as_float(vv.x & 0xFFFF0000u);
+        vsT[(c4 + 2) * VS + r] = (f16)__uint_as_float(vv.y << 16);
+        vsT[(c4 + 3) * VS + r] = (f16)__uint_as_float(vv.y & 0xFFFF0000u);
+      }
+      __syncthreads();  // A
+      f16x8 sB[4];
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) sB[s2] = sbuf[s2 * 64 + lane];
+      f32x4 U = zero4(), U2 = zero4();
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        if (s2 <= (tw >> 1)) {
+          const f16x4 lo = *reinterpret_cast<const f16x4*>(&vsT[l16 * VS + 32 * s2 + 4 * lg]);
+          const f16x4 hi = *reinterpret_cast<const f16x4*>(&vsT[l16 * VS + 32 * s2 + 16 + 4 * lg]);
+          const f16x8 vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+          if (s2 == 0) U = mma_f16(F.t[0], vb, U);
+          else U2 = mma_f16(F.t[1], vb, U2);
+        }
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) {
+        if (s2 & 1) U2 = mma_f16(F.w[s2], sB[s2], U2);
+        else U = mma_f16(F.w[s2], sB[s2], U);
+      }
+      ubuf[tw * 64 + lane] = f16x4{(f16)(U[0] + U2[0]), (f16)(U[1] + U2[1]), (f16)(U[2] + U2[2]), (f16)(U[3] + U2[3])};
+      __syncthreads();  // B
+      f16x8 uB[2];
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const f16x4 a = ubuf[(2 * s2) * 64 + lane], b = ubuf[(2 * s2 + 1) * 64 + lane];
+        uB[s2] = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+      }
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const f32x4 a = mma_f16(F.k[2 * i], uB[0], f32x4{F.gl[i].x * S[i][0], F.gl[i].y * S[i][1], F.gl[i].z * S[i][2], F.gl[i].w * S[i][3]});
+        const f32x4 b = mma_f16(F.k[2 * i + 1], uB[1], zero4());
+        S[i] = f32x4{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
+      }
+    };
+    ChainFrags f0, f1, f2;
     if (nch > 0) {
-      copy(0);
-      touch(0);
-      if (nch > 1) {
-        copy(1);
-        touch(1);
-      }
-    }
-    for (int c = 0; c < nch; ++c) {
-      // chunk c complete in its slot: everything issued after it (its touch
-      // and chunk c+1's copy and touch) may still be in flight
-      if (c + 1 < nch) {
-        if (L == 0) __builtin_amdgcn_s_waitcnt(vmcnt_imm<1 + 32 + 1>());
-        else __builtin_amdgcn_s_waitcnt(vmcnt_imm<1 + 33 + 1>());
-      } else {
-        __builtin_amdgcn_s_waitcnt(vmcnt_imm<1>());
-      }
-      // Bare barriers: the wait above already makes chunk c's LDS writes
-      // complete, and a fenced barrier would also wait for chunk c+1's copy.
-      __builtin_amdgcn_s_barrier();  // A: slot c%2 holds chunk c
-      __builtin_amdgcn_s_barrier();  // B: compute waves have read chunk c's fragments
-      if (c + 2 < nch) {
-        copy(c + 2);
-        touch(c + 2);
-      }
+      load(f0, 0);
+      load(f1, min(1, last));
     }
     __builtin_amdgcn_s_waitcnt(0);
+    for (int c = 0; c < nch; c += 3) {
+      load(f2, min(c + 2, last));
+      step(f0, c);
+      if (c + 1 >= nch) break;
+      load(f0, min(c + 3, last));
+      step(f1, c + 1);
+      if (c + 2 >= nch) break;
+      load(f1, min(c + 4, last));
+      step(f2, c + 2);
+    }
+    asm volatile("" ::"v"(sink));
+    if (p.s1) {
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        const int k0 = SUB * (2 * tw + i) + 4 * lg;
+        StateIO<StT>::store(p.s1, sbase + k0, S[i]);
+      }
+    }
     return;
   }
 
-  // ---- compute waves -------------------------------------------------------
-  // state tile: wave holds key tiles 2w, 2w+1; lane (column l16, key rows 4lg..4lg+3)
-  const size_t sbase = ((size_t)n * p.H + h) * HD * HD + (size_t)(v0 + l16) * HD;
-  f32x4 S[2];
-#pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int k0 = SUB * (2 * wave + i) + 4 * lg;
-    S[i] = p.s0 ? StateIO<StT>::load(p.s0, sbase + k0) : zero4();
-  }
-  const size_t vstride = (size_t)p.H * HD;
-  const int vcol = v0 + 4 * (tid & 3);
-  const uint16_t* vchain = p.v + ((size_t)tok0 * p.H + h) * HD + vcol;
-  auto load_v = [&](int c) {
-    const int Lc = min(CH, len - c * CH);
-    return *reinterpret_cast<const uint2*>(vchain + (size_t)c * CH * vstride + (size_t)min(tid >> 2, Lc - 1) * vstride);
-  };
-  auto lfrag = [&](const uint8_t* slot, int off, int frag) {
-    return *reinterpret_cast<const f16x8*>(slot + off + frag * FRAG_BYTES + lane * 16);
-  };
-  // Output: lane writes rows 16*wave + 4*lg + j (j < 4) of column v0 + l16;
-  // the row pointer advances by one chunk per step.
+  // ---- output waves ----------------------------------------------------------
   const size_t row_step = (size_t)p.H * HD;
-  uint16_t* orow = p.out + ((size_t)(tok0 + SUB * wave + 4 * lg) * p.H + h) * HD + v0 + l16;
-  // one chunk step; chunk c's value rows are in vcur, chunk c+1's are loaded into vnxt
-  auto cstep = [&](int c, const uint2 vcur, uint2& vnxt) {
+  uint16_t* orow = p.out + ((size_t)(tok0 + SUB * tw + 4 * lg) * p.H + h) * HD + v0 + l16;
+  auto load = [&](OutFrags& F, int c) {
+    const uint8_t* R = record(c);
+#pragma unroll
+    for (int s2 = 0; s2 < 4; ++s2) F.q[s2] = ldfrag(R, REC_QHAT, tw * 4 + s2, lane);
+    F.m[0] = ldfrag(R, REC_M, tw * 2, lane);
+    F.m[1] = ldfrag(R, REC_M, tw * 2 + (tw >= 2 ? 1 : 0), lane);
+  };
+  auto step = [&](const OutFrags& F, int c) {
     const int L = min(CH, len - c * CH);
-    vnxt = load_v(min(c + 1, nch - 1));
-    // 1. publish this wave's fp16 slice of S and the value tile
-    {
-      f16x8 sb;
+    __syncthreads();  // A: S_c slices published
+    f16x8 sB[4];
 #pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sb[j] = (f16)S[0][j];
-        sb[4 + j] = (f16)S[1][j];
-      }
-      sbuf[wave * 64 + lane] = sb;
-      const int r = tid >> 2, c4 = 4 * (tid & 3);
-      const uint2 vv = r < L ? vcur : make_uint2(0u, 0u);
-      vsT[(c4 + 0) * VS + r] = (f16)__uint_as_float(vv.x << 16);
-      vsT[(c4 + 1) * VS + r] = (f16)__uint_as_float(vv.x & 0xFFFF0000u);
-      vsT[(c4 + 2) * VS + r] = (f16)__uint_as_float(vv.y << 16);
-      vsT[(c4 + 3) * VS + r] = (f16)__uint_as_float(vv.y & 0xFFFF0000u);
-    }
-    __syncthreads();  // A
-    // The chunk-to-chunk chain is S -> U -> S': U's operands are read and its
-    // products issued first, U is published, and only then come the output
-    // side products (Qhat S), which overlap the wait at barrier B.
-    const uint8_t* slot = smem + (c & 1) * REC_BYTES;
-    f16x8 sB[4], fw[4], ft[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      sB[s2] = sbuf[s2 * 64 + lane];
-      fw[s2] = lfrag(slot, REC_WNEG, wave * 4 + s2);
-    }
-    ft[0] = lfrag(slot, REC_TB, wave * 2);
-    ft[1] = wave >= 2 ? lfrag(slot, REC_TB, wave * 2 + 1) : ft[0];
-    f32x4 U = zero4(), U2 = zero4();
-#pragma unroll
-    for (int s2 = 0; s2 < 2; ++s2) {
-      if (s2 <= (wave >> 1)) {
-        const f16x4 lo = *reinterpret_cast<const f16x4*>(&vsT[l16 * VS + 32 * s2 + 4 * lg]);
-        const f16x4 hi = *reinterpret_cast<const f16x4*>(&vsT[l16 * VS + 32 * s2 + 16 + 4 * lg]);
-        const f16x8 vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-        if (s2 == 0) U = mma_f16(ft[0], vb, U);
-        else U2 = mma_f16(ft[1], vb, U2);
-      }
-    }
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      if (s2 & 1) U2 = mma_f16(fw[s2], sB[s2], U2);
-      else U = mma_f16(fw[s2], sB[s2], U);
-    }
-#pragma unroll
-    for (int j = 0; j < 4; ++j) U[j] += U2[j];
-    ubuf[wave * 64 + lane] = f16x4{(f16)U[0], (f16)U[1], (f16)U[2], (f16)U[3]};
-    // output-side and state-update operands, then Qhat S
-    f16x8 fq[4], fk[4], fm[2];
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) {
-      fq[s2] = lfrag(slot, REC_QHAT, wave * 4 + s2);
-      fk[s2] = lfrag(slot, REC_KBAR, (2 * wave + (s2 >> 1)) * 2 + (s2 & 1));
-    }
-    fm[0] = lfrag(slot, REC_M, wave * 2);
-    fm[1] = wave >= 2 ? lfrag(slot, REC_M, wave * 2 + 1) : fm[0];
-    float4 gl[2];
-#pragma unroll
-    for (int i = 0; i < 2; ++i)
-      gl[i] = *reinterpret_cast<const float4*>(slot + REC_GL + 4 * (SUB * (2 * wave + i) + 4 * lg));
+    for (int s2 = 0; s2 < 4; ++s2) sB[s2] = sbuf[s2 * 64 + lane];
     f32x4 OQ = zero4(), OQ2 = zero4();
 #pragma unroll
     for (int s2 = 0; s2 < 4; ++s2) {
-      if (s2 & 1) OQ2 = mma_f16(fq[s2], sB[s2], OQ2);
-      else OQ = mma_f16(fq[s2], sB[s2], OQ);
+      if (s2 & 1) OQ2 = mma_f16(F.q[s2], sB[s2], OQ2);
+      else OQ = mma_f16(F.q[s2], sB[s2], OQ);
     }
-    __syncthreads();  // B: U visible; this chunk's slot may be refilled
-    // S <- Diag(exp(Gamma_L)) S + Kbar^T U first (it feeds the next chunk),
-    // then O = scale (Qhat S + M U)
+    __syncthreads();  // B: U_c published
     f16x8 uB[2];
 #pragma unroll
     for (int s2 = 0; s2 < 2; ++s2) {
       const f16x4 a = ubuf[(2 * s2) * 64 + lane], b = ubuf[(2 * s2 + 1) * 64 + lane];
       uB[s2] = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
     }
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      // two independent products, summed: one matrix-core latency on the chain
-      const f32x4 a = mma_f16(fk[2 * i], uB[0], f32x4{gl[i].x * S[i][0], gl[i].y * S[i][1], gl[i].z * S[i][2], gl[i].w * S[i][3]});
-      const f32x4 b = mma_f16(fk[2 * i + 1], uB[1], zero4());
-      S[i] = f32x4{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
-    }
-    f32x4 O = OQ;
-#pragma unroll
-    for (int j = 0; j < 4; ++j) O[j] += OQ2[j];
-    O = mma_f16(fm[0], uB[0], O);
-    if (wave >= 2) O = mma_f16(fm[1], uB[1], O);
+    f32x4 O = f32x4{OQ[0] + OQ2[0], OQ[1] + OQ2[1], OQ[2] + OQ2[2], OQ[3] + OQ2[3]};
+    O = mma_f16(F.m[0], uB[0], O);
+    if (tw >= 2) O = mma_f16(F.m[1], uB[1], O);
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const int r = SUB * wave + 4 * lg + j;
+      const int r = SUB * tw + 4 * lg + j;
       // rows past the chunk's end go to a sink, keeping the store unconditional
-      // (a conditional store would make later waits cover all stores)
       uint16_t* dst = r < L ? orow + (size_t)j * row_step : p.sink + lane;
       *dst = f32_to_bf16(p.scale * O[j]);
     }
     orow += (size_t)CH * row_step;
   };
-  uint2 va = make_uint2(0u, 0u), vb = make_uint2(0u, 0u);
-  if (nch > 0) va = load_v(0);
-  __builtin_amdgcn_s_waitcnt(0);
-  for (int c = 0; c < nch; ++c) {
-    cstep(c, va, vb);
-    va = vb;
+  OutFrags f0, f1, f2;
+  if (nch > 0) {
+    load(f0, 0);
+    load(f1, min(1, last));
   }
-  if (p.s1) {
-#pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      const int k0 = SUB * (2 * wave + i) + 4 * lg;
-      StateIO<StT>::store(p.s1, sbase + k0, S[i]);
-    }
+  __builtin_amdgcn_s_waitcnt(0);
+  for (int c = 0; c < nch; c += 3) {
+    load(f2, min(c + 2, last));
+    step(f0, c);
+    if (c + 1 >= nch) break;
+    load(f0, min(c + 3, last));
+    step(f1, c + 1);
+    if (c + 2 >= nch) break;
+    load(f1, min(c + 4, last));
+    step(f2, c + 2);
   }
 }
 
@@ -557,16 +526,9 @@ void launch_recur(const RecurParams& p, bool bf16_state, hipStream_t stream) {
   }
   const int g = recur_grid(p.n_chains);
   dim3 grid(g);
-  if (g <= cus) {  // one workgroup per CU: LDS ring with loader waves
-    static bool attr[2] = {false, false};
-    if (!attr[bf16_state]) {
-      (void)hipFuncSetAttribute(bf16_state ? reinterpret_cast<const void*>(&recur_lds_kernel<uint16_t>)
-                                           : reinterpret_cast<const void*>(&recur_lds_kernel<float>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, LR_LDS);
-      attr[bf16_state] = true;
-    }
-    if (bf16_state) recur_lds_kernel<uint16_t><<<grid, LR_THREADS, LR_LDS, stream>>>(p);
-    else recur_lds_kernel<float><<<grid, LR_THREADS, LR_LDS, stream>>>(p);
+  if (g <= cus) {  // one workgroup per CU: chain and output waves
+    if (bf16_state) recur_split_kernel<uint16_t><<<grid, 512, 0, stream>>>(p);
+    else recur_split_kernel<float><<<grid, 512, 0, stream>>>(p);
     return;
   }
   const bool deep = g <= 4 * cus;  // few chains: latency per chain matters most
