@@ -80,6 +80,20 @@ def test_many_chains_shallow_pipeline(state_dtype):
     check(inp, state_dtype=state_dtype, what="many chains %s" % state_dtype)
 
 
+@pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16])
+def test_two_column_tiles_per_workgroup(state_dtype):
+    # 6 rows x 8 heads = 48 chains: too many for one 16-column tile per CU,
+    # few enough for 32-column workgroups (one per CU)
+    inp = make_inputs(6, 150, 8, 4, state_std=0.05, seed=25, A_log=(-4.0, -1.0))
+    check(inp, state_dtype=state_dtype, what="two column tiles %s" % state_dtype)
+
+
+def test_two_column_tiles_packed():
+    lens = [1, 64, 300, 65, 0, 129]
+    inp = make_inputs(1, sum(lens), 8, 2, state_std=0.05, N=len(lens), lengths=lens, seed=26)
+    check(inp, what="two column tiles packed %s" % lens)
+
+
 def test_packed_sequences_edge_lengths():
     lens = [19, 64, 1, 130, 0, 77, 65, 63]
     inp = make_inputs(1, sum(lens), 3, 3, state_std=0.02, N=len(lens), lengths=lens, seed=15)
