@@ -138,7 +138,7 @@ def traffic_from(root, copy_bytes, workload="kda_dense"):
     out = {"_calibration": {"copy_bytes": copy_bytes, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
                             "fetch_factor": kf, "write_factor": kw}}
     rec = {}
-    for kern, tag in (("kda_chunk_local", "chunk_local_kernel"), ("kda_recur", "recur_kernel"),
+    for kern, tag in (("kda_chunk_local", "chunk_local_kernel"), ("kda_recur", "recur_"),
                       ("kda_table", "table_kernel")):
         f = _per_dispatch_kib(run_f, "FETCH_SIZE", lambda k, t=tag: t in k)
         w = _per_dispatch_kib(run_w, "WRITE_SIZE", lambda k, t=tag: t in k)
