@@ -226,6 +226,51 @@ def time_workload(name, steps, warmup):
     return ms, per_kernel, inp, w, pct
 
 
+def run_sweep(steps, warmup):
+    """Grouped-value-head sweep: every head shape x sequence pattern of the
+    forward table on the FlashQLA H200 results page, timed as packed calls.
+    Prints one JSON line with a row per (shape, pattern)."""
+    import torch
+    from chunked_gated_delta_10_amd import kda
+    from chunked_gated_delta_10_amd.inputs import SWEEP_HEAD_SHAPES, SWEEP_PATTERNS, cu_seqlens_from_lengths, \
+        sweep_inputs
+    sys.path.insert(0, os.path.join(ROOT, "tests"))
+    import kda_util as U
+    rows = []
+    for h_qk, h_v in SWEEP_HEAD_SHAPES:
+        inp = sweep_inputs(h_qk, h_v)
+        d = U.to_device(inp)
+        print("shape h_qk=%d h_v=%d" % (h_qk, h_v), file=sys.stderr, flush=True)
+        for pname, lens in SWEEP_PATTERNS.items():
+            T = sum(lens)
+            cu = torch.from_numpy(cu_seqlens_from_lengths(lens)).cuda()
+            q, k, v, g, b = (d[n][:, :T] for n in ("q", "k", "v", "g_raw", "b"))
+            out = torch.empty((1, T, h_v, D), dtype=torch.bfloat16, device="cuda")
+            fin = torch.empty((len(lens), h_v, D, D), dtype=torch.float32, device="cuda")
+            ws = torch.empty(kda.workspace_bytes(1, T, h_qk, h_v, len(lens)), dtype=torch.uint8, device="cuda")
+
+            def step():
+                kda.fwd_varlen(q, k, v, g, b, d["A_log"], cu, scale=inp["scale"], final_state=fin, out=out,
+                               workspace=ws)
+            for _ in range(warmup):
+                step()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            rows.append({"h_qk": h_qk, "h_v": h_v, "seqlens": pname, "tokens": T, "ms": round(ms, 4),
+                         "tokens_per_s": round(T / (ms * 1e-3), 1)})
+            del out, fin, ws
+        del d
+        torch.cuda.empty_cache()
+    print(json.dumps({"sweep": "grouped value heads, scalar decay, K=V=128, no initial state, fp32 final state",
+                      "steps": steps, "warmup": warmup, "rows": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -240,6 +285,8 @@ def main():
                     help="write profiles/traffic.json from rocprofv3 counter runs under DIR (no GPU needed)")
     ap.add_argument("--copy-bytes", type=int, default=1024 * 1024 * 1024,
                     help="size of the calibration copy used with --traffic-from")
+    ap.add_argument("--sweep", action="store_true",
+                    help="only run the grouped-value-head sweep (head shapes x sequence patterns)")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(args.traffic_from, args.copy_bytes)
@@ -258,6 +305,9 @@ def main():
         return
     from chunked_gated_delta_10_amd import kda
     kda.load()
+    if args.sweep:
+        run_sweep(args.steps, args.warmup)
+        return
 
     name = "kda_dense"
     ms, per_kernel, inp, w, pct = time_workload(name, args.steps, args.warmup)

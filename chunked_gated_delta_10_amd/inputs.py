@@ -155,3 +155,23 @@ def workload_inputs(name: str) -> dict:
     w = WORKLOADS[name]
     return make_inputs(w.B, w.T, w.H, w.H_qk, gate_per_channel=w.gate_per_channel, A_log=w.A_log,
                        state_std=w.state_std, N=w.N, seed=w.seed, K=w.K, V=w.V, decode=w.decode)
+
+
+# Grouped-value-head sweep (the forward table of the FlashQLA H200 benchmark
+# results page): head shapes (h_qk, h_v) and packed sequence patterns.  Every
+# row uses the scalar per-token decay g = -softplus(N(0,1)) (A_log = 0), no
+# initial state, and is drawn once per head shape at 32768 tokens; a pattern
+# uses the first sum(lengths) tokens.
+SWEEP_HEAD_SHAPES = [(2, 8), (4, 16), (8, 24), (8, 32), (16, 16), (16, 32), (16, 48), (16, 64)]
+SWEEP_PATTERNS: Dict[str, Tuple[int, ...]] = {
+    "1x2048": (2048,), "1x4096": (4096,), "1x8192": (8192,), "1x16384": (16384,), "1x32768": (32768,),
+    "28672+4096": (28672, 4096), "16384+16384": (16384, 16384), "4096+28672": (4096, 28672),
+    "12288+4096": (12288, 4096), "1024+7168": (1024, 7168),
+    "8192x4": (8192,) * 4, "4096x8": (4096,) * 8, "2048x4": (2048,) * 4, "1024x8": (1024,) * 8,
+}
+SWEEP_TOKENS = 32768
+
+
+def sweep_inputs(h_qk: int, h_v: int, seed: int = 2000) -> dict:
+    """Inputs of one head shape of the grouped-head sweep (B=1, T=32768)."""
+    return make_inputs(1, SWEEP_TOKENS, h_v, h_qk, gate_per_channel=False, A_log=0.0, seed=seed + 100 * h_qk + h_v)

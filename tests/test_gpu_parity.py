@@ -12,7 +12,8 @@ import pytest
 import torch
 
 from chunked_gated_delta_10_amd import kda
-from chunked_gated_delta_10_amd.inputs import WORKLOADS, make_inputs, workload_inputs
+from chunked_gated_delta_10_amd.inputs import (SWEEP_HEAD_SHAPES, SWEEP_PATTERNS, WORKLOADS, make_inputs,
+                                               sweep_inputs, workload_inputs)
 import kda_util as U
 
 pytestmark = pytest.mark.gpu
@@ -74,8 +75,8 @@ def test_bf16_state():
 
 @pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16])
 def test_many_chains_shallow_pipeline(state_dtype):
-    # 40 rows x 8 heads = 320 chains -> 2560 value-tile workgroups, past the
-    # grid size where the recurrence switches to its two-stage fragment ring
+    # 40 rows x 8 heads = 320 chains -> 1280 two-tile recurrence workgroups,
+    # several rounds of one workgroup per CU
     inp = make_inputs(40, 150, 8, 4, state_std=0.05, seed=24, A_log=(-4.0, -1.0))
     check(inp, state_dtype=state_dtype, what="many chains %s" % state_dtype)
 
@@ -83,7 +84,7 @@ def test_many_chains_shallow_pipeline(state_dtype):
 @pytest.mark.parametrize("state_dtype", [torch.float32, torch.bfloat16])
 def test_two_column_tiles_per_workgroup(state_dtype):
     # 6 rows x 8 heads = 48 chains: too many for one 16-column tile per CU,
-    # few enough for 32-column workgroups (one per CU)
+    # so 32-column workgroups, all resident at once
     inp = make_inputs(6, 150, 8, 4, state_std=0.05, seed=25, A_log=(-4.0, -1.0))
     check(inp, state_dtype=state_dtype, what="two column tiles %s" % state_dtype)
 
@@ -92,6 +93,15 @@ def test_two_column_tiles_packed():
     lens = [1, 64, 300, 65, 0, 129]
     inp = make_inputs(1, sum(lens), 8, 2, state_std=0.05, N=len(lens), lengths=lens, seed=26)
     check(inp, what="two column tiles packed %s" % lens)
+
+
+@pytest.mark.parametrize("h_qk,h_v", SWEEP_HEAD_SHAPES)
+def test_grouped_head_shapes_packed(h_qk, h_v):
+    # every head shape of the grouped-head sweep, scalar decay, packed A+B+C
+    lens = [150, 41, 64]
+    inp = make_inputs(1, sum(lens), h_v, h_qk, gate_per_channel=False, A_log=0.0, N=len(lens), lengths=lens,
+                      seed=30 + h_v + h_qk)
+    check(inp, what="grouped heads h_qk=%d h_v=%d packed %s" % (h_qk, h_v, lens))
 
 
 def test_packed_sequences_edge_lengths():
@@ -243,6 +253,22 @@ def test_full_size_workload_sampled_chains(name):
     else:
         picks = [(0, 0), (C - 1, w.H - 1), (0, w.H // 2 + 1)]
     check(inp, what=name + " sampled chains", chain_mask=sampled_mask(C, w.H, picks))
+
+
+@pytest.mark.parametrize("h_qk,h_v,pattern", [(2, 8, "28672+4096"), (16, 64, "8192x4")])
+def test_full_size_sweep_rows_sampled_chains(h_qk, h_v, pattern):
+    # two rows of the grouped-head sweep at their full size, in the launch
+    # configuration the sweep times; the oracle checks sampled chains
+    lens = SWEEP_PATTERNS[pattern]
+    full = sweep_inputs(h_qk, h_v)
+    T = sum(lens)
+    inp = dict(full)
+    for n in ("q", "k", "v", "g_raw", "b"):
+        inp[n] = np.ascontiguousarray(full[n][:, :T])
+    inp["cu_seqlens"] = np.concatenate([[0], np.cumsum(lens)]).astype(np.int32)
+    picks = [(0, 0), (len(lens) - 1, h_v - 1)]
+    check(inp, what="sweep h_qk=%d h_v=%d %s sampled chains" % (h_qk, h_v, pattern),
+          chain_mask=sampled_mask(len(lens), h_v, picks))
 
 
 def test_full_size_decode():

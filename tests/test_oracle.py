@@ -386,6 +386,14 @@ def test_varlen_length_recipe():
     assert lens.sum() == 16384 and lens.min() == 19 and lens.max() == 3147 and len(lens) == 20
 
 
+def test_grouped_head_sweep_recipe():
+    from chunked_gated_delta_10_amd.inputs import SWEEP_HEAD_SHAPES, SWEEP_PATTERNS, SWEEP_TOKENS
+    for h_qk, h_v in SWEEP_HEAD_SHAPES:
+        assert h_v % h_qk == 0
+    for lens in SWEEP_PATTERNS.values():
+        assert 0 < sum(lens) <= SWEEP_TOKENS and min(lens) > 0
+
+
 def test_bf16_rounding_is_nearest_even():
     x = np.array([1.0, 1.00390625, 1.01171875, -3.0e-3, 65504.0, 1e-30], dtype=np.float32)
     bits = bf16_bits(x)
