@@ -285,6 +285,9 @@ def main():
                     help="write profiles/traffic.json from rocprofv3 counter runs under DIR (no GPU needed)")
     ap.add_argument("--copy-bytes", type=int, default=1024 * 1024 * 1024,
                     help="size of the calibration copy used with --traffic-from")
+    ap.add_argument("--only", metavar="WORKLOAD",
+                    help="only time one workload (kda_tiny, kda_dense, kda_varlen, gdn_gva, kda_decode) and print "
+                         "its per-kernel averages; for profiling runs")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the grouped-value-head sweep (head shapes x sequence patterns)")
     args = ap.parse_args()
@@ -307,6 +310,11 @@ def main():
     kda.load()
     if args.sweep:
         run_sweep(args.steps, args.warmup)
+        return
+    if args.only:
+        ms, per_kernel, _, w, pct = time_workload(args.only, args.steps, args.warmup)
+        print(json.dumps({"workload": args.only, "ms_per_step": round(ms, 4), "step_ms_percentiles": pct,
+                          "kernels_avg_ms": {k: round(v, 4) for k, v in per_kernel.items()}}), flush=True)
         return
 
     name = "kda_dense"
