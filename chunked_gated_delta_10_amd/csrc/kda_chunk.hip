@@ -91,14 +91,13 @@ __device__ __forceinline__ float row_prefix_sum(float x) {
   x += dpp0<0x118>(x);
   return x;
 }
-// sum over the lanes after this one (0 for the last lane of the row)
-__device__ __forceinline__ float row_suffix_sum_excl(float x) {
-  float y = dpp0<0x101>(x);  // row_shl:1
-  y += dpp0<0x101>(y);
-  y += dpp0<0x102>(y);
-  y += dpp0<0x104>(y);
-  y += dpp0<0x108>(y);
-  return y;
+// Sum over the lanes after this one (0 for the last lane of the row), from
+// the inclusive prefix sum: the row total (lane 15's prefix, broadcast with
+// row_newbcast:15) minus this lane's prefix, one v_sub_f32_dpp.
+__device__ __forceinline__ float row_suffix_from_prefix(float prefix) {
+  const float total =
+      __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, prefix), 0x15F, 0xF, 0xF, false));
+  return total - prefix;
 }
 
 __device__ __forceinline__ void unpack4(uint2 w, float* out) {
@@ -248,8 +247,8 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
           }
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
-            S[q] = row_suffix_sum_excl(P[q]);  // log2 kappa
-            P[q] = row_prefix_sum(P[q]);       // log2 rho
+            P[q] = row_prefix_sum(P[q]);           // log2 rho
+            S[q] = row_suffix_from_prefix(P[q]);  // log2 kappa
           }
           float Dv[8];
 #pragma unroll
