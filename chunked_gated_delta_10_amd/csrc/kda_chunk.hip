@@ -41,6 +41,8 @@
 // products and the 64 x 64 matrices A and T go through LDS (~69 KB), so two
 // workgroups share a CU and hide each other's latencies (one waits on its
 // loads while the other computes).  One workgroup per (chunk, head).
+#include <type_traits>
+
 #include "kda_device.h"
 #include "kda_kernels.h"
 
@@ -161,7 +163,7 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
   float* ROW = reinterpret_cast<float*>(smem + L_ROW);
   int* FLAG = reinterpret_cast<int*>(smem + L_FLAG);
 
-  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
   const int n = wave;              // sub-chunk of this wave
   const int r = SUB * n + l16;     // this lane's token row in the chunk
@@ -389,88 +391,99 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
       }
       const float EGr = PER_CHANNEL ? 0.f : exp2f(Gr * LOG2E);
       const float EGLr = PER_CHANNEL ? 0.f : exp2f((GL - Gr) * LOG2E);
-#pragma unroll
-      for (int s = 0; s < 4; ++s) {
-        float ep[8], eg[8], lam[8];
-        float Dm[4][8];
-        if (PER_CHANNEL) {
-#pragma unroll
-          for (int m = 0; m < NSUB; ++m) {
-            const float4 lo = *reinterpret_cast<const float4*>(&DS[m * HD + 32 * s + 4 * lg]);
-            const float4 hi = *reinterpret_cast<const float4*>(&DS[m * HD + 32 * s + 16 + 4 * lg]);
-            Dm[m][0] = lo.x; Dm[m][1] = lo.y; Dm[m][2] = lo.z; Dm[m][3] = lo.w;
-            Dm[m][4] = hi.x; Dm[m][5] = hi.y; Dm[m][6] = hi.z; Dm[m][7] = hi.w;
-          }
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            float a1 = 1.f, a2 = 1.f;
-#pragma unroll
+      // The slice loop is instantiated per sub-chunk index N (wave-uniform), so
+      // the decay products and the (N, a < N) blocks resolve at compile time.
+      auto step2 = [&](auto Nc) {
+        constexpr int N = decltype(Nc)::value;
+  #pragma unroll
+        for (int s = 0; s < 4; ++s) {
+          float ep[8], eg[8], lam[8];
+          float Dm[4][8];
+          if (PER_CHANNEL) {
+  #pragma unroll
             for (int m = 0; m < NSUB; ++m) {
-              if (m < n) a1 *= Dm[m][q];
-              if (m > n) a2 *= Dm[m][q];
+              const float4 lo = *reinterpret_cast<const float4*>(&DS[m * HD + 32 * s + 4 * lg]);
+              const float4 hi = *reinterpret_cast<const float4*>(&DS[m * HD + 32 * s + 16 + 4 * lg]);
+              Dm[m][0] = lo.x; Dm[m][1] = lo.y; Dm[m][2] = lo.z; Dm[m][3] = lo.w;
+              Dm[m][4] = hi.x; Dm[m][5] = hi.y; Dm[m][6] = hi.z; Dm[m][7] = hi.w;
             }
-            ep[q] = a1;
-            eg[q] = a2;
-            lam[q] = 1.f;
-          }
-        } else {
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            ep[q] = EGr;
-            eg[q] = EGLr;
-            lam[q] = 1.f;
-          }
-        }
-        // Qhat fragment (n, s) straight from registers
-        {
-          float v[8];
-#pragma unroll
-          for (int q = 0; q < 8; ++q) v[q] = Q[8 * s + q] * ep[q];
-          store_frag(rec, REC_QHAT, n * 4 + s, lane, v);
-        }
-        // Khat and Kbar of this sub-chunk, transposed by selection products
-        {
-          f16x8 kh, kb;
-#pragma unroll
-          for (int q = 0; q < 8; ++q) {
-            kh[q] = (f16)(X[8 * s + q] * ep[q]);
-            kb[q] = (f16)((PER_CHANNEL ? Y[8 * s + q] : X[8 * s + q]) * eg[q]);
-          }
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int kt = 2 * s + hh;  // key tile
-            const f32x4 th = mma_f16(kh, sel[hh], zero4());
-            const f32x4 tb = mma_f16(kb, sel[hh], zero4());
-            const f16x4 th4 = {(f16)th[0], (f16)th[1], (f16)th[2], (f16)th[3]};
-            const f16x4 tb4 = {(f16)tb[0], (f16)tb[1], (f16)tb[2], (f16)tb[3]};
-            *reinterpret_cast<f16x4*>(KHb + ((kt * 2 + (n >> 1)) * 64 + lane) * 16 + (n & 1) * 8) = th4;
-            *reinterpret_cast<f16x4*>(rec + REC_KBAR + (kt * 2 + (n >> 1)) * FRAG_BYTES + lane * 16 + (n & 1) * 8) = tb4;
-          }
-        }
-        // blocks (n, a), a < n: (X lam) Y_a^T and Y_a (Q lam)^T
-#pragma unroll
-        for (int a = 2; a >= 0; --a) {
-          if (a < n) {
-            if (PER_CHANNEL && a + 1 < n) {
-#pragma unroll
-              for (int q = 0; q < 8; ++q) lam[q] *= Dm[a + 1][q];
-            }
-            f16x8 xl, ql;
-#pragma unroll
+  #pragma unroll
             for (int q = 0; q < 8; ++q) {
-              xl[q] = (f16)(X[8 * s + q] * lam[q]);
-              ql[q] = (f16)(Q[8 * s + q] * lam[q]);
+              float a1 = 1.f, a2 = 1.f;
+  #pragma unroll
+              for (int m = 0; m < NSUB; ++m) {
+                if (m < N) a1 *= Dm[m][q];
+                if (m > N) a2 *= Dm[m][q];
+              }
+              ep[q] = a1;
+              eg[q] = a2;
+              lam[q] = 1.f;
             }
-            const f16x8 ya = YB[(a * 4 + s) * 64 + lane];
-            accA[a] = mma_f16(xl, ya, accA[a]);
-            accM[a] = mma_f16(ya, ql, accM[a]);
+          } else {
+  #pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              ep[q] = EGr;
+              eg[q] = EGLr;
+              lam[q] = 1.f;
+            }
+          }
+          // Qhat fragment (N, s) straight from registers
+          {
+            float v[8];
+  #pragma unroll
+            for (int q = 0; q < 8; ++q) v[q] = Q[8 * s + q] * ep[q];
+            store_frag(rec, REC_QHAT, N * 4 + s, lane, v);
+          }
+          // Khat and Kbar of this sub-chunk, transposed by selection products
+          {
+            f16x8 kh, kb;
+  #pragma unroll
+            for (int q = 0; q < 8; ++q) {
+              kh[q] = (f16)(X[8 * s + q] * ep[q]);
+              kb[q] = (f16)((PER_CHANNEL ? Y[8 * s + q] : X[8 * s + q]) * eg[q]);
+            }
+  #pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int kt = 2 * s + hh;  // key tile
+              const f32x4 th = mma_f16(kh, sel[hh], zero4());
+              const f32x4 tb = mma_f16(kb, sel[hh], zero4());
+              const f16x4 th4 = {(f16)th[0], (f16)th[1], (f16)th[2], (f16)th[3]};
+              const f16x4 tb4 = {(f16)tb[0], (f16)tb[1], (f16)tb[2], (f16)tb[3]};
+              *reinterpret_cast<f16x4*>(KHb + ((kt * 2 + (N >> 1)) * 64 + lane) * 16 + (N & 1) * 8) = th4;
+              *reinterpret_cast<f16x4*>(rec + REC_KBAR + (kt * 2 + (N >> 1)) * FRAG_BYTES + lane * 16 + (N & 1) * 8) = tb4;
+            }
+          }
+          // blocks (N, a), a < N: (X lam) Y_a^T and Y_a (Q lam)^T
+  #pragma unroll
+          for (int a = 2; a >= 0; --a) {
+            if (a < N) {
+              if (PER_CHANNEL && a + 1 < N) {
+  #pragma unroll
+                for (int q = 0; q < 8; ++q) lam[q] *= Dm[a + 1][q];
+              }
+              f16x8 xl, ql;
+  #pragma unroll
+              for (int q = 0; q < 8; ++q) {
+                xl[q] = (f16)(X[8 * s + q] * lam[q]);
+                ql[q] = (f16)(Q[8 * s + q] * lam[q]);
+              }
+              const f16x8 ya = YB[(a * 4 + s) * 64 + lane];
+              accA[a] = mma_f16(xl, ya, accA[a]);
+              accM[a] = mma_f16(ya, ql, accM[a]);
+            }
+          }
+          if (!PER_CHANNEL) {  // scalar mode: the diagonal block is an fp16 Gram block too
+            const f16x8 xh = to_f16x8(&X[8 * s]);
+            accA_d = mma_f16(xh, xh, accA_d);
+            accM_d = mma_f16(xh, to_f16x8(&Q[8 * s]), accM_d);
           }
         }
-        if (!PER_CHANNEL) {  // scalar mode: the diagonal block is an fp16 Gram block too
-          const f16x8 xh = to_f16x8(&X[8 * s]);
-          accA_d = mma_f16(xh, xh, accA_d);
-          accM_d = mma_f16(xh, to_f16x8(&Q[8 * s]), accM_d);
-        }
+      };
+      switch (n) {
+        case 0: step2(std::integral_constant<int, 0>()); break;
+        case 1: step2(std::integral_constant<int, 1>()); break;
+        case 2: step2(std::integral_constant<int, 2>()); break;
+        default: step2(std::integral_constant<int, 3>()); break;
       }
       if (tid < HD) {  // exp(Gamma_L) per key
         const float gl = PER_CHANNEL ? DS[tid] * DS[HD + tid] * DS[2 * HD + tid] * DS[3 * HD + tid]
