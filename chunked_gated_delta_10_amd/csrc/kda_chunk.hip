@@ -193,6 +193,9 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
     if (len > 0) {  // uniform over the workgroup
       Pref cur;
       load_rows<PER_CHANNEL>(cur, p, ce_cur, h, wave, lane);
+      // keep every input load ahead of the first use, so the three streams
+      // (q, k, g) are in flight together rather than g after q and k arrive
+      __builtin_amdgcn_sched_barrier(0);
       const float alog_cur = A_log[h];
       uint8_t* rec = p.rec + ((size_t)e * p.H + h) * REC_BYTES;
       const bool live = r < len;
