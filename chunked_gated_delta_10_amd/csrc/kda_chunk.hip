@@ -53,7 +53,7 @@ namespace {
 constexpr int NT = 256;  // threads per workgroup (4 waves)
 constexpr int MS = 68;   // row stride (floats) of the 64 x 64 matrices
 constexpr float LOG2E = 1.4426950408889634f;
-constexpr float TINY_LOG2 = -100.f;  // log2 of the smallest sub-chunk decay the fast diagonal path takes
+constexpr float TINY_D = 7.888609052210118e-31f;  // 2^-100: the smallest sub-chunk decay the fast diagonal path takes
 
 // LDS layout (bytes)
 constexpr int L_YB = 0;                          // Y = kn*kappa (fp16) of sub-chunks 0..2 [3][4 slices][64] f16x8
@@ -266,7 +266,7 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
             Q[v] = qn[q] * rho;
             Y[v] = kn[q] * kap;
             Dv[q] = rho * kap;
-            tiny |= !(P[q] + S[q] >= TINY_LOG2);
+            tiny |= !(Dv[q] >= TINY_D);
             // diagonal block on fp32 matrix cores: the lane's value is the
             // A/B operand of the 16x16x4 product for key (s, q)
             if (q & 1) {

@@ -173,11 +173,12 @@ __device__ __forceinline__ void gate_decay(float x, float a, float& d, float& g)
 }
 
 // log2 of the decay factor: -a * softplus(x) / ln 2 (same evaluation as
-// above, without a branch: the clamped exponent keeps the unused side finite).
+// above, without a branch: for x > 20 the select drops the log-exp side,
+// which may then be +inf but never NaN for a finite x).
 __device__ __forceinline__ float gate_log2(float x, float a) {
   constexpr float LOG2E = 1.4426950408889634f;
   const float y = x * LOG2E;
-  const float t = __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(fminf(y, 64.f)));
+  const float t = __builtin_amdgcn_logf(1.f + __builtin_amdgcn_exp2f(y));
   return -a * (x > 20.f ? y : t);
 }
 
