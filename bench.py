@@ -31,7 +31,7 @@ KERNEL_SOURCES = ["chunked_gated_delta_10_amd/csrc/" + f for f in
                   ("kda_chunk.hip", "kda_recur.hip", "kda_table.hip", "kda_decode.hip", "kda_device.h", "kda_kernels.h")]
 
 
-def algorithmic_bytes(w, with_state=True):
+def algorithmic_bytes(w, with_state=True, state_bytes=4):
     """Each input read once and each output written once (bytes), split by kernel."""
     tok = w.B * w.T
     qk = 2 * tok * w.H_qk * D * 2
@@ -40,7 +40,7 @@ def algorithmic_bytes(w, with_state=True):
     v = tok * w.H * D * 2
     out = tok * w.H * D * 2
     C_ = w.N if w.N else w.B
-    state = C_ * w.H * D * D * 4
+    state = C_ * w.H * D * D * state_bytes
     s_in = state if w.state_std is not None else 0
     s_out = state if with_state else 0
     return {"kda_chunk_local": qk + g + beta + w.H * 4, "kda_recur": v + out + s_in + s_out}
@@ -171,8 +171,9 @@ def cpu_baseline(inp, w, tokens):
                       % (w.name, w.B * w.H, w.B, w.H, tokens, w.T, dt)}
 
 
-def time_workload(name, steps, warmup):
-    """Returns (ms per step, per-kernel {name: avg ms}, inputs, workload)."""
+def time_workload(name, steps, warmup, bf16_state=False):
+    """Returns (ms per step, per-kernel {name: avg ms}, inputs, workload, percentiles).  With
+    bf16_state the initial and final states are bf16 instead of fp32."""
     import torch
     from chunked_gated_delta_10_amd import kda
     from chunked_gated_delta_10_amd.inputs import WORKLOADS, workload_inputs
@@ -180,7 +181,8 @@ def time_workload(name, steps, warmup):
     import kda_util as U
     w = WORKLOADS[name]
     inp = workload_inputs(name)
-    d = U.to_device(inp)
+    sdt = torch.bfloat16 if bf16_state else torch.float32
+    d = U.to_device(inp, sdt)
     if w.decode:
         st = d["initial_state"]
         out = torch.empty((w.B, w.H, D), dtype=torch.bfloat16, device="cuda")
@@ -190,7 +192,7 @@ def time_workload(name, steps, warmup):
     else:
         C_ = w.N if w.N else w.B
         out = torch.empty((w.B, w.T, w.H, D), dtype=torch.bfloat16, device="cuda")
-        fin = torch.empty((C_, w.H, D, D), dtype=torch.float32, device="cuda")
+        fin = torch.empty((C_, w.H, D, D), dtype=sdt, device="cuda")
         ws = torch.empty(kda.workspace_bytes(w.B, w.T, w.H_qk, w.H, w.N), dtype=torch.uint8, device="cuda")
         if w.N:
             def step():
@@ -353,9 +355,11 @@ def main():
     }
     if not args.no_extra:
         extra = {}
-        for other in ("kda_varlen", "gdn_gva", "kda_decode"):
-            oms, opk, _, ow, _ = time_workload(other, max(10, args.steps // 5), 3)
-            ab = algorithmic_bytes(ow)
+        for other in ("kda_varlen", "gdn_gva", "kda_decode", "kda_dense_bf16_state"):
+            bf16_state = other.endswith("_bf16_state")
+            oms, opk, _, ow, _ = time_workload(other.replace("_bf16_state", ""), max(10, args.steps // 5), 3,
+                                               bf16_state=bf16_state)
+            ab = algorithmic_bytes(ow, state_bytes=2 if bf16_state else 4)
             tok = ow.B if ow.decode else ow.B * ow.T
             tot = sum(ab.values())
             extra[other] = {"ms_per_step": round(oms, 4), "tokens_per_s": round(tok / (oms * 1e-3), 1),
