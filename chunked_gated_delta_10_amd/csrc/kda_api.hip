@@ -173,6 +173,8 @@ kda_status run_forward(const FwdArgs& a) {
   if (a.s1 && !aligned16(a.s1)) return fail(KDA_ERR_ALIGN, "final_state is not 16-byte aligned");
   if (a.cu && (reinterpret_cast<uintptr_t>(a.cu) & 3u)) return fail(KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
   const int n_entries = a.cu ? cdiv(a.T, kda::CH) + a.n_seqs : a.n_seqs * cdiv(a.T, kda::CH);
+  if ((long)n_entries * a.H >= (1L << 31))
+    return fail(KDA_ERR_SHAPE, "problem too large (chunks x heads must fit in int32)");
   const Layout L = layout(a.n_seqs, n_entries, a.H);
   if (!a.ws) return fail(KDA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
   if (a.ws_bytes < L.total)

@@ -61,7 +61,8 @@ extern "C" {
 typedef enum {
   KDA_OK = 0,
   KDA_ERR_NULL = 1,                  /* a required pointer is NULL */
-  KDA_ERR_SHAPE = 2,                 /* a size is negative, K or V != 128, H % H_qk != 0, ... */
+  KDA_ERR_SHAPE = 2,                 /* a size is negative, K or V != 128, H % H_qk != 0, or tokens,
+                                        sequences x H or chunks x H do not fit in int32 */
   KDA_ERR_DTYPE = 3,                 /* unknown state dtype */
   KDA_ERR_STATE_DTYPE_MISMATCH = 4,  /* initial and final state dtypes differ */
   KDA_ERR_WORKSPACE = 5,             /* workspace NULL or smaller than kda_fwd_workspace_bytes() */
