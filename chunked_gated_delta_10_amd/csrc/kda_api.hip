@@ -137,6 +137,7 @@ struct FwdArgs {
   void* ws;
   size_t ws_bytes;
   hipStream_t stream;
+  bool delta;         // false: decay-only linear attention (beta unused)
 };
 
 kda_status validate_common(const FwdArgs& a) {
@@ -162,11 +163,12 @@ kda_status run_forward(const FwdArgs& a) {
   if (a.n_seqs == 0) return ok();
   const long tokens = (long)a.rows * a.T;
   if (tokens > 0) {
-    const void* req[] = {a.q, a.k, a.v, a.g_raw, a.beta, a.A_log, a.out};
-    const char* names[] = {"q", "k", "v", "g_raw", "beta_logits", "A_log", "out"};
-    for (int i = 0; i < 7; ++i)
+    const void* req[] = {a.q, a.k, a.v, a.g_raw, a.A_log, a.out, a.beta};
+    const char* names[] = {"q", "k", "v", "g_raw", "A_log", "out", "beta_logits"};
+    const int n_req = a.delta ? 7 : 6;
+    for (int i = 0; i < n_req; ++i)
       if (!req[i]) return fail(KDA_ERR_NULL, "%s is NULL", names[i]);
-    for (int i = 0; i < 7; ++i)
+    for (int i = 0; i < n_req; ++i)
       if (!aligned16(req[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
   }
   if (a.s0 && !aligned16(a.s0)) return fail(KDA_ERR_ALIGN, "initial_state is not 16-byte aligned");
@@ -207,7 +209,7 @@ kda_status run_forward(const FwdArgs& a) {
     kda::ChunkParams cp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                         static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log, chunks, a.H, a.H_qk, ws + L.rec};
     Timed t(K_CHUNK, a.stream);
-    kda::launch_chunk_local(cp, n_entries, a.gate_per_channel == 1, a.stream);
+    kda::launch_chunk_local(cp, n_entries, a.gate_per_channel == 1, a.delta, a.stream);
   }
   kda::RecurParams rp{ws + L.rec, seqs, order, a.n_seqs * a.H, n_entries, a.H, static_cast<const uint16_t*>(a.v),
                       static_cast<uint16_t*>(a.out), a.s0, a.s1, a.scale,
@@ -222,6 +224,42 @@ kda_status run_forward(const FwdArgs& a) {
     std::fprintf(stderr, "[kda] fwd seqs=%d T=%d H=%d H_qk=%d entries=%d chunk-grid=%dx%d recur-grid=%d state=%s\n",
                  a.n_seqs, a.T, a.H, a.H_qk, n_entries, n_entries, a.H, kda::recur_grid(a.n_seqs * a.H),
                  bf16_state ? "bf16" : "fp32");
+  return ok();
+}
+
+kda_status run_decode(const void* q, const void* k, const void* v, const void* g_raw, const float* beta_logits,
+                      const float* A_log, float scale, int gate_per_channel, void* state, kda_state_dtype state_dtype,
+                      void* out, int B, int H_qk, int H, int K, int V, hipStream_t stream, bool delta) {
+  if (B < 0 || H_qk <= 0 || H <= 0)
+    return fail(KDA_ERR_SHAPE, "sizes must be non-negative with H, H_qk > 0 (got B=%d H_qk=%d H=%d)", B, H_qk, H);
+  if (K != kda::HD || V != kda::HD) return fail(KDA_ERR_SHAPE, "only K = V = 128 is supported (got K=%d V=%d)", K, V);
+  if (H % H_qk != 0) return fail(KDA_ERR_SHAPE, "H (%d) must be a multiple of H_qk (%d)", H, H_qk);
+  if (gate_per_channel != 0 && gate_per_channel != 1)
+    return fail(KDA_ERR_SHAPE, "gate_per_channel must be 0 or 1 (got %d)", gate_per_channel);
+  if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP32)
+    return fail(KDA_ERR_DTYPE, "state dtype %d is not bf16 (1) or fp32 (2)", (int)state_dtype);
+  if ((long)B * H >= (1L << 31)) return fail(KDA_ERR_SHAPE, "problem too large");
+  if (B == 0) return ok();
+  const void* req[] = {q, k, v, g_raw, A_log, state, out, beta_logits};
+  const char* names[] = {"q", "k", "v", "g_raw", "A_log", "state", "out", "beta_logits"};
+  const int n_req = delta ? 8 : 7;
+  for (int i = 0; i < n_req; ++i)
+    if (!req[i]) return fail(KDA_ERR_NULL, "%s is NULL", names[i]);
+  for (int i = 0; i < n_req; ++i)
+    if (!aligned16(req[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  (void)hipGetLastError();
+  kda::DecodeParams p{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
+                      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(g_raw), beta_logits, A_log,
+                      state, static_cast<uint16_t*>(out), H, H_qk, scale};
+  {
+    Timed t(K_DECODE, stream);
+    kda::launch_decode(p, B, state_dtype == KDA_STATE_BF16, gate_per_channel == 1, delta, stream);
+  }
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  if (env_flag("KDA_LOG"))
+    std::fprintf(stderr, "[kda] %s decode B=%d H=%d H_qk=%d grid=%d state=%s\n", delta ? "delta-rule" : "linear",
+                 B, H, H_qk, B * H, state_dtype == KDA_STATE_BF16 ? "bf16" : "fp32");
   return ok();
 }
 
@@ -243,7 +281,7 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const void* g_ra
                    int T, int H_qk, int H, int K, int V, void* workspace, size_t workspace_bytes, void* stream) {
   FwdArgs a{q, k, v, g_raw, beta_logits, A_log, scale, gate_per_channel, initial_state, init_dtype, out,
             final_state, final_dtype, nullptr, B, T, B, H_qk, H, K, V, workspace, workspace_bytes,
-            static_cast<hipStream_t>(stream)};
+            static_cast<hipStream_t>(stream), true};
   return run_forward(a);
 }
 
@@ -255,7 +293,29 @@ kda_status kda_fwd_varlen(const void* q, const void* k, const void* v, const voi
   if (N > 0 && !cu_seqlens) return fail(KDA_ERR_NULL, "cu_seqlens is NULL");
   FwdArgs a{q, k, v, g_raw, beta_logits, A_log, scale, gate_per_channel, initial_state, init_dtype, out,
             final_state, final_dtype, cu_seqlens, N, T, 1, H_qk, H, K, V, workspace, workspace_bytes,
-            static_cast<hipStream_t>(stream)};
+            static_cast<hipStream_t>(stream), true};
+  return run_forward(a);
+}
+
+kda_status kda_la_fwd(const void* q, const void* k, const void* v, const void* g_raw, const float* A_log, float scale,
+                      int gate_per_channel, const void* initial_state, kda_state_dtype init_dtype, void* out,
+                      void* final_state, kda_state_dtype final_dtype, int B, int T, int H_qk, int H, int K, int V,
+                      void* workspace, size_t workspace_bytes, void* stream) {
+  FwdArgs a{q, k, v, g_raw, nullptr, A_log, scale, gate_per_channel, initial_state, init_dtype, out,
+            final_state, final_dtype, nullptr, B, T, B, H_qk, H, K, V, workspace, workspace_bytes,
+            static_cast<hipStream_t>(stream), false};
+  return run_forward(a);
+}
+
+kda_status kda_la_fwd_varlen(const void* q, const void* k, const void* v, const void* g_raw, const float* A_log,
+                             float scale, int gate_per_channel, const void* initial_state, kda_state_dtype init_dtype,
+                             void* out, void* final_state, kda_state_dtype final_dtype, const int32_t* cu_seqlens,
+                             int N, int T, int H_qk, int H, int K, int V, void* workspace, size_t workspace_bytes,
+                             void* stream) {
+  if (N > 0 && !cu_seqlens) return fail(KDA_ERR_NULL, "cu_seqlens is NULL");
+  FwdArgs a{q, k, v, g_raw, nullptr, A_log, scale, gate_per_channel, initial_state, init_dtype, out,
+            final_state, final_dtype, cu_seqlens, N, T, 1, H_qk, H, K, V, workspace, workspace_bytes,
+            static_cast<hipStream_t>(stream), false};
   return run_forward(a);
 }
 
@@ -263,36 +323,15 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
                            const float* A_log, float scale, int gate_per_channel, void* state,
                            kda_state_dtype state_dtype, void* out, int B, int H_qk, int H, int K, int V,
                            void* stream) {
-  if (B < 0 || H_qk <= 0 || H <= 0)
-    return fail(KDA_ERR_SHAPE, "sizes must be non-negative with H, H_qk > 0 (got B=%d H_qk=%d H=%d)", B, H_qk, H);
-  if (K != kda::HD || V != kda::HD) return fail(KDA_ERR_SHAPE, "only K = V = 128 is supported (got K=%d V=%d)", K, V);
-  if (H % H_qk != 0) return fail(KDA_ERR_SHAPE, "H (%d) must be a multiple of H_qk (%d)", H, H_qk);
-  if (gate_per_channel != 0 && gate_per_channel != 1)
-    return fail(KDA_ERR_SHAPE, "gate_per_channel must be 0 or 1 (got %d)", gate_per_channel);
-  if (state_dtype != KDA_STATE_BF16 && state_dtype != KDA_STATE_FP32)
-    return fail(KDA_ERR_DTYPE, "state dtype %d is not bf16 (1) or fp32 (2)", (int)state_dtype);
-  if ((long)B * H >= (1L << 31)) return fail(KDA_ERR_SHAPE, "problem too large");
-  if (B == 0) return ok();
-  const void* req[] = {q, k, v, g_raw, beta_logits, A_log, state, out};
-  const char* names[] = {"q", "k", "v", "g_raw", "beta_logits", "A_log", "state", "out"};
-  for (int i = 0; i < 8; ++i)
-    if (!req[i]) return fail(KDA_ERR_NULL, "%s is NULL", names[i]);
-  for (int i = 0; i < 8; ++i)
-    if (!aligned16(req[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
-  (void)hipGetLastError();
-  kda::DecodeParams p{static_cast<const uint16_t*>(q), static_cast<const uint16_t*>(k),
-                      static_cast<const uint16_t*>(v), static_cast<const uint16_t*>(g_raw), beta_logits, A_log,
-                      state, static_cast<uint16_t*>(out), H, H_qk, scale};
-  {
-    Timed t(K_DECODE, static_cast<hipStream_t>(stream));
-    kda::launch_decode(p, B, state_dtype == KDA_STATE_BF16, gate_per_channel == 1, static_cast<hipStream_t>(stream));
-  }
-  const hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
-  if (env_flag("KDA_LOG"))
-    std::fprintf(stderr, "[kda] decode B=%d H=%d H_qk=%d grid=%d state=%s\n", B, H, H_qk, B * H,
-                 state_dtype == KDA_STATE_BF16 ? "bf16" : "fp32");
-  return ok();
+  return run_decode(q, k, v, g_raw, beta_logits, A_log, scale, gate_per_channel, state, state_dtype, out, B, H_qk, H,
+                    K, V, static_cast<hipStream_t>(stream), true);
+}
+
+kda_status kda_la_decode_step(const void* q, const void* k, const void* v, const void* g_raw, const float* A_log,
+                              float scale, int gate_per_channel, void* state, kda_state_dtype state_dtype, void* out,
+                              int B, int H_qk, int H, int K, int V, void* stream) {
+  return run_decode(q, k, v, g_raw, nullptr, A_log, scale, gate_per_channel, state, state_dtype, out, B, H_qk, H, K,
+                    V, static_cast<hipStream_t>(stream), false);
 }
 
 const char* kda_status_string(kda_status s) {

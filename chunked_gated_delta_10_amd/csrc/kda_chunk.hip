@@ -121,7 +121,7 @@ struct Pref {
   float beta;              // logit of the token
 };
 
-template <bool PER_CHANNEL>
+template <bool PER_CHANNEL, bool DELTA>
 __device__ __forceinline__ void load_rows(Pref& P, const ChunkParams& p, int4 ce, int h, int wave, int lane) {
   // Loads are unconditional (rows past the chunk end are clamped to its last
   // row and zeroed when used) so they issue back to back without waits.
@@ -138,7 +138,7 @@ __device__ __forceinline__ void load_rows(Pref& P, const ChunkParams& p, int4 ce
     P.q[i] = *reinterpret_cast<const uint2*>(qp + off);
     P.k[i] = *reinterpret_cast<const uint2*>(kp + off);
   }
-  P.beta = p.beta[t * p.H + h];
+  P.beta = DELTA ? p.beta[t * p.H + h] : 0.f;  // no write strength without the delta rule
   if (PER_CHANNEL) {
     const uint16_t* gp = p.g_raw + (t * p.H + h) * HD + g4;
 #pragma unroll
@@ -150,7 +150,11 @@ __device__ __forceinline__ void load_rows(Pref& P, const ChunkParams& p, int4 ce
 
 }  // namespace
 
-template <bool PER_CHANNEL>
+// DELTA = false: decay-only linear attention.  The same chunk records with
+// the UT transform reduced to the identity: no q/k normalisation, write
+// strength 1, A = 0 (so T = I) and W = 0 (K-hat is not formed), which makes
+// the recurrence's U equal to V.
+template <bool PER_CHANNEL, bool DELTA>
 __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p, const int n_jobs) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   f16x8* YB = reinterpret_cast<f16x8*>(smem + L_YB);
@@ -192,7 +196,7 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
     const int len = ce_cur.z;
     if (len > 0) {  // uniform over the workgroup
       Pref cur;
-      load_rows<PER_CHANNEL>(cur, p, ce_cur, h, wave, lane);
+      load_rows<PER_CHANNEL, DELTA>(cur, p, ce_cur, h, wave, lane);
       // keep every input load ahead of the first use, so the three streams
       // (q, k, g) are in flight together rather than g after q and k arrive
       __builtin_amdgcn_sched_barrier(0);
@@ -218,9 +222,9 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
       sk += __shfl_xor(sk, 16);
       sq += __shfl_xor(sq, 32);
       sk += __shfl_xor(sk, 32);
-      const float rq = live ? 1.f / sqrtf(sq + 1e-6f) : 0.f;
-      const float rk = live ? 1.f / sqrtf(sk + 1e-6f) : 0.f;
-      const float beta = live ? sigmoidf_(cur.beta) : 0.f;
+      const float rq = live ? (DELTA ? 1.f / sqrtf(sq + 1e-6f) : 1.f) : 0.f;
+      const float rk = live ? (DELTA ? 1.f / sqrtf(sk + 1e-6f) : 1.f) : 0.f;
+      const float beta = live ? (DELTA ? sigmoidf_(cur.beta) : 1.f) : 0.f;
       if (lg == 0) {
         ROW[R_BETA + r] = beta;
         ROW[R_RK + r] = rk;
@@ -270,10 +274,10 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
             // diagonal block on fp32 matrix cores: the lane's value is the
             // A/B operand of the 16x16x4 product for key (s, q)
             if (q & 1) {
-              accA2 = mma_f32(kn[q] * ikap, Y[v], accA2);
+              if (DELTA) accA2 = mma_f32(kn[q] * ikap, Y[v], accA2);
               accM2 = mma_f32(Y[v], qn[q] * ikap, accM2);
             } else {
-              accA_d = mma_f32(kn[q] * ikap, Y[v], accA_d);
+              if (DELTA) accA_d = mma_f32(kn[q] * ikap, Y[v], accA_d);
               accM_d = mma_f32(Y[v], qn[q] * ikap, accM_d);
             }
           }
@@ -442,17 +446,19 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
             f16x8 kh, kb;
   #pragma unroll
             for (int q = 0; q < 8; ++q) {
-              kh[q] = (f16)(X[8 * s + q] * ep[q]);
+              kh[q] = DELTA ? (f16)(X[8 * s + q] * ep[q]) : (f16)0.f;
               kb[q] = (f16)((PER_CHANNEL ? Y[8 * s + q] : X[8 * s + q]) * eg[q]);
             }
   #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
               const int kt = 2 * s + hh;  // key tile
-              const f32x4 th = mma_f16(kh, sel[hh], zero4());
+              if (DELTA) {  // K-hat^T feeds only W
+                const f32x4 th = mma_f16(kh, sel[hh], zero4());
+                const f16x4 th4 = {(f16)th[0], (f16)th[1], (f16)th[2], (f16)th[3]};
+                *reinterpret_cast<f16x4*>(KHb + ((kt * 2 + (N >> 1)) * 64 + lane) * 16 + (N & 1) * 8) = th4;
+              }
               const f32x4 tb = mma_f16(kb, sel[hh], zero4());
-              const f16x4 th4 = {(f16)th[0], (f16)th[1], (f16)th[2], (f16)th[3]};
               const f16x4 tb4 = {(f16)tb[0], (f16)tb[1], (f16)tb[2], (f16)tb[3]};
-              *reinterpret_cast<f16x4*>(KHb + ((kt * 2 + (N >> 1)) * 64 + lane) * 16 + (N & 1) * 8) = th4;
               *reinterpret_cast<f16x4*>(rec + REC_KBAR + (kt * 2 + (N >> 1)) * FRAG_BYTES + lane * 16 + (N & 1) * 8) = tb4;
             }
           }
@@ -471,13 +477,13 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
                 ql[q] = (f16)(Q[8 * s + q] * lam[q]);
               }
               const f16x8 ya = YB[(a * 4 + s) * 64 + lane];
-              accA[a] = mma_f16(xl, ya, accA[a]);
+              if (DELTA) accA[a] = mma_f16(xl, ya, accA[a]);
               accM[a] = mma_f16(ya, ql, accM[a]);
             }
           }
           if (!PER_CHANNEL) {  // scalar mode: the diagonal block is an fp16 Gram block too
             const f16x8 xh = to_f16x8(&X[8 * s]);
-            accA_d = mma_f16(xh, xh, accA_d);
+            if (DELTA) accA_d = mma_f16(xh, xh, accA_d);
             accM_d = mma_f16(xh, to_f16x8(&Q[8 * s]), accM_d);
           }
         }
@@ -521,7 +527,7 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
         for (int j = 0; j < 4; ++j) {
           const int rl = 4 * lg + j, il = l16;
           float v = 0.f;
-          if (il < rl) {
+          if (DELTA && il < rl) {
             if (flagged) v = TM[upper_off(n) + rl * MS + il];
             else {
               v = accA_d[j] * brow[j];
@@ -538,8 +544,8 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
             const float gi = PER_CHANNEL ? 0.f : gam(SUB * a + l16);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              float v = accA[a][j] * brow[j];
-              if (!PER_CHANNEL) v *= exp2f((grow[j] - gi) * LOG2E);
+              float v = DELTA ? accA[a][j] * brow[j] : 0.f;
+              if (DELTA && !PER_CHANNEL) v *= exp2f((grow[j] - gi) * LOG2E);
               AM[(SUB * n + 4 * lg + j) * MS + SUB * a + l16] = v;
             }
           }
@@ -664,8 +670,10 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
           for (int hh = 0; hh < 2; ++hh) {
             const int kt = 2 * sp + hh;
             f32x4 acc = zero4();
-            acc = mma_f16(KH[(kt * 2) * 64 + lane], tbB[0], acc);
-            if (ns > 1) acc = mma_f16(KH[(kt * 2 + 1) * 64 + lane], tbB[1], acc);
+            if (DELTA) {  // W = 0 for decay-only attention
+              acc = mma_f16(KH[(kt * 2) * 64 + lane], tbB[0], acc);
+              if (ns > 1) acc = mma_f16(KH[(kt * 2 + 1) * 64 + lane], tbB[1], acc);
+            }
 #pragma unroll
             for (int j = 0; j < 4; ++j) v[hh * 4 + j] = -acc[j];
           }
@@ -676,25 +684,29 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
   }
 }
 
-void launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, hipStream_t stream) {
+namespace {
+template <bool PER_CHANNEL, bool DELTA>
+void launch_chunk_variant(const ChunkParams& p, int n_jobs, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_local_kernel<PER_CHANNEL, DELTA>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+    attr_set = true;
+  }
+  // one job per workgroup; two are resident per CU (LDS-bound)
+  chunk_local_kernel<PER_CHANNEL, DELTA><<<n_jobs, NT, LDS_BYTES, stream>>>(p, n_jobs);
+}
+}  // namespace
+
+void launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, bool delta, hipStream_t stream) {
   const int n_jobs = n_entries * p.H;
   if (n_jobs <= 0) return;
-  const int grid = n_jobs;  // one job per workgroup; two are resident per CU (LDS-bound)
-  static bool attr_set[2] = {false, false};
-  if (per_channel) {
-    if (!attr_set[1]) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_local_kernel<true>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-      attr_set[1] = true;
-    }
-    chunk_local_kernel<true><<<grid, NT, LDS_BYTES, stream>>>(p, n_jobs);
+  if (delta) {
+    if (per_channel) launch_chunk_variant<true, true>(p, n_jobs, stream);
+    else launch_chunk_variant<false, true>(p, n_jobs, stream);
   } else {
-    if (!attr_set[0]) {
-      (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_local_kernel<false>),
-                                hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
-      attr_set[0] = true;
-    }
-    chunk_local_kernel<false><<<grid, NT, LDS_BYTES, stream>>>(p, n_jobs);
+    if (per_channel) launch_chunk_variant<true, false>(p, n_jobs, stream);
+    else launch_chunk_variant<false, false>(p, n_jobs, stream);
   }
 }
 

@@ -75,7 +75,9 @@ __device__ __forceinline__ void load_vec8(const uint16_t* base, int ks, float* x
 
 }  // namespace
 
-template <typename StT, bool PER_CHANNEL>
+// DELTA = false: decay-only linear attention, s_v = exp(g) . s_v + v_v k with
+// q and k as given (u_v = v_v: no erase, no write strength, no normalisation).
+template <typename StT, bool PER_CHANNEL, bool DELTA>
 __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   constexpr int ROWS = 8;  // rows per lane
   const int tid = threadIdx.x;
@@ -119,7 +121,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   }
   sq = rowsum16(sq);
   sk = rowsum16(sk);
-  const float rq = 1.f / sqrtf(sq + 1e-6f), rk = 1.f / sqrtf(sk + 1e-6f);
+  const float rq = DELTA ? 1.f / sqrtf(sq + 1e-6f) : 1.f, rk = DELTA ? 1.f / sqrtf(sk + 1e-6f) : 1.f;
   float qk = 0.f;
 #pragma unroll
   for (int j = 0; j < 8; ++j) {
@@ -128,7 +130,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     qk += qv[j] * kv[j];
   }
   qk = rowsum16(qk);
-  const float beta = sigmoidf_(p.beta[bh]);
+  const float beta = DELTA ? sigmoidf_(p.beta[bh]) : 1.f;
   float vrow[ROWS];
 #pragma unroll
   for (int i = 0; i < ROWS; ++i) vrow[i] = bf16_to_f32(p.v[(size_t)bh * HD + rg + 16 * i]);
@@ -144,7 +146,7 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
     }
     a = rowsum16(a);
     c = rowsum16(c);
-    const float u = beta * (vrow[i] - a);
+    const float u = DELTA ? beta * (vrow[i] - a) : vrow[i];
 #pragma unroll
     for (int j = 0; j < 8; ++j) s[i][j] += u * kv[j];
     RowIO<StT>::store(p.state, sbase + (size_t)(rg + 16 * i) * HD, ks, s[i]);
@@ -152,14 +154,22 @@ __global__ __launch_bounds__(256) void decode_kernel(DecodeParams p) {
   }
 }
 
-void launch_decode(const DecodeParams& p, int B, bool bf16_state, bool per_channel, hipStream_t stream) {
+namespace {
+template <typename StT, bool DELTA>
+void launch_decode_state(const DecodeParams& p, dim3 grid, bool per_channel, hipStream_t stream) {
+  if (per_channel) decode_kernel<StT, true, DELTA><<<grid, 256, 0, stream>>>(p);
+  else decode_kernel<StT, false, DELTA><<<grid, 256, 0, stream>>>(p);
+}
+}  // namespace
+
+void launch_decode(const DecodeParams& p, int B, bool bf16_state, bool per_channel, bool delta, hipStream_t stream) {
   dim3 grid((unsigned)(B * p.H));
   if (bf16_state) {
-    if (per_channel) decode_kernel<uint16_t, true><<<grid, 256, 0, stream>>>(p);
-    else decode_kernel<uint16_t, false><<<grid, 256, 0, stream>>>(p);
+    if (delta) launch_decode_state<uint16_t, true>(p, grid, per_channel, stream);
+    else launch_decode_state<uint16_t, false>(p, grid, per_channel, stream);
   } else {
-    if (per_channel) decode_kernel<float, true><<<grid, 256, 0, stream>>>(p);
-    else decode_kernel<float, false><<<grid, 256, 0, stream>>>(p);
+    if (delta) launch_decode_state<float, true>(p, grid, per_channel, stream);
+    else launch_decode_state<float, false>(p, grid, per_channel, stream);
   }
 }
 

@@ -19,7 +19,9 @@ Workloads are the shapes of the cuLA KDA tables (fixed-length B x T sweep
 and the random-length varlen row with 20 sequences, lengths 19..3147, total
 16384), the FlashQLA H200 gated-delta forward row (1 x 32768 tokens,
 h_qk = 16, h_v = 64) and the cuLA single-token decode table (batch 256,
-64 heads, head dim 128).
+64 heads, head dim 128); the decay-only linear-attention workloads take the
+shapes of the cuLA lightning-attention tables (packed sequences, decode at
+batch 256, 64 heads, head dim 128).
 """
 
 from __future__ import annotations
@@ -53,6 +55,7 @@ class Workload:
     N: int = 0                                  # packed sequences (varlen) when > 0
     decode: bool = False
     seed: int = 0
+    delta: bool = True                          # False: decay-only linear attention (no beta)
     K: int = HEAD_DIM
     V: int = HEAD_DIM
     note: str = ""
@@ -75,6 +78,15 @@ WORKLOADS: Dict[str, Workload] = {
                         note="gated delta rule, scalar decay, h_qk=16 h_v=64, T=32768"),
     "kda_decode": Workload("kda_decode", B=256, T=1, H=64, H_qk=64, state_std=0.02, decode=True, seed=1004,
                            note="KDA single-token decode, B=256 H=64, fp32 state in place"),
+    # decay-only linear attention (the cuLA page's lightning-attention tables):
+    # packed no-state forward over 16 random-length sequences, and the
+    # single-token decode at batch 256, 64 heads, head dim 128
+    "la_varlen": Workload("la_varlen", B=1, T=16384, H=64, H_qk=64, gate_per_channel=False, A_log=(0.0, 0.0),
+                          N=16, seed=1005, delta=False,
+                          note="decay-only linear attention, 16 packed sequences (19..3147), H=64, no state"),
+    "la_decode": Workload("la_decode", B=256, T=1, H=64, H_qk=64, gate_per_channel=False, A_log=(0.0, 0.0),
+                          state_std=0.02, decode=True, seed=1006, delta=False,
+                          note="decay-only linear attention decode, B=256 H=64, fp32 state in place"),
 }
 
 

@@ -60,6 +60,12 @@ def load():
     lib.kda_fwd_varlen.argtypes = [P, P, P, P, P, P, F, I, P, I, P, P, I, P, I, I, I, I, I, I, P, Z, P]
     lib.kda_decode_step.restype = I
     lib.kda_decode_step.argtypes = [P, P, P, P, P, P, F, I, P, I, P, I, I, I, I, I, P]
+    lib.kda_la_fwd.restype = I
+    lib.kda_la_fwd.argtypes = [P, P, P, P, P, F, I, P, I, P, P, I, I, I, I, I, I, I, P, Z, P]
+    lib.kda_la_fwd_varlen.restype = I
+    lib.kda_la_fwd_varlen.argtypes = [P, P, P, P, P, F, I, P, I, P, P, I, P, I, I, I, I, I, I, P, Z, P]
+    lib.kda_la_decode_step.restype = I
+    lib.kda_la_decode_step.argtypes = [P, P, P, P, P, F, I, P, I, P, I, I, I, I, I, P]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [I]
     lib.kda_last_error.restype = ctypes.c_char_p
@@ -137,7 +143,8 @@ def _prep(q, k, v, g_raw, beta_logits, A_log):
     _need(k, "k", torch.bfloat16)
     _need(v, "v", torch.bfloat16)
     _need(g_raw, "g_raw", torch.bfloat16)
-    _need(beta_logits, "beta_logits", torch.float32)
+    if beta_logits is not None:
+        _need(beta_logits, "beta_logits", torch.float32)
     _need(A_log, "A_log", torch.float32)
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
         raise ValueError("q, k must be [B, T, H_qk, K] and v [B, T, H, V]")
@@ -149,7 +156,7 @@ def _prep(q, k, v, g_raw, beta_logits, A_log):
         per_channel = 0
     else:
         raise ValueError("g_raw must be [B, T, H, K] (per channel) or [B, T, H] (scalar)")
-    if beta_logits.shape != (B, T, H) or A_log.shape != (H,):
+    if (beta_logits is not None and beta_logits.shape != (B, T, H)) or A_log.shape != (H,):
         raise ValueError("beta_logits must be [B, T, H] and A_log [H]")
     return B, T, H_qk, H, K, V, per_channel
 
@@ -240,4 +247,95 @@ def decode_step(q, k, v, g_raw, beta_logits, A_log, state: torch.Tensor, scale: 
     _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale,
                                per_channel, _ptr(state), _state_code(state), _ptr(out), B, H_qk, H, K, V,
                                _stream(stream)))
+    return out
+
+
+# ---- decay-only linear attention ---------------------------------------------
+# The same chunked path without the delta rule: S_t = Diag(exp(g_t)) S_{t-1}
+# + k_t v_t^T, o_t = scale * S_t^T q_t, q and k used as given.
+
+
+def _states(initial_state, final_state, output_final_state, state_dtype, C, H, V, K, dev):
+    if final_state is None and output_final_state:
+        sd = state_dtype or (initial_state.dtype if initial_state is not None else torch.float32)
+        final_state = torch.empty((C, H, V, K), dtype=sd, device=dev)
+    for t, n in ((initial_state, "initial_state"), (final_state, "final_state")):
+        if t is not None and (tuple(t.shape) != (C, H, V, K) or not t.is_contiguous()):
+            raise ValueError("%s must be a contiguous [%d, H, V, K] tensor" % (n, C))
+    return final_state
+
+
+def la_fwd(q, k, v, g_raw, A_log, scale: Optional[float] = None, initial_state: Optional[torch.Tensor] = None,
+           output_final_state: bool = True, final_state: Optional[torch.Tensor] = None,
+           out: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+           state_dtype: Optional[torch.dtype] = None, stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked decay-only linear attention over B rows of T tokens.  Returns (out, final_state)."""
+    lib = load()
+    B, T, H_qk, H, K, V, per_channel = _prep(q, k, v, g_raw, None, A_log)
+    scale = K ** -0.5 if scale is None else float(scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
+    final_state = _states(initial_state, final_state, output_final_state, state_dtype, B, H, V, K, dev)
+    nbytes = workspace_bytes(B, T, H_qk, H, 0)
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _workspace(nbytes, dev)
+    _check(lib.kda_la_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(A_log), scale, per_channel,
+                          _ptr(initial_state), _state_code(initial_state), _ptr(out), _ptr(final_state),
+                          _state_code(final_state), B, T, H_qk, H, K, V, _ptr(workspace), workspace.numel(),
+                          _stream(stream)))
+    return out, final_state
+
+
+def la_fwd_varlen(q, k, v, g_raw, A_log, cu_seqlens: torch.Tensor, scale: Optional[float] = None,
+                  initial_state: Optional[torch.Tensor] = None, output_final_state: bool = True,
+                  final_state: Optional[torch.Tensor] = None, out: Optional[torch.Tensor] = None,
+                  workspace: Optional[torch.Tensor] = None, state_dtype: Optional[torch.dtype] = None,
+                  stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """Chunked decay-only linear attention over packed sequences (B = 1).  Returns (out, final_state)."""
+    lib = load()
+    B, T, H_qk, H, K, V, per_channel = _prep(q, k, v, g_raw, None, A_log)
+    if B != 1:
+        raise ValueError("packed sequences need B == 1")
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    N = cu_seqlens.numel() - 1
+    scale = K ** -0.5 if scale is None else float(scale)
+    dev = q.device
+    if out is None:
+        out = torch.empty((1, T, H, V), dtype=torch.bfloat16, device=dev)
+    final_state = _states(initial_state, final_state, output_final_state, state_dtype, N, H, V, K, dev)
+    nbytes = workspace_bytes(1, T, H_qk, H, max(N, 0))
+    if workspace is None or workspace.numel() < nbytes:
+        workspace = _workspace(nbytes, dev)
+    _check(lib.kda_la_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(A_log), scale, per_channel,
+                                 _ptr(initial_state), _state_code(initial_state), _ptr(out), _ptr(final_state),
+                                 _state_code(final_state), _ptr(cu_seqlens), N, T, H_qk, H, K, V, _ptr(workspace),
+                                 workspace.numel(), _stream(stream)))
+    return out, final_state
+
+
+def la_decode_step(q, k, v, g_raw, A_log, state: torch.Tensor, scale: Optional[float] = None,
+                   out: Optional[torch.Tensor] = None, stream=None) -> torch.Tensor:
+    """One decay-only linear-attention decode step; `state` [B, H, V, K] is updated in place."""
+    lib = load()
+    for t, n, dt in ((q, "q", torch.bfloat16), (k, "k", torch.bfloat16), (v, "v", torch.bfloat16),
+                     (g_raw, "g_raw", torch.bfloat16), (A_log, "A_log", torch.float32)):
+        _need(t, n, dt)
+    if q.dim() != 3 or k.shape != q.shape or v.dim() != 3:
+        raise ValueError("q, k must be [B, H_qk, K] and v [B, H, V]")
+    B, H_qk, K = q.shape
+    H, V = v.shape[1], v.shape[2]
+    if g_raw.shape == (B, H, K):
+        per_channel = 1
+    elif g_raw.shape == (B, H):
+        per_channel = 0
+    else:
+        raise ValueError("g_raw must be [B, H, K] or [B, H]")
+    if tuple(state.shape) != (B, H, V, K) or not state.is_contiguous():
+        raise ValueError("state must be a contiguous [B, H, V, K] tensor")
+    scale = K ** -0.5 if scale is None else float(scale)
+    if out is None:
+        out = torch.empty((B, H, V), dtype=torch.bfloat16, device=q.device)
+    _check(lib.kda_la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(A_log), scale, per_channel,
+                                  _ptr(state), _state_code(state), _ptr(out), B, H_qk, H, K, V, _stream(stream)))
     return out

@@ -128,6 +128,35 @@ kda_status kda_decode_step(const void* q, const void* k, const void* v, const vo
                            void* out, int B, int H_qk, int H, int K, int V, void* stream);
 
 /*
+ * Decay-only linear attention ("lightning attention": the cuLA benchmark
+ * page times its chunked no-state / varlen forward and its single-token
+ * decode, in the lightning-attention section, without defining it).  Read as
+ * the KDA recurrence without the delta rule:
+ *   S_t = Diag(exp(g_t)) S_{t-1} + k_t v_t^T,   o_t = scale * S_t^T q_t,
+ * with g_t = -exp(A_log[h]) * softplus(g_raw_t) (one scalar per token-head
+ * when gate_per_channel == 0, the per-head decay of lightning attention, or
+ * per channel), q and k used as given (no normalisation), no write strength.
+ * Arguments, layouts, shapes, workspace (kda_fwd_workspace_bytes), errors
+ * and the B/N/T == 0 behaviour are those of kda_fwd / kda_fwd_varlen /
+ * kda_decode_step without beta_logits.
+ */
+kda_status kda_la_fwd(const void* q, const void* k, const void* v, const void* g_raw, const float* A_log,
+                      float scale, int gate_per_channel, const void* initial_state,
+                      kda_state_dtype init_dtype, void* out, void* final_state,
+                      kda_state_dtype final_dtype, int B, int T, int H_qk, int H, int K, int V,
+                      void* workspace, size_t workspace_bytes, void* stream);
+kda_status kda_la_fwd_varlen(const void* q, const void* k, const void* v, const void* g_raw,
+                             const float* A_log, float scale, int gate_per_channel,
+                             const void* initial_state, kda_state_dtype init_dtype, void* out,
+                             void* final_state, kda_state_dtype final_dtype,
+                             const int32_t* cu_seqlens, int N, int T, int H_qk, int H, int K, int V,
+                             void* workspace, size_t workspace_bytes, void* stream);
+kda_status kda_la_decode_step(const void* q, const void* k, const void* v, const void* g_raw,
+                              const float* A_log, float scale, int gate_per_channel, void* state,
+                              kda_state_dtype state_dtype, void* out, int B, int H_qk, int H, int K,
+                              int V, void* stream);
+
+/*
  * Diagnostics: per-kernel timing with HIP events (used by the benchmark).
  * While enabled on the calling thread, each kernel launched by the entry
  * points above is bracketed by two hipEventRecord calls on the caller's

@@ -1,0 +1,157 @@
+"""GPU parity of decay-only linear attention (kda_la_fwd, kda_la_fwd_varlen,
+kda_la_decode_step) against the fp64 oracle in oracle/la.py.
+
+The bar is the KDA one (out rel-L2 <= 5e-3, fp32 final state rel-L2 <=
+1e-3) with the absolute output bound scaled by the largest reference output.
+q and k are not normalised here, so outputs reach ~10 instead of O(1); the
+bf16 output alone then rounds by up to 2^-9 of that (0.03 at |o| = 10), and
+the fp16 chunk records hold intra-chunk products q.k of size ~K with a
+relative rounding of 2^-11.  Both are relative errors, so the absolute bound
+scales with the output's magnitude; for KDA's O(1) outputs the two bounds
+coincide.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+from oracle import la
+from chunked_gated_delta_10_amd import kda
+from chunked_gated_delta_10_amd.inputs import WORKLOADS, make_inputs, workload_inputs
+import kda_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+def run_gpu(inp, state_dtype=torch.float32):
+    d = U.to_device(inp, state_dtype)
+    if d["cu_seqlens"] is not None:
+        out, fin = kda.la_fwd_varlen(d["q"], d["k"], d["v"], d["g_raw"], d["A_log"], d["cu_seqlens"],
+                                     scale=inp["scale"], initial_state=d["initial_state"], state_dtype=state_dtype)
+    else:
+        out, fin = kda.la_fwd(d["q"], d["k"], d["v"], d["g_raw"], d["A_log"], scale=inp["scale"],
+                              initial_state=d["initial_state"], state_dtype=state_dtype)
+    torch.cuda.synchronize()
+    return out.float().cpu().numpy().astype(np.float64), fin.float().cpu().numpy().astype(np.float64)
+
+
+def run_oracle(inp, chain_mask=None):
+    return la.la_fwd(inp["q"], inp["k"], inp["v"], inp["g_raw"], inp["A_log"], inp["scale"],
+                     gate_per_channel=inp["gate_per_channel"], initial_state=inp.get("initial_state"),
+                     cu_seqlens=inp.get("cu_seqlens"), chain_mask=chain_mask)
+
+
+def assert_parity(out, fin, ref_out, ref_fin, state_dtype=torch.float32, what=""):
+    sel = ~np.isnan(ref_out)
+    o, ro = out[sel], ref_out[sel]
+    peak = float(np.max(np.abs(ro))) if ro.size else 0.0
+    maxabs = float(np.max(np.abs(o - ro))) if o.size else 0.0
+    rel = U.rel_l2(o, ro)
+    fsel = ~np.isnan(ref_fin)
+    frel = U.rel_l2(fin[fsel], ref_fin[fsel])
+    bar_abs = U.OUT_MAXABS * max(1.0, peak)
+    bar_state = U.STATE_REL_FP32 if state_dtype == torch.float32 else U.STATE_REL_BF16
+    msg = "%s out max-abs %.3e (bar %.3e, peak %.2f) rel-L2 %.3e | final rel-L2 %.3e" % (
+        what, maxabs, bar_abs, peak, rel, frel)
+    print(msg, flush=True)
+    assert np.all(np.isfinite(out)), "non-finite output " + msg
+    assert maxabs <= bar_abs and rel <= U.OUT_REL, msg
+    assert frel <= bar_state, msg
+
+
+def check(inp, state_dtype=torch.float32, what="", chain_mask=None):
+    print("case:", what, flush=True)
+    out, fin = run_gpu(inp, state_dtype)
+    ref_out, ref_fin = run_oracle(U.state_as_stored(inp, state_dtype), chain_mask=chain_mask)
+    assert_parity(out, fin, ref_out, ref_fin, state_dtype, what)
+
+
+@pytest.mark.parametrize("T", [64, 150, 257])
+def test_scalar_decay_ragged(T):
+    inp = make_inputs(2, T, 4, 4, gate_per_channel=False, A_log=(-1.0, 0.5), state_std=0.05, seed=400 + T)
+    check(inp, what="la scalar decay T=%d" % T)
+
+
+def test_per_channel_decay():
+    inp = make_inputs(2, 130, 3, 3, gate_per_channel=True, A_log=(-2.0, 0.0), state_std=0.05, seed=410)
+    check(inp, what="la per-channel decay")
+
+
+def test_long_memory():
+    inp = make_inputs(1, 700, 2, 2, gate_per_channel=False, A_log=(-5.0, -4.0), state_std=0.05, seed=411)
+    check(inp, what="la mild decay T=700")
+
+
+def test_grouped_heads():
+    inp = make_inputs(1, 100, 8, 2, gate_per_channel=False, A_log=0.0, seed=412)
+    check(inp, what="la grouped heads 2->8")
+
+
+def test_packed_without_state():
+    lens = [1, 64, 0, 77, 130]
+    inp = make_inputs(1, sum(lens), 4, 4, gate_per_channel=False, A_log=0.0, N=len(lens), lengths=lens, seed=413)
+    check(inp, what="la packed no state %s" % lens)
+
+
+def test_packed_many_chains_with_state():
+    lens = [33, 200, 5, 64, 129, 1, 90]
+    inp = make_inputs(1, sum(lens), 8, 8, gate_per_channel=False, A_log=(-2.0, 0.0), state_std=0.05,
+                      N=len(lens), lengths=lens, seed=414)
+    check(inp, what="la packed with state, 56 chains")
+
+
+def test_bf16_state():
+    inp = make_inputs(2, 190, 2, 2, gate_per_channel=False, A_log=(-3.0, -1.0), state_std=0.05, seed=415)
+    check(inp, state_dtype=torch.bfloat16, what="la bf16 state")
+
+
+def run_decode_gpu(q, k, v, g_raw, A_log, state, scale, state_dtype=torch.float32):
+    st = torch.from_numpy(state).to(device="cuda", dtype=state_dtype)
+    o = kda.la_decode_step(U.bf16_tensor(q), U.bf16_tensor(k), U.bf16_tensor(v), U.bf16_tensor(g_raw),
+                           torch.from_numpy(A_log).cuda(), st, scale=scale)
+    torch.cuda.synchronize()
+    return o.float().cpu().numpy().astype(np.float64), st.float().cpu().numpy().astype(np.float64)
+
+
+@pytest.mark.parametrize("per_channel", [False, True])
+@pytest.mark.parametrize("sdt", [torch.float32, torch.bfloat16])
+def test_decode_step(per_channel, sdt):
+    d = make_inputs(5, 1, 4, 2, gate_per_channel=per_channel, state_std=0.05, seed=420, decode=True)
+    s0 = U.state_as_stored(d, sdt)["initial_state"]
+    out, st = run_decode_gpu(d["q"], d["k"], d["v"], d["g_raw"], d["A_log"], d["initial_state"], d["scale"], sdt)
+    ro, rs = la.la_decode(d["q"], d["k"], d["v"], d["g_raw"], d["A_log"], d["scale"], s0, gate_per_channel=per_channel)
+    assert_parity(out, st, ro, rs, sdt, what="la decode per_channel=%s %s" % (per_channel, sdt))
+
+
+def test_decode_steps_match_chunked_forward():
+    T = 7
+    inp = make_inputs(3, T, 2, 2, gate_per_channel=False, A_log=(-2.0, -1.0), state_std=0.05, seed=421)
+    out_f, fin_f = run_gpu(inp)
+    st = inp["initial_state"].copy()
+    outs = []
+    for t in range(T):
+        o, st = run_decode_gpu(inp["q"][:, t], inp["k"][:, t], inp["v"][:, t], inp["g_raw"][:, t], inp["A_log"],
+                               st.astype(np.float32), inp["scale"])
+        outs.append(o)
+    ref_out, ref_fin = run_oracle(inp)
+    assert_parity(np.stack(outs, axis=1), st, ref_out, ref_fin, what="la T decode steps")
+    np.testing.assert_allclose(np.stack(outs, axis=1), out_f, rtol=0, atol=5e-2)
+
+
+def test_full_size_varlen_sampled_chains():
+    w = WORKLOADS["la_varlen"]
+    inp = workload_inputs("la_varlen")
+    lens = np.diff(inp["cu_seqlens"])
+    longest = int(np.argmax(lens))
+    mask = np.zeros((w.N, w.H), dtype=bool)
+    mask[longest, 0] = mask[longest, w.H - 1] = mask[w.N - 1, 17] = True
+    check(inp, what="la_varlen sampled chains", chain_mask=mask)
+
+
+def test_full_size_decode():
+    inp = workload_inputs("la_decode")
+    out, st = run_decode_gpu(inp["q"], inp["k"], inp["v"], inp["g_raw"], inp["A_log"], inp["initial_state"],
+                             inp["scale"])
+    ro, rs = la.la_decode(inp["q"], inp["k"], inp["v"], inp["g_raw"], inp["A_log"], inp["scale"],
+                          inp["initial_state"], gate_per_channel=False)
+    assert_parity(out, st, ro, rs, what="la_decode B=256 H=64")
