@@ -36,7 +36,7 @@ def algorithmic_bytes(w, with_state=True, state_bytes=4):
     tok = w.B * w.T
     qk = 2 * tok * w.H_qk * D * 2
     g = tok * w.H * (D if w.gate_per_channel else 1) * 2
-    beta = tok * w.H * 4
+    beta = tok * w.H * 4 if w.delta else 0
     v = tok * w.H * D * 2
     out = tok * w.H * D * 2
     C_ = w.N if w.N else w.B
@@ -187,14 +187,28 @@ def time_workload(name, steps, warmup, bf16_state=False):
         st = d["initial_state"]
         out = torch.empty((w.B, w.H, D), dtype=torch.bfloat16, device="cuda")
 
-        def step():
-            kda.decode_step(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], st, scale=inp["scale"], out=out)
+        if w.delta:
+            def step():
+                kda.decode_step(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], st, scale=inp["scale"],
+                                out=out)
+        else:
+            def step():
+                kda.la_decode_step(d["q"], d["k"], d["v"], d["g_raw"], d["A_log"], st, scale=inp["scale"], out=out)
     else:
         C_ = w.N if w.N else w.B
         out = torch.empty((w.B, w.T, w.H, D), dtype=torch.bfloat16, device="cuda")
         fin = torch.empty((C_, w.H, D, D), dtype=sdt, device="cuda")
         ws = torch.empty(kda.workspace_bytes(w.B, w.T, w.H_qk, w.H, w.N), dtype=torch.uint8, device="cuda")
-        if w.N:
+        if not w.delta:
+            def step():
+                if w.N:
+                    kda.la_fwd_varlen(d["q"], d["k"], d["v"], d["g_raw"], d["A_log"], d["cu_seqlens"],
+                                      scale=inp["scale"], initial_state=d["initial_state"], final_state=fin, out=out,
+                                      workspace=ws)
+                else:
+                    kda.la_fwd(d["q"], d["k"], d["v"], d["g_raw"], d["A_log"], scale=inp["scale"],
+                               initial_state=d["initial_state"], final_state=fin, out=out, workspace=ws)
+        elif w.N:
             def step():
                 kda.fwd_varlen(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], d["cu_seqlens"],
                                scale=inp["scale"], initial_state=d["initial_state"], final_state=fin, out=out,
@@ -288,7 +302,7 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=1024 * 1024 * 1024,
                     help="size of the calibration copy used with --traffic-from")
     ap.add_argument("--only", metavar="WORKLOAD",
-                    help="only time one workload (kda_tiny, kda_dense, kda_varlen, gdn_gva, kda_decode) and print "
+                    help="only time one workload (kda_tiny, kda_dense, kda_varlen, gdn_gva, kda_decode, la_varlen, la_decode) and print "
                          "its per-kernel averages; for profiling runs")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the grouped-value-head sweep (head shapes x sequence patterns)")
@@ -355,7 +369,7 @@ def main():
     }
     if not args.no_extra:
         extra = {}
-        for other in ("kda_varlen", "gdn_gva", "kda_decode", "kda_dense_bf16_state"):
+        for other in ("kda_varlen", "gdn_gva", "kda_decode", "kda_dense_bf16_state", "la_varlen", "la_decode"):
             bf16_state = other.endswith("_bf16_state")
             oms, opk, _, ow, _ = time_workload(other.replace("_bf16_state", ""), max(10, args.steps // 5), 3,
                                                bf16_state=bf16_state)

@@ -216,7 +216,7 @@ kda_status run_forward(const FwdArgs& a) {
                       reinterpret_cast<uint16_t*>(ws + L.sink)};
   {
     Timed t(K_RECUR, a.stream);
-    kda::launch_recur(rp, bf16_state, a.stream);
+    kda::launch_recur(rp, bf16_state, a.delta, a.stream);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

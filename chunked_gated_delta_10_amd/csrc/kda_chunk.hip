@@ -522,12 +522,14 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
           grow[j] = PER_CHANNEL ? 0.f : gam(rr);
         }
         // diagonal block: lane holds A[16n + 4lg + j][16n + l16]
+        // (no A without the delta rule: T = I, steps 4 and 5 are skipped)
+        if (DELTA) {
         float dv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int rl = 4 * lg + j, il = l16;
           float v = 0.f;
-          if (DELTA && il < rl) {
+          if (il < rl) {
             if (flagged) v = TM[upper_off(n) + rl * MS + il];
             else {
               v = accA_d[j] * brow[j];
@@ -544,11 +546,12 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
             const float gi = PER_CHANNEL ? 0.f : gam(SUB * a + l16);
 #pragma unroll
             for (int j = 0; j < 4; ++j) {
-              float v = DELTA ? accA[a][j] * brow[j] : 0.f;
-              if (DELTA && !PER_CHANNEL) v *= exp2f((grow[j] - gi) * LOG2E);
+              float v = accA[a][j] * brow[j];
+              if (!PER_CHANNEL) v *= exp2f((grow[j] - gi) * LOG2E);
               AM[(SUB * n + 4 * lg + j) * MS + SUB * a + l16] = v;
             }
           }
+        }
         }
         // M^T blocks: lane holds M[16n + l16][16a + 4lg + j]
         const float gr = PER_CHANNEL ? 0.f : gam(r);
@@ -595,7 +598,7 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
       // ---- 4. T_nn = (I + A_nn)^-1 by column-oriented substitution -----------
       // Lane c < 16 owns column c; A_nn's columns come from AT (written by this
       // wave just above, so no barrier is needed).
-      if (lane < SUB) {
+      if (DELTA && lane < SUB) {
         const float* ATn = AT + n * 256;
         float acc[SUB];
 #pragma unroll
@@ -612,12 +615,12 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
 #pragma unroll
         for (int i = 0; i < SUB; ++i) TM[(SUB * n + i) * MS + SUB * n + lane] = acc[i];
       }
-      __syncthreads();  // A rows, diagonal T blocks and Khat^T visible
+      if (DELTA) __syncthreads();  // A rows, diagonal T blocks and Khat^T visible
 
       // ---- 5. off-diagonal blocks of T, level by level (fp32 matrix cores) ----
       //   T_ba = -T_bb * sum_{a<=j<b} A_bj T_ja
 #pragma unroll
-      for (int lev = 1; lev < NSUB; ++lev) {
+      for (int lev = 1; lev < (DELTA ? NSUB : 1); ++lev) {
         if (wave < NSUB - lev) {
           const int a = wave, b = wave + lev;
           f32x4 Xs = zero4();
@@ -650,8 +653,16 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
           if (s < ns) {
             const int j0 = 32 * s + 4 * lg, j1 = j0 + 16;
             float tv[8], bb[8];
-            *reinterpret_cast<float4*>(&tv[0]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j0]);
-            *reinterpret_cast<float4*>(&tv[4]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j1]);
+            if (DELTA) {
+              *reinterpret_cast<float4*>(&tv[0]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j0]);
+              *reinterpret_cast<float4*>(&tv[4]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j1]);
+            } else {  // T = I
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                tv[q] = j0 + q == rt ? 1.f : 0.f;
+                tv[4 + q] = j1 + q == rt ? 1.f : 0.f;
+              }
+            }
             *reinterpret_cast<float4*>(&bb[0]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j0]);
             *reinterpret_cast<float4*>(&bb[4]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j1]);
 #pragma unroll

@@ -62,7 +62,7 @@ struct TableParams {
 void launch_table(const TableParams& p, hipStream_t stream);
 // delta = false: decay-only linear attention (no erase, no write strength, no q/k normalisation)
 void launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, bool delta, hipStream_t stream);
-void launch_recur(const RecurParams& p, bool bf16_state, hipStream_t stream);
+void launch_recur(const RecurParams& p, bool bf16_state, bool delta, hipStream_t stream);
 int recur_grid(int n_chains);
 void launch_decode(const DecodeParams& p, int B, bool bf16_state, bool per_channel, bool delta, hipStream_t stream);
 

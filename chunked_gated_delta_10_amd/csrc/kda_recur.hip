@@ -101,7 +101,10 @@ __device__ __forceinline__ void unpack_bf16(uint2 x, f16* o) {
   o[3] = (f16)__uint_as_float(x.y & 0xFFFF0000u);
 }
 
-template <typename StT, int NCT>
+// DELTA = false (decay-only linear attention): the chunk records carry
+// T diag(b) = I and W = 0, so U = V is read straight from the value tile and
+// neither W nor T diag(b) is loaded.
+template <typename StT, int NCT, bool DELTA>
 __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
   constexpr int VC = VT * NCT;       // value columns per workgroup
   constexpr int NW = NVT / NCT;      // workgroups per chain
@@ -203,6 +206,10 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
       __syncthreads();  // A
 #pragma unroll
       for (int j = 0; j < NCT; ++j) {
+        if (!DELTA) {  // U = V: rows 16 tw + 4 lg .. +3 of column 16 j + l16
+          ubuf[j][tw * 64 + lane] = *reinterpret_cast<const f16x4*>(&vsT[(VT * j + l16) * VS + SUB * tw + 4 * lg]);
+          continue;
+        }
         f16x8 sB[4];
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) sB[s2] = sbuf[j][s2 * 64 + lane];
@@ -360,16 +367,24 @@ int recur_grid(int n_chains) {
   return g <= cu_count() ? g : grid_for(n_chains, NVT / 2);
 }
 
-void launch_recur(const RecurParams& p, bool bf16_state, hipStream_t stream) {
+namespace {
+template <bool DELTA>
+void launch_recur_variant(const RecurParams& p, bool bf16_state, hipStream_t stream) {
   const int g = grid_for(p.n_chains, NVT);
   if (g <= cu_count()) {  // few chains: one column tile per workgroup, all on CUs of their own
-    if (bf16_state) recur_split_kernel<uint16_t, 1><<<g, 512, 0, stream>>>(p);
-    else recur_split_kernel<float, 1><<<g, 512, 0, stream>>>(p);
+    if (bf16_state) recur_split_kernel<uint16_t, 1, DELTA><<<g, 512, 0, stream>>>(p);
+    else recur_split_kernel<float, 1, DELTA><<<g, 512, 0, stream>>>(p);
     return;
   }
   const int g2 = grid_for(p.n_chains, NVT / 2);  // two column tiles per workgroup
-  if (bf16_state) recur_split_kernel<uint16_t, 2><<<g2, 512, 0, stream>>>(p);
-  else recur_split_kernel<float, 2><<<g2, 512, 0, stream>>>(p);
+  if (bf16_state) recur_split_kernel<uint16_t, 2, DELTA><<<g2, 512, 0, stream>>>(p);
+  else recur_split_kernel<float, 2, DELTA><<<g2, 512, 0, stream>>>(p);
+}
+}  // namespace
+
+void launch_recur(const RecurParams& p, bool bf16_state, bool delta, hipStream_t stream) {
+  if (delta) launch_recur_variant<true>(p, bf16_state, stream);
+  else launch_recur_variant<false>(p, bf16_state, stream);
 }
 
 }  // namespace kda
