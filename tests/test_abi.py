@@ -89,3 +89,35 @@ def test_decode_validation(lib):
     assert call(st=None) == 1
     assert call(out=P + 2) == 6
     assert call(B=0) == 0
+
+
+def test_linear_attention_validation(lib):
+    def fwd_la(**over):
+        a = dict(q=P, k=P, v=P, g=P, alog=P, scale=0.088, pc=0, s0=None, s0dt=NONE, out=P, s1=P, s1dt=F32,
+                 B=1, T=64, Hqk=2, H=2, K=128, V=128, ws=P, wsb=1 << 40)
+        a.update(over)
+        return lib.kda_la_fwd(a["q"], a["k"], a["v"], a["g"], a["alog"], a["scale"], a["pc"], a["s0"], a["s0dt"],
+                              a["out"], a["s1"], a["s1dt"], a["B"], a["T"], a["Hqk"], a["H"], a["K"], a["V"],
+                              a["ws"], a["wsb"], None)
+    assert fwd_la(K=64) == 2
+    assert fwd_la(H=3) == 2
+    assert fwd_la(q=None) == 1
+    assert fwd_la(alog=None) == 1
+    assert fwd_la(out=P + 8) == 6
+    assert fwd_la(ws=None) == 5
+    assert fwd_la(s0=P, s0dt=BF16) == 4
+    assert fwd_la(B=0) == 0
+    assert lib.kda_la_fwd_varlen(P, P, P, P, P, 0.088, 0, None, NONE, P, P, F32, None, 3, 100, 2, 2, 128, 128, P,
+                                 1 << 40, None) == 1
+    assert lib.kda_la_fwd_varlen(P, P, P, P, P, 0.088, 0, None, NONE, P, P, F32, P, 3, 100, 2, 2, 96, 128, P,
+                                 1 << 40, None) == 2
+
+    def dec(**over):
+        a = dict(q=P, k=P, v=P, g=P, alog=P, scale=0.088, pc=0, st=P, dt=F32, out=P, B=4, Hqk=2, H=4, K=128, V=128)
+        a.update(over)
+        return lib.kda_la_decode_step(a["q"], a["k"], a["v"], a["g"], a["alog"], a["scale"], a["pc"], a["st"],
+                                      a["dt"], a["out"], a["B"], a["Hqk"], a["H"], a["K"], a["V"], None)
+    assert dec(K=64) == 2
+    assert dec(dt=NONE) == 3
+    assert dec(st=None) == 1
+    assert dec(B=0) == 0
