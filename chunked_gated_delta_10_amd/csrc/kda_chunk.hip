@@ -500,196 +500,207 @@ __global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p,
         *reinterpret_cast<float*>(rec + REC_GL + 4 * tid) = gl;
       }
 
-      // ---- 3. A rows of this sub-chunk -> LDS; M fragments -> record ----------
-      {
-        // scalar mode: Gamma_x from the per-token prefix within its sub-chunk
-        // plus the totals of the sub-chunks before it
-        float gbase[NSUB];
-        if (!PER_CHANNEL) {
-          float acc = 0.f;
-#pragma unroll
-          for (int m = 0; m < NSUB; ++m) {
-            gbase[m] = acc;
-            acc += ROW[R_GS + m];
-          }
-        }
-        auto gam = [&](int x) { return ROW[R_GP + x] + gbase[x >> 4]; };
-        float brow[4], grow[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int rr = SUB * n + 4 * lg + j;
-          brow[j] = ROW[R_BETA + rr];
-          grow[j] = PER_CHANNEL ? 0.f : gam(rr);
-        }
-        // diagonal block: lane holds A[16n + 4lg + j][16n + l16]
-        // (no A without the delta rule: T = I, steps 4 and 5 are skipped)
-        if (DELTA) {
-        float dv[4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int rl = 4 * lg + j, il = l16;
-          float v = 0.f;
-          if (il < rl) {
-            if (flagged) v = TM[upper_off(n) + rl * MS + il];
-            else {
-              v = accA_d[j] * brow[j];
-              if (!PER_CHANNEL) v *= exp2f((grow[j] - gam(SUB * n + il)) * LOG2E);
+      // Steps 3 to 6 are instantiated per sub-chunk index N like step 2 (the
+      // same barriers in every instantiation).
+      auto steps3to6 = [&](auto Nc) {
+        constexpr int N = decltype(Nc)::value;
+        // ---- 3. A rows of this sub-chunk -> LDS; M fragments -> record ----------
+        {
+          // scalar mode: Gamma_x from the per-token prefix within its sub-chunk
+          // plus the totals of the sub-chunks before it
+          float gbase[NSUB];
+          if (!PER_CHANNEL) {
+            float acc = 0.f;
+  #pragma unroll
+            for (int m = 0; m < NSUB; ++m) {
+              gbase[m] = acc;
+              acc += ROW[R_GS + m];
             }
           }
-          dv[j] = v;
-          AM[(SUB * n + rl) * MS + SUB * n + il] = v;
-        }
-        *reinterpret_cast<float4*>(&AT[n * 256 + l16 * 16 + 4 * lg]) = make_float4(dv[0], dv[1], dv[2], dv[3]);
-#pragma unroll
-        for (int a = 0; a < 3; ++a) {
-          if (a < n) {
-            const float gi = PER_CHANNEL ? 0.f : gam(SUB * a + l16);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) {
-              float v = accA[a][j] * brow[j];
-              if (!PER_CHANNEL) v *= exp2f((grow[j] - gi) * LOG2E);
-              AM[(SUB * n + 4 * lg + j) * MS + SUB * a + l16] = v;
-            }
-          }
-        }
-        }
-        // M^T blocks: lane holds M[16n + l16][16a + 4lg + j]
-        const float gr = PER_CHANNEL ? 0.f : gam(r);
-        float md[4], mo[3][4];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          const int il = 4 * lg + j;
-          float v = 0.f;
-          if (il <= l16) {
-            if (flagged) v = AM[upper_off(n) + l16 * MS + il];
-            else {
-              v = accM_d[j];
-              if (!PER_CHANNEL) v *= exp2f((gr - gam(SUB * n + il)) * LOG2E);
-            }
-          }
-          md[j] = v;
-        }
-#pragma unroll
-        for (int a = 0; a < 3; ++a)
-#pragma unroll
+          auto gam = [&](int x) { return ROW[R_GP + x] + gbase[x >> 4]; };
+          float brow[4], grow[4];
+  #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            float v = accM[a][j];
-            if (!PER_CHANNEL && a < n) v *= exp2f((gr - gam(SUB * a + 4 * lg + j)) * LOG2E);
-            mo[a][j] = v;
+            const int rr = SUB * N + 4 * lg + j;
+            brow[j] = ROW[R_BETA + rr];
+            grow[j] = PER_CHANNEL ? 0.f : gam(rr);
           }
-        float v[8];
-        // fragment (n, 0): blocks (n, 0), (n, 1)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          v[j] = n == 0 ? md[j] : mo[0][j];
-          v[4 + j] = n == 0 ? 0.f : (n == 1 ? md[j] : mo[1][j]);
-        }
-        store_frag(rec, REC_M, n * 2, lane, v);
-        if (n >= 2) {  // fragment (n, 1): blocks (n, 2), (n, 3)
-#pragma unroll
+          // diagonal block: lane holds A[16n + 4lg + j][16n + l16]
+          // (no A without the delta rule: T = I, steps 4 and 5 are skipped)
+          if (DELTA) {
+          float dv[4];
+  #pragma unroll
           for (int j = 0; j < 4; ++j) {
-            v[j] = n == 2 ? md[j] : mo[2][j];
-            v[4 + j] = n == 3 ? md[j] : 0.f;
-          }
-          store_frag(rec, REC_M, n * 2 + 1, lane, v);
-        }
-      }
-
-      // ---- 4. T_nn = (I + A_nn)^-1 by column-oriented substitution -----------
-      // Lane c < 16 owns column c; A_nn's columns come from AT (written by this
-      // wave just above, so no barrier is needed).
-      if (DELTA && lane < SUB) {
-        const float* ATn = AT + n * 256;
-        float acc[SUB];
-#pragma unroll
-        for (int i = 0; i < SUB; ++i) acc[i] = (i == lane) ? 1.f : 0.f;
-#pragma unroll
-        for (int j = 0; j < SUB - 1; ++j) {
-          float col[SUB];
-#pragma unroll
-          for (int q = 0; q < SUB; q += 4) *reinterpret_cast<float4*>(&col[q]) = *reinterpret_cast<const float4*>(&ATn[j * SUB + q]);
-          const float xj = acc[j];
-#pragma unroll
-          for (int i = j + 1; i < SUB; ++i) acc[i] -= col[i] * xj;
-        }
-#pragma unroll
-        for (int i = 0; i < SUB; ++i) TM[(SUB * n + i) * MS + SUB * n + lane] = acc[i];
-      }
-      if (DELTA) __syncthreads();  // A rows, diagonal T blocks and Khat^T visible
-
-      // ---- 5. off-diagonal blocks of T, level by level (fp32 matrix cores) ----
-      //   T_ba = -T_bb * sum_{a<=j<b} A_bj T_ja
-#pragma unroll
-      for (int lev = 1; lev < (DELTA ? NSUB : 1); ++lev) {
-        if (wave < NSUB - lev) {
-          const int a = wave, b = wave + lev;
-          f32x4 Xs = zero4();
-          for (int j = a; j < b; ++j) {
-#pragma unroll
-            for (int s = 0; s < 4; ++s) {
-              const float av = AM[(SUB * b + l16) * MS + SUB * j + 4 * s + lg];
-              const float tv = TM[(SUB * j + 4 * s + lg) * MS + SUB * a + l16];
-              Xs = mma_f32(av, tv, Xs);
-            }
-          }
-          // contraction order permuted so that Xs's own C layout is the B operand
-          f32x4 Ys = zero4();
-#pragma unroll
-          for (int s = 0; s < 4; ++s) Ys = mma_f32(TM[(SUB * b + l16) * MS + SUB * b + 4 * lg + s], Xs[s], Ys);
-#pragma unroll
-          for (int j = 0; j < 4; ++j) TM[(SUB * b + 4 * lg + j) * MS + SUB * a + l16] = -Ys[j];
-        }
-        __syncthreads();
-      }
-
-      // ---- 6. -W^T = -Khat^T (T diag(b))^T and T diag(b) fragments -----------
-      {
-        const int t = wave, rt = SUB * t + l16;
-        const int ns = (t >> 1) + 1;  // token slices with nonzero T entries for this tile
-        f16x8 tbB[2];
-#pragma unroll
-        for (int s = 0; s < 2; ++s) {
-          float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-          if (s < ns) {
-            const int j0 = 32 * s + 4 * lg, j1 = j0 + 16;
-            float tv[8], bb[8];
-            if (DELTA) {
-              *reinterpret_cast<float4*>(&tv[0]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j0]);
-              *reinterpret_cast<float4*>(&tv[4]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j1]);
-            } else {  // T = I
-#pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                tv[q] = j0 + q == rt ? 1.f : 0.f;
-                tv[4 + q] = j1 + q == rt ? 1.f : 0.f;
+            const int rl = 4 * lg + j, il = l16;
+            float v = 0.f;
+            if (il < rl) {
+              if (flagged) v = TM[upper_off(N) + rl * MS + il];
+              else {
+                v = accA_d[j] * brow[j];
+                if (!PER_CHANNEL) v *= exp2f((grow[j] - gam(SUB * N + il)) * LOG2E);
               }
             }
-            *reinterpret_cast<float4*>(&bb[0]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j0]);
-            *reinterpret_cast<float4*>(&bb[4]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j1]);
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-              v[q] = (j0 + q <= rt) ? tv[q] * bb[q] : 0.f;
-              v[4 + q] = (j1 + q <= rt) ? tv[4 + q] * bb[4 + q] : 0.f;
-            }
-            store_frag(rec, REC_TB, t * 2 + s, lane, v);
+            dv[j] = v;
+            AM[(SUB * N + rl) * MS + SUB * N + il] = v;
           }
-          tbB[s] = to_f16x8(v);
-        }
-#pragma unroll
-        for (int sp = 0; sp < 4; ++sp) {
+          *reinterpret_cast<float4*>(&AT[N * 256 + l16 * 16 + 4 * lg]) = make_float4(dv[0], dv[1], dv[2], dv[3]);
+  #pragma unroll
+          for (int a = 0; a < 3; ++a) {
+            if (a < N) {
+              const float gi = PER_CHANNEL ? 0.f : gam(SUB * a + l16);
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) {
+                float v = accA[a][j] * brow[j];
+                if (!PER_CHANNEL) v *= exp2f((grow[j] - gi) * LOG2E);
+                AM[(SUB * N + 4 * lg + j) * MS + SUB * a + l16] = v;
+              }
+            }
+          }
+          }
+          // M^T blocks: lane holds M[16n + l16][16a + 4lg + j]
+          const float gr = PER_CHANNEL ? 0.f : gam(r);
+          float md[4], mo[3][4];
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            const int il = 4 * lg + j;
+            float v = 0.f;
+            if (il <= l16) {
+              if (flagged) v = AM[upper_off(N) + l16 * MS + il];
+              else {
+                v = accM_d[j];
+                if (!PER_CHANNEL) v *= exp2f((gr - gam(SUB * N + il)) * LOG2E);
+              }
+            }
+            md[j] = v;
+          }
+  #pragma unroll
+          for (int a = 0; a < 3; ++a)
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              float v = accM[a][j];
+              if (!PER_CHANNEL && a < N) v *= exp2f((gr - gam(SUB * a + 4 * lg + j)) * LOG2E);
+              mo[a][j] = v;
+            }
           float v[8];
-#pragma unroll
-          for (int hh = 0; hh < 2; ++hh) {
-            const int kt = 2 * sp + hh;
-            f32x4 acc = zero4();
-            if (DELTA) {  // W = 0 for decay-only attention
-              acc = mma_f16(KH[(kt * 2) * 64 + lane], tbB[0], acc);
-              if (ns > 1) acc = mma_f16(KH[(kt * 2 + 1) * 64 + lane], tbB[1], acc);
-            }
-#pragma unroll
-            for (int j = 0; j < 4; ++j) v[hh * 4 + j] = -acc[j];
+          // fragment (n, 0): blocks (n, 0), (n, 1)
+  #pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[j] = N == 0 ? md[j] : mo[0][j];
+            v[4 + j] = N == 0 ? 0.f : (N == 1 ? md[j] : mo[1][j]);
           }
-          store_frag(rec, REC_WNEG, t * 4 + sp, lane, v);
+          store_frag(rec, REC_M, N * 2, lane, v);
+          if (N >= 2) {  // fragment (n, 1): blocks (n, 2), (n, 3)
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) {
+              v[j] = N == 2 ? md[j] : mo[2][j];
+              v[4 + j] = N == 3 ? md[j] : 0.f;
+            }
+            store_frag(rec, REC_M, N * 2 + 1, lane, v);
+          }
         }
+
+        // ---- 4. T_nn = (I + A_nn)^-1 by column-oriented substitution -----------
+        // Lane c < 16 owns column c; A_nn's columns come from AT (written by this
+        // wave just above, so no barrier is needed).
+        if (DELTA && lane < SUB) {
+          const float* ATn = AT + N * 256;
+          float acc[SUB];
+  #pragma unroll
+          for (int i = 0; i < SUB; ++i) acc[i] = (i == lane) ? 1.f : 0.f;
+  #pragma unroll
+          for (int j = 0; j < SUB - 1; ++j) {
+            float col[SUB];
+  #pragma unroll
+            for (int q = 0; q < SUB; q += 4) *reinterpret_cast<float4*>(&col[q]) = *reinterpret_cast<const float4*>(&ATn[j * SUB + q]);
+            const float xj = acc[j];
+  #pragma unroll
+            for (int i = j + 1; i < SUB; ++i) acc[i] -= col[i] * xj;
+          }
+  #pragma unroll
+          for (int i = 0; i < SUB; ++i) TM[(SUB * N + i) * MS + SUB * N + lane] = acc[i];
+        }
+        if (DELTA) __syncthreads();  // A rows, diagonal T blocks and Khat^T visible
+
+        // ---- 5. off-diagonal blocks of T, level by level (fp32 matrix cores) ----
+        //   T_ba = -T_bb * sum_{a<=j<b} A_bj T_ja
+  #pragma unroll
+        for (int lev = 1; lev < (DELTA ? NSUB : 1); ++lev) {
+          if (N < NSUB - lev) {
+            const int a = N, b = N + lev;
+            f32x4 Xs = zero4();
+            for (int j = a; j < b; ++j) {
+  #pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                const float av = AM[(SUB * b + l16) * MS + SUB * j + 4 * s + lg];
+                const float tv = TM[(SUB * j + 4 * s + lg) * MS + SUB * a + l16];
+                Xs = mma_f32(av, tv, Xs);
+              }
+            }
+            // contraction order permuted so that Xs's own C layout is the B operand
+            f32x4 Ys = zero4();
+  #pragma unroll
+            for (int s = 0; s < 4; ++s) Ys = mma_f32(TM[(SUB * b + l16) * MS + SUB * b + 4 * lg + s], Xs[s], Ys);
+  #pragma unroll
+            for (int j = 0; j < 4; ++j) TM[(SUB * b + 4 * lg + j) * MS + SUB * a + l16] = -Ys[j];
+          }
+          __syncthreads();
+        }
+
+        // ---- 6. -W^T = -Khat^T (T diag(b))^T and T diag(b) fragments -----------
+        {
+          const int t = N, rt = SUB * t + l16;
+          const int ns = (t >> 1) + 1;  // token slices with nonzero T entries for this tile
+          f16x8 tbB[2];
+  #pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (s < ns) {
+              const int j0 = 32 * s + 4 * lg, j1 = j0 + 16;
+              float tv[8], bb[8];
+              if (DELTA) {
+                *reinterpret_cast<float4*>(&tv[0]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j0]);
+                *reinterpret_cast<float4*>(&tv[4]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j1]);
+              } else {  // T = I
+  #pragma unroll
+                for (int q = 0; q < 4; ++q) {
+                  tv[q] = j0 + q == rt ? 1.f : 0.f;
+                  tv[4 + q] = j1 + q == rt ? 1.f : 0.f;
+                }
+              }
+              *reinterpret_cast<float4*>(&bb[0]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j0]);
+              *reinterpret_cast<float4*>(&bb[4]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j1]);
+  #pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                v[q] = (j0 + q <= rt) ? tv[q] * bb[q] : 0.f;
+                v[4 + q] = (j1 + q <= rt) ? tv[4 + q] * bb[4 + q] : 0.f;
+              }
+              store_frag(rec, REC_TB, t * 2 + s, lane, v);
+            }
+            tbB[s] = to_f16x8(v);
+          }
+  #pragma unroll
+          for (int sp = 0; sp < 4; ++sp) {
+            float v[8];
+  #pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int kt = 2 * sp + hh;
+              f32x4 acc = zero4();
+              if (DELTA) {  // W = 0 for decay-only attention
+                acc = mma_f16(KH[(kt * 2) * 64 + lane], tbB[0], acc);
+                if (ns > 1) acc = mma_f16(KH[(kt * 2 + 1) * 64 + lane], tbB[1], acc);
+              }
+  #pragma unroll
+              for (int j = 0; j < 4; ++j) v[hh * 4 + j] = -acc[j];
+            }
+            store_frag(rec, REC_WNEG, t * 4 + sp, lane, v);
+          }
+        }
+      };
+      switch (n) {
+        case 0: steps3to6(std::integral_constant<int, 0>()); break;
+        case 1: steps3to6(std::integral_constant<int, 1>()); break;
+        case 2: steps3to6(std::integral_constant<int, 2>()); break;
+        default: steps3to6(std::integral_constant<int, 3>()); break;
       }
     }
   }
