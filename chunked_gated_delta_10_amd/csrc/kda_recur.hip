@@ -130,110 +130,199 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
   const int v0 = vt * VC;
   auto record = [&](int c) { return p.rec + ((size_t)(chunk0 + c) * p.H + h) * REC_BYTES; };
 
+  // Each role is instantiated per token tile TW (wave-uniform), so the
+  // lower-triangular blocks each tile needs resolve at compile time.
   if (wave < 4) {
     // ---- chain waves ---------------------------------------------------------
-    // S[j][i]: column tile j, key tile 2 tw + i; lane (column l16, keys 4lg..4lg+3)
-    const size_t sbase = ((size_t)n * p.H + h) * HD * HD + (size_t)(v0 + l16) * HD;
-    f32x4 S[NCT][2];
+    auto chain_role = [&](auto TWc) {
+      constexpr int TW = decltype(TWc)::value;
+      // S[j][i]: column tile j, key tile 2 tw + i; lane (column l16, keys 4lg..4lg+3)
+      const size_t sbase = ((size_t)n * p.H + h) * HD * HD + (size_t)(v0 + l16) * HD;
+      f32x4 S[NCT][2];
 #pragma unroll
-    for (int j = 0; j < NCT; ++j)
+      for (int j = 0; j < NCT; ++j)
 #pragma unroll
-      for (int i = 0; i < 2; ++i) {
-        const int k0 = SUB * (2 * tw + i) + 4 * lg;
-        S[j][i] = p.s0 ? StateIO<StT>::load(p.s0, sbase + (size_t)VT * j * HD + k0) : zero4();
-      }
-    const size_t vstride = (size_t)p.H * HD;
-    const int vq = tid & 3;  // this thread's value columns: v0 + 4 NCT vq ..
-    const uint16_t* vchain = p.v + ((size_t)tok0 * p.H + h) * HD + v0 + 4 * NCT * vq;
-    const int tl = tid < T_REC + T_V ? tid : 0;
-    const bool trec = tl < T_REC;
-    const int rec_line = min(vt * T_REC + (trec ? tl : 0), REC_LINES - 1);
-    const int vrow = (vt * T_V + (trec ? 0 : tl - T_REC)) >> 1, vhalf = (tl - T_REC) & 1;
-    auto load = [&](ChainFrags<NCT>& F, int c) {
-      const uint8_t* R = record(c);
+        for (int i = 0; i < 2; ++i) {
+          const int k0 = SUB * (2 * TW + i) + 4 * lg;
+          S[j][i] = p.s0 ? StateIO<StT>::load(p.s0, sbase + (size_t)VT * j * HD + k0) : zero4();
+        }
+      const size_t vstride = (size_t)p.H * HD;
+      const int vq = tid & 3;  // this thread's value columns: v0 + 4 NCT vq ..
+      const uint16_t* vchain = p.v + ((size_t)tok0 * p.H + h) * HD + v0 + 4 * NCT * vq;
+      const int tl = tid < T_REC + T_V ? tid : 0;
+      const bool trec = tl < T_REC;
+      const int rec_line = min(vt * T_REC + (trec ? tl : 0), REC_LINES - 1);
+      const int vrow = (vt * T_V + (trec ? 0 : tl - T_REC)) >> 1, vhalf = (tl - T_REC) & 1;
+      auto load = [&](ChainFrags<NCT>& F, int c) {
+        const uint8_t* R = record(c);
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        F.w[s2] = ldfrag(R, REC_WNEG, tw * 4 + s2, lane);
-        F.k[s2] = ldfrag(R, REC_KBAR, (2 * tw + (s2 >> 1)) * 2 + (s2 & 1), lane);
-      }
-      F.t[0] = ldfrag(R, REC_TB, tw * 2, lane);
-      F.t[1] = ldfrag(R, REC_TB, tw * 2 + (tw >= 2 ? 1 : 0), lane);
+        for (int s2 = 0; s2 < 4; ++s2) {
+          F.w[s2] = ldfrag(R, REC_WNEG, TW * 4 + s2, lane);
+          F.k[s2] = ldfrag(R, REC_KBAR, (2 * TW + (s2 >> 1)) * 2 + (s2 & 1), lane);
+        }
+        F.t[0] = ldfrag(R, REC_TB, TW * 2, lane);
+        F.t[1] = ldfrag(R, REC_TB, TW * 2 + (TW >= 2 ? 1 : 0), lane);
 #pragma unroll
-      for (int i = 0; i < 2; ++i)
-        F.gl[i] = *reinterpret_cast<const float4*>(R + REC_GL + 4 * (SUB * (2 * tw + i) + 4 * lg));
-      // rows past the chunk's end are clamped here and zeroed at use
-      const int Lc = min(CH, len - c * CH);
-      F.v = *reinterpret_cast<const decltype(F.v)*>(vchain + (size_t)c * CH * vstride +
-                                                      (size_t)min(tid >> 2, Lc - 1) * vstride);
-      const int ct = min(c + PF_AHEAD, last);
-      const uint32_t* tp;
-      if (trec) {
-        tp = reinterpret_cast<const uint32_t*>(record(ct) + (size_t)rec_line * LINE);
-      } else {
-        const int Lt = min(CH, len - ct * CH);
-        tp = reinterpret_cast<const uint32_t*>(p.v + ((size_t)(tok0 + ct * CH + min(vrow, Lt - 1)) * p.H + h) * HD +
-                                               vhalf * (LINE / 2));
-      }
-      F.touch = *tp;
-    };
-    uint32_t sink = 0;
-    auto step = [&](const ChainFrags<NCT>& F, int c) {
-      sink ^= F.touch;
-      const int L = min(CH, len - c * CH);
-      {
+        for (int i = 0; i < 2; ++i)
+          F.gl[i] = *reinterpret_cast<const float4*>(R + REC_GL + 4 * (SUB * (2 * TW + i) + 4 * lg));
+        // rows past the chunk's end are clamped here and zeroed at use
+        const int Lc = min(CH, len - c * CH);
+        F.v = *reinterpret_cast<const decltype(F.v)*>(vchain + (size_t)c * CH * vstride +
+                                                        (size_t)min(tid >> 2, Lc - 1) * vstride);
+        const int ct = min(c + PF_AHEAD, last);
+        const uint32_t* tp;
+        if (trec) {
+          tp = reinterpret_cast<const uint32_t*>(record(ct) + (size_t)rec_line * LINE);
+        } else {
+          const int Lt = min(CH, len - ct * CH);
+          tp = reinterpret_cast<const uint32_t*>(p.v + ((size_t)(tok0 + ct * CH + min(vrow, Lt - 1)) * p.H + h) * HD +
+                                                 vhalf * (LINE / 2));
+        }
+        F.touch = *tp;
+      };
+      uint32_t sink = 0;
+      auto step = [&](const ChainFrags<NCT>& F, int c) {
+        sink ^= F.touch;
+        const int L = min(CH, len - c * CH);
+        {
+#pragma unroll
+          for (int j = 0; j < NCT; ++j) {
+            f16x8 sb;
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+              sb[e] = (f16)S[j][0][e];
+              sb[4 + e] = (f16)S[j][1][e];
+            }
+            sbuf[j][TW * 64 + lane] = sb;
+          }
+          const int r = tid >> 2;
+          f16 vh[4 * NCT];
+          if constexpr (NCT == 1) {
+            unpack_bf16(r < L ? F.v : make_uint2(0u, 0u), vh);
+          } else {
+            const uint4 vv = r < L ? F.v : make_uint4(0u, 0u, 0u, 0u);
+            unpack_bf16(make_uint2(vv.x, vv.y), vh);
+            unpack_bf16(make_uint2(vv.z, vv.w), vh + 4);
+          }
+#pragma unroll
+          for (int e = 0; e < 4 * NCT; ++e) vsT[(4 * NCT * vq + e) * VS + r] = vh[e];
+        }
+        __syncthreads();  // A
 #pragma unroll
         for (int j = 0; j < NCT; ++j) {
-          f16x8 sb;
-#pragma unroll
-          for (int e = 0; e < 4; ++e) {
-            sb[e] = (f16)S[j][0][e];
-            sb[4 + e] = (f16)S[j][1][e];
+          if (!DELTA) {  // U = V: rows 16 tw + 4 lg .. +3 of column 16 j + l16
+            ubuf[j][TW * 64 + lane] = *reinterpret_cast<const f16x4*>(&vsT[(VT * j + l16) * VS + SUB * TW + 4 * lg]);
+            continue;
           }
-          sbuf[j][tw * 64 + lane] = sb;
-        }
-        const int r = tid >> 2;
-        f16 vh[4 * NCT];
-        if constexpr (NCT == 1) {
-          unpack_bf16(r < L ? F.v : make_uint2(0u, 0u), vh);
-        } else {
-          const uint4 vv = r < L ? F.v : make_uint4(0u, 0u, 0u, 0u);
-          unpack_bf16(make_uint2(vv.x, vv.y), vh);
-          unpack_bf16(make_uint2(vv.z, vv.w), vh + 4);
-        }
+          f16x8 sB[4];
 #pragma unroll
-        for (int e = 0; e < 4 * NCT; ++e) vsT[(4 * NCT * vq + e) * VS + r] = vh[e];
+          for (int s2 = 0; s2 < 4; ++s2) sB[s2] = sbuf[j][s2 * 64 + lane];
+          f32x4 U = zero4(), U2 = zero4();
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            if (s2 <= (TW >> 1)) {
+              const f16* vr = &vsT[(VT * j + l16) * VS + 32 * s2 + 4 * lg];
+              const f16x4 lo = *reinterpret_cast<const f16x4*>(vr);
+              const f16x4 hi = *reinterpret_cast<const f16x4*>(vr + 16);
+              const f16x8 vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
+              if (s2 == 0) U = mma_f16(F.t[0], vb, U);
+              else U2 = mma_f16(F.t[1], vb, U2);
+            }
+          }
+#pragma unroll
+          for (int s2 = 0; s2 < 4; ++s2) {
+            if (s2 & 1) U2 = mma_f16(F.w[s2], sB[s2], U2);
+            else U = mma_f16(F.w[s2], sB[s2], U);
+          }
+          ubuf[j][TW * 64 + lane] =
+              f16x4{(f16)(U[0] + U2[0]), (f16)(U[1] + U2[1]), (f16)(U[2] + U2[2]), (f16)(U[3] + U2[3])};
+        }
+        __syncthreads();  // B
+#pragma unroll
+        for (int j = 0; j < NCT; ++j) {
+          f16x8 uB[2];
+#pragma unroll
+          for (int s2 = 0; s2 < 2; ++s2) {
+            const f16x4 a = ubuf[j][(2 * s2) * 64 + lane], b = ubuf[j][(2 * s2 + 1) * 64 + lane];
+            uB[s2] = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+          }
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const f32x4 a = mma_f16(F.k[2 * i], uB[0],
+                                    f32x4{F.gl[i].x * S[j][i][0], F.gl[i].y * S[j][i][1], F.gl[i].z * S[j][i][2],
+                                          F.gl[i].w * S[j][i][3]});
+            const f32x4 b = mma_f16(F.k[2 * i + 1], uB[1], zero4());
+            S[j][i] = f32x4{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
+          }
+        }
+      };
+      ChainFrags<NCT> f0, f1, f2;
+      if (nch > 0) {
+        load(f0, 0);
+        load(f1, min(1, last));
       }
-      __syncthreads();  // A
+      __builtin_amdgcn_s_waitcnt(0);
+      for (int c = 0; c < nch; c += 3) {
+        load(f2, min(c + 2, last));
+        step(f0, c);
+        if (c + 1 >= nch) break;
+        load(f0, min(c + 3, last));
+        step(f1, c + 1);
+        if (c + 2 >= nch) break;
+        load(f1, min(c + 4, last));
+        step(f2, c + 2);
+      }
+      asm volatile("" ::"v"(sink));
+      if (p.s1) {
+#pragma unroll
+        for (int j = 0; j < NCT; ++j)
+#pragma unroll
+          for (int i = 0; i < 2; ++i) {
+            const int k0 = SUB * (2 * TW + i) + 4 * lg;
+            StateIO<StT>::store(p.s1, sbase + (size_t)VT * j * HD + k0, S[j][i]);
+          }
+      }
+    };
+    switch (tw) {
+      case 0: chain_role(std::integral_constant<int, 0>()); break;
+      case 1: chain_role(std::integral_constant<int, 1>()); break;
+      case 2: chain_role(std::integral_constant<int, 2>()); break;
+      default: chain_role(std::integral_constant<int, 3>()); break;
+    }
+    return;
+  }
+
+
+  // ---- output waves ----------------------------------------------------------
+  auto out_role = [&](auto TWc) {
+    constexpr int TW = decltype(TWc)::value;
+    const size_t row_step = (size_t)p.H * HD;
+    uint16_t* orow = p.out + ((size_t)(tok0 + SUB * TW + 4 * lg) * p.H + h) * HD + v0 + l16;
+    auto load = [&](OutFrags& F, int c) {
+      const uint8_t* R = record(c);
+#pragma unroll
+      for (int s2 = 0; s2 < 4; ++s2) F.q[s2] = ldfrag(R, REC_QHAT, TW * 4 + s2, lane);
+      F.m[0] = ldfrag(R, REC_M, TW * 2, lane);
+      F.m[1] = ldfrag(R, REC_M, TW * 2 + (TW >= 2 ? 1 : 0), lane);
+    };
+    auto step = [&](const OutFrags& F, int c) {
+      const int L = min(CH, len - c * CH);
+      __syncthreads();  // A: S_c slices published
+      f32x4 OQ[NCT];
 #pragma unroll
       for (int j = 0; j < NCT; ++j) {
-        if (!DELTA) {  // U = V: rows 16 tw + 4 lg .. +3 of column 16 j + l16
-          ubuf[j][tw * 64 + lane] = *reinterpret_cast<const f16x4*>(&vsT[(VT * j + l16) * VS + SUB * tw + 4 * lg]);
-          continue;
-        }
         f16x8 sB[4];
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) sB[s2] = sbuf[j][s2 * 64 + lane];
-        f32x4 U = zero4(), U2 = zero4();
-#pragma unroll
-        for (int s2 = 0; s2 < 2; ++s2) {
-          if (s2 <= (tw >> 1)) {
-            const f16* vr = &vsT[(VT * j + l16) * VS + 32 * s2 + 4 * lg];
-            const f16x4 lo = *reinterpret_cast<const f16x4*>(vr);
-            const f16x4 hi = *reinterpret_cast<const f16x4*>(vr + 16);
-            const f16x8 vb = {lo[0], lo[1], lo[2], lo[3], hi[0], hi[1], hi[2], hi[3]};
-            if (s2 == 0) U = mma_f16(F.t[0], vb, U);
-            else U2 = mma_f16(F.t[1], vb, U2);
-          }
-        }
+        f32x4 a = zero4(), b = zero4();
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-          if (s2 & 1) U2 = mma_f16(F.w[s2], sB[s2], U2);
-          else U = mma_f16(F.w[s2], sB[s2], U);
+          if (s2 & 1) b = mma_f16(F.q[s2], sB[s2], b);
+          else a = mma_f16(F.q[s2], sB[s2], a);
         }
-        ubuf[j][tw * 64 + lane] =
-            f16x4{(f16)(U[0] + U2[0]), (f16)(U[1] + U2[1]), (f16)(U[2] + U2[2]), (f16)(U[3] + U2[3])};
+        OQ[j] = f32x4{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
       }
-      __syncthreads();  // B
+      __syncthreads();  // B: U_c published
 #pragma unroll
       for (int j = 0; j < NCT; ++j) {
         f16x8 uB[2];
@@ -242,17 +331,19 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
           const f16x4 a = ubuf[j][(2 * s2) * 64 + lane], b = ubuf[j][(2 * s2 + 1) * 64 + lane];
           uB[s2] = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
         }
+        f32x4 O = mma_f16(F.m[0], uB[0], OQ[j]);
+        if (TW >= 2) O = mma_f16(F.m[1], uB[1], O);
 #pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const f32x4 a = mma_f16(F.k[2 * i], uB[0],
-                                  f32x4{F.gl[i].x * S[j][i][0], F.gl[i].y * S[j][i][1], F.gl[i].z * S[j][i][2],
-                                        F.gl[i].w * S[j][i][3]});
-          const f32x4 b = mma_f16(F.k[2 * i + 1], uB[1], zero4());
-          S[j][i] = f32x4{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
+        for (int e = 0; e < 4; ++e) {
+          const int r = SUB * TW + 4 * lg + e;
+          // rows past the chunk's end go to a sink, keeping the store unconditional
+          uint16_t* dst = r < L ? orow + (size_t)e * row_step + VT * j : p.sink + lane;
+          *dst = f32_to_bf16(p.scale * O[e]);
         }
       }
+      orow += (size_t)CH * row_step;
     };
-    ChainFrags<NCT> f0, f1, f2;
+    OutFrags f0, f1, f2;
     if (nch > 0) {
       load(f0, 0);
       load(f1, min(1, last));
@@ -268,82 +359,12 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
       load(f1, min(c + 4, last));
       step(f2, c + 2);
     }
-    asm volatile("" ::"v"(sink));
-    if (p.s1) {
-#pragma unroll
-      for (int j = 0; j < NCT; ++j)
-#pragma unroll
-        for (int i = 0; i < 2; ++i) {
-          const int k0 = SUB * (2 * tw + i) + 4 * lg;
-          StateIO<StT>::store(p.s1, sbase + (size_t)VT * j * HD + k0, S[j][i]);
-        }
-    }
-    return;
-  }
-
-  // ---- output waves ----------------------------------------------------------
-  const size_t row_step = (size_t)p.H * HD;
-  uint16_t* orow = p.out + ((size_t)(tok0 + SUB * tw + 4 * lg) * p.H + h) * HD + v0 + l16;
-  auto load = [&](OutFrags& F, int c) {
-    const uint8_t* R = record(c);
-#pragma unroll
-    for (int s2 = 0; s2 < 4; ++s2) F.q[s2] = ldfrag(R, REC_QHAT, tw * 4 + s2, lane);
-    F.m[0] = ldfrag(R, REC_M, tw * 2, lane);
-    F.m[1] = ldfrag(R, REC_M, tw * 2 + (tw >= 2 ? 1 : 0), lane);
   };
-  auto step = [&](const OutFrags& F, int c) {
-    const int L = min(CH, len - c * CH);
-    __syncthreads();  // A: S_c slices published
-    f32x4 OQ[NCT];
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      f16x8 sB[4];
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) sB[s2] = sbuf[j][s2 * 64 + lane];
-      f32x4 a = zero4(), b = zero4();
-#pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) {
-        if (s2 & 1) b = mma_f16(F.q[s2], sB[s2], b);
-        else a = mma_f16(F.q[s2], sB[s2], a);
-      }
-      OQ[j] = f32x4{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
-    }
-    __syncthreads();  // B: U_c published
-#pragma unroll
-    for (int j = 0; j < NCT; ++j) {
-      f16x8 uB[2];
-#pragma unroll
-      for (int s2 = 0; s2 < 2; ++s2) {
-        const f16x4 a = ubuf[j][(2 * s2) * 64 + lane], b = ubuf[j][(2 * s2 + 1) * 64 + lane];
-        uB[s2] = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
-      }
-      f32x4 O = mma_f16(F.m[0], uB[0], OQ[j]);
-      if (tw >= 2) O = mma_f16(F.m[1], uB[1], O);
-#pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int r = SUB * tw + 4 * lg + e;
-        // rows past the chunk's end go to a sink, keeping the store unconditional
-        uint16_t* dst = r < L ? orow + (size_t)e * row_step + VT * j : p.sink + lane;
-        *dst = f32_to_bf16(p.scale * O[e]);
-      }
-    }
-    orow += (size_t)CH * row_step;
-  };
-  OutFrags f0, f1, f2;
-  if (nch > 0) {
-    load(f0, 0);
-    load(f1, min(1, last));
-  }
-  __builtin_amdgcn_s_waitcnt(0);
-  for (int c = 0; c < nch; c += 3) {
-    load(f2, min(c + 2, last));
-    step(f0, c);
-    if (c + 1 >= nch) break;
-    load(f0, min(c + 3, last));
-    step(f1, c + 1);
-    if (c + 2 >= nch) break;
-    load(f1, min(c + 4, last));
-    step(f2, c + 2);
+  switch (tw) {
+    case 0: out_role(std::integral_constant<int, 0>()); break;
+    case 1: out_role(std::integral_constant<int, 1>()); break;
+    case 2: out_role(std::integral_constant<int, 2>()); break;
+    default: out_role(std::integral_constant<int, 3>()); break;
   }
 }
 
