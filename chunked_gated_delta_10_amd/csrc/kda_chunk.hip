@@ -68,6 +68,19 @@ constexpr int LDS_BYTES = L_FLAG + 8 * 4;
 static_assert(3 * 16 * 64 * 4 <= 16 * 64 * 16, "fallback scratch must fit in the Khat^T region");
 static_assert(2 * LDS_BYTES <= 160 * 1024, "two workgroups per CU");
 
+// Decay-only linear attention with one decay per token-head touches only YB
+// and ROW (no A, no inverse, no K-hat, no per-channel decay products, no
+// exact fallback), so it gets a compact layout and more jobs per CU.
+template <bool PER_CHANNEL, bool DELTA>
+struct Lds {
+  static constexpr bool COMPACT = !PER_CHANNEL && !DELTA;
+  static constexpr int YB = L_YB;
+  static constexpr int ROW = COMPACT ? L_KH : L_ROW;
+  static constexpr int FLAG = COMPACT ? ROW + (5 * CH + 8) * 4 : L_FLAG;
+  static constexpr int BYTES = COMPACT ? FLAG + 8 * 4 : LDS_BYTES;
+  static constexpr int JOBS_PER_CU = COMPACT ? 3 : 2;  // by registers (and LDS in the full layout)
+};
+
 // ROW sub-arrays (floats)
 constexpr int R_BETA = 0, R_RK = CH, R_RQ = 2 * CH, R_GP = 3 * CH, R_GS = 5 * CH;
 
@@ -155,17 +168,19 @@ __device__ __forceinline__ void load_rows(Pref& P, const ChunkParams& p, int4 ce
 // strength 1, A = 0 (so T = I) and W = 0 (K-hat is not formed), which makes
 // the recurrence's U equal to V.
 template <bool PER_CHANNEL, bool DELTA>
-__global__ __launch_bounds__(NT, 2) void chunk_local_kernel(const ChunkParams p, const int n_jobs) {
+__global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void chunk_local_kernel(const ChunkParams p,
+                                                                                                 const int n_jobs) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  f16x8* YB = reinterpret_cast<f16x8*>(smem + L_YB);
+  using LD = Lds<PER_CHANNEL, DELTA>;
+  f16x8* YB = reinterpret_cast<f16x8*>(smem + LD::YB);
   uint8_t* KHb = smem + L_KH;
   const f16x8* KH = reinterpret_cast<const f16x8*>(smem + L_KH);
   float* AM = reinterpret_cast<float*>(smem + L_AM);
   float* TM = reinterpret_cast<float*>(smem + L_TM);
   float* AT = reinterpret_cast<float*>(smem + L_AT);
   float* DS = reinterpret_cast<float*>(smem + L_DS);
-  float* ROW = reinterpret_cast<float*>(smem + L_ROW);
-  int* FLAG = reinterpret_cast<int*>(smem + L_FLAG);
+  float* ROW = reinterpret_cast<float*>(smem + LD::ROW);
+  int* FLAG = reinterpret_cast<int*>(smem + LD::FLAG);
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
@@ -712,11 +727,11 @@ void launch_chunk_variant(const ChunkParams& p, int n_jobs, hipStream_t stream) 
   static bool attr_set = false;
   if (!attr_set) {
     (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_local_kernel<PER_CHANNEL, DELTA>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, LDS_BYTES);
+                              hipFuncAttributeMaxDynamicSharedMemorySize, Lds<PER_CHANNEL, DELTA>::BYTES);
     attr_set = true;
   }
-  // one job per workgroup; two are resident per CU (LDS-bound)
-  chunk_local_kernel<PER_CHANNEL, DELTA><<<n_jobs, NT, LDS_BYTES, stream>>>(p, n_jobs);
+  // one job per workgroup; two (full layout, LDS-bound) or three (compact) per CU
+  chunk_local_kernel<PER_CHANNEL, DELTA><<<n_jobs, NT, Lds<PER_CHANNEL, DELTA>::BYTES, stream>>>(p, n_jobs);
 }
 }  // namespace
 
