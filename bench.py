@@ -220,25 +220,34 @@ def time_workload(name, steps, warmup, bf16_state=False):
     for _ in range(warmup):
         step()
     torch.cuda.synchronize()
-    kda.kernel_timing(True)
+    # 1. the timed steps.  The library's per-kernel events (diagnostic: they add ~20 us to a step) bracket
+    #    the launches of every 10th step only, so the kernel averages come from the timed region itself.
+    kda.kernel_timing(False)
     kda.kernel_timing_read()
-    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     t0 = time.perf_counter()
+    e0.record()
+    for i in range(steps):
+        kda.kernel_timing(i % 10 == 0)
+        step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t0
+    kda.kernel_timing(False)
+    kt = kda.kernel_timing_read()
+    ms = max(wall * 1000.0, e0.elapsed_time(e1)) / steps
+    per_kernel = {k: v[0] / v[1] for k, v in kt.items()}
+    # 2. per-step spread, with one event between steps (outside the timed region)
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     evs[0].record()
     for i in range(steps):
         step()
         evs[i + 1].record()
     torch.cuda.synchronize()
-    wall = time.perf_counter() - t0
-    kt = kda.kernel_timing_read()
-    kda.kernel_timing(False)
-    gpu_ms = evs[0].elapsed_time(evs[-1])
-    ms = max(wall * 1000.0, gpu_ms) / steps
     per_step = sorted(evs[i].elapsed_time(evs[i + 1]) for i in range(steps))
     pct = {"p10": round(per_step[int(0.1 * (steps - 1))], 4), "p50": round(per_step[int(0.5 * (steps - 1))], 4),
            "p90": round(per_step[int(0.9 * (steps - 1))], 4)}
-    per_kernel = {k: v[0] / v[1] for k, v in kt.items()}
     return ms, per_kernel, inp, w, pct
 
 
