@@ -200,20 +200,24 @@ kda_status run_forward(const FwdArgs& a) {
   int* order = reinterpret_cast<int*>(ws + L.order);
 
   (void)hipGetLastError();  // clear any stale error before launching
-  kda::TableParams tp{a.cu, a.n_seqs, a.T, n_entries, seqs, chunks, order};
-  {
+  // Packed sequences need the device schedule (sequence starts, chunk entries,
+  // longest-first order) built from cu_seqlens; B rows of T tokens do not:
+  // the kernels derive their schedule arithmetically.
+  if (a.cu) {
+    kda::TableParams tp{a.cu, a.n_seqs, a.T, n_entries, seqs, chunks, order};
     Timed t(K_TABLE, a.stream);
     kda::launch_table(tp, a.stream);
   }
   if (n_entries > 0 && tokens > 0) {
     kda::ChunkParams cp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                        static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log, chunks, a.H, a.H_qk, ws + L.rec};
+                        static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log, chunks, a.H, a.H_qk, ws + L.rec,
+                        a.cu ? 0 : a.T};
     Timed t(K_CHUNK, a.stream);
     kda::launch_chunk_local(cp, n_entries, a.gate_per_channel == 1, a.delta, a.stream);
   }
   kda::RecurParams rp{ws + L.rec, seqs, order, a.n_seqs * a.H, n_entries, a.H, static_cast<const uint16_t*>(a.v),
                       static_cast<uint16_t*>(a.out), a.s0, a.s1, a.scale,
-                      reinterpret_cast<uint16_t*>(ws + L.sink)};
+                      reinterpret_cast<uint16_t*>(ws + L.sink), a.cu ? -1 : a.T};
   {
     Timed t(K_RECUR, a.stream);
     kda::launch_recur(rp, bf16_state, a.delta, a.stream);

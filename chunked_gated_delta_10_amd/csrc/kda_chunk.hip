@@ -207,7 +207,13 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
   {
     const int job = blockIdx.x;
     const int e = __builtin_amdgcn_readfirstlane(job / H), h = __builtin_amdgcn_readfirstlane(job % H);
-    const int4 ce_cur = entry(e);
+    int4 ce_cur;
+    if (p.dense_T > 0) {  // B rows of T tokens: entry e is chunk e % NC of row e / NC
+      const int T = p.dense_T, nc = (T + CH - 1) / CH, b = e / nc, c = e - b * nc;
+      ce_cur = make_int4(b, b * T + c * CH, min(CH, T - c * CH), c);
+    } else {
+      ce_cur = entry(e);
+    }
     const int len = ce_cur.z;
     if (len > 0) {  // uniform over the workgroup
       Pref cur;

@@ -16,6 +16,7 @@ struct ChunkParams {
   const int4* chunks;     // schedule entries
   int H, H_qk;
   uint8_t* rec;           // [entries][H] chunk records
+  int dense_T;            // > 0: B rows of dense_T tokens, schedule by arithmetic; 0: read `chunks`
 };
 
 // Recurrence kernel (kda_recur.hip): one workgroup per (chain, value tile).
@@ -32,6 +33,7 @@ struct RecurParams {
   void* s1;               // same layout, or null
   float scale;
   uint16_t* sink;         // 64 scratch values: destination of output rows past a chunk's end
+  int dense_T;            // >= 0: B rows of dense_T tokens, schedule by arithmetic; -1: read `seqs`/`order`
 };
 
 // Decode kernel (kda_decode.hip): one workgroup per (batch row, head).

@@ -121,8 +121,17 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
   const int x = blockIdx.x, xcd = x & 7, y = x >> 3;
   const int vt = y % NW, ch = (y / NW) * 8 + xcd;
   if (ch >= p.n_chains) return;
-  const int n = p.order[ch / p.H], h = ch % p.H;
-  const int4 sq = p.seqs[n];
+  const int h = ch % p.H;
+  int n;
+  int4 sq;
+  if (p.dense_T >= 0) {  // B rows of T tokens, in row order
+    const int T = p.dense_T;
+    n = ch / p.H;
+    sq = make_int4(n * T, T, n * ((T + CH - 1) / CH), 0);
+  } else {
+    n = p.order[ch / p.H];
+    sq = p.seqs[n];
+  }
   const int tok0 = sq.x, len = sq.y, chunk0 = sq.z;
   // never walk past the schedule, whatever cu_seqlens held
   const int nch = max(0, min((len + CH - 1) / CH, p.n_entries - chunk0));
