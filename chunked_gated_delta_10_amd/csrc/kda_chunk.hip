@@ -40,7 +40,13 @@
 // with 0/1 selection matrices.  Only the fp16 Y operands, the sub-chunk decay
 // products and the 64 x 64 matrices A and T go through LDS (~69 KB), so two
 // workgroups share a CU and hide each other's latencies (one waits on its
-// loads while the other computes).  One workgroup per (chunk, head).
+// loads while the other computes).  One workgroup per (chunk, head); the
+// schedule entry comes from the schedule table for packed sequences and by
+// arithmetic for B rows of T tokens.
+//
+// Decay-only linear attention (DELTA = false) writes the same records with
+// the UT transform reduced to the identity: no q/k normalisation, b = 1,
+// A = 0 (T = I) and W = 0.
 #include <type_traits>
 
 #include "kda_device.h"

@@ -8,6 +8,8 @@
 //   o_v  = scale (c_v + u_v (qn . kn))   (since S_t^T qn = S'^T qn + (qn.kn) u)
 //   s_v  = s'_v + u_v kn
 // so the state streams through once: read 512 B, write 512 B per row.
+// Decay-only linear attention drops the normalisation, b and the erase:
+// u_v = v_v.
 //
 // Workgroup = one (batch row, head), 256 threads; a group of 16 lanes owns
 // one state row per step (8 key channels per lane, two 16-byte accesses that

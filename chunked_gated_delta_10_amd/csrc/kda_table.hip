@@ -1,5 +1,7 @@
 // kda_table.hip -- chunk schedule built on the device from cu_seqlens (or
-// from B rows of T tokens), so the host never reads the offsets.
+// from B rows of T tokens), so the host never reads the offsets.  The
+// forward pass launches it for packed sequences; for B rows of T tokens the
+// other kernels derive the same schedule arithmetically.
 //
 // Every sequence is cut into 64-token chunks starting at its first token
 // (chunking restarts at each sequence start; the last chunk may be short).
