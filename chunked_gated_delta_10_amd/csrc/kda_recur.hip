@@ -14,8 +14,11 @@
 // chunk c+1.  The fp16 copies of S and U travel between waves through LDS.
 //
 // Workgroups of one chain are given ids congruent mod 8 so they land on the
-// same XCD and share its L2 for the chunk records, and each of them warms a
-// later record's share in that L2.
+// same XCD and share its L2 for the chunk records.  In the one-tile form
+// (eight workgroups per chain) each of them also warms its share of the
+// record two chunks ahead in that L2; with two tiles per workgroup (many
+// chains, the grid runs in rounds) the touches only add HBM requests and are
+// left out (measured: grouped-head recurrence 0.93 -> 0.83 ms without them).
 #include "kda_device.h"
 #include "kda_kernels.h"
 
@@ -27,7 +30,7 @@ constexpr int VT = 16;        // value columns per workgroup
 constexpr int NVT = HD / VT;  // value tiles per chain
 constexpr int VS = CH + 8;    // row stride (fp16) of the transposed value tile
 
-constexpr int PF_AHEAD = 3;                          // chunks the L2 touches run ahead of the loads
+constexpr int PF_AHEAD = 2;                          // chunks the L2 touches run ahead of the loads
 constexpr int LINE = 128;                            // L2 line bytes
 constexpr int REC_LINES = (REC_BYTES + LINE - 1) / LINE;
 
@@ -73,8 +76,8 @@ __device__ __forceinline__ f16x8 ldfrag(const uint8_t* rec, int off, int frag, i
 // U, key tiles 2w, 2w+1 of S) and waves 4..7 only the output (token tile
 // w-4), so the output work of chunk c overlaps the chain of chunk c+1.  Each
 // role streams its own fragments through three register sets, two chunks
-// ahead; the chain waves also issue the L2 touches.  Both roles meet at the
-// same two barriers per chunk.
+// ahead; in the one-tile form the chain waves also issue the L2 touches.
+// Both roles meet at the same two barriers per chunk.
 //
 // A workgroup owns NCT adjacent 16-column tiles.  Every fragment of the
 // chunk record is loaded once per workgroup and used for all NCT tiles, so
@@ -178,16 +181,20 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
         const int Lc = min(CH, len - c * CH);
         F.v = *reinterpret_cast<const decltype(F.v)*>(vchain + (size_t)c * CH * vstride +
                                                         (size_t)min(tid >> 2, Lc - 1) * vstride);
-        const int ct = min(c + PF_AHEAD, last);
-        const uint32_t* tp;
-        if (trec) {
-          tp = reinterpret_cast<const uint32_t*>(record(ct) + (size_t)rec_line * LINE);
+        if constexpr (NCT == 1) {
+          const int ct = min(c + PF_AHEAD, last);
+          const uint32_t* tp;
+          if (trec) {
+            tp = reinterpret_cast<const uint32_t*>(record(ct) + (size_t)rec_line * LINE);
+          } else {
+            const int Lt = min(CH, len - ct * CH);
+            tp = reinterpret_cast<const uint32_t*>(p.v + ((size_t)(tok0 + ct * CH + min(vrow, Lt - 1)) * p.H + h) *
+                                                       HD + vhalf * (LINE / 2));
+          }
+          F.touch = *tp;
         } else {
-          const int Lt = min(CH, len - ct * CH);
-          tp = reinterpret_cast<const uint32_t*>(p.v + ((size_t)(tok0 + ct * CH + min(vrow, Lt - 1)) * p.H + h) * HD +
-                                                 vhalf * (LINE / 2));
+          F.touch = 0u;
         }
-        F.touch = *tp;
       };
       uint32_t sink = 0;
       auto step = [&](const ChainFrags<NCT>& F, int c) {
