@@ -215,12 +215,12 @@ kda_status run_forward(const FwdArgs& a) {
     Timed t(K_CHUNK, a.stream);
     kda::launch_chunk_local(cp, n_entries, a.gate_per_channel == 1, a.delta, a.stream);
   }
-  kda::RecurParams rp{ws + L.rec, seqs, order, a.n_seqs * a.H, n_entries, a.H, static_cast<const uint16_t*>(a.v),
+  kda::RecurParams rp{ws + L.rec, seqs, order, a.n_seqs * a.H, n_entries, a.H, a.H_qk, static_cast<const uint16_t*>(a.v),
                       static_cast<uint16_t*>(a.out), a.s0, a.s1, a.scale,
                       reinterpret_cast<uint16_t*>(ws + L.sink), a.cu ? -1 : a.T};
   {
     Timed t(K_RECUR, a.stream);
-    kda::launch_recur(rp, bf16_state, a.delta, a.stream);
+    kda::launch_recur(rp, bf16_state, a.gate_per_channel == 1, a.delta, a.stream);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));

@@ -28,7 +28,9 @@
 // run on fp32 matrix cores (exact fp32 products) while D_b >= 2^-100 and fall
 // back to an exact per-channel evaluation in the log domain otherwise.
 // In scalar-gate mode exp(Gamma_r - Gamma_i) is one number per (r, i) and is
-// applied after the Gram products.
+// applied after the Gram products; with value heads grouped on q/k heads the
+// records keep the group's qn and kn^T once and the per-token factors
+// exp(Gamma_r), exp(Gamma_L - Gamma_r) per head (SHARE).
 //
 // Work layout: 4 waves, wave n owns sub-chunk n.  Lane (l16, g) of wave n
 // holds token 16n + l16 and the 32 key channels
@@ -173,9 +175,14 @@ __device__ __forceinline__ void load_rows(Pref& P, const ChunkParams& p, int4 ce
 // the UT transform reduced to the identity: no q/k normalisation, write
 // strength 1, A = 0 (so T = I) and W = 0 (K-hat is not formed), which makes
 // the recurrence's U equal to V.
-template <bool PER_CHANNEL, bool DELTA>
+// SHARE (scalar gate with value heads grouped on q/k heads): the record keeps
+// qn and kn^T in the slots of Qhat and Kbar^T, written only by the first
+// value head of each group, and the per-token factors exp(Gamma_r) and
+// exp(Gamma_L - Gamma_r) in its last block; the recurrence scales rows.
+template <bool PER_CHANNEL, bool DELTA, bool SHARE>
 __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void chunk_local_kernel(const ChunkParams p,
                                                                                                  const int n_jobs) {
+  static_assert(!(SHARE && PER_CHANNEL), "shared q/k fragments need a scalar gate");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   using LD = Lds<PER_CHANNEL, DELTA>;
   f16x8* YB = reinterpret_cast<f16x8*>(smem + LD::YB);
@@ -425,6 +432,13 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
       }
       const float EGr = PER_CHANNEL ? 0.f : exp2f(Gr * LOG2E);
       const float EGLr = PER_CHANNEL ? 0.f : exp2f((GL - Gr) * LOG2E);
+      // SHARE: only the group's first value head writes qn and kn^T
+      const bool lead = !SHARE || h % (H / p.H_qk) == 0;
+      if (SHARE && lg == 0) {
+        float* gl = reinterpret_cast<float*>(rec + REC_GL);
+        gl[r] = EGr;
+        gl[CH + r] = EGLr;
+      }
       // The slice loop is instantiated per sub-chunk index N (wave-uniform), so
       // the decay products and the (N, a < N) blocks resolve at compile time.
       auto step2 = [&](auto Nc) {
@@ -461,11 +475,11 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
               lam[q] = 1.f;
             }
           }
-          // Qhat fragment (N, s) straight from registers
-          {
+          // Qhat fragment (N, s) straight from registers (scalar gate: qn)
+          if (lead) {
             float v[8];
   #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = Q[8 * s + q] * ep[q];
+            for (int q = 0; q < 8; ++q) v[q] = SHARE ? Q[8 * s + q] : Q[8 * s + q] * ep[q];
             store_frag(rec, REC_QHAT, N * 4 + s, lane, v);
           }
           // Khat and Kbar of this sub-chunk, transposed by selection products
@@ -474,7 +488,7 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
   #pragma unroll
             for (int q = 0; q < 8; ++q) {
               kh[q] = DELTA ? (f16)(X[8 * s + q] * ep[q]) : (f16)0.f;
-              kb[q] = (f16)((PER_CHANNEL ? Y[8 * s + q] : X[8 * s + q]) * eg[q]);
+              kb[q] = SHARE ? (f16)X[8 * s + q] : (f16)((PER_CHANNEL ? Y[8 * s + q] : X[8 * s + q]) * eg[q]);
             }
   #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
@@ -484,9 +498,12 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
                 const f16x4 th4 = {(f16)th[0], (f16)th[1], (f16)th[2], (f16)th[3]};
                 *reinterpret_cast<f16x4*>(KHb + ((kt * 2 + (N >> 1)) * 64 + lane) * 16 + (N & 1) * 8) = th4;
               }
-              const f32x4 tb = mma_f16(kb, sel[hh], zero4());
-              const f16x4 tb4 = {(f16)tb[0], (f16)tb[1], (f16)tb[2], (f16)tb[3]};
-              *reinterpret_cast<f16x4*>(rec + REC_KBAR + (kt * 2 + (N >> 1)) * FRAG_BYTES + lane * 16 + (N & 1) * 8) = tb4;
+              if (lead) {  // Kbar^T (scalar gate: kn^T)
+                const f32x4 tb = mma_f16(kb, sel[hh], zero4());
+                const f16x4 tb4 = {(f16)tb[0], (f16)tb[1], (f16)tb[2], (f16)tb[3]};
+                *reinterpret_cast<f16x4*>(rec + REC_KBAR + (kt * 2 + (N >> 1)) * FRAG_BYTES + lane * 16 + (N & 1) * 8) =
+                    tb4;
+              }
             }
           }
           // blocks (N, a), a < N: (X lam) Y_a^T and Y_a (Q lam)^T
@@ -521,7 +538,7 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
         case 2: step2(std::integral_constant<int, 2>()); break;
         default: step2(std::integral_constant<int, 3>()); break;
       }
-      if (tid < HD) {  // exp(Gamma_L) per key
+      if (!SHARE && tid < HD) {  // exp(Gamma_L) per key
         const float gl = PER_CHANNEL ? DS[tid] * DS[HD + tid] * DS[2 * HD + tid] * DS[3 * HD + tid]
                                      : exp2f(GL * LOG2E);
         *reinterpret_cast<float*>(rec + REC_GL + 4 * tid) = gl;
@@ -734,28 +751,33 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
 }
 
 namespace {
-template <bool PER_CHANNEL, bool DELTA>
+template <bool PER_CHANNEL, bool DELTA, bool SHARE>
 void launch_chunk_variant(const ChunkParams& p, int n_jobs, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_local_kernel<PER_CHANNEL, DELTA>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_local_kernel<PER_CHANNEL, DELTA, SHARE>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, Lds<PER_CHANNEL, DELTA>::BYTES);
     attr_set = true;
   }
   // one job per workgroup; two (full layout, LDS-bound) or three (compact) per CU
-  chunk_local_kernel<PER_CHANNEL, DELTA><<<n_jobs, NT, Lds<PER_CHANNEL, DELTA>::BYTES, stream>>>(p, n_jobs);
+  chunk_local_kernel<PER_CHANNEL, DELTA, SHARE><<<n_jobs, NT, Lds<PER_CHANNEL, DELTA>::BYTES, stream>>>(p, n_jobs);
 }
 }  // namespace
+
+bool shares_qk_fragments(bool per_channel, int H, int H_qk) { return !per_channel && H != H_qk; }
 
 void launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, bool delta, hipStream_t stream) {
   const int n_jobs = n_entries * p.H;
   if (n_jobs <= 0) return;
+  const bool share = shares_qk_fragments(per_channel, p.H, p.H_qk);
   if (delta) {
-    if (per_channel) launch_chunk_variant<true, true>(p, n_jobs, stream);
-    else launch_chunk_variant<false, true>(p, n_jobs, stream);
+    if (per_channel) launch_chunk_variant<true, true, false>(p, n_jobs, stream);
+    else if (share) launch_chunk_variant<false, true, true>(p, n_jobs, stream);
+    else launch_chunk_variant<false, true, false>(p, n_jobs, stream);
   } else {
-    if (per_channel) launch_chunk_variant<true, false>(p, n_jobs, stream);
-    else launch_chunk_variant<false, false>(p, n_jobs, stream);
+    if (per_channel) launch_chunk_variant<true, false, false>(p, n_jobs, stream);
+    else if (share) launch_chunk_variant<false, false, true>(p, n_jobs, stream);
+    else launch_chunk_variant<false, false, false>(p, n_jobs, stream);
   }
 }
 

@@ -41,6 +41,12 @@ constexpr int NSUB = CH / SUB;
 //   m[t][s]     M (decayed q.k, i <= r)    A operand, token tile t, token slice s
 //   tb[t][s]    T diag(b)                  A operand, token tile t, token slice s
 //   gl[k]       exp(Gamma_last)[k], fp32
+// Scalar gate with value heads grouped on q/k heads (one decay per
+// token-head, so exp(Gamma) scales whole rows): qhat holds qn and kbar holds
+// kn^T, both written only in the record of the group's first value head and
+// read by all heads of the group, and gl holds exp(Gamma_r) (r < 64)
+// followed by exp(Gamma_last - Gamma_r); exp(Gamma_last) = gl[63], since
+// rows past a chunk's end carry no decay.
 // ---------------------------------------------------------------------------
 constexpr int FRAG_HALVES = 64 * 8;                   // fp16 elements per fragment
 constexpr int FRAG_BYTES = FRAG_HALVES * 2;           // 1024

@@ -26,7 +26,7 @@ struct RecurParams {
   const int* order;       // sequences in processing order (longest first)
   int n_chains;           // sequences * H
   int n_entries;          // schedule entries (records per head)
-  int H;
+  int H, H_qk;
   const uint16_t* v;      // bf16 [tokens, H, 128]
   uint16_t* out;          // bf16 [tokens, H, 128]
   const void* s0;         // [seqs, H, 128, 128] fp32 or bf16, or null
@@ -64,7 +64,10 @@ struct TableParams {
 void launch_table(const TableParams& p, hipStream_t stream);
 // delta = false: decay-only linear attention (no erase, no write strength, no q/k normalisation)
 void launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, bool delta, hipStream_t stream);
-void launch_recur(const RecurParams& p, bool bf16_state, bool delta, hipStream_t stream);
+void launch_recur(const RecurParams& p, bool bf16_state, bool per_channel, bool delta, hipStream_t stream);
+// Scalar gate with value heads grouped on q/k heads: the value heads of a
+// group share one copy of the qn and kn^T record fragments.
+bool shares_qk_fragments(bool per_channel, int H, int H_qk);
 int recur_grid(int n_chains);
 void launch_decode(const DecodeParams& p, int B, bool bf16_state, bool per_channel, bool delta, hipStream_t stream);
 

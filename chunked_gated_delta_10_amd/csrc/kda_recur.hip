@@ -95,6 +95,7 @@ struct ChainFrags {
 };
 struct OutFrags {
   f16x8 q[4], m[2];
+  float4 eg;  // scalar gate: exp(Gamma_r) of this lane's four output rows
 };
 
 __device__ __forceinline__ void unpack_bf16(uint2 x, f16* o) {
@@ -107,7 +108,17 @@ __device__ __forceinline__ void unpack_bf16(uint2 x, f16* o) {
 // DELTA = false (decay-only linear attention): the chunk records carry
 // T diag(b) = I and W = 0, so U = V is read straight from the value tile and
 // neither W nor T diag(b) is loaded.
-template <typename StT, int NCT, bool DELTA>
+//
+// PC = false (one decay per token-head, value heads grouped on q/k heads,
+// records with shared q/k fragments): Qhat = diag(exp(Gamma)) qn and
+// Kbar^T = kn^T diag(exp(Gamma_L - Gamma)), so the record of the first value
+// head of each q/k group holds qn and kn^T for the whole group and every
+// record holds the two per-token factors.  The output waves scale the rows of
+// qn S by exp(Gamma_r); the chain waves scale U's rows by
+// exp(Gamma_L - Gamma_r) (a second LDS copy, since M U needs U itself) and
+// decay S by the single exp(Gamma_L).  A group's chains get the same XCD, so
+// its shared fragments are read from HBM once.
+template <typename StT, int NCT, bool DELTA, bool PC>
 __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
   constexpr int VC = VT * NCT;       // value columns per workgroup
   constexpr int NW = NVT / NCT;      // workgroups per chain
@@ -116,15 +127,19 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
   static_assert(T_REC + T_V <= 256, "one touch per chain thread");
   __shared__ __attribute__((aligned(16))) f16x8 sbuf[NCT][4 * 64];  // S slices (B operand)
   __shared__ __attribute__((aligned(16))) f16x4 ubuf[NCT][4 * 64];  // U tiles (C layout)
+  __shared__ __attribute__((aligned(16))) f16x4 ubuf2[PC ? 1 : NCT][4 * 64];  // scalar gate: decayed U tiles
   __shared__ __attribute__((aligned(16))) f16 vsT[VC * VS];         // value tile, [column][token]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
   const int tw = wave & 3;
   const int x = blockIdx.x, xcd = x & 7, y = x >> 3;
-  const int vt = y % NW, ch = (y / NW) * 8 + xcd;
+  // chains are dealt to XCDs in runs of G (the value heads of one q/k group)
+  const int G = PC ? 1 : p.H / p.H_qk;
+  const int vt = y % NW, slot = y / NW, blk = slot / G;
+  const int ch = blk * 8 * G + G * xcd + (slot - blk * G);
   if (ch >= p.n_chains) return;
-  const int h = ch % p.H;
+  const int h = ch % p.H, h0 = h - h % G;  // h0: the group's first value head
   int n;
   int4 sq;
   if (p.dense_T >= 0) {  // B rows of T tokens, in row order
@@ -141,6 +156,7 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
   const int last = nch - 1;
   const int v0 = vt * VC;
   auto record = [&](int c) { return p.rec + ((size_t)(chunk0 + c) * p.H + h) * REC_BYTES; };
+  auto shared_record = [&](int c) { return p.rec + ((size_t)(chunk0 + c) * p.H + h0) * REC_BYTES; };
 
   // Each role is instantiated per token tile TW (wave-uniform), so the
   // lower-triangular blocks each tile needs resolve at compile time.
@@ -167,16 +183,22 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
       const int vrow = (vt * T_V + (trec ? 0 : tl - T_REC)) >> 1, vhalf = (tl - T_REC) & 1;
       auto load = [&](ChainFrags<NCT>& F, int c) {
         const uint8_t* R = record(c);
+        const uint8_t* RK = PC ? R : shared_record(c);
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
           F.w[s2] = ldfrag(R, REC_WNEG, TW * 4 + s2, lane);
-          F.k[s2] = ldfrag(R, REC_KBAR, (2 * TW + (s2 >> 1)) * 2 + (s2 & 1), lane);
+          F.k[s2] = ldfrag(RK, REC_KBAR, (2 * TW + (s2 >> 1)) * 2 + (s2 & 1), lane);
         }
         F.t[0] = ldfrag(R, REC_TB, TW * 2, lane);
         F.t[1] = ldfrag(R, REC_TB, TW * 2 + (TW >= 2 ? 1 : 0), lane);
+        if (PC) {  // exp(Gamma_L) of this lane's state rows
 #pragma unroll
-        for (int i = 0; i < 2; ++i)
-          F.gl[i] = *reinterpret_cast<const float4*>(R + REC_GL + 4 * (SUB * (2 * TW + i) + 4 * lg));
+          for (int i = 0; i < 2; ++i)
+            F.gl[i] = *reinterpret_cast<const float4*>(R + REC_GL + 4 * (SUB * (2 * TW + i) + 4 * lg));
+        } else {   // exp(Gamma_L - Gamma_r) of this lane's U rows; exp(Gamma_L) = exp(Gamma) of the last row
+          F.gl[0] = *reinterpret_cast<const float4*>(R + REC_GL + 4 * (CH + SUB * TW + 4 * lg));
+          F.gl[1] = *reinterpret_cast<const float4*>(R + REC_GL + 4 * (CH - 4));
+        }
         // rows past the chunk's end are clamped here and zeroed at use
         const int Lc = min(CH, len - c * CH);
         F.v = *reinterpret_cast<const decltype(F.v)*>(vchain + (size_t)c * CH * vstride +
@@ -227,7 +249,11 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
 #pragma unroll
         for (int j = 0; j < NCT; ++j) {
           if (!DELTA) {  // U = V: rows 16 tw + 4 lg .. +3 of column 16 j + l16
-            ubuf[j][TW * 64 + lane] = *reinterpret_cast<const f16x4*>(&vsT[(VT * j + l16) * VS + SUB * TW + 4 * lg]);
+            const f16x4 u = *reinterpret_cast<const f16x4*>(&vsT[(VT * j + l16) * VS + SUB * TW + 4 * lg]);
+            ubuf[j][TW * 64 + lane] = u;
+            if (!PC)
+              ubuf2[j][TW * 64 + lane] = f16x4{(f16)((float)u[0] * F.gl[0].x), (f16)((float)u[1] * F.gl[0].y),
+                                               (f16)((float)u[2] * F.gl[0].z), (f16)((float)u[3] * F.gl[0].w)};
             continue;
           }
           f16x8 sB[4];
@@ -250,23 +276,27 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
             if (s2 & 1) U2 = mma_f16(F.w[s2], sB[s2], U2);
             else U = mma_f16(F.w[s2], sB[s2], U);
           }
-          ubuf[j][TW * 64 + lane] =
-              f16x4{(f16)(U[0] + U2[0]), (f16)(U[1] + U2[1]), (f16)(U[2] + U2[2]), (f16)(U[3] + U2[3])};
+          const f32x4 Us = {U[0] + U2[0], U[1] + U2[1], U[2] + U2[2], U[3] + U2[3]};
+          ubuf[j][TW * 64 + lane] = f16x4{(f16)Us[0], (f16)Us[1], (f16)Us[2], (f16)Us[3]};
+          if (!PC)
+            ubuf2[j][TW * 64 + lane] = f16x4{(f16)(Us[0] * F.gl[0].x), (f16)(Us[1] * F.gl[0].y),
+                                             (f16)(Us[2] * F.gl[0].z), (f16)(Us[3] * F.gl[0].w)};
         }
         __syncthreads();  // B
 #pragma unroll
         for (int j = 0; j < NCT; ++j) {
           f16x8 uB[2];
+          const f16x4* ub = PC ? ubuf[j] : ubuf2[PC ? 0 : j];
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
-            const f16x4 a = ubuf[j][(2 * s2) * 64 + lane], b = ubuf[j][(2 * s2 + 1) * 64 + lane];
+            const f16x4 a = ub[(2 * s2) * 64 + lane], b = ub[(2 * s2 + 1) * 64 + lane];
             uB[s2] = f16x8{a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
           }
 #pragma unroll
           for (int i = 0; i < 2; ++i) {
+            const float4 d = PC ? F.gl[i] : make_float4(F.gl[1].w, F.gl[1].w, F.gl[1].w, F.gl[1].w);
             const f32x4 a = mma_f16(F.k[2 * i], uB[0],
-                                    f32x4{F.gl[i].x * S[j][i][0], F.gl[i].y * S[j][i][1], F.gl[i].z * S[j][i][2],
-                                          F.gl[i].w * S[j][i][3]});
+                                    f32x4{d.x * S[j][i][0], d.y * S[j][i][1], d.z * S[j][i][2], d.w * S[j][i][3]});
             const f32x4 b = mma_f16(F.k[2 * i + 1], uB[1], zero4());
             S[j][i] = f32x4{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
           }
@@ -316,10 +346,12 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
     uint16_t* orow = p.out + ((size_t)(tok0 + SUB * TW + 4 * lg) * p.H + h) * HD + v0 + l16;
     auto load = [&](OutFrags& F, int c) {
       const uint8_t* R = record(c);
+      const uint8_t* RQ = PC ? R : shared_record(c);
 #pragma unroll
-      for (int s2 = 0; s2 < 4; ++s2) F.q[s2] = ldfrag(R, REC_QHAT, TW * 4 + s2, lane);
+      for (int s2 = 0; s2 < 4; ++s2) F.q[s2] = ldfrag(RQ, REC_QHAT, TW * 4 + s2, lane);
       F.m[0] = ldfrag(R, REC_M, TW * 2, lane);
       F.m[1] = ldfrag(R, REC_M, TW * 2 + (TW >= 2 ? 1 : 0), lane);
+      if (!PC) F.eg = *reinterpret_cast<const float4*>(R + REC_GL + 4 * (SUB * TW + 4 * lg));
     };
     auto step = [&](const OutFrags& F, int c) {
       const int L = min(CH, len - c * CH);
@@ -337,6 +369,7 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
           else a = mma_f16(F.q[s2], sB[s2], a);
         }
         OQ[j] = f32x4{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
+        if (!PC) OQ[j] = f32x4{OQ[j][0] * F.eg.x, OQ[j][1] * F.eg.y, OQ[j][2] * F.eg.z, OQ[j][3] * F.eg.w};
       }
       __syncthreads();  // B: U_c published
 #pragma unroll
@@ -385,8 +418,11 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
 }
 
 namespace {
-// workgroups for n_chains chains with `tiles` workgroups per chain
-int grid_for(int n_chains, int tiles) { return ((n_chains + 7) / 8) * 8 * tiles; }
+// workgroups for n_chains chains with `tiles` workgroups per chain, chains
+// dealt to the 8 XCDs in runs of `group`
+int grid_for(int n_chains, int tiles, int group = 1) {
+  return ((n_chains + 8 * group - 1) / (8 * group)) * 8 * group * tiles;
+}
 
 int cu_count() {
   static int cus = 0;
@@ -405,23 +441,31 @@ int recur_grid(int n_chains) {
 }
 
 namespace {
-template <bool DELTA>
+template <bool DELTA, bool PC>
 void launch_recur_variant(const RecurParams& p, bool bf16_state, hipStream_t stream) {
-  const int g = grid_for(p.n_chains, NVT);
-  if (g <= cu_count()) {  // few chains: one column tile per workgroup, all on CUs of their own
-    if (bf16_state) recur_split_kernel<uint16_t, 1, DELTA><<<g, 512, 0, stream>>>(p);
-    else recur_split_kernel<float, 1, DELTA><<<g, 512, 0, stream>>>(p);
+  const int G = PC ? 1 : p.H / p.H_qk;
+  if (grid_for(p.n_chains, NVT) <= cu_count()) {  // few chains: one column tile per workgroup, all on CUs of their own
+    const int g = grid_for(p.n_chains, NVT, G);
+    if (bf16_state) recur_split_kernel<uint16_t, 1, DELTA, PC><<<g, 512, 0, stream>>>(p);
+    else recur_split_kernel<float, 1, DELTA, PC><<<g, 512, 0, stream>>>(p);
     return;
   }
-  const int g2 = grid_for(p.n_chains, NVT / 2);  // two column tiles per workgroup
-  if (bf16_state) recur_split_kernel<uint16_t, 2, DELTA><<<g2, 512, 0, stream>>>(p);
-  else recur_split_kernel<float, 2, DELTA><<<g2, 512, 0, stream>>>(p);
+  const int g2 = grid_for(p.n_chains, NVT / 2, G);  // two column tiles per workgroup
+  if (bf16_state) recur_split_kernel<uint16_t, 2, DELTA, PC><<<g2, 512, 0, stream>>>(p);
+  else recur_split_kernel<float, 2, DELTA, PC><<<g2, 512, 0, stream>>>(p);
 }
 }  // namespace
 
-void launch_recur(const RecurParams& p, bool bf16_state, bool delta, hipStream_t stream) {
-  if (delta) launch_recur_variant<true>(p, bf16_state, stream);
-  else launch_recur_variant<false>(p, bf16_state, stream);
+void launch_recur(const RecurParams& p, bool bf16_state, bool per_channel, bool delta, hipStream_t stream) {
+  // records without shared q/k fragments carry Qhat, Kbar^T and exp(Gamma_L) per key
+  if (!shares_qk_fragments(per_channel, p.H, p.H_qk)) per_channel = true;
+  if (delta) {
+    if (per_channel) launch_recur_variant<true, true>(p, bf16_state, stream);
+    else launch_recur_variant<true, false>(p, bf16_state, stream);
+  } else {
+    if (per_channel) launch_recur_variant<false, true>(p, bf16_state, stream);
+    else launch_recur_variant<false, false>(p, bf16_state, stream);
+  }
 }
 
 }  // namespace kda

@@ -87,6 +87,14 @@ def test_grouped_heads():
     check(inp, what="la grouped heads 2->8")
 
 
+def test_grouped_heads_packed_with_state():
+    # value heads grouped on q/k heads share the q/k record fragments
+    lens = [70, 0, 1, 200, 64]
+    inp = make_inputs(1, sum(lens), 12, 3, gate_per_channel=False, A_log=(-2.0, 0.0), state_std=0.05,
+                      N=len(lens), lengths=lens, seed=416)
+    check(inp, what="la grouped heads 3->12 packed with state %s" % lens)
+
+
 def test_packed_without_state():
     lens = [1, 64, 0, 77, 130]
     inp = make_inputs(1, sum(lens), 4, 4, gate_per_channel=False, A_log=0.0, N=len(lens), lengths=lens, seed=413)

@@ -63,6 +63,23 @@ def test_scalar_gate_with_state():
     check(inp, what="scalar gate with state")
 
 
+@pytest.mark.parametrize("B,state_dtype", [(2, torch.float32), (6, torch.bfloat16), (40, torch.float32)])
+def test_scalar_gate_shared_qk_fragments(B, state_dtype):
+    # the value heads of a q/k group share one copy of the qn and kn^T record
+    # fragments: 16 chains (one column tile per workgroup, with L2 touches),
+    # 48 chains (two tiles) and 320 chains (two tiles, several rounds)
+    inp = make_inputs(B, 150, 8, 2, gate_per_channel=False, A_log=(-3.0, 0.0), state_std=0.05, seed=27 + B)
+    check(inp, state_dtype=state_dtype, what="scalar gate shared q/k fragments B=%d %s" % (B, state_dtype))
+
+
+def test_scalar_gate_shared_qk_fragments_packed():
+    # three value heads per q/k head, packed sequences with an empty one and a state
+    lens = [1, 64, 300, 0, 65, 129]
+    inp = make_inputs(1, sum(lens), 12, 4, gate_per_channel=False, A_log=(-2.0, 0.0), state_std=0.05,
+                      N=len(lens), lengths=lens, seed=28)
+    check(inp, what="scalar gate shared q/k fragments packed %s" % lens)
+
+
 def test_grouped_heads_per_channel_gate():
     inp = make_inputs(1, 200, 6, 2, state_std=0.02, seed=13)
     check(inp, what="per-channel gate, grouped heads")
