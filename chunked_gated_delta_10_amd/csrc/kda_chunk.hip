@@ -28,9 +28,9 @@
 // run on fp32 matrix cores (exact fp32 products) while D_b >= 2^-100 and fall
 // back to an exact per-channel evaluation in the log domain otherwise.
 // In scalar-gate mode exp(Gamma_r - Gamma_i) is one number per (r, i) and is
-// applied after the Gram products; with value heads grouped on q/k heads the
-// records keep the group's qn and kn^T once and the per-token factors
-// exp(Gamma_r), exp(Gamma_L - Gamma_r) per head (SHARE).
+// applied after the Gram products.  With value heads grouped on q/k heads a
+// separate kernel (chunk_group_kernel below) forms the head-independent part
+// once per q/k head and writes records that keep the group's qn and kn^T once.
 //
 // Work layout: 4 waves, wave n owns sub-chunk n.  Lane (l16, g) of wave n
 // holds token 16n + l16 and the 32 key channels
@@ -175,14 +175,9 @@ __device__ __forceinline__ void load_rows(Pref& P, const ChunkParams& p, int4 ce
 // the UT transform reduced to the identity: no q/k normalisation, write
 // strength 1, A = 0 (so T = I) and W = 0 (K-hat is not formed), which makes
 // the recurrence's U equal to V.
-// SHARE (scalar gate with value heads grouped on q/k heads): the record keeps
-// qn and kn^T in the slots of Qhat and Kbar^T, written only by the first
-// value head of each group, and the per-token factors exp(Gamma_r) and
-// exp(Gamma_L - Gamma_r) in its last block; the recurrence scales rows.
-template <bool PER_CHANNEL, bool DELTA, bool SHARE>
+template <bool PER_CHANNEL, bool DELTA>
 __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void chunk_local_kernel(const ChunkParams p,
                                                                                                  const int n_jobs) {
-  static_assert(!(SHARE && PER_CHANNEL), "shared q/k fragments need a scalar gate");
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
   using LD = Lds<PER_CHANNEL, DELTA>;
   f16x8* YB = reinterpret_cast<f16x8*>(smem + LD::YB);
@@ -432,13 +427,6 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
       }
       const float EGr = PER_CHANNEL ? 0.f : exp2f(Gr * LOG2E);
       const float EGLr = PER_CHANNEL ? 0.f : exp2f((GL - Gr) * LOG2E);
-      // SHARE: only the group's first value head writes qn and kn^T
-      const bool lead = !SHARE || h % (H / p.H_qk) == 0;
-      if (SHARE && lg == 0) {
-        float* gl = reinterpret_cast<float*>(rec + REC_GL);
-        gl[r] = EGr;
-        gl[CH + r] = EGLr;
-      }
       // The slice loop is instantiated per sub-chunk index N (wave-uniform), so
       // the decay products and the (N, a < N) blocks resolve at compile time.
       auto step2 = [&](auto Nc) {
@@ -475,11 +463,11 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
               lam[q] = 1.f;
             }
           }
-          // Qhat fragment (N, s) straight from registers (scalar gate: qn)
-          if (lead) {
+          // Qhat fragment (N, s) straight from registers
+          {
             float v[8];
   #pragma unroll
-            for (int q = 0; q < 8; ++q) v[q] = SHARE ? Q[8 * s + q] : Q[8 * s + q] * ep[q];
+            for (int q = 0; q < 8; ++q) v[q] = Q[8 * s + q] * ep[q];
             store_frag(rec, REC_QHAT, N * 4 + s, lane, v);
           }
           // Khat and Kbar of this sub-chunk, transposed by selection products
@@ -488,7 +476,7 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
   #pragma unroll
             for (int q = 0; q < 8; ++q) {
               kh[q] = DELTA ? (f16)(X[8 * s + q] * ep[q]) : (f16)0.f;
-              kb[q] = SHARE ? (f16)X[8 * s + q] : (f16)((PER_CHANNEL ? Y[8 * s + q] : X[8 * s + q]) * eg[q]);
+              kb[q] = (f16)((PER_CHANNEL ? Y[8 * s + q] : X[8 * s + q]) * eg[q]);
             }
   #pragma unroll
             for (int hh = 0; hh < 2; ++hh) {
@@ -498,12 +486,9 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
                 const f16x4 th4 = {(f16)th[0], (f16)th[1], (f16)th[2], (f16)th[3]};
                 *reinterpret_cast<f16x4*>(KHb + ((kt * 2 + (N >> 1)) * 64 + lane) * 16 + (N & 1) * 8) = th4;
               }
-              if (lead) {  // Kbar^T (scalar gate: kn^T)
-                const f32x4 tb = mma_f16(kb, sel[hh], zero4());
-                const f16x4 tb4 = {(f16)tb[0], (f16)tb[1], (f16)tb[2], (f16)tb[3]};
-                *reinterpret_cast<f16x4*>(rec + REC_KBAR + (kt * 2 + (N >> 1)) * FRAG_BYTES + lane * 16 + (N & 1) * 8) =
-                    tb4;
-              }
+              const f32x4 tb = mma_f16(kb, sel[hh], zero4());
+              const f16x4 tb4 = {(f16)tb[0], (f16)tb[1], (f16)tb[2], (f16)tb[3]};
+              *reinterpret_cast<f16x4*>(rec + REC_KBAR + (kt * 2 + (N >> 1)) * FRAG_BYTES + lane * 16 + (N & 1) * 8) = tb4;
             }
           }
           // blocks (N, a), a < N: (X lam) Y_a^T and Y_a (Q lam)^T
@@ -538,7 +523,7 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
         case 2: step2(std::integral_constant<int, 2>()); break;
         default: step2(std::integral_constant<int, 3>()); break;
       }
-      if (!SHARE && tid < HD) {  // exp(Gamma_L) per key
+      if (tid < HD) {  // exp(Gamma_L) per key
         const float gl = PER_CHANNEL ? DS[tid] * DS[HD + tid] * DS[2 * HD + tid] * DS[3 * HD + tid]
                                      : exp2f(GL * LOG2E);
         *reinterpret_cast<float*>(rec + REC_GL + 4 * tid) = gl;
@@ -750,17 +735,379 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
   }
 }
 
+// ---------------------------------------------------------------------------
+// Scalar gate with value heads grouped on q/k heads: one workgroup per
+// (chunk, q/k head).  With one decay per token-head the normalised rows, the
+// Gram products kn kn^T and qn kn^T and the transposes kn^T do not depend on
+// the value head, so they are formed once; the workgroup then walks the G
+// value heads of the group, each with its own gates and write strengths:
+// decays applied to the Gram blocks, A and M, T = (I + A)^-1,
+// W = T diag(b) diag(exp(Gamma)) kn and the record fragments.  The records
+// have the shared-q/k format (qn and kn^T in the group's first record, the
+// per-token factors exp(Gamma_r), exp(Gamma_L - Gamma_r) in every record).
+// ---------------------------------------------------------------------------
+template <bool DELTA>
+__global__ __launch_bounds__(NT, (Lds<false, DELTA>::JOBS_PER_CU)) void chunk_group_kernel(const ChunkParams p,
+                                                                                           const int n_jobs) {
+  extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
+  using LD = Lds<false, DELTA>;
+  f16x8* YB = reinterpret_cast<f16x8*>(smem + LD::YB);
+  uint8_t* KHb = smem + L_KH;  // kn^T fragments (full layout only: W needs them)
+  const f16x8* KH = reinterpret_cast<const f16x8*>(smem + L_KH);
+  float* AM = reinterpret_cast<float*>(smem + L_AM);
+  float* TM = reinterpret_cast<float*>(smem + L_TM);
+  float* AT = reinterpret_cast<float*>(smem + L_AT);
+  float* ROW = reinterpret_cast<float*>(smem + LD::ROW);
+  constexpr int R_EG = R_RK;  // exp(Gamma_r) of the current value head
+
+  const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+  const int l16 = lane & 15, lg = lane >> 4;
+  const int n = wave, r = SUB * n + l16;
+
+  f16x8 sel[2];
+#pragma unroll
+  for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+    for (int e = 0; e < 8; ++e) sel[hh][e] = ((e >> 2) == hh && (e & 3) == l16 - 4 * lg) ? (f16)1.f : (f16)0.f;
+
+  const int H = p.H, HQ = p.H_qk, G = H / HQ;
+  typedef __attribute__((address_space(4))) const int cint;
+  typedef __attribute__((address_space(4))) const float cfloat;
+  cint* chunks = (cint*)p.chunks;
+  cfloat* A_log = (cfloat*)p.A_log;
+  const int job = blockIdx.x;
+  const int e = __builtin_amdgcn_readfirstlane(job / HQ), hq = __builtin_amdgcn_readfirstlane(job % HQ);
+  int4 ce;
+  if (p.dense_T > 0) {  // B rows of T tokens: entry e is chunk e % NC of row e / NC
+    const int T = p.dense_T, nc = (T + CH - 1) / CH, b = e / nc, c = e - b * nc;
+    ce = make_int4(b, b * T + c * CH, min(CH, T - c * CH), c);
+  } else {
+    ce = make_int4(chunks[4 * e], chunks[4 * e + 1], chunks[4 * e + 2], chunks[4 * e + 3]);
+  }
+  const int len = ce.z, tok0 = ce.y;
+  if (len <= 0) return;  // uniform over the workgroup
+  const bool live = r < len;
+  const size_t t = (size_t)(tok0 + min(r, len - 1));  // rows past the end are clamped and zeroed when used
+  const int h_first = hq * G;
+
+  // inputs: this lane's q/k row slices, and the gate and write strength of the group's first head
+  uint2 qv[8], kv[8];
+  {
+    const uint16_t* qp = p.q + (t * HQ + hq) * HD + 4 * lg;
+    const uint16_t* kp = p.k + (t * HQ + hq) * HD + 4 * lg;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const int off = 32 * (i >> 1) + 16 * (i & 1);
+      qv[i] = *reinterpret_cast<const uint2*>(qp + off);
+      kv[i] = *reinterpret_cast<const uint2*>(kp + off);
+    }
+  }
+  uint32_t gs_next = p.g_raw[t * H + h_first];
+  float bl_next = DELTA ? p.beta[t * H + h_first] : 0.f;
+  __builtin_amdgcn_sched_barrier(0);
+
+  // ---- shared part: normalised rows, qn and kn^T fragments, Gram blocks ------
+  float X[32], Q[32];  // kn, qn
+  {
+    float sq = 0.f, sk = 0.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      float x[4], y[4];
+      unpack4(qv[i], x);
+      unpack4(kv[i], y);
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        sq += x[j] * x[j];
+        sk += y[j] * y[j];
+      }
+    }
+    sq += __shfl_xor(sq, 16);
+    sk += __shfl_xor(sk, 16);
+    sq += __shfl_xor(sq, 32);
+    sk += __shfl_xor(sk, 32);
+    const float rq = live ? (DELTA ? 1.f / sqrtf(sq + 1e-6f) : 1.f) : 0.f;
+    const float rk = live ? (DELTA ? 1.f / sqrtf(sk + 1e-6f) : 1.f) : 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      float kn[8], qn[8];
+      unpack4(kv[2 * s], kn);
+      unpack4(kv[2 * s + 1], kn + 4);
+      unpack4(qv[2 * s], qn);
+      unpack4(qv[2 * s + 1], qn + 4);
+#pragma unroll
+      for (int q = 0; q < 8; ++q) {
+        X[8 * s + q] = kn[q] * rk;
+        Q[8 * s + q] = qn[q] * rq;
+      }
+    }
+  }
+  uint8_t* rec0 = p.rec + ((size_t)e * H + h_first) * REC_BYTES;
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const f16x8 xh = to_f16x8(&X[8 * s]);
+    if (n < 3) YB[(n * 4 + s) * 64 + lane] = xh;
+    store_frag(rec0, REC_QHAT, n * 4 + s, lane, &Q[8 * s]);
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh) {  // kn^T by selection products
+      const int kt = 2 * s + hh;
+      const f32x4 tb = mma_f16(xh, sel[hh], zero4());
+      const f16x4 tb4 = {(f16)tb[0], (f16)tb[1], (f16)tb[2], (f16)tb[3]};
+      if (DELTA) *reinterpret_cast<f16x4*>(KHb + ((kt * 2 + (n >> 1)) * 64 + lane) * 16 + (n & 1) * 8) = tb4;
+      *reinterpret_cast<f16x4*>(rec0 + REC_KBAR + (kt * 2 + (n >> 1)) * FRAG_BYTES + lane * 16 + (n & 1) * 8) = tb4;
+    }
+  }
+  __syncthreads();  // Y operands (and kn^T for W) visible
+
+  f32x4 accA[3], accM[3], accA_d = zero4(), accM_d = zero4();
+#pragma unroll
+  for (int a = 0; a < 3; ++a) {
+    accA[a] = zero4();
+    accM[a] = zero4();
+  }
+
+  // Everything below is instantiated per sub-chunk index N (wave-uniform);
+  // every instantiation passes the same barriers.
+  auto body = [&](auto Nc) {
+    constexpr int N = decltype(Nc)::value;
+    // Gram blocks (N, a <= N), shared by the group's value heads
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 xh = to_f16x8(&X[8 * s]), qh = to_f16x8(&Q[8 * s]);
+#pragma unroll
+      for (int a = 2; a >= 0; --a) {
+        if (a < N) {
+          const f16x8 ya = YB[(a * 4 + s) * 64 + lane];
+          if (DELTA) accA[a] = mma_f16(xh, ya, accA[a]);
+          accM[a] = mma_f16(ya, qh, accM[a]);
+        }
+      }
+      if (DELTA) accA_d = mma_f16(xh, xh, accA_d);
+      accM_d = mma_f16(xh, qh, accM_d);
+    }
+
+#pragma unroll 1
+    for (int gi = 0; gi < G; ++gi) {
+      const int h = h_first + gi;
+      const uint32_t gs = gs_next;
+      const float bl = bl_next;
+      {  // the next head's gate and write strength (clamped, so the loads are unconditional)
+        const int hn = h_first + min(gi + 1, G - 1);
+        gs_next = p.g_raw[t * H + hn];
+        if (DELTA) bl_next = p.beta[t * H + hn];
+      }
+      const float a_h = __expf(A_log[h]);
+      float g = 0.f;
+      if (live) {
+        float d;
+        gate_decay(bf16_to_f32((uint16_t)gs), a_h, d, g);
+      }
+      const float beta = live ? (DELTA ? sigmoidf_(bl) : 1.f) : 0.f;
+      const float Gloc = row_prefix_sum(g);  // gate prefix within the sub-chunk
+      if (lg == 0) {
+        ROW[R_BETA + r] = beta;
+        ROW[R_GP + r] = Gloc;
+      }
+      if (lane == 15) ROW[R_GS + n] = Gloc;
+      __syncthreads();  // this head's per-token values visible
+
+      float gbase[NSUB], GL = 0.f;
+#pragma unroll
+      for (int m = 0; m < NSUB; ++m) {
+        gbase[m] = GL;
+        GL += ROW[R_GS + m];
+      }
+      auto gam = [&](int x) { return ROW[R_GP + x] + gbase[x >> 4]; };
+      const float Gr = Gloc + gbase[N];
+      const float EGr = exp2f(Gr * LOG2E), EGLr = exp2f((GL - Gr) * LOG2E);
+      uint8_t* rec = p.rec + ((size_t)e * H + h) * REC_BYTES;
+      if (lg == 0) {
+        float* glp = reinterpret_cast<float*>(rec + REC_GL);
+        glp[r] = EGr;
+        glp[CH + r] = EGLr;
+        if (DELTA) ROW[R_EG + r] = EGr;
+      }
+
+      // ---- A rows of this sub-chunk -> LDS; M fragments -> record ------------
+      float brow[4], grow[4];
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const int rr = SUB * N + 4 * lg + j;
+        brow[j] = ROW[R_BETA + rr];
+        grow[j] = gam(rr);
+      }
+      if (DELTA) {
+        float dv[4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int rl = 4 * lg + j, il = l16;
+          float v = 0.f;
+          if (il < rl) v = accA_d[j] * brow[j] * exp2f((grow[j] - gam(SUB * N + il)) * LOG2E);
+          dv[j] = v;
+          AM[(SUB * N + rl) * MS + SUB * N + il] = v;
+        }
+        *reinterpret_cast<float4*>(&AT[N * 256 + l16 * 16 + 4 * lg]) = make_float4(dv[0], dv[1], dv[2], dv[3]);
+#pragma unroll
+        for (int a = 0; a < 3; ++a) {
+          if (a < N) {
+            const float gi_ = gam(SUB * a + l16);
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+              AM[(SUB * N + 4 * lg + j) * MS + SUB * a + l16] = accA[a][j] * brow[j] * exp2f((grow[j] - gi_) * LOG2E);
+          }
+        }
+      }
+      {
+        const float gr = gam(r);
+        float md[4], mo[3][4];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+          const int il = 4 * lg + j;
+          md[j] = il <= l16 ? accM_d[j] * exp2f((gr - gam(SUB * N + il)) * LOG2E) : 0.f;
+        }
+#pragma unroll
+        for (int a = 0; a < 3; ++a)
+#pragma unroll
+          for (int j = 0; j < 4; ++j)
+            mo[a][j] = a < N ? accM[a][j] * exp2f((gr - gam(SUB * a + 4 * lg + j)) * LOG2E) : 0.f;
+        float v[8];
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {  // fragment (n, 0): blocks (n, 0), (n, 1)
+          v[j] = N == 0 ? md[j] : mo[0][j];
+          v[4 + j] = N == 0 ? 0.f : (N == 1 ? md[j] : mo[1][j]);
+        }
+        store_frag(rec, REC_M, N * 2, lane, v);
+        if (N >= 2) {  // fragment (n, 1): blocks (n, 2), (n, 3)
+#pragma unroll
+          for (int j = 0; j < 4; ++j) {
+            v[j] = N == 2 ? md[j] : mo[2][j];
+            v[4 + j] = N == 3 ? md[j] : 0.f;
+          }
+          store_frag(rec, REC_M, N * 2 + 1, lane, v);
+        }
+      }
+
+      if (DELTA) {
+        // ---- T_nn = (I + A_nn)^-1 by column-oriented substitution ---------------
+        if (lane < SUB) {
+          const float* ATn = AT + N * 256;
+          float acc[SUB];
+#pragma unroll
+          for (int i = 0; i < SUB; ++i) acc[i] = (i == lane) ? 1.f : 0.f;
+#pragma unroll
+          for (int j = 0; j < SUB - 1; ++j) {
+            float col[SUB];
+#pragma unroll
+            for (int q = 0; q < SUB; q += 4)
+              *reinterpret_cast<float4*>(&col[q]) = *reinterpret_cast<const float4*>(&ATn[j * SUB + q]);
+            const float xj = acc[j];
+#pragma unroll
+            for (int i = j + 1; i < SUB; ++i) acc[i] -= col[i] * xj;
+          }
+#pragma unroll
+          for (int i = 0; i < SUB; ++i) TM[(SUB * N + i) * MS + SUB * N + lane] = acc[i];
+        }
+        __syncthreads();  // A rows, diagonal T blocks and exp(Gamma) visible
+
+        // ---- off-diagonal blocks of T, level by level ---------------------------
+#pragma unroll
+        for (int lev = 1; lev < NSUB; ++lev) {
+          if (N < NSUB - lev) {
+            const int a = N, b = N + lev;
+            f32x4 Xs = zero4();
+            for (int j = a; j < b; ++j) {
+#pragma unroll
+              for (int s = 0; s < 4; ++s) {
+                const float av = AM[(SUB * b + l16) * MS + SUB * j + 4 * s + lg];
+                const float tv = TM[(SUB * j + 4 * s + lg) * MS + SUB * a + l16];
+                Xs = mma_f32(av, tv, Xs);
+              }
+            }
+            f32x4 Ys = zero4();
+#pragma unroll
+            for (int s = 0; s < 4; ++s) Ys = mma_f32(TM[(SUB * b + l16) * MS + SUB * b + 4 * lg + s], Xs[s], Ys);
+#pragma unroll
+            for (int j = 0; j < 4; ++j) TM[(SUB * b + 4 * lg + j) * MS + SUB * a + l16] = -Ys[j];
+          }
+          __syncthreads();
+        }
+
+        // ---- T diag(b) fragments and -W^T = -kn^T (T diag(b) diag(exp(Gamma)))^T ----
+        {
+          const int rt = SUB * N + l16;
+          constexpr int ns = (N >> 1) + 1;  // token slices with nonzero T entries for this tile
+          f16x8 tbB[2];
+#pragma unroll
+          for (int s = 0; s < 2; ++s) {
+            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, w[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+            if (s < ns) {
+              const int j0 = 32 * s + 4 * lg, j1 = j0 + 16;
+              float tv[8], bb[8], eg[8];
+              *reinterpret_cast<float4*>(&tv[0]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j0]);
+              *reinterpret_cast<float4*>(&tv[4]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j1]);
+              *reinterpret_cast<float4*>(&bb[0]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j0]);
+              *reinterpret_cast<float4*>(&bb[4]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j1]);
+              *reinterpret_cast<float4*>(&eg[0]) = *reinterpret_cast<const float4*>(&ROW[R_EG + j0]);
+              *reinterpret_cast<float4*>(&eg[4]) = *reinterpret_cast<const float4*>(&ROW[R_EG + j1]);
+#pragma unroll
+              for (int q = 0; q < 4; ++q) {
+                v[q] = (j0 + q <= rt) ? tv[q] * bb[q] : 0.f;
+                v[4 + q] = (j1 + q <= rt) ? tv[4 + q] * bb[4 + q] : 0.f;
+              }
+#pragma unroll
+              for (int q = 0; q < 8; ++q) w[q] = v[q] * eg[q];
+              store_frag(rec, REC_TB, N * 2 + s, lane, v);
+            }
+            tbB[s] = to_f16x8(w);
+          }
+#pragma unroll
+          for (int sp = 0; sp < 4; ++sp) {
+            float v[8];
+#pragma unroll
+            for (int hh = 0; hh < 2; ++hh) {
+              const int kt = 2 * sp + hh;
+              f32x4 acc = mma_f16(KH[(kt * 2) * 64 + lane], tbB[0], zero4());
+              if (ns > 1) acc = mma_f16(KH[(kt * 2 + 1) * 64 + lane], tbB[1], acc);
+#pragma unroll
+              for (int j = 0; j < 4; ++j) v[hh * 4 + j] = -acc[j];
+            }
+            store_frag(rec, REC_WNEG, N * 4 + sp, lane, v);
+          }
+        }
+      }
+      __syncthreads();  // this head's per-token values, A and T consumed before the next head
+    }
+  };
+  switch (n) {
+    case 0: body(std::integral_constant<int, 0>()); break;
+    case 1: body(std::integral_constant<int, 1>()); break;
+    case 2: body(std::integral_constant<int, 2>()); break;
+    default: body(std::integral_constant<int, 3>()); break;
+  }
+}
+
 namespace {
-template <bool PER_CHANNEL, bool DELTA, bool SHARE>
+template <bool PER_CHANNEL, bool DELTA>
 void launch_chunk_variant(const ChunkParams& p, int n_jobs, hipStream_t stream) {
   static bool attr_set = false;
   if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_local_kernel<PER_CHANNEL, DELTA, SHARE>),
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_local_kernel<PER_CHANNEL, DELTA>),
                               hipFuncAttributeMaxDynamicSharedMemorySize, Lds<PER_CHANNEL, DELTA>::BYTES);
     attr_set = true;
   }
   // one job per workgroup; two (full layout, LDS-bound) or three (compact) per CU
-  chunk_local_kernel<PER_CHANNEL, DELTA, SHARE><<<n_jobs, NT, Lds<PER_CHANNEL, DELTA>::BYTES, stream>>>(p, n_jobs);
+  chunk_local_kernel<PER_CHANNEL, DELTA><<<n_jobs, NT, Lds<PER_CHANNEL, DELTA>::BYTES, stream>>>(p, n_jobs);
+}
+
+// one job per (chunk, q/k head); two (full layout) or three (compact) per CU
+template <bool DELTA>
+void launch_group_variant(const ChunkParams& p, int n_jobs, hipStream_t stream) {
+  static bool attr_set = false;
+  if (!attr_set) {
+    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_group_kernel<DELTA>),
+                              hipFuncAttributeMaxDynamicSharedMemorySize, Lds<false, DELTA>::BYTES);
+    attr_set = true;
+  }
+  chunk_group_kernel<DELTA><<<n_jobs, NT, Lds<false, DELTA>::BYTES, stream>>>(p, n_jobs);
 }
 }  // namespace
 
@@ -769,15 +1116,17 @@ bool shares_qk_fragments(bool per_channel, int H, int H_qk) { return !per_channe
 void launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, bool delta, hipStream_t stream) {
   const int n_jobs = n_entries * p.H;
   if (n_jobs <= 0) return;
-  const bool share = shares_qk_fragments(per_channel, p.H, p.H_qk);
+  if (shares_qk_fragments(per_channel, p.H, p.H_qk)) {  // one workgroup per (chunk, q/k head)
+    if (delta) launch_group_variant<true>(p, n_entries * p.H_qk, stream);
+    else launch_group_variant<false>(p, n_entries * p.H_qk, stream);
+    return;
+  }
   if (delta) {
-    if (per_channel) launch_chunk_variant<true, true, false>(p, n_jobs, stream);
-    else if (share) launch_chunk_variant<false, true, true>(p, n_jobs, stream);
-    else launch_chunk_variant<false, true, false>(p, n_jobs, stream);
+    if (per_channel) launch_chunk_variant<true, true>(p, n_jobs, stream);
+    else launch_chunk_variant<false, true>(p, n_jobs, stream);
   } else {
-    if (per_channel) launch_chunk_variant<true, false, false>(p, n_jobs, stream);
-    else if (share) launch_chunk_variant<false, false, true>(p, n_jobs, stream);
-    else launch_chunk_variant<false, false, false>(p, n_jobs, stream);
+    if (per_channel) launch_chunk_variant<true, false>(p, n_jobs, stream);
+    else launch_chunk_variant<false, false>(p, n_jobs, stream);
   }
 }
 
