@@ -40,7 +40,7 @@
 // a row) all run on registers loaded straight from memory.  Transposed
 // (key-major) operands Khat^T and Kbar^T come out of matrix-core products
 // with 0/1 selection matrices.  Only the fp16 Y operands, the sub-chunk decay
-// products and the 64 x 64 matrices A and T go through LDS (~69 KB), so two
+// products and the 64 x 64 matrices A and T go through LDS (~65 KB), so two
 // workgroups share a CU and hide each other's latencies (one waits on its
 // loads while the other computes).  One workgroup per (chunk, head); the
 // schedule entry comes from the schedule table for packed sequences and by
@@ -68,8 +68,7 @@ constexpr int L_YB = 0;                          // Y = kn*kappa (fp16) of sub-c
 constexpr int L_KH = L_YB + 3 * 4 * 64 * 16;     // Khat^T fragments [8 key tiles][2 token slices][64] f16x8
 constexpr int L_AM = L_KH + 16 * 64 * 16;        // A [64][MS] fp32 (upper blocks: exact diagonal M scratch)
 constexpr int L_TM = L_AM + CH * MS * 4;         // T [64][MS] fp32 (upper blocks: exact diagonal A scratch)
-constexpr int L_AT = L_TM + CH * MS * 4;         // diagonal blocks of A, column-major [4][16][16]
-constexpr int L_DS = L_AT + NSUB * 256 * 4;      // D_n[key] [4][128]
+constexpr int L_DS = L_TM + CH * MS * 4;         // D_n[key] [4][128]
 constexpr int L_ROW = L_DS + NSUB * HD * 4;      // per-token values, see R_*
 constexpr int L_FLAG = L_ROW + (5 * CH + 8) * 4;  // exact-fallback flags of the 4 sub-chunks
 constexpr int LDS_BYTES = L_FLAG + 8 * 4;
@@ -130,6 +129,32 @@ __device__ __forceinline__ void unpack4(uint2 w, float* out) {
   out[3] = __uint_as_float(w.y & 0xFFFF0000u);
 }
 
+// X Y for 16 x 16 fp32 blocks in matrix-core C layout (lane (l16, lg) holds
+// rows 4 lg .. 4 lg + 3 of column l16), given X^T and Y in C layout: product
+// jj contracts over index 4 lg + jj, so both operands are read in place.
+__device__ __forceinline__ f32x4 mul_cc(const f32x4& XT, const f32x4& Y) {
+  f32x4 z = mma_f32(XT[0], Y[0], zero4());
+  z = mma_f32(XT[1], Y[1], z);
+  z = mma_f32(XT[2], Y[2], z);
+  return mma_f32(XT[3], Y[3], z);
+}
+
+// (I + N)^-1 for a strictly lower triangular 16 x 16 block N (so N^16 = 0):
+// (I - N)(I + N^2)(I + N^4)(I + N^8).  The factors are polynomials in N and
+// commute, so each product takes the transpose of a power of N as its left
+// operand: eight block products on fp32 matrix cores, all in registers.
+// Nc, NT: N and N^T in C layout; result in C layout.
+__device__ __forceinline__ f32x4 unit_lower_inverse(const f32x4& Nc, const f32x4& NT, int l16, int lg) {
+  const f32x4 N2 = mul_cc(NT, Nc), N2T = mul_cc(Nc, NT);
+  const f32x4 N3 = mul_cc(NT, N2), N4 = mul_cc(N2T, N2), N4T = mul_cc(N2, N2T);
+  const f32x4 N8T = mul_cc(N4, N4T);
+  f32x4 P1;  // (I - N)(I + N^2) = I - N + N^2 - N^3
+#pragma unroll
+  for (int j = 0; j < 4; ++j) P1[j] = (4 * lg + j == l16 ? 1.f : 0.f) - Nc[j] + N2[j] - N3[j];
+  const f32x4 P2 = P1 + mul_cc(N4T, P1);  // (I + N^4) P1
+  return P2 + mul_cc(N8T, P2);            // (I + N^8) P2
+}
+
 __device__ __forceinline__ void store_frag(uint8_t* rec, int off, int frag, int lane, const float* v) {
   *reinterpret_cast<f16x8*>(rec + off + frag * FRAG_BYTES + lane * 16) = to_f16x8(v);
 }
@@ -185,7 +210,6 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
   const f16x8* KH = reinterpret_cast<const f16x8*>(smem + L_KH);
   float* AM = reinterpret_cast<float*>(smem + L_AM);
   float* TM = reinterpret_cast<float*>(smem + L_TM);
-  float* AT = reinterpret_cast<float*>(smem + L_AT);
   float* DS = reinterpret_cast<float*>(smem + L_DS);
   float* ROW = reinterpret_cast<float*>(smem + LD::ROW);
   int* FLAG = reinterpret_cast<int*>(smem + LD::FLAG);
@@ -533,6 +557,7 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
       // same barriers in every instantiation).
       auto steps3to6 = [&](auto Nc) {
         constexpr int N = decltype(Nc)::value;
+        f32x4 Ncl = zero4();  // the diagonal block A_nn in C layout
         // ---- 3. A rows of this sub-chunk -> LDS; M fragments -> record ----------
         {
           // scalar mode: Gamma_x from the per-token prefix within its sub-chunk
@@ -572,7 +597,7 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
             dv[j] = v;
             AM[(SUB * N + rl) * MS + SUB * N + il] = v;
           }
-          *reinterpret_cast<float4*>(&AT[N * 256 + l16 * 16 + 4 * lg]) = make_float4(dv[0], dv[1], dv[2], dv[3]);
+          Ncl = f32x4{dv[0], dv[1], dv[2], dv[3]};
   #pragma unroll
           for (int a = 0; a < 3; ++a) {
             if (a < N) {
@@ -628,51 +653,54 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
           }
         }
 
-        // ---- 4. T_nn = (I + A_nn)^-1 by column-oriented substitution -----------
-        // Lane c < 16 owns column c; A_nn's columns come from AT (written by this
-        // wave just above, so no barrier is needed).
-        if (DELTA && lane < SUB) {
-          const float* ATn = AT + N * 256;
-          float acc[SUB];
+        // ---- 4. T_nn = (I + A_nn)^-1 on fp32 matrix cores ----------------------
+        // A_nn^T in C layout is one row read of the A rows this wave wrote just
+        // above (no barrier needed within a wave).
+        f32x4 Tnn = zero4();
+        if (DELTA) {
+          const float4 nt = *reinterpret_cast<const float4*>(&AM[(SUB * N + l16) * MS + SUB * N + 4 * lg]);
+          Tnn = unit_lower_inverse(Ncl, f32x4{nt.x, nt.y, nt.z, nt.w}, l16, lg);
   #pragma unroll
-          for (int i = 0; i < SUB; ++i) acc[i] = (i == lane) ? 1.f : 0.f;
-  #pragma unroll
-          for (int j = 0; j < SUB - 1; ++j) {
-            float col[SUB];
-  #pragma unroll
-            for (int q = 0; q < SUB; q += 4) *reinterpret_cast<float4*>(&col[q]) = *reinterpret_cast<const float4*>(&ATn[j * SUB + q]);
-            const float xj = acc[j];
-  #pragma unroll
-            for (int i = j + 1; i < SUB; ++i) acc[i] -= col[i] * xj;
-          }
-  #pragma unroll
-          for (int i = 0; i < SUB; ++i) TM[(SUB * N + i) * MS + SUB * N + lane] = acc[i];
+          for (int j = 0; j < 4; ++j) TM[(SUB * N + 4 * lg + j) * MS + SUB * N + l16] = Tnn[j];
+          __syncthreads();  // A rows, diagonal T blocks and Khat^T visible
         }
-        if (DELTA) __syncthreads();  // A rows, diagonal T blocks and Khat^T visible
 
-        // ---- 5. off-diagonal blocks of T, level by level (fp32 matrix cores) ----
+        // ---- 5. off-diagonal blocks of T by block column (fp32 matrix cores) ----
         //   T_ba = -T_bb * sum_{a<=j<b} A_bj T_ja
+        // Block column a depends only on A, the diagonal blocks and its own
+        // earlier blocks, so wave a computes it alone, holding its blocks in
+        // registers in C layout; the contraction index is permuted (4 lg + jj
+        // in product jj) so that C layout is the B operand and every A operand
+        // is one 16-byte row read.
+        if (DELTA) {
+          constexpr int a = N;
+          if (a < NSUB - 1) {
+            f32x4 Tc[NSUB];
+            Tc[a] = Tnn;
   #pragma unroll
-        for (int lev = 1; lev < (DELTA ? NSUB : 1); ++lev) {
-          if (N < NSUB - lev) {
-            const int a = N, b = N + lev;
-            f32x4 Xs = zero4();
-            for (int j = a; j < b; ++j) {
+            for (int b = a + 1; b < NSUB; ++b) {
+              f32x4 Xs = zero4();
   #pragma unroll
-              for (int s = 0; s < 4; ++s) {
-                const float av = AM[(SUB * b + l16) * MS + SUB * j + 4 * s + lg];
-                const float tv = TM[(SUB * j + 4 * s + lg) * MS + SUB * a + l16];
-                Xs = mma_f32(av, tv, Xs);
+              for (int j = a; j < b; ++j) {
+                const float4 av = *reinterpret_cast<const float4*>(&AM[(SUB * b + l16) * MS + SUB * j + 4 * lg]);
+                Xs = mma_f32(av.x, Tc[j][0], Xs);
+                Xs = mma_f32(av.y, Tc[j][1], Xs);
+                Xs = mma_f32(av.z, Tc[j][2], Xs);
+                Xs = mma_f32(av.w, Tc[j][3], Xs);
+              }
+              const float4 tb = *reinterpret_cast<const float4*>(&TM[(SUB * b + l16) * MS + SUB * b + 4 * lg]);
+              f32x4 Ys = mma_f32(tb.x, Xs[0], zero4());
+              Ys = mma_f32(tb.y, Xs[1], Ys);
+              Ys = mma_f32(tb.z, Xs[2], Ys);
+              Ys = mma_f32(tb.w, Xs[3], Ys);
+  #pragma unroll
+              for (int jj = 0; jj < 4; ++jj) {
+                Tc[b][jj] = -Ys[jj];
+                TM[(SUB * b + 4 * lg + jj) * MS + SUB * a + l16] = -Ys[jj];
               }
             }
-            // contraction order permuted so that Xs's own C layout is the B operand
-            f32x4 Ys = zero4();
-  #pragma unroll
-            for (int s = 0; s < 4; ++s) Ys = mma_f32(TM[(SUB * b + l16) * MS + SUB * b + 4 * lg + s], Xs[s], Ys);
-  #pragma unroll
-            for (int j = 0; j < 4; ++j) TM[(SUB * b + 4 * lg + j) * MS + SUB * a + l16] = -Ys[j];
           }
-          __syncthreads();
+          __syncthreads();  // every block of T visible
         }
 
         // ---- 6. -W^T = -Khat^T (T diag(b))^T and T diag(b) fragments -----------
@@ -756,7 +784,6 @@ __global__ __launch_bounds__(NT, (Lds<false, DELTA>::JOBS_PER_CU)) void chunk_gr
   const f16x8* KH = reinterpret_cast<const f16x8*>(smem + L_KH);
   float* AM = reinterpret_cast<float*>(smem + L_AM);
   float* TM = reinterpret_cast<float*>(smem + L_TM);
-  float* AT = reinterpret_cast<float*>(smem + L_AT);
   float* ROW = reinterpret_cast<float*>(smem + LD::ROW);
   constexpr int R_EG = R_RK;  // exp(Gamma_r) of the current value head
 
@@ -935,17 +962,16 @@ __global__ __launch_bounds__(NT, (Lds<false, DELTA>::JOBS_PER_CU)) void chunk_gr
         brow[j] = ROW[R_BETA + rr];
         grow[j] = gam(rr);
       }
+      f32x4 Ncl = zero4();  // the diagonal block A_nn in C layout
       if (DELTA) {
-        float dv[4];
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
           const int rl = 4 * lg + j, il = l16;
           float v = 0.f;
           if (il < rl) v = accA_d[j] * brow[j] * exp2f((grow[j] - gam(SUB * N + il)) * LOG2E);
-          dv[j] = v;
+          Ncl[j] = v;
           AM[(SUB * N + rl) * MS + SUB * N + il] = v;
         }
-        *reinterpret_cast<float4*>(&AT[N * 256 + l16 * 16 + 4 * lg]) = make_float4(dv[0], dv[1], dv[2], dv[3]);
 #pragma unroll
         for (int a = 0; a < 3; ++a) {
           if (a < N) {
@@ -987,48 +1013,43 @@ __global__ __launch_bounds__(NT, (Lds<false, DELTA>::JOBS_PER_CU)) void chunk_gr
       }
 
       if (DELTA) {
-        // ---- T_nn = (I + A_nn)^-1 by column-oriented substitution ---------------
-        if (lane < SUB) {
-          const float* ATn = AT + N * 256;
-          float acc[SUB];
+        // ---- T_nn = (I + A_nn)^-1 on fp32 matrix cores (as in chunk_local_kernel) --
+        const float4 nt = *reinterpret_cast<const float4*>(&AM[(SUB * N + l16) * MS + SUB * N + 4 * lg]);
+        const f32x4 Tnn = unit_lower_inverse(Ncl, f32x4{nt.x, nt.y, nt.z, nt.w}, l16, lg);
 #pragma unroll
-          for (int i = 0; i < SUB; ++i) acc[i] = (i == lane) ? 1.f : 0.f;
-#pragma unroll
-          for (int j = 0; j < SUB - 1; ++j) {
-            float col[SUB];
-#pragma unroll
-            for (int q = 0; q < SUB; q += 4)
-              *reinterpret_cast<float4*>(&col[q]) = *reinterpret_cast<const float4*>(&ATn[j * SUB + q]);
-            const float xj = acc[j];
-#pragma unroll
-            for (int i = j + 1; i < SUB; ++i) acc[i] -= col[i] * xj;
-          }
-#pragma unroll
-          for (int i = 0; i < SUB; ++i) TM[(SUB * N + i) * MS + SUB * N + lane] = acc[i];
-        }
+        for (int j = 0; j < 4; ++j) TM[(SUB * N + 4 * lg + j) * MS + SUB * N + l16] = Tnn[j];
         __syncthreads();  // A rows, diagonal T blocks and exp(Gamma) visible
 
-        // ---- off-diagonal blocks of T, level by level ---------------------------
+        // ---- off-diagonal blocks of T by block column (as in chunk_local_kernel) --
+        {
+          constexpr int a = N;
+          if (a < NSUB - 1) {
+            f32x4 Tc[NSUB];
+            Tc[a] = Tnn;
 #pragma unroll
-        for (int lev = 1; lev < NSUB; ++lev) {
-          if (N < NSUB - lev) {
-            const int a = N, b = N + lev;
-            f32x4 Xs = zero4();
-            for (int j = a; j < b; ++j) {
+            for (int b = a + 1; b < NSUB; ++b) {
+              f32x4 Xs = zero4();
 #pragma unroll
-              for (int s = 0; s < 4; ++s) {
-                const float av = AM[(SUB * b + l16) * MS + SUB * j + 4 * s + lg];
-                const float tv = TM[(SUB * j + 4 * s + lg) * MS + SUB * a + l16];
-                Xs = mma_f32(av, tv, Xs);
+              for (int j = a; j < b; ++j) {
+                const float4 av = *reinterpret_cast<const float4*>(&AM[(SUB * b + l16) * MS + SUB * j + 4 * lg]);
+                Xs = mma_f32(av.x, Tc[j][0], Xs);
+                Xs = mma_f32(av.y, Tc[j][1], Xs);
+                Xs = mma_f32(av.z, Tc[j][2], Xs);
+                Xs = mma_f32(av.w, Tc[j][3], Xs);
+              }
+              const float4 tb = *reinterpret_cast<const float4*>(&TM[(SUB * b + l16) * MS + SUB * b + 4 * lg]);
+              f32x4 Ys = mma_f32(tb.x, Xs[0], zero4());
+              Ys = mma_f32(tb.y, Xs[1], Ys);
+              Ys = mma_f32(tb.z, Xs[2], Ys);
+              Ys = mma_f32(tb.w, Xs[3], Ys);
+#pragma unroll
+              for (int jj = 0; jj < 4; ++jj) {
+                Tc[b][jj] = -Ys[jj];
+                TM[(SUB * b + 4 * lg + jj) * MS + SUB * a + l16] = -Ys[jj];
               }
             }
-            f32x4 Ys = zero4();
-#pragma unroll
-            for (int s = 0; s < 4; ++s) Ys = mma_f32(TM[(SUB * b + l16) * MS + SUB * b + 4 * lg + s], Xs[s], Ys);
-#pragma unroll
-            for (int j = 0; j < 4; ++j) TM[(SUB * b + 4 * lg + j) * MS + SUB * a + l16] = -Ys[j];
           }
-          __syncthreads();
+          __syncthreads();  // every block of T visible
         }
 
         // ---- T diag(b) fragments and -W^T = -kn^T (T diag(b) diag(exp(Gamma)))^T ----
