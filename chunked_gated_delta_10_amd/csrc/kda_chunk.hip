@@ -1132,12 +1132,10 @@ void launch_group_variant(const ChunkParams& p, int n_jobs, hipStream_t stream) 
 }
 }  // namespace
 
-bool shares_qk_fragments(bool per_channel, int H, int H_qk) { return !per_channel && H != H_qk; }
-
 void launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, bool delta, hipStream_t stream) {
   const int n_jobs = n_entries * p.H;
   if (n_jobs <= 0) return;
-  if (shares_qk_fragments(per_channel, p.H, p.H_qk)) {  // one workgroup per (chunk, q/k head)
+  if (shares_qk_fragments(per_channel, p.H, p.H_qk, n_entries)) {  // one workgroup per (chunk, q/k head)
     if (delta) launch_group_variant<true>(p, n_entries * p.H_qk, stream);
     else launch_group_variant<false>(p, n_entries * p.H_qk, stream);
     return;

@@ -65,9 +65,12 @@ void launch_table(const TableParams& p, hipStream_t stream);
 // delta = false: decay-only linear attention (no erase, no write strength, no q/k normalisation)
 void launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, bool delta, hipStream_t stream);
 void launch_recur(const RecurParams& p, bool bf16_state, bool per_channel, bool delta, hipStream_t stream);
-// Scalar gate with value heads grouped on q/k heads: the value heads of a
-// group share one copy of the qn and kn^T record fragments.
-bool shares_qk_fragments(bool per_channel, int H, int H_qk);
+// Scalar gate with value heads grouped on q/k heads and at least
+// GROUP_MIN_JOBS (schedule entry, q/k head) jobs: the value heads of a group
+// share one copy of the qn and kn^T record fragments, written by the grouped
+// chunk-local kernel.  Fewer jobs take the per-head kernel and records.
+constexpr int GROUP_MIN_JOBS = 256;
+bool shares_qk_fragments(bool per_channel, int H, int H_qk, int n_entries);
 int recur_grid(int n_chains);
 void launch_decode(const DecodeParams& p, int B, bool bf16_state, bool per_channel, bool delta, hipStream_t stream);
 

@@ -116,8 +116,7 @@ __device__ __forceinline__ void unpack_bf16(uint2 x, f16* o) {
 // record holds the two per-token factors.  The output waves scale the rows of
 // qn S by exp(Gamma_r); the chain waves scale U's rows by
 // exp(Gamma_L - Gamma_r) (a second LDS copy, since M U needs U itself) and
-// decay S by the single exp(Gamma_L).  A group's chains get the same XCD, so
-// its shared fragments are read from HBM once.
+// decay S by the single exp(Gamma_L).
 template <typename StT, int NCT, bool DELTA, bool PC>
 __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
   constexpr int VC = VT * NCT;       // value columns per workgroup
@@ -134,10 +133,8 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
   const int l16 = lane & 15, lg = lane >> 4;
   const int tw = wave & 3;
   const int x = blockIdx.x, xcd = x & 7, y = x >> 3;
-  // chains are dealt to XCDs in runs of G (the value heads of one q/k group)
-  const int G = PC ? 1 : p.H / p.H_qk;
-  const int vt = y % NW, slot = y / NW, blk = slot / G;
-  const int ch = blk * 8 * G + G * xcd + (slot - blk * G);
+  const int G = PC ? 1 : p.H / p.H_qk;  // value heads per q/k head
+  const int vt = y % NW, ch = (y / NW) * 8 + xcd;
   if (ch >= p.n_chains) return;
   const int h = ch % p.H, h0 = h - h % G;  // h0: the group's first value head
   int n;
@@ -418,11 +415,8 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
 }
 
 namespace {
-// workgroups for n_chains chains with `tiles` workgroups per chain, chains
-// dealt to the 8 XCDs in runs of `group`
-int grid_for(int n_chains, int tiles, int group = 1) {
-  return ((n_chains + 8 * group - 1) / (8 * group)) * 8 * group * tiles;
-}
+// workgroups for n_chains chains with `tiles` workgroups per chain
+int grid_for(int n_chains, int tiles) { return ((n_chains + 7) / 8) * 8 * tiles; }
 
 int cu_count() {
   static int cus = 0;
@@ -435,6 +429,13 @@ int cu_count() {
 }
 }  // namespace
 
+bool shares_qk_fragments(bool per_channel, int H, int H_qk, int n_entries) {
+  // the grouped chunk-local kernel walks a group's heads in series, so it
+  // needs enough (chunk, q/k head) jobs to fill the chip; below that the
+  // per-head kernel and its records are faster
+  return !per_channel && H != H_qk && (long)n_entries * H_qk >= GROUP_MIN_JOBS;
+}
+
 int recur_grid(int n_chains) {
   const int g = grid_for(n_chains, NVT);
   return g <= cu_count() ? g : grid_for(n_chains, NVT / 2);
@@ -443,14 +444,13 @@ int recur_grid(int n_chains) {
 namespace {
 template <bool DELTA, bool PC>
 void launch_recur_variant(const RecurParams& p, bool bf16_state, hipStream_t stream) {
-  const int G = PC ? 1 : p.H / p.H_qk;
   if (grid_for(p.n_chains, NVT) <= cu_count()) {  // few chains: one column tile per workgroup, all on CUs of their own
-    const int g = grid_for(p.n_chains, NVT, G);
+    const int g = grid_for(p.n_chains, NVT);
     if (bf16_state) recur_split_kernel<uint16_t, 1, DELTA, PC><<<g, 512, 0, stream>>>(p);
     else recur_split_kernel<float, 1, DELTA, PC><<<g, 512, 0, stream>>>(p);
     return;
   }
-  const int g2 = grid_for(p.n_chains, NVT / 2, G);  // two column tiles per workgroup
+  const int g2 = grid_for(p.n_chains, NVT / 2);  // two column tiles per workgroup
   if (bf16_state) recur_split_kernel<uint16_t, 2, DELTA, PC><<<g2, 512, 0, stream>>>(p);
   else recur_split_kernel<float, 2, DELTA, PC><<<g2, 512, 0, stream>>>(p);
 }
@@ -458,7 +458,7 @@ void launch_recur_variant(const RecurParams& p, bool bf16_state, hipStream_t str
 
 void launch_recur(const RecurParams& p, bool bf16_state, bool per_channel, bool delta, hipStream_t stream) {
   // records without shared q/k fragments carry Qhat, Kbar^T and exp(Gamma_L) per key
-  if (!shares_qk_fragments(per_channel, p.H, p.H_qk)) per_channel = true;
+  if (!shares_qk_fragments(per_channel, p.H, p.H_qk, p.n_entries)) per_channel = true;
   if (delta) {
     if (per_channel) launch_recur_variant<true, true>(p, bf16_state, stream);
     else launch_recur_variant<true, false>(p, bf16_state, stream);

@@ -87,12 +87,13 @@ def test_grouped_heads():
     check(inp, what="la grouped heads 2->8")
 
 
-def test_grouped_heads_packed_with_state():
-    # value heads grouped on q/k heads share the q/k record fragments
-    lens = [70, 0, 1, 200, 64]
-    inp = make_inputs(1, sum(lens), 12, 3, gate_per_channel=False, A_log=(-2.0, 0.0), state_std=0.05,
-                      N=len(lens), lengths=lens, seed=416)
-    check(inp, what="la grouped heads 3->12 packed with state %s" % lens)
+@pytest.mark.parametrize("lens", [[70, 0, 1, 200, 64], [700, 0, 1, 2400, 64, 1000]])
+def test_grouped_heads_packed_with_state(lens):
+    # 44 (chunk, q/k head) jobs take the per-head kernel; 288 jobs the grouped
+    # kernel, whose records keep the group's q/k fragments once
+    inp = make_inputs(1, sum(lens), 12, 4, gate_per_channel=False, A_log=(-2.0, 0.0), state_std=0.05,
+                      N=len(lens), lengths=lens, seed=416 + len(lens[3:4]) + lens[0])
+    check(inp, what="la grouped heads 4->12 packed with state %s" % lens)
 
 
 def test_packed_without_state():

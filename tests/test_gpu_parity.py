@@ -63,21 +63,29 @@ def test_scalar_gate_with_state():
     check(inp, what="scalar gate with state")
 
 
-@pytest.mark.parametrize("B,state_dtype", [(2, torch.float32), (6, torch.bfloat16), (40, torch.float32)])
-def test_scalar_gate_shared_qk_fragments(B, state_dtype):
-    # the value heads of a q/k group share one copy of the qn and kn^T record
-    # fragments: 16 chains (one column tile per workgroup, with L2 touches),
-    # 48 chains (two tiles) and 320 chains (two tiles, several rounds)
-    inp = make_inputs(B, 150, 8, 2, gate_per_channel=False, A_log=(-3.0, 0.0), state_std=0.05, seed=27 + B)
-    check(inp, state_dtype=state_dtype, what="scalar gate shared q/k fragments B=%d %s" % (B, state_dtype))
+@pytest.mark.parametrize("B,T,H,H_qk,state_dtype", [
+    (2, 150, 8, 2, torch.float32),    # 12 (chunk, q/k head) jobs: per-head kernel and records
+    (6, 150, 8, 2, torch.bfloat16),   # 36 jobs: per-head path, two column tiles
+    (44, 150, 8, 2, torch.float32),   # 264 jobs: grouped kernel, 352 chains in several rounds
+    (44, 150, 8, 2, torch.bfloat16),
+    (1, 8192, 16, 2, torch.float32),  # 256 jobs: grouped kernel, 16 chains (one tile, L2 touches)
+])
+def test_scalar_gate_grouped_heads_both_paths(B, T, H, H_qk, state_dtype):
+    # With at least 256 (chunk, q/k head) jobs the value heads of a q/k group
+    # share one copy of the qn and kn^T record fragments, written by the
+    # grouped chunk-local kernel; smaller grids take the per-head kernel.
+    inp = make_inputs(B, T, H, H_qk, gate_per_channel=False, A_log=(-3.0, 0.0), state_std=0.05, seed=27 + B + T)
+    check(inp, state_dtype=state_dtype, what="scalar gate grouped B=%d T=%d H=%d H_qk=%d %s" % (B, T, H, H_qk,
+                                                                                             state_dtype))
 
 
-def test_scalar_gate_shared_qk_fragments_packed():
-    # three value heads per q/k head, packed sequences with an empty one and a state
-    lens = [1, 64, 300, 0, 65, 129]
+@pytest.mark.parametrize("lens", [[1, 64, 300, 0, 65, 129], [1, 64, 3000, 0, 65, 129, 700]])
+def test_scalar_gate_grouped_heads_packed(lens):
+    # three value heads per q/k head, packed sequences with an empty one and a
+    # state: 60 jobs (per-head path) and 276 jobs (grouped kernel)
     inp = make_inputs(1, sum(lens), 12, 4, gate_per_channel=False, A_log=(-2.0, 0.0), state_std=0.05,
-                      N=len(lens), lengths=lens, seed=28)
-    check(inp, what="scalar gate shared q/k fragments packed %s" % lens)
+                      N=len(lens), lengths=lens, seed=28 + len(lens))
+    check(inp, what="scalar gate grouped packed %s" % lens)
 
 
 def test_grouped_heads_per_channel_gate():
