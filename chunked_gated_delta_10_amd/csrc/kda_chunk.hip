@@ -33,13 +33,13 @@
 // once per q/k head and writes records that keep the group's qn and kn^T once.
 //
 // Work layout: 4 waves, wave n owns sub-chunk n.  Lane (l16, g) of wave n
-// holds token 16n + l16 and the 32 key channels
-//   32s + 4g + e (e < 4),  32s + 16 + 4g + (e - 4) (e >= 4),   s = 0..3,
-// i.e. exactly the A-operand order of the record fragments, so the Gram
-// products, Qhat and the decay scans (DPP shifts along the 16 token lanes of
-// a row) all run on registers loaded straight from memory.  Transposed
-// (key-major) operands Khat^T and Kbar^T come out of matrix-core products
-// with 0/1 selection matrices.  Only the fp16 Y operands, the sub-chunk decay
+// holds token 16n + l16 and the 32 key channels 32s + 8g + e (e < 8,
+// s = 0..3): one 16-byte load per slice and tensor, and the natural key
+// order of a 16x16x32 matrix-core operand, so the Gram products and the
+// decay scans (DPP shifts along the 16 token lanes of a row) run on registers
+// loaded straight from memory.  Products with 0/1 selection matrices give the
+// transposed (key-major) operands Khat^T and Kbar^T and put Qhat into the
+// record's key order (32s + 4g + e, then 32s + 16 + 4g + e).  Only the fp16 Y operands, the sub-chunk decay
 // products and the 64 x 64 matrices A and T go through LDS (~65 KB), so two
 // workgroups share a CU and hide each other's latencies (one waits on its
 // loads while the other computes).  One workgroup per (chunk, head); the
@@ -155,12 +155,22 @@ __device__ __forceinline__ f32x4 unit_lower_inverse(const f32x4& Nc, const f32x4
   return P2 + mul_cc(N8T, P2);            // (I + N^8) P2
 }
 
+// Store an A-operand fragment held in natural key order (this lane: keys
+// 32s + 8 lg + e of token l16) in the record's order (keys 32s + 4 lg + e,
+// then 32s + 16 + 4 lg + e): sel[h] x' picks keys 32s + 16h + 4 lg + j of
+// token l16 into the C layout, exactly (0/1 products, fp32 accumulation).
+__device__ __forceinline__ void store_reordered(uint8_t* frag, f16x8 x, const f16x8* sel, int lane) {
+  const f32x4 lo = mma_f16(sel[0], x, zero4()), hi = mma_f16(sel[1], x, zero4());
+  const f16x8 o = {(f16)lo[0], (f16)lo[1], (f16)lo[2], (f16)lo[3], (f16)hi[0], (f16)hi[1], (f16)hi[2], (f16)hi[3]};
+  *reinterpret_cast<f16x8*>(frag + lane * 16) = o;
+}
+
 __device__ __forceinline__ void store_frag(uint8_t* rec, int off, int frag, int lane, const float* v) {
   *reinterpret_cast<f16x8*>(rec + off + frag * FRAG_BYTES + lane * 16) = to_f16x8(v);
 }
 
 // One job's inputs for this lane: token 16*wave + lane%16, key channels of
-// slice s: 32s + 4g .. +3 (half 0) and 32s + 16 + 4g .. +3 (half 1).
+// slice s: 32s + 8g .. +3 (half 0) and 32s + 8g + 4 .. +7 (half 1).
 struct Pref {
   uint2 q[8], k[8], g[8];  // [2s + half], bf16; g only in per-channel mode
   uint32_t gs;             // scalar gate of the token, bf16 in the low half
@@ -174,21 +184,28 @@ __device__ __forceinline__ void load_rows(Pref& P, const ChunkParams& p, int4 ce
   const int len = ce.z, tok0 = ce.y;
   if (len <= 0) return;
   const int hq = h / (p.H / p.H_qk);
-  const int r = min(SUB * wave + (lane & 15), len - 1), g4 = 4 * (lane >> 4);
+  const int r = min(SUB * wave + (lane & 15), len - 1), g8 = 8 * (lane >> 4);
   const size_t t = (size_t)(tok0 + r);
-  const uint16_t* qp = p.q + (t * p.H_qk + hq) * HD + g4;
-  const uint16_t* kp = p.k + (t * p.H_qk + hq) * HD + g4;
+  const uint16_t* qp = p.q + (t * p.H_qk + hq) * HD + g8;
+  const uint16_t* kp = p.k + (t * p.H_qk + hq) * HD + g8;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) {
-    const int off = 32 * (i >> 1) + 16 * (i & 1);
-    P.q[i] = *reinterpret_cast<const uint2*>(qp + off);
-    P.k[i] = *reinterpret_cast<const uint2*>(kp + off);
+  for (int s = 0; s < 4; ++s) {
+    const uint4 a = *reinterpret_cast<const uint4*>(qp + 32 * s);
+    const uint4 b = *reinterpret_cast<const uint4*>(kp + 32 * s);
+    P.q[2 * s] = make_uint2(a.x, a.y);
+    P.q[2 * s + 1] = make_uint2(a.z, a.w);
+    P.k[2 * s] = make_uint2(b.x, b.y);
+    P.k[2 * s + 1] = make_uint2(b.z, b.w);
   }
   P.beta = DELTA ? p.beta[t * p.H + h] : 0.f;  // no write strength without the delta rule
   if (PER_CHANNEL) {
-    const uint16_t* gp = p.g_raw + (t * p.H + h) * HD + g4;
+    const uint16_t* gp = p.g_raw + (t * p.H + h) * HD + g8;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) P.g[i] = *reinterpret_cast<const uint2*>(gp + 32 * (i >> 1) + 16 * (i & 1));
+    for (int s = 0; s < 4; ++s) {
+      const uint4 c = *reinterpret_cast<const uint4*>(gp + 32 * s);
+      P.g[2 * s] = make_uint2(c.x, c.y);
+      P.g[2 * s + 1] = make_uint2(c.z, c.w);
+    }
   } else {
     P.gs = p.g_raw[t * p.H + h];
   }
@@ -220,11 +237,12 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
   const int r = SUB * n + l16;     // this lane's token row in the chunk
 
   // 0/1 selection operands: sel[h] picks key 32s + 16h + l16 out of slice s
+  // (this lane's element e of a slice is key 32s + 8 lg + e)
   f16x8 sel[2];
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sel[hh][e] = ((e >> 2) == hh && (e & 3) == l16 - 4 * lg) ? (f16)1.f : (f16)0.f;
+    for (int e = 0; e < 8; ++e) sel[hh][e] = (8 * lg + e == 16 * hh + l16) ? (f16)1.f : (f16)0.f;
 
   // Job indices are wave-uniform; the schedule and A_log are read through
   // the constant address space so these loads go to the scalar unit.
@@ -335,8 +353,8 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
             }
           }
           if (l16 == 0) {  // D_n of this lane group's 8 keys
-            *reinterpret_cast<float4*>(&DS[n * HD + 32 * s + 4 * lg]) = make_float4(Dv[0], Dv[1], Dv[2], Dv[3]);
-            *reinterpret_cast<float4*>(&DS[n * HD + 32 * s + 16 + 4 * lg]) = make_float4(Dv[4], Dv[5], Dv[6], Dv[7]);
+            *reinterpret_cast<float4*>(&DS[n * HD + 32 * s + 8 * lg]) = make_float4(Dv[0], Dv[1], Dv[2], Dv[3]);
+            *reinterpret_cast<float4*>(&DS[n * HD + 32 * s + 8 * lg + 4]) = make_float4(Dv[4], Dv[5], Dv[6], Dv[7]);
           }
           if (n < 3) {
             f16x8 yh;
@@ -462,8 +480,8 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
           if (PER_CHANNEL) {
   #pragma unroll
             for (int m = 0; m < NSUB; ++m) {
-              const float4 lo = *reinterpret_cast<const float4*>(&DS[m * HD + 32 * s + 4 * lg]);
-              const float4 hi = *reinterpret_cast<const float4*>(&DS[m * HD + 32 * s + 16 + 4 * lg]);
+              const float4 lo = *reinterpret_cast<const float4*>(&DS[m * HD + 32 * s + 8 * lg]);
+              const float4 hi = *reinterpret_cast<const float4*>(&DS[m * HD + 32 * s + 8 * lg + 4]);
               Dm[m][0] = lo.x; Dm[m][1] = lo.y; Dm[m][2] = lo.z; Dm[m][3] = lo.w;
               Dm[m][4] = hi.x; Dm[m][5] = hi.y; Dm[m][6] = hi.z; Dm[m][7] = hi.w;
             }
@@ -487,12 +505,12 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
               lam[q] = 1.f;
             }
           }
-          // Qhat fragment (N, s) straight from registers
+          // Qhat fragment (N, s), put into the record's key order
           {
             float v[8];
   #pragma unroll
             for (int q = 0; q < 8; ++q) v[q] = Q[8 * s + q] * ep[q];
-            store_frag(rec, REC_QHAT, N * 4 + s, lane, v);
+            store_reordered(rec + REC_QHAT + (N * 4 + s) * FRAG_BYTES, to_f16x8(v), sel, lane);
           }
           // Khat and Kbar of this sub-chunk, transposed by selection products
           {
@@ -795,7 +813,7 @@ __global__ __launch_bounds__(NT, (Lds<false, DELTA>::JOBS_PER_CU)) void chunk_gr
 #pragma unroll
   for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-    for (int e = 0; e < 8; ++e) sel[hh][e] = ((e >> 2) == hh && (e & 3) == l16 - 4 * lg) ? (f16)1.f : (f16)0.f;
+    for (int e = 0; e < 8; ++e) sel[hh][e] = (8 * lg + e == 16 * hh + l16) ? (f16)1.f : (f16)0.f;
 
   const int H = p.H, HQ = p.H_qk, G = H / HQ;
   typedef __attribute__((address_space(4))) const int cint;
@@ -820,13 +838,16 @@ __global__ __launch_bounds__(NT, (Lds<false, DELTA>::JOBS_PER_CU)) void chunk_gr
   // inputs: this lane's q/k row slices, and the gate and write strength of the group's first head
   uint2 qv[8], kv[8];
   {
-    const uint16_t* qp = p.q + (t * HQ + hq) * HD + 4 * lg;
-    const uint16_t* kp = p.k + (t * HQ + hq) * HD + 4 * lg;
+    const uint16_t* qp = p.q + (t * HQ + hq) * HD + 8 * lg;
+    const uint16_t* kp = p.k + (t * HQ + hq) * HD + 8 * lg;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const int off = 32 * (i >> 1) + 16 * (i & 1);
-      qv[i] = *reinterpret_cast<const uint2*>(qp + off);
-      kv[i] = *reinterpret_cast<const uint2*>(kp + off);
+    for (int s = 0; s < 4; ++s) {
+      const uint4 a = *reinterpret_cast<const uint4*>(qp + 32 * s);
+      const uint4 b = *reinterpret_cast<const uint4*>(kp + 32 * s);
+      qv[2 * s] = make_uint2(a.x, a.y);
+      qv[2 * s + 1] = make_uint2(a.z, a.w);
+      kv[2 * s] = make_uint2(b.x, b.y);
+      kv[2 * s + 1] = make_uint2(b.z, b.w);
     }
   }
   uint32_t gs_next = p.g_raw[t * H + h_first];
@@ -873,7 +894,7 @@ __global__ __launch_bounds__(NT, (Lds<false, DELTA>::JOBS_PER_CU)) void chunk_gr
   for (int s = 0; s < 4; ++s) {
     const f16x8 xh = to_f16x8(&X[8 * s]);
     if (n < 3) YB[(n * 4 + s) * 64 + lane] = xh;
-    store_frag(rec0, REC_QHAT, n * 4 + s, lane, &Q[8 * s]);
+    store_reordered(rec0 + REC_QHAT + (n * 4 + s) * FRAG_BYTES, to_f16x8(&Q[8 * s]), sel, lane);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {  // kn^T by selection products
       const int kt = 2 * s + hh;
