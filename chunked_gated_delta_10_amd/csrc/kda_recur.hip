@@ -1,9 +1,10 @@
 // kda_recur.hip -- the sequential part of the chunked forward pass.
 //
-// A workgroup owns one (sequence, value head) chain and one or two adjacent
-// 16-column value tiles: the columns of the state evolve independently, so a
-// chain's 128 value columns are spread over 8 or 4 workgroups that never
-// communicate.  Per chunk, with the chunk record produced by the chunk-local
+// A workgroup owns one (sequence, value head) chain and one, two or four
+// adjacent 16-column value tiles: the columns of the state evolve
+// independently, so a chain's 128 value columns are spread over 8, 4 or 2
+// workgroups that never communicate (four tiles only for decay-only linear
+// attention over many chains).  Per chunk, with the chunk record produced by the chunk-local
 // kernel and the 128 x 16 state tiles S (fp32, held in registers in
 // matrix-core C layout):
 //   U  = T diag(b) V - W S
@@ -87,10 +88,17 @@ __device__ __forceinline__ f16x8 ldfrag(const uint8_t* rec, int off, int frag, i
 // tile spreads few chains over more CUs for the shorter chain latency.
 // ---------------------------------------------------------------------------
 template <int NCT>
+struct Bf16Row {  // 4 NCT bf16 of a value row (NCT >= 2)
+  uint4 q[NCT / 2];
+};
+template <int NCT>
+using ValueRow = typename std::conditional<NCT == 1, uint2, Bf16Row<NCT>>::type;
+
+template <int NCT>
 struct ChainFrags {
   f16x8 w[4], t[2], k[4];
   float4 gl[2];
-  typename std::conditional<NCT == 1, uint2, uint4>::type v;  // 4 NCT bf16 of the value tile
+  ValueRow<NCT> v;  // 4 NCT bf16 of the value tile
   uint32_t touch;
 };
 struct OutFrags {
@@ -123,7 +131,7 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
   constexpr int NW = NVT / NCT;      // workgroups per chain
   constexpr int T_REC = (REC_LINES + NW - 1) / NW;  // record lines touched per workgroup
   constexpr int T_V = 2 * CH / NW;                 // value-row lines touched per workgroup
-  static_assert(T_REC + T_V <= 256, "one touch per chain thread");
+  static_assert(NCT != 1 || T_REC + T_V <= 256, "one touch per chain thread");
   __shared__ __attribute__((aligned(16))) f16x8 sbuf[NCT][4 * 64];  // S slices (B operand)
   __shared__ __attribute__((aligned(16))) f16x4 ubuf[NCT][4 * 64];  // U tiles (C layout)
   __shared__ __attribute__((aligned(16))) f16x4 ubuf2[PC ? 1 : NCT][4 * 64];  // scalar gate: decayed U tiles
@@ -235,9 +243,12 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
           if constexpr (NCT == 1) {
             unpack_bf16(r < L ? F.v : make_uint2(0u, 0u), vh);
           } else {
-            const uint4 vv = r < L ? F.v : make_uint4(0u, 0u, 0u, 0u);
-            unpack_bf16(make_uint2(vv.x, vv.y), vh);
-            unpack_bf16(make_uint2(vv.z, vv.w), vh + 4);
+#pragma unroll
+            for (int i = 0; i < NCT / 2; ++i) {
+              const uint4 vv = r < L ? F.v.q[i] : make_uint4(0u, 0u, 0u, 0u);
+              unpack_bf16(make_uint2(vv.x, vv.y), vh + 8 * i);
+              unpack_bf16(make_uint2(vv.z, vv.w), vh + 8 * i + 4);
+            }
           }
 #pragma unroll
           for (int e = 0; e < 4 * NCT; ++e) vsT[(4 * NCT * vq + e) * VS + r] = vh[e];
@@ -451,6 +462,17 @@ void launch_recur_variant(const RecurParams& p, bool bf16_state, hipStream_t str
     return;
   }
   const int g2 = grid_for(p.n_chains, NVT / 2);  // two column tiles per workgroup
+  if constexpr (!DELTA) {
+    if (g2 > 2 * cu_count()) {
+      // decay-only linear attention over many chains: its chain step has no
+      // W S product, so four column tiles per workgroup cost little compute
+      // and halve again the record bytes each column pulls
+      const int g4 = grid_for(p.n_chains, NVT / 4);
+      if (bf16_state) recur_split_kernel<uint16_t, 4, false, PC><<<g4, 512, 0, stream>>>(p);
+      else recur_split_kernel<float, 4, false, PC><<<g4, 512, 0, stream>>>(p);
+      return;
+    }
+  }
   if (bf16_state) recur_split_kernel<uint16_t, 2, DELTA, PC><<<g2, 512, 0, stream>>>(p);
   else recur_split_kernel<float, 2, DELTA, PC><<<g2, 512, 0, stream>>>(p);
 }

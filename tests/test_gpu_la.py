@@ -109,6 +109,16 @@ def test_packed_many_chains_with_state():
     check(inp, what="la packed with state, 56 chains")
 
 
+@pytest.mark.parametrize("B,T,H,H_qk,state_dtype", [
+    (20, 100, 8, 8, torch.float32),     # 160 chains: four column tiles per recurrence workgroup
+    (20, 100, 8, 8, torch.bfloat16),
+    (20, 520, 8, 2, torch.float32),     # 160 chains, 360 (chunk, q/k head) jobs: shared q/k records
+])
+def test_many_chains_four_column_tiles(B, T, H, H_qk, state_dtype):
+    inp = make_inputs(B, T, H, H_qk, gate_per_channel=False, A_log=(-2.0, 0.0), state_std=0.05, seed=417 + B + T + H_qk)
+    check(inp, state_dtype=state_dtype, what="la many chains B=%d T=%d H=%d H_qk=%d %s" % (B, T, H, H_qk, state_dtype))
+
+
 def test_bf16_state():
     inp = make_inputs(2, 190, 2, 2, gate_per_channel=False, A_log=(-3.0, -1.0), state_std=0.05, seed=415)
     check(inp, state_dtype=torch.bfloat16, what="la bf16 state")
