@@ -25,8 +25,10 @@
 // whose first factor can reach 1/D_b.
 // The per-token log2-decays are scanned along the sub-chunk (prefix and
 // suffix sums) and every factor is one exp2 of a scan value.  Diagonal blocks
-// run on fp32 matrix cores (exact fp32 products) while D_b >= 2^-100 and fall
-// back to an exact per-channel evaluation in the log domain otherwise.
+// run on bf16 matrix cores with every operand split into hi + lo parts (about
+// 16 significant bits, and bf16 keeps the range of 1/D_b) while
+// D_b >= 2^-100 and fall back to an exact per-channel evaluation in the log
+// domain otherwise.
 // In scalar-gate mode exp(Gamma_r - Gamma_i) is one number per (r, i) and is
 // applied after the Gram products.  With value heads grouped on q/k heads a
 // separate kernel (chunk_group_kernel below) forms the head-independent part
@@ -330,7 +332,7 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
             P[q] = row_prefix_sum(P[q]);           // log2 rho
             S[q] = row_suffix_from_prefix(P[q]);  // log2 kappa
           }
-          float Dv[8];
+          float Dv[8], kik[8], qik[8];
 #pragma unroll
           for (int q = 0; q < 8; ++q) {
             const float rho = __builtin_amdgcn_exp2f(P[q]);
@@ -342,15 +344,26 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
             Y[v] = kn[q] * kap;
             Dv[q] = rho * kap;
             tiny |= !(Dv[q] >= TINY_D);
-            // diagonal block on fp32 matrix cores: the lane's value is the
-            // A/B operand of the 16x16x4 product for key (s, q)
-            if (q & 1) {
-              if (DELTA) accA2 = mma_f32(kn[q] * ikap, Y[v], accA2);
-              accM2 = mma_f32(Y[v], qn[q] * ikap, accM2);
-            } else {
-              if (DELTA) accA_d = mma_f32(kn[q] * ikap, Y[v], accA_d);
-              accM_d = mma_f32(Y[v], qn[q] * ikap, accM_d);
+            kik[q] = kn[q] * ikap;
+            qik[q] = qn[q] * ikap;
+          }
+          // diagonal block on bf16 matrix cores with hi + lo splits of every
+          // operand (about 16 significant bits; bf16 keeps the range of the
+          // row factor 1/kappa, which reaches 2^100)
+          {
+            bf16x8 yh, yl, qh, ql;
+            split_bf16x8(&Y[8 * s], yh, yl);
+            split_bf16x8(qik, qh, ql);
+            if (DELTA) {
+              bf16x8 kh, kl;
+              split_bf16x8(kik, kh, kl);
+              accA_d = mma_bf16(kh, yh, accA_d);
+              accA2 = mma_bf16(kh, yl, accA2);
+              accA2 = mma_bf16(kl, yh, accA2);
             }
+            accM_d = mma_bf16(yh, qh, accM_d);
+            accM2 = mma_bf16(yh, ql, accM2);
+            accM2 = mma_bf16(yl, qh, accM2);
           }
           if (l16 == 0) {  // D_n of this lane group's 8 keys
             *reinterpret_cast<float4*>(&DS[n * HD + 32 * s + 8 * lg]) = make_float4(Dv[0], Dv[1], Dv[2], Dv[3]);
