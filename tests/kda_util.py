@@ -68,7 +68,37 @@ def rel_l2(x, y):
     return float(np.linalg.norm(x - y) / n) if n > 0 else float(np.linalg.norm(x))
 
 
-def assert_parity(out, fin, ref_out, ref_fin, state_dtype=torch.float32, what=""):
+def chain_errors(out, fin, ref_out, ref_fin, cu_seqlens=None):
+    """Per-(chain, head) rel-L2 of the output and of the final state.
+
+    out / ref_out: [B, T, H, V] (forward) or [B, H, V] (one decode step);
+    fin / ref_fin: [C, H, V, K].  A chain is a batch row, or a packed
+    sequence when cu_seqlens is given.  Chains the oracle did not compute
+    (NaN in the reference) are skipped.  Returns a list of
+    (chain, head, out rel-L2, final-state rel-L2).
+    """
+    if out.ndim == 3:
+        out, ref_out = out[:, None], ref_out[:, None]
+    B, T, H, _ = ref_out.shape
+    if cu_seqlens is None:
+        spans = [(b, b, slice(None)) for b in range(B)]
+    else:
+        cu = np.asarray(cu_seqlens)
+        spans = [(n, 0, slice(int(cu[n]), int(cu[n + 1]))) for n in range(len(cu) - 1)]
+    res = []
+    for c, b, sl in spans:
+        for h in range(H):
+            ro, rf = ref_out[b, sl, h], ref_fin[c, h]
+            if np.isnan(rf).any() or np.isnan(ro).any():
+                continue
+            res.append((c, h, rel_l2(out[b, sl, h], ro), rel_l2(fin[c, h], rf)))
+    return res
+
+
+def assert_parity(out, fin, ref_out, ref_fin, state_dtype=torch.float32, what="", cu_seqlens=None):
+    """Pooled bars (out max-abs and rel-L2, final-state rel-L2) over every
+    compared element, plus the rel-L2 bars per (chain, head), so an error
+    confined to one chain cannot hide in the pooled norm."""
     sel = ~np.isnan(ref_out)
     o, ro = out[sel], ref_out[sel]
     maxabs = float(np.max(np.abs(o - ro))) if o.size else 0.0
@@ -76,9 +106,17 @@ def assert_parity(out, fin, ref_out, ref_fin, state_dtype=torch.float32, what=""
     srel_bar = STATE_REL_FP32 if state_dtype == torch.float32 else STATE_REL_BF16
     fsel = ~np.isnan(ref_fin)
     frel = rel_l2(fin[fsel], ref_fin[fsel])
-    msg = "%s out max-abs %.3e rel-L2 %.3e | final rel-L2 %.3e" % (what, maxabs, rel, frel)
+    per = chain_errors(out, fin, ref_out, ref_fin, cu_seqlens)
+    worst_o = max(per, key=lambda r: r[2]) if per else (-1, -1, 0.0, 0.0)
+    worst_f = max(per, key=lambda r: r[3]) if per else (-1, -1, 0.0, 0.0)
+    msg = ("%s out max-abs %.3e rel-L2 %.3e | final rel-L2 %.3e | %d chains, worst out rel-L2 %.3e (chain %d "
+           "head %d), worst final rel-L2 %.3e (chain %d head %d)" % (
+               what, maxabs, rel, frel, len(per), worst_o[2], worst_o[0], worst_o[1], worst_f[3], worst_f[0],
+               worst_f[1]))
     print(msg, flush=True)
     assert np.all(np.isfinite(out)), "non-finite output " + msg
     assert maxabs <= OUT_MAXABS and rel <= OUT_REL, msg
     assert frel <= srel_bar, msg
+    assert worst_o[2] <= OUT_REL, "per-chain output bar: " + msg
+    assert worst_f[3] <= srel_bar, "per-chain final-state bar: " + msg
     return maxabs, rel, frel

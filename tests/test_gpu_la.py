@@ -2,13 +2,13 @@
 kda_la_decode_step) against the fp64 oracle in oracle/la.py.
 
 The bar is the KDA one (out rel-L2 <= 5e-3, fp32 final state rel-L2 <=
-1e-3) with the absolute output bound scaled by the largest reference output.
-q and k are not normalised here, so outputs reach ~10 instead of O(1); the
-bf16 output alone then rounds by up to 2^-9 of that (0.03 at |o| = 10), and
-the fp16 chunk records hold intra-chunk products q.k of size ~K with a
-relative rounding of 2^-11.  Both are relative errors, so the absolute bound
-scales with the output's magnitude; for KDA's O(1) outputs the two bounds
-coincide.
+1e-3, pooled and per (chain, head)) with the absolute output bound scaled by
+the largest reference output.  q and k are not normalised here, so outputs
+reach ~10 instead of O(1), and the bf16 rounding of the output alone is then
+up to 2^-9 of that (0.02 at |o| = 10): a correct result's absolute error
+grows with the output's magnitude through that rounding.  Scaling the KDA
+bound by max(1, max|o_ref|) keeps the same ten-fold margin over the output
+rounding that the KDA bar has at O(1) outputs.
 """
 
 import numpy as np
@@ -41,7 +41,7 @@ def run_oracle(inp, chain_mask=None):
                      cu_seqlens=inp.get("cu_seqlens"), chain_mask=chain_mask)
 
 
-def assert_parity(out, fin, ref_out, ref_fin, state_dtype=torch.float32, what=""):
+def assert_parity(out, fin, ref_out, ref_fin, state_dtype=torch.float32, what="", cu_seqlens=None):
     sel = ~np.isnan(ref_out)
     o, ro = out[sel], ref_out[sel]
     peak = float(np.max(np.abs(ro))) if ro.size else 0.0
@@ -51,19 +51,23 @@ def assert_parity(out, fin, ref_out, ref_fin, state_dtype=torch.float32, what=""
     frel = U.rel_l2(fin[fsel], ref_fin[fsel])
     bar_abs = U.OUT_MAXABS * max(1.0, peak)
     bar_state = U.STATE_REL_FP32 if state_dtype == torch.float32 else U.STATE_REL_BF16
-    msg = "%s out max-abs %.3e (bar %.3e, peak %.2f) rel-L2 %.3e | final rel-L2 %.3e" % (
-        what, maxabs, bar_abs, peak, rel, frel)
+    per = U.chain_errors(out, fin, ref_out, ref_fin, cu_seqlens)
+    wo = max((r[2] for r in per), default=0.0)
+    wf = max((r[3] for r in per), default=0.0)
+    msg = "%s out max-abs %.3e (bar %.3e, peak %.2f) rel-L2 %.3e | final rel-L2 %.3e | %d chains, worst %.3e / %.3e" % (
+        what, maxabs, bar_abs, peak, rel, frel, len(per), wo, wf)
     print(msg, flush=True)
     assert np.all(np.isfinite(out)), "non-finite output " + msg
     assert maxabs <= bar_abs and rel <= U.OUT_REL, msg
     assert frel <= bar_state, msg
+    assert wo <= U.OUT_REL and wf <= bar_state, "per-chain bar: " + msg
 
 
 def check(inp, state_dtype=torch.float32, what="", chain_mask=None):
     print("case:", what, flush=True)
     out, fin = run_gpu(inp, state_dtype)
     ref_out, ref_fin = run_oracle(U.state_as_stored(inp, state_dtype), chain_mask=chain_mask)
-    assert_parity(out, fin, ref_out, ref_fin, state_dtype, what)
+    assert_parity(out, fin, ref_out, ref_fin, state_dtype, what, cu_seqlens=inp.get("cu_seqlens"))
 
 
 @pytest.mark.parametrize("T", [64, 150, 257])
