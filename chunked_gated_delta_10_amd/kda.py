@@ -113,6 +113,47 @@ def _need(t: torch.Tensor, name: str, dtype: torch.dtype):
         raise ValueError("%s must be contiguous" % name)
 
 
+def _same_device(first: torch.Tensor, *rest) -> None:
+    for t in rest:
+        if t is not None and t.device != first.device:
+            raise ValueError("inputs are on different devices (%s and %s)" % (first.device, t.device))
+
+
+def _check_out(out: torch.Tensor, shape, device) -> None:
+    """A caller-supplied output must be exactly what the kernels write: the
+    library cannot see buffer sizes, so a short or mistyped buffer would be
+    written past its end."""
+    if out.dtype != torch.bfloat16:
+        raise TypeError("out must be bfloat16, got %s" % out.dtype)
+    if tuple(out.shape) != tuple(shape):
+        raise ValueError("out must have shape %s, got %s" % (tuple(shape), tuple(out.shape)))
+    if not out.is_contiguous():
+        raise ValueError("out must be contiguous")
+    if out.device != device:
+        raise ValueError("out is on %s, the inputs on %s" % (out.device, device))
+
+
+def _check_state(t: Optional[torch.Tensor], name: str, shape, device) -> None:
+    if t is None:
+        return
+    _state_code(t)
+    if tuple(t.shape) != tuple(shape) or not t.is_contiguous():
+        raise ValueError("%s must be a contiguous %s tensor, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if t.device != device:
+        raise ValueError("%s is on %s, the inputs on %s" % (name, t.device, device))
+
+
+def _check_workspace(ws: torch.Tensor, nbytes: int, device) -> None:
+    if ws.dtype != torch.uint8:
+        raise TypeError("workspace must be a uint8 tensor, got %s" % ws.dtype)
+    if not ws.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    if ws.device != device:
+        raise ValueError("workspace is on %s, the inputs on %s" % (ws.device, device))
+    if ws.numel() < nbytes:
+        raise ValueError("workspace holds %d bytes, %d needed" % (ws.numel(), nbytes))
+
+
 def kernel_timing(enable: bool) -> None:
     """Turn per-kernel HIP-event timing of this thread's launches on or off."""
     load().kda_kernel_timing_enable(1 if enable else 0)
@@ -146,6 +187,7 @@ def _prep(q, k, v, g_raw, beta_logits, A_log):
     if beta_logits is not None:
         _need(beta_logits, "beta_logits", torch.float32)
     _need(A_log, "A_log", torch.float32)
+    _same_device(q, k, v, g_raw, beta_logits, A_log)
     if q.dim() != 4 or k.shape != q.shape or v.dim() != 4 or v.shape[:2] != q.shape[:2]:
         raise ValueError("q, k must be [B, T, H_qk, K] and v [B, T, H, V]")
     B, T, H_qk, K = q.shape
@@ -173,15 +215,16 @@ def fwd(q, k, v, g_raw, beta_logits, A_log, scale: Optional[float] = None,
     dev = q.device
     if out is None:
         out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
+    _check_out(out, (B, T, H, V), dev)
     if final_state is None and output_final_state:
         sd = state_dtype or (initial_state.dtype if initial_state is not None else torch.float32)
         final_state = torch.empty((B, H, V, K), dtype=sd, device=dev)
-    for t, n in ((initial_state, "initial_state"), (final_state, "final_state")):
-        if t is not None and (tuple(t.shape) != (B, H, V, K) or not t.is_contiguous()):
-            raise ValueError("%s must be a contiguous [B, H, V, K] tensor" % n)
+    _check_state(initial_state, "initial_state", (B, H, V, K), dev)
+    _check_state(final_state, "final_state", (B, H, V, K), dev)
     nbytes = workspace_bytes(B, T, H_qk, H, 0)
-    if workspace is None or workspace.numel() < nbytes:
+    if workspace is None:
         workspace = _workspace(nbytes, dev)
+    _check_workspace(workspace, nbytes, dev)
     _check(lib.kda_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale,
                        per_channel, _ptr(initial_state), _state_code(initial_state), _ptr(out),
                        _ptr(final_state), _state_code(final_state), B, T, H_qk, H, K, V, _ptr(workspace),
@@ -203,17 +246,20 @@ def fwd_varlen(q, k, v, g_raw, beta_logits, A_log, cu_seqlens: torch.Tensor, sca
     N = cu_seqlens.numel() - 1
     scale = K ** -0.5 if scale is None else float(scale)
     dev = q.device
+    if cu_seqlens.device != dev:
+        raise ValueError("cu_seqlens is on %s, the inputs on %s" % (cu_seqlens.device, dev))
     if out is None:
         out = torch.empty((1, T, H, V), dtype=torch.bfloat16, device=dev)
+    _check_out(out, (1, T, H, V), dev)
     if final_state is None and output_final_state:
         sd = state_dtype or (initial_state.dtype if initial_state is not None else torch.float32)
         final_state = torch.empty((N, H, V, K), dtype=sd, device=dev)
-    for t, n in ((initial_state, "initial_state"), (final_state, "final_state")):
-        if t is not None and (tuple(t.shape) != (N, H, V, K) or not t.is_contiguous()):
-            raise ValueError("%s must be a contiguous [N, H, V, K] tensor" % n)
+    _check_state(initial_state, "initial_state", (N, H, V, K), dev)
+    _check_state(final_state, "final_state", (N, H, V, K), dev)
     nbytes = workspace_bytes(1, T, H_qk, H, max(N, 0))
-    if workspace is None or workspace.numel() < nbytes:
+    if workspace is None:
         workspace = _workspace(nbytes, dev)
+    _check_workspace(workspace, nbytes, dev)
     _check(lib.kda_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale,
                               per_channel, _ptr(initial_state), _state_code(initial_state), _ptr(out),
                               _ptr(final_state), _state_code(final_state), _ptr(cu_seqlens), N, T, H_qk, H, K, V,
@@ -229,6 +275,7 @@ def decode_step(q, k, v, g_raw, beta_logits, A_log, state: torch.Tensor, scale: 
                      (g_raw, "g_raw", torch.bfloat16), (beta_logits, "beta_logits", torch.float32),
                      (A_log, "A_log", torch.float32)):
         _need(t, n, dt)
+    _same_device(q, k, v, g_raw, A_log)
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3:
         raise ValueError("q, k must be [B, H_qk, K] and v [B, H, V]")
     B, H_qk, K = q.shape
@@ -239,11 +286,11 @@ def decode_step(q, k, v, g_raw, beta_logits, A_log, state: torch.Tensor, scale: 
         per_channel = 0
     else:
         raise ValueError("g_raw must be [B, H, K] or [B, H]")
-    if tuple(state.shape) != (B, H, V, K) or not state.is_contiguous():
-        raise ValueError("state must be a contiguous [B, H, V, K] tensor")
+    _check_state(state, "state", (B, H, V, K), q.device)
     scale = K ** -0.5 if scale is None else float(scale)
     if out is None:
         out = torch.empty((B, H, V), dtype=torch.bfloat16, device=q.device)
+    _check_out(out, (B, H, V), q.device)
     _check(lib.kda_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale,
                                per_channel, _ptr(state), _state_code(state), _ptr(out), B, H_qk, H, K, V,
                                _stream(stream)))
@@ -259,9 +306,8 @@ def _states(initial_state, final_state, output_final_state, state_dtype, C, H, V
     if final_state is None and output_final_state:
         sd = state_dtype or (initial_state.dtype if initial_state is not None else torch.float32)
         final_state = torch.empty((C, H, V, K), dtype=sd, device=dev)
-    for t, n in ((initial_state, "initial_state"), (final_state, "final_state")):
-        if t is not None and (tuple(t.shape) != (C, H, V, K) or not t.is_contiguous()):
-            raise ValueError("%s must be a contiguous [%d, H, V, K] tensor" % (n, C))
+    _check_state(initial_state, "initial_state", (C, H, V, K), dev)
+    _check_state(final_state, "final_state", (C, H, V, K), dev)
     return final_state
 
 
@@ -276,10 +322,12 @@ def la_fwd(q, k, v, g_raw, A_log, scale: Optional[float] = None, initial_state: 
     dev = q.device
     if out is None:
         out = torch.empty((B, T, H, V), dtype=torch.bfloat16, device=dev)
+    _check_out(out, (B, T, H, V), dev)
     final_state = _states(initial_state, final_state, output_final_state, state_dtype, B, H, V, K, dev)
     nbytes = workspace_bytes(B, T, H_qk, H, 0)
-    if workspace is None or workspace.numel() < nbytes:
+    if workspace is None:
         workspace = _workspace(nbytes, dev)
+    _check_workspace(workspace, nbytes, dev)
     _check(lib.kda_la_fwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(A_log), scale, per_channel,
                           _ptr(initial_state), _state_code(initial_state), _ptr(out), _ptr(final_state),
                           _state_code(final_state), B, T, H_qk, H, K, V, _ptr(workspace), workspace.numel(),
@@ -301,12 +349,16 @@ def la_fwd_varlen(q, k, v, g_raw, A_log, cu_seqlens: torch.Tensor, scale: Option
     N = cu_seqlens.numel() - 1
     scale = K ** -0.5 if scale is None else float(scale)
     dev = q.device
+    if cu_seqlens.device != dev:
+        raise ValueError("cu_seqlens is on %s, the inputs on %s" % (cu_seqlens.device, dev))
     if out is None:
         out = torch.empty((1, T, H, V), dtype=torch.bfloat16, device=dev)
+    _check_out(out, (1, T, H, V), dev)
     final_state = _states(initial_state, final_state, output_final_state, state_dtype, N, H, V, K, dev)
     nbytes = workspace_bytes(1, T, H_qk, H, max(N, 0))
-    if workspace is None or workspace.numel() < nbytes:
+    if workspace is None:
         workspace = _workspace(nbytes, dev)
+    _check_workspace(workspace, nbytes, dev)
     _check(lib.kda_la_fwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(A_log), scale, per_channel,
                                  _ptr(initial_state), _state_code(initial_state), _ptr(out), _ptr(final_state),
                                  _state_code(final_state), _ptr(cu_seqlens), N, T, H_qk, H, K, V, _ptr(workspace),
@@ -321,6 +373,7 @@ def la_decode_step(q, k, v, g_raw, A_log, state: torch.Tensor, scale: Optional[f
     for t, n, dt in ((q, "q", torch.bfloat16), (k, "k", torch.bfloat16), (v, "v", torch.bfloat16),
                      (g_raw, "g_raw", torch.bfloat16), (A_log, "A_log", torch.float32)):
         _need(t, n, dt)
+    _same_device(q, k, v, g_raw, A_log)
     if q.dim() != 3 or k.shape != q.shape or v.dim() != 3:
         raise ValueError("q, k must be [B, H_qk, K] and v [B, H, V]")
     B, H_qk, K = q.shape
@@ -331,11 +384,11 @@ def la_decode_step(q, k, v, g_raw, A_log, state: torch.Tensor, scale: Optional[f
         per_channel = 0
     else:
         raise ValueError("g_raw must be [B, H, K] or [B, H]")
-    if tuple(state.shape) != (B, H, V, K) or not state.is_contiguous():
-        raise ValueError("state must be a contiguous [B, H, V, K] tensor")
+    _check_state(state, "state", (B, H, V, K), q.device)
     scale = K ** -0.5 if scale is None else float(scale)
     if out is None:
         out = torch.empty((B, H, V), dtype=torch.bfloat16, device=q.device)
+    _check_out(out, (B, H, V), q.device)
     _check(lib.kda_la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(A_log), scale, per_channel,
                                   _ptr(state), _state_code(state), _ptr(out), B, H_qk, H, K, V, _stream(stream)))
     return out
