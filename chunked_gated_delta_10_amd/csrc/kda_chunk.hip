@@ -141,20 +141,42 @@ __device__ __forceinline__ f32x4 mul_cc(const f32x4& XT, const f32x4& Y) {
   return mma_f32(XT[3], Y[3], z);
 }
 
-// (I + N)^-1 for a strictly lower triangular 16 x 16 block N (so N^16 = 0):
-// (I - N)(I + N^2)(I + N^4)(I + N^8).  The factors are polynomials in N and
-// commute, so each product takes the transpose of a power of N as its left
-// operand: eight block products on fp32 matrix cores, all in registers.
+// (I + N)^-1 for a strictly lower triangular 16 x 16 block N: blocked
+// forward substitution with block sizes doubling 1 -> 2 -> 4 -> 8 -> 16.
+// With D_k the block-diagonal part of the inverse made of its k x k diagonal
+// blocks (D_1 = I) and M_k the part of N inside the 2k x 2k diagonal blocks
+// but outside the k x k ones, every 2k x 2k diagonal block of the inverse is
+// [[T11, 0], [-T22 N21 T11, T22]], that is D_2k = D_k - D_k M_k D_k.  Every
+// intermediate is a block of the inverse or of N (no powers of N, which
+// reach ~3e3 for nearly parallel keys and would cancel in fp32), so the
+// rounding is that of forward substitution.  Eight block products on fp32
+// matrix cores, all in registers; D and D^T are both carried in C layout so
+// every product reads its operands in place.
 // Nc, NT: N and N^T in C layout; result in C layout.
 __device__ __forceinline__ f32x4 unit_lower_inverse(const f32x4& Nc, const f32x4& NT, int l16, int lg) {
-  const f32x4 N2 = mul_cc(NT, Nc), N2T = mul_cc(Nc, NT);
-  const f32x4 N3 = mul_cc(NT, N2), N4 = mul_cc(N2T, N2), N4T = mul_cc(N2, N2T);
-  const f32x4 N8T = mul_cc(N4, N4T);
-  f32x4 P1;  // (I - N)(I + N^2) = I - N + N^2 - N^3
+  f32x4 D, DT;
 #pragma unroll
-  for (int j = 0; j < 4; ++j) P1[j] = (4 * lg + j == l16 ? 1.f : 0.f) - Nc[j] + N2[j] - N3[j];
-  const f32x4 P2 = P1 + mul_cc(N4T, P1);  // (I + N^4) P1
-  return P2 + mul_cc(N8T, P2);            // (I + N^8) P2
+  for (int j = 0; j < 4; ++j) {  // D_2 = I - M_1
+    const int r = 4 * lg + j, c = l16;
+    const float eye = r == c ? 1.f : 0.f;
+    const bool in1 = (r >> 1) == (c >> 1) && r != c;
+    D[j] = eye - (in1 ? Nc[j] : 0.f);
+    DT[j] = eye - (in1 ? NT[j] : 0.f);
+  }
+#pragma unroll
+  for (int k = 2; k < SUB; k *= 2) {
+    f32x4 MT;  // M_k^T (the mask is symmetric in row and column)
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * lg + j, c = l16;
+      MT[j] = ((r / (2 * k)) == (c / (2 * k)) && (r / k) != (c / k)) ? NT[j] : 0.f;
+    }
+    const f32x4 P = mul_cc(MT, D);   // M_k D_k
+    const f32x4 Q = mul_cc(DT, P);   // D_k M_k D_k
+    if (2 * k < SUB) DT = DT - mul_cc(P, DT);  // (D_k M_k D_k)^T = P^T D_k^T
+    D = D - Q;
+  }
+  return D;
 }
 
 // Store an A-operand fragment held in natural key order (this lane: keys
@@ -684,7 +706,7 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
           }
         }
 
-        // ---- 4. T_nn = (I + A_nn)^-1 on fp32 matrix cores ----------------------
+        // ---- 4. T_nn = (I + A_nn)^-1 on fp32 matrix cores (blocked substitution) -
         // A_nn^T in C layout is one row read of the A rows this wave wrote just
         // above (no barrier needed within a wave).
         f32x4 Tnn = zero4();
@@ -1141,46 +1163,48 @@ __global__ __launch_bounds__(NT, (Lds<false, DELTA>::JOBS_PER_CU)) void chunk_gr
 }
 
 namespace {
+// The dynamic LDS size above 64 KB is a per-device kernel attribute.
 template <bool PER_CHANNEL, bool DELTA>
-void launch_chunk_variant(const ChunkParams& p, int n_jobs, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_local_kernel<PER_CHANNEL, DELTA>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, Lds<PER_CHANNEL, DELTA>::BYTES);
-    attr_set = true;
-  }
+hipError_t launch_chunk_variant(const ChunkParams& p, int n_jobs, hipStream_t stream) {
+  static std::atomic<int> attr_set[MAX_DEVICES];
+  const hipError_t e = once_per_device(attr_set, [] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_local_kernel<PER_CHANNEL, DELTA>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, Lds<PER_CHANNEL, DELTA>::BYTES);
+  });
+  if (e != hipSuccess) return e;
   // one job per workgroup; two (full layout, LDS-bound) or three (compact) per CU
   chunk_local_kernel<PER_CHANNEL, DELTA><<<n_jobs, NT, Lds<PER_CHANNEL, DELTA>::BYTES, stream>>>(p, n_jobs);
+  return hipSuccess;
 }
 
 // one job per (chunk, q/k head); two (full layout) or three (compact) per CU
 template <bool DELTA>
-void launch_group_variant(const ChunkParams& p, int n_jobs, hipStream_t stream) {
-  static bool attr_set = false;
-  if (!attr_set) {
-    (void)hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_group_kernel<DELTA>),
-                              hipFuncAttributeMaxDynamicSharedMemorySize, Lds<false, DELTA>::BYTES);
-    attr_set = true;
-  }
+hipError_t launch_group_variant(const ChunkParams& p, int n_jobs, hipStream_t stream) {
+  static std::atomic<int> attr_set[MAX_DEVICES];
+  const hipError_t e = once_per_device(attr_set, [] {
+    return hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_group_kernel<DELTA>),
+                               hipFuncAttributeMaxDynamicSharedMemorySize, Lds<false, DELTA>::BYTES);
+  });
+  if (e != hipSuccess) return e;
   chunk_group_kernel<DELTA><<<n_jobs, NT, Lds<false, DELTA>::BYTES, stream>>>(p, n_jobs);
+  return hipSuccess;
 }
 }  // namespace
 
-void launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, bool delta, hipStream_t stream) {
+hipError_t launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, bool delta,
+                              hipStream_t stream) {
   const int n_jobs = n_entries * p.H;
-  if (n_jobs <= 0) return;
+  if (n_jobs <= 0) return hipSuccess;
   if (shares_qk_fragments(per_channel, p.H, p.H_qk, n_entries)) {  // one workgroup per (chunk, q/k head)
-    if (delta) launch_group_variant<true>(p, n_entries * p.H_qk, stream);
-    else launch_group_variant<false>(p, n_entries * p.H_qk, stream);
-    return;
+    if (delta) return launch_group_variant<true>(p, n_entries * p.H_qk, stream);
+    return launch_group_variant<false>(p, n_entries * p.H_qk, stream);
   }
   if (delta) {
-    if (per_channel) launch_chunk_variant<true, true>(p, n_jobs, stream);
-    else launch_chunk_variant<false, true>(p, n_jobs, stream);
-  } else {
-    if (per_channel) launch_chunk_variant<true, false>(p, n_jobs, stream);
-    else launch_chunk_variant<false, false>(p, n_jobs, stream);
+    if (per_channel) return launch_chunk_variant<true, true>(p, n_jobs, stream);
+    return launch_chunk_variant<false, true>(p, n_jobs, stream);
   }
+  if (per_channel) return launch_chunk_variant<true, false>(p, n_jobs, stream);
+  return launch_chunk_variant<false, false>(p, n_jobs, stream);
 }
 
 }  // namespace kda
