@@ -213,7 +213,8 @@ kda_status run_forward(const FwdArgs& a) {
                         static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log, chunks, a.H, a.H_qk, ws + L.rec,
                         a.cu ? 0 : a.T};
     Timed t(K_CHUNK, a.stream);
-    kda::launch_chunk_local(cp, n_entries, a.gate_per_channel == 1, a.delta, a.stream);
+    const hipError_t e = kda::launch_chunk_local(cp, n_entries, a.gate_per_channel == 1, a.delta, a.stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel setup failed: %s", hipGetErrorString(e));
   }
   kda::RecurParams rp{ws + L.rec, seqs, order, a.n_seqs * a.H, n_entries, a.H, a.H_qk, static_cast<const uint16_t*>(a.v),
                       static_cast<uint16_t*>(a.out), a.s0, a.s1, a.scale,

@@ -4,7 +4,34 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <atomic>
+
 namespace kda {
+
+// ---- host-side, per-device setup ---------------------------------------------
+constexpr int MAX_DEVICES = 64;
+
+// The calling thread's current device (0 if it cannot be read).
+inline int current_device() {
+  int d = 0;
+  return (hipGetDevice(&d) == hipSuccess && d >= 0 && d < MAX_DEVICES) ? d : 0;
+}
+
+// Runs set() on the current device until it has once succeeded there
+// (e.g. a kernel attribute, which is per device).  Concurrent first calls
+// may both run set(), which is harmless for idempotent settings.  Returns
+// set()'s error, or hipSuccess once done.
+template <typename F>
+hipError_t once_per_device(std::atomic<int> (&done)[MAX_DEVICES], F set) {
+  const int d = current_device();
+  if (done[d].load(std::memory_order_acquire)) return hipSuccess;
+  const hipError_t e = set();
+  if (e == hipSuccess) done[d].store(1, std::memory_order_release);
+  return e;
+}
+
+// Compute units of the current device (cached per device).
+int device_cu_count();
 
 // Chunk-local kernel (kda_chunk.hip): one workgroup per (schedule entry, head).
 struct ChunkParams {
@@ -62,8 +89,10 @@ struct TableParams {
 };
 
 void launch_table(const TableParams& p, hipStream_t stream);
-// delta = false: decay-only linear attention (no erase, no write strength, no q/k normalisation)
-void launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, bool delta, hipStream_t stream);
+// delta = false: decay-only linear attention (no erase, no write strength, no q/k normalisation).
+// Returns the error of the kernel's one-time attribute setup on this device (launch errors are
+// read by the caller with hipGetLastError).
+hipError_t launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, bool delta, hipStream_t stream);
 void launch_recur(const RecurParams& p, bool bf16_state, bool per_channel, bool delta, hipStream_t stream);
 // Scalar gate with value heads grouped on q/k heads and at least
 // GROUP_MIN_JOBS (schedule entry, q/k head) jobs: the value heads of a group

@@ -429,16 +429,19 @@ namespace {
 // workgroups for n_chains chains with `tiles` workgroups per chain
 int grid_for(int n_chains, int tiles) { return ((n_chains + 7) / 8) * 8 * tiles; }
 
-int cu_count() {
-  static int cus = 0;
-  if (cus == 0) {
-    int dev = 0, v = 0;
-    cus = (hipGetDevice(&dev) == hipSuccess &&
-           hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess && v > 0) ? v : 256;
-  }
-  return cus;
-}
+int cu_count() { return device_cu_count(); }
 }  // namespace
+
+int device_cu_count() {
+  static std::atomic<int> cus[MAX_DEVICES];
+  const int d = current_device();
+  int v = cus[d].load(std::memory_order_relaxed);
+  if (v == 0) {
+    if (hipDeviceGetAttribute(&v, hipDeviceAttributeMultiprocessorCount, d) != hipSuccess || v <= 0) v = 256;
+    cus[d].store(v, std::memory_order_relaxed);
+  }
+  return v;
+}
 
 bool shares_qk_fragments(bool per_channel, int H, int H_qk, int n_entries) {
   // the grouped chunk-local kernel walks a group's heads in series, so it
