@@ -122,7 +122,8 @@ def cu_seqlens_from_lengths(lens) -> np.ndarray:
 def make_inputs(B: int, T: int, H: int, H_qk: int, *, gate_per_channel: bool = True,
                 A_log=(-1.0, 1.0), state_std: Optional[float] = None, N: int = 0,
                 lengths=None, seed: int = 0, K: int = HEAD_DIM, V: int = HEAD_DIM,
-                decode: bool = False, g_shift: float = 0.0, b_shift: float = 0.0) -> dict:
+                decode: bool = False, g_shift: float = 0.0, b_shift: float = 0.0,
+                k_noise: Optional[float] = None) -> dict:
     """Draw one batch of inputs.
 
     Returns a dict of numpy arrays: q, k, v, g_raw (uint16 bf16 bits), b, A_log
@@ -130,7 +131,9 @@ def make_inputs(B: int, T: int, H: int, H_qk: int, *, gate_per_channel: bool = T
     plus the scale 1/sqrt(K).  With decode=True the token axis is dropped
     (q: [B, H_qk, K]).  g_shift / b_shift add a constant to the normal draws
     of g_raw / b before rounding (used by tests that need milder or harsher
-    gates).
+    gates).  With k_noise set, keys are nearly parallel: each q/k head draws
+    one direction d ~ N(0, I) after every other draw, and its keys become
+    d + k_noise * (the normal draw), so the decayed Gram entries sit near 1.
     """
     rng = np.random.default_rng(seed)
     lead = (B,) if decode else (B, T)
@@ -156,6 +159,9 @@ def make_inputs(B: int, T: int, H: int, H_qk: int, *, gate_per_channel: bool = T
     s0 = None
     if state_std is not None:
         s0 = (rng.standard_normal((C, H, V, K), dtype=np.float32) * np.float32(state_std)).astype(np.float32)
+    if k_noise is not None:
+        d = rng.standard_normal((H_qk, K), dtype=np.float32)
+        k = (d + np.float32(k_noise) * k).astype(np.float32)
     return {
         "q": bf16_bits(q), "k": bf16_bits(k), "v": bf16_bits(v), "g_raw": bf16_bits(g),
         "A_log": a_log, "b": b.astype(np.float32), "initial_state": s0, "cu_seqlens": cu,
@@ -174,11 +180,13 @@ def workload_inputs(name: str) -> dict:
 # row uses the scalar per-token decay g = -softplus(N(0,1)) (A_log = 0), no
 # initial state, and is drawn once per head shape at 32768 tokens; a pattern
 # uses the first sum(lengths) tokens.
-SWEEP_HEAD_SHAPES = [(2, 8), (4, 16), (8, 24), (8, 32), (16, 16), (16, 32), (16, 48), (16, 64)]
+SWEEP_HEAD_SHAPES = [(2, 8), (4, 16), (8, 24), (8, 32), (16, 16), (16, 32), (16, 48), (16, 64), (32, 32)]
 SWEEP_PATTERNS: Dict[str, Tuple[int, ...]] = {
     "1x2048": (2048,), "1x4096": (4096,), "1x8192": (8192,), "1x16384": (16384,), "1x32768": (32768,),
-    "28672+4096": (28672, 4096), "16384+16384": (16384, 16384), "4096+28672": (4096, 28672),
-    "12288+4096": (12288, 4096), "1024+7168": (1024, 7168),
+    "28672+4096": (28672, 4096), "24576+8192": (24576, 8192), "16384+16384": (16384, 16384),
+    "8192+24576": (8192, 24576), "4096+28672": (4096, 28672),
+    "12288+4096": (12288, 4096), "6144+2048": (6144, 2048), "4096+4096": (4096, 4096), "2048+6144": (2048, 6144),
+    "1024+7168": (1024, 7168),
     "8192x4": (8192,) * 4, "4096x8": (4096,) * 8, "2048x4": (2048,) * 4, "1024x8": (1024,) * 8,
 }
 SWEEP_TOKENS = 32768

@@ -23,7 +23,7 @@ def check(inp, state_dtype=torch.float32, what="", chain_mask=None):
     print("case:", what, flush=True)
     out, fin = U.run_gpu(inp, state_dtype)
     ref_out, ref_fin = U.run_oracle(U.state_as_stored(inp, state_dtype), chain_mask=chain_mask)
-    return U.assert_parity(out, fin, ref_out, ref_fin, state_dtype, what)
+    return U.assert_parity(out, fin, ref_out, ref_fin, state_dtype, what, cu_seqlens=inp.get("cu_seqlens"))
 
 
 def test_tiny_workload():
@@ -280,7 +280,7 @@ def test_full_size_workload_sampled_chains(name):
     check(inp, what=name + " sampled chains", chain_mask=sampled_mask(C, w.H, picks))
 
 
-@pytest.mark.parametrize("h_qk,h_v,pattern", [(2, 8, "28672+4096"), (16, 64, "8192x4")])
+@pytest.mark.parametrize("h_qk,h_v,pattern", [(2, 8, "28672+4096"), (16, 64, "8192x4"), (32, 32, "24576+8192")])
 def test_full_size_sweep_rows_sampled_chains(h_qk, h_v, pattern):
     # two rows of the grouped-head sweep at their full size, in the launch
     # configuration the sweep times; the oracle checks sampled chains

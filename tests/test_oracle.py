@@ -392,6 +392,12 @@ def test_grouped_head_sweep_recipe():
         assert h_v % h_qk == 0
     for lens in SWEEP_PATTERNS.values():
         assert 0 < sum(lens) <= SWEEP_TOKENS and min(lens) > 0
+    # the FlashQLA H200 forward table: nine head shapes (the symmetric
+    # h_qk = h_v = 32 block included) and nineteen sequence patterns each
+    assert len(SWEEP_HEAD_SHAPES) == 9 and (32, 32) in SWEEP_HEAD_SHAPES
+    assert len(SWEEP_PATTERNS) == 19
+    for name in ("24576+8192", "8192+24576", "6144+2048", "4096+4096", "2048+6144"):
+        assert sum(SWEEP_PATTERNS[name]) == sum(int(x) for x in name.split("+"))
 
 
 def test_bf16_rounding_is_nearest_even():
