@@ -154,21 +154,62 @@ def traffic_from(root, copy_bytes, workload="kda_dense"):
     print(json.dumps(out, indent=1))
 
 
-def cpu_baseline(inp, w, tokens):
-    """The fp64 oracle, untuned, on the first `tokens` tokens of every row of the same workload."""
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return None
+
+
+def cpu_baseline(inp, w, tokens, tokens_1t):
+    """The fp64 oracle, untuned, on the same workload: all chains over the first
+    `tokens` tokens of every row with every allowed thread, and the first
+    `tokens_1t` tokens of every row on one thread."""
     import numpy as np
     import oracle
-    sub = {}
-    for n in ("q", "k", "v", "g_raw", "b"):
-        sub[n] = np.ascontiguousarray(inp[n][:, :tokens])
-    cores = min(os.cpu_count() or 1, w.B * w.H)
-    t0 = time.perf_counter()
-    oracle.kda_fwd(sub["q"], sub["k"], sub["v"], sub["g_raw"], sub["b"], inp["A_log"], inp["scale"],
-                   gate_per_channel=w.gate_per_channel, initial_state=inp["initial_state"], nthreads=cores)
-    dt = time.perf_counter() - t0
+    env_threads = os.environ.get("OMP_NUM_THREADS")
+    allowed = int(env_threads) if env_threads and env_threads.isdigit() else (os.cpu_count() or 1)
+    cores = max(1, min(allowed, w.B * w.H))   # the oracle is parallel over chains only
+
+    def run(n_tok, threads):
+        sub = {n: np.ascontiguousarray(inp[n][:, :n_tok]) for n in ("q", "k", "v", "g_raw", "b")}
+        t0 = time.perf_counter()
+        oracle.kda_fwd(sub["q"], sub["k"], sub["v"], sub["g_raw"], sub["b"], inp["A_log"], inp["scale"],
+                       gate_per_channel=w.gate_per_channel, initial_state=inp["initial_state"], nthreads=threads)
+        return time.perf_counter() - t0
+
+    dt = run(tokens, cores)
+    dt1 = run(tokens_1t, 1)
     return {"value": w.B * tokens / dt, "unit": "tokens/s", "cores": cores, "kind": "oracle",
-            "sample": "%s: all %d chains (B=%d x H=%d), first %d of %d tokens per row, fp32 initial state; %.1f s"
-                      % (w.name, w.B * w.H, w.B, w.H, tokens, w.T, dt)}
+            "sample": "%s: all %d chains (B=%d x H=%d), first %d of %d tokens per row, fp32 initial state, "
+                      "%d threads; %.1f s" % (w.name, w.B * w.H, w.B, w.H, tokens, w.T, cores, dt),
+            "single_thread": {"value": w.B * tokens_1t / dt1, "unit": "tokens/s", "cores": 1,
+                              "sample": "all %d chains, first %d tokens per row, 1 thread; %.1f s"
+                                        % (w.B * w.H, tokens_1t, dt1)},
+            "cpu_model": _cpu_model(), "nproc": os.cpu_count(), "omp_num_threads": env_threads,
+            "build": "gcc -O3 -fopenmp (plain C, fp64, token by token)"}
+
+
+def device_inputs(inp, state_dtype):
+    """Copy one batch of seeded host inputs (bf16 bit patterns, fp32, int32) to the GPU."""
+    import numpy as np
+    import torch
+
+    def bf16(bits):
+        return torch.from_numpy(np.ascontiguousarray(bits).view(np.int16)).view(torch.bfloat16).cuda()
+
+    d = {n: bf16(inp[n]) for n in ("q", "k", "v", "g_raw")}
+    d["b"] = torch.from_numpy(inp["b"]).cuda()
+    d["A_log"] = torch.from_numpy(inp["A_log"]).cuda()
+    s0 = inp.get("initial_state")
+    d["initial_state"] = None if s0 is None else torch.from_numpy(s0).to(device="cuda", dtype=state_dtype)
+    cu = inp.get("cu_seqlens")
+    d["cu_seqlens"] = None if cu is None else torch.from_numpy(cu).cuda()
+    return d
 
 
 def time_workload(name, steps, warmup, bf16_state=False):
@@ -177,12 +218,10 @@ def time_workload(name, steps, warmup, bf16_state=False):
     import torch
     from chunked_gated_delta_10_amd import kda
     from chunked_gated_delta_10_amd.inputs import WORKLOADS, workload_inputs
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    import kda_util as U
     w = WORKLOADS[name]
     inp = workload_inputs(name)
     sdt = torch.bfloat16 if bf16_state else torch.float32
-    d = U.to_device(inp, sdt)
+    d = device_inputs(inp, sdt)
     if w.decode:
         st = d["initial_state"]
         out = torch.empty((w.B, w.H, D), dtype=torch.bfloat16, device="cuda")
@@ -259,12 +298,10 @@ def run_sweep(steps, warmup):
     from chunked_gated_delta_10_amd import kda
     from chunked_gated_delta_10_amd.inputs import SWEEP_HEAD_SHAPES, SWEEP_PATTERNS, cu_seqlens_from_lengths, \
         sweep_inputs
-    sys.path.insert(0, os.path.join(ROOT, "tests"))
-    import kda_util as U
     rows = []
     for h_qk, h_v in SWEEP_HEAD_SHAPES:
         inp = sweep_inputs(h_qk, h_v)
-        d = U.to_device(inp)
+        d = device_inputs(inp, torch.float32)
         print("shape h_qk=%d h_v=%d" % (h_qk, h_v), file=sys.stderr, flush=True)
         for pname, lens in SWEEP_PATTERNS.items():
             T = sum(lens)
@@ -301,7 +338,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=100)
     ap.add_argument("--warmup", type=int, default=10)
-    ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens per row in the oracle's timed sample")
+    ap.add_argument("--cpu-tokens", type=int, default=16384, help="tokens per row in the oracle's all-thread sample")
+    ap.add_argument("--cpu-tokens-1t", type=int, default=2048, help="tokens per row in the oracle's one-thread sample")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-extra", action="store_true", help="skip the secondary workloads")
     ap.add_argument("--copy-calibration", type=int, metavar="MIB",
@@ -391,7 +429,7 @@ def main():
                             "kernels_avg_ms": {k: round(v, 4) for k, v in opk.items()}}
         result["other_workloads"] = extra
     if not args.no_cpu_baseline:
-        result["cpu_baseline"] = cpu_baseline(inp, w, min(args.cpu_tokens, w.T))
+        result["cpu_baseline"] = cpu_baseline(inp, w, min(args.cpu_tokens, w.T), min(args.cpu_tokens_1t, w.T))
     print(json.dumps(result), flush=True)
 
 

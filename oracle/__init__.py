@@ -36,7 +36,7 @@ def build(force: bool = True) -> str:
     if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
         return _LIB
     tmp = _LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O2", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-o", tmp, _SRC, "-lm"]
+    cmd = ["gcc", "-O3", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
     os.replace(tmp, _LIB)
     return _LIB
