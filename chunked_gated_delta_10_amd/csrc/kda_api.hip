@@ -10,12 +10,16 @@
 #include <cstdio>
 #include <cstdlib>
 #include <cstring>
+#include <mutex>
 #include <string>
 #include <vector>
 
 #include "kda.h"
 #include "kda_device.h"
 #include "kda_kernels.h"
+
+// Scratch of kda_fwd_noalloc (file scope, one copy per device).
+static __device__ __align__(256) uint8_t scratch[KDA_NOALLOC_SCRATCH_BYTES];
 
 namespace {
 
@@ -94,8 +98,8 @@ struct Timed {
   int id;
   hipStream_t s;
   hipEvent_t a = nullptr, b = nullptr;
-  Timed(int id_, hipStream_t s_) : id(id_), s(s_) {
-    if (!g_timing.on) return;
+  Timed(int id_, hipStream_t s_, bool allowed = true) : id(id_), s(s_) {
+    if (!g_timing.on || !allowed) return;
     a = g_timing.get();
     b = g_timing.get();
     if (a && b) (void)hipEventRecord(a, s);
@@ -138,6 +142,7 @@ struct FwdArgs {
   size_t ws_bytes;
   hipStream_t stream;
   bool delta;         // false: decay-only linear attention (beta unused)
+  bool noalloc = false;  // the allocation-free entry point: the workspace is the static scratch array
 };
 
 kda_status validate_common(const FwdArgs& a) {
@@ -154,11 +159,21 @@ kda_status validate_common(const FwdArgs& a) {
   return KDA_OK;
 }
 
-kda_status run_forward(const FwdArgs& a) {
+struct FwdPlan {
+  bool bf16_state = false;
+  int n_entries = 0;
+  Layout L{};
+};
+
+// Host-only validation of a forward call (no device access).  KDA_OK with
+// plan->n_entries < 0 means a successful no-op (no sequences).
+kda_status validate_forward(const FwdArgs& a, FwdPlan* plan = nullptr) {
+  FwdPlan local;
+  FwdPlan& P = plan ? *plan : local;
+  P.n_entries = -1;
   kda_status st = validate_common(a);
   if (st != KDA_OK) return st;
-  bool bf16_state = false;
-  st = check_state_dtypes(a.s0, a.s0_dt, a.s1, a.s1_dt, &bf16_state);
+  st = check_state_dtypes(a.s0, a.s0_dt, a.s1, a.s1_dt, &P.bf16_state);
   if (st != KDA_OK) return st;
   if (a.n_seqs == 0) return ok();
   const long tokens = (long)a.rows * a.T;
@@ -178,10 +193,28 @@ kda_status run_forward(const FwdArgs& a) {
   if ((long)n_entries * a.H >= (1L << 31))
     return fail(KDA_ERR_SHAPE, "problem too large (chunks x heads must fit in int32)");
   const Layout L = layout(a.n_seqs, n_entries, a.H);
+  if (a.noalloc && L.total > KDA_NOALLOC_SCRATCH_BYTES)
+    return fail(KDA_ERR_WORKSPACE,
+                "kda_fwd_noalloc: these sizes need %zu bytes of scratch, the static scratch array holds %zu "
+                "(at most about %d (chunk, head) pairs); call kda_fwd with a workspace instead",
+                L.total, (size_t)KDA_NOALLOC_SCRATCH_BYTES, (int)(KDA_NOALLOC_SCRATCH_BYTES / kda::REC_BYTES) - 1);
   if (!a.ws) return fail(KDA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
   if (a.ws_bytes < L.total)
     return fail(KDA_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", a.ws_bytes, L.total);
   if (reinterpret_cast<uintptr_t>(a.ws) & (ALIGN - 1)) return fail(KDA_ERR_ALIGN, "workspace is not 256-byte aligned");
+  P.n_entries = n_entries;
+  P.L = L;
+  return ok();
+}
+
+kda_status run_forward(const FwdArgs& a) {
+  FwdPlan P;
+  kda_status st = validate_forward(a, &P);
+  if (st != KDA_OK || P.n_entries < 0) return st;
+  const bool bf16_state = P.bf16_state;
+  const int n_entries = P.n_entries;
+  const Layout L = P.L;
+  const long tokens = (long)a.rows * a.T;
 
   if (a.cu && env_flag("KDA_DEBUG")) {
     std::vector<int32_t> h(a.n_seqs + 1);
@@ -205,14 +238,14 @@ kda_status run_forward(const FwdArgs& a) {
   // the kernels derive their schedule arithmetically.
   if (a.cu) {
     kda::TableParams tp{a.cu, a.n_seqs, a.T, n_entries, seqs, chunks, order};
-    Timed t(K_TABLE, a.stream);
+    Timed t(K_TABLE, a.stream, !a.noalloc);
     kda::launch_table(tp, a.stream);
   }
   if (n_entries > 0 && tokens > 0) {
     kda::ChunkParams cp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                         static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log, chunks, a.H, a.H_qk, ws + L.rec,
                         a.cu ? 0 : a.T};
-    Timed t(K_CHUNK, a.stream);
+    Timed t(K_CHUNK, a.stream, !a.noalloc);
     const hipError_t e = kda::launch_chunk_local(cp, n_entries, a.gate_per_channel == 1, a.delta, a.stream);
     if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel setup failed: %s", hipGetErrorString(e));
   }
@@ -220,7 +253,7 @@ kda_status run_forward(const FwdArgs& a) {
                       static_cast<uint16_t*>(a.out), a.s0, a.s1, a.scale,
                       reinterpret_cast<uint16_t*>(ws + L.sink), a.cu ? -1 : a.T};
   {
-    Timed t(K_RECUR, a.stream);
+    Timed t(K_RECUR, a.stream, !a.noalloc);
     kda::launch_recur(rp, bf16_state, a.gate_per_channel == 1, a.delta, a.stream);
   }
   const hipError_t e = hipGetLastError();
@@ -230,6 +263,31 @@ kda_status run_forward(const FwdArgs& a) {
                  a.n_seqs, a.T, a.H, a.H_qk, n_entries, n_entries, a.H, kda::recur_grid(a.n_seqs * a.H),
                  bf16_state ? "bf16" : "fp32");
   return ok();
+}
+
+// ---- static scratch of the allocation-free entry point ---------------------
+// One copy per device, held until the process ends.  Host code never uses
+// the array's name as an address: the per-device address comes from
+// hipGetSymbolAddress, called once per device with that device current.
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kda::MAX_DEVICES];
+
+kda_status scratch_address(void** out) {
+  int dev = 0;
+  const hipError_t e0 = hipGetDevice(&dev);
+  if (e0 != hipSuccess) return fail(KDA_ERR_HIP, "hipGetDevice failed: %s", hipGetErrorString(e0));
+  if (dev < 0 || dev >= kda::MAX_DEVICES) return fail(KDA_ERR_HIP, "device %d beyond the supported %d", dev,
+                                                      kda::MAX_DEVICES);
+  std::lock_guard<std::mutex> lock(g_scratch_mu);
+  if (!g_scratch_ptr[dev]) {
+    void* ptr = nullptr;
+    const hipError_t e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess || !ptr)
+      return fail(KDA_ERR_HIP, "hipGetSymbolAddress(scratch) failed on device %d: %s", dev, hipGetErrorString(e));
+    g_scratch_ptr[dev] = ptr;
+  }
+  *out = g_scratch_ptr[dev];
+  return KDA_OK;
 }
 
 kda_status run_decode(const void* q, const void* k, const void* v, const void* g_raw, const float* beta_logits,
@@ -287,6 +345,27 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const void* g_ra
   FwdArgs a{q, k, v, g_raw, beta_logits, A_log, scale, gate_per_channel, initial_state, init_dtype, out,
             final_state, final_dtype, nullptr, B, T, B, H_qk, H, K, V, workspace, workspace_bytes,
             static_cast<hipStream_t>(stream), true};
+  return run_forward(a);
+}
+
+kda_status kda_fwd_noalloc(const void* q, const void* k, const void* v, const void* g_raw,
+                           const float* beta_logits, const float* A_log, float scale, int gate_per_channel,
+                           const void* initial_state, kda_state_dtype init_dtype, void* out, void* final_state,
+                           kda_state_dtype final_dtype, int B, int T, int H_qk, int H, int K, int V, void* stream) {
+  FwdArgs a{q, k, v, g_raw, beta_logits, A_log, scale, gate_per_channel, initial_state, init_dtype, out,
+            final_state, final_dtype, nullptr, B, T, B, H_qk, H, K, V, nullptr, 0,
+            static_cast<hipStream_t>(stream), true, true};
+  // Validate everything that needs no device first (sizes against the scratch
+  // capacity included), then look up this device's copy of the scratch.
+  FwdArgs probe = a;
+  probe.ws = reinterpret_cast<void*>(ALIGN);  // stands in for the scratch address during validation only
+  probe.ws_bytes = KDA_NOALLOC_SCRATCH_BYTES;
+  FwdPlan plan;
+  kda_status st = validate_forward(probe, &plan);
+  if (st != KDA_OK || plan.n_entries < 0) return st;
+  st = scratch_address(&a.ws);
+  if (st != KDA_OK) return st;
+  a.ws_bytes = KDA_NOALLOC_SCRATCH_BYTES;
   return run_forward(a);
 }
 

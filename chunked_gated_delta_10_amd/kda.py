@@ -56,6 +56,8 @@ def load():
     lib.kda_fwd_workspace_bytes.argtypes = [I, I, I, I, I]
     lib.kda_fwd.restype = I
     lib.kda_fwd.argtypes = [P, P, P, P, P, P, F, I, P, I, P, P, I, I, I, I, I, I, I, P, Z, P]
+    lib.kda_fwd_noalloc.restype = I
+    lib.kda_fwd_noalloc.argtypes = [P, P, P, P, P, P, F, I, P, I, P, P, I, I, I, I, I, I, I, P]
     lib.kda_fwd_varlen.restype = I
     lib.kda_fwd_varlen.argtypes = [P, P, P, P, P, P, F, I, P, I, P, P, I, P, I, I, I, I, I, I, P, Z, P]
     lib.kda_decode_step.restype = I
@@ -229,6 +231,30 @@ def fwd(q, k, v, g_raw, beta_logits, A_log, scale: Optional[float] = None,
                        per_channel, _ptr(initial_state), _state_code(initial_state), _ptr(out),
                        _ptr(final_state), _state_code(final_state), B, T, H_qk, H, K, V, _ptr(workspace),
                        workspace.numel(), _stream(stream)))
+    return out, final_state
+
+
+# Capacity of the static scratch array behind fwd_noalloc (KDA_NOALLOC_SCRATCH_BYTES in include/kda.h).
+NOALLOC_SCRATCH_BYTES = 64 << 20
+
+
+def fwd_noalloc(q, k, v, g_raw, beta_logits, A_log, out: torch.Tensor, final_state: Optional[torch.Tensor],
+                scale: Optional[float] = None, initial_state: Optional[torch.Tensor] = None,
+                stream=None) -> Tuple[torch.Tensor, Optional[torch.Tensor]]:
+    """kda_fwd through the allocation-free entry point: the caller passes `out`
+    (and `final_state`, or None), and the library's static scratch array holds
+    the intermediates, so nothing is allocated, by torch or by the library.
+    Sizes beyond the scratch capacity raise KdaError (KDA_ERR_WORKSPACE)."""
+    lib = load()
+    B, T, H_qk, H, K, V, per_channel = _prep(q, k, v, g_raw, beta_logits, A_log)
+    scale = K ** -0.5 if scale is None else float(scale)
+    dev = q.device
+    _check_out(out, (B, T, H, V), dev)
+    _check_state(initial_state, "initial_state", (B, H, V, K), dev)
+    _check_state(final_state, "final_state", (B, H, V, K), dev)
+    _check(lib.kda_fwd_noalloc(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale,
+                               per_channel, _ptr(initial_state), _state_code(initial_state), _ptr(out),
+                               _ptr(final_state), _state_code(final_state), B, T, H_qk, H, K, V, _stream(stream)))
     return out, final_state
 
 

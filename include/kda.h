@@ -24,8 +24,12 @@
  * Conventions shared by every entry point
  * ----------------------------------------
  * - Every tensor pointer is a caller-owned DEVICE pointer to contiguous
- *   row-major memory, 16-byte aligned.  The library never allocates, frees
- *   or retains device memory, creates no streams and keeps no device state.
+ *   row-major memory, 16-byte aligned.  The entry points never allocate or
+ *   free device memory and create no streams.  Device state the library
+ *   holds: the static scratch array of kda_fwd_noalloc (one copy per device,
+ *   loaded with the library's code object and held until the process ends),
+ *   and, only while the timing diagnostics below are enabled, the HIP events
+ *   they record (created on first use per thread and reused).
  * - Work is enqueued asynchronously on `stream` (a hipStream_t; NULL = the
  *   default stream).  Nothing synchronises the host.
  * - Arguments are validated on the host before anything is enqueued; on a
@@ -93,6 +97,27 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const void* g_ra
                    void* out, void* final_state, kda_state_dtype final_dtype, int B, int T,
                    int H_qk, int H, int K, int V, void* workspace, size_t workspace_bytes,
                    void* stream);
+
+/*
+ * Allocation-free variant of kda_fwd, for callers that cannot call
+ * hipMalloc (code under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation).  Arguments are those of kda_fwd without the
+ * workspace: its intermediates go to a static device array of
+ * KDA_NOALLOC_SCRATCH_BYTES (one copy per device, whose address is looked up
+ * once per device on the first call there).  Sizes whose workspace
+ * (kda_fwd_workspace_bytes(B, T, H_qk, H, 0)) exceeds that capacity are
+ * rejected with KDA_ERR_WORKSPACE before anything is enqueued: about 1000
+ * (64-token chunk, head) pairs, e.g. B = 1, T = 4032, H = 16.  Calls on one
+ * device share its scratch: calls that overlap on one device (on different
+ * streams, or from different threads without ordering) race and give
+ * undefined results.  Nothing in the scratch needs to start at zero.
+ */
+#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)
+kda_status kda_fwd_noalloc(const void* q, const void* k, const void* v, const void* g_raw,
+                           const float* beta_logits, const float* A_log, float scale,
+                           int gate_per_channel, const void* initial_state, kda_state_dtype init_dtype,
+                           void* out, void* final_state, kda_state_dtype final_dtype, int B, int T,
+                           int H_qk, int H, int K, int V, void* stream);
 
 /*
  * Chunked forward pass over N packed sequences (the FlashKDA summary: with

@@ -121,3 +121,36 @@ def test_linear_attention_validation(lib):
     assert dec(dt=NONE) == 3
     assert dec(st=None) == 1
     assert dec(B=0) == 0
+
+
+def fwd_noalloc(lib, **over):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, alog=P, scale=0.088, pc=1, s0=None, s0dt=NONE, out=P, s1=P, s1dt=F32,
+             B=1, T=64, Hqk=2, H=2, K=128, V=128)
+    a.update(over)
+    return lib.kda_fwd_noalloc(a["q"], a["k"], a["v"], a["g"], a["beta"], a["alog"], a["scale"], a["pc"], a["s0"],
+                               a["s0dt"], a["out"], a["s1"], a["s1dt"], a["B"], a["T"], a["Hqk"], a["H"], a["K"],
+                               a["V"], None)
+
+
+def test_noalloc_scratch_capacity_matches_header():
+    with open(kda.HEADER_PATH) as f:
+        text = f.read()
+    assert "#define KDA_NOALLOC_SCRATCH_BYTES ((size_t)64 << 20)" in text
+    assert kda.NOALLOC_SCRATCH_BYTES == 64 << 20
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(K=64), 2), (dict(H=3), 2), (dict(q=None), 1), (dict(out=P + 8), 6), (dict(s1dt=7), 3),
+    (dict(B=1, T=64 * 1100, Hqk=1, H=1), 5),    # 1100 (chunk, head) records exceed the scratch
+    (dict(B=4, T=4096, Hqk=16, H=16), 5),
+])
+def test_noalloc_validation(lib, over, code):
+    # rejected on the host, before the scratch address is looked up or anything is enqueued
+    st = fwd_noalloc(lib, **over)
+    assert st == code, (st, lib.kda_last_error())
+    if code == 5:
+        assert b"static scratch" in lib.kda_last_error()
+
+
+def test_noalloc_zero_batch_is_a_no_op(lib):
+    assert fwd_noalloc(lib, B=0) == 0

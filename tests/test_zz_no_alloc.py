@@ -1,0 +1,57 @@
+"""The allocation-free entry point (kda_fwd_noalloc) against kda_fwd, through
+the C ABI, on two calls in a row: the second one smaller, so it runs on a
+scratch array that still holds the first call's intermediates."""
+
+import numpy as np
+import pytest
+import torch
+
+from chunked_gated_delta_10_amd import kda
+from chunked_gated_delta_10_amd.inputs import make_inputs
+import kda_util as U
+
+pytestmark = pytest.mark.gpu
+
+
+def run_both(inp):
+    d = U.to_device(inp)
+    B, T = inp["q"].shape[:2]
+    H = inp["v"].shape[2]
+    ref_out, ref_fin = kda.fwd(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], scale=inp["scale"],
+                               initial_state=d["initial_state"])
+    out = torch.empty((B, T, H, 128), dtype=torch.bfloat16, device="cuda")
+    fin = torch.empty((B, H, 128, 128), dtype=torch.float32, device="cuda")
+    torch.cuda.synchronize()
+    before = torch.cuda.memory_allocated()
+    kda.fwd_noalloc(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], out, fin, scale=inp["scale"],
+                    initial_state=d["initial_state"])
+    torch.cuda.synchronize()
+    assert torch.cuda.memory_allocated() == before
+    return (out.float().cpu().numpy().astype(np.float64), fin.cpu().numpy().astype(np.float64),
+            ref_out.float().cpu().numpy().astype(np.float64), ref_fin.cpu().numpy().astype(np.float64))
+
+
+def test_noalloc_matches_kda_fwd_on_two_calls_second_smaller():
+    cases = [make_inputs(2, 1000, 4, 2, state_std=0.02, seed=60, A_log=(-3.0, 0.0)),
+             make_inputs(1, 300, 2, 2, state_std=0.05, seed=61)]
+    for i, inp in enumerate(cases):
+        print("case: noalloc call %d, shape %s" % (i, inp["v"].shape), flush=True)
+        out, fin, ref_out, ref_fin = run_both(inp)
+        # the same kernels on the same inputs: identical to kda_fwd
+        np.testing.assert_array_equal(out, ref_out)
+        np.testing.assert_array_equal(fin, ref_fin)
+        o_or, f_or = U.run_oracle(inp)
+        U.assert_parity(out, fin, o_or, f_or, what="noalloc call %d" % i)
+
+
+def test_noalloc_rejects_sizes_beyond_the_scratch():
+    inp = make_inputs(1, 64, 1, 1, seed=62)
+    d = U.to_device(inp)
+    big_T = 64 * 1100
+    q = torch.zeros((1, big_T, 1, 128), dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros((1, big_T, 1, 128), dtype=torch.bfloat16, device="cuda")
+    b = torch.zeros((1, big_T, 1), dtype=torch.float32, device="cuda")
+    out = torch.empty((1, big_T, 1, 128), dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(kda.KdaError) as e:
+        kda.fwd_noalloc(q, q, q, g, b, d["A_log"], out, None)
+    assert e.value.status == 5 and "static scratch" in e.value.detail
