@@ -28,7 +28,8 @@ MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix throughput, publi
 D, C = 128, 64                 # head dim, chunk length
 FLOP_PER_TOKEN_HEAD = 6 * D * D + 5 * C * D   # 139,264 (algorithmic, per token and head)
 KERNEL_SOURCES = ["chunked_gated_delta_10_amd/csrc/" + f for f in
-                  ("kda_chunk.hip", "kda_recur.hip", "kda_table.hip", "kda_decode.hip", "kda_device.h", "kda_kernels.h")]
+                  ("kda_chunk.hip", "kda_chunk_job.h", "kda_fused.hip", "kda_recur.hip", "kda_table.hip",
+                   "kda_decode.hip", "kda_device.h", "kda_kernels.h")]
 
 
 def algorithmic_bytes(w, with_state=True, state_bytes=4):
@@ -43,7 +44,10 @@ def algorithmic_bytes(w, with_state=True, state_bytes=4):
     state = C_ * w.H * D * D * state_bytes
     s_in = state if w.state_std is not None else 0
     s_out = state if with_state else 0
-    return {"kda_chunk_local": qk + g + beta + w.H * 4, "kda_recur": v + out + s_in + s_out}
+    local = qk + g + beta + w.H * 4
+    chain = v + out + s_in + s_out
+    # the fused kernel does both parts in one launch
+    return {"kda_chunk_local": local, "kda_recur": chain, "kda_fused": local + chain}
 
 
 def sources_hash():
@@ -139,7 +143,7 @@ def traffic_from(root, copy_bytes, workload="kda_dense"):
                             "fetch_factor": kf, "write_factor": kw}}
     rec = {}
     for kern, tag in (("kda_chunk_local", "chunk_local_kernel"), ("kda_recur", "recur_"),
-                      ("kda_table", "table_kernel")):
+                      ("kda_table", "table_kernel"), ("kda_fused", "fused_kernel")):
         f = _per_dispatch_kib(run_f, "FETCH_SIZE", lambda k, t=tag: t in k)
         w = _per_dispatch_kib(run_w, "WRITE_SIZE", lambda k, t=tag: t in k)
         if f is None or w is None:
@@ -385,7 +389,7 @@ def main():
     tokens = w.B * w.T
     value = tokens / (ms / 1000.0)
     alg = algorithmic_bytes(w)
-    alg_total = sum(alg.values())
+    alg_total = alg["kda_fused"]
     flops = FLOP_PER_TOKEN_HEAD * tokens * w.H
     kernels = {}
     for k, avg in per_kernel.items():
@@ -422,7 +426,7 @@ def main():
                                                bf16_state=bf16_state)
             ab = algorithmic_bytes(ow, state_bytes=2 if bf16_state else 4)
             tok = ow.B if ow.decode else ow.B * ow.T
-            tot = sum(ab.values())
+            tot = ab["kda_fused"]
             extra[other] = {"ms_per_step": round(oms, 4), "tokens_per_s": round(tok / (oms * 1e-3), 1),
                             "algorithmic_bytes": tot,
                             "hbm_frac": round(tot / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),

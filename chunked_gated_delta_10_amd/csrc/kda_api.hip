@@ -9,6 +9,7 @@
 #include <cstdarg>
 #include <cstdio>
 #include <cstdlib>
+#include <algorithm>
 #include <cstring>
 #include <mutex>
 #include <string>
@@ -51,29 +52,49 @@ constexpr size_t ALIGN = 256;
 size_t round_up(size_t x) { return (x + ALIGN - 1) / ALIGN * ALIGN; }
 
 struct Layout {
-  size_t rec, seqs, chunks, order, sink, total;
-  int n_entries;
+  size_t seqs, chunks, order, sink, rec, flags, total;
+  bool fused;
+  kda::FusedLayout F;
 };
 
-// Workspace: chunk records, then the schedule (sequence table, chunk table,
-// order) and a small sink for output rows past a chunk's end.
-Layout layout(int n_seqs, int n_entries, int H) {
+int cdiv(long a, long b);
+
+// Workspace: a 256-byte header (word 0: the error bits of the last forward
+// call), the schedule (sequence table, chunk table, order), a small sink for
+// output rows past a chunk's end, then either the chunk records of every
+// (chunk, head) (two-kernel path) or the fused kernel's record rings and
+// flags.
+Layout layout(int n_seqs, int n_entries, int H, bool fused) {
   Layout L;
-  L.n_entries = n_entries;
-  L.rec = 0;
-  L.seqs = round_up((size_t)n_entries * H * kda::REC_BYTES);
+  L.fused = fused;
+  L.seqs = ALIGN;
   L.chunks = L.seqs + round_up((size_t)n_seqs * sizeof(int4));
   L.order = L.chunks + round_up((size_t)n_entries * sizeof(int4));
   L.sink = L.order + round_up((size_t)n_seqs * sizeof(int));
-  L.total = L.sink + round_up(64 * sizeof(uint16_t));
+  L.rec = L.sink + round_up(64 * sizeof(uint16_t));
+  if (fused) {
+    L.F = kda::fused_layout(n_seqs * H);
+    L.flags = L.rec + round_up(L.F.ring_bytes);
+    L.total = L.flags + round_up((size_t)L.F.n_flags * sizeof(int));
+  } else {
+    L.flags = 0;
+    L.total = L.rec + round_up((size_t)n_entries * H * kda::REC_BYTES);
+  }
   return L;
 }
 
 int cdiv(long a, long b) { return (int)((a + b - 1) / b); }
 
+// KDA_PRECISE=1 selects the fused persistent kernel for the per-channel
+// delta-rule forward (split-precision state path; see include/kda.h) when
+// the device supports it; otherwise the two-kernel path runs.
+bool takes_fused(bool delta, int gate_per_channel) {
+  return delta && gate_per_channel == 1 && env_flag("KDA_PRECISE") && kda::fused_available();
+}
+
 // ---- per-kernel event timing (diagnostics) --------------------------------
-enum { K_TABLE = 0, K_CHUNK = 1, K_RECUR = 2, K_DECODE = 3, K_COUNT = 4 };
-const char* const kKernelNames[K_COUNT] = {"kda_table", "kda_chunk_local", "kda_recur", "kda_decode"};
+enum { K_TABLE = 0, K_CHUNK = 1, K_RECUR = 2, K_DECODE = 3, K_FUSED = 4, K_COUNT = 5 };
+const char* const kKernelNames[K_COUNT] = {"kda_table", "kda_chunk_local", "kda_recur", "kda_decode", "kda_fused"};
 
 struct Timing {
   bool on = false;
@@ -192,11 +213,11 @@ kda_status validate_forward(const FwdArgs& a, FwdPlan* plan = nullptr) {
   const int n_entries = a.cu ? cdiv(a.T, kda::CH) + a.n_seqs : a.n_seqs * cdiv(a.T, kda::CH);
   if ((long)n_entries * a.H >= (1L << 31))
     return fail(KDA_ERR_SHAPE, "problem too large (chunks x heads must fit in int32)");
-  const Layout L = layout(a.n_seqs, n_entries, a.H);
+  const Layout L = layout(a.n_seqs, n_entries, a.H, takes_fused(a.delta, a.gate_per_channel));
   if (a.noalloc && L.total > KDA_NOALLOC_SCRATCH_BYTES)
     return fail(KDA_ERR_WORKSPACE,
                 "kda_fwd_noalloc: these sizes need %zu bytes of scratch, the static scratch array holds %zu "
-                "(at most about %d (chunk, head) pairs); call kda_fwd with a workspace instead",
+                "(the two-kernel path keeps about %d (chunk, head) records); call kda_fwd with a workspace instead",
                 L.total, (size_t)KDA_NOALLOC_SCRATCH_BYTES, (int)(KDA_NOALLOC_SCRATCH_BYTES / kda::REC_BYTES) - 1);
   if (!a.ws) return fail(KDA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
   if (a.ws_bytes < L.total)
@@ -241,27 +262,36 @@ kda_status run_forward(const FwdArgs& a) {
     Timed t(K_TABLE, a.stream, !a.noalloc);
     kda::launch_table(tp, a.stream);
   }
-  if (n_entries > 0 && tokens > 0) {
-    kda::ChunkParams cp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                        static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log, chunks, a.H, a.H_qk, ws + L.rec,
-                        a.cu ? 0 : a.T};
-    Timed t(K_CHUNK, a.stream, !a.noalloc);
-    const hipError_t e = kda::launch_chunk_local(cp, n_entries, a.gate_per_channel == 1, a.delta, a.stream);
-    if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel setup failed: %s", hipGetErrorString(e));
-  }
-  kda::RecurParams rp{ws + L.rec, seqs, order, a.n_seqs * a.H, n_entries, a.H, a.H_qk, static_cast<const uint16_t*>(a.v),
-                      static_cast<uint16_t*>(a.out), a.s0, a.s1, a.scale,
-                      reinterpret_cast<uint16_t*>(ws + L.sink), a.cu ? -1 : a.T};
-  {
+  const kda::ChunkParams cp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                            static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log, chunks, a.H, a.H_qk,
+                            L.fused ? nullptr : ws + L.rec, a.cu ? 0 : a.T, static_cast<const uint16_t*>(a.v)};
+  int* err = reinterpret_cast<int*>(ws);
+  uint16_t* sink = reinterpret_cast<uint16_t*>(ws + L.sink);
+  if (L.fused) {
+    int* flags = reinterpret_cast<int*>(ws + L.flags);
+    const kda::FusedParams fp{cp, static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.s0, a.s1,
+                              a.scale, seqs, order, a.cu ? -1 : a.T, a.n_seqs * a.H, L.F.n_teams, L.F.tpx, L.F.R, L.F.P,
+                              ws + L.rec, flags, flags + (size_t)L.F.n_teams * L.F.R * 32, L.F.n_flags, err, sink};
+    Timed t(K_FUSED, a.stream, !a.noalloc);
+    const hipError_t e = kda::launch_fused(fp, L.F.grid, bf16_state, a.stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "fused kernel launch failed: %s", hipGetErrorString(e));
+  } else {
+    if (n_entries > 0 && tokens > 0) {
+      Timed t(K_CHUNK, a.stream, !a.noalloc);
+      const hipError_t e = kda::launch_chunk_local(cp, n_entries, a.gate_per_channel == 1, a.delta, a.stream);
+      if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel setup failed: %s", hipGetErrorString(e));
+    }
+    kda::RecurParams rp{ws + L.rec, seqs, order, a.n_seqs * a.H, n_entries, a.H, a.H_qk,
+                        static_cast<const uint16_t*>(a.v), static_cast<uint16_t*>(a.out), a.s0, a.s1, a.scale, sink,
+                        a.cu ? -1 : a.T, err};
     Timed t(K_RECUR, a.stream, !a.noalloc);
     kda::launch_recur(rp, bf16_state, a.gate_per_channel == 1, a.delta, a.stream);
   }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   if (env_flag("KDA_LOG"))
-    std::fprintf(stderr, "[kda] fwd seqs=%d T=%d H=%d H_qk=%d entries=%d chunk-grid=%dx%d recur-grid=%d state=%s\n",
-                 a.n_seqs, a.T, a.H, a.H_qk, n_entries, n_entries, a.H, kda::recur_grid(a.n_seqs * a.H),
-                 bf16_state ? "bf16" : "fp32");
+    std::fprintf(stderr, "[kda] fwd seqs=%d T=%d H=%d H_qk=%d entries=%d path=%s state=%s\n", a.n_seqs, a.T, a.H,
+                 a.H_qk, n_entries, L.fused ? "fused" : "split", bf16_state ? "bf16" : "fp32");
   return ok();
 }
 
@@ -335,7 +365,8 @@ size_t kda_fwd_workspace_bytes(int B, int T, int H_qk, int H, int N) {
   if (N > 0 && B != 1) return 0;
   const int n_seqs = N > 0 ? N : B;
   const int n_entries = N > 0 ? cdiv(T, kda::CH) + N : B * cdiv(T, kda::CH);
-  return layout(n_seqs, n_entries, H).total;
+  const size_t split = layout(n_seqs, n_entries, H, false).total;
+  return kda::fused_available() ? std::max(split, layout(n_seqs, n_entries, H, true).total) : split;
 }
 
 kda_status kda_fwd(const void* q, const void* k, const void* v, const void* g_raw, const float* beta_logits,
@@ -416,6 +447,26 @@ kda_status kda_la_decode_step(const void* q, const void* k, const void* v, const
                               int B, int H_qk, int H, int K, int V, void* stream) {
   return run_decode(q, k, v, g_raw, nullptr, A_log, scale, gate_per_channel, state, state_dtype, out, B, H_qk, H, K,
                     V, static_cast<hipStream_t>(stream), false);
+}
+
+kda_status kda_fwd_check(const void* workspace, void* stream) {
+  const void* word = workspace;
+  if (!word) {
+    void* scratch_ptr = nullptr;
+    const kda_status st = scratch_address(&scratch_ptr);
+    if (st != KDA_OK) return st;
+    word = scratch_ptr;
+  }
+  int bits = 0;
+  hipStream_t s = static_cast<hipStream_t>(stream);
+  if (hipStreamSynchronize(s) != hipSuccess ||
+      hipMemcpy(&bits, word, sizeof(int), hipMemcpyDeviceToHost) != hipSuccess)
+    return fail(KDA_ERR_HIP, "kda_fwd_check: %s", hipGetErrorString(hipGetLastError()));
+  if (bits == 0) return ok();
+  return fail(KDA_ERR_HIP, "the last forward call on this workspace reported error bits 0x%x (%s%s%s)", bits,
+              (bits & 1) ? "a workgroup ran on an unexpected XCD; " : "",
+              (bits & 2) ? "a consumer's bounded wait for a record timed out; " : "",
+              (bits & 4) ? "a producer's bounded wait for a free ring slot timed out" : "");
 }
 
 const char* kda_status_string(kda_status s) {

@@ -57,6 +57,14 @@ constexpr int REC_M = REC_KBAR + 16 * FRAG_BYTES;     // 8 fragments (t, s) = t*
 constexpr int REC_TB = REC_M + 8 * FRAG_BYTES;        // 8 fragments
 constexpr int REC_GL = REC_TB + 8 * FRAG_BYTES;       // 128 floats
 constexpr int REC_BYTES = REC_GL + HD * 4;            // 66048
+// Records of the fused kernel add the low parts (x - fp16(x)) of Kbar^T and
+// T diag(b), in the same fragment order, and a copy of the chunk's value
+// rows (bf16 [64][128], rows past the chunk's end undefined), so that the
+// consumers read nothing but records.
+constexpr int REC_KBAR_LO = REC_BYTES;                   // 16 fragments
+constexpr int REC_TB_LO = REC_KBAR_LO + 16 * FRAG_BYTES;  // 8 fragments
+constexpr int REC_V = REC_TB_LO + 8 * FRAG_BYTES;         // 64 rows x 256 bytes
+constexpr int REC2_BYTES = REC_V + CH * HD * 2;           // 107008
 
 // Chunk schedule entry (int4): x = sequence, y = first token (flattened
 // token index), z = valid tokens (0 = unused entry), w = chunk index within

@@ -44,6 +44,7 @@ struct ChunkParams {
   int H, H_qk;
   uint8_t* rec;           // [entries][H] chunk records
   int dense_T;            // > 0: B rows of dense_T tokens, schedule by arithmetic; 0: read `chunks`
+  const uint16_t* v;      // bf16 [tokens, H, 128]: copied into the fused kernel's records (else unused)
 };
 
 // Recurrence kernel (kda_recur.hip): one workgroup per (chain, value tile).
@@ -61,7 +62,40 @@ struct RecurParams {
   float scale;
   uint16_t* sink;         // 64 scratch values: destination of output rows past a chunk's end
   int dense_T;            // >= 0: B rows of dense_T tokens, schedule by arithmetic; -1: read `seqs`/`order`
+  int* err;               // error word of the workspace header: cleared (this path reports no errors)
 };
+
+// Fused persistent forward (kda_fused.hip): per-channel gate, delta rule.
+struct FusedParams {
+  ChunkParams cp;         // producer inputs: q, k, g_raw, beta, A_log, H, H_qk (rec, chunks unused)
+  const uint16_t* v;      // bf16 [tokens, H, 128]
+  uint16_t* out;          // bf16 [tokens, H, 128]
+  const void* s0;         // [seqs, H, 128, 128] fp32 or bf16, or null
+  void* s1;               // same layout, or null
+  float scale;
+  const int4* seqs;       // packed sequences: first token, length (dense_T < 0)
+  const int* order;       // packed sequences in processing order (longest first)
+  int dense_T;            // >= 0: B rows of dense_T tokens
+  int n_chains;           // sequences * H
+  int n_teams, tpx, R, P;  // teams (8 * tpx), teams per XCD, ring slots and producers per team
+  uint8_t* ring;          // [n_teams][R] records of REC2_BYTES
+  int* ready;             // [n_teams][R] ready flags, then prog [n_teams][NCW]; one per 128 bytes
+  int* prog;
+  int n_flags_total;      // ints covered by ready and prog
+  int* err;               // error bits of the launch (0 = fine)
+  uint16_t* sink;         // 64 scratch values for output rows past a chunk's end
+};
+struct FusedLayout {
+  int grid, tpx, R, P, n_teams, n_flags;
+  size_t ring_bytes;
+};
+// Team layout and ring size for n_chains chains on the current device.
+FusedLayout fused_layout(int n_chains);
+// Cooperative launches, two fused workgroups per CU and a CU count divisible
+// by 8 on the current device (checked once per device).
+bool fused_available();
+// Clears the flags and the error word, then launches the cooperative kernel.
+hipError_t launch_fused(const FusedParams& p, int grid, bool bf16_state, hipStream_t stream);
 
 // Decode kernel (kda_decode.hip): one workgroup per (batch row, head).
 struct DecodeParams {

@@ -141,6 +141,7 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
   const int l16 = lane & 15, lg = lane >> 4;
   const int tw = wave & 3;
   const int x = blockIdx.x, xcd = x & 7, y = x >> 3;
+  if (x == 0 && tid == 0 && p.err) *p.err = 0;
   const int G = PC ? 1 : p.H / p.H_qk;  // value heads per q/k head
   const int vt = y % NW, ch = (y / NW) * 8 + xcd;
   if (ch >= p.n_chains) return;

@@ -68,6 +68,8 @@ def load():
     lib.kda_la_fwd_varlen.argtypes = [P, P, P, P, P, F, I, P, I, P, P, I, P, I, I, I, I, I, I, P, Z, P]
     lib.kda_la_decode_step.restype = I
     lib.kda_la_decode_step.argtypes = [P, P, P, P, P, F, I, P, I, P, I, I, I, I, I, P]
+    lib.kda_fwd_check.restype = I
+    lib.kda_fwd_check.argtypes = [P, P]
     lib.kda_status_string.restype = ctypes.c_char_p
     lib.kda_status_string.argtypes = [I]
     lib.kda_last_error.restype = ctypes.c_char_p
@@ -171,6 +173,12 @@ def kernel_timing_read() -> dict:
     if k < 0:
         raise RuntimeError("kda_kernel_timing_read failed")
     return {lib.kda_kernel_name(i).decode(): (ms[i], cnt[i]) for i in range(k) if cnt[i] > 0}
+
+
+def check(workspace: Optional[torch.Tensor] = None, stream=None) -> None:
+    """Waits for the stream and raises KdaError if the last forward call on
+    `workspace` (None: the allocation-free scratch) recorded an internal error."""
+    _check(load().kda_fwd_check(_ptr(workspace), _stream(stream)))
 
 
 def workspace_bytes(B: int, T: int, H_qk: int, H: int, N: int = 0) -> int:

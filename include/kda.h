@@ -51,6 +51,14 @@
  *   initial_state = NULL means a zero state; final_state = NULL means the
  *   final state is not written.  initial_state may equal final_state (the
  *   state is read before it is overwritten).
+ * - Precise mode: with the environment variable KDA_PRECISE=1 the
+ *   per-channel delta-rule forward (kda_fwd, kda_fwd_varlen, kda_fwd_noalloc
+ *   with gate_per_channel = 1) runs as one persistent cooperative kernel
+ *   that adds low parts (x - fp16(x)) to the fp16 operands of the state
+ *   update: about 2-3x lower final-state error when keys within a chunk are
+ *   nearly parallel with strong writes and little decay, at about 1.5x the
+ *   time.  Check its launches with kda_fwd_check.  Other calls, and devices
+ *   without cooperative launch, take the default two-kernel path.
  */
 #ifndef KDA_H
 #define KDA_H
@@ -107,7 +115,8 @@ kda_status kda_fwd(const void* q, const void* k, const void* v, const void* g_ra
  * once per device on the first call there).  Sizes whose workspace
  * (kda_fwd_workspace_bytes(B, T, H_qk, H, 0)) exceeds that capacity are
  * rejected with KDA_ERR_WORKSPACE before anything is enqueued: about 1000
- * (64-token chunk, head) pairs, e.g. B = 1, T = 4032, H = 16.  Calls on one
+ * (64-token chunk, head) pairs, e.g. B = 1, T = 4032, H = 16, on the default
+ * path; the precise mode's records live in fixed rings that fit for any T.  Calls on one
  * device share its scratch: calls that overlap on one device (on different
  * streams, or from different threads without ordering) race and give
  * undefined results.  Nothing in the scratch needs to start at zero.
@@ -189,11 +198,23 @@ kda_status kda_la_decode_step(const void* q, const void* k, const void* v, const
  * milliseconds and launch count per kernel id into the caller's arrays
  * (up to max_kernels entries), forgets them, and returns the number of
  * kernel ids (or -1 on a HIP error).  Kernel ids: 0 schedule, 1 chunk-local,
- * 2 recurrence, 3 decode.  The events are created by the library and reused.
+ * 2 recurrence, 3 decode, 4 fused forward.  The events are created by the
+ * library and reused.
  */
 void kda_kernel_timing_enable(int enable);
 int kda_kernel_timing_read(double* total_ms, int* launches, int max_kernels);
 const char* kda_kernel_name(int id);
+
+/*
+ * Waits for `stream`, then reports whether the last forward call on
+ * `workspace` (NULL: the current device's kda_fwd_noalloc scratch) met an
+ * internal error: for the per-channel delta-rule forward, which runs as one
+ * persistent kernel whose workgroups exchange chunk records through the L2
+ * of their XCD, a bounded wait that timed out or a workgroup on an
+ * unexpected XCD.  The results of such a call are invalid.  Returns KDA_OK
+ * when no error was recorded, KDA_ERR_HIP (with a description) otherwise.
+ */
+kda_status kda_fwd_check(const void* workspace, void* stream);
 
 /* Static, human-readable name of a status code. */
 const char* kda_status_string(kda_status status);

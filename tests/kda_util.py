@@ -37,12 +37,19 @@ def to_device(inp: dict, state_dtype=torch.float32, device="cuda") -> dict:
 
 def run_gpu(inp: dict, state_dtype=torch.float32, **kw):
     d = to_device(inp, state_dtype)
+    B, T, H_qk = inp["q"].shape[:3]
+    H = inp["v"].shape[2]
+    cu = inp.get("cu_seqlens")
+    N = 0 if cu is None else len(cu) - 1
+    ws = torch.empty(max(kda.workspace_bytes(B, T, H_qk, H, N), 256), dtype=torch.uint8, device="cuda")
     if d["cu_seqlens"] is not None:
         out, fin = kda.fwd_varlen(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], d["cu_seqlens"],
-                                  scale=inp["scale"], initial_state=d["initial_state"], state_dtype=state_dtype, **kw)
+                                  scale=inp["scale"], initial_state=d["initial_state"], state_dtype=state_dtype,
+                                  workspace=ws, **kw)
     else:
         out, fin = kda.fwd(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], scale=inp["scale"],
-                           initial_state=d["initial_state"], state_dtype=state_dtype, **kw)
+                           initial_state=d["initial_state"], state_dtype=state_dtype, workspace=ws, **kw)
+    kda.check(ws)  # no internal error (timed-out wait, unexpected placement) in the launch
     torch.cuda.synchronize()
     return out.float().cpu().numpy().astype(np.float64), fin.float().cpu().numpy().astype(np.float64)
 

@@ -141,8 +141,10 @@ def test_noalloc_scratch_capacity_matches_header():
 
 @pytest.mark.parametrize("over,code", [
     (dict(K=64), 2), (dict(H=3), 2), (dict(q=None), 1), (dict(out=P + 8), 6), (dict(s1dt=7), 3),
-    (dict(B=1, T=64 * 1100, Hqk=1, H=1), 5),    # 1100 (chunk, head) records exceed the scratch
-    (dict(B=4, T=4096, Hqk=16, H=16), 5),
+    # scalar gate (two-kernel path, records of every (chunk, head)): 1100 and
+    # 4096 records exceed the scratch; rejected before any device work
+    (dict(B=1, T=64 * 1100, Hqk=1, H=1, pc=0), 5),
+    (dict(B=4, T=4096, Hqk=16, H=16, pc=0), 5),
 ])
 def test_noalloc_validation(lib, over, code):
     # rejected on the host, before the scratch address is looked up or anything is enqueued

@@ -25,6 +25,7 @@ def run_both(inp):
     before = torch.cuda.memory_allocated()
     kda.fwd_noalloc(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], out, fin, scale=inp["scale"],
                     initial_state=d["initial_state"])
+    kda.check(None)  # the scratch's error word: no internal error in the launch
     torch.cuda.synchronize()
     assert torch.cuda.memory_allocated() == before
     return (out.float().cpu().numpy().astype(np.float64), fin.cpu().numpy().astype(np.float64),
@@ -49,7 +50,7 @@ def test_noalloc_rejects_sizes_beyond_the_scratch():
     d = U.to_device(inp)
     big_T = 64 * 1100
     q = torch.zeros((1, big_T, 1, 128), dtype=torch.bfloat16, device="cuda")
-    g = torch.zeros((1, big_T, 1, 128), dtype=torch.bfloat16, device="cuda")
+    g = torch.zeros((1, big_T, 1), dtype=torch.bfloat16, device="cuda")  # scalar gate: two-kernel path
     b = torch.zeros((1, big_T, 1), dtype=torch.float32, device="cuda")
     out = torch.empty((1, big_T, 1, 128), dtype=torch.bfloat16, device="cuda")
     with pytest.raises(kda.KdaError) as e:
