@@ -18,7 +18,8 @@ from typing import Optional, Tuple
 import torch
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
-LIB_PATH = os.path.join(_HERE, "libkda.so")
+# KDA_LIB names another build of the same library (e.g. a host-sanitizer build for the CPU tests)
+LIB_PATH = os.environ.get("KDA_LIB") or os.path.join(_HERE, "libkda.so")
 HEADER_PATH = os.path.join(os.path.dirname(_HERE), "include", "kda.h")
 
 KDA_STATE_NONE, KDA_STATE_BF16, KDA_STATE_FP32 = 0, 1, 2

@@ -82,7 +82,16 @@ typedef enum {
   KDA_ERR_HIP = 7                    /* the HIP runtime reported an error */
 } kda_status;
 
-typedef enum { KDA_STATE_NONE = 0, KDA_STATE_BF16 = 1, KDA_STATE_FP32 = 2 } kda_state_dtype;
+/* The two range markers widen the enum to every int value, so a dtype outside
+ * the three named ones, passed from C, is still a value of the type (and is
+ * rejected with KDA_ERR_DTYPE) rather than undefined behaviour in C++. */
+typedef enum {
+  KDA_STATE_NONE = 0,
+  KDA_STATE_BF16 = 1,
+  KDA_STATE_FP32 = 2,
+  KDA_STATE_RANGE_MIN_ = -2147483647 - 1,
+  KDA_STATE_RANGE_MAX_ = 2147483647
+} kda_state_dtype;
 
 /*
  * Bytes of device workspace kda_fwd (N = 0) or kda_fwd_varlen (N > 0

@@ -31,23 +31,34 @@ _LIB = os.path.join(_HERE, "libkda_oracle.so")
 _lib = None
 
 
-def build(force: bool = True) -> str:
-    """Compile kda_oracle.c into libkda_oracle.so next to it (gcc, OpenMP)."""
-    if not force and os.path.exists(_LIB) and os.path.getmtime(_LIB) >= os.path.getmtime(_SRC):
-        return _LIB
-    tmp = _LIB + ".tmp%d" % os.getpid()
-    cmd = ["gcc", "-O3", "-fopenmp", "-shared", "-fPIC", "-std=c99", "-o", tmp, _SRC, "-lm"]
+SANITIZE_FLAGS = ["-O1", "-g", "-fno-omit-frame-pointer", "-fsanitize=address,undefined",
+                  "-fno-sanitize-recover=undefined"]
+
+
+def build(force: bool = True, sanitize: bool = False, out: Optional[str] = None) -> str:
+    """Compile kda_oracle.c into libkda_oracle.so next to it (gcc, OpenMP).
+
+    sanitize=True builds an AddressSanitizer + UndefinedBehaviorSanitizer
+    copy instead (to ``out``); loading it needs gcc's libasan preloaded."""
+    lib = out or _LIB
+    if not force and os.path.exists(lib) and os.path.getmtime(lib) >= os.path.getmtime(_SRC):
+        return lib
+    tmp = lib + ".tmp%d" % os.getpid()
+    opt = SANITIZE_FLAGS if sanitize else ["-O3"]
+    cmd = ["gcc"] + opt + ["-fopenmp", "-shared", "-fPIC", "-std=c99", "-o", tmp, _SRC, "-lm"]
     subprocess.run(cmd, check=True)
-    os.replace(tmp, _LIB)
-    return _LIB
+    os.replace(tmp, lib)
+    return lib
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    build(force=False)
-    lib = ctypes.CDLL(_LIB)
+    path = os.environ.get("KDA_ORACLE_LIB")  # another build of kda_oracle.c (e.g. a sanitizer build)
+    if not path:
+        path = build(force=False)
+    lib = ctypes.CDLL(path)
     d = ctypes.POINTER(ctypes.c_double)
     lib.kda_oracle_fwd.restype = ctypes.c_int
     lib.kda_oracle_fwd.argtypes = [d, d, d, d, d, d, ctypes.c_double, ctypes.c_int, d, d, d,
