@@ -125,34 +125,42 @@ def _per_dispatch_kib(rows, counter, match):
 
 
 def traffic_from(root, copy_bytes, workload="kda_dense"):
-    """Turn four rocprofv3 --pmc runs into profiles/traffic.json.
+    """Turn four rocprofv3 --pmc runs into the `workload` entry of profiles/traffic.json
+    (other workloads' entries are kept).
 
     Expects under `root`: pmc_fetch/ and pmc_write/ (FETCH_SIZE, WRITE_SIZE of
-    the bench run) and cal_fetch/, cal_write/ (the same counters over
-    --copy-calibration).  Each counter is scaled by ideal/measured of the copy
-    (a copy of N bytes fetches N and writes N bytes)."""
+    the bench run; pmc_fetch_<workload>/ and pmc_write_<workload>/ for a
+    workload other than kda_dense) and cal_fetch/, cal_write/ (the same
+    counters over --copy-calibration).  Each counter is scaled by
+    ideal/measured of the copy (a copy of N bytes fetches N and writes N
+    bytes)."""
     cal_f = _counter_rows(os.path.join(root, "cal_fetch"))
     cal_w = _counter_rows(os.path.join(root, "cal_write"))
     copy_f = max(v for _, c, v in cal_f if c == "FETCH_SIZE")
     copy_w = max(v for _, c, v in cal_w if c == "WRITE_SIZE")
     kf = copy_bytes / (copy_f * 1024.0)
     kw = copy_bytes / (copy_w * 1024.0)
-    run_f = _counter_rows(os.path.join(root, "pmc_fetch"))
-    run_w = _counter_rows(os.path.join(root, "pmc_write"))
-    out = {"_calibration": {"copy_bytes": copy_bytes, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
-                            "fetch_factor": kf, "write_factor": kw}}
+    sfx = "" if workload == "kda_dense" else "_" + workload
+    run_f = _counter_rows(os.path.join(root, "pmc_fetch" + sfx))
+    run_w = _counter_rows(os.path.join(root, "pmc_write" + sfx))
+    path = os.path.join(ROOT, "profiles", "traffic.json")
+    out = {}
+    if os.path.exists(path):
+        with open(path) as fh:
+            out = json.load(fh)
+    out["_calibration"] = {"copy_bytes": copy_bytes, "copy_fetch_kib": copy_f, "copy_write_kib": copy_w,
+                           "fetch_factor": kf, "write_factor": kw}
     rec = {}
-    for kern, tag in (("kda_chunk_local", "chunk_local_kernel"), ("kda_recur", "recur_"),
-                      ("kda_table", "table_kernel"), ("kda_fused", "fused_kernel")):
-        f = _per_dispatch_kib(run_f, "FETCH_SIZE", lambda k, t=tag: t in k)
-        w = _per_dispatch_kib(run_w, "WRITE_SIZE", lambda k, t=tag: t in k)
+    for kern, tags in (("kda_chunk_local", ("chunk_local_kernel", "chunk_group_kernel")), ("kda_recur", ("recur_",)),
+                       ("kda_table", ("table_kernel",)), ("kda_fused", ("fused_kernel",))):
+        f = _per_dispatch_kib(run_f, "FETCH_SIZE", lambda k, t=tags: any(x in k for x in t))
+        w = _per_dispatch_kib(run_w, "WRITE_SIZE", lambda k, t=tags: any(x in k for x in t))
         if f is None or w is None:
             continue
         rec[kern] = {"fetch_kib": f, "write_kib": w, "hbm_read_bytes": f * 1024 * kf,
                      "hbm_write_bytes": w * 1024 * kw, "hbm_bytes_per_launch": f * 1024 * kf + w * 1024 * kw,
                      "sources_hash": sources_hash()}
     out[workload] = rec
-    path = os.path.join(ROOT, "profiles", "traffic.json")
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)
     print(json.dumps(out, indent=1))
@@ -350,6 +358,8 @@ def main():
                     help="only run a plain device copy of MIB MiB (counter calibration)")
     ap.add_argument("--traffic-from", metavar="DIR",
                     help="write profiles/traffic.json from rocprofv3 counter runs under DIR (no GPU needed)")
+    ap.add_argument("--traffic-workload", default="kda_dense",
+                    help="the workload the counter runs of --traffic-from were taken on")
     ap.add_argument("--copy-bytes", type=int, default=1024 * 1024 * 1024,
                     help="size of the calibration copy used with --traffic-from")
     ap.add_argument("--only", metavar="WORKLOAD",
@@ -359,7 +369,7 @@ def main():
                     help="only run the grouped-value-head sweep (head shapes x sequence patterns)")
     args = ap.parse_args()
     if args.traffic_from:
-        traffic_from(args.traffic_from, args.copy_bytes)
+        traffic_from(args.traffic_from, args.copy_bytes, args.traffic_workload)
         return
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
