@@ -32,23 +32,35 @@ __global__ __launch_bounds__(NT, (Lds<PER_CHANNEL, DELTA>::JOBS_PER_CU)) void ch
 // Gram products kn kn^T and qn kn^T and the transposes kn^T do not depend on
 // the value head, so they are formed once; the workgroup then walks the G
 // value heads of the group, each with its own gates and write strengths:
-// decays applied to the Gram blocks, A and M, T = (I + A)^-1,
-// W = T diag(b) diag(exp(Gamma)) kn and the record fragments.  The records
-// have the shared-q/k format (qn and kn^T in the group's first record, the
-// per-token factors exp(Gamma_r), exp(Gamma_L - Gamma_r) in every record).
+// decays applied to the Gram blocks, A and M, T = (I + A)^-1 and the record
+// fragments.  The records have the shared-q/k format: qn, kn^T and (delta
+// rule) kn in the group's first record, the per-token factors exp(Gamma_r),
+// exp(Gamma_L - Gamma_r), M and T diag(b) in every record, and no W (the
+// recurrence forms W S as T diag(b) diag(exp(Gamma)) (kn S)).
 // ---------------------------------------------------------------------------
+// LDS of the grouped kernel: Y blocks, A, T and the per-token rows; no K-hat^T
+// (no W is formed) and no exact-fallback scratch (with one decay per
+// token-head every decay factor is applied after the products and is <= 1).
+// 48 KB, so three jobs share a CU.
 template <bool DELTA>
-__global__ __launch_bounds__(NT, (Lds<false, DELTA>::JOBS_PER_CU)) void chunk_group_kernel(const ChunkParams p,
-                                                                                           const int n_jobs) {
+struct GroupLds {
+  static constexpr int YB = L_YB;
+  static constexpr int AM = L_YB + 3 * 4 * 64 * 16;
+  static constexpr int TM = AM + (DELTA ? CH * MS * 4 : 0);
+  static constexpr int ROW = TM + (DELTA ? CH * MS * 4 : 0);
+  static constexpr int BYTES = ROW + (5 * CH + 8) * 4;
+  static constexpr int JOBS_PER_CU = 3;
+};
+static_assert(3 * GroupLds<true>::BYTES <= 160 * 1024, "three grouped jobs per CU");
+
+template <bool DELTA>
+__global__ __launch_bounds__(NT, 3) void chunk_group_kernel(const ChunkParams p, const int n_jobs) {
   extern __shared__ __attribute__((aligned(16))) uint8_t smem[];
-  using LD = Lds<false, DELTA>;
+  using LD = GroupLds<DELTA>;
   f16x8* YB = reinterpret_cast<f16x8*>(smem + LD::YB);
-  uint8_t* KHb = smem + L_KH;  // kn^T fragments (full layout only: W needs them)
-  const f16x8* KH = reinterpret_cast<const f16x8*>(smem + L_KH);
-  float* AM = reinterpret_cast<float*>(smem + L_AM);
-  float* TM = reinterpret_cast<float*>(smem + L_TM);
+  float* AM = reinterpret_cast<float*>(smem + LD::AM);
+  float* TM = reinterpret_cast<float*>(smem + LD::TM);
   float* ROW = reinterpret_cast<float*>(smem + LD::ROW);
-  constexpr int R_EG = R_RK;  // exp(Gamma_r) of the current value head
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
   const int l16 = lane & 15, lg = lane >> 4;
@@ -140,16 +152,18 @@ __global__ __launch_bounds__(NT, (Lds<false, DELTA>::JOBS_PER_CU)) void chunk_gr
     const f16x8 xh = to_f16x8(&X[8 * s]);
     if (n < 3) YB[(n * 4 + s) * 64 + lane] = xh;
     store_reordered(rec0 + REC_QHAT + (n * 4 + s) * FRAG_BYTES, to_f16x8(&Q[8 * s]), sel, lane);
+    // the delta rule's W S is formed in the recurrence from kn S (W = T diag(b) diag(exp(Gamma)) kn):
+    // kn goes to the first head's W slot in the A-operand order of Qhat, and no head stores W
+    if (DELTA) store_reordered(rec0 + REC_WNEG + (n * 4 + s) * FRAG_BYTES, xh, sel, lane);
 #pragma unroll
     for (int hh = 0; hh < 2; ++hh) {  // kn^T by selection products
       const int kt = 2 * s + hh;
       const f32x4 tb = mma_f16(xh, sel[hh], zero4());
       const f16x4 tb4 = {(f16)tb[0], (f16)tb[1], (f16)tb[2], (f16)tb[3]};
-      if (DELTA) *reinterpret_cast<f16x4*>(KHb + ((kt * 2 + (n >> 1)) * 64 + lane) * 16 + (n & 1) * 8) = tb4;
       *reinterpret_cast<f16x4*>(rec0 + REC_KBAR + (kt * 2 + (n >> 1)) * FRAG_BYTES + lane * 16 + (n & 1) * 8) = tb4;
     }
   }
-  __syncthreads();  // Y operands (and kn^T for W) visible
+  __syncthreads();  // Y operands visible
 
   f32x4 accA[3], accM[3], accA_d = zero4(), accM_d = zero4();
 #pragma unroll
@@ -217,7 +231,6 @@ __global__ __launch_bounds__(NT, (Lds<false, DELTA>::JOBS_PER_CU)) void chunk_gr
         float* glp = reinterpret_cast<float*>(rec + REC_GL);
         glp[r] = EGr;
         glp[CH + r] = EGLr;
-        if (DELTA) ROW[R_EG + r] = EGr;
       }
 
       // ---- A rows of this sub-chunk -> LDS; M fragments -> record ------------
@@ -284,7 +297,7 @@ __global__ __launch_bounds__(NT, (Lds<false, DELTA>::JOBS_PER_CU)) void chunk_gr
         const f32x4 Tnn = unit_lower_inverse(Ncl, f32x4{nt.x, nt.y, nt.z, nt.w}, l16, lg);
 #pragma unroll
         for (int j = 0; j < 4; ++j) TM[(SUB * N + 4 * lg + j) * MS + SUB * N + l16] = Tnn[j];
-        __syncthreads();  // A rows, diagonal T blocks and exp(Gamma) visible
+        __syncthreads();  // A rows and diagonal T blocks visible
 
         // ---- off-diagonal blocks of T by block column (as in chunk_local_kernel) --
         {
@@ -318,46 +331,24 @@ __global__ __launch_bounds__(NT, (Lds<false, DELTA>::JOBS_PER_CU)) void chunk_gr
           __syncthreads();  // every block of T visible
         }
 
-        // ---- T diag(b) fragments and -W^T = -kn^T (T diag(b) diag(exp(Gamma)))^T ----
+        // ---- T diag(b) fragments ------------------------------------------------
         {
           const int rt = SUB * N + l16;
           constexpr int ns = (N >> 1) + 1;  // token slices with nonzero T entries for this tile
-          f16x8 tbB[2];
 #pragma unroll
-          for (int s = 0; s < 2; ++s) {
-            float v[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f}, w[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-            if (s < ns) {
-              const int j0 = 32 * s + 4 * lg, j1 = j0 + 16;
-              float tv[8], bb[8], eg[8];
-              *reinterpret_cast<float4*>(&tv[0]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j0]);
-              *reinterpret_cast<float4*>(&tv[4]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j1]);
-              *reinterpret_cast<float4*>(&bb[0]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j0]);
-              *reinterpret_cast<float4*>(&bb[4]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j1]);
-              *reinterpret_cast<float4*>(&eg[0]) = *reinterpret_cast<const float4*>(&ROW[R_EG + j0]);
-              *reinterpret_cast<float4*>(&eg[4]) = *reinterpret_cast<const float4*>(&ROW[R_EG + j1]);
+          for (int s = 0; s < ns; ++s) {
+            const int j0 = 32 * s + 4 * lg, j1 = j0 + 16;
+            float v[8], tv[8], bb[8];
+            *reinterpret_cast<float4*>(&tv[0]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j0]);
+            *reinterpret_cast<float4*>(&tv[4]) = *reinterpret_cast<const float4*>(&TM[rt * MS + j1]);
+            *reinterpret_cast<float4*>(&bb[0]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j0]);
+            *reinterpret_cast<float4*>(&bb[4]) = *reinterpret_cast<const float4*>(&ROW[R_BETA + j1]);
 #pragma unroll
-              for (int q = 0; q < 4; ++q) {
-                v[q] = (j0 + q <= rt) ? tv[q] * bb[q] : 0.f;
-                v[4 + q] = (j1 + q <= rt) ? tv[4 + q] * bb[4 + q] : 0.f;
-              }
-#pragma unroll
-              for (int q = 0; q < 8; ++q) w[q] = v[q] * eg[q];
-              store_frag(rec, REC_TB, N * 2 + s, lane, v);
+            for (int q = 0; q < 4; ++q) {
+              v[q] = (j0 + q <= rt) ? tv[q] * bb[q] : 0.f;
+              v[4 + q] = (j1 + q <= rt) ? tv[4 + q] * bb[4 + q] : 0.f;
             }
-            tbB[s] = to_f16x8(w);
-          }
-#pragma unroll
-          for (int sp = 0; sp < 4; ++sp) {
-            float v[8];
-#pragma unroll
-            for (int hh = 0; hh < 2; ++hh) {
-              const int kt = 2 * sp + hh;
-              f32x4 acc = mma_f16(KH[(kt * 2) * 64 + lane], tbB[0], zero4());
-              if (ns > 1) acc = mma_f16(KH[(kt * 2 + 1) * 64 + lane], tbB[1], acc);
-#pragma unroll
-              for (int j = 0; j < 4; ++j) v[hh * 4 + j] = -acc[j];
-            }
-            store_frag(rec, REC_WNEG, N * 4 + sp, lane, v);
+            store_frag(rec, REC_TB, N * 2 + s, lane, v);
           }
         }
       }
@@ -387,16 +378,16 @@ hipError_t launch_chunk_variant(const ChunkParams& p, int n_jobs, hipStream_t st
   return hipSuccess;
 }
 
-// one job per (chunk, q/k head); two (full layout) or three (compact) per CU
+// one job per (chunk, q/k head), three per CU
 template <bool DELTA>
 hipError_t launch_group_variant(const ChunkParams& p, int n_jobs, hipStream_t stream) {
   static std::atomic<int> attr_set[MAX_DEVICES];
   const hipError_t e = once_per_device(attr_set, [] {
     return hipFuncSetAttribute(reinterpret_cast<const void*>(&chunk_group_kernel<DELTA>),
-                               hipFuncAttributeMaxDynamicSharedMemorySize, Lds<false, DELTA>::BYTES);
+                               hipFuncAttributeMaxDynamicSharedMemorySize, GroupLds<DELTA>::BYTES);
   });
   if (e != hipSuccess) return e;
-  chunk_group_kernel<DELTA><<<n_jobs, NT, Lds<false, DELTA>::BYTES, stream>>>(p, n_jobs);
+  chunk_group_kernel<DELTA><<<n_jobs, NT, GroupLds<DELTA>::BYTES, stream>>>(p, n_jobs);
   return hipSuccess;
 }
 }  // namespace

@@ -96,8 +96,9 @@ using ValueRow = typename std::conditional<NCT == 1, uint2, Bf16Row<NCT>>::type;
 
 template <int NCT>
 struct ChainFrags {
-  f16x8 w[4], t[2], k[4];
+  f16x8 w[4], t[2], k[4];  // w: -W, or kn for shared q/k records with the delta rule
   float4 gl[2];
+  float4 eg;  // shared q/k records with the delta rule: exp(Gamma_r) of this lane's four U rows
   ValueRow<NCT> v;  // 4 NCT bf16 of the value tile
   uint32_t touch;
 };
@@ -124,7 +125,13 @@ __device__ __forceinline__ void unpack_bf16(uint2 x, f16* o) {
 // record holds the two per-token factors.  The output waves scale the rows of
 // qn S by exp(Gamma_r); the chain waves scale U's rows by
 // exp(Gamma_L - Gamma_r) (a second LDS copy, since M U needs U itself) and
-// decay S by the single exp(Gamma_L).
+// decay S by the single exp(Gamma_L).  With the delta rule these records hold
+// no W either: W = T diag(b) diag(exp(Gamma)) kn, so the chain forms
+//   U = T diag(b) (V - diag(exp(Gamma)) (kn S))
+// from the group's kn fragments (stored once per group, in the first head's W
+// slot): kn S is a product of the same shape as W S, the residual
+// V - exp(Gamma_r) (kn S)_r is formed in fp32 and passed through LDS as the
+// B operand of T diag(b), at the cost of one more barrier per chunk.
 template <typename StT, int NCT, bool DELTA, bool PC>
 __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
   constexpr int VC = VT * NCT;       // value columns per workgroup
@@ -135,6 +142,8 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
   __shared__ __attribute__((aligned(16))) f16x8 sbuf[NCT][4 * 64];  // S slices (B operand)
   __shared__ __attribute__((aligned(16))) f16x4 ubuf[NCT][4 * 64];  // U tiles (C layout)
   __shared__ __attribute__((aligned(16))) f16x4 ubuf2[PC ? 1 : NCT][4 * 64];  // scalar gate: decayed U tiles
+  constexpr bool KN = DELTA && !PC;  // U from kn S (records without W)
+  __shared__ __attribute__((aligned(16))) f16x4 rbuf[KN ? NCT : 1][4 * 64];   // V - exp(Gamma) kn S (C layout)
   __shared__ __attribute__((aligned(16))) f16 vsT[VC * VS];         // value tile, [column][token]
 
   const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
@@ -192,9 +201,10 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
         const uint8_t* RK = PC ? R : shared_record(c);
 #pragma unroll
         for (int s2 = 0; s2 < 4; ++s2) {
-          F.w[s2] = ldfrag(R, REC_WNEG, TW * 4 + s2, lane);
+          F.w[s2] = ldfrag(KN ? RK : R, REC_WNEG, TW * 4 + s2, lane);
           F.k[s2] = ldfrag(RK, REC_KBAR, (2 * TW + (s2 >> 1)) * 2 + (s2 & 1), lane);
         }
+        if constexpr (KN) F.eg = *reinterpret_cast<const float4*>(R + REC_GL + 4 * (SUB * TW + 4 * lg));
         F.t[0] = ldfrag(R, REC_TB, TW * 2, lane);
         F.t[1] = ldfrag(R, REC_TB, TW * 2 + (TW >= 2 ? 1 : 0), lane);
         if (PC) {  // exp(Gamma_L) of this lane's state rows
@@ -269,6 +279,20 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
 #pragma unroll
           for (int s2 = 0; s2 < 4; ++s2) sB[s2] = sbuf[j][s2 * 64 + lane];
           f32x4 U = zero4(), U2 = zero4();
+          if constexpr (KN) {
+            // residual rows 16 tw + 4 lg .. +3 of column 16 j + l16: V - exp(Gamma_r) (kn S)_r
+#pragma unroll
+            for (int s2 = 0; s2 < 4; ++s2) {
+              if (s2 & 1) U2 = mma_f16(F.w[s2], sB[s2], U2);
+              else U = mma_f16(F.w[s2], sB[s2], U);
+            }
+            const f16x4 vr = *reinterpret_cast<const f16x4*>(&vsT[(VT * j + l16) * VS + SUB * TW + 4 * lg]);
+            rbuf[j][TW * 64 + lane] = f16x4{(f16)((float)vr[0] - F.eg.x * (U[0] + U2[0])),
+                                            (f16)((float)vr[1] - F.eg.y * (U[1] + U2[1])),
+                                            (f16)((float)vr[2] - F.eg.z * (U[2] + U2[2])),
+                                            (f16)((float)vr[3] - F.eg.w * (U[3] + U2[3]))};
+            continue;
+          }
 #pragma unroll
           for (int s2 = 0; s2 < 2; ++s2) {
             if (s2 <= (TW >> 1)) {
@@ -290,6 +314,26 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
           if (!PC)
             ubuf2[j][TW * 64 + lane] = f16x4{(f16)(Us[0] * F.gl[0].x), (f16)(Us[1] * F.gl[0].y),
                                              (f16)(Us[2] * F.gl[0].z), (f16)(Us[3] * F.gl[0].w)};
+        }
+        if constexpr (KN) {
+          __syncthreads();  // A2: residual tiles published
+#pragma unroll
+          for (int j = 0; j < NCT; ++j) {
+            f32x4 U = zero4(), U2 = zero4();
+#pragma unroll
+            for (int s2 = 0; s2 < 2; ++s2) {
+              if (s2 <= (TW >> 1)) {  // tokens 32 s2 + 4 lg + e, then 32 s2 + 16 + 4 lg + e (T's slice order)
+                const f16x4 a = rbuf[j][(2 * s2) * 64 + lane], b = rbuf[j][(2 * s2 + 1) * 64 + lane];
+                const f16x8 rb = {a[0], a[1], a[2], a[3], b[0], b[1], b[2], b[3]};
+                if (s2 == 0) U = mma_f16(F.t[0], rb, U);
+                else U2 = mma_f16(F.t[1], rb, U2);
+              }
+            }
+            const f32x4 Us = {U[0] + U2[0], U[1] + U2[1], U[2] + U2[2], U[3] + U2[3]};
+            ubuf[j][TW * 64 + lane] = f16x4{(f16)Us[0], (f16)Us[1], (f16)Us[2], (f16)Us[3]};
+            ubuf2[j][TW * 64 + lane] = f16x4{(f16)(Us[0] * F.gl[0].x), (f16)(Us[1] * F.gl[0].y),
+                                             (f16)(Us[2] * F.gl[0].z), (f16)(Us[3] * F.gl[0].w)};
+          }
         }
         __syncthreads();  // B
 #pragma unroll
@@ -380,6 +424,7 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
         OQ[j] = f32x4{a[0] + b[0], a[1] + b[1], a[2] + b[2], a[3] + b[3]};
         if (!PC) OQ[j] = f32x4{OQ[j][0] * F.eg.x, OQ[j][1] * F.eg.y, OQ[j][2] * F.eg.z, OQ[j][3] * F.eg.w};
       }
+      if constexpr (KN) __syncthreads();  // A2 (the chain waves' residual exchange)
       __syncthreads();  // B: U_c published
 #pragma unroll
       for (int j = 0; j < NCT; ++j) {
