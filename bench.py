@@ -426,16 +426,16 @@ def main():
         "roofline": roofline,
         "kernels": kernels,
         "step_ms_percentiles": pct,
-        "hbm_copy_gbs": copy_bandwidth(),
     }
     if not args.no_extra:
         extra = {}
-        # the bf16-state variant of the headline shape first, in the same state of the chip as the headline
-        # (after the HBM-saturating decode runs both kernels measured ~10% slower, state or no state)
+        # the bf16-state variant of the headline shape first, with the headline's step count, before anything
+        # else runs (measured after the copy probe or the decode runs, both of its kernels ran ~10% slower,
+        # the chunk-local one included, which never touches the state)
         for other in ("kda_dense_bf16_state", "kda_varlen", "gdn_gva", "kda_decode", "la_varlen", "la_decode"):
             bf16_state = other.endswith("_bf16_state")
-            oms, opk, _, ow, _ = time_workload(other.replace("_bf16_state", ""), max(10, args.steps // 5), 10,
-                                               bf16_state=bf16_state)
+            osteps = args.steps if bf16_state else max(10, args.steps // 5)
+            oms, opk, _, ow, _ = time_workload(other.replace("_bf16_state", ""), osteps, 10, bf16_state=bf16_state)
             ab = algorithmic_bytes(ow, state_bytes=2 if bf16_state else 4)
             tok = ow.B if ow.decode else ow.B * ow.T
             tot = ab["kda_fused"]
@@ -444,6 +444,8 @@ def main():
                             "hbm_frac": round(tot / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                             "kernels_avg_ms": {k: round(v, 4) for k, v in opk.items()}}
         result["other_workloads"] = extra
+    # after every timed workload: the probe's 2 GiB of buffers are allocated and freed last
+    result["hbm_copy_gbs"] = copy_bandwidth()
     if not args.no_cpu_baseline:
         result["cpu_baseline"] = cpu_baseline(inp, w, min(args.cpu_tokens, w.T), min(args.cpu_tokens_1t, w.T))
     print(json.dumps(result), flush=True)
