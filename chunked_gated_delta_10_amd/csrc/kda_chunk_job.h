@@ -601,7 +601,9 @@ __device__ __forceinline__ void chunk_job(const ChunkParams& p, uint8_t* smem, c
               }
               const f32x4 tb = mma_f16(kb, sel[hh], zero4());
               const f16x4 tb4 = {(f16)tb[0], (f16)tb[1], (f16)tb[2], (f16)tb[3]};
-              st_rec<!PRECISE>(rec + REC_KBAR + (kt * 2 + (N >> 1)) * FRAG_BYTES + lane * 16 + (N & 1) * 8, tb4);
+              // half-fragment pieces from two waves: an ordinary store, so L2 merges them into whole
+              // lines (non-temporal, they reach memory as 571 instead of 508 MB of writes)
+              *reinterpret_cast<f16x4*>(rec + REC_KBAR + (kt * 2 + (N >> 1)) * FRAG_BYTES + lane * 16 + (N & 1) * 8) = tb4;
               if (PRECISE) {
                 const f32x4 tl = mma_f16(kbl, sel[hh], zero4());
                 const f16x4 tl4 = {(f16)tl[0], (f16)tl[1], (f16)tl[2], (f16)tl[3]};
