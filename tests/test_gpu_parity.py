@@ -79,6 +79,15 @@ def test_scalar_gate_grouped_heads_both_paths(B, T, H, H_qk, state_dtype):
                                                                                              state_dtype))
 
 
+@pytest.mark.parametrize("A_log", [(2.5, 3.0), (-8.0, -6.0)])
+def test_grouped_kernel_extreme_scalar_decays(A_log):
+    # The grouped kernel's records (264 jobs) with decays that underflow within
+    # a chunk (exp(A_log) ~ 12..20) or hardly decay at all: the recurrence's
+    # residual V - exp(Gamma_r) (kn S) and its row factors at both extremes.
+    inp = make_inputs(44, 150, 8, 2, gate_per_channel=False, A_log=A_log, state_std=0.05, seed=71)
+    check(inp, what="grouped kernel, scalar decays A_log in %s" % (A_log,))
+
+
 @pytest.mark.parametrize("lens", [[1, 64, 300, 0, 65, 129], [1, 64, 3000, 0, 65, 129, 700]])
 def test_scalar_gate_grouped_heads_packed(lens):
     # three value heads per q/k head, packed sequences with an empty one and a
