@@ -178,3 +178,34 @@ def test_full_size_decode():
     ro, rs = la.la_decode(inp["q"], inp["k"], inp["v"], inp["g_raw"], inp["A_log"], inp["scale"],
                           inp["initial_state"], gate_per_channel=False)
     assert_parity(out, st, ro, rs, what="la_decode B=256 H=64")
+
+
+LA_REGIMES = {"workload": (-1.0, 1.0), "slow decay": (-6.0, -4.0), "harsh decay": (2.0, 3.0)}
+
+
+@pytest.mark.parametrize("i", range(12))
+def test_random_configuration(i):
+    # seeded random configurations (deterministic): gate mode, q/k heads and the value heads grouped on
+    # them, dense rows or packed sequences (empty ones allowed), ragged lengths, state dtype, gate regime
+    rng = np.random.default_rng(1900 + i)
+    per_channel = bool(rng.integers(0, 2))
+    H_qk = int(rng.choice([1, 2, 4]))
+    H = H_qk * int(rng.choice([1, 2, 3]))
+    regime = str(rng.choice(sorted(LA_REGIMES)))
+    state = str(rng.choice(["none", "fp32", "bf16"]))
+    kw = dict(gate_per_channel=per_channel, A_log=LA_REGIMES[regime], seed=2000 + i)
+    if state != "none":
+        kw["state_std"] = 0.05
+    if rng.integers(0, 2):
+        lens = [int(x) for x in rng.integers(0, 300, int(rng.integers(1, 6)))]
+        if sum(lens) == 0:
+            lens[0] = 1
+        inp = make_inputs(1, sum(lens), H, H_qk, N=len(lens), lengths=lens, **kw)
+        shape = "packed %s" % lens
+    else:
+        B, T = int(rng.integers(1, 4)), int(rng.integers(1, 500))
+        inp = make_inputs(B, T, H, H_qk, **kw)
+        shape = "B=%d T=%d" % (B, T)
+    sdt = torch.bfloat16 if state == "bf16" else torch.float32
+    check(inp, sdt, what="la case %d: %s H=%d H_qk=%d %s decay, %s, state %s" % (
+        i, shape, H, H_qk, "per-channel" if per_channel else "scalar", regime, state))
