@@ -197,3 +197,93 @@ def test_chunk_form_forward_state_matches_the_c_oracle():
     _, fin = oracle.kda_fwd(x["q"], x["k"], x["v"], x["g_raw"], x["beta_logits"], x["A_log"], 0.5,
                             initial_state=x["initial_state"])
     np.testing.assert_allclose(S.T, fin[0, 0], rtol=1e-11, atol=1e-12)
+
+
+def scalar_gate_chunk_backward(q, k, v, g_raw, bl, a_log, scale, dout, dfinal, S0, C):
+    """The scalar-gate (gated delta rule) special case in the form a kernel would use: every decay is a
+    scalar per token, so the decay factors reduce to row scalings by e_r = exp(G_r), f_r = exp(G_L - G_r)
+    and one 64 x 64 mask Lam[r, i] = exp(G_r - G_i) (r >= i, all <= 1) on the Gram matrices
+    P = qn kn^T and Gm = kn kn^T: no exponential of a positive exponent appears anywhere."""
+    T_, K = q.shape
+    nq = np.sqrt((q * q).sum(-1, keepdims=True) + EPS)
+    nk = np.sqrt((k * k).sum(-1, keepdims=True) + EPS)
+    qn, kn = q / nq, k / nk
+    g = -np.exp(a_log) * np.logaddexp(0.0, g_raw)            # [T]
+    beta = 1.0 / (1.0 + np.exp(-bl))
+    bounds = [(s, min(s + C, T_)) for s in range(0, T_, C)]
+    S = S0.copy()
+    fw = []
+    for s, e in bounds:
+        G = np.cumsum(g[s:e])
+        ee, ff, eL = np.exp(G), np.exp(G[-1] - G), np.exp(G[-1])
+        Lam = np.tril(np.exp(np.minimum(G[:, None] - G[None, :], 0.0)))
+        P, Gm = qn[s:e] @ kn[s:e].T, kn[s:e] @ kn[s:e].T
+        M = P * Lam
+        A = np.tril(beta[s:e, None] * Gm * Lam, -1)
+        T = np.linalg.inv(np.eye(e - s) + A)
+        R = v[s:e] - ee[:, None] * (kn[s:e] @ S)
+        U = T @ (beta[s:e, None] * R)
+        fw.append(dict(G=G, ee=ee, ff=ff, eL=eL, Lam=Lam, P=P, Gm=Gm, M=M, T=T, R=R, U=U, S=S.copy()))
+        S = eL * S + kn[s:e].T @ (ff[:, None] * U)
+    dqn, dkn, dv = np.zeros_like(qn), np.zeros_like(kn), np.zeros_like(v)
+    dg, dbeta = np.zeros_like(g), np.zeros_like(beta)
+    dS = dfinal.copy()
+    for (s, e), c in zip(reversed(bounds), reversed(fw)):
+        dO = scale * dout[s:e]
+        qc, kc, b, Sc = qn[s:e], kn[s:e], beta[s:e], c["S"]
+        # adjoint chunk step (what the sequential kernel computes per value-column tile)
+        dU = c["M"].T @ dO + c["ff"][:, None] * (kc @ dS)
+        dS_prev = qc.T @ (c["ee"][:, None] * dO) - kc.T @ ((b * c["ee"])[:, None] * (c["T"].T @ dU)) + c["eL"] * dS
+        # chunk-parallel gradients
+        SdO = dO @ Sc.T                                        # [L, K]
+        dqn[s:e] += c["ee"][:, None] * SdO
+        de = (qc * SdO).sum(1)
+        UdS = c["U"] @ dS.T                                    # [L, K]
+        dkn[s:e] += c["ff"][:, None] * UdS
+        df = (kc * UdS).sum(1)
+        deL = (dS * Sc).sum()
+        dM = np.tril(dO @ c["U"].T)
+        Y = c["T"].T @ dU
+        dR = b[:, None] * Y
+        db = (Y * c["R"]).sum(1)
+        dv[s:e] += dR
+        kS = kc @ Sc
+        dkn[s:e] -= c["ee"][:, None] * (dR @ Sc.T)
+        de -= (dR * kS).sum(1)
+        dT = dU @ (b[:, None] * c["R"]).T
+        dA = np.tril(-c["T"].T @ dT @ c["T"].T, -1)
+        db += (dA * c["Gm"] * c["Lam"]).sum(1)
+        dGm = b[:, None] * dA * c["Lam"]
+        dLam = b[:, None] * dA * c["Gm"] + dM * c["P"]
+        dP = dM * c["Lam"]
+        dkn[s:e] += (dGm + dGm.T) @ kc + dP.T @ qc
+        dqn[s:e] += dP @ kc
+        W = dLam * c["Lam"]
+        dG = W.sum(1) - W.sum(0) + de * c["ee"] - df * c["ff"]
+        dG[-1] += (df * c["ff"]).sum() + deL * c["eL"]
+        dg[s:e] += np.cumsum(dG[::-1])[::-1]
+        dbeta[s:e] += db
+        dS = dS_prev
+    dq = dqn / nq - q * (q * dqn).sum(-1, keepdims=True) / nq ** 3
+    dk = dkn / nk - k * (k * dkn).sum(-1, keepdims=True) / nk ** 3
+    sig = 1.0 / (1.0 + np.exp(-g_raw))
+    return dict(dq=dq, dk=dk, dv=dv, dg_raw=dg * (-np.exp(a_log)) * sig, dbeta_logits=dbeta * beta * (1 - beta),
+                dA_log=(dg * g).sum(), dinitial_state=dS)
+
+
+@pytest.mark.parametrize("T,C,A_log", [(13, 4, -1.0), (40, 16, 0.5), (37, 8, 3.0)])
+def test_scalar_gate_chunk_form_backward_matches_the_oracle(T, C, A_log):
+    rng = np.random.default_rng(T + C)
+    K = V = 6
+    q, k, v = rng.standard_normal((T, K)), rng.standard_normal((T, K)), rng.standard_normal((T, V))
+    g_raw, bl = rng.standard_normal(T), rng.standard_normal(T)
+    S0, dout, dfinal = 0.3 * rng.standard_normal((K, V)), rng.standard_normal((T, V)), rng.standard_normal((K, V))
+    got = scalar_gate_chunk_backward(q, k, v, g_raw, bl, A_log, 0.5, dout, dfinal, S0, C)
+    ref = KB.kda_bwd(q[None, :, None], k[None, :, None], v[None, :, None], g_raw[None, :, None], bl[None, :, None],
+                     np.array([A_log]), 0.5, dout[None, :, None], dfinal.T[None, None], gate_per_channel=False,
+                     initial_state=S0.T[None, None])
+    squeeze = dict(dq=lambda a: a[0, :, 0], dk=lambda a: a[0, :, 0], dv=lambda a: a[0, :, 0],
+                   dg_raw=lambda a: a[0, :, 0], dbeta_logits=lambda a: a[0, :, 0], dA_log=lambda a: a[0],
+                   dinitial_state=lambda a: a[0, 0].T)
+    for name, r in ref.items():
+        np.testing.assert_allclose(got[name], squeeze[name](r), rtol=1e-9, atol=1e-10, err_msg=name)
