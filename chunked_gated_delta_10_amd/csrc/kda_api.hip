@@ -356,6 +356,120 @@ kda_status run_decode(const void* q, const void* k, const void* v, const void* g
   return ok();
 }
 
+// ---- backward (scalar gate) ------------------------------------------------
+// Workspace: the forward's (schedule, sink, chunk records), then the state
+// entering every (chunk, head), the gradient of the state leaving it, the
+// per-(chunk, head) prep blocks, and the gradient kernel's per-job scratch.
+constexpr size_t BWD_MAX_SLOTS = 2048;
+
+struct BwdLayout {
+  Layout F;
+  size_t states, dstates, prep, scratch, slots, total;
+};
+
+BwdLayout bwd_layout(int n_seqs, int n_entries, int H) {
+  BwdLayout L;
+  L.F = layout(n_seqs, n_entries, H, false);
+  const size_t jobs = (size_t)n_entries * H;
+  L.slots = std::min(jobs, BWD_MAX_SLOTS);
+  L.states = L.F.total;
+  L.dstates = L.states + round_up(jobs * kda::HD * kda::HD * sizeof(float));
+  L.prep = L.dstates + round_up(jobs * kda::HD * kda::HD * sizeof(float));
+  L.scratch = L.prep + round_up(jobs * kda::PREP_FLOATS * sizeof(float));
+  L.total = L.scratch + round_up(L.slots * kda::BWD_SLOT_FLOATS * sizeof(float));
+  return L;
+}
+
+struct BwdArgs {
+  const void *q, *k, *v, *g_raw;
+  const float *beta, *A_log;
+  float scale;
+  int gate_per_channel;
+  const float* s0;
+  const void* dout;
+  const float* dfinal;
+  float *dq, *dk, *dv, *dg_raw, *dbeta, *dA_log, *dinit;
+  const int32_t* cu;
+  int n_seqs, T, rows, H_qk, H, K, V;
+  void* ws;
+  size_t ws_bytes;
+  hipStream_t stream;
+};
+
+kda_status run_backward(const BwdArgs& a) {
+  FwdArgs f{a.q, a.k, a.v, a.g_raw, a.beta, a.A_log, a.scale, a.gate_per_channel, nullptr, KDA_STATE_NONE,
+            nullptr, nullptr, KDA_STATE_NONE, a.cu, a.n_seqs, a.T, a.rows, a.H_qk, a.H, a.K, a.V, nullptr, 0,
+            a.stream, true};
+  kda_status st = validate_common(f);
+  if (st != KDA_OK) return st;
+  if (a.gate_per_channel != 0)
+    return fail(KDA_ERR_SHAPE, "the backward pass supports the scalar gate only (gate_per_channel = 0)");
+  if (a.n_seqs == 0) return ok();
+  const long tokens = (long)a.rows * a.T;
+  if (tokens > 0) {
+    const void* req[] = {a.q, a.k, a.v, a.g_raw, a.beta, a.A_log, a.dout, a.dq, a.dk, a.dv, a.dg_raw, a.dbeta};
+    const char* names[] = {"q", "k", "v", "g_raw", "beta_logits", "A_log", "dout", "dq", "dk", "dv", "dg_raw",
+                           "dbeta_logits"};
+    for (int i = 0; i < 12; ++i)
+      if (!req[i]) return fail(KDA_ERR_NULL, "%s is NULL", names[i]);
+    for (int i = 0; i < 12; ++i)
+      if (!aligned16(req[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", names[i]);
+  }
+  if (!a.dA_log) return fail(KDA_ERR_NULL, "dA_log is NULL");
+  const void* opt[] = {a.s0, a.dfinal, a.dinit, a.dA_log};
+  const char* onames[] = {"initial_state", "dfinal", "dinitial_state", "dA_log"};
+  for (int i = 0; i < 4; ++i)
+    if (opt[i] && !aligned16(opt[i])) return fail(KDA_ERR_ALIGN, "%s is not 16-byte aligned", onames[i]);
+  if (a.cu && (reinterpret_cast<uintptr_t>(a.cu) & 3u)) return fail(KDA_ERR_ALIGN, "cu_seqlens is not 4-byte aligned");
+  const int n_entries = a.cu ? cdiv(a.T, kda::CH) + a.n_seqs : a.n_seqs * cdiv(a.T, kda::CH);
+  if ((long)n_entries * a.H >= (1L << 31))
+    return fail(KDA_ERR_SHAPE, "problem too large (chunks x heads must fit in int32)");
+  const BwdLayout L = bwd_layout(a.n_seqs, n_entries, a.H);
+  if (!a.ws) return fail(KDA_ERR_WORKSPACE, "workspace is NULL (need %zu bytes)", L.total);
+  if (a.ws_bytes < L.total)
+    return fail(KDA_ERR_WORKSPACE, "workspace too small: %zu bytes given, %zu needed", a.ws_bytes, L.total);
+  if (reinterpret_cast<uintptr_t>(a.ws) & (ALIGN - 1)) return fail(KDA_ERR_ALIGN, "workspace is not 256-byte aligned");
+
+  uint8_t* ws = static_cast<uint8_t*>(a.ws);
+  int4* seqs = reinterpret_cast<int4*>(ws + L.F.seqs);
+  int4* chunks = reinterpret_cast<int4*>(ws + L.F.chunks);
+  int* order = reinterpret_cast<int*>(ws + L.F.order);
+  int* err = reinterpret_cast<int*>(ws);
+  uint16_t* sink = reinterpret_cast<uint16_t*>(ws + L.F.sink);
+  float* states = reinterpret_cast<float*>(ws + L.states);
+  (void)hipGetLastError();
+  if (a.cu) {
+    kda::TableParams tp{a.cu, a.n_seqs, a.T, n_entries, seqs, chunks, order};
+    kda::launch_table(tp, a.stream);
+  }
+  // the forward again, keeping the state entering every chunk
+  if (n_entries > 0 && tokens > 0) {
+    const kda::ChunkParams cp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                              static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log, chunks, a.H, a.H_qk,
+                              ws + L.F.rec, a.cu ? 0 : a.T, static_cast<const uint16_t*>(a.v)};
+    const hipError_t e = kda::launch_chunk_local(cp, n_entries, false, true, a.stream);
+    if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel setup failed: %s", hipGetErrorString(e));
+    kda::RecurParams rp{ws + L.F.rec, seqs, order, a.n_seqs * a.H, n_entries, a.H, a.H_qk,
+                        static_cast<const uint16_t*>(a.v), nullptr, a.s0, nullptr, a.scale, sink,
+                        a.cu ? -1 : a.T, err, states};
+    kda::launch_recur_states(rp, false, a.stream);
+  }
+  kda::BwdParams bp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
+                    static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log,
+                    static_cast<const uint16_t*>(a.dout), a.dfinal, a.scale, a.H, a.H_qk, a.cu ? -1 : a.T, chunks,
+                    seqs, order, tokens > 0 ? n_entries : 0, a.n_seqs * a.H, states,
+                    reinterpret_cast<float*>(ws + L.dstates), reinterpret_cast<float*>(ws + L.prep),
+                    reinterpret_cast<float*>(ws + L.scratch), 0, a.dq, a.dk, a.dv, a.dg_raw, a.dbeta, a.dA_log,
+                    a.dinit};
+  kda::launch_bwd(bp, (size_t)tokens * a.H_qk * kda::HD, L.slots, a.stream);
+  const hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
+  if (env_flag("KDA_LOG"))
+    std::fprintf(stderr, "[kda] bwd seqs=%d T=%d H=%d H_qk=%d entries=%d slots=%zu\n", a.n_seqs, a.T, a.H, a.H_qk,
+                 n_entries, L.slots);
+  return ok();
+}
+
 }  // namespace
 
 extern "C" {
@@ -467,6 +581,38 @@ kda_status kda_fwd_check(const void* workspace, void* stream) {
               (bits & 1) ? "a workgroup ran on an unexpected XCD; " : "",
               (bits & 2) ? "a consumer's bounded wait for a record timed out; " : "",
               (bits & 4) ? "a producer's bounded wait for a free ring slot timed out" : "");
+}
+
+size_t kda_bwd_workspace_bytes(int B, int T, int H_qk, int H, int N) {
+  if (B < 0 || T < 0 || H_qk <= 0 || H <= 0 || N < 0 || H % H_qk != 0) return 0;
+  if (N > 0 && B != 1) return 0;
+  const int n_seqs = N > 0 ? N : B;
+  const int n_entries = N > 0 ? cdiv(T, kda::CH) + N : B * cdiv(T, kda::CH);
+  return bwd_layout(n_seqs, n_entries, H).total;
+}
+
+kda_status kda_bwd(const void* q, const void* k, const void* v, const void* g_raw, const float* beta_logits,
+                   const float* A_log, float scale, int gate_per_channel, const float* initial_state,
+                   const void* dout, const float* dfinal, float* dq, float* dk, float* dv, float* dg_raw,
+                   float* dbeta_logits, float* dA_log, float* dinitial_state, int B, int T, int H_qk, int H, int K,
+                   int V, void* workspace, size_t workspace_bytes, void* stream) {
+  BwdArgs a{q, k, v, g_raw, beta_logits, A_log, scale, gate_per_channel, initial_state, dout, dfinal, dq, dk, dv,
+            dg_raw, dbeta_logits, dA_log, dinitial_state, nullptr, B, T, B, H_qk, H, K, V, workspace,
+            workspace_bytes, static_cast<hipStream_t>(stream)};
+  return run_backward(a);
+}
+
+kda_status kda_bwd_varlen(const void* q, const void* k, const void* v, const void* g_raw, const float* beta_logits,
+                          const float* A_log, float scale, int gate_per_channel, const float* initial_state,
+                          const void* dout, const float* dfinal, float* dq, float* dk, float* dv, float* dg_raw,
+                          float* dbeta_logits, float* dA_log, float* dinitial_state, const int32_t* cu_seqlens,
+                          int N, int T, int H_qk, int H, int K, int V, void* workspace, size_t workspace_bytes,
+                          void* stream) {
+  if (N > 0 && !cu_seqlens) return fail(KDA_ERR_NULL, "cu_seqlens is NULL");
+  BwdArgs a{q, k, v, g_raw, beta_logits, A_log, scale, gate_per_channel, initial_state, dout, dfinal, dq, dk, dv,
+            dg_raw, dbeta_logits, dA_log, dinitial_state, cu_seqlens, N, T, 1, H_qk, H, K, V, workspace,
+            workspace_bytes, static_cast<hipStream_t>(stream)};
+  return run_backward(a);
 }
 
 const char* kda_status_string(kda_status s) {

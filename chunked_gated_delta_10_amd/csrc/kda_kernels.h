@@ -63,6 +63,7 @@ struct RecurParams {
   uint16_t* sink;         // 64 scratch values: destination of output rows past a chunk's end
   int dense_T;            // >= 0: B rows of dense_T tokens, schedule by arithmetic; -1: read `seqs`/`order`
   int* err;               // error word of the workspace header: cleared (this path reports no errors)
+  float* states = nullptr;  // backward's forward: fp32 state entering every chunk, [entries][H][128][128]
 };
 
 // Fused persistent forward (kda_fused.hip): per-channel gate, delta rule.
@@ -128,6 +129,9 @@ void launch_table(const TableParams& p, hipStream_t stream);
 // read by the caller with hipGetLastError).
 hipError_t launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, bool delta, hipStream_t stream);
 void launch_recur(const RecurParams& p, bool bf16_state, bool per_channel, bool delta, hipStream_t stream);
+// The backward pass's forward (delta rule, fp32 states): stores the state entering every chunk in
+// p.states and writes no outputs.
+void launch_recur_states(const RecurParams& p, bool per_channel, hipStream_t stream);
 // Scalar gate with value heads grouped on q/k heads and at least
 // GROUP_MIN_JOBS (schedule entry, q/k head) jobs: the value heads of a group
 // share one copy of the qn and kn^T record fragments, written by the grouped
@@ -136,5 +140,42 @@ constexpr int GROUP_MIN_JOBS = 256;
 bool shares_qk_fragments(bool per_channel, int H, int H_qk, int n_entries);
 int recur_grid(int n_chains);
 void launch_decode(const DecodeParams& p, int B, bool bf16_state, bool per_channel, bool delta, hipStream_t stream);
+
+// Backward pass, scalar gate, delta rule (kda_bwd.hip).
+constexpr int BWD_MM = 64 * 64, BWD_MK = 64 * 128;
+constexpr int PREP_FLOATS = 2 * BWD_MK + 4 * BWD_MM + 8 * 64;        // per (entry, head)
+constexpr int BWD_SLOT_FLOATS = 13 * BWD_MK + 6 * BWD_MM + 8 * 64;   // per concurrent gradient job
+struct BwdParams {
+  const uint16_t* q;      // bf16 [tokens, H_qk, 128]
+  const uint16_t* k;
+  const uint16_t* v;      // bf16 [tokens, H, 128]
+  const uint16_t* g_raw;  // bf16 [tokens, H]
+  const float* beta;      // fp32 [tokens, H] (logits)
+  const float* A_log;     // fp32 [H]
+  const uint16_t* dout;   // bf16 [tokens, H, 128]
+  const float* dfinal;    // fp32 [seqs, H, 128, 128] ([V][K]) or null
+  float scale;
+  int H, H_qk;
+  int dense_T;            // >= 0: B rows of dense_T tokens; -1: read chunks / seqs / order
+  const int4* chunks;
+  const int4* seqs;
+  const int* order;
+  int n_entries, n_chains;
+  const float* states;    // [entries][H][V][K]: the state entering every chunk
+  float* dstates;         // [entries][H][V][K]: the gradient of the state leaving every chunk
+  float* prep;            // [entries][H][PREP_FLOATS]
+  float* scratch;         // [slots][BWD_SLOT_FLOATS]
+  int job0;               // first (entry, head) job of a gradient launch
+  float* dq;              // fp32 [tokens, H_qk, 128]
+  float* dk;
+  float* dv;              // fp32 [tokens, H, 128]
+  float* dg_raw;          // fp32 [tokens, H]
+  float* dbeta;           // fp32 [tokens, H]
+  float* dA_log;          // fp32 [H]
+  float* dinit;           // fp32 [seqs, H, 128, 128] or null
+};
+// qk_floats: elements of dq (= of dk), cleared first when value heads share q/k heads; slots: concurrent
+// gradient jobs the scratch holds.
+void launch_bwd(const BwdParams& p, size_t qk_floats, size_t slots, hipStream_t stream);
 
 }  // namespace kda

@@ -69,6 +69,13 @@ def load():
     lib.kda_la_fwd_varlen.argtypes = [P, P, P, P, P, F, I, P, I, P, P, I, P, I, I, I, I, I, I, P, Z, P]
     lib.kda_la_decode_step.restype = I
     lib.kda_la_decode_step.argtypes = [P, P, P, P, P, F, I, P, I, P, I, I, I, I, I, P]
+    lib.kda_bwd_workspace_bytes.restype = Z
+    lib.kda_bwd_workspace_bytes.argtypes = [I, I, I, I, I]
+    lib.kda_bwd.restype = I
+    lib.kda_bwd.argtypes = [P, P, P, P, P, P, F, I, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P, Z, P]
+    lib.kda_bwd_varlen.restype = I
+    lib.kda_bwd_varlen.argtypes = [P, P, P, P, P, P, F, I, P, P, P, P, P, P, P, P, P, P, P, I, I, I, I, I, I, P,
+                                   Z, P]
     lib.kda_fwd_check.restype = I
     lib.kda_fwd_check.argtypes = [P, P]
     lib.kda_status_string.restype = ctypes.c_char_p
@@ -427,3 +434,86 @@ def la_decode_step(q, k, v, g_raw, A_log, state: torch.Tensor, scale: Optional[f
     _check(lib.kda_la_decode_step(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(A_log), scale, per_channel,
                                   _ptr(state), _state_code(state), _ptr(out), B, H_qk, H, K, V, _stream(stream)))
     return out
+
+
+# ---- backward (scalar gate) ----------------------------------------------------
+
+
+def bwd_workspace_bytes(B: int, T: int, H_qk: int, H: int, N: int = 0) -> int:
+    return int(load().kda_bwd_workspace_bytes(B, T, H_qk, H, N))
+
+
+def _grad_buffers(B, T, H_qk, H, K, V, C, dev, want_dinit):
+    f = dict(dtype=torch.float32, device=dev)
+    return dict(dq=torch.empty((B, T, H_qk, K), **f), dk=torch.empty((B, T, H_qk, K), **f),
+                dv=torch.empty((B, T, H, V), **f), dg_raw=torch.empty((B, T, H), **f),
+                dbeta_logits=torch.empty((B, T, H), **f), dA_log=torch.empty((H,), **f),
+                dinitial_state=torch.empty((C, H, V, K), **f) if want_dinit else None)
+
+
+def _bwd_checks(dout, dfinal, initial_state, B, T, H, V, K, C, dev):
+    _need(dout, "dout", torch.bfloat16)
+    if tuple(dout.shape) != (B, T, H, V) or dout.device != dev:
+        raise ValueError("dout must be a bf16 [B, T, H, V] tensor on the inputs' device")
+    for t, n in ((dfinal, "dfinal"), (initial_state, "initial_state")):
+        if t is None:
+            continue
+        _need(t, n, torch.float32)
+        if tuple(t.shape) != (C, H, V, K) or t.device != dev:
+            raise ValueError("%s must be a float32 %s tensor on the inputs' device" % (n, (C, H, V, K)))
+
+
+def bwd(q, k, v, g_raw, beta_logits, A_log, dout, dfinal: Optional[torch.Tensor] = None,
+        scale: Optional[float] = None, initial_state: Optional[torch.Tensor] = None,
+        workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
+    """Gradients of sum(dout * out) + sum(dfinal * final_state) through fwd (scalar gate, g_raw [B, T, H]).
+
+    Returns {dq, dk, dv, dg_raw, dbeta_logits, dA_log, dinitial_state}, all float32."""
+    lib = load()
+    B, T, H_qk, H, K, V, per_channel = _prep(q, k, v, g_raw, beta_logits, A_log)
+    if per_channel:
+        raise ValueError("the backward pass supports the scalar gate only (g_raw [B, T, H])")
+    scale = K ** -0.5 if scale is None else float(scale)
+    dev = q.device
+    _bwd_checks(dout, dfinal, initial_state, B, T, H, V, K, B, dev)
+    nbytes = bwd_workspace_bytes(B, T, H_qk, H, 0)
+    if workspace is None:
+        workspace = _workspace(nbytes, dev)
+    _check_workspace(workspace, nbytes, dev)
+    g = _grad_buffers(B, T, H_qk, H, K, V, B, dev, True)
+    _check(lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale, 0,
+                       _ptr(initial_state), _ptr(dout), _ptr(dfinal), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
+                       _ptr(g["dg_raw"]), _ptr(g["dbeta_logits"]), _ptr(g["dA_log"]), _ptr(g["dinitial_state"]),
+                       B, T, H_qk, H, K, V, _ptr(workspace), workspace.numel(), _stream(stream)))
+    return g
+
+
+def bwd_varlen(q, k, v, g_raw, beta_logits, A_log, dout, cu_seqlens: torch.Tensor,
+               dfinal: Optional[torch.Tensor] = None, scale: Optional[float] = None,
+               initial_state: Optional[torch.Tensor] = None, workspace: Optional[torch.Tensor] = None,
+               stream=None) -> dict:
+    """bwd over packed sequences (B = 1); states and dinitial_state are [N, H, V, K]."""
+    lib = load()
+    B, T, H_qk, H, K, V, per_channel = _prep(q, k, v, g_raw, beta_logits, A_log)
+    if per_channel:
+        raise ValueError("the backward pass supports the scalar gate only (g_raw [1, T, H])")
+    if B != 1:
+        raise ValueError("packed sequences need B == 1")
+    _need(cu_seqlens, "cu_seqlens", torch.int32)
+    N = cu_seqlens.numel() - 1
+    scale = K ** -0.5 if scale is None else float(scale)
+    dev = q.device
+    if cu_seqlens.device != dev:
+        raise ValueError("cu_seqlens is on %s, the inputs on %s" % (cu_seqlens.device, dev))
+    _bwd_checks(dout, dfinal, initial_state, 1, T, H, V, K, N, dev)
+    nbytes = bwd_workspace_bytes(1, T, H_qk, H, max(N, 0))
+    if workspace is None:
+        workspace = _workspace(nbytes, dev)
+    _check_workspace(workspace, nbytes, dev)
+    g = _grad_buffers(1, T, H_qk, H, K, V, max(N, 0), dev, True)
+    _check(lib.kda_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale, 0,
+                              _ptr(initial_state), _ptr(dout), _ptr(dfinal), _ptr(g["dq"]), _ptr(g["dk"]),
+                              _ptr(g["dv"]), _ptr(g["dg_raw"]), _ptr(g["dbeta_logits"]), _ptr(g["dA_log"]),
+                              _ptr(g["dinitial_state"]), _ptr(cu_seqlens), N, T, H_qk, H, K, V, _ptr(workspace),
+                              workspace.numel(), _stream(stream)))
+    return g

@@ -200,6 +200,51 @@ kda_status kda_la_decode_step(const void* q, const void* k, const void* v, const
                               int V, void* stream);
 
 /*
+ * Backward pass of the scalar-gate forward (gate_per_channel = 0: the gated
+ * delta rule with grouped value heads whose backward the FlashQLA H200 page
+ * times, "BACKWARD BENCHMARKS" table; the page does not define it, and it is
+ * read as the gradient of a scalar loss through kda_fwd).  Returns the
+ * gradients of
+ *     L = sum(dout * out) + sum(dfinal * final_state)
+ * where (out, final_state) = kda_fwd with the same inputs, with respect to
+ * q, k, v, g_raw, beta_logits, A_log and initial_state.
+ *
+ * Inputs: q, k, v, g_raw (bf16 [B, T, H]), beta_logits, A_log, scale as for
+ * kda_fwd; initial_state fp32 [B, H, V, K] or NULL (zero state); dout bf16
+ * [B, T, H, 128]; dfinal fp32 [B, H, V, K] or NULL (zero).  Outputs, fp32,
+ * caller-allocated, each written whole (no accumulation into what they
+ * held): dq, dk [B, T, H_qk, 128] (summed over the value heads of each q/k
+ * head); dv [B, T, H, 128]; dg_raw, dbeta_logits [B, T, H]; dA_log [H];
+ * dinitial_state [B, H, V, K], or NULL (not written).
+ *
+ * The forward is recomputed inside the call (the state entering every
+ * 64-token chunk is kept in the workspace: 64 KiB per (chunk, head)), so
+ * nothing from an earlier kda_fwd call is needed.  Workspace bytes:
+ * kda_bwd_workspace_bytes(B, T, H_qk, H, 0) (N > 0: kda_bwd_varlen), 256-byte
+ * aligned, contents garbage before and after.  gate_per_channel = 1 is
+ * rejected with KDA_ERR_SHAPE.  dq, dk (when H > H_qk) and dA_log are
+ * accumulated with float atomics, so their last bits may differ from run to
+ * run.  Other errors and the B/N/T == 0 behaviour follow kda_fwd /
+ * kda_fwd_varlen (T == 0: dinitial_state = dfinal, or zero).
+ */
+size_t kda_bwd_workspace_bytes(int B, int T, int H_qk, int H, int N);
+kda_status kda_bwd(const void* q, const void* k, const void* v, const void* g_raw,
+                   const float* beta_logits, const float* A_log, float scale, int gate_per_channel,
+                   const float* initial_state, const void* dout, const float* dfinal, float* dq,
+                   float* dk, float* dv, float* dg_raw, float* dbeta_logits, float* dA_log,
+                   float* dinitial_state, int B, int T, int H_qk, int H, int K, int V,
+                   void* workspace, size_t workspace_bytes, void* stream);
+/* The same over N packed sequences (B = 1, cu_seqlens as for kda_fwd_varlen;
+ * states [N, H, V, K]). */
+kda_status kda_bwd_varlen(const void* q, const void* k, const void* v, const void* g_raw,
+                          const float* beta_logits, const float* A_log, float scale,
+                          int gate_per_channel, const float* initial_state, const void* dout,
+                          const float* dfinal, float* dq, float* dk, float* dv, float* dg_raw,
+                          float* dbeta_logits, float* dA_log, float* dinitial_state,
+                          const int32_t* cu_seqlens, int N, int T, int H_qk, int H, int K, int V,
+                          void* workspace, size_t workspace_bytes, void* stream);
+
+/*
  * Diagnostics: per-kernel timing with HIP events (used by the benchmark).
  * While enabled on the calling thread, each kernel launched by the entry
  * points above is bracketed by two hipEventRecord calls on the caller's

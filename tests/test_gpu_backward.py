@@ -1,0 +1,156 @@
+"""GPU parity of the scalar-gate backward pass (kda.bwd / kda.bwd_varlen, C ABI
+kda_bwd / kda_bwd_varlen) against the fp64 backward oracle.
+
+The oracle (oracle/kda_backward.py) is reverse-mode differentiation of the
+token-by-token forward, pinned on the CPU to complex-step and finite
+differences.  The GPU recomputes the forward with the two-kernel path (fp16
+matrix-core operands, fp32 state), then runs the chunk-form backward in fp32.
+Every gradient is bilinear in the recomputed states and the upstream
+gradients, so its relative error tracks the forward's state error (held to
+1e-3 rel-L2 by the forward tests) times a small factor: each gradient is held
+to GRAD_REL rel-L2 and to GRAD_MAXABS of its own largest magnitude.
+"""
+
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from oracle import kda_backward as KB
+from chunked_gated_delta_10_amd import kda
+from chunked_gated_delta_10_amd.inputs import make_inputs, bf16_bits
+
+from kda_util import bf16_tensor, rel_l2
+
+pytestmark = pytest.mark.gpu
+
+GRAD_REL = 5e-3
+GRAD_MAXABS = 2e-2  # of max |reference| of the same gradient
+NAMES = ("dq", "dk", "dv", "dg_raw", "dbeta_logits", "dA_log", "dinitial_state")
+
+
+def upstream(inp, seed, dfinal_std=0.1):
+    rng = np.random.default_rng(seed)
+    B, T, H = inp["v"].shape[:3]
+    cu = inp.get("cu_seqlens")
+    C = B if cu is None else len(cu) - 1
+    dout = bf16_bits(rng.standard_normal((B, T, H, 128), dtype=np.float32))
+    dfinal = None if dfinal_std is None else (rng.standard_normal((C, H, 128, 128), dtype=np.float32)
+                                              * np.float32(dfinal_std))
+    return dout, dfinal
+
+
+def run_gpu_bwd(inp, dout, dfinal):
+    dev = "cuda"
+    t = {n: bf16_tensor(inp[n], dev) for n in ("q", "k", "v", "g_raw")}
+    b = torch.from_numpy(inp["b"]).to(dev)
+    a = torch.from_numpy(inp["A_log"]).to(dev)
+    s0 = None if inp["initial_state"] is None else torch.from_numpy(inp["initial_state"]).to(dev)
+    do = bf16_tensor(dout, dev)
+    df = None if dfinal is None else torch.from_numpy(dfinal).to(dev)
+    cu = inp.get("cu_seqlens")
+    if cu is None:
+        g = kda.bwd(t["q"], t["k"], t["v"], t["g_raw"], b, a, do, dfinal=df, scale=inp["scale"], initial_state=s0)
+    else:
+        g = kda.bwd_varlen(t["q"], t["k"], t["v"], t["g_raw"], b, a, do, torch.from_numpy(cu).to(dev),
+                           dfinal=df, scale=inp["scale"], initial_state=s0)
+    torch.cuda.synchronize()
+    return {n: g[n].cpu().numpy().astype(np.float64) for n in NAMES}
+
+
+def run_oracle_bwd(inp, dout, dfinal, heads=None):
+    """The oracle on all value heads, or on `heads` only (q/k heads not shared: H == H_qk)."""
+    w = oracle.widen
+    q, k, v, g, b, a = w(inp["q"]), w(inp["k"]), w(inp["v"]), w(inp["g_raw"]), inp["b"], inp["A_log"]
+    do = w(dout)
+    s0, df = inp["initial_state"], dfinal
+    B, T, H = v.shape[:3]
+    C = B if inp.get("cu_seqlens") is None else len(inp["cu_seqlens"]) - 1
+    if df is None:
+        df = np.zeros((C, H, 128, 128))
+    if heads is not None:
+        hs = list(heads)
+        q, k, v, g, b, a, do = q[:, :, hs], k[:, :, hs], v[:, :, hs], g[:, :, hs], b[:, :, hs], a[hs], do[:, :, hs]
+        s0 = None if s0 is None else s0[:, hs]
+        df = df[:, hs]
+    return KB.kda_bwd(q, k, v, g, b, a, inp["scale"], do, df, gate_per_channel=False, initial_state=s0,
+                      cu_seqlens=inp.get("cu_seqlens"))
+
+
+def compare(got, ref, label):
+    errs = {}
+    for n in NAMES:
+        r, x = ref[n], got[n]
+        assert x.shape == r.shape, (label, n, x.shape, r.shape)
+        assert np.all(np.isfinite(x)), (label, n)
+        rel = rel_l2(x, r)
+        mx = float(np.max(np.abs(x - r)) / max(np.max(np.abs(r)), 1e-30))
+        errs[n] = (rel, mx)
+    print(label, " ".join("%s %.1e/%.1e" % (n, *errs[n]) for n in NAMES), flush=True)
+    for n, (rel, mx) in errs.items():
+        assert rel <= GRAD_REL and mx <= GRAD_MAXABS, (label, n, rel, mx)
+
+
+CASES = [
+    # (label, make_inputs kwargs, dfinal std or None)
+    ("dense B=2 T=200 H=2 state", dict(B=2, T=200, H=2, H_qk=2, state_std=0.05, seed=71), 0.1),
+    ("dense B=1 T=64 H=1 no state", dict(B=1, T=64, H=1, H_qk=1, seed=72), None),
+    ("dense B=1 T=1 H=2", dict(B=1, T=1, H=2, H_qk=2, state_std=0.05, seed=73), 0.1),
+    ("grouped B=1 T=130 H=4 H_qk=2", dict(B=1, T=130, H=4, H_qk=2, state_std=0.05, seed=74), 0.1),
+    ("grouped B=1 T=97 H=6 H_qk=1", dict(B=1, T=97, H=6, H_qk=1, seed=75), 0.1),
+    ("strong decay A_log=1.5", dict(B=1, T=150, H=2, H_qk=2, A_log=1.5, state_std=0.05, seed=76), 0.1),
+    ("weak decay A_log=-4", dict(B=1, T=150, H=2, H_qk=2, A_log=-4.0, state_std=0.05, seed=77), 0.1),
+    ("varlen N=5 with empty and 1-token",
+     dict(B=1, T=230, H=2, H_qk=2, N=5, lengths=[64, 0, 1, 100, 65], state_std=0.05, seed=78), 0.1),
+]
+
+
+@pytest.mark.parametrize("label,kw,dstd", CASES, ids=[c[0] for c in CASES])
+def test_backward_matches_the_oracle(label, kw, dstd):
+    inp = make_inputs(gate_per_channel=False, **{"A_log": (-1.0, 1.0), **kw})
+    dout, dfinal = upstream(inp, kw["seed"] + 500, dstd)
+    got = run_gpu_bwd(inp, dout, dfinal)
+    ref = run_oracle_bwd(inp, dout, dfinal)
+    compare(got, ref, label)
+
+
+def test_backward_grouped_records_path():
+    # 64 chunks x 4 q/k heads = 256 (entry, q/k head) jobs: the recomputed forward takes the grouped
+    # chunk-local kernel and the records shared by the value heads of a group
+    inp = make_inputs(1, 4096, 8, 4, gate_per_channel=False, A_log=(-1.0, 1.0), state_std=0.05, seed=79)
+    dout, dfinal = upstream(inp, 579)
+    got = run_gpu_bwd(inp, dout, dfinal)
+    ref = run_oracle_bwd(inp, dout, dfinal)
+    compare(got, ref, "grouped records T=4096 H=8 H_qk=4")
+
+
+def test_backward_many_gradient_launches_sampled_heads():
+    # 128 chunks x 32 heads = 4096 (chunk, head) jobs: more than the scratch slots of one gradient
+    # launch, so the jobs run in several launches; heads 0 and 31 are checked against the oracle
+    inp = make_inputs(1, 8192, 32, 32, gate_per_channel=False, A_log=(-1.0, 1.0), state_std=0.05, seed=80)
+    dout, dfinal = upstream(inp, 580)
+    got = run_gpu_bwd(inp, dout, dfinal)
+    heads = [0, 31]
+    ref = run_oracle_bwd(inp, dout, dfinal, heads=heads)
+    sub = {n: (got[n][heads] if n == "dA_log" else got[n][:, heads] if n == "dinitial_state"
+               else got[n][:, :, heads]) for n in NAMES}
+    compare(sub, ref, "T=8192 H=32, heads 0 and 31")
+
+
+def test_backward_zero_tokens():
+    # T = 0: no token gradients; dinitial_state = dfinal, dA_log = 0
+    H = 2
+    z = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device="cuda")
+    df = torch.randn(3, H, 128, 128, device="cuda")
+    g = kda.bwd_varlen(z(1, 0, H, 128), z(1, 0, H, 128), z(1, 0, H, 128), z(1, 0, H),
+                       torch.zeros(1, 0, H, device="cuda"), torch.zeros(H, device="cuda"), z(1, 0, H, 128),
+                       torch.zeros(4, dtype=torch.int32, device="cuda"), dfinal=df)
+    torch.cuda.synchronize()
+    assert torch.equal(g["dinitial_state"], df)
+    assert torch.count_nonzero(g["dA_log"]) == 0
+
+
+def test_backward_rejects_the_per_channel_gate():
+    x = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16, device="cuda")
+    with pytest.raises(ValueError):
+        kda.bwd(x, x, x, x, torch.zeros(1, 64, 1, device="cuda"), torch.zeros(1, device="cuda"), x)
