@@ -358,25 +358,21 @@ kda_status run_decode(const void* q, const void* k, const void* v, const void* g
 
 // ---- backward (scalar gate) ------------------------------------------------
 // Workspace: the forward's (schedule, sink, chunk records), then the state
-// entering every (chunk, head), the gradient of the state leaving it, the
-// per-(chunk, head) prep blocks, and the gradient kernel's per-job scratch.
-constexpr size_t BWD_MAX_SLOTS = 2048;
-
+// entering every (chunk, head) and the gradient of the state leaving it
+// (fp16, 32 KiB each), and the adjoint's operand records (48 KiB each).
 struct BwdLayout {
   Layout F;
-  size_t states, dstates, prep, scratch, slots, total;
+  size_t states, dstates, brec, total;
 };
 
 BwdLayout bwd_layout(int n_seqs, int n_entries, int H) {
   BwdLayout L;
   L.F = layout(n_seqs, n_entries, H, false);
   const size_t jobs = (size_t)n_entries * H;
-  L.slots = std::min(jobs, BWD_MAX_SLOTS);
   L.states = L.F.total;
-  L.dstates = L.states + round_up(jobs * kda::HD * kda::HD * sizeof(float));
-  L.prep = L.dstates + round_up(jobs * kda::HD * kda::HD * sizeof(float));
-  L.scratch = L.prep + round_up(jobs * kda::PREP_FLOATS * sizeof(float));
-  L.total = L.scratch + round_up(L.slots * kda::BWD_SLOT_FLOATS * sizeof(float));
+  L.dstates = L.states + round_up(jobs * kda::HD * kda::HD * sizeof(uint16_t));
+  L.brec = L.dstates + round_up(jobs * kda::HD * kda::HD * sizeof(uint16_t));
+  L.total = L.brec + round_up(jobs * kda::BREC_BYTES);
   return L;
 }
 
@@ -436,7 +432,7 @@ kda_status run_backward(const BwdArgs& a) {
   int* order = reinterpret_cast<int*>(ws + L.F.order);
   int* err = reinterpret_cast<int*>(ws);
   uint16_t* sink = reinterpret_cast<uint16_t*>(ws + L.F.sink);
-  float* states = reinterpret_cast<float*>(ws + L.states);
+  uint16_t* states = reinterpret_cast<uint16_t*>(ws + L.states);
   (void)hipGetLastError();
   if (a.cu) {
     kda::TableParams tp{a.cu, a.n_seqs, a.T, n_entries, seqs, chunks, order};
@@ -458,15 +454,14 @@ kda_status run_backward(const BwdArgs& a) {
                     static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log,
                     static_cast<const uint16_t*>(a.dout), a.dfinal, a.scale, a.H, a.H_qk, a.cu ? -1 : a.T, chunks,
                     seqs, order, tokens > 0 ? n_entries : 0, a.n_seqs * a.H, states,
-                    reinterpret_cast<float*>(ws + L.dstates), reinterpret_cast<float*>(ws + L.prep),
-                    reinterpret_cast<float*>(ws + L.scratch), 0, a.dq, a.dk, a.dv, a.dg_raw, a.dbeta, a.dA_log,
-                    a.dinit};
-  kda::launch_bwd(bp, (size_t)tokens * a.H_qk * kda::HD, L.slots, a.stream);
+                    reinterpret_cast<uint16_t*>(ws + L.dstates), ws + L.brec, a.dq, a.dk, a.dv, a.dg_raw, a.dbeta,
+                    a.dA_log, a.dinit};
+  kda::launch_bwd(bp, (size_t)tokens * a.H_qk * kda::HD, a.stream);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   if (env_flag("KDA_LOG"))
-    std::fprintf(stderr, "[kda] bwd seqs=%d T=%d H=%d H_qk=%d entries=%d slots=%zu\n", a.n_seqs, a.T, a.H, a.H_qk,
-                 n_entries, L.slots);
+    std::fprintf(stderr, "[kda] bwd seqs=%d T=%d H=%d H_qk=%d entries=%d\n", a.n_seqs, a.T, a.H, a.H_qk,
+                 n_entries);
   return ok();
 }
 

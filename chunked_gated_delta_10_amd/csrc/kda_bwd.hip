@@ -1,6 +1,6 @@
 // kda_bwd.hip -- backward pass of the chunked forward with one decay per
-// token-head (the gated delta rule; the FlashQLA H200 results page,
-// "BACKWARD BENCHMARKS" table).
+// token-head (the gated delta rule whose backward the FlashQLA H200 results
+// page times, "BACKWARD BENCHMARKS" table).
 //
 // L = sum(dout * out) + sum(dfinal * final_state).  With a scalar decay per
 // token every decay factor of a 64-token chunk is a row scaling by
@@ -10,19 +10,29 @@
 // Gm = kn kn^T, M = lower(P . Lam), A = strict_lower(diag(b) (Gm . Lam)),
 // T = (I + A)^-1, R = V - diag(e) kn S_c and U = T diag(b) R, one chunk is
 //   O = scale (diag(e) qn S_c + M U),  S_c+1 = e_L S_c + kn^T diag(f) U.
-// Its adjoint, with dO' = scale dO and dS' the gradient of S_c+1:
-//   dU   = M^T dO' + diag(f) kn dS'
-//   dS_c = qn^T diag(e) dO' - kn^T diag(b e) T^T dU + e_L dS'
-// and the gradients of the chunk's own inputs follow from dU, dS', S_c by
-// 64 x 64 and 64 x 128 algebra (grad_kernel below).
+// Its adjoint, with dO' = scale dO and dS' the gradient of S_c+1, is linear:
+//   dS_c = Phi dS' + Bc dO'
+//   Phi = e_L I - kn^T diag(b e) T^T diag(f) kn         (128 x 128)
+//   Bc  = qn^T diag(e) - kn^T diag(b e) T^T M^T          (128 x 64)
+// so the chain over chunks (last to first) is one matrix-core step per
+// chunk, like the forward recurrence, and everything else is chunk-parallel:
+//   dU = M^T dO' + diag(f) kn dS',  Y = T^T dU,  dV = diag(b) Y,
+//   dT = dU (b R)^T,  dA = strict_lower(-T^T dT T^T),
+//   dP = lower(dO' U^T) . Lam,  dGm = diag(b) dA . Lam,
+//   dqn = diag(e) dO' S_c^T + dP kn,
+//   dkn = diag(f) U dS'^T - diag(e) dV S_c^T + (dGm + dGm^T) kn + dP^T qn,
+//   d(Lam) . Lam = (diag(b) dA . Gm + lower(dO' U^T) . P) . Lam, whose row and
+//   column sums, with the e, f and e_L terms, give dG and dg = its reverse
+//   cumulative sum; then the prologue (norms, gate, sigmoid) in reverse.
 //
-// Kernels, in launch order (the forward's chunk-local kernel and a
-// recurrence that stores the state entering every chunk run first):
-//   prep_kernel     per (chunk, head): qn, kn, the gate rows, P, Gm, M, T
-//   adjoint_kernel  per (chain, 16 value columns): the adjoint over chunks,
-//                   last to first; stores dS' of every chunk and dS_0
+// Kernels, after the forward's chunk-local kernel and a recurrence that
+// stores the state entering every chunk (fp16):
+//   coef_kernel     per (chunk, head): Phi and Bc as fp16 operand fragments
+//   adjoint_kernel  per (chain, 16 value columns): dS over chunks, last to
+//                   first; stores dS' of every chunk (fp16) and dS_0 (fp32)
 //   grad_kernel     per (chunk, head): every input gradient of the chunk
-// All arithmetic is fp32 (vector ALU, LDS-tiled products).
+// Products run on fp16 matrix cores with fp32 accumulation (the precision of
+// the forward's chunk path); T = (I + A)^-1 is formed in fp32.
 #include "kda_device.h"
 #include "kda_kernels.h"
 
@@ -30,222 +40,392 @@ namespace kda {
 
 namespace {
 
-constexpr int BT = 256;                 // threads per workgroup
-constexpr int MM = CH * CH;             // floats of a 64 x 64 block
-constexpr int MK = CH * HD;             // floats of a 64 x 128 block
-// prep block of one (chunk, head), floats
-constexpr int P_QN = 0, P_KN = P_QN + MK, P_M = P_KN + MK, P_T = P_M + MM, P_GM = P_T + MM, P_P = P_GM + MM;
-constexpr int P_ROWS = P_P + MM;
-constexpr int R_E = 0, R_F = CH, R_B = 2 * CH, R_GAM = 3 * CH, R_G = 4 * CH, R_NQ = 5 * CH, R_NK = 6 * CH,
-              R_EL = 7 * CH;  // e, f, b, Gamma, g, |q|, |k| per row; e_L and the live length after
-constexpr int PREP_FLOATS_ = P_ROWS + 8 * CH;
-static_assert(PREP_FLOATS_ == PREP_FLOATS, "prep block size");
-// grad-kernel scratch of one job, floats
-constexpr int S_DO = 0, S_R = S_DO + MK, S_KS = S_R + MK, S_SDO = S_KS + MK, S_KDS = S_SDO + MK, S_BR = S_KDS + MK,
-              S_U = S_BR + MK, S_UDS = S_U + MK, S_DU = S_UDS + MK, S_DR = S_DU + MK, S_DRS = S_DR + MK,
-              S_DQN = S_DRS + MK, S_DKN = S_DQN + MK, S_DM = S_DKN + MK, S_DT = S_DM + MM, S_X1 = S_DT + MM,
-              S_DA = S_X1 + MM, S_DG2 = S_DA + MM, S_DP = S_DG2 + MM, S_ROWS = S_DP + MM;
-constexpr int SLOT_FLOATS_ = S_ROWS + 8 * CH;
-static_assert(SLOT_FLOATS_ == BWD_SLOT_FLOATS, "scratch slot size");
+constexpr int NTH = 512;              // threads of the chunk-parallel kernels (8 waves)
+constexpr int LDW = HD + 8;           // halves per row: fp16 matrices of 128 columns
+constexpr int LDN = CH + 8;           // halves per row: fp16 matrices of 64 columns
+constexpr int LDF = CH + 4;           // floats per row: fp32 64 x 64 matrices
+constexpr int MAT_W = CH * LDW * 2;   // bytes of a 64 x 128 fp16 matrix
+constexpr int MAT_N = CH * LDN * 2;   // 64 x 64 fp16
+constexpr int MAT_NT = HD * LDN * 2;  // 128 x 64 fp16
+constexpr int MAT_F = CH * LDF * 4;   // 64 x 64 fp32
+constexpr int BR_PHI = 0;             // record: Phi fragments [8 row tiles][4 slices]
+constexpr int BR_BC = 32 * FRAG_BYTES;  // Bc fragments [8 row tiles][2 slices]
+static_assert(BR_BC + 16 * FRAG_BYTES == BREC_BYTES, "record size");
+
+struct RowsLds {
+  float e[CH], f[CH], b[CH], gam[CH], g[CH], nq[CH], nk[CH];
+  float eL;
+  int len;
+};
+// per-row sums collected across waves (grad kernel)
+struct RedLds {
+  float de[CH], df[CH], db[CH], wr[CH], wc[CH], qd[CH], kd[CH];
+  float deL[NTH / 64];
+};
 
 __device__ __forceinline__ float bf(uint16_t x) { return __uint_as_float((uint32_t)x << 16); }
 __device__ __forceinline__ float softplus_(float x) { return x > 20.f ? x : log1pf(expf(x)); }
 __device__ __forceinline__ float sigmoid_(float x) { return 1.f / (1.f + expf(-x)); }
 
-// (sequence, first token, length, chunk index) of schedule entry e
-__device__ __forceinline__ int4 entry_of(const BwdParams& p, int e) {
-  if (p.dense_T >= 0) {
-    const int T = p.dense_T, nc = (T + CH - 1) / CH, b = e / nc, c = e - b * nc;
-    return make_int4(b, b * T + c * CH, min(CH, T - c * CH), c);
-  }
-  return p.chunks[e];
+// Operand fragments (lane l: row r0 + l % 16, contraction index k0 + 8 (l / 16) + e).
+// Contraction index contiguous in X (row-major X[row][k]): one 16-byte read.
+__device__ __forceinline__ f16x8 frag_rm(const f16* X, int ld, int r0, int k0, int lane) {
+  return *reinterpret_cast<const f16x8*>(X + (r0 + (lane & 15)) * ld + k0 + 8 * (lane >> 4));
+}
+// Contraction index strided (X stored [k][row]).
+__device__ __forceinline__ f16x8 frag_cm(const f16* X, int ld, int r0, int k0, int lane) {
+  const f16* p = X + (k0 + 8 * (lane >> 4)) * ld + r0 + (lane & 15);
+  f16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = p[e * ld];
+  return v;
+}
+// Strided fragment of a row-scaled matrix: element e is s[k] X[k][r0 + l % 16], k = k0 + 8 (l / 16) + e.
+__device__ __forceinline__ f16x8 frag_cm_scaled(const f16* X, int ld, const float* s, int r0, int k0, int lane) {
+  const int k = k0 + 8 * (lane >> 4);
+  const f16* p = X + k * ld + r0 + (lane & 15);
+  f16x8 v;
+#pragma unroll
+  for (int e = 0; e < 8; ++e) v[e] = (f16)(s[k + e] * (float)p[e * ld]);
+  return v;
 }
 
-// C = alpha op(A) op(B) (+ C when ACC) for the whole workgroup; fp32, row-major,
-// C with leading dimension N.  op(A) is M x K (TA: A is stored K x M), op(B) is
-// K x N (TB: B is stored N x K).  sh: LDS of 16 (M + N) floats.
-template <int M, int N, int K, bool TA, bool TB, bool ACC>
-__device__ void wg_gemm(float* __restrict__ C, const float* __restrict__ A, int lda, const float* __restrict__ B,
-                        int ldb, float alpha, float* sh) {
-  constexpr int TM = M / 16, TN = N / 16;
-  const int t = threadIdx.x, tr = t >> 4, tc = t & 15;
-  float acc[TM][TN];
-#pragma unroll
-  for (int i = 0; i < TM; ++i)
-#pragma unroll
-    for (int j = 0; j < TN; ++j) acc[i][j] = 0.f;
-  float* As = sh;           // [16][M]
-  float* Bs = sh + 16 * M;  // [16][N]
-  for (int k0 = 0; k0 < K; k0 += 16) {
-    for (int i = t; i < M * 16; i += BT) {
-      if (TA) {
-        const int m = i % M, kk = i / M;
-        As[kk * M + m] = A[(size_t)(k0 + kk) * lda + m];
-      } else {
-        const int kk = i & 15, m = i >> 4;
-        As[kk * M + m] = A[(size_t)m * lda + k0 + kk];
-      }
+// ---------------------------------------------------------------------------
+// Shared prologue of the chunk-parallel kernels.
+// ---------------------------------------------------------------------------
+// (first token, length) of schedule entry e
+__device__ __forceinline__ int2 entry_of(const BwdParams& p, int e) {
+  if (p.dense_T >= 0) {
+    const int T = p.dense_T, nc = (T + CH - 1) / CH, b = e / nc, c = e - b * nc;
+    return make_int2(b * T + c * CH, min(CH, T - c * CH));
+  }
+  const int4 ce = p.chunks[e];
+  return make_int2(ce.y, ce.z);
+}
+
+// Gate rows and normalised q, k rows (fp16, rows past the chunk's end zero).
+__device__ void load_chunk(const BwdParams& p, int tok0, int len, int h, int hq, f16* QN, f16* KN, RowsLds& R) {
+  const int t = threadIdx.x;
+  if (t < CH) {
+    const bool live = t < len;
+    float g = 0.f, b = 0.f;
+    if (live) {
+      const size_t th = (size_t)(tok0 + t) * p.H + h;
+      g = -expf(p.A_log[h]) * softplus_(bf(p.g_raw[th]));
+      b = sigmoid_(p.beta[th]);
     }
-    for (int i = t; i < N * 16; i += BT) {
-      if (TB) {
-        const int kk = i & 15, n = i >> 4;
-        Bs[kk * N + n] = B[(size_t)n * ldb + k0 + kk];
-      } else {
-        const int n = i % N, kk = i / N;
-        Bs[kk * N + n] = B[(size_t)(k0 + kk) * ldb + n];
-      }
+    float G = g;  // inclusive scan over the 64 lanes
+#pragma unroll
+    for (int o = 1; o < CH; o <<= 1) {
+      const float y = __shfl_up(G, o);
+      if (t >= o) G += y;
     }
-    __syncthreads();
-#pragma unroll 4
-    for (int kk = 0; kk < 16; ++kk) {
-      float a[TM], b[TN];
-#pragma unroll
-      for (int i = 0; i < TM; ++i) a[i] = As[kk * M + tr * TM + i];
-#pragma unroll
-      for (int j = 0; j < TN; ++j) b[j] = Bs[kk * N + tc * TN + j];
-#pragma unroll
-      for (int i = 0; i < TM; ++i)
-#pragma unroll
-        for (int j = 0; j < TN; ++j) acc[i][j] += a[i] * b[j];
+    const float GL = __shfl(G, max(len, 1) - 1);
+    R.g[t] = g;
+    R.b[t] = b;
+    R.gam[t] = G;
+    R.e[t] = expf(G);
+    R.f[t] = expf(GL - G);
+    if (t == 0) {
+      R.eL = expf(GL);
+      R.len = len;
     }
-    __syncthreads();
+  }
+  // thread -> row t / 8, channels 16 (t % 8) .. + 15
+  const int r = t >> 3, c0 = (t & 7) * 16;
+  float qv[16], kv[16];
+  if (r < len) {
+    const size_t base = ((size_t)(tok0 + r) * p.H_qk + hq) * HD + c0;
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.q + base), qv);
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.q + base + 8), qv + 8);
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.k + base), kv);
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(p.k + base + 8), kv + 8);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 16; ++i) qv[i] = kv[i] = 0.f;
+  }
+  float sq = 0.f, sk = 0.f;
+#pragma unroll
+  for (int i = 0; i < 16; ++i) {
+    sq += qv[i] * qv[i];
+    sk += kv[i] * kv[i];
   }
 #pragma unroll
-  for (int i = 0; i < TM; ++i)
+  for (int o = 1; o < 8; o <<= 1) {
+    sq += __shfl_xor(sq, o);
+    sk += __shfl_xor(sk, o);
+  }
+  const float nq = sqrtf(sq + 1e-6f), nk = sqrtf(sk + 1e-6f), iq = 1.f / nq, ik = 1.f / nk;
 #pragma unroll
-    for (int j = 0; j < TN; ++j) {
-      float* c = C + (size_t)(tr * TM + i) * N + tc * TN + j;
-      *c = ACC ? *c + alpha * acc[i][j] : alpha * acc[i][j];
+  for (int i = 0; i < 16; ++i) {
+    qv[i] *= iq;
+    kv[i] *= ik;
+  }
+  *reinterpret_cast<f16x8*>(QN + r * LDW + c0) = to_f16x8(qv);
+  *reinterpret_cast<f16x8*>(QN + r * LDW + c0 + 8) = to_f16x8(qv + 8);
+  *reinterpret_cast<f16x8*>(KN + r * LDW + c0) = to_f16x8(kv);
+  *reinterpret_cast<f16x8*>(KN + r * LDW + c0 + 8) = to_f16x8(kv + 8);
+  if ((t & 7) == 0) {
+    R.nq[r] = nq;
+    R.nk[r] = nk;
+  }
+}
+
+// (I + N)^-1 of a strictly lower 16 x 16 block on fp32 matrix cores: blocked
+// forward substitution with block sizes doubling 1 -> 2 -> 4 -> 8 -> 16
+// (D_2k = D_k - D_k M_k D_k, every intermediate a block of the inverse or of
+// N).  Nc, NT: N and N^T in C layout; result in C layout.
+__device__ __forceinline__ f32x4 mul_cc_(const f32x4& XT, const f32x4& Y) {
+  f32x4 z = mma_f32(XT[0], Y[0], zero4());
+  z = mma_f32(XT[1], Y[1], z);
+  z = mma_f32(XT[2], Y[2], z);
+  return mma_f32(XT[3], Y[3], z);
+}
+__device__ __forceinline__ f32x4 lower_inverse16(const f32x4& Nc, const f32x4& NT, int l16, int lg) {
+  f32x4 D, DT;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int r = 4 * lg + j, c = l16;
+    const float eye = r == c ? 1.f : 0.f;
+    const bool in1 = (r >> 1) == (c >> 1) && r != c;
+    D[j] = eye - (in1 ? Nc[j] : 0.f);
+    DT[j] = eye - (in1 ? NT[j] : 0.f);
+  }
+#pragma unroll
+  for (int k = 2; k < SUB; k *= 2) {
+    f32x4 MT;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const int r = 4 * lg + j, c = l16;
+      MT[j] = ((r / (2 * k)) == (c / (2 * k)) && (r / k) != (c / k)) ? NT[j] : 0.f;
     }
-  __syncthreads();  // C complete for the next product
+    const f32x4 P = mul_cc_(MT, D);
+    const f32x4 Q = mul_cc_(DT, P);
+    if (2 * k < SUB) DT = DT - mul_cc_(P, DT);
+    D = D - Q;
+  }
+  return D;
+}
+
+// Off-diagonal 16 x 16 blocks of T in block column a: T_ba = -T_bb sum_{a<=j<b} A_bj T_ja.
+// The contraction index of product jj is 4 lg + jj, so C layout is the B operand in place.
+template <int A>
+__device__ __forceinline__ void t_column(const float* AF, float* TF, f32x4 Td, int l16, int lg) {
+  f32x4 Tc[NSUB];
+  Tc[A] = Td;
+#pragma unroll
+  for (int b = A + 1; b < NSUB; ++b) {
+    f32x4 X = zero4();
+#pragma unroll
+    for (int j = A; j < b; ++j) {
+      const float4 av = *reinterpret_cast<const float4*>(&AF[(SUB * b + l16) * LDF + SUB * j + 4 * lg]);
+      X = mma_f32(av.x, Tc[j][0], X);
+      X = mma_f32(av.y, Tc[j][1], X);
+      X = mma_f32(av.z, Tc[j][2], X);
+      X = mma_f32(av.w, Tc[j][3], X);
+    }
+    const float4 tb = *reinterpret_cast<const float4*>(&TF[(SUB * b + l16) * LDF + SUB * b + 4 * lg]);
+    f32x4 Y = mma_f32(tb.x, X[0], zero4());
+    Y = mma_f32(tb.y, X[1], Y);
+    Y = mma_f32(tb.z, X[2], Y);
+    Y = mma_f32(tb.w, X[3], Y);
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      Tc[b][jj] = -Y[jj];
+      TF[(SUB * b + 4 * lg + jj) * LDF + SUB * A + l16] = -Y[jj];
+    }
+  }
+}
+
+// P = qn kn^T and Gm = kn kn^T on this wave's tiles (row tile w / 2, column
+// tiles 2 (w % 2) + j), kept in registers; M = lower(P . Lam) to Mt
+// (transposed) and/or Mr (row-major); A = strict_lower(b Gm . Lam) to AF;
+// then T = (I + A)^-1 into T16 (fp16, row-major).  Ends with a barrier.
+__device__ void gram_and_T(const f16* QN, const f16* KN, const RowsLds& R, f16* Mt, f16* Mr, float* AF, float* TF,
+                           f16* T16, f32x4 (&P)[2], f32x4 (&Gm)[2]) {
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63, l16 = lane & 15, lg = lane >> 4;
+  const int rt = w >> 1, ct0 = 2 * (w & 1);
+#pragma unroll
+  for (int j = 0; j < 2; ++j) P[j] = Gm[j] = zero4();
+#pragma unroll
+  for (int s = 0; s < HD / 32; ++s) {
+    const f16x8 aq = frag_rm(QN, LDW, 16 * rt, 32 * s, lane), ak = frag_rm(KN, LDW, 16 * rt, 32 * s, lane);
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const f16x8 bk = frag_rm(KN, LDW, 16 * (ct0 + j), 32 * s, lane);
+      P[j] = mma_f16(aq, bk, P[j]);
+      Gm[j] = mma_f16(ak, bk, Gm[j]);
+    }
+  }
+#pragma unroll
+  for (int j = 0; j < 2; ++j) {
+    const int c = 16 * (ct0 + j) + l16;
+    f16x4 mcol;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 16 * rt + 4 * lg + jj;
+      const float lam = r >= c ? expf(fminf(R.gam[r] - R.gam[c], 0.f)) : 0.f;
+      const float m = P[j][jj] * lam;
+      mcol[jj] = (f16)m;
+      if (Mr) Mr[r * LDN + c] = (f16)m;
+      AF[r * LDF + c] = r > c ? R.b[r] * Gm[j][jj] * lam : 0.f;
+    }
+    if (Mt) *reinterpret_cast<f16x4*>(Mt + c * LDN + 16 * rt + 4 * lg) = mcol;
+  }
+  __syncthreads();
+  f32x4 Td = zero4();
+  if (w < NSUB) {  // diagonal blocks
+    const int n = w;
+    f32x4 Nc, NT;
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      Nc[j] = AF[(SUB * n + 4 * lg + j) * LDF + SUB * n + l16];
+      NT[j] = AF[(SUB * n + l16) * LDF + SUB * n + 4 * lg + j];
+    }
+    Td = lower_inverse16(Nc, NT, l16, lg);
+#pragma unroll
+    for (int j = 0; j < 4; ++j) TF[(SUB * n + 4 * lg + j) * LDF + SUB * n + l16] = Td[j];
+  }
+  __syncthreads();
+  if (w == 0) t_column<0>(AF, TF, Td, l16, lg);
+  else if (w == 1) t_column<1>(AF, TF, Td, l16, lg);
+  else if (w == 2) t_column<2>(AF, TF, Td, l16, lg);
+  __syncthreads();
+  for (int i = t; i < CH * CH; i += NTH) {
+    const int r = i >> 6, c = i & 63;
+    T16[r * LDN + c] = (f16)((r >> 4) >= (c >> 4) ? TF[r * LDF + c] : 0.f);
+  }
+  __syncthreads();
 }
 
 }  // namespace
 
 // ---------------------------------------------------------------------------
-// Per (chunk, head): normalised rows, gate rows, Gram matrices, M and T.
+// coef_kernel: per (chunk, head), Phi and Bc as A-operand fragments of the
+// adjoint's products.  A fragment (row tile m, slice s) holds, for lane l,
+// row 16 m + l % 16 and contraction indices 32 s + 4 (l / 16) + e (e < 4) and
+// 32 s + 16 + 4 (l / 16) + e - 4 (e >= 4): the order in which the C layout of
+// two stacked 16-row tiles is a B operand (kda_device.h).  Computed as
+//   Y1 = T^T diag(f) kn,  Phi^T = e_L I - Y1^T diag(b e) kn,
+//   Z1 = T diag(b e) kn,  Bc^T = diag(e) qn - M Z1,
+// so that the C layout of Phi^T and Bc^T is the fragment order of Phi and Bc.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(BT) void bwd_prep_kernel(BwdParams p) {
-  __shared__ float sQ[CH][HD + 1], sK[CH][HD + 1];
-  __shared__ float sA[CH][CH + 1], sT[CH][CH + 1];
-  __shared__ float sRow[8 * CH];
+__global__ __launch_bounds__(NTH) void bwd_coef_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * MAT_W + 2 * MAT_N + 2 * MAT_NT];
+  __shared__ RowsLds R;
+  __shared__ float be[CH];
+  f16* QN = reinterpret_cast<f16*>(smem);
+  f16* KN = reinterpret_cast<f16*>(smem + MAT_W);
+  f16* M16 = reinterpret_cast<f16*>(smem + 2 * MAT_W);
+  f16* T16 = reinterpret_cast<f16*>(smem + 2 * MAT_W + MAT_N);
+  uint8_t* X = smem + 2 * MAT_W + 2 * MAT_N;  // AF, TF; then Y1t, Z1t
+  float* AF = reinterpret_cast<float*>(X);
+  float* TF = reinterpret_cast<float*>(X + MAT_F);
+  f16* Y1t = reinterpret_cast<f16*>(X);
+  f16* Z1t = reinterpret_cast<f16*>(X + MAT_NT);
+  static_assert(2 * MAT_F <= 2 * MAT_NT, "fp32 solve fits the region");
+
   const int job = blockIdx.x, e = job / p.H, h = job - e * p.H, hq = h / (p.H / p.H_qk);
-  const int4 ce = entry_of(p, e);
-  const int len = ce.z, tok0 = ce.y;
-  float* blk = p.prep + (size_t)job * PREP_FLOATS;
-  const int t = threadIdx.x, r = t >> 2, qd = t & 3;
-  // rows: load, normalise (4 threads per row, 32 channels each)
-  {
-    float qv[32], kv[32], sq = 0.f, sk = 0.f;
-    const bool live = r < len;
-    const size_t row = (size_t)(tok0 + (live ? r : 0)) * p.H_qk + hq;
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      qv[i] = live ? bf(p.q[row * HD + 32 * qd + i]) : 0.f;
-      kv[i] = live ? bf(p.k[row * HD + 32 * qd + i]) : 0.f;
-      sq += qv[i] * qv[i];
-      sk += kv[i] * kv[i];
-    }
-    sq += __shfl_xor(sq, 1);
-    sq += __shfl_xor(sq, 2);
-    sk += __shfl_xor(sk, 1);
-    sk += __shfl_xor(sk, 2);
-    const float nq = sqrtf(sq + 1e-6f), nk = sqrtf(sk + 1e-6f);
-#pragma unroll
-    for (int i = 0; i < 32; ++i) {
-      sQ[r][32 * qd + i] = qv[i] / nq;
-      sK[r][32 * qd + i] = kv[i] / nk;
-      blk[P_QN + r * HD + 32 * qd + i] = qv[i] / nq;
-      blk[P_KN + r * HD + 32 * qd + i] = kv[i] / nk;
-    }
-    if (qd == 0) {
-      sRow[R_NQ + r] = nq;
-      sRow[R_NK + r] = nk;
-    }
-  }
-  if (t < CH) {  // gate and write strength of row t
-    const bool live = t < len;
-    const size_t th = (size_t)(tok0 + (live ? t : 0)) * p.H + h;
-    sRow[R_G + t] = live ? -expf(p.A_log[h]) * softplus_(bf(p.g_raw[th])) : 0.f;
-    sRow[R_B + t] = live ? sigmoid_(p.beta[th]) : 0.f;
-  }
+  const int2 ce = entry_of(p, e);
+  const int tok0 = ce.x, len = ce.y;
+  if (len <= 0) return;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63, l16 = lane & 15, lg = lane >> 4;
+  load_chunk(p, tok0, len, h, hq, QN, KN, R);
   __syncthreads();
-  if (t == 0) {  // cumulative gate and the chunk-end factors
-    float G = 0.f;
-    for (int i = 0; i < CH; ++i) {
-      G += sRow[R_G + i];
-      sRow[R_GAM + i] = G;
-    }
-    const float GL = sRow[R_GAM + max(len, 1) - 1];
-    sRow[R_EL] = expf(GL);
-    sRow[R_EL + 1] = (float)len;
-  }
-  __syncthreads();
-  if (t < CH) {
-    sRow[R_E + t] = expf(sRow[R_GAM + t]);
-    sRow[R_F + t] = expf(sRow[R_GAM + max(len, 1) - 1] - sRow[R_GAM + t]);
-  }
-  // P = qn kn^T, Gm = kn kn^T; M = lower(P . Lam), A = strict_lower(b (Gm . Lam))
+  if (t < CH) be[t] = R.b[t] * R.e[t];
+  f32x4 P[2], Gm[2];
+  gram_and_T(QN, KN, R, nullptr, M16, AF, TF, T16, P, Gm);
+
+  // Y1 = T^T diag(f) kn and Z1 = T diag(b e) kn: rows i (4 tiles), columns d (tile w); K = 64
   {
-    const int r0 = (t >> 4) * 4, c0 = (t & 15) * 4;
-    float pp[4][4] = {}, gg[4][4] = {};
-    for (int k = 0; k < HD; ++k) {
-      float a[4], b[4], c[4];
+    f32x4 Y1[4], Z1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Y1[i] = Z1[i] = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f16x8 bf_ = frag_cm_scaled(KN, LDW, R.f, 16 * w, 32 * s, lane);
+      const f16x8 bb = frag_cm_scaled(KN, LDW, be, 16 * w, 32 * s, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) {
-        a[i] = sQ[r0 + i][k];
-        b[i] = sK[r0 + i][k];
-        c[i] = sK[c0 + i][k];
+        Y1[i] = mma_f16(frag_cm(T16, LDN, 16 * i, 32 * s, lane), bf_, Y1[i]);
+        Z1[i] = mma_f16(frag_rm(T16, LDN, 16 * i, 32 * s, lane), bb, Z1[i]);
       }
-#pragma unroll
-      for (int i = 0; i < 4; ++i)
-#pragma unroll
-        for (int j = 0; j < 4; ++j) {
-          pp[i][j] += a[i] * c[j];
-          gg[i][j] += b[i] * c[j];
-        }
     }
-    __syncthreads();  // sRow e, f written
+    // (the solve's fp32 scratch is dead: gram_and_T ended with a barrier)
+    const int d = 16 * w + l16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        const int ri = r0 + i, cj = c0 + j;
-        const float lam = ri >= cj ? expf(fminf(sRow[R_GAM + ri] - sRow[R_GAM + cj], 0.f)) : 0.f;
-        blk[P_P + ri * CH + cj] = pp[i][j];
-        blk[P_GM + ri * CH + cj] = gg[i][j];
-        blk[P_M + ri * CH + cj] = pp[i][j] * lam;
-        sA[ri][cj] = ri > cj ? sRow[R_B + ri] * gg[i][j] * lam : 0.f;
-      }
-  }
-  __syncthreads();
-  if (t < CH) {  // T = (I + A)^-1 by forward substitution, thread t owns column t
-    const int j = t;
-    for (int i = 0; i < CH; ++i) {
-      float v = 0.f;
-      if (i == j) {
-        v = 1.f;
-      } else if (i > j) {
-        for (int m = j; m < i; ++m) v -= sA[i][m] * sT[m][j];
-      }
-      sT[i][j] = v;
+    for (int i = 0; i < 4; ++i) {
+      *reinterpret_cast<f16x4*>(Y1t + d * LDN + 16 * i + 4 * lg) =
+          f16x4{(f16)Y1[i][0], (f16)Y1[i][1], (f16)Y1[i][2], (f16)Y1[i][3]};
+      *reinterpret_cast<f16x4*>(Z1t + d * LDN + 16 * i + 4 * lg) =
+          f16x4{(f16)Z1[i][0], (f16)Z1[i][1], (f16)Z1[i][2], (f16)Z1[i][3]};
     }
   }
   __syncthreads();
-  for (int i = t; i < MM; i += BT) blk[P_T + i] = sT[i / CH][i % CH];
-  for (int i = t; i < 8 * CH; i += BT) blk[P_ROWS + i] = sRow[i];
+  uint8_t* rec = p.brec + (size_t)job * BREC_BYTES;
+  // Phi^T: rows d' (8 tiles), columns d (tile w); K = 64 over tokens
+  {
+    f32x4 A[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) A[i] = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f16x8 bb = frag_cm_scaled(KN, LDW, be, 16 * w, 32 * s, lane);
+#pragma unroll
+      for (int i = 0; i < 8; ++i) A[i] = mma_f16(frag_rm(Y1t, LDN, 16 * i, 32 * s, lane), bb, A[i]);
+    }
+    const int d = 16 * w + l16;
+    const float eL = R.eL;
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      f16x8 o;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int d0 = 32 * s + 4 * lg + jj, d1 = d0 + 16;
+        o[jj] = (f16)((d0 == d ? eL : 0.f) - A[2 * s][jj]);
+        o[4 + jj] = (f16)((d1 == d ? eL : 0.f) - A[2 * s + 1][jj]);
+      }
+      *reinterpret_cast<f16x8*>(rec + BR_PHI + (w * 4 + s) * FRAG_BYTES + lane * 16) = o;
+    }
+  }
+  // Bc^T = diag(e) qn - M Z1: rows i (4 tiles), columns d (tile w); K = 64
+  {
+    f32x4 B[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) B[i] = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f16x8 bz = frag_rm(Z1t, LDN, 16 * w, 32 * s, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) B[i] = mma_f16(frag_rm(M16, LDN, 16 * i, 32 * s, lane), bz, B[i]);
+    }
+    const int d = 16 * w + l16;
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      f16x8 o;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int i0 = 32 * s + 4 * lg + jj, i1 = i0 + 16;
+        o[jj] = (f16)(R.e[i0] * (float)QN[i0 * LDW + d] - B[2 * s][jj]);
+        o[4 + jj] = (f16)(R.e[i1] * (float)QN[i1 * LDW + d] - B[2 * s + 1][jj]);
+      }
+      *reinterpret_cast<f16x8*>(rec + BR_BC + (w * 2 + s) * FRAG_BYTES + lane * 16) = o;
+    }
+  }
 }
 
 // ---------------------------------------------------------------------------
-// Per (chain, 16 value columns): the adjoint of the chunk recurrence, last
-// chunk first.  dS (128 x 16) lives in LDS.
+// adjoint_kernel: per (chain, 16 value columns), dS = Phi dS' + Bc dO' over
+// the chain's chunks, last first.  Wave w holds rows 32 w .. 32 w + 31 of dS
+// in C layout (fp32); the four waves' rows, converted to fp16, are the B
+// operand of the next step (published through LDS, one barrier per chunk).
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(BT) void bwd_adjoint_kernel(BwdParams p) {
-  __shared__ float sQ[CH][HD + 1], sK[CH][HD + 1];
-  __shared__ float sM[CH][CH + 1], sT[CH][CH + 1];
-  __shared__ float sdS[HD][17], sdO[CH][17], sdU[CH][17], sZ[CH][17];
-  __shared__ float sRow[8 * CH];
-  const int x = blockIdx.x, vt = x & 7, ch = x >> 3;
+__global__ __launch_bounds__(256) void bwd_adjoint_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) f16x8 sB[2][4][64];
+  const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
+  // the 8 workgroups of a chain share an XCD (blocks are dealt to XCDs round robin)
+  const int x = blockIdx.x, xcd = x & 7, y = x >> 3, vt = y & 7, ch = (y >> 3) * 8 + xcd;
+  if (ch >= p.n_chains) return;
   const int h = ch % p.H;
   int n, tok0, len, chunk0;
   if (p.dense_T >= 0) {
@@ -261,296 +441,466 @@ __global__ __launch_bounds__(BT) void bwd_adjoint_kernel(BwdParams p) {
     chunk0 = sq.z;
   }
   const int nch = max(0, min((len + CH - 1) / CH, p.n_entries - chunk0));
-  const int v0 = 16 * vt, t = threadIdx.x;
-  const size_t sbase = ((size_t)n * p.H + h) * HD * HD;
-  // dS <- dfinal (columns v0 .. v0 + 15): thread -> column t / 16, keys 8 (t % 16) .. + 7
-  const int cv = t >> 4, k8 = (t & 15) * 8;
+  const int v = 16 * vt + l16;
+  const size_t sbase = ((size_t)n * p.H + h) * HD * HD + (size_t)v * HD;
+  f32x4 dS[2];
 #pragma unroll
-  for (int i = 0; i < 8; ++i)
-    sdS[k8 + i][cv] = p.dfinal ? p.dfinal[sbase + (size_t)(v0 + cv) * HD + k8 + i] : 0.f;
-  for (int c = nch - 1; c >= 0; --c) {
-    const size_t e = (size_t)(chunk0 + c);
-    const float* blk = p.prep + (e * p.H + h) * PREP_FLOATS;
-    __syncthreads();  // the previous chunk's dS is complete
-    // dS' of this chunk (the gradient of the state leaving it)
-    float* ds = p.dstates + (e * p.H + h) * HD * HD + (size_t)(v0 + cv) * HD + k8;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) ds[i] = sdS[k8 + i][cv];
-    for (int i = t; i < MK; i += BT) {
-      sQ[i / HD][i % HD] = blk[P_QN + i];
-      sK[i / HD][i % HD] = blk[P_KN + i];
-    }
-    for (int i = t; i < MM; i += BT) {
-      sM[i / CH][i % CH] = blk[P_M + i];
-      sT[i / CH][i % CH] = blk[P_T + i];
-    }
-    for (int i = t; i < 8 * CH; i += BT) sRow[i] = blk[P_ROWS + i];
-    const int L = min(CH, len - c * CH);
-    for (int i = t; i < CH * 16; i += BT) {
-      const int r = i >> 4, v = i & 15;
-      sdO[r][v] = r < L ? p.scale * bf(p.dout[((size_t)(tok0 + c * CH + r) * p.H + h) * HD + v0 + v]) : 0.f;
-    }
-    __syncthreads();
-    // dU = M^T dO' + diag(f) kn dS     (thread: row r, columns 4 cq .. + 3)
-    {
-      const int r = t >> 2, c4 = (t & 3) * 4;
-      float x[4] = {}, m[4] = {};
-      for (int k = 0; k < HD; ++k) {
-        const float a = sK[r][k];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) x[j] += a * sdS[k][c4 + j];
-      }
-      for (int i = 0; i < CH; ++i) {
-        const float a = sM[i][r];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) m[j] += a * sdO[i][c4 + j];
-      }
-      const float f = sRow[R_F + r];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) sdU[r][c4 + j] = m[j] + f * x[j];
-    }
-    __syncthreads();
-    // Z = diag(b e) T^T dU;  dO' rows scaled by e for the next product
-    {
-      const int r = t >> 2, c4 = (t & 3) * 4;
-      float z[4] = {};
-      for (int i = 0; i < CH; ++i) {
-        const float a = sT[i][r];
-#pragma unroll
-        for (int j = 0; j < 4; ++j) z[j] += a * sdU[i][c4 + j];
-      }
-      const float be = sRow[R_B + r] * sRow[R_E + r], er = sRow[R_E + r];
-#pragma unroll
-      for (int j = 0; j < 4; ++j) {
-        sZ[r][c4 + j] = be * z[j];
-        sdO[r][c4 + j] *= er;
-      }
-    }
-    __syncthreads();
-    // dS <- qn^T diag(e) dO' - kn^T Z + e_L dS     (thread: key k, columns 8 cw .. + 7)
-    {
-      const int k = t >> 1, c8 = (t & 1) * 8;
-      float a8[8] = {};
-      for (int r = 0; r < CH; ++r) {
-        const float qa = sQ[r][k], ka = sK[r][k];
-#pragma unroll
-        for (int j = 0; j < 8; ++j) a8[j] += qa * sdO[r][c8 + j] - ka * sZ[r][c8 + j];
-      }
-      const float eL = sRow[R_EL];
-#pragma unroll
-      for (int j = 0; j < 8; ++j) sdS[k][c8 + j] = a8[j] + eL * sdS[k][c8 + j];
+  for (int i = 0; i < 2; ++i) {
+    const int d = 32 * w + 16 * i + 4 * lg;
+    if (p.dfinal) {
+      const float4 x4 = *reinterpret_cast<const float4*>(p.dfinal + sbase + d);
+      dS[i] = f32x4{x4.x, x4.y, x4.z, x4.w};
+    } else {
+      dS[i] = zero4();
     }
   }
-  __syncthreads();
+  const size_t vstride = (size_t)p.H * HD;
+  for (int c = nch - 1; c >= 0; --c) {
+    const size_t eh = (size_t)(chunk0 + c) * p.H + h;
+    const uint8_t* rec = p.brec + eh * BREC_BYTES;
+    // dS' of this chunk
+    f16* ds = reinterpret_cast<f16*>(p.dstates) + eh * HD * HD + (size_t)v * HD;
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<f16x4*>(ds + 32 * w + 16 * i + 4 * lg) =
+          f16x4{(f16)dS[i][0], (f16)dS[i][1], (f16)dS[i][2], (f16)dS[i][3]};
+    sB[c & 1][w][lane] = f16x8{(f16)dS[0][0], (f16)dS[0][1], (f16)dS[0][2], (f16)dS[0][3],
+                               (f16)dS[1][0], (f16)dS[1][1], (f16)dS[1][2], (f16)dS[1][3]};
+    // dO' as a B operand: tokens in fragment order, rows past the chunk's end zero
+    const int L = min(CH, len - c * CH);
+    const uint16_t* dob = p.dout + ((size_t)tok0 + (size_t)c * CH) * vstride + (size_t)h * HD + v;
+    f16x8 dO[2];
+#pragma unroll
+    for (int s = 0; s < 2; ++s)
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        const int tk = 32 * s + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
+        dO[s][e] = (f16)(tk < L ? p.scale * bf(dob[(size_t)tk * vstride]) : 0.f);
+      }
+    f16x8 Af[2][4], Bf[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+#pragma unroll
+      for (int s = 0; s < 4; ++s)
+        Af[i][s] = *reinterpret_cast<const f16x8*>(rec + BR_PHI + ((2 * w + i) * 4 + s) * FRAG_BYTES + lane * 16);
+#pragma unroll
+      for (int s = 0; s < 2; ++s)
+        Bf[i][s] = *reinterpret_cast<const f16x8*>(rec + BR_BC + ((2 * w + i) * 2 + s) * FRAG_BYTES + lane * 16);
+    }
+    __syncthreads();  // every wave's rows of dS' published
+    f16x8 sb[4];
+#pragma unroll
+    for (int s = 0; s < 4; ++s) sb[s] = sB[c & 1][s][lane];
+#pragma unroll
+    for (int i = 0; i < 2; ++i) {
+      f32x4 a = zero4();
+#pragma unroll
+      for (int s = 0; s < 4; ++s) a = mma_f16(Af[i][s], sb[s], a);
+#pragma unroll
+      for (int s = 0; s < 2; ++s) a = mma_f16(Bf[i][s], dO[s], a);
+      dS[i] = a;
+    }
+  }
   if (p.dinit) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i) p.dinit[sbase + (size_t)(v0 + cv) * HD + k8 + i] = sdS[k8 + i][cv];
+    for (int i = 0; i < 2; ++i)
+      *reinterpret_cast<float4*>(p.dinit + sbase + 32 * w + 16 * i + 4 * lg) =
+          make_float4(dS[i][0], dS[i][1], dS[i][2], dS[i][3]);
   }
 }
 
 // ---------------------------------------------------------------------------
-// Per (chunk, head): every gradient of the chunk's inputs.  Intermediates of
-// the job live in its scratch slot (L2), products through wg_gemm.
+// grad_kernel: per (chunk, head), every gradient of the chunk's inputs.
+// Eight waves; 64 x 128 results are split by 16-column tiles (wave w: tile
+// w, all 64 rows), 64 x 64 ones by tiles (row tile w / 2, column tiles
+// 2 (w % 2) + j), so a wave's registers hold the same elements from product
+// to product.  S_c and dS' are read from global memory (fp16) as operands.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(BT) void bwd_grad_kernel(BwdParams p) {
-  __shared__ float sh[16 * (CH + HD)];
-  __shared__ float red[BT];
-  const int job = p.job0 + blockIdx.x, e = job / p.H, h = job - e * p.H, G = p.H / p.H_qk, hq = h / G;
-  const int4 ce = entry_of(p, e);
-  const int len = ce.z, tok0 = ce.y;
-  if (len <= 0) return;  // uniform over the workgroup
-  const float* blk = p.prep + (size_t)job * PREP_FLOATS;
-  float* sc = p.scratch + (size_t)blockIdx.x * BWD_SLOT_FLOATS;
-  const float* QN = blk + P_QN;
-  const float* KN = blk + P_KN;
-  const float* rows = blk + P_ROWS;
-  const float* St = p.states + ((size_t)e * p.H + h) * HD * HD;    // [V][K]: S^T
-  const float* dSt = p.dstates + ((size_t)e * p.H + h) * HD * HD;  // [V][K]: dS'^T
-  const int t = threadIdx.x;
-  // dO' and V (zero past the chunk's end)
-  for (int i = t; i < MK; i += BT) {
-    const int r = i / HD, c = i % HD;
-    const size_t at = ((size_t)(tok0 + min(r, len - 1)) * p.H + h) * HD + c;
-    sc[S_DO + i] = r < len ? p.scale * bf(p.dout[at]) : 0.f;
-    sc[S_R + i] = r < len ? bf(p.v[at]) : 0.f;
-  }
-  __syncthreads();
-  wg_gemm<CH, HD, HD, false, true, false>(sc + S_KS, KN, HD, St, HD, 1.f, sh);     // kn S
-  wg_gemm<CH, HD, HD, false, false, false>(sc + S_SDO, sc + S_DO, HD, St, HD, 1.f, sh);  // dO' S^T
-  wg_gemm<CH, HD, HD, false, true, false>(sc + S_KDS, KN, HD, dSt, HD, 1.f, sh);   // kn dS'
-  for (int i = t; i < MK; i += BT) {  // R = V - diag(e) kn S;  b R
-    const int r = i / HD;
-    const float R = sc[S_R + i] - rows[R_E + r] * sc[S_KS + i];
-    sc[S_R + i] = R;
-    sc[S_BR + i] = rows[R_B + r] * R;
-  }
-  __syncthreads();
-  wg_gemm<CH, HD, CH, false, false, false>(sc + S_U, blk + P_T, CH, sc + S_BR, HD, 1.f, sh);    // U = T b R
-  wg_gemm<CH, HD, HD, false, false, false>(sc + S_UDS, sc + S_U, HD, dSt, HD, 1.f, sh);         // U dS'^T
-  for (int i = t; i < MK; i += BT) sc[S_DU + i] = rows[R_F + i / HD] * sc[S_KDS + i];
-  __syncthreads();
-  wg_gemm<CH, HD, CH, true, false, true>(sc + S_DU, blk + P_M, CH, sc + S_DO, HD, 1.f, sh);     // += M^T dO'
-  wg_gemm<CH, HD, CH, true, false, false>(sc + S_DR, blk + P_T, CH, sc + S_DU, HD, 1.f, sh);    // Y = T^T dU
-  // dR = diag(b) Y (= dV), and db1 = rowsum(Y . R)
-  float* srow = sc + S_ROWS;  // de, df, db, dG
+namespace {
+// LDS of the grad kernel, bytes
+constexpr int G_QN = 0, G_KN = G_QN + MAT_W, G_MT = G_KN + MAT_W, G_T16 = G_MT + MAT_N, G_DO = G_T16 + MAT_N,
+              G_X = G_DO + MAT_W,             // AF + TF, then bR + U
+              G_DU = G_X + 2 * MAT_W, G_DR = G_DU + MAT_W, G_END = G_DR + MAT_W;
+// after the last reads of dO', bR, U, dU, dR: the 64 x 64 results
+constexpr int G_DT = G_DO, G_X1 = G_DT + MAT_N, G_DP = G_X1 + MAT_N, G_DPT = G_DP + MAT_N, G_DG = G_DPT + MAT_N,
+              G_DGT = G_DG + MAT_N;
+static_assert(2 * MAT_F <= 2 * MAT_W, "fp32 solve fits the region");
+static_assert(G_DGT + MAT_N <= G_END, "64 x 64 results fit");
+}  // namespace
+
+__global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
+  __shared__ __attribute__((aligned(16))) uint8_t smem[G_END];
+  __shared__ RowsLds R;
+  __shared__ RedLds red;
+  f16* QN = reinterpret_cast<f16*>(smem + G_QN);
+  f16* KN = reinterpret_cast<f16*>(smem + G_KN);
+  f16* Mt = reinterpret_cast<f16*>(smem + G_MT);
+  f16* T16 = reinterpret_cast<f16*>(smem + G_T16);
+  f16* DO = reinterpret_cast<f16*>(smem + G_DO);
+  float* AF = reinterpret_cast<float*>(smem + G_X);
+  float* TF = reinterpret_cast<float*>(smem + G_X + MAT_F);
+  f16* BR = reinterpret_cast<f16*>(smem + G_X);
+  f16* U = reinterpret_cast<f16*>(smem + G_X + MAT_W);
+  f16* DU = reinterpret_cast<f16*>(smem + G_DU);
+  f16* DR = reinterpret_cast<f16*>(smem + G_DR);
+  f16* DT = reinterpret_cast<f16*>(smem + G_DT);
+  f16* X1t = reinterpret_cast<f16*>(smem + G_X1);
+  f16* DP = reinterpret_cast<f16*>(smem + G_DP);
+  f16* DPt = reinterpret_cast<f16*>(smem + G_DPT);
+  f16* DG = reinterpret_cast<f16*>(smem + G_DG);
+  f16* DGt = reinterpret_cast<f16*>(smem + G_DGT);
+
+  const int job = blockIdx.x, e = job / p.H, h = job - e * p.H, G = p.H / p.H_qk, hq = h / G;
+  const int2 ce = entry_of(p, e);
+  const int tok0 = ce.x, len = ce.y;
+  if (len <= 0) return;
+  const int t = threadIdx.x, w = t >> 6, lane = t & 63, l16 = lane & 15, lg = lane >> 4;
+  const f16* Sg = reinterpret_cast<const f16*>(p.states) + (size_t)job * HD * HD;    // [V][K]
+  const f16* dSg = reinterpret_cast<const f16*>(p.dstates) + (size_t)job * HD * HD;  // [V][K]
+  const size_t vrow = (size_t)p.H * HD;
+  const uint16_t* vbase = p.v + (size_t)tok0 * vrow + (size_t)h * HD;
+
+  load_chunk(p, tok0, len, h, hq, QN, KN, R);
+  // dO' rows (fp16, zero past the chunk's end): thread -> row t / 8, 16 columns
   {
-    const int r = t >> 2, qd = t & 3;
-    float db = 0.f;
-    const float b = rows[R_B + r];
-    for (int c = 32 * qd; c < 32 * qd + 32; ++c) {
-      const float y = sc[S_DR + r * HD + c];
-      db += y * sc[S_R + r * HD + c];
-      sc[S_DR + r * HD + c] = b * y;
+    const int r = t >> 3, c0 = (t & 7) * 16;
+    float x[16];
+    if (r < len) {
+      const uint16_t* src = p.dout + (size_t)(tok0 + r) * vrow + (size_t)h * HD + c0;
+      unpack_bf16x8(*reinterpret_cast<const uint4*>(src), x);
+      unpack_bf16x8(*reinterpret_cast<const uint4*>(src + 8), x + 8);
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] *= p.scale;
+    } else {
+#pragma unroll
+      for (int i = 0; i < 16; ++i) x[i] = 0.f;
     }
-    db += __shfl_xor(db, 1);
-    db += __shfl_xor(db, 2);
-    if (qd == 0) srow[2 * CH + r] = db;
+    *reinterpret_cast<f16x8*>(DO + r * LDW + c0) = to_f16x8(x);
+    *reinterpret_cast<f16x8*>(DO + r * LDW + c0 + 8) = to_f16x8(x + 8);
   }
-  __syncthreads();
-  wg_gemm<CH, HD, HD, false, false, false>(sc + S_DRS, sc + S_DR, HD, St, HD, 1.f, sh);   // dR S^T
-  wg_gemm<CH, CH, HD, false, true, false>(sc + S_DM, sc + S_DO, HD, sc + S_U, HD, 1.f, sh);   // dO' U^T
-  wg_gemm<CH, CH, HD, false, true, false>(sc + S_DT, sc + S_DU, HD, sc + S_BR, HD, 1.f, sh);  // dU (b R)^T
-  wg_gemm<CH, CH, CH, false, true, false>(sc + S_X1, sc + S_DT, CH, blk + P_T, CH, 1.f, sh);  // dT T^T
-  wg_gemm<CH, CH, CH, true, false, false>(sc + S_DA, blk + P_T, CH, sc + S_X1, CH, -1.f, sh); // -T^T (dT T^T)
-  // 64 x 64 elementwise: dM, dA masked; dGm + dGm^T, dP; the rows and columns of dLam . Lam
-  const float* GM = blk + P_GM;
-  const float* PP = blk + P_P;
-  for (int i = t; i < MM; i += BT) {
-    const int r = i / CH, c = i % CH;
-    const float lam = r >= c ? expf(fminf(rows[R_GAM + r] - rows[R_GAM + c], 0.f)) : 0.f;
-    const float dm = r >= c ? sc[S_DM + i] : 0.f;
-    const float da = r > c ? sc[S_DA + i] : 0.f;
-    const float b = rows[R_B + r];
-    sc[S_DM + i] = (da * GM[i] * lam);            // db2 terms (row sums below)
-    sc[S_X1 + i] = (b * da * GM[i] + dm * PP[i]) * lam;  // W = dLam . Lam
-    sc[S_DP + i] = dm * lam;                      // dP
-    sc[S_DT + i] = b * da * lam;                  // dGm
-  }
-  __syncthreads();
-  for (int i = t; i < MM; i += BT) {
-    const int r = i / CH, c = i % CH;
-    sc[S_DG2 + i] = sc[S_DT + i] + sc[S_DT + c * CH + r];  // dGm + dGm^T
-  }
-  __syncthreads();
-  // dqn = diag(e) (dO' S^T) + dP kn;  dkn = diag(f) (U dS'^T) - diag(e) (dR S^T) + (dGm + dGm^T) kn + dP^T qn
-  for (int i = t; i < MK; i += BT) {
-    const int r = i / HD;
-    sc[S_DQN + i] = rows[R_E + r] * sc[S_SDO + i];
-    sc[S_DKN + i] = rows[R_F + r] * sc[S_UDS + i] - rows[R_E + r] * sc[S_DRS + i];
-  }
-  __syncthreads();
-  wg_gemm<CH, HD, CH, false, false, true>(sc + S_DQN, sc + S_DP, CH, KN, HD, 1.f, sh);
-  wg_gemm<CH, HD, CH, false, false, true>(sc + S_DKN, sc + S_DG2, CH, KN, HD, 1.f, sh);
-  wg_gemm<CH, HD, CH, true, false, true>(sc + S_DKN, sc + S_DP, CH, QN, HD, 1.f, sh);
-  // row terms: de = rowsum(qn . dO'S^T) - rowsum(dR . kn S), df = rowsum(kn . U dS'^T), db2, rows and
-  // columns of W;  deL = sum(dS' . S)
-  float deL = 0.f;
-  for (int i = t; i < HD * HD; i += BT) deL += dSt[i] * St[i];
-  red[t] = deL;
+  // sum(dS' . S) over the 128 x 128 block, and the row sums cleared
   {
-    const int r = t >> 2, qd = t & 3;
-    float de = 0.f, df = 0.f;
-    for (int c = 32 * qd; c < 32 * qd + 32; ++c) {
-      de += QN[r * HD + c] * sc[S_SDO + r * HD + c] - sc[S_DR + r * HD + c] * sc[S_KS + r * HD + c];
-      df += KN[r * HD + c] * sc[S_UDS + r * HD + c];
+    float a = 0.f;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const size_t o = (size_t)(t + NTH * i) * 8;
+      const f16x8 s8 = *reinterpret_cast<const f16x8*>(Sg + o), d8 = *reinterpret_cast<const f16x8*>(dSg + o);
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a += (float)s8[j] * (float)d8[j];
     }
-    float db2 = 0.f, wr = 0.f, wc = 0.f;
-    for (int c = 16 * qd; c < 16 * qd + 16; ++c) {
-      db2 += sc[S_DM + r * CH + c];
-      wr += sc[S_X1 + r * CH + c];
-      wc += sc[S_X1 + c * CH + r];
+    a = sum64(a);
+    if (lane == 0) red.deL[w] = a;
+    if (t < CH) red.de[t] = red.df[t] = red.db[t] = red.wr[t] = red.wc[t] = red.qd[t] = red.kd[t] = 0.f;
+  }
+  __syncthreads();
+  f32x4 P[2], Gm[2];
+  gram_and_T(QN, KN, R, Mt, nullptr, AF, TF, T16, P, Gm);
+
+  const int vc = 16 * w + l16;  // this lane's column of the 64 x 128 results
+  // ---- KS = kn S (rows r, columns v); R = V - diag(e) KS; bR -------------
+  f32x4 KS[4], RR[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) KS[i] = zero4();
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    const f16x8 b = *reinterpret_cast<const f16x8*>(Sg + (size_t)vc * HD + 32 * s + 8 * lg);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) KS[i] = mma_f16(frag_rm(KN, LDW, 16 * i, 32 * s, lane), b, KS[i]);
+  }
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 16 * i + 4 * lg + jj;
+      const float vv = r < len ? bf(vbase[(size_t)r * vrow + vc]) : 0.f;
+      RR[i][jj] = vv - R.e[r] * KS[i][jj];
+      BR[r * LDW + vc] = (f16)(R.b[r] * RR[i][jj]);
+    }
+  __syncthreads();  // bR complete
+  // ---- U^T = (b R)^T T^T (rows v: tile w, columns r: 4 tiles) -> U row-major
+  {
+    f32x4 UT[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) UT[i] = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f16x8 a = frag_cm(BR, LDW, 16 * w, 32 * s, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) UT[i] = mma_f16(a, frag_rm(T16, LDN, 16 * i, 32 * s, lane), UT[i]);
     }
 #pragma unroll
-    for (int o = 1; o <= 2; o <<= 1) {
-      de += __shfl_xor(de, o);
-      df += __shfl_xor(df, o);
-      db2 += __shfl_xor(db2, o);
-      wr += __shfl_xor(wr, o);
-      wc += __shfl_xor(wc, o);
-    }
-    __syncthreads();  // red[] complete
-    if (qd == 0) {
-      srow[r] = de;
-      srow[CH + r] = df;
-      srow[2 * CH + r] += db2;
-      srow[3 * CH + r] = wr - wc + de * rows[R_E + r] - df * rows[R_F + r];  // dG without the chunk-end terms
-    }
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<f16x4*>(U + (16 * i + l16) * LDW + 16 * w + 4 * lg) =
+          f16x4{(f16)UT[i][0], (f16)UT[i][1], (f16)UT[i][2], (f16)UT[i][3]};
   }
-  __syncthreads();
-  if (t == 0) {  // chunk-end terms on the last live row, then dg = reverse cumulative sum of dG
-    float tot = 0.f;
-    for (int i = 0; i < BT; ++i) tot += red[i];
-    float dfs = 0.f;
-    for (int r = 0; r < len; ++r) dfs += srow[CH + r] * rows[R_F + r];
-    srow[3 * CH + len - 1] += dfs + tot * rows[R_EL];
-    float acc = 0.f, dal = 0.f;
-    for (int r = len - 1; r >= 0; --r) {
-      acc += srow[3 * CH + r];
-      srow[3 * CH + r] = acc;                       // dg_r
-      dal += acc * rows[R_G + r];
-    }
-    atomicAdd(p.dA_log + h, dal);
-  }
-  __syncthreads();
-  // per-token outputs: dv, dg_raw, dbeta; dq, dk through the L2 normalisation (summed over the group)
-  for (int i = t; i < len * HD; i += BT) {
-    const int r = i / HD, c = i % HD;
-    p.dv[((size_t)(tok0 + r) * p.H + h) * HD + c] = sc[S_DR + i];
-  }
-  if (t < len) {
-    const size_t th = (size_t)(tok0 + t) * p.H + h;
-    const float graw = bf(p.g_raw[th]), b = rows[R_B + t];
-    p.dg_raw[th] = srow[3 * CH + t] * (-expf(p.A_log[h])) * sigmoid_(graw);
-    p.dbeta[th] = srow[2 * CH + t] * b * (1.f - b);
-  }
+  // ---- dU = diag(f) kn dS' + M^T dO' (rows r, columns v) -----------------
   {
-    const int r = t >> 2, qd = t & 3;
-    if (r < len) {
-      float dq = 0.f, dk = 0.f;  // qn . dqn, kn . dkn
-      for (int c = 32 * qd; c < 32 * qd + 32; ++c) {
-        dq += QN[r * HD + c] * sc[S_DQN + r * HD + c];
-        dk += KN[r * HD + c] * sc[S_DKN + r * HD + c];
+    f32x4 D[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) D[i] = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 b = *reinterpret_cast<const f16x8*>(dSg + (size_t)vc * HD + 32 * s + 8 * lg);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) D[i] = mma_f16(frag_rm(KN, LDW, 16 * i, 32 * s, lane), b, D[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) D[i][jj] *= R.f[16 * i + 4 * lg + jj];
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f16x8 b = frag_cm(DO, LDW, 16 * w, 32 * s, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) D[i] = mma_f16(frag_rm(Mt, LDN, 16 * i, 32 * s, lane), b, D[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) DU[(16 * i + 4 * lg + jj) * LDW + vc] = (f16)D[i][jj];
+  }
+  __syncthreads();  // U, dU complete
+  // ---- Y = T^T dU; dV = diag(b) Y; db += rowsum(Y . R); de -= rowsum(dV . KS)
+  {
+    f32x4 Y[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Y[i] = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f16x8 b = frag_cm(DU, LDW, 16 * w, 32 * s, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Y[i] = mma_f16(frag_cm(T16, LDN, 16 * i, 32 * s, lane), b, Y[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * i + 4 * lg + jj;
+        const float dv = R.b[r] * Y[i][jj];
+        if (r < len) p.dv[(size_t)(tok0 + r) * vrow + (size_t)h * HD + vc] = dv;
+        DR[r * LDW + vc] = (f16)dv;
+        const float db = rowsum16(Y[i][jj] * RR[i][jj]), de = rowsum16(dv * KS[i][jj]);
+        if (l16 == 0) {
+          atomicAdd(&red.db[r], db);
+          atomicAdd(&red.de[r], -de);
+        }
       }
-      dq += __shfl_xor(dq, 1);
-      dq += __shfl_xor(dq, 2);
-      dk += __shfl_xor(dk, 1);
-      dk += __shfl_xor(dk, 2);
-      const float nq = rows[R_NQ + r], nk = rows[R_NK + r];
-      const size_t at = ((size_t)(tok0 + r) * p.H_qk + hq) * HD;
-      for (int c = 32 * qd; c < 32 * qd + 32; ++c) {
-        // d/dq of q / n(q): (dqn - qn (qn . dqn)) / n
-        const float gq = (sc[S_DQN + r * HD + c] - QN[r * HD + c] * dq) / nq;
-        const float gk = (sc[S_DKN + r * HD + c] - KN[r * HD + c] * dk) / nk;
+  }
+  __syncthreads();  // dR complete
+  // ---- [dO'; dR] S^T and U dS'^T (rows r, columns d: tile w) ------------------
+  f32x4 dqn[4], dkn[4];
+  {
+    f32x4 SD[4], DRS[4], UD[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) SD[i] = DRS[i] = UD[i] = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      f16x8 bs, bd;  // S^T and dS'^T operands: element e = X[v = 32 s + 8 lg + e][d]
+#pragma unroll
+      for (int e2 = 0; e2 < 8; ++e2) {
+        const size_t o = (size_t)(32 * s + 8 * lg + e2) * HD + vc;
+        bs[e2] = Sg[o];
+        bd[e2] = dSg[o];
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        SD[i] = mma_f16(frag_rm(DO, LDW, 16 * i, 32 * s, lane), bs, SD[i]);
+        DRS[i] = mma_f16(frag_rm(DR, LDW, 16 * i, 32 * s, lane), bs, DRS[i]);
+        UD[i] = mma_f16(frag_rm(U, LDW, 16 * i, 32 * s, lane), bd, UD[i]);
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * i + 4 * lg + jj;
+        dqn[i][jj] = R.e[r] * SD[i][jj];
+        dkn[i][jj] = R.f[r] * UD[i][jj] - R.e[r] * DRS[i][jj];
+        const float de = rowsum16((float)QN[r * LDW + vc] * SD[i][jj]);
+        const float df = rowsum16((float)KN[r * LDW + vc] * UD[i][jj]);
+        if (l16 == 0) {
+          atomicAdd(&red.de[r], de);
+          atomicAdd(&red.df[r], df);
+        }
+      }
+  }
+  // ---- dM = dO' U^T, dT = dU (b R)^T (64 x 64 tiles of this wave) -------------
+  const int rt = w >> 1, ct0 = 2 * (w & 1);
+  f32x4 DM[2];
+  {
+    f32x4 DTa[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) DM[j] = DTa[j] = zero4();
+#pragma unroll
+    for (int s = 0; s < 4; ++s) {
+      const f16x8 ado = frag_rm(DO, LDW, 16 * rt, 32 * s, lane), adu = frag_rm(DU, LDW, 16 * rt, 32 * s, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) {
+        DM[j] = mma_f16(ado, frag_rm(U, LDW, 16 * (ct0 + j), 32 * s, lane), DM[j]);
+        DTa[j] = mma_f16(adu, frag_rm(BR, LDW, 16 * (ct0 + j), 32 * s, lane), DTa[j]);
+      }
+    }
+    __syncthreads();  // last reads of dO', bR, U, dU, dR: their space now holds the 64 x 64 results
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) DT[(16 * rt + 4 * lg + jj) * LDN + 16 * (ct0 + j) + l16] = (f16)DTa[j][jj];
+  }
+  __syncthreads();
+  // ---- X1 = dT T^T -> X1t -----------------------------------------------------
+  {
+    f32x4 X[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) X[j] = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f16x8 a = frag_rm(DT, LDN, 16 * rt, 32 * s, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) X[j] = mma_f16(a, frag_rm(T16, LDN, 16 * (ct0 + j), 32 * s, lane), X[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j)
+      *reinterpret_cast<f16x4*>(X1t + (16 * (ct0 + j) + l16) * LDN + 16 * rt + 4 * lg) =
+          f16x4{(f16)X[j][0], (f16)X[j][1], (f16)X[j][2], (f16)X[j][3]};
+  }
+  __syncthreads();
+  // ---- dA = -T^T X1 and the 64 x 64 elementwise terms ----------------------
+  {
+    f32x4 DA[2];
+#pragma unroll
+    for (int j = 0; j < 2; ++j) DA[j] = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f16x8 a = frag_cm(T16, LDN, 16 * rt, 32 * s, lane);
+#pragma unroll
+      for (int j = 0; j < 2; ++j) DA[j] = mma_f16(a, frag_rm(X1t, LDN, 16 * (ct0 + j), 32 * s, lane), DA[j]);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const int c = 16 * (ct0 + j) + l16;
+      f16x4 pc, gc;
+      float wcol = 0.f;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int r = 16 * rt + 4 * lg + jj;
+        const float lam = r >= c ? expf(fminf(R.gam[r] - R.gam[c], 0.f)) : 0.f;
+        const float dm = r >= c ? DM[j][jj] : 0.f;
+        const float da = r > c ? -DA[j][jj] : 0.f;
+        const float dp = dm * lam, dgm = R.b[r] * da * lam;
+        const float wv = (R.b[r] * da * Gm[j][jj] + dm * P[j][jj]) * lam;
+        DP[r * LDN + c] = (f16)dp;
+        DG[r * LDN + c] = (f16)dgm;
+        pc[jj] = (f16)dp;
+        gc[jj] = (f16)dgm;
+        wcol += wv;
+        const float db2 = rowsum16(da * Gm[j][jj] * lam), wr = rowsum16(wv);
+        if (l16 == 0) {
+          atomicAdd(&red.db[r], db2);
+          atomicAdd(&red.wr[r], wr);
+        }
+      }
+      *reinterpret_cast<f16x4*>(DPt + c * LDN + 16 * rt + 4 * lg) = pc;
+      *reinterpret_cast<f16x4*>(DGt + c * LDN + 16 * rt + 4 * lg) = gc;
+      wcol += __shfl_xor(wcol, 16);
+      wcol += __shfl_xor(wcol, 32);
+      if (lg == 0) atomicAdd(&red.wc[c], wcol);
+    }
+  }
+  __syncthreads();
+  // ---- dqn += dP kn;  dkn += (dGm + dGm^T) kn + dP^T qn ---------------------
+#pragma unroll
+  for (int s = 0; s < 2; ++s) {
+    const f16x8 bk = frag_cm(KN, LDW, 16 * w, 32 * s, lane), bq = frag_cm(QN, LDW, 16 * w, 32 * s, lane);
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const f16x8 ag = frag_rm(DG, LDN, 16 * i, 32 * s, lane) + frag_rm(DGt, LDN, 16 * i, 32 * s, lane);
+      dqn[i] = mma_f16(frag_rm(DP, LDN, 16 * i, 32 * s, lane), bk, dqn[i]);
+      dkn[i] = mma_f16(ag, bk, dkn[i]);
+      dkn[i] = mma_f16(frag_rm(DPt, LDN, 16 * i, 32 * s, lane), bq, dkn[i]);
+    }
+  }
+  // row dots qn . dqn, kn . dkn (fp32 qn, kn from the inputs)
+  float qf[4][4], kf[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 16 * i + 4 * lg + jj;
+      float qx = 0.f, kx = 0.f;
+      if (r < len) {
+        const size_t o = ((size_t)(tok0 + r) * p.H_qk + hq) * HD + vc;
+        qx = bf(p.q[o]) / R.nq[r];
+        kx = bf(p.k[o]) / R.nk[r];
+      }
+      qf[i][jj] = qx;
+      kf[i][jj] = kx;
+      const float qd = rowsum16(qx * dqn[i][jj]), kd = rowsum16(kx * dkn[i][jj]);
+      if (l16 == 0) {
+        atomicAdd(&red.qd[r], qd);
+        atomicAdd(&red.kd[r], kd);
+      }
+    }
+  __syncthreads();
+  // dq, dk through the normalisation: (dxn - xn (xn . dxn)) / |x|
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int r = 16 * i + 4 * lg + jj;
+      if (r < len) {
+        const size_t o = ((size_t)(tok0 + r) * p.H_qk + hq) * HD + vc;
+        const float gq = (dqn[i][jj] - qf[i][jj] * red.qd[r]) / R.nq[r];
+        const float gk = (dkn[i][jj] - kf[i][jj] * red.kd[r]) / R.nk[r];
         if (G == 1) {
-          p.dq[at + c] = gq;
-          p.dk[at + c] = gk;
+          p.dq[o] = gq;
+          p.dk[o] = gk;
         } else {
-          atomicAdd(p.dq + at + c, gq);
-          atomicAdd(p.dk + at + c, gk);
+          atomicAdd(p.dq + o, gq);
+          atomicAdd(p.dk + o, gk);
         }
       }
     }
+  // ---- dG, dg (reverse cumulative sum), dg_raw, dbeta, dA_log --------------
+  if (t < CH) {
+    const bool live = t < len;
+    float deL = 0.f;
+#pragma unroll
+    for (int i = 0; i < NTH / 64; ++i) deL += red.deL[i];
+    const float dff = live ? red.df[t] * R.f[t] : 0.f;
+    const float sum_df = sum64(dff);
+    float dG = live ? red.wr[t] - red.wc[t] + red.de[t] * R.e[t] - dff : 0.f;
+    if (t == len - 1) dG += sum_df + deL * R.eL;
+    float acc = dG;  // reverse inclusive scan over the 64 lanes
+#pragma unroll
+    for (int o = 1; o < CH; o <<= 1) {
+      const float y = __shfl_down(acc, o);
+      if (t + o < CH) acc += y;
+    }
+    const float dal = sum64(live ? acc * R.g[t] : 0.f);
+    if (live) {
+      const size_t th = (size_t)(tok0 + t) * p.H + h;
+      const float b = R.b[t];
+      p.dg_raw[th] = acc * (-expf(p.A_log[h])) * sigmoid_(bf(p.g_raw[th]));
+      p.dbeta[th] = red.db[t] * b * (1.f - b);
+    }
+    if (t == 0) atomicAdd(p.dA_log + h, dal);
   }
 }
 
-__global__ __launch_bounds__(BT) void bwd_fill_kernel(float* a, size_t n) {
-  for (size_t i = (size_t)blockIdx.x * BT + threadIdx.x; i < n; i += (size_t)gridDim.x * BT) a[i] = 0.f;
+__global__ __launch_bounds__(256) void bwd_fill_kernel(float* a, size_t n) {
+  for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) a[i] = 0.f;
 }
 
-void launch_bwd(const BwdParams& p0, size_t qk_floats, size_t slots, hipStream_t stream) {
-  BwdParams p = p0;
+void launch_bwd(const BwdParams& p, size_t qk_floats, hipStream_t stream) {
   const int jobs = p.n_entries * p.H;
-  if (p.H != p.H_qk) {  // dq, dk are accumulated over each group's value heads
-    bwd_fill_kernel<<<1024, BT, 0, stream>>>(p.dq, qk_floats);
-    bwd_fill_kernel<<<1024, BT, 0, stream>>>(p.dk, qk_floats);
+  if (p.H != p.H_qk && qk_floats > 0) {  // dq, dk are accumulated over each group's value heads
+    bwd_fill_kernel<<<1024, 256, 0, stream>>>(p.dq, qk_floats);
+    bwd_fill_kernel<<<1024, 256, 0, stream>>>(p.dk, qk_floats);
   }
-  bwd_fill_kernel<<<1, BT, 0, stream>>>(p.dA_log, (size_t)p.H);
-  if (jobs > 0) bwd_prep_kernel<<<jobs, BT, 0, stream>>>(p);
-  if (p.n_chains > 0) bwd_adjoint_kernel<<<p.n_chains * 8, BT, 0, stream>>>(p);
-  for (int j0 = 0; j0 < jobs; j0 += (int)slots) {
-    p.job0 = j0;
-    bwd_grad_kernel<<<(int)std::min<size_t>(slots, (size_t)(jobs - j0)), BT, 0, stream>>>(p);
-  }
+  bwd_fill_kernel<<<1, 256, 0, stream>>>(p.dA_log, (size_t)p.H);
+  if (jobs > 0) bwd_coef_kernel<<<jobs, NTH, 0, stream>>>(p);
+  if (p.n_chains > 0) bwd_adjoint_kernel<<<((p.n_chains + 7) / 8) * 64, 256, 0, stream>>>(p);
+  if (jobs > 0) bwd_grad_kernel<<<jobs, NTH, 0, stream>>>(p);
 }
 
 }  // namespace kda

@@ -63,7 +63,7 @@ struct RecurParams {
   uint16_t* sink;         // 64 scratch values: destination of output rows past a chunk's end
   int dense_T;            // >= 0: B rows of dense_T tokens, schedule by arithmetic; -1: read `seqs`/`order`
   int* err;               // error word of the workspace header: cleared (this path reports no errors)
-  float* states = nullptr;  // backward's forward: fp32 state entering every chunk, [entries][H][128][128]
+  uint16_t* states = nullptr;  // backward's forward: fp16 state entering every chunk, [entries][H][V][K]
 };
 
 // Fused persistent forward (kda_fused.hip): per-channel gate, delta rule.
@@ -142,9 +142,7 @@ int recur_grid(int n_chains);
 void launch_decode(const DecodeParams& p, int B, bool bf16_state, bool per_channel, bool delta, hipStream_t stream);
 
 // Backward pass, scalar gate, delta rule (kda_bwd.hip).
-constexpr int BWD_MM = 64 * 64, BWD_MK = 64 * 128;
-constexpr int PREP_FLOATS = 2 * BWD_MK + 4 * BWD_MM + 8 * 64;        // per (entry, head)
-constexpr int BWD_SLOT_FLOATS = 13 * BWD_MK + 6 * BWD_MM + 8 * 64;   // per concurrent gradient job
+constexpr int BREC_BYTES = 48 * 1024;  // per (entry, head): the adjoint's operand fragments
 struct BwdParams {
   const uint16_t* q;      // bf16 [tokens, H_qk, 128]
   const uint16_t* k;
@@ -161,11 +159,9 @@ struct BwdParams {
   const int4* seqs;
   const int* order;
   int n_entries, n_chains;
-  const float* states;    // [entries][H][V][K]: the state entering every chunk
-  float* dstates;         // [entries][H][V][K]: the gradient of the state leaving every chunk
-  float* prep;            // [entries][H][PREP_FLOATS]
-  float* scratch;         // [slots][BWD_SLOT_FLOATS]
-  int job0;               // first (entry, head) job of a gradient launch
+  const uint16_t* states;  // fp16 [entries][H][V][K]: the state entering every chunk
+  uint16_t* dstates;       // fp16 [entries][H][V][K]: the gradient of the state leaving every chunk
+  uint8_t* brec;           // [entries][H][BREC_BYTES]
   float* dq;              // fp32 [tokens, H_qk, 128]
   float* dk;
   float* dv;              // fp32 [tokens, H, 128]
@@ -174,8 +170,7 @@ struct BwdParams {
   float* dA_log;          // fp32 [H]
   float* dinit;           // fp32 [seqs, H, 128, 128] or null
 };
-// qk_floats: elements of dq (= of dk), cleared first when value heads share q/k heads; slots: concurrent
-// gradient jobs the scratch holds.
-void launch_bwd(const BwdParams& p, size_t qk_floats, size_t slots, hipStream_t stream);
+// qk_floats: elements of dq (= of dk), cleared first when value heads share q/k heads.
+void launch_bwd(const BwdParams& p, size_t qk_floats, hipStream_t stream);
 
 }  // namespace kda

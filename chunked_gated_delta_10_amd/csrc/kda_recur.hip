@@ -134,7 +134,7 @@ __device__ __forceinline__ void unpack_bf16(uint2 x, f16* o) {
 // B operand of T diag(b), at the cost of one more barrier per chunk.
 //
 // ST (the backward pass's forward): the chain waves also store the state
-// entering every chunk (fp32, p.states [entries][H][V][K]) and the output
+// entering every chunk (fp16, p.states [entries][H][V][K]) and the output
 // waves only keep the barriers (no outputs are needed).
 template <typename StT, int NCT, bool DELTA, bool PC, bool ST = false>
 __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
@@ -242,13 +242,15 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
       auto step = [&](const ChainFrags<NCT>& F, int c) {
         sink ^= F.touch;
         const int L = min(CH, len - c * CH);
-        if constexpr (ST) {  // the state entering chunk c
-          float* st = p.states + ((size_t)(chunk0 + c) * p.H + h) * HD * HD + (size_t)(v0 + l16) * HD;
+        if constexpr (ST) {  // the state entering chunk c, fp16
+          f16* st = reinterpret_cast<f16*>(p.states) + ((size_t)(chunk0 + c) * p.H + h) * HD * HD +
+                    (size_t)(v0 + l16) * HD;
 #pragma unroll
           for (int j = 0; j < NCT; ++j)
 #pragma unroll
             for (int i = 0; i < 2; ++i)
-              StateIO<float>::store(st, (size_t)VT * j * HD + SUB * (2 * TW + i) + 4 * lg, S[j][i]);
+              *reinterpret_cast<f16x4*>(st + (size_t)VT * j * HD + SUB * (2 * TW + i) + 4 * lg) =
+                  f16x4{(f16)S[j][i][0], (f16)S[j][i][1], (f16)S[j][i][2], (f16)S[j][i][3]};
         }
         {
 #pragma unroll
