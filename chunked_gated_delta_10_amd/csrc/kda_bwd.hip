@@ -28,7 +28,7 @@
 // Kernels, after the forward's chunk-local kernel and a recurrence that
 // stores the state entering every chunk (fp16):
 //   coef_kernel     per (chunk, head): Phi and Bc as fp16 operand fragments
-//   adjoint_kernel  per (chain, 16 value columns): dS over chunks, last to
+//   adjoint_kernel  per (chain, value-column tile): dS over chunks, last to
 //                   first; stores dS' of every chunk (fp16) and dS_0 (fp32)
 //   grad_kernel     per (chunk, head): every input gradient of the chunk
 // Products run on fp16 matrix cores with fp32 accumulation (the precision of
@@ -108,12 +108,11 @@ __device__ void load_chunk(const BwdParams& p, int tok0, int len, int h, int hq,
   const int t = threadIdx.x;
   if (t < CH) {
     const bool live = t < len;
-    float g = 0.f, b = 0.f;
-    if (live) {
-      const size_t th = (size_t)(tok0 + t) * p.H + h;
-      g = -expf(p.A_log[h]) * softplus_(bf(p.g_raw[th]));
-      b = sigmoid_(p.beta[th]);
-    }
+    const size_t th = (size_t)(tok0 + min(t, len - 1)) * p.H + h;  // loads clamped, values selected
+    const float graw = bf(p.g_raw[th]), blog = p.beta[th];
+    const float m = live ? 1.f : 0.f;
+    const float g = m * (-expf(p.A_log[h]) * softplus_(graw));
+    const float b = m * sigmoid_(blog);
     float G = g;  // inclusive scan over the 64 lanes
 #pragma unroll
     for (int o = 1; o < CH; o <<= 1) {
@@ -134,15 +133,18 @@ __device__ void load_chunk(const BwdParams& p, int tok0, int len, int h, int hq,
   // thread -> row t / 8, channels 16 (t % 8) .. + 15
   const int r = t >> 3, c0 = (t & 7) * 16;
   float qv[16], kv[16];
-  if (r < len) {
-    const size_t base = ((size_t)(tok0 + r) * p.H_qk + hq) * HD + c0;
+  {
+    const size_t base = ((size_t)(tok0 + min(r, len - 1)) * p.H_qk + hq) * HD + c0;
     unpack_bf16x8(*reinterpret_cast<const uint4*>(p.q + base), qv);
     unpack_bf16x8(*reinterpret_cast<const uint4*>(p.q + base + 8), qv + 8);
     unpack_bf16x8(*reinterpret_cast<const uint4*>(p.k + base), kv);
     unpack_bf16x8(*reinterpret_cast<const uint4*>(p.k + base + 8), kv + 8);
-  } else {
+    const float m = r < len ? 1.f : 0.f;
 #pragma unroll
-    for (int i = 0; i < 16; ++i) qv[i] = kv[i] = 0.f;
+    for (int i = 0; i < 16; ++i) {
+      qv[i] *= m;
+      kv[i] *= m;
+    }
   }
   float sq = 0.f, sk = 0.f;
 #pragma unroll
@@ -415,16 +417,24 @@ __global__ __launch_bounds__(NTH) void bwd_coef_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// adjoint_kernel: per (chain, 16 value columns), dS = Phi dS' + Bc dO' over
-// the chain's chunks, last first.  Wave w holds rows 32 w .. 32 w + 31 of dS
-// in C layout (fp32); the four waves' rows, converted to fp16, are the B
-// operand of the next step (published through LDS, one barrier per chunk).
+// adjoint_kernel: per (chain, 16 NCT value columns), dS = Phi dS' + Bc dO'
+// over the chain's chunks, last first.  Wave w holds rows 32 w .. 32 w + 31
+// of dS for every column tile in C layout (fp32); the four waves' rows,
+// converted to fp16, are the B operand of the next step, and the dO'
+// fragments (loaded once per workgroup, a share per wave) go the same way:
+// both through LDS, one barrier per chunk.  The record fragments and dO' of
+// the next chunk are loaded while the current one is processed.
 // ---------------------------------------------------------------------------
+template <int NCT>
 __global__ __launch_bounds__(256) void bwd_adjoint_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) f16x8 sB[2][4][64];
+  constexpr int NW = 8 / NCT;       // workgroups per chain
+  constexpr int NF = 2 * NCT;       // dO' fragments per chunk (column tile, token slice)
+  constexpr int FPW = (NF + 3) / 4;  // of which each wave loads up to FPW
+  __shared__ __attribute__((aligned(16))) f16x8 sB[2][NCT][4][64];
+  __shared__ __attribute__((aligned(16))) f16x8 sD[2][NF][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
-  // the 8 workgroups of a chain share an XCD (blocks are dealt to XCDs round robin)
-  const int x = blockIdx.x, xcd = x & 7, y = x >> 3, vt = y & 7, ch = (y >> 3) * 8 + xcd;
+  // the workgroups of a chain share an XCD (blocks are dealt to XCDs round robin)
+  const int x = blockIdx.x, xcd = x & 7, y = x >> 3, vt = y % NW, ch = (y / NW) * 8 + xcd;
   if (ch >= p.n_chains) return;
   const int h = ch % p.H;
   int n, tok0, len, chunk0;
@@ -441,71 +451,118 @@ __global__ __launch_bounds__(256) void bwd_adjoint_kernel(BwdParams p) {
     chunk0 = sq.z;
   }
   const int nch = max(0, min((len + CH - 1) / CH, p.n_entries - chunk0));
-  const int v = 16 * vt + l16;
-  const size_t sbase = ((size_t)n * p.H + h) * HD * HD + (size_t)v * HD;
-  f32x4 dS[2];
+  const int v0 = 16 * NCT * vt;
+  const size_t sbase = ((size_t)n * p.H + h) * HD * HD;
+  f32x4 dS[NCT][2];
 #pragma unroll
-  for (int i = 0; i < 2; ++i) {
-    const int d = 32 * w + 16 * i + 4 * lg;
-    if (p.dfinal) {
-      const float4 x4 = *reinterpret_cast<const float4*>(p.dfinal + sbase + d);
-      dS[i] = f32x4{x4.x, x4.y, x4.z, x4.w};
-    } else {
-      dS[i] = zero4();
-    }
-  }
-  const size_t vstride = (size_t)p.H * HD;
-  for (int c = nch - 1; c >= 0; --c) {
-    const size_t eh = (size_t)(chunk0 + c) * p.H + h;
-    const uint8_t* rec = p.brec + eh * BREC_BYTES;
-    // dS' of this chunk
-    f16* ds = reinterpret_cast<f16*>(p.dstates) + eh * HD * HD + (size_t)v * HD;
+  for (int j = 0; j < NCT; ++j)
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<f16x4*>(ds + 32 * w + 16 * i + 4 * lg) =
-          f16x4{(f16)dS[i][0], (f16)dS[i][1], (f16)dS[i][2], (f16)dS[i][3]};
-    sB[c & 1][w][lane] = f16x8{(f16)dS[0][0], (f16)dS[0][1], (f16)dS[0][2], (f16)dS[0][3],
-                               (f16)dS[1][0], (f16)dS[1][1], (f16)dS[1][2], (f16)dS[1][3]};
-    // dO' as a B operand: tokens in fragment order, rows past the chunk's end zero
-    const int L = min(CH, len - c * CH);
-    const uint16_t* dob = p.dout + ((size_t)tok0 + (size_t)c * CH) * vstride + (size_t)h * HD + v;
-    f16x8 dO[2];
-#pragma unroll
-    for (int s = 0; s < 2; ++s)
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const int tk = 32 * s + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
-        dO[s][e] = (f16)(tk < L ? p.scale * bf(dob[(size_t)tk * vstride]) : 0.f);
+    for (int i = 0; i < 2; ++i) {
+      const size_t o = sbase + (size_t)(v0 + 16 * j + l16) * HD + 32 * w + 16 * i + 4 * lg;
+      if (p.dfinal) {
+        const float4 x4 = *reinterpret_cast<const float4*>(p.dfinal + o);
+        dS[j][i] = f32x4{x4.x, x4.y, x4.z, x4.w};
+      } else {
+        dS[j][i] = zero4();
       }
-    f16x8 Af[2][4], Bf[2][2];
+    }
+  const size_t vstride = (size_t)p.H * HD;
+  // raw dO' values are kept as loaded and converted in step(): a load's
+  // result used right away would make the wait cover the prefetches issued
+  // before it (the memory counter drains in order)
+  struct Frags {
+    f16x8 a[2][4], b[2][2];
+    uint16_t d[FPW][8];
+  };
+  auto load = [&](Frags& F, int c) {
+    // dO' first: tokens of slice s in fragment order (rows past the chunk's end clamped here, zeroed in step)
+    const int L = min(CH, len - c * CH);
+    const uint16_t* dob = p.dout + ((size_t)tok0 + (size_t)c * CH) * vstride + (size_t)h * HD + v0 + l16;
+#pragma unroll
+    for (int q = 0; q < FPW; ++q) {
+      const int f = w + 4 * q;
+      if (f < NF) {
+        const int j = f >> 1, s = f & 1;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tk = 32 * s + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
+          F.d[q][e] = dob[(size_t)min(tk, L - 1) * vstride + 16 * j];
+        }
+      }
+    }
+    const uint8_t* rec = p.brec + ((size_t)(chunk0 + c) * p.H + h) * BREC_BYTES;
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        Af[i][s] = *reinterpret_cast<const f16x8*>(rec + BR_PHI + ((2 * w + i) * 4 + s) * FRAG_BYTES + lane * 16);
+        F.a[i][s] = *reinterpret_cast<const f16x8*>(rec + BR_PHI + ((2 * w + i) * 4 + s) * FRAG_BYTES + lane * 16);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        Bf[i][s] = *reinterpret_cast<const f16x8*>(rec + BR_BC + ((2 * w + i) * 2 + s) * FRAG_BYTES + lane * 16);
+        F.b[i][s] = *reinterpret_cast<const f16x8*>(rec + BR_BC + ((2 * w + i) * 2 + s) * FRAG_BYTES + lane * 16);
     }
-    __syncthreads();  // every wave's rows of dS' published
-    f16x8 sb[4];
+  };
+  auto step = [&](const Frags& F, int c) {
+    const size_t eh = (size_t)(chunk0 + c) * p.H + h;
+    f16* ds = reinterpret_cast<f16*>(p.dstates) + eh * HD * HD;
+    const int buf = c & 1;
 #pragma unroll
-    for (int s = 0; s < 4; ++s) sb[s] = sB[c & 1][s][lane];
+    for (int j = 0; j < NCT; ++j) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i) {
-      f32x4 a = zero4();
-#pragma unroll
-      for (int s = 0; s < 4; ++s) a = mma_f16(Af[i][s], sb[s], a);
-#pragma unroll
-      for (int s = 0; s < 2; ++s) a = mma_f16(Bf[i][s], dO[s], a);
-      dS[i] = a;
+      for (int i = 0; i < 2; ++i)  // dS' of this chunk
+        *reinterpret_cast<f16x4*>(ds + (size_t)(v0 + 16 * j + l16) * HD + 32 * w + 16 * i + 4 * lg) =
+            f16x4{(f16)dS[j][i][0], (f16)dS[j][i][1], (f16)dS[j][i][2], (f16)dS[j][i][3]};
+      sB[buf][j][w][lane] = f16x8{(f16)dS[j][0][0], (f16)dS[j][0][1], (f16)dS[j][0][2], (f16)dS[j][0][3],
+                                  (f16)dS[j][1][0], (f16)dS[j][1][1], (f16)dS[j][1][2], (f16)dS[j][1][3]};
     }
+    const int L = min(CH, len - c * CH);
+#pragma unroll
+    for (int q = 0; q < FPW; ++q) {
+      const int f = w + 4 * q;
+      if (f < NF) {
+        f16x8 d;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) {
+          const int tk = 32 * (f & 1) + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
+          d[e] = (f16)(bf(F.d[q][e]) * (tk < L ? p.scale : 0.f));
+        }
+        sD[buf][f][lane] = d;
+      }
+    }
+    __syncthreads();  // every wave's rows of dS' and every dO' fragment published
+#pragma unroll
+    for (int j = 0; j < NCT; ++j) {
+      f16x8 sb[4], sd[2];
+#pragma unroll
+      for (int s = 0; s < 4; ++s) sb[s] = sB[buf][j][s][lane];
+#pragma unroll
+      for (int s = 0; s < 2; ++s) sd[s] = sD[buf][2 * j + s][lane];
+#pragma unroll
+      for (int i = 0; i < 2; ++i) {
+        f32x4 a = zero4();
+#pragma unroll
+        for (int s = 0; s < 4; ++s) a = mma_f16(F.a[i][s], sb[s], a);
+#pragma unroll
+        for (int s = 0; s < 2; ++s) a = mma_f16(F.b[i][s], sd[s], a);
+        dS[j][i] = a;
+      }
+    }
+  };
+  Frags f0, f1;
+  if (nch > 0) load(f0, nch - 1);
+  for (int c = nch - 1; c >= 0; c -= 2) {
+    load(f1, max(c - 1, 0));
+    step(f0, c);
+    if (c - 1 < 0) break;
+    load(f0, max(c - 2, 0));
+    step(f1, c - 1);
   }
   if (p.dinit) {
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
-      *reinterpret_cast<float4*>(p.dinit + sbase + 32 * w + 16 * i + 4 * lg) =
-          make_float4(dS[i][0], dS[i][1], dS[i][2], dS[i][3]);
+    for (int j = 0; j < NCT; ++j)
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        *reinterpret_cast<float4*>(p.dinit + sbase + (size_t)(v0 + 16 * j + l16) * HD + 32 * w + 16 * i + 4 * lg) =
+            make_float4(dS[j][i][0], dS[j][i][1], dS[j][i][2], dS[j][i][3]);
   }
 }
 
@@ -565,16 +622,12 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
   {
     const int r = t >> 3, c0 = (t & 7) * 16;
     float x[16];
-    if (r < len) {
-      const uint16_t* src = p.dout + (size_t)(tok0 + r) * vrow + (size_t)h * HD + c0;
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(src), x);
-      unpack_bf16x8(*reinterpret_cast<const uint4*>(src + 8), x + 8);
+    const uint16_t* src = p.dout + (size_t)(tok0 + min(r, len - 1)) * vrow + (size_t)h * HD + c0;
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(src), x);
+    unpack_bf16x8(*reinterpret_cast<const uint4*>(src + 8), x + 8);
+    const float sc = r < len ? p.scale : 0.f;
 #pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] *= p.scale;
-    } else {
-#pragma unroll
-      for (int i = 0; i < 16; ++i) x[i] = 0.f;
-    }
+    for (int i = 0; i < 16; ++i) x[i] *= sc;
     *reinterpret_cast<f16x8*>(DO + r * LDW + c0) = to_f16x8(x);
     *reinterpret_cast<f16x8*>(DO + r * LDW + c0 + 8) = to_f16x8(x + 8);
   }
@@ -612,7 +665,7 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int r = 16 * i + 4 * lg + jj;
-      const float vv = r < len ? bf(vbase[(size_t)r * vrow + vc]) : 0.f;
+      const float vv = bf(vbase[(size_t)min(r, len - 1) * vrow + vc]) * (r < len ? 1.f : 0.f);
       RR[i][jj] = vv - R.e[r] * KS[i][jj];
       BR[r * LDW + vc] = (f16)(R.b[r] * RR[i][jj]);
     }
@@ -826,12 +879,9 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int r = 16 * i + 4 * lg + jj;
-      float qx = 0.f, kx = 0.f;
-      if (r < len) {
-        const size_t o = ((size_t)(tok0 + r) * p.H_qk + hq) * HD + vc;
-        qx = bf(p.q[o]) / R.nq[r];
-        kx = bf(p.k[o]) / R.nk[r];
-      }
+      const size_t o = ((size_t)(tok0 + min(r, len - 1)) * p.H_qk + hq) * HD + vc;
+      const float qr = bf(p.q[o]), kr = bf(p.k[o]);
+      const float m = r < len ? 1.f : 0.f, qx = m * qr / R.nq[r], kx = m * kr / R.nk[r];
       qf[i][jj] = qx;
       kf[i][jj] = kx;
       const float qd = rowsum16(qx * dqn[i][jj]), kd = rowsum16(kx * dkn[i][jj]);
@@ -899,7 +949,12 @@ void launch_bwd(const BwdParams& p, size_t qk_floats, hipStream_t stream) {
   }
   bwd_fill_kernel<<<1, 256, 0, stream>>>(p.dA_log, (size_t)p.H);
   if (jobs > 0) bwd_coef_kernel<<<jobs, NTH, 0, stream>>>(p);
-  if (p.n_chains > 0) bwd_adjoint_kernel<<<((p.n_chains + 7) / 8) * 64, 256, 0, stream>>>(p);
+  if (p.n_chains > 0) {  // the widest column tiles that keep every workgroup resident (two per CU)
+    const int slots = 2 * device_cu_count(), g8 = (p.n_chains + 7) / 8 * 8;
+    if (g8 * 8 <= slots) bwd_adjoint_kernel<1><<<g8 * 8, 256, 0, stream>>>(p);
+    else if (g8 * 4 <= slots) bwd_adjoint_kernel<2><<<g8 * 4, 256, 0, stream>>>(p);
+    else bwd_adjoint_kernel<4><<<g8 * 2, 256, 0, stream>>>(p);
+  }
   if (jobs > 0) bwd_grad_kernel<<<jobs, NTH, 0, stream>>>(p);
 }
 
