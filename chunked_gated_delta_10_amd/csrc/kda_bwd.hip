@@ -617,6 +617,22 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
   const size_t vrow = (size_t)p.H * HD;
   const uint16_t* vbase = p.v + (size_t)tok0 * vrow + (size_t)h * HD;
 
+  const int vc = 16 * w + l16;  // this lane's column of the 64 x 128 results
+  // Operands read from global memory, issued first so that their latency
+  // overlaps the prologue: S_c and dS' as the B operands of kn S and kn dS'
+  // (together they cover each block once, which also gives sum(dS' . S)),
+  // and this lane's value entries.
+  f16x8 sfr[4], dsfr[4];
+#pragma unroll
+  for (int s = 0; s < 4; ++s) {
+    sfr[s] = *reinterpret_cast<const f16x8*>(Sg + (size_t)vc * HD + 32 * s + 8 * lg);
+    dsfr[s] = *reinterpret_cast<const f16x8*>(dSg + (size_t)vc * HD + 32 * s + 8 * lg);
+  }
+  uint16_t vraw[4][4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i)
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) vraw[i][jj] = vbase[(size_t)min(16 * i + 4 * lg + jj, len - 1) * vrow + vc];
   load_chunk(p, tok0, len, h, hq, QN, KN, R);
   // dO' rows (fp16, zero past the chunk's end): thread -> row t / 8, 16 columns
   {
@@ -631,41 +647,33 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
     *reinterpret_cast<f16x8*>(DO + r * LDW + c0) = to_f16x8(x);
     *reinterpret_cast<f16x8*>(DO + r * LDW + c0 + 8) = to_f16x8(x + 8);
   }
-  // sum(dS' . S) over the 128 x 128 block, and the row sums cleared
-  {
-    float a = 0.f;
-#pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      const size_t o = (size_t)(t + NTH * i) * 8;
-      const f16x8 s8 = *reinterpret_cast<const f16x8*>(Sg + o), d8 = *reinterpret_cast<const f16x8*>(dSg + o);
-#pragma unroll
-      for (int j = 0; j < 8; ++j) a += (float)s8[j] * (float)d8[j];
-    }
-    a = sum64(a);
-    if (lane == 0) red.deL[w] = a;
-    if (t < CH) red.de[t] = red.df[t] = red.db[t] = red.wr[t] = red.wc[t] = red.qd[t] = red.kd[t] = 0.f;
-  }
+  if (t < CH) red.de[t] = red.df[t] = red.db[t] = red.wr[t] = red.wc[t] = red.qd[t] = red.kd[t] = 0.f;
   __syncthreads();
   f32x4 P[2], Gm[2];
   gram_and_T(QN, KN, R, Mt, nullptr, AF, TF, T16, P, Gm);
-
-  const int vc = 16 * w + l16;  // this lane's column of the 64 x 128 results
+  {  // sum(dS' . S) over the 128 x 128 block
+    float a = 0.f;
+#pragma unroll
+    for (int s = 0; s < 4; ++s)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) a += (float)sfr[s][j] * (float)dsfr[s][j];
+    a = sum64(a);
+    if (lane == 0) red.deL[w] = a;
+  }
   // ---- KS = kn S (rows r, columns v); R = V - diag(e) KS; bR -------------
   f32x4 KS[4], RR[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) KS[i] = zero4();
 #pragma unroll
-  for (int s = 0; s < 4; ++s) {
-    const f16x8 b = *reinterpret_cast<const f16x8*>(Sg + (size_t)vc * HD + 32 * s + 8 * lg);
+  for (int s = 0; s < 4; ++s)
 #pragma unroll
-    for (int i = 0; i < 4; ++i) KS[i] = mma_f16(frag_rm(KN, LDW, 16 * i, 32 * s, lane), b, KS[i]);
-  }
+    for (int i = 0; i < 4; ++i) KS[i] = mma_f16(frag_rm(KN, LDW, 16 * i, 32 * s, lane), sfr[s], KS[i]);
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int r = 16 * i + 4 * lg + jj;
-      const float vv = bf(vbase[(size_t)min(r, len - 1) * vrow + vc]) * (r < len ? 1.f : 0.f);
+      const float vv = bf(vraw[i][jj]) * (r < len ? 1.f : 0.f);
       RR[i][jj] = vv - R.e[r] * KS[i][jj];
       BR[r * LDW + vc] = (f16)(R.b[r] * RR[i][jj]);
     }
@@ -692,11 +700,9 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
     for (int i = 0; i < 4; ++i) D[i] = zero4();
 #pragma unroll
-    for (int s = 0; s < 4; ++s) {
-      const f16x8 b = *reinterpret_cast<const f16x8*>(dSg + (size_t)vc * HD + 32 * s + 8 * lg);
+    for (int s = 0; s < 4; ++s)
 #pragma unroll
-      for (int i = 0; i < 4; ++i) D[i] = mma_f16(frag_rm(KN, LDW, 16 * i, 32 * s, lane), b, D[i]);
-    }
+      for (int i = 0; i < 4; ++i) D[i] = mma_f16(frag_rm(KN, LDW, 16 * i, 32 * s, lane), dsfr[s], D[i]);
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
@@ -872,16 +878,14 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
       dkn[i] = mma_f16(frag_rm(DPt, LDN, 16 * i, 32 * s, lane), bq, dkn[i]);
     }
   }
-  // row dots qn . dqn, kn . dkn (fp32 qn, kn from the inputs)
+  // row dots qn . dqn, kn . dkn
   float qf[4][4], kf[4][4];
 #pragma unroll
   for (int i = 0; i < 4; ++i)
 #pragma unroll
     for (int jj = 0; jj < 4; ++jj) {
       const int r = 16 * i + 4 * lg + jj;
-      const size_t o = ((size_t)(tok0 + min(r, len - 1)) * p.H_qk + hq) * HD + vc;
-      const float qr = bf(p.q[o]), kr = bf(p.k[o]);
-      const float m = r < len ? 1.f : 0.f, qx = m * qr / R.nq[r], kx = m * kr / R.nk[r];
+      const float qx = (float)QN[r * LDW + vc], kx = (float)KN[r * LDW + vc];
       qf[i][jj] = qx;
       kf[i][jj] = kx;
       const float qd = rowsum16(qx * dqn[i][jj]), kd = rowsum16(kx * dkn[i][jj]);
