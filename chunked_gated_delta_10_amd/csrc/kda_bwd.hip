@@ -52,13 +52,13 @@ constexpr int BR_PHI = 0;             // record: Phi fragments [8 row tiles][4 s
 constexpr int BR_BC = 32 * FRAG_BYTES;  // Bc fragments [8 row tiles][2 slices]
 static_assert(BR_BC + 16 * FRAG_BYTES == BREC_BYTES, "record size");
 
-struct RowsLds {
+struct __attribute__((aligned(16))) RowsLds {
   float e[CH], f[CH], b[CH], gam[CH], g[CH], nq[CH], nk[CH];
   float eL;
   int len;
 };
 // per-row sums collected across waves (grad kernel)
-struct RedLds {
+struct __attribute__((aligned(16))) RedLds {
   float de[CH], df[CH], db[CH], wr[CH], wc[CH], qd[CH], kd[CH];
   float deL[NTH / 64];
 };
@@ -244,7 +244,7 @@ __device__ __forceinline__ void t_column(const float* AF, float* TF, f32x4 Td, i
 // (transposed) and/or Mr (row-major); A = strict_lower(b Gm . Lam) to AF;
 // then T = (I + A)^-1 into T16 (fp16, row-major).  Ends with a barrier.
 __device__ void gram_and_T(const f16* QN, const f16* KN, const RowsLds& R, f16* Mt, f16* Mr, float* AF, float* TF,
-                           f16* T16, f32x4 (&P)[2], f32x4 (&Gm)[2]) {
+                           f16* T16, f16* Tt16, f32x4 (&P)[2], f32x4 (&Gm)[2]) {
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, l16 = lane & 15, lg = lane >> 4;
   const int rt = w >> 1, ct0 = 2 * (w & 1);
 #pragma unroll
@@ -295,7 +295,9 @@ __device__ void gram_and_T(const f16* QN, const f16* KN, const RowsLds& R, f16* 
   __syncthreads();
   for (int i = t; i < CH * CH; i += NTH) {
     const int r = i >> 6, c = i & 63;
-    T16[r * LDN + c] = (f16)((r >> 4) >= (c >> 4) ? TF[r * LDF + c] : 0.f);
+    const f16 x = (f16)((r >> 4) >= (c >> 4) ? TF[r * LDF + c] : 0.f);
+    T16[r * LDN + c] = x;
+    if (Tt16) Tt16[c * LDN + r] = x;
   }
   __syncthreads();
 }
@@ -313,59 +315,65 @@ __device__ void gram_and_T(const f16* QN, const f16* KN, const RowsLds& R, f16* 
 // so that the C layout of Phi^T and Bc^T is the fragment order of Phi and Bc.
 // ---------------------------------------------------------------------------
 __global__ __launch_bounds__(NTH) void bwd_coef_kernel(BwdParams p) {
-  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * MAT_W + 2 * MAT_N + 2 * MAT_NT];
+  // 72 KB, two workgroups per CU: the fp32 T solve uses QN's space (qn is
+  // read from the inputs after the Gram products) and one 128 x 64 buffer
+  // holds Y1^T, then Z1^T
+  __shared__ __attribute__((aligned(16))) uint8_t smem[2 * MAT_W + 2 * MAT_N + MAT_NT];
   __shared__ RowsLds R;
   __shared__ float be[CH];
   f16* QN = reinterpret_cast<f16*>(smem);
   f16* KN = reinterpret_cast<f16*>(smem + MAT_W);
   f16* M16 = reinterpret_cast<f16*>(smem + 2 * MAT_W);
   f16* T16 = reinterpret_cast<f16*>(smem + 2 * MAT_W + MAT_N);
-  uint8_t* X = smem + 2 * MAT_W + 2 * MAT_N;  // AF, TF; then Y1t, Z1t
+  uint8_t* X = smem + 2 * MAT_W + 2 * MAT_N;
   float* AF = reinterpret_cast<float*>(X);
-  float* TF = reinterpret_cast<float*>(X + MAT_F);
-  f16* Y1t = reinterpret_cast<f16*>(X);
-  f16* Z1t = reinterpret_cast<f16*>(X + MAT_NT);
-  static_assert(2 * MAT_F <= 2 * MAT_NT, "fp32 solve fits the region");
+  float* TF = reinterpret_cast<float*>(smem);  // over QN
+  f16* YZt = reinterpret_cast<f16*>(X);        // Y1^T, then Z1^T
+  static_assert(MAT_F <= MAT_W && MAT_F <= MAT_NT, "fp32 solve fits");
 
   const int job = blockIdx.x, e = job / p.H, h = job - e * p.H, hq = h / (p.H / p.H_qk);
   const int2 ce = entry_of(p, e);
   const int tok0 = ce.x, len = ce.y;
   if (len <= 0) return;
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, l16 = lane & 15, lg = lane >> 4;
+  const int d = 16 * w + l16;  // this lane's key column of the 128-wide results
+  // e_i qn[i][d] for Bc^T's rows i = 32 s + 4 lg + jj (+ 16): raw q entries, loaded first
+  uint16_t qraw[2][2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int i = 32 * s + 16 * hh + 4 * lg + jj;
+        qraw[s][hh][jj] = p.q[((size_t)(tok0 + min(i, len - 1)) * p.H_qk + hq) * HD + d];
+      }
   load_chunk(p, tok0, len, h, hq, QN, KN, R);
   __syncthreads();
   if (t < CH) be[t] = R.b[t] * R.e[t];
   f32x4 P[2], Gm[2];
-  gram_and_T(QN, KN, R, nullptr, M16, AF, TF, T16, P, Gm);
+  gram_and_T(QN, KN, R, nullptr, M16, AF, TF, T16, nullptr, P, Gm);
+  uint8_t* rec = p.brec + (size_t)job * BREC_BYTES;
 
-  // Y1 = T^T diag(f) kn and Z1 = T diag(b e) kn: rows i (4 tiles), columns d (tile w); K = 64
+  // Y1 = T^T diag(f) kn: rows i (4 tiles), columns d (tile w); K = 64
   {
-    f32x4 Y1[4], Z1[4];
+    f32x4 Y1[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) Y1[i] = Z1[i] = zero4();
+    for (int i = 0; i < 4; ++i) Y1[i] = zero4();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       const f16x8 bf_ = frag_cm_scaled(KN, LDW, R.f, 16 * w, 32 * s, lane);
-      const f16x8 bb = frag_cm_scaled(KN, LDW, be, 16 * w, 32 * s, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        Y1[i] = mma_f16(frag_cm(T16, LDN, 16 * i, 32 * s, lane), bf_, Y1[i]);
-        Z1[i] = mma_f16(frag_rm(T16, LDN, 16 * i, 32 * s, lane), bb, Z1[i]);
-      }
+      for (int i = 0; i < 4; ++i) Y1[i] = mma_f16(frag_cm(T16, LDN, 16 * i, 32 * s, lane), bf_, Y1[i]);
     }
     // (the solve's fp32 scratch is dead: gram_and_T ended with a barrier)
-    const int d = 16 * w + l16;
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      *reinterpret_cast<f16x4*>(Y1t + d * LDN + 16 * i + 4 * lg) =
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<f16x4*>(YZt + d * LDN + 16 * i + 4 * lg) =
           f16x4{(f16)Y1[i][0], (f16)Y1[i][1], (f16)Y1[i][2], (f16)Y1[i][3]};
-      *reinterpret_cast<f16x4*>(Z1t + d * LDN + 16 * i + 4 * lg) =
-          f16x4{(f16)Z1[i][0], (f16)Z1[i][1], (f16)Z1[i][2], (f16)Z1[i][3]};
-    }
   }
   __syncthreads();
-  uint8_t* rec = p.brec + (size_t)job * BREC_BYTES;
-  // Phi^T: rows d' (8 tiles), columns d (tile w); K = 64 over tokens
+  // Phi^T = e_L I - Y1^T diag(b e) kn: rows d' (8 tiles), columns d (tile w); K = 64 over tokens
   {
     f32x4 A[8];
 #pragma unroll
@@ -374,9 +382,8 @@ __global__ __launch_bounds__(NTH) void bwd_coef_kernel(BwdParams p) {
     for (int s = 0; s < 2; ++s) {
       const f16x8 bb = frag_cm_scaled(KN, LDW, be, 16 * w, 32 * s, lane);
 #pragma unroll
-      for (int i = 0; i < 8; ++i) A[i] = mma_f16(frag_rm(Y1t, LDN, 16 * i, 32 * s, lane), bb, A[i]);
+      for (int i = 0; i < 8; ++i) A[i] = mma_f16(frag_rm(YZt, LDN, 16 * i, 32 * s, lane), bb, A[i]);
     }
-    const int d = 16 * w + l16;
     const float eL = R.eL;
 #pragma unroll
     for (int s = 0; s < 4; ++s) {
@@ -390,6 +397,24 @@ __global__ __launch_bounds__(NTH) void bwd_coef_kernel(BwdParams p) {
       *reinterpret_cast<f16x8*>(rec + BR_PHI + (w * 4 + s) * FRAG_BYTES + lane * 16) = o;
     }
   }
+  __syncthreads();  // Y1^T read for the last time
+  // Z1 = T diag(b e) kn
+  {
+    f32x4 Z1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) Z1[i] = zero4();
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      const f16x8 bb = frag_cm_scaled(KN, LDW, be, 16 * w, 32 * s, lane);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) Z1[i] = mma_f16(frag_rm(T16, LDN, 16 * i, 32 * s, lane), bb, Z1[i]);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<f16x4*>(YZt + d * LDN + 16 * i + 4 * lg) =
+          f16x4{(f16)Z1[i][0], (f16)Z1[i][1], (f16)Z1[i][2], (f16)Z1[i][3]};
+  }
+  __syncthreads();
   // Bc^T = diag(e) qn - M Z1: rows i (4 tiles), columns d (tile w); K = 64
   {
     f32x4 B[4];
@@ -397,20 +422,21 @@ __global__ __launch_bounds__(NTH) void bwd_coef_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i) B[i] = zero4();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const f16x8 bz = frag_rm(Z1t, LDN, 16 * w, 32 * s, lane);
+      const f16x8 bz = frag_rm(YZt, LDN, 16 * w, 32 * s, lane);
 #pragma unroll
       for (int i = 0; i < 4; ++i) B[i] = mma_f16(frag_rm(M16, LDN, 16 * i, 32 * s, lane), bz, B[i]);
     }
-    const int d = 16 * w + l16;
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
       f16x8 o;
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int i0 = 32 * s + 4 * lg + jj, i1 = i0 + 16;
-        o[jj] = (f16)(R.e[i0] * (float)QN[i0 * LDW + d] - B[2 * s][jj]);
-        o[4 + jj] = (f16)(R.e[i1] * (float)QN[i1 * LDW + d] - B[2 * s + 1][jj]);
-      }
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int i = 32 * s + 16 * hh + 4 * lg + jj;
+          const float qn = i < len ? bf(qraw[s][hh][jj]) / R.nq[i] : 0.f;
+          o[4 * hh + jj] = (f16)(R.e[i] * qn - B[2 * s + hh][jj]);
+        }
       *reinterpret_cast<f16x8*>(rec + BR_BC + (w * 2 + s) * FRAG_BYTES + lane * 16) = o;
     }
   }
@@ -575,7 +601,8 @@ __global__ __launch_bounds__(256) void bwd_adjoint_kernel(BwdParams p) {
 // ---------------------------------------------------------------------------
 namespace {
 // LDS of the grad kernel, bytes
-constexpr int G_QN = 0, G_KN = G_QN + MAT_W, G_MT = G_KN + MAT_W, G_T16 = G_MT + MAT_N, G_DO = G_T16 + MAT_N,
+constexpr int G_QN = 0, G_KN = G_QN + MAT_W, G_MT = G_KN + MAT_W, G_T16 = G_MT + MAT_N, G_TT = G_T16 + MAT_N,
+              G_DO = G_TT + MAT_N,
               G_X = G_DO + MAT_W,             // AF + TF, then bR + U
               G_DU = G_X + 2 * MAT_W, G_DR = G_DU + MAT_W, G_END = G_DR + MAT_W;
 // after the last reads of dO', bR, U, dU, dR: the 64 x 64 results
@@ -593,6 +620,7 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
   f16* KN = reinterpret_cast<f16*>(smem + G_KN);
   f16* Mt = reinterpret_cast<f16*>(smem + G_MT);
   f16* T16 = reinterpret_cast<f16*>(smem + G_T16);
+  f16* Tt16 = reinterpret_cast<f16*>(smem + G_TT);  // T^T, row-major
   f16* DO = reinterpret_cast<f16*>(smem + G_DO);
   float* AF = reinterpret_cast<float*>(smem + G_X);
   float* TF = reinterpret_cast<float*>(smem + G_X + MAT_F);
@@ -650,7 +678,7 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
   if (t < CH) red.de[t] = red.df[t] = red.db[t] = red.wr[t] = red.wc[t] = red.qd[t] = red.kd[t] = 0.f;
   __syncthreads();
   f32x4 P[2], Gm[2];
-  gram_and_T(QN, KN, R, Mt, nullptr, AF, TF, T16, P, Gm);
+  gram_and_T(QN, KN, R, Mt, nullptr, AF, TF, T16, Tt16, P, Gm);
   {  // sum(dS' . S) over the 128 x 128 block
     float a = 0.f;
 #pragma unroll
@@ -728,7 +756,7 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
     for (int s = 0; s < 2; ++s) {
       const f16x8 b = frag_cm(DU, LDW, 16 * w, 32 * s, lane);
 #pragma unroll
-      for (int i = 0; i < 4; ++i) Y[i] = mma_f16(frag_cm(T16, LDN, 16 * i, 32 * s, lane), b, Y[i]);
+      for (int i = 0; i < 4; ++i) Y[i] = mma_f16(frag_rm(Tt16, LDN, 16 * i, 32 * s, lane), b, Y[i]);
     }
 #pragma unroll
     for (int i = 0; i < 4; ++i)
@@ -830,7 +858,7 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
     for (int j = 0; j < 2; ++j) DA[j] = zero4();
 #pragma unroll
     for (int s = 0; s < 2; ++s) {
-      const f16x8 a = frag_cm(T16, LDN, 16 * rt, 32 * s, lane);
+      const f16x8 a = frag_rm(Tt16, LDN, 16 * rt, 32 * s, lane);
 #pragma unroll
       for (int j = 0; j < 2; ++j) DA[j] = mma_f16(a, frag_rm(X1t, LDN, 16 * (ct0 + j), 32 * s, lane), DA[j]);
     }
