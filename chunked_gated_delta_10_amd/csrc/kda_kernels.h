@@ -142,7 +142,7 @@ int recur_grid(int n_chains);
 void launch_decode(const DecodeParams& p, int B, bool bf16_state, bool per_channel, bool delta, hipStream_t stream);
 
 // Backward pass, scalar gate, delta rule (kda_bwd.hip).
-constexpr int BREC_BYTES = 48 * 1024;  // per (entry, head): the adjoint's operand fragments
+constexpr int BREC_BYTES = 56 * 1024;  // per (entry, head): the adjoint's operand fragments and T
 struct BwdParams {
   const uint16_t* q;      // bf16 [tokens, H_qk, 128]
   const uint16_t* k;
@@ -169,6 +169,7 @@ struct BwdParams {
   float* dbeta;           // fp32 [tokens, H]
   float* dA_log;          // fp32 [H]
   float* dinit;           // fp32 [seqs, H, 128, 128] or null
+  int touch_ahead = 0;    // gradient kernel: prefetch the inputs of job + touch_ahead
 };
 // qk_floats: elements of dq (= of dk), cleared first when value heads share q/k heads.
 void launch_bwd(const BwdParams& p, size_t qk_floats, hipStream_t stream);
