@@ -29,7 +29,7 @@ D, C = 128, 64                 # head dim, chunk length
 FLOP_PER_TOKEN_HEAD = 6 * D * D + 5 * C * D   # 139,264 (algorithmic, per token and head)
 KERNEL_SOURCES = ["chunked_gated_delta_10_amd/csrc/" + f for f in
                   ("kda_chunk.hip", "kda_chunk_job.h", "kda_fused.hip", "kda_recur.hip", "kda_table.hip",
-                   "kda_decode.hip", "kda_device.h", "kda_kernels.h")]
+                   "kda_decode.hip", "kda_device.h", "kda_kernels.h", "kda_bwd.hip")]
 
 
 def algorithmic_bytes(w, with_state=True, state_bytes=4):
@@ -48,6 +48,25 @@ def algorithmic_bytes(w, with_state=True, state_bytes=4):
     chain = v + out + s_in + s_out
     # the fused kernel does both parts in one launch
     return {"kda_chunk_local": local, "kda_recur": chain, "kda_fused": local + chain}
+
+
+def backward_bytes(w):
+    """The backward operator's own inputs read once and outputs written once (bytes): q, k, v, dout (bf16),
+    g_raw (bf16), beta logits (fp32) in; dq, dk, dv, dg_raw, dbeta (fp32) out.  The gradient kernel touches
+    all of them.  The recomputed forward, the chunk states and the adjoint's records are the method's own
+    intermediates and are not counted."""
+    tok = w.B * w.T
+    C_ = w.N if w.N else w.B
+    reads = 2 * tok * w.H_qk * D * 2 + 2 * tok * w.H * D * 2 + tok * w.H * (2 + 4)
+    writes = 2 * tok * w.H_qk * D * 4 + tok * w.H * D * 4 + 2 * tok * w.H * 4
+    return {"kda_bwd_grad": reads + writes, "total": reads + writes + w.H * 8 + C_ * w.H * D * D * 4}
+
+
+# Algorithmic FLOP per token-head of the backward: the recomputed forward (FLOP_PER_TOKEN_HEAD) plus the
+# chunk form's products per 64-token chunk: seven C x D x D (kn dS', dO' S^T, dV S^T, U dS'^T, kn S, and
+# the adjoint's qn^T dO', kn^T Z), ten C x C x D (M^T dO', T^T dU, U, dO' U^T, dU (bR)^T, dP kn, dGm kn,
+# dP^T qn, qn kn^T, kn kn^T) and two C x C x C (dA = -T^T dT T^T): 548,864 in all.
+BWD_FLOP_PER_TOKEN_HEAD = FLOP_PER_TOKEN_HEAD + 2 * (7 * C * D * D + 10 * C * C * D + 2 * C ** 3) // C
 
 
 def sources_hash():
@@ -152,7 +171,9 @@ def traffic_from(root, copy_bytes, workload="kda_dense"):
                            "fetch_factor": kf, "write_factor": kw}
     rec = {}
     for kern, tags in (("kda_chunk_local", ("chunk_local_kernel", "chunk_group_kernel")), ("kda_recur", ("recur_",)),
-                       ("kda_table", ("table_kernel",)), ("kda_fused", ("fused_kernel",))):
+                       ("kda_table", ("table_kernel",)), ("kda_fused", ("fused_kernel",)),
+                       ("kda_bwd_coef", ("bwd_coef",)), ("kda_bwd_adjoint", ("bwd_adjoint",)),
+                       ("kda_bwd_grad", ("bwd_grad",))):
         f = _per_dispatch_kib(run_f, "FETCH_SIZE", lambda k, t=tags: any(x in k for x in t))
         w = _per_dispatch_kib(run_w, "WRITE_SIZE", lambda k, t=tags: any(x in k for x in t))
         if f is None or w is None:
@@ -234,7 +255,16 @@ def time_workload(name, steps, warmup, bf16_state=False):
     inp = workload_inputs(name)
     sdt = torch.bfloat16 if bf16_state else torch.float32
     d = device_inputs(inp, sdt)
-    if w.decode:
+    if w.backward:
+        from chunked_gated_delta_10_amd.inputs import backward_upstream
+        dout_bits, _ = backward_upstream(inp, w.seed + 1000)
+        dout = torch.from_numpy(dout_bits.view("int16")).view(torch.bfloat16).cuda()
+        ws = torch.empty(kda.bwd_workspace_bytes(w.B, w.T, w.H_qk, w.H, w.N), dtype=torch.uint8, device="cuda")
+
+        def step():
+            kda.bwd_varlen(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], dout, d["cu_seqlens"],
+                           scale=inp["scale"], workspace=ws)
+    elif w.decode:
         st = d["initial_state"]
         out = torch.empty((w.B, w.H, D), dtype=torch.bfloat16, device="cuda")
 
@@ -363,7 +393,8 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=1024 * 1024 * 1024,
                     help="size of the calibration copy used with --traffic-from")
     ap.add_argument("--only", metavar="WORKLOAD",
-                    help="only time one workload (kda_tiny, kda_dense, kda_varlen, gdn_gva, kda_decode, la_varlen, la_decode) and print "
+                    help="only time one workload (kda_tiny, kda_dense, kda_varlen, gdn_gva, kda_decode, la_varlen, la_decode, "
+                         "gdn_bwd) and print "
                          "its per-kernel averages; for profiling runs")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the grouped-value-head sweep (head shapes x sequence patterns)")
@@ -432,17 +463,28 @@ def main():
         # the bf16-state variant of the headline shape first, with the headline's step count, before anything
         # else runs (measured after the copy probe or the decode runs, both of its kernels ran ~10% slower,
         # the chunk-local one included, which never touches the state)
-        for other in ("kda_dense_bf16_state", "kda_varlen", "gdn_gva", "kda_decode", "la_varlen", "la_decode"):
+        for other in ("kda_dense_bf16_state", "kda_varlen", "gdn_gva", "kda_decode", "la_varlen", "la_decode",
+                      "gdn_bwd"):
             bf16_state = other.endswith("_bf16_state")
             osteps = args.steps if bf16_state else max(10, args.steps // 5)
             oms, opk, _, ow, _ = time_workload(other.replace("_bf16_state", ""), osteps, 10, bf16_state=bf16_state)
             ab = algorithmic_bytes(ow, state_bytes=2 if bf16_state else 4)
             tok = ow.B if ow.decode else ow.B * ow.T
-            tot = ab["kda_fused"]
+            tot = backward_bytes(ow)["total"] if ow.backward else ab["kda_fused"]
             extra[other] = {"ms_per_step": round(oms, 4), "tokens_per_s": round(tok / (oms * 1e-3), 1),
                             "algorithmic_bytes": tot,
                             "hbm_frac": round(tot / (oms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                             "kernels_avg_ms": {k: round(v, 4) for k, v in opk.items()}}
+            if ow.backward and "kda_bwd_grad" in opk:
+                gb = backward_bytes(ow)["kda_bwd_grad"]
+                ach = gb / (opk["kda_bwd_grad"] * 1e-3) / 1e9
+                fl = BWD_FLOP_PER_TOKEN_HEAD * tok * ow.H
+                extra[other]["roofline"] = {
+                    "bound": "hbm", "kernel": "kda_bwd_grad", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                    "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": load_traffic("kda_bwd_grad", other),
+                    "algorithmic_bytes_per_launch": gb, "avg_launch_ms": round(opk["kda_bwd_grad"], 4),
+                    "step": {"algorithmic_flop": fl,
+                             "mfma_frac": round(fl / (oms * 1e-3) / 1e12 / MFMA_PEAK_TFLOPS, 4)}}
         result["other_workloads"] = extra
     # after every timed workload: the probe's 2 GiB of buffers are allocated and freed last
     result["hbm_copy_gbs"] = copy_bandwidth()

@@ -93,8 +93,12 @@ bool takes_fused(bool delta, int gate_per_channel) {
 }
 
 // ---- per-kernel event timing (diagnostics) --------------------------------
-enum { K_TABLE = 0, K_CHUNK = 1, K_RECUR = 2, K_DECODE = 3, K_FUSED = 4, K_COUNT = 5 };
-const char* const kKernelNames[K_COUNT] = {"kda_table", "kda_chunk_local", "kda_recur", "kda_decode", "kda_fused"};
+enum {
+  K_TABLE = 0, K_CHUNK = 1, K_RECUR = 2, K_DECODE = 3, K_FUSED = 4, K_BWD_COEF = 5, K_BWD_ADJ = 6, K_BWD_GRAD = 7,
+  K_COUNT = 8
+};
+const char* const kKernelNames[K_COUNT] = {"kda_table",    "kda_chunk_local", "kda_recur",       "kda_decode",
+                                           "kda_fused",    "kda_bwd_coef",    "kda_bwd_adjoint", "kda_bwd_grad"};
 
 struct Timing {
   bool on = false;
@@ -436,6 +440,7 @@ kda_status run_backward(const BwdArgs& a) {
   (void)hipGetLastError();
   if (a.cu) {
     kda::TableParams tp{a.cu, a.n_seqs, a.T, n_entries, seqs, chunks, order};
+    Timed t(K_TABLE, a.stream);
     kda::launch_table(tp, a.stream);
   }
   // the forward again, keeping the state entering every chunk
@@ -443,11 +448,15 @@ kda_status run_backward(const BwdArgs& a) {
     const kda::ChunkParams cp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                               static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log, chunks, a.H, a.H_qk,
                               ws + L.F.rec, a.cu ? 0 : a.T, static_cast<const uint16_t*>(a.v)};
-    const hipError_t e = kda::launch_chunk_local(cp, n_entries, false, true, a.stream);
-    if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel setup failed: %s", hipGetErrorString(e));
+    {
+      Timed t(K_CHUNK, a.stream);
+      const hipError_t e = kda::launch_chunk_local(cp, n_entries, false, true, a.stream);
+      if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel setup failed: %s", hipGetErrorString(e));
+    }
     kda::RecurParams rp{ws + L.F.rec, seqs, order, a.n_seqs * a.H, n_entries, a.H, a.H_qk,
                         static_cast<const uint16_t*>(a.v), nullptr, a.s0, nullptr, a.scale, sink,
                         a.cu ? -1 : a.T, err, states};
+    Timed t(K_RECUR, a.stream);
     kda::launch_recur_states(rp, false, a.stream);
   }
   kda::BwdParams bp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
@@ -456,7 +465,11 @@ kda_status run_backward(const BwdArgs& a) {
                     seqs, order, tokens > 0 ? n_entries : 0, a.n_seqs * a.H, states,
                     reinterpret_cast<uint16_t*>(ws + L.dstates), ws + L.brec, a.dq, a.dk, a.dv, a.dg_raw, a.dbeta,
                     a.dA_log, a.dinit};
-  kda::launch_bwd(bp, (size_t)tokens * a.H_qk * kda::HD, a.stream);
+  const int ids[3] = {K_BWD_COEF, K_BWD_ADJ, K_BWD_GRAD};
+  for (int stage = 0; stage < 3; ++stage) {
+    Timed t(ids[stage], a.stream);
+    kda::launch_bwd(bp, (size_t)tokens * a.H_qk * kda::HD, stage, a.stream);
+  }
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel launch failed: %s", hipGetErrorString(e));
   if (env_flag("KDA_LOG"))

@@ -1005,21 +1005,23 @@ __global__ __launch_bounds__(256) void bwd_fill_kernel(float* a, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) a[i] = 0.f;
 }
 
-void launch_bwd(const BwdParams& p, size_t qk_floats, hipStream_t stream) {
+void launch_bwd(const BwdParams& p, size_t qk_floats, int stage, hipStream_t stream) {
   const int jobs = p.n_entries * p.H;
-  if (p.H != p.H_qk && qk_floats > 0) {  // dq, dk are accumulated over each group's value heads
-    bwd_fill_kernel<<<1024, 256, 0, stream>>>(p.dq, qk_floats);
-    bwd_fill_kernel<<<1024, 256, 0, stream>>>(p.dk, qk_floats);
-  }
-  bwd_fill_kernel<<<1, 256, 0, stream>>>(p.dA_log, (size_t)p.H);
-  if (jobs > 0) bwd_coef_kernel<<<jobs, NTH, 0, stream>>>(p);
-  if (p.n_chains > 0) {  // the widest column tiles that keep every workgroup resident (two per CU)
-    const int slots = 2 * device_cu_count(), g8 = (p.n_chains + 7) / 8 * 8;
-    if (g8 * 8 <= slots) bwd_adjoint_kernel<1><<<g8 * 8, 256, 0, stream>>>(p);
-    else if (g8 * 4 <= slots) bwd_adjoint_kernel<2><<<g8 * 4, 256, 0, stream>>>(p);
-    else bwd_adjoint_kernel<4><<<g8 * 2, 256, 0, stream>>>(p);
-  }
-  if (jobs > 0) {
+  if (stage == 0) {
+    if (p.H != p.H_qk && qk_floats > 0) {  // dq, dk are accumulated over each group's value heads
+      bwd_fill_kernel<<<1024, 256, 0, stream>>>(p.dq, qk_floats);
+      bwd_fill_kernel<<<1024, 256, 0, stream>>>(p.dk, qk_floats);
+    }
+    bwd_fill_kernel<<<1, 256, 0, stream>>>(p.dA_log, (size_t)p.H);
+    if (jobs > 0) bwd_coef_kernel<<<jobs, NTH, 0, stream>>>(p);
+  } else if (stage == 1) {
+    if (p.n_chains > 0) {  // the widest column tiles that keep every workgroup resident (two per CU)
+      const int slots = 2 * device_cu_count(), g8 = (p.n_chains + 7) / 8 * 8;
+      if (g8 * 8 <= slots) bwd_adjoint_kernel<1><<<g8 * 8, 256, 0, stream>>>(p);
+      else if (g8 * 4 <= slots) bwd_adjoint_kernel<2><<<g8 * 4, 256, 0, stream>>>(p);
+      else bwd_adjoint_kernel<4><<<g8 * 2, 256, 0, stream>>>(p);
+    }
+  } else if (jobs > 0) {
     BwdParams q = p;
     q.touch_ahead = device_cu_count();
     bwd_grad_kernel<<<jobs, NTH, 0, stream>>>(q);

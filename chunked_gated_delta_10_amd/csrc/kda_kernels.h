@@ -171,7 +171,8 @@ struct BwdParams {
   float* dinit;           // fp32 [seqs, H, 128, 128] or null
   int touch_ahead = 0;    // gradient kernel: prefetch the inputs of job + touch_ahead
 };
-// qk_floats: elements of dq (= of dk), cleared first when value heads share q/k heads.
-void launch_bwd(const BwdParams& p, size_t qk_floats, hipStream_t stream);
+// Stages, in this order: 0 the coefficient records (after clearing dA_log, and dq, dk when value heads
+// share q/k heads; qk_floats: elements of dq), 1 the adjoint chain, 2 the gradients.
+void launch_bwd(const BwdParams& p, size_t qk_floats, int stage, hipStream_t stream);
 
 }  // namespace kda

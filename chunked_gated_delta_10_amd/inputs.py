@@ -56,6 +56,8 @@ class Workload:
     decode: bool = False
     seed: int = 0
     delta: bool = True                          # False: decay-only linear attention (no beta)
+    lengths: Optional[Tuple[int, ...]] = None   # packed sequence lengths (default: random, see varlen_lengths)
+    backward: bool = False                      # the backward pass (upstream gradient from backward_upstream)
     K: int = HEAD_DIM
     V: int = HEAD_DIM
     note: str = ""
@@ -87,6 +89,11 @@ WORKLOADS: Dict[str, Workload] = {
     "la_decode": Workload("la_decode", B=256, T=1, H=64, H_qk=64, gate_per_channel=False, A_log=(0.0, 0.0),
                           state_std=0.02, decode=True, seed=1006, delta=False,
                           note="decay-only linear attention decode, B=256 H=64, fp32 state in place"),
+    # the backward of the gated delta rule (the FlashQLA H200 page's backward table: sequences split into 8,
+    # here its 32-head, 32k-token row)
+    "gdn_bwd": Workload("gdn_bwd", B=1, T=32768, H=32, H_qk=32, gate_per_channel=False, A_log=(0.0, 0.0), N=8,
+                        lengths=(4096,) * 8, seed=1007, backward=True,
+                        note="gated delta rule backward, scalar decay, 8 sequences x 4096 tokens, 32 heads"),
 }
 
 
@@ -172,7 +179,23 @@ def make_inputs(B: int, T: int, H: int, H_qk: int, *, gate_per_channel: bool = T
 def workload_inputs(name: str) -> dict:
     w = WORKLOADS[name]
     return make_inputs(w.B, w.T, w.H, w.H_qk, gate_per_channel=w.gate_per_channel, A_log=w.A_log,
-                       state_std=w.state_std, N=w.N, seed=w.seed, K=w.K, V=w.V, decode=w.decode)
+                       state_std=w.state_std, N=w.N, lengths=w.lengths, seed=w.seed, K=w.K, V=w.V,
+                       decode=w.decode)
+
+
+def backward_upstream(inp: dict, seed: int, dfinal_std: Optional[float] = None):
+    """Upstream gradients for a backward call: dout ~ N(0, 1) stored bf16 (bits), shaped like the output,
+    and dfinal ~ N(0, dfinal_std^2) fp32 in the state layout (None: no final-state gradient)."""
+    rng = np.random.default_rng(seed)
+    B, T, H, V = inp["v"].shape
+    cu = inp.get("cu_seqlens")
+    C = B if cu is None else len(cu) - 1
+    K = inp["q"].shape[-1]
+    dout = bf16_bits(rng.standard_normal((B, T, H, V), dtype=np.float32))
+    dfinal = None
+    if dfinal_std is not None:
+        dfinal = (rng.standard_normal((C, H, V, K), dtype=np.float32) * np.float32(dfinal_std)).astype(np.float32)
+    return dout, dfinal
 
 
 # Grouped-value-head sweep (the forward table of the FlashQLA H200 benchmark

@@ -174,7 +174,7 @@ def kernel_timing(enable: bool) -> None:
 def kernel_timing_read() -> dict:
     """{kernel name: (total ms, launches)} since the last read (waits for the events)."""
     lib = load()
-    n = 8
+    n = 16
     ms = (ctypes.c_double * n)()
     cnt = (ctypes.c_int * n)()
     k = lib.kda_kernel_timing_read(ms, cnt, n)

@@ -252,8 +252,9 @@ kda_status kda_bwd_varlen(const void* q, const void* k, const void* v, const voi
  * milliseconds and launch count per kernel id into the caller's arrays
  * (up to max_kernels entries), forgets them, and returns the number of
  * kernel ids (or -1 on a HIP error).  Kernel ids: 0 schedule, 1 chunk-local,
- * 2 recurrence, 3 decode, 4 fused forward.  The events are created by the
- * library and reused.
+ * 2 recurrence, 3 decode, 4 fused forward, 5 backward coefficients,
+ * 6 backward adjoint, 7 backward gradients (the backward's recomputed forward
+ * reports as 1 and 2).  The events are created by the library and reused.
  */
 void kda_kernel_timing_enable(int enable);
 int kda_kernel_timing_read(double* total_ms, int* launches, int max_kernels);
