@@ -95,10 +95,11 @@ bool takes_fused(bool delta, int gate_per_channel) {
 // ---- per-kernel event timing (diagnostics) --------------------------------
 enum {
   K_TABLE = 0, K_CHUNK = 1, K_RECUR = 2, K_DECODE = 3, K_FUSED = 4, K_BWD_COEF = 5, K_BWD_ADJ = 6, K_BWD_GRAD = 7,
-  K_COUNT = 8
+  K_BWD_STATES = 8, K_COUNT = 9
 };
 const char* const kKernelNames[K_COUNT] = {"kda_table",    "kda_chunk_local", "kda_recur",       "kda_decode",
-                                           "kda_fused",    "kda_bwd_coef",    "kda_bwd_adjoint", "kda_bwd_grad"};
+                                           "kda_fused",    "kda_bwd_coef",    "kda_bwd_adjoint", "kda_bwd_grad",
+                                           "kda_bwd_states"};
 
 struct Timing {
   bool on = false;
@@ -361,19 +362,21 @@ kda_status run_decode(const void* q, const void* k, const void* v, const void* g
 }
 
 // ---- backward (scalar gate) ------------------------------------------------
-// Workspace: the forward's (schedule, sink, chunk records), then the state
-// entering every (chunk, head) and the gradient of the state leaving it
-// (fp16, 32 KiB each), and the adjoint's operand records (48 KiB each).
+// Workspace: a 256-byte header, the schedule (sequence table, chunk table,
+// order), then the state entering every (chunk, head) and the gradient of
+// the state leaving it (fp16, 32 KiB each), and the chains' operator records
+// (kda::BREC_BYTES each).
 struct BwdLayout {
-  Layout F;
-  size_t states, dstates, brec, total;
+  size_t seqs, chunks, order, states, dstates, brec, total;
 };
 
 BwdLayout bwd_layout(int n_seqs, int n_entries, int H) {
   BwdLayout L;
-  L.F = layout(n_seqs, n_entries, H, false);
   const size_t jobs = (size_t)n_entries * H;
-  L.states = L.F.total;
+  L.seqs = ALIGN;
+  L.chunks = L.seqs + round_up((size_t)n_seqs * sizeof(int4));
+  L.order = L.chunks + round_up((size_t)n_entries * sizeof(int4));
+  L.states = L.order + round_up((size_t)n_seqs * sizeof(int));
   L.dstates = L.states + round_up(jobs * kda::HD * kda::HD * sizeof(uint16_t));
   L.brec = L.dstates + round_up(jobs * kda::HD * kda::HD * sizeof(uint16_t));
   L.total = L.brec + round_up(jobs * kda::BREC_BYTES);
@@ -431,42 +434,24 @@ kda_status run_backward(const BwdArgs& a) {
   if (reinterpret_cast<uintptr_t>(a.ws) & (ALIGN - 1)) return fail(KDA_ERR_ALIGN, "workspace is not 256-byte aligned");
 
   uint8_t* ws = static_cast<uint8_t*>(a.ws);
-  int4* seqs = reinterpret_cast<int4*>(ws + L.F.seqs);
-  int4* chunks = reinterpret_cast<int4*>(ws + L.F.chunks);
-  int* order = reinterpret_cast<int*>(ws + L.F.order);
-  int* err = reinterpret_cast<int*>(ws);
-  uint16_t* sink = reinterpret_cast<uint16_t*>(ws + L.F.sink);
-  uint16_t* states = reinterpret_cast<uint16_t*>(ws + L.states);
+  int4* seqs = reinterpret_cast<int4*>(ws + L.seqs);
+  int4* chunks = reinterpret_cast<int4*>(ws + L.chunks);
+  int* order = reinterpret_cast<int*>(ws + L.order);
   (void)hipGetLastError();
   if (a.cu) {
     kda::TableParams tp{a.cu, a.n_seqs, a.T, n_entries, seqs, chunks, order};
     Timed t(K_TABLE, a.stream);
     kda::launch_table(tp, a.stream);
   }
-  // the forward again, keeping the state entering every chunk
-  if (n_entries > 0 && tokens > 0) {
-    const kda::ChunkParams cp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
-                              static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log, chunks, a.H, a.H_qk,
-                              ws + L.F.rec, a.cu ? 0 : a.T, static_cast<const uint16_t*>(a.v)};
-    {
-      Timed t(K_CHUNK, a.stream);
-      const hipError_t e = kda::launch_chunk_local(cp, n_entries, false, true, a.stream);
-      if (e != hipSuccess) return fail(KDA_ERR_HIP, "kernel setup failed: %s", hipGetErrorString(e));
-    }
-    kda::RecurParams rp{ws + L.F.rec, seqs, order, a.n_seqs * a.H, n_entries, a.H, a.H_qk,
-                        static_cast<const uint16_t*>(a.v), nullptr, a.s0, nullptr, a.scale, sink,
-                        a.cu ? -1 : a.T, err, states};
-    Timed t(K_RECUR, a.stream);
-    kda::launch_recur_states(rp, false, a.stream);
-  }
   kda::BwdParams bp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                     static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log,
-                    static_cast<const uint16_t*>(a.dout), a.dfinal, a.scale, a.H, a.H_qk, a.cu ? -1 : a.T, chunks,
-                    seqs, order, tokens > 0 ? n_entries : 0, a.n_seqs * a.H, states,
-                    reinterpret_cast<uint16_t*>(ws + L.dstates), ws + L.brec, a.dq, a.dk, a.dv, a.dg_raw, a.dbeta,
-                    a.dA_log, a.dinit};
-  const int ids[3] = {K_BWD_COEF, K_BWD_ADJ, K_BWD_GRAD};
-  for (int stage = 0; stage < 3; ++stage) {
+                    static_cast<const uint16_t*>(a.dout), a.dfinal, a.s0, a.scale, a.H, a.H_qk, a.cu ? -1 : a.T,
+                    chunks, seqs, order, tokens > 0 ? n_entries : 0, a.n_seqs * a.H,
+                    reinterpret_cast<uint16_t*>(ws + L.states), reinterpret_cast<uint16_t*>(ws + L.dstates),
+                    ws + L.brec, a.dq, a.dk, a.dv, a.dg_raw, a.dbeta, a.dA_log, a.dinit};
+  // coefficients; the forward chain (chunk states); the adjoint chain; the gradients
+  const int ids[4] = {K_BWD_COEF, K_BWD_STATES, K_BWD_ADJ, K_BWD_GRAD};
+  for (int stage = 0; stage < 4; ++stage) {
     Timed t(ids[stage], a.stream);
     kda::launch_bwd(bp, (size_t)tokens * a.H_qk * kda::HD, stage, a.stream);
   }

@@ -25,12 +25,14 @@
 //   column sums, with the e, f and e_L terms, give dG and dg = its reverse
 //   cumulative sum; then the prologue (norms, gate, sigmoid) in reverse.
 //
-// Kernels, after the forward's chunk-local kernel and a recurrence that
-// stores the state entering every chunk (fp16):
-//   coef_kernel     per (chunk, head): Phi and Bc as fp16 operand fragments
-//   adjoint_kernel  per (chain, value-column tile): dS over chunks, last to
-//                   first; stores dS' of every chunk (fp16) and dS_0 (fp32)
-//   grad_kernel     per (chunk, head): every input gradient of the chunk
+// The forward is linear in the state as well: S_c+1 = Phi^T S_c + Gc V with
+// Gc = kn^T diag(f) T diag(b), so both chains are the same kernel.  Kernels:
+//   coef_kernel   per (chunk, head): Phi, Phi^T, Bc, Gc as fp16 operand
+//                 fragments, and T
+//   chain_kernel  per (chain, value-column tile), FWD: the state entering
+//                 every chunk (fp16); then, last chunk first, dS' of every
+//                 chunk (fp16) and dS_0 (fp32)
+//   grad_kernel   per (chunk, head): every input gradient of the chunk
 // Products run on fp16 matrix cores with fp32 accumulation (the precision of
 // the forward's chunk path); T = (I + A)^-1 is formed in fp32.
 #include <algorithm>
@@ -53,7 +55,9 @@ constexpr int MAT_F = CH * LDF * 4;   // 64 x 64 fp32
 constexpr int BR_PHI = 0;             // record: Phi fragments [8 row tiles][4 slices]
 constexpr int BR_BC = 32 * FRAG_BYTES;  // Bc fragments [8 row tiles][2 slices]
 constexpr int BR_T = BR_BC + 16 * FRAG_BYTES;  // T, fp16 [64][64]
-static_assert(BR_T + CH * CH * 2 == BREC_BYTES, "record size");
+constexpr int BR_PHIT = BR_T + CH * CH * 2;    // Phi^T fragments [8 row tiles][4 slices]
+constexpr int BR_GC = BR_PHIT + 32 * FRAG_BYTES;  // Gc fragments [8 row tiles][2 slices]
+static_assert(BR_GC + 16 * FRAG_BYTES == BREC_BYTES, "record size");
 
 struct __attribute__((aligned(16))) RowsLds {
   float e[CH], f[CH], b[CH], gam[CH], g[CH], nq[CH], nk[CH];
@@ -318,7 +322,8 @@ __device__ void gram_and_T(const f16* QN, const f16* KN, const RowsLds& R, f16* 
 //   Z1 = T diag(b e) kn,  Bc^T = diag(e) qn - M Z1,
 // so that the C layout of Phi^T and Bc^T is the fragment order of Phi and Bc.
 // ---------------------------------------------------------------------------
-__global__ __launch_bounds__(NTH) void bwd_coef_kernel(BwdParams p) {
+// two workgroups per CU: at least four waves per SIMD
+__global__ __launch_bounds__(NTH, 4) void bwd_coef_kernel(BwdParams p) {
   // 72 KB, two workgroups per CU: the fp32 T solve uses QN's space (qn is
   // read from the inputs after the Gram products) and one 128 x 64 buffer
   // holds Y1^T, then Z1^T
@@ -378,6 +383,16 @@ __global__ __launch_bounds__(NTH) void bwd_coef_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i)
       *reinterpret_cast<f16x4*>(YZt + d * LDN + 16 * i + 4 * lg) =
           f16x4{(f16)Y1[i][0], (f16)Y1[i][1], (f16)Y1[i][2], (f16)Y1[i][3]};
+    // Gc = kn^T diag(f) T diag(b): its transpose is diag(b) Y1, rows i, columns d
+#pragma unroll
+    for (int s = 0; s < 2; ++s) {
+      f16x8 o;
+#pragma unroll
+      for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) o[4 * hh + jj] = (f16)(R.b[32 * s + 16 * hh + 4 * lg + jj] * Y1[2 * s + hh][jj]);
+      *reinterpret_cast<f16x8*>(rec + BR_GC + (w * 2 + s) * FRAG_BYTES + lane * 16) = o;
+    }
   }
   __syncthreads();
   // Phi^T = e_L I - Y1^T diag(b e) kn: rows d' (8 tiles), columns d (tile w); K = 64 over tokens
@@ -402,6 +417,33 @@ __global__ __launch_bounds__(NTH) void bwd_coef_kernel(BwdParams p) {
         o[4 + jj] = (f16)((d1 == d ? eL : 0.f) - A[2 * s + 1][jj]);
       }
       *reinterpret_cast<f16x8*>(rec + BR_PHI + (w * 4 + s) * FRAG_BYTES + lane * 16) = o;
+    }
+  }
+  // Phi = e_L I - (diag(b e) kn)^T Y1: rows d (8 tiles), columns d' (tile w); its C layout is the
+  // fragment order of Phi^T, the forward chain's operator
+  {
+    const f16x8 by0 = frag_rm(YZt, LDN, 16 * w, 0, lane), by1 = frag_rm(YZt, LDN, 16 * w, 32, lane);
+    const float eL = R.eL;
+#pragma unroll
+    for (int half = 0; half < 2; ++half) {  // row tiles 4 half .. 4 half + 3: slices 2 half, 2 half + 1
+      f32x4 A[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        A[i] = mma_f16(frag_cm_scaled(KN, LDW, be, 16 * (4 * half + i), 0, lane), by0, zero4());
+        A[i] = mma_f16(frag_cm_scaled(KN, LDW, be, 16 * (4 * half + i), 32, lane), by1, A[i]);
+      }
+#pragma unroll
+      for (int s2 = 0; s2 < 2; ++s2) {
+        const int s = 2 * half + s2;
+        f16x8 o;
+#pragma unroll
+        for (int jj = 0; jj < 4; ++jj) {
+          const int d0 = 32 * s + 4 * lg + jj, d1 = d0 + 16;
+          o[jj] = (f16)((d0 == d ? eL : 0.f) - A[2 * s2][jj]);
+          o[4 + jj] = (f16)((d1 == d ? eL : 0.f) - A[2 * s2 + 1][jj]);
+        }
+        *reinterpret_cast<f16x8*>(rec + BR_PHIT + (w * 4 + s) * FRAG_BYTES + lane * 16) = o;
+      }
     }
   }
   __syncthreads();  // Y1^T read for the last time
@@ -450,19 +492,25 @@ __global__ __launch_bounds__(NTH) void bwd_coef_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// adjoint_kernel: per (chain, 16 NCT value columns), dS = Phi dS' + Bc dO'
-// over the chain's chunks, last first.  Wave w holds rows 32 w .. 32 w + 31
-// of dS for every column tile in C layout (fp32); the four waves' rows,
-// converted to fp16, are the B operand of the next step, and the dO'
-// fragments (loaded once per workgroup, a share per wave) go the same way:
-// both through LDS, one barrier per chunk.  The record fragments and dO' of
-// the next chunk are loaded while the current one is processed.
+// chain_kernel: the two chains over a sequence's chunks, one workgroup per
+// (chain, 16 NCT value columns).
+//   FWD:  S_c+1 = Phi^T S_c + Gc V_c, first chunk first, from the initial
+//         state; stores S_c (the state entering chunk c, fp16).
+//   else: dS_c = Phi dS' + Bc dO', last chunk first, from dfinal; stores dS'
+//         (the gradient of the state leaving chunk c, fp16) and dS_0 (fp32).
+// Wave w holds rows 32 w .. 32 w + 31 of the state for every column tile in
+// C layout (fp32); the four waves' rows, converted to fp16, are the B operand
+// of the next step, and the token-row fragments (V or dO', loaded once per
+// workgroup, a share per wave) go the same way: both through LDS, one
+// barrier per chunk.  The next chunk's operator fragments and token rows are
+// loaded while the current chunk is processed.
 // ---------------------------------------------------------------------------
-template <int NCT>
-__global__ __launch_bounds__(256) void bwd_adjoint_kernel(BwdParams p) {
+template <int NCT, bool FWD>
+__global__ __launch_bounds__(256, 2) void bwd_chain_kernel(BwdParams p) {  // two workgroups per CU
   constexpr int NW = 8 / NCT;       // workgroups per chain
-  constexpr int NF = 2 * NCT;       // dO' fragments per chunk (column tile, token slice)
+  constexpr int NF = 2 * NCT;       // token-row fragments per chunk (column tile, token slice)
   constexpr int FPW = (NF + 3) / 4;  // of which each wave loads up to FPW
+  constexpr int OFF_A = FWD ? BR_PHIT : BR_PHI, OFF_B = FWD ? BR_GC : BR_BC;
   __shared__ __attribute__((aligned(16))) f16x8 sB[2][NCT][4][64];
   __shared__ __attribute__((aligned(16))) f16x8 sD[2][NF][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
@@ -486,21 +534,24 @@ __global__ __launch_bounds__(256) void bwd_adjoint_kernel(BwdParams p) {
   const int nch = max(0, min((len + CH - 1) / CH, p.n_entries - chunk0));
   const int v0 = 16 * NCT * vt;
   const size_t sbase = ((size_t)n * p.H + h) * HD * HD;
-  f32x4 dS[NCT][2];
+  const float* s_in = FWD ? p.s0 : p.dfinal;
+  f32x4 S[NCT][2];
 #pragma unroll
   for (int j = 0; j < NCT; ++j)
 #pragma unroll
     for (int i = 0; i < 2; ++i) {
       const size_t o = sbase + (size_t)(v0 + 16 * j + l16) * HD + 32 * w + 16 * i + 4 * lg;
-      if (p.dfinal) {
-        const float4 x4 = *reinterpret_cast<const float4*>(p.dfinal + o);
-        dS[j][i] = f32x4{x4.x, x4.y, x4.z, x4.w};
+      if (s_in) {
+        const float4 x4 = *reinterpret_cast<const float4*>(s_in + o);
+        S[j][i] = f32x4{x4.x, x4.y, x4.z, x4.w};
       } else {
-        dS[j][i] = zero4();
+        S[j][i] = zero4();
       }
     }
   const size_t vstride = (size_t)p.H * HD;
-  // raw dO' values are kept as loaded and converted in step(): a load's
+  const uint16_t* rows = FWD ? p.v : p.dout;
+  const float rscale = FWD ? 1.f : p.scale;
+  // raw token-row values are kept as loaded and converted in step(): a load's
   // result used right away would make the wait cover the prefetches issued
   // before it (the memory counter drains in order)
   struct Frags {
@@ -508,9 +559,10 @@ __global__ __launch_bounds__(256) void bwd_adjoint_kernel(BwdParams p) {
     uint16_t d[FPW][8];
   };
   auto load = [&](Frags& F, int c) {
-    // dO' first: tokens of slice s in fragment order (rows past the chunk's end clamped here, zeroed in step)
+    // token rows first: tokens of slice s in fragment order (rows past the chunk's end clamped here,
+    // zeroed in step)
     const int L = min(CH, len - c * CH);
-    const uint16_t* dob = p.dout + ((size_t)tok0 + (size_t)c * CH) * vstride + (size_t)h * HD + v0 + l16;
+    const uint16_t* rb = rows + ((size_t)tok0 + (size_t)c * CH) * vstride + (size_t)h * HD + v0 + l16;
 #pragma unroll
     for (int q = 0; q < FPW; ++q) {
       const int f = w + 4 * q;
@@ -519,7 +571,7 @@ __global__ __launch_bounds__(256) void bwd_adjoint_kernel(BwdParams p) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int tk = 32 * s + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
-          F.d[q][e] = dob[(size_t)min(tk, L - 1) * vstride + 16 * j];
+          F.d[q][e] = rb[(size_t)min(tk, L - 1) * vstride + 16 * j];
         }
       }
     }
@@ -528,40 +580,40 @@ __global__ __launch_bounds__(256) void bwd_adjoint_kernel(BwdParams p) {
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        F.a[i][s] = *reinterpret_cast<const f16x8*>(rec + BR_PHI + ((2 * w + i) * 4 + s) * FRAG_BYTES + lane * 16);
+        F.a[i][s] = *reinterpret_cast<const f16x8*>(rec + OFF_A + ((2 * w + i) * 4 + s) * FRAG_BYTES + lane * 16);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        F.b[i][s] = *reinterpret_cast<const f16x8*>(rec + BR_BC + ((2 * w + i) * 2 + s) * FRAG_BYTES + lane * 16);
+        F.b[i][s] = *reinterpret_cast<const f16x8*>(rec + OFF_B + ((2 * w + i) * 2 + s) * FRAG_BYTES + lane * 16);
     }
   };
   auto step = [&](const Frags& F, int c) {
     const size_t eh = (size_t)(chunk0 + c) * p.H + h;
-    f16* ds = reinterpret_cast<f16*>(p.dstates) + eh * HD * HD;
+    f16* st = reinterpret_cast<f16*>(FWD ? p.states : p.dstates) + eh * HD * HD;
     const int buf = c & 1;
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)  // dS' of this chunk
-        *reinterpret_cast<f16x4*>(ds + (size_t)(v0 + 16 * j + l16) * HD + 32 * w + 16 * i + 4 * lg) =
-            f16x4{(f16)dS[j][i][0], (f16)dS[j][i][1], (f16)dS[j][i][2], (f16)dS[j][i][3]};
-      sB[buf][j][w][lane] = f16x8{(f16)dS[j][0][0], (f16)dS[j][0][1], (f16)dS[j][0][2], (f16)dS[j][0][3],
-                                  (f16)dS[j][1][0], (f16)dS[j][1][1], (f16)dS[j][1][2], (f16)dS[j][1][3]};
+      for (int i = 0; i < 2; ++i)  // the state entering (FWD) or the gradient leaving this chunk
+        *reinterpret_cast<f16x4*>(st + (size_t)(v0 + 16 * j + l16) * HD + 32 * w + 16 * i + 4 * lg) =
+            f16x4{(f16)S[j][i][0], (f16)S[j][i][1], (f16)S[j][i][2], (f16)S[j][i][3]};
+      sB[buf][j][w][lane] = f16x8{(f16)S[j][0][0], (f16)S[j][0][1], (f16)S[j][0][2], (f16)S[j][0][3],
+                                  (f16)S[j][1][0], (f16)S[j][1][1], (f16)S[j][1][2], (f16)S[j][1][3]};
     }
     const int L = min(CH, len - c * CH);
 #pragma unroll
     for (int q = 0; q < FPW; ++q) {
       const int f = w + 4 * q;
       if (f < NF) {
-        f16x8 d;
+        f16x8 dv;
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int tk = 32 * (f & 1) + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
-          d[e] = (f16)(bf(F.d[q][e]) * (tk < L ? p.scale : 0.f));
+          dv[e] = (f16)(bf(F.d[q][e]) * (tk < L ? rscale : 0.f));
         }
-        sD[buf][f][lane] = d;
+        sD[buf][f][lane] = dv;
       }
     }
-    __syncthreads();  // every wave's rows of dS' and every dO' fragment published
+    __syncthreads();  // every wave's rows of the state and every token-row fragment published
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
       f16x8 sb[4], sd[2];
@@ -576,26 +628,28 @@ __global__ __launch_bounds__(256) void bwd_adjoint_kernel(BwdParams p) {
         for (int s = 0; s < 4; ++s) a = mma_f16(F.a[i][s], sb[s], a);
 #pragma unroll
         for (int s = 0; s < 2; ++s) a = mma_f16(F.b[i][s], sd[s], a);
-        dS[j][i] = a;
+        S[j][i] = a;
       }
     }
   };
+  // chunk k-th in processing order
+  auto at = [&](int k) { return FWD ? min(k, nch - 1) : max(nch - 1 - k, 0); };
   Frags f0, f1;
-  if (nch > 0) load(f0, nch - 1);
-  for (int c = nch - 1; c >= 0; c -= 2) {
-    load(f1, max(c - 1, 0));
-    step(f0, c);
-    if (c - 1 < 0) break;
-    load(f0, max(c - 2, 0));
-    step(f1, c - 1);
+  if (nch > 0) load(f0, at(0));
+  for (int k = 0; k < nch; k += 2) {
+    load(f1, at(k + 1));
+    step(f0, at(k));
+    if (k + 1 >= nch) break;
+    load(f0, at(k + 2));
+    step(f1, at(k + 1));
   }
-  if (p.dinit) {
+  if (!FWD && p.dinit) {
 #pragma unroll
     for (int j = 0; j < NCT; ++j)
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         *reinterpret_cast<float4*>(p.dinit + sbase + (size_t)(v0 + 16 * j + l16) * HD + 32 * w + 16 * i + 4 * lg) =
-            make_float4(dS[j][i][0], dS[j][i][1], dS[j][i][2], dS[j][i][3]);
+            make_float4(S[j][i][0], S[j][i][1], S[j][i][2], S[j][i][3]);
   }
 }
 
@@ -1005,6 +1059,16 @@ __global__ __launch_bounds__(256) void bwd_fill_kernel(float* a, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) a[i] = 0.f;
 }
 
+template <bool FWD>
+void launch_chain(const BwdParams& p, hipStream_t stream) {
+  if (p.n_chains <= 0) return;
+  // the widest column tiles that keep every workgroup resident (two per CU)
+  const int slots = 2 * device_cu_count(), g8 = (p.n_chains + 7) / 8 * 8;
+  if (g8 * 8 <= slots) bwd_chain_kernel<1, FWD><<<g8 * 8, 256, 0, stream>>>(p);
+  else if (g8 * 4 <= slots) bwd_chain_kernel<2, FWD><<<g8 * 4, 256, 0, stream>>>(p);
+  else bwd_chain_kernel<4, FWD><<<g8 * 2, 256, 0, stream>>>(p);
+}
+
 void launch_bwd(const BwdParams& p, size_t qk_floats, int stage, hipStream_t stream) {
   const int jobs = p.n_entries * p.H;
   if (stage == 0) {
@@ -1015,12 +1079,9 @@ void launch_bwd(const BwdParams& p, size_t qk_floats, int stage, hipStream_t str
     bwd_fill_kernel<<<1, 256, 0, stream>>>(p.dA_log, (size_t)p.H);
     if (jobs > 0) bwd_coef_kernel<<<jobs, NTH, 0, stream>>>(p);
   } else if (stage == 1) {
-    if (p.n_chains > 0) {  // the widest column tiles that keep every workgroup resident (two per CU)
-      const int slots = 2 * device_cu_count(), g8 = (p.n_chains + 7) / 8 * 8;
-      if (g8 * 8 <= slots) bwd_adjoint_kernel<1><<<g8 * 8, 256, 0, stream>>>(p);
-      else if (g8 * 4 <= slots) bwd_adjoint_kernel<2><<<g8 * 4, 256, 0, stream>>>(p);
-      else bwd_adjoint_kernel<4><<<g8 * 2, 256, 0, stream>>>(p);
-    }
+    launch_chain<true>(p, stream);
+  } else if (stage == 2) {
+    launch_chain<false>(p, stream);
   } else if (jobs > 0) {
     BwdParams q = p;
     q.touch_ahead = device_cu_count();

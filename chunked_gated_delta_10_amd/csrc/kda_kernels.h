@@ -63,7 +63,6 @@ struct RecurParams {
   uint16_t* sink;         // 64 scratch values: destination of output rows past a chunk's end
   int dense_T;            // >= 0: B rows of dense_T tokens, schedule by arithmetic; -1: read `seqs`/`order`
   int* err;               // error word of the workspace header: cleared (this path reports no errors)
-  uint16_t* states = nullptr;  // backward's forward: fp16 state entering every chunk, [entries][H][V][K]
 };
 
 // Fused persistent forward (kda_fused.hip): per-channel gate, delta rule.
@@ -129,9 +128,6 @@ void launch_table(const TableParams& p, hipStream_t stream);
 // read by the caller with hipGetLastError).
 hipError_t launch_chunk_local(const ChunkParams& p, int n_entries, bool per_channel, bool delta, hipStream_t stream);
 void launch_recur(const RecurParams& p, bool bf16_state, bool per_channel, bool delta, hipStream_t stream);
-// The backward pass's forward (delta rule, fp32 states): stores the state entering every chunk in
-// p.states and writes no outputs.
-void launch_recur_states(const RecurParams& p, bool per_channel, hipStream_t stream);
 // Scalar gate with value heads grouped on q/k heads and at least
 // GROUP_MIN_JOBS (schedule entry, q/k head) jobs: the value heads of a group
 // share one copy of the qn and kn^T record fragments, written by the grouped
@@ -142,7 +138,7 @@ int recur_grid(int n_chains);
 void launch_decode(const DecodeParams& p, int B, bool bf16_state, bool per_channel, bool delta, hipStream_t stream);
 
 // Backward pass, scalar gate, delta rule (kda_bwd.hip).
-constexpr int BREC_BYTES = 56 * 1024;  // per (entry, head): the adjoint's operand fragments and T
+constexpr int BREC_BYTES = 104 * 1024;  // per (entry, head): operand fragments of both chains, and T
 struct BwdParams {
   const uint16_t* q;      // bf16 [tokens, H_qk, 128]
   const uint16_t* k;
@@ -152,6 +148,7 @@ struct BwdParams {
   const float* A_log;     // fp32 [H]
   const uint16_t* dout;   // bf16 [tokens, H, 128]
   const float* dfinal;    // fp32 [seqs, H, 128, 128] ([V][K]) or null
+  const float* s0;        // fp32 initial state, same layout, or null
   float scale;
   int H, H_qk;
   int dense_T;            // >= 0: B rows of dense_T tokens; -1: read chunks / seqs / order
@@ -159,7 +156,7 @@ struct BwdParams {
   const int4* seqs;
   const int* order;
   int n_entries, n_chains;
-  const uint16_t* states;  // fp16 [entries][H][V][K]: the state entering every chunk
+  uint16_t* states;        // fp16 [entries][H][V][K]: the state entering every chunk
   uint16_t* dstates;       // fp16 [entries][H][V][K]: the gradient of the state leaving every chunk
   uint8_t* brec;           // [entries][H][BREC_BYTES]
   float* dq;              // fp32 [tokens, H_qk, 128]
@@ -172,7 +169,8 @@ struct BwdParams {
   int touch_ahead = 0;    // gradient kernel: prefetch the inputs of job + touch_ahead
 };
 // Stages, in this order: 0 the coefficient records (after clearing dA_log, and dq, dk when value heads
-// share q/k heads; qk_floats: elements of dq), 1 the adjoint chain, 2 the gradients.
+// share q/k heads; qk_floats: elements of dq), 1 the forward chain (chunk states), 2 the adjoint chain,
+// 3 the gradients.
 void launch_bwd(const BwdParams& p, size_t qk_floats, int stage, hipStream_t stream);
 
 }  // namespace kda

@@ -132,11 +132,7 @@ __device__ __forceinline__ void unpack_bf16(uint2 x, f16* o) {
 // slot): kn S is a product of the same shape as W S, the residual
 // V - exp(Gamma_r) (kn S)_r is formed in fp32 and passed through LDS as the
 // B operand of T diag(b), at the cost of one more barrier per chunk.
-//
-// ST (the backward pass's forward): the chain waves also store the state
-// entering every chunk (fp16, p.states [entries][H][V][K]) and the output
-// waves only keep the barriers (no outputs are needed).
-template <typename StT, int NCT, bool DELTA, bool PC, bool ST = false>
+template <typename StT, int NCT, bool DELTA, bool PC>
 __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
   constexpr int VC = VT * NCT;       // value columns per workgroup
   constexpr int NW = NVT / NCT;      // workgroups per chain
@@ -242,16 +238,6 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
       auto step = [&](const ChainFrags<NCT>& F, int c) {
         sink ^= F.touch;
         const int L = min(CH, len - c * CH);
-        if constexpr (ST) {  // the state entering chunk c, fp16
-          f16* st = reinterpret_cast<f16*>(p.states) + ((size_t)(chunk0 + c) * p.H + h) * HD * HD +
-                    (size_t)(v0 + l16) * HD;
-#pragma unroll
-          for (int j = 0; j < NCT; ++j)
-#pragma unroll
-            for (int i = 0; i < 2; ++i)
-              *reinterpret_cast<f16x4*>(st + (size_t)VT * j * HD + SUB * (2 * TW + i) + 4 * lg) =
-                  f16x4{(f16)S[j][i][0], (f16)S[j][i][1], (f16)S[j][i][2], (f16)S[j][i][3]};
-        }
         {
 #pragma unroll
           for (int j = 0; j < NCT; ++j) {
@@ -407,14 +393,6 @@ __global__ __launch_bounds__(512) void recur_split_kernel(RecurParams p) {
 
 
   // ---- output waves ----------------------------------------------------------
-  if constexpr (ST) {  // no outputs: keep the chain waves' barriers only
-    for (int c = 0; c < nch; ++c) {
-      __syncthreads();  // A
-      if constexpr (KN) __syncthreads();  // A2
-      __syncthreads();  // B
-    }
-    return;
-  }
   auto out_role = [&](auto TWc) {
     constexpr int TW = decltype(TWc)::value;
     const size_t row_step = (size_t)p.H * HD;
@@ -558,18 +536,6 @@ void launch_recur(const RecurParams& p, bool bf16_state, bool per_channel, bool 
   } else {
     if (per_channel) launch_recur_variant<false, true>(p, bf16_state, stream);
     else launch_recur_variant<false, false>(p, bf16_state, stream);
-  }
-}
-
-void launch_recur_states(const RecurParams& p, bool per_channel, hipStream_t stream) {
-  const bool pc = per_channel || !shares_qk_fragments(per_channel, p.H, p.H_qk, p.n_entries);
-  const int g1 = grid_for(p.n_chains, NVT), g2 = grid_for(p.n_chains, NVT / 2);
-  if (g1 <= cu_count()) {
-    if (pc) recur_split_kernel<float, 1, true, true, true><<<g1, 512, 0, stream>>>(p);
-    else recur_split_kernel<float, 1, true, false, true><<<g1, 512, 0, stream>>>(p);
-  } else {
-    if (pc) recur_split_kernel<float, 2, true, true, true><<<g2, 512, 0, stream>>>(p);
-    else recur_split_kernel<float, 2, true, false, true><<<g2, 512, 0, stream>>>(p);
   }
 }
 

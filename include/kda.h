@@ -218,8 +218,8 @@ kda_status kda_la_decode_step(const void* q, const void* k, const void* v, const
  * dinitial_state [B, H, V, K], or NULL (not written).
  *
  * The forward is recomputed inside the call (the state entering every
- * 64-token chunk is kept in the workspace: 64 KiB per (chunk, head)), so
- * nothing from an earlier kda_fwd call is needed.  Workspace bytes:
+ * 64-token chunk is kept in the workspace, fp16), so nothing from an earlier
+ * kda_fwd call is needed.  Workspace bytes:
  * kda_bwd_workspace_bytes(B, T, H_qk, H, 0) (N > 0: kda_bwd_varlen), 256-byte
  * aligned, contents garbage before and after.  gate_per_channel = 1 is
  * rejected with KDA_ERR_SHAPE.  dq, dk (when H > H_qk) and dA_log are
@@ -253,8 +253,8 @@ kda_status kda_bwd_varlen(const void* q, const void* k, const void* v, const voi
  * (up to max_kernels entries), forgets them, and returns the number of
  * kernel ids (or -1 on a HIP error).  Kernel ids: 0 schedule, 1 chunk-local,
  * 2 recurrence, 3 decode, 4 fused forward, 5 backward coefficients,
- * 6 backward adjoint, 7 backward gradients (the backward's recomputed forward
- * reports as 1 and 2).  The events are created by the library and reused.
+ * 6 backward adjoint chain, 7 backward gradients, 8 backward forward chain
+ * (the chunk states).  The events are created by the library and reused.
  */
 void kda_kernel_timing_enable(int enable);
 int kda_kernel_timing_read(double* total_ms, int* launches, int max_kernels);

@@ -3,12 +3,14 @@ kda_bwd / kda_bwd_varlen) against the fp64 backward oracle.
 
 The oracle (oracle/kda_backward.py) is reverse-mode differentiation of the
 token-by-token forward, pinned on the CPU to complex-step and finite
-differences.  The GPU recomputes the forward with the two-kernel path (fp16
-matrix-core operands, fp32 state), then runs the chunk-form backward in fp32.
-Every gradient is bilinear in the recomputed states and the upstream
-gradients, so its relative error tracks the forward's state error (held to
-1e-3 rel-L2 by the forward tests) times a small factor: each gradient is held
-to GRAD_REL rel-L2 and to GRAD_MAXABS of its own largest magnitude.
+differences.  The GPU runs the chunk form of both chains (the forward's chunk
+states, then the adjoint) and the chunk-parallel gradients on fp16 matrix
+cores with fp32 accumulation and fp16 storage of the chunk states: the
+precision of the forward's own chunk path, whose state error the forward
+tests hold to 1e-3 rel-L2.  Every gradient is bilinear in those states and the
+upstream gradients, so its relative error is of that order times a small
+factor: each gradient is held to GRAD_REL rel-L2 and to GRAD_MAXABS of its
+own largest magnitude.
 """
 
 import numpy as np
@@ -114,19 +116,18 @@ def test_backward_matches_the_oracle(label, kw, dstd):
     compare(got, ref, label)
 
 
-def test_backward_grouped_records_path():
-    # 64 chunks x 4 q/k heads = 256 (entry, q/k head) jobs: the recomputed forward takes the grouped
-    # chunk-local kernel and the records shared by the value heads of a group
+def test_backward_grouped_heads_long_sequence():
+    # 64 chunks, two value heads on each q/k head: dq, dk summed over the group across many chunks
     inp = make_inputs(1, 4096, 8, 4, gate_per_channel=False, A_log=(-1.0, 1.0), state_std=0.05, seed=79)
     dout, dfinal = upstream(inp, 579)
     got = run_gpu_bwd(inp, dout, dfinal)
     ref = run_oracle_bwd(inp, dout, dfinal)
-    compare(got, ref, "grouped records T=4096 H=8 H_qk=4")
+    compare(got, ref, "grouped heads T=4096 H=8 H_qk=4")
 
 
-def test_backward_many_gradient_launches_sampled_heads():
-    # 128 chunks x 32 heads = 4096 (chunk, head) jobs: more than the scratch slots of one gradient
-    # launch, so the jobs run in several launches; heads 0 and 31 are checked against the oracle
+def test_backward_many_jobs_sampled_heads():
+    # 128 chunks x 32 heads = 4096 (chunk, head) jobs, chains on the widest column tiles; heads 0 and 31
+    # are checked against the oracle
     inp = make_inputs(1, 8192, 32, 32, gate_per_channel=False, A_log=(-1.0, 1.0), state_std=0.05, seed=80)
     dout, dfinal = upstream(inp, 580)
     got = run_gpu_bwd(inp, dout, dfinal)
