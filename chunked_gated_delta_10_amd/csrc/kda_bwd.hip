@@ -358,6 +358,18 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_kernel(BwdParams p) {
         qraw[s][hh][jj] = p.q[((size_t)(tok0 + min(i, len - 1)) * p.H_qk + hq) * HD + d];
       }
   load_chunk(p, tok0, len, h, hq, QN, KN, R);
+  // touch the q, k rows of the job one round ahead (two workgroups per CU run at a time)
+  uint32_t touch = 0;
+  if (job + p.touch_ahead < p.n_entries * p.H && t < 256) {
+    const int jn = job + p.touch_ahead, en = jn / p.H, hn = jn - en * p.H;
+    const int2 cn = entry_of(p, en);
+    if (cn.y > 0) {
+      const int row = min((t & 127) >> 1, cn.y - 1);
+      touch = *reinterpret_cast<const uint32_t*>((t < 128 ? p.q : p.k) +
+                                                 ((size_t)(cn.x + row) * p.H_qk + hn / (p.H / p.H_qk)) * HD +
+                                                 (t & 1) * 64);
+    }
+  }
   __syncthreads();
   if (t < CH) be[t] = R.b[t] * R.e[t];
   f32x4 P[2], Gm[2];
@@ -489,6 +501,7 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_kernel(BwdParams p) {
       *reinterpret_cast<f16x8*>(rec + BR_BC + (w * 2 + s) * FRAG_BYTES + lane * 16) = o;
     }
   }
+  asm volatile("" ::"v"(touch));
 }
 
 // ---------------------------------------------------------------------------
@@ -558,6 +571,8 @@ __global__ __launch_bounds__(256, 2) void bwd_chain_kernel(BwdParams p) {  // tw
     f16x8 a[2][4], b[2][2];
     uint16_t d[FPW][8];
   };
+  // chunk k-th in processing order
+  auto at = [&](int k) { return FWD ? min(k, nch - 1) : max(nch - 1 - k, 0); };
   auto load = [&](Frags& F, int c) {
     // token rows first: tokens of slice s in fragment order (rows past the chunk's end clamped here,
     // zeroed in step)
@@ -632,8 +647,6 @@ __global__ __launch_bounds__(256, 2) void bwd_chain_kernel(BwdParams p) {  // tw
       }
     }
   };
-  // chunk k-th in processing order
-  auto at = [&](int k) { return FWD ? min(k, nch - 1) : max(nch - 1 - k, 0); };
   Frags f0, f1;
   if (nch > 0) load(f0, at(0));
   for (int k = 0; k < nch; k += 2) {
@@ -1077,7 +1090,11 @@ void launch_bwd(const BwdParams& p, size_t qk_floats, int stage, hipStream_t str
       bwd_fill_kernel<<<1024, 256, 0, stream>>>(p.dk, qk_floats);
     }
     bwd_fill_kernel<<<1, 256, 0, stream>>>(p.dA_log, (size_t)p.H);
-    if (jobs > 0) bwd_coef_kernel<<<jobs, NTH, 0, stream>>>(p);
+    if (jobs > 0) {
+      BwdParams q = p;
+      q.touch_ahead = 2 * device_cu_count();
+      bwd_coef_kernel<<<jobs, NTH, 0, stream>>>(q);
+    }
   } else if (stage == 1) {
     launch_chain<true>(p, stream);
   } else if (stage == 2) {

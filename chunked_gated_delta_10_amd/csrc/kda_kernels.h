@@ -166,7 +166,7 @@ struct BwdParams {
   float* dbeta;           // fp32 [tokens, H]
   float* dA_log;          // fp32 [H]
   float* dinit;           // fp32 [seqs, H, 128, 128] or null
-  int touch_ahead = 0;    // gradient kernel: prefetch the inputs of job + touch_ahead
+  int touch_ahead = 0;    // chunk-parallel kernels: prefetch the inputs of job + touch_ahead
 };
 // Stages, in this order: 0 the coefficient records (after clearing dA_log, and dq, dk when value heads
 // share q/k heads; qk_floats: elements of dq), 1 the forward chain (chunk states), 2 the adjoint chain,
