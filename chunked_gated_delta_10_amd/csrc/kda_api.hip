@@ -94,12 +94,11 @@ bool takes_fused(bool delta, int gate_per_channel) {
 
 // ---- per-kernel event timing (diagnostics) --------------------------------
 enum {
-  K_TABLE = 0, K_CHUNK = 1, K_RECUR = 2, K_DECODE = 3, K_FUSED = 4, K_BWD_COEF = 5, K_BWD_ADJ = 6, K_BWD_GRAD = 7,
-  K_BWD_STATES = 8, K_COUNT = 9
+  K_TABLE = 0, K_CHUNK = 1, K_RECUR = 2, K_DECODE = 3, K_FUSED = 4, K_BWD_COEF = 5, K_BWD_CHAINS = 6, K_BWD_GRAD = 7,
+  K_COUNT = 8
 };
-const char* const kKernelNames[K_COUNT] = {"kda_table",    "kda_chunk_local", "kda_recur",       "kda_decode",
-                                           "kda_fused",    "kda_bwd_coef",    "kda_bwd_adjoint", "kda_bwd_grad",
-                                           "kda_bwd_states"};
+const char* const kKernelNames[K_COUNT] = {"kda_table", "kda_chunk_local", "kda_recur",      "kda_decode",
+                                           "kda_fused", "kda_bwd_coef",    "kda_bwd_chains", "kda_bwd_grad"};
 
 struct Timing {
   bool on = false;
@@ -449,9 +448,9 @@ kda_status run_backward(const BwdArgs& a) {
                     chunks, seqs, order, tokens > 0 ? n_entries : 0, a.n_seqs * a.H,
                     reinterpret_cast<uint16_t*>(ws + L.states), reinterpret_cast<uint16_t*>(ws + L.dstates),
                     ws + L.brec, a.dq, a.dk, a.dv, a.dg_raw, a.dbeta, a.dA_log, a.dinit};
-  // coefficients; the forward chain (chunk states); the adjoint chain; the gradients
-  const int ids[4] = {K_BWD_COEF, K_BWD_STATES, K_BWD_ADJ, K_BWD_GRAD};
-  for (int stage = 0; stage < 4; ++stage) {
+  // coefficients; both chains (chunk states and their gradients); the gradients
+  const int ids[3] = {K_BWD_COEF, K_BWD_CHAINS, K_BWD_GRAD};
+  for (int stage = 0; stage < 3; ++stage) {
     Timed t(ids[stage], a.stream);
     kda::launch_bwd(bp, (size_t)tokens * a.H_qk * kda::HD, stage, a.stream);
   }

@@ -29,9 +29,9 @@
 // Gc = kn^T diag(f) T diag(b), so both chains are the same kernel.  Kernels:
 //   coef_kernel   per (chunk, head): Phi, Phi^T, Bc, Gc as fp16 operand
 //                 fragments, and T
-//   chain_kernel  per (chain, value-column tile), FWD: the state entering
-//                 every chunk (fp16); then, last chunk first, dS' of every
-//                 chunk (fp16) and dS_0 (fp32)
+//   chain_kernel  per (chain, value-column tile), both chains in one launch:
+//                 the state entering every chunk (fp16); dS' of every chunk
+//                 (fp16, last chunk first) and dS_0 (fp32)
 //   grad_kernel   per (chunk, head): every input gradient of the chunk
 // Products run on fp16 matrix cores with fp32 accumulation (the precision of
 // the forward's chunk path); T = (I + A)^-1 is formed in fp32.
@@ -505,30 +505,36 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_kernel(BwdParams p) {
 }
 
 // ---------------------------------------------------------------------------
-// chain_kernel: the two chains over a sequence's chunks, one workgroup per
-// (chain, 16 NCT value columns).
-//   FWD:  S_c+1 = Phi^T S_c + Gc V_c, first chunk first, from the initial
-//         state; stores S_c (the state entering chunk c, fp16).
-//   else: dS_c = Phi dS' + Bc dO', last chunk first, from dfinal; stores dS'
-//         (the gradient of the state leaving chunk c, fp16) and dS_0 (fp32).
+// chain_kernel: the two chains over a sequence's chunks, which do not depend
+// on each other, in one launch: the first half of the grid runs the forward
+// chain, the second half the adjoint; one workgroup per (chain, 16 NCT value
+// columns).
+//   forward: S_c+1 = Phi^T S_c + Gc V_c, first chunk first, from the initial
+//            state; stores S_c (the state entering chunk c, fp16).
+//   adjoint: dS_c = Phi dS' + Bc dO', last chunk first, from dfinal; stores
+//            dS' (the gradient of the state leaving chunk c, fp16) and dS_0
+//            (fp32).
 // Wave w holds rows 32 w .. 32 w + 31 of the state for every column tile in
 // C layout (fp32); the four waves' rows, converted to fp16, are the B operand
 // of the next step, and the token-row fragments (V or dO', loaded once per
-// workgroup, a share per wave) go the same way: both through LDS, one
-// barrier per chunk.  The next chunk's operator fragments and token rows are
+// workgroup, a share per wave) go the same way: both through LDS, two
+// barriers per chunk.  The next chunk's operator fragments and token rows are
 // loaded while the current chunk is processed.
 // ---------------------------------------------------------------------------
-template <int NCT, bool FWD>
+template <int NCT>
 __global__ __launch_bounds__(256, 2) void bwd_chain_kernel(BwdParams p) {  // two workgroups per CU
   constexpr int NW = 8 / NCT;       // workgroups per chain
   constexpr int NF = 2 * NCT;       // token-row fragments per chunk (column tile, token slice)
   constexpr int FPW = (NF + 3) / 4;  // of which each wave loads up to FPW
-  constexpr int OFF_A = FWD ? BR_PHIT : BR_PHI, OFF_B = FWD ? BR_GC : BR_BC;
-  __shared__ __attribute__((aligned(16))) f16x8 sB[2][NCT][4][64];
-  __shared__ __attribute__((aligned(16))) f16x8 sD[2][NF][64];
+  __shared__ __attribute__((aligned(16))) f16x8 sB[NCT][4][64];
+  __shared__ __attribute__((aligned(16))) f16x8 sD[NF][64];
   const int tid = threadIdx.x, lane = tid & 63, w = tid >> 6, l16 = lane & 15, lg = lane >> 4;
-  // the workgroups of a chain share an XCD (blocks are dealt to XCDs round robin)
-  const int x = blockIdx.x, xcd = x & 7, y = x >> 3, vt = y % NW, ch = (y / NW) * 8 + xcd;
+  const int half = gridDim.x / 2;
+  const bool fwd = (int)blockIdx.x < half;  // uniform over the workgroup
+  const int off_a = fwd ? BR_PHIT : BR_PHI, off_b = fwd ? BR_GC : BR_BC;
+  // the workgroups of a chain share an XCD (blocks are dealt to XCDs round robin; half is a multiple of 8)
+  const int x = fwd ? blockIdx.x : blockIdx.x - half, xcd = x & 7, y = x >> 3, vt = y % NW,
+            ch = (y / NW) * 8 + xcd;
   if (ch >= p.n_chains) return;
   const int h = ch % p.H;
   int n, tok0, len, chunk0;
@@ -547,7 +553,7 @@ __global__ __launch_bounds__(256, 2) void bwd_chain_kernel(BwdParams p) {  // tw
   const int nch = max(0, min((len + CH - 1) / CH, p.n_entries - chunk0));
   const int v0 = 16 * NCT * vt;
   const size_t sbase = ((size_t)n * p.H + h) * HD * HD;
-  const float* s_in = FWD ? p.s0 : p.dfinal;
+  const float* s_in = fwd ? p.s0 : p.dfinal;
   f32x4 S[NCT][2];
 #pragma unroll
   for (int j = 0; j < NCT; ++j)
@@ -562,17 +568,17 @@ __global__ __launch_bounds__(256, 2) void bwd_chain_kernel(BwdParams p) {  // tw
       }
     }
   const size_t vstride = (size_t)p.H * HD;
-  const uint16_t* rows = FWD ? p.v : p.dout;
-  const float rscale = FWD ? 1.f : p.scale;
+  const uint16_t* rows = fwd ? p.v : p.dout;
+  const float rscale = fwd ? 1.f : p.scale;
+  f16* st_base = reinterpret_cast<f16*>(fwd ? p.states : p.dstates);
   // raw token-row values are kept as loaded and converted in step(): a load's
   // result used right away would make the wait cover the prefetches issued
   // before it (the memory counter drains in order)
+  typedef unsigned short us2 __attribute__((ext_vector_type(2)));  // two raw values in one register
   struct Frags {
     f16x8 a[2][4], b[2][2];
-    uint16_t d[FPW][8];
+    us2 d[FPW][4];
   };
-  // chunk k-th in processing order
-  auto at = [&](int k) { return FWD ? min(k, nch - 1) : max(nch - 1 - k, 0); };
   auto load = [&](Frags& F, int c) {
     // token rows first: tokens of slice s in fragment order (rows past the chunk's end clamped here,
     // zeroed in step)
@@ -586,7 +592,7 @@ __global__ __launch_bounds__(256, 2) void bwd_chain_kernel(BwdParams p) {  // tw
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int tk = 32 * s + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
-          F.d[q][e] = rb[(size_t)min(tk, L - 1) * vstride + 16 * j];
+          F.d[q][e >> 1][e & 1] = rb[(size_t)min(tk, L - 1) * vstride + 16 * j];
         }
       }
     }
@@ -595,24 +601,22 @@ __global__ __launch_bounds__(256, 2) void bwd_chain_kernel(BwdParams p) {  // tw
     for (int i = 0; i < 2; ++i) {
 #pragma unroll
       for (int s = 0; s < 4; ++s)
-        F.a[i][s] = *reinterpret_cast<const f16x8*>(rec + OFF_A + ((2 * w + i) * 4 + s) * FRAG_BYTES + lane * 16);
+        F.a[i][s] = *reinterpret_cast<const f16x8*>(rec + off_a + ((2 * w + i) * 4 + s) * FRAG_BYTES + lane * 16);
 #pragma unroll
       for (int s = 0; s < 2; ++s)
-        F.b[i][s] = *reinterpret_cast<const f16x8*>(rec + OFF_B + ((2 * w + i) * 2 + s) * FRAG_BYTES + lane * 16);
+        F.b[i][s] = *reinterpret_cast<const f16x8*>(rec + off_b + ((2 * w + i) * 2 + s) * FRAG_BYTES + lane * 16);
     }
   };
   auto step = [&](const Frags& F, int c) {
-    const size_t eh = (size_t)(chunk0 + c) * p.H + h;
-    f16* st = reinterpret_cast<f16*>(FWD ? p.states : p.dstates) + eh * HD * HD;
-    const int buf = c & 1;
+    f16* st = st_base + ((size_t)(chunk0 + c) * p.H + h) * HD * HD;
 #pragma unroll
     for (int j = 0; j < NCT; ++j) {
 #pragma unroll
-      for (int i = 0; i < 2; ++i)  // the state entering (FWD) or the gradient leaving this chunk
+      for (int i = 0; i < 2; ++i)  // the state entering (forward) or the gradient leaving this chunk
         *reinterpret_cast<f16x4*>(st + (size_t)(v0 + 16 * j + l16) * HD + 32 * w + 16 * i + 4 * lg) =
             f16x4{(f16)S[j][i][0], (f16)S[j][i][1], (f16)S[j][i][2], (f16)S[j][i][3]};
-      sB[buf][j][w][lane] = f16x8{(f16)S[j][0][0], (f16)S[j][0][1], (f16)S[j][0][2], (f16)S[j][0][3],
-                                  (f16)S[j][1][0], (f16)S[j][1][1], (f16)S[j][1][2], (f16)S[j][1][3]};
+      sB[j][w][lane] = f16x8{(f16)S[j][0][0], (f16)S[j][0][1], (f16)S[j][0][2], (f16)S[j][0][3],
+                             (f16)S[j][1][0], (f16)S[j][1][1], (f16)S[j][1][2], (f16)S[j][1][3]};
     }
     const int L = min(CH, len - c * CH);
 #pragma unroll
@@ -623,9 +627,9 @@ __global__ __launch_bounds__(256, 2) void bwd_chain_kernel(BwdParams p) {  // tw
 #pragma unroll
         for (int e = 0; e < 8; ++e) {
           const int tk = 32 * (f & 1) + (e < 4 ? 4 * lg + e : 16 + 4 * lg + e - 4);
-          dv[e] = (f16)(bf(F.d[q][e]) * (tk < L ? rscale : 0.f));
+          dv[e] = (f16)(bf(F.d[q][e >> 1][e & 1]) * (tk < L ? rscale : 0.f));
         }
-        sD[buf][f][lane] = dv;
+        sD[f][lane] = dv;
       }
     }
     __syncthreads();  // every wave's rows of the state and every token-row fragment published
@@ -633,9 +637,9 @@ __global__ __launch_bounds__(256, 2) void bwd_chain_kernel(BwdParams p) {  // tw
     for (int j = 0; j < NCT; ++j) {
       f16x8 sb[4], sd[2];
 #pragma unroll
-      for (int s = 0; s < 4; ++s) sb[s] = sB[buf][j][s][lane];
+      for (int s = 0; s < 4; ++s) sb[s] = sB[j][s][lane];
 #pragma unroll
-      for (int s = 0; s < 2; ++s) sd[s] = sD[buf][2 * j + s][lane];
+      for (int s = 0; s < 2; ++s) sd[s] = sD[2 * j + s][lane];
 #pragma unroll
       for (int i = 0; i < 2; ++i) {
         f32x4 a = zero4();
@@ -646,7 +650,10 @@ __global__ __launch_bounds__(256, 2) void bwd_chain_kernel(BwdParams p) {  // tw
         S[j][i] = a;
       }
     }
+    __syncthreads();  // every wave has read the published operands
   };
+  // chunk k-th in processing order
+  auto at = [&](int k) { return fwd ? min(k, nch - 1) : max(nch - 1 - k, 0); };
   Frags f0, f1;
   if (nch > 0) load(f0, at(0));
   for (int k = 0; k < nch; k += 2) {
@@ -656,7 +663,7 @@ __global__ __launch_bounds__(256, 2) void bwd_chain_kernel(BwdParams p) {  // tw
     load(f0, at(k + 2));
     step(f1, at(k + 1));
   }
-  if (!FWD && p.dinit) {
+  if (!fwd && p.dinit) {
 #pragma unroll
     for (int j = 0; j < NCT; ++j)
 #pragma unroll
@@ -1072,14 +1079,14 @@ __global__ __launch_bounds__(256) void bwd_fill_kernel(float* a, size_t n) {
   for (size_t i = (size_t)blockIdx.x * 256 + threadIdx.x; i < n; i += (size_t)gridDim.x * 256) a[i] = 0.f;
 }
 
-template <bool FWD>
-void launch_chain(const BwdParams& p, hipStream_t stream) {
+void launch_chains(const BwdParams& p, hipStream_t stream) {
   if (p.n_chains <= 0) return;
-  // the widest column tiles that keep every workgroup resident (two per CU)
+  // the narrowest column tiles that keep every workgroup of both chains resident (two per CU)
   const int slots = 2 * device_cu_count(), g8 = (p.n_chains + 7) / 8 * 8;
-  if (g8 * 8 <= slots) bwd_chain_kernel<1, FWD><<<g8 * 8, 256, 0, stream>>>(p);
-  else if (g8 * 4 <= slots) bwd_chain_kernel<2, FWD><<<g8 * 4, 256, 0, stream>>>(p);
-  else bwd_chain_kernel<4, FWD><<<g8 * 2, 256, 0, stream>>>(p);
+  if (2 * g8 * 8 <= slots) bwd_chain_kernel<1><<<2 * g8 * 8, 256, 0, stream>>>(p);
+  else if (2 * g8 * 4 <= slots) bwd_chain_kernel<2><<<2 * g8 * 4, 256, 0, stream>>>(p);
+  else if (2 * g8 * 2 <= slots) bwd_chain_kernel<4><<<2 * g8 * 2, 256, 0, stream>>>(p);
+  else bwd_chain_kernel<8><<<2 * g8, 256, 0, stream>>>(p);
 }
 
 void launch_bwd(const BwdParams& p, size_t qk_floats, int stage, hipStream_t stream) {
@@ -1096,9 +1103,7 @@ void launch_bwd(const BwdParams& p, size_t qk_floats, int stage, hipStream_t str
       bwd_coef_kernel<<<jobs, NTH, 0, stream>>>(q);
     }
   } else if (stage == 1) {
-    launch_chain<true>(p, stream);
-  } else if (stage == 2) {
-    launch_chain<false>(p, stream);
+    launch_chains(p, stream);
   } else if (jobs > 0) {
     BwdParams q = p;
     q.touch_ahead = device_cu_count();

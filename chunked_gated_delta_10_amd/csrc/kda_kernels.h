@@ -169,8 +169,8 @@ struct BwdParams {
   int touch_ahead = 0;    // chunk-parallel kernels: prefetch the inputs of job + touch_ahead
 };
 // Stages, in this order: 0 the coefficient records (after clearing dA_log, and dq, dk when value heads
-// share q/k heads; qk_floats: elements of dq), 1 the forward chain (chunk states), 2 the adjoint chain,
-// 3 the gradients.
+// share q/k heads; qk_floats: elements of dq), 1 both chains (the chunk states and their gradients),
+// 2 the gradients.
 void launch_bwd(const BwdParams& p, size_t qk_floats, int stage, hipStream_t stream);
 
 }  // namespace kda

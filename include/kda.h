@@ -253,8 +253,8 @@ kda_status kda_bwd_varlen(const void* q, const void* k, const void* v, const voi
  * (up to max_kernels entries), forgets them, and returns the number of
  * kernel ids (or -1 on a HIP error).  Kernel ids: 0 schedule, 1 chunk-local,
  * 2 recurrence, 3 decode, 4 fused forward, 5 backward coefficients,
- * 6 backward adjoint chain, 7 backward gradients, 8 backward forward chain
- * (the chunk states).  The events are created by the library and reused.
+ * 6 backward chains (chunk states and their gradients), 7 backward
+ * gradients.  The events are created by the library and reused.
  */
 void kda_kernel_timing_enable(int enable);
 int kda_kernel_timing_read(double* total_ms, int* launches, int max_kernels);
