@@ -868,7 +868,8 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
       for (int jj = 0; jj < 4; ++jj) {
         const int r = 16 * i + 4 * lg + jj;
         const float dv = R.b[r] * Y[i][jj];
-        if (r < len) p.dv[(size_t)(tok0 + r) * vrow + (size_t)h * HD + vc] = dv;
+        // outputs are written once and not read again: non-temporal, so they do not evict inputs from L2
+        if (r < len) __builtin_nontemporal_store(dv, p.dv + (size_t)(tok0 + r) * vrow + (size_t)h * HD + vc);
         DR[r * LDW + vc] = (f16)dv;
         const float db = rowsum16(Y[i][jj] * RR[i][jj]), de = rowsum16(dv * KS[i][jj]);
         if (l16 == 0) {
@@ -1038,8 +1039,8 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
         const float gq = (dqn[i][jj] - qf[i][jj] * red.qd[r]) / R.nq[r];
         const float gk = (dkn[i][jj] - kf[i][jj] * red.kd[r]) / R.nk[r];
         if (G == 1) {
-          p.dq[o] = gq;
-          p.dk[o] = gk;
+          __builtin_nontemporal_store(gq, p.dq + o);
+          __builtin_nontemporal_store(gk, p.dk + o);
         } else {
           atomicAdd(p.dq + o, gq);
           atomicAdd(p.dk + o, gk);
