@@ -27,9 +27,13 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, published
 MFMA_PEAK_TFLOPS = 2500.0      # MI355X dense bf16/fp16 matrix throughput, published
 D, C = 128, 64                 # head dim, chunk length
 FLOP_PER_TOKEN_HEAD = 6 * D * D + 5 * C * D   # 139,264 (algorithmic, per token and head)
-KERNEL_SOURCES = ["chunked_gated_delta_10_amd/csrc/" + f for f in
-                  ("kda_chunk.hip", "kda_chunk_job.h", "kda_fused.hip", "kda_recur.hip", "kda_table.hip",
-                   "kda_decode.hip", "kda_device.h", "kda_kernels.h", "kda_bwd.hip")]
+# the sources each kernel's code is built from: a counter-derived traffic figure is reported only while
+# they are unchanged
+FORWARD_SOURCES = ["chunked_gated_delta_10_amd/csrc/" + f for f in
+                   ("kda_chunk.hip", "kda_chunk_job.h", "kda_fused.hip", "kda_recur.hip", "kda_table.hip",
+                    "kda_decode.hip", "kda_device.h", "kda_kernels.h")]
+BACKWARD_SOURCES = ["chunked_gated_delta_10_amd/csrc/" + f for f in ("kda_bwd.hip", "kda_bwd.h", "kda_device.h",
+                                                                     "kda_kernels.h")]
 
 
 def algorithmic_bytes(w, with_state=True, state_bytes=4):
@@ -69,9 +73,9 @@ def backward_bytes(w):
 BWD_FLOP_PER_TOKEN_HEAD = FLOP_PER_TOKEN_HEAD + 2 * (7 * C * D * D + 10 * C * C * D + 2 * C ** 3) // C
 
 
-def sources_hash():
+def sources_hash(kernel="kda_recur"):
     h = hashlib.sha256()
-    for p in KERNEL_SOURCES:
+    for p in (BACKWARD_SOURCES if kernel.startswith("kda_bwd") else FORWARD_SOURCES):
         with open(os.path.join(ROOT, p), "rb") as f:
             h.update(f.read())
     return h.hexdigest()[:16]
@@ -85,7 +89,7 @@ def load_traffic(kernel, workload):
     with open(path) as f:
         data = json.load(f)
     rec = data.get(workload, {}).get(kernel)
-    if not rec or rec.get("sources_hash") != sources_hash():
+    if not rec or rec.get("sources_hash") != sources_hash(kernel):
         return None
     return rec.get("hbm_bytes_per_launch")
 
@@ -172,7 +176,7 @@ def traffic_from(root, copy_bytes, workload="kda_dense"):
     rec = {}
     for kern, tags in (("kda_chunk_local", ("chunk_local_kernel", "chunk_group_kernel")), ("kda_recur", ("recur_",)),
                        ("kda_table", ("table_kernel",)), ("kda_fused", ("fused_kernel",)),
-                       ("kda_bwd_coef", ("bwd_coef",)), ("kda_bwd_adjoint", ("bwd_adjoint",)),
+                       ("kda_bwd_coef", ("bwd_coef",)), ("kda_bwd_chains", ("bwd_chain",)),
                        ("kda_bwd_grad", ("bwd_grad",))):
         f = _per_dispatch_kib(run_f, "FETCH_SIZE", lambda k, t=tags: any(x in k for x in t))
         w = _per_dispatch_kib(run_w, "WRITE_SIZE", lambda k, t=tags: any(x in k for x in t))
@@ -180,7 +184,7 @@ def traffic_from(root, copy_bytes, workload="kda_dense"):
             continue
         rec[kern] = {"fetch_kib": f, "write_kib": w, "hbm_read_bytes": f * 1024 * kf,
                      "hbm_write_bytes": w * 1024 * kw, "hbm_bytes_per_launch": f * 1024 * kf + w * 1024 * kw,
-                     "sources_hash": sources_hash()}
+                     "sources_hash": sources_hash(kern)}
     out[workload] = rec
     with open(path, "w") as fh:
         json.dump(out, fh, indent=1)

@@ -16,6 +16,7 @@
 #include <vector>
 
 #include "kda.h"
+#include "kda_bwd.h"
 #include "kda_device.h"
 #include "kda_kernels.h"
 

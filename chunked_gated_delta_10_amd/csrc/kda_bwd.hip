@@ -37,6 +37,7 @@
 // the forward's chunk path); T = (I + A)^-1 is formed in fp32.
 #include <algorithm>
 
+#include "kda_bwd.h"
 #include "kda_device.h"
 #include "kda_kernels.h"
 
@@ -358,18 +359,6 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_kernel(BwdParams p) {
         qraw[s][hh][jj] = p.q[((size_t)(tok0 + min(i, len - 1)) * p.H_qk + hq) * HD + d];
       }
   load_chunk(p, tok0, len, h, hq, QN, KN, R);
-  // touch the q, k rows of the job one round ahead (two workgroups per CU run at a time)
-  uint32_t touch = 0;
-  if (job + p.touch_ahead < p.n_entries * p.H && t < 256) {
-    const int jn = job + p.touch_ahead, en = jn / p.H, hn = jn - en * p.H;
-    const int2 cn = entry_of(p, en);
-    if (cn.y > 0) {
-      const int row = min((t & 127) >> 1, cn.y - 1);
-      touch = *reinterpret_cast<const uint32_t*>((t < 128 ? p.q : p.k) +
-                                                 ((size_t)(cn.x + row) * p.H_qk + hn / (p.H / p.H_qk)) * HD +
-                                                 (t & 1) * 64);
-    }
-  }
   __syncthreads();
   if (t < CH) be[t] = R.b[t] * R.e[t];
   f32x4 P[2], Gm[2];
@@ -501,7 +490,6 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_kernel(BwdParams p) {
       *reinterpret_cast<f16x8*>(rec + BR_BC + (w * 2 + s) * FRAG_BYTES + lane * 16) = o;
     }
   }
-  asm volatile("" ::"v"(touch));
 }
 
 // ---------------------------------------------------------------------------
@@ -713,7 +701,7 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
   f16* DG = reinterpret_cast<f16*>(smem + G_DG);
   f16* DGt = reinterpret_cast<f16*>(smem + G_DGT);
 
-  const int job = blockIdx.x, jobs = p.n_entries * p.H, G = p.H / p.H_qk;
+  const int job = blockIdx.x, G = p.H / p.H_qk;
   const int e = job / p.H, h = job - e * p.H, hq = h / G;
   const int2 ce = entry_of(p, e);
   const int tok0 = ce.x, len = ce.y;
@@ -765,24 +753,6 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
   __syncthreads();
   f32x4 P[2], Gm[2];
   gram_and_T<false>(QN, KN, R, Mt, nullptr, nullptr, nullptr, nullptr, P, Gm);
-  // One workgroup fits a CU, so jobs run in rounds of about one per CU: touch
-  // the inputs of the job one round ahead (one 4-byte load per 128-byte line of
-  // its state blocks and token rows) so that they are in the caches when it
-  // starts.  The values are folded into a sink at the end, long after they arrived.
-  uint32_t touch0 = 0, touch1 = 0;
-  if (job + p.touch_ahead < jobs) {
-    const int jn = job + p.touch_ahead, en = jn / p.H, hn = jn - en * p.H;
-    const int2 cn = entry_of(p, en);
-    if (cn.y > 0) {
-      touch0 = *reinterpret_cast<const uint32_t*>((t < 256 ? p.states : p.dstates) + (size_t)jn * HD * HD +
-                                                  (size_t)(t & 255) * 64);
-      const int tt = t & 127, which = t >> 7, row = min(tt >> 1, cn.y - 1), half = tt & 1;
-      const uint16_t* base = which == 0 ? p.q : which == 1 ? p.k : which == 2 ? p.v : p.dout;
-      const size_t o = which < 2 ? ((size_t)(cn.x + row) * p.H_qk + hn / G) * HD
-                                 : ((size_t)(cn.x + row) * p.H + hn) * HD;
-      touch1 = *reinterpret_cast<const uint32_t*>(base + o + half * 64);
-    }
-  }
   {  // sum(dS' . S) over the 128 x 128 block
     float a = 0.f;
 #pragma unroll
@@ -1072,8 +1042,6 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
     }
     if (t == 0) atomicAdd(p.dA_log + h, dal);
   }
-  const uint32_t sink = touch0 ^ touch1;
-  asm volatile("" ::"v"(sink));
 }
 
 __global__ __launch_bounds__(256) void bwd_fill_kernel(float* a, size_t n) {
@@ -1098,17 +1066,11 @@ void launch_bwd(const BwdParams& p, size_t qk_floats, int stage, hipStream_t str
       bwd_fill_kernel<<<1024, 256, 0, stream>>>(p.dk, qk_floats);
     }
     bwd_fill_kernel<<<1, 256, 0, stream>>>(p.dA_log, (size_t)p.H);
-    if (jobs > 0) {
-      BwdParams q = p;
-      q.touch_ahead = 2 * device_cu_count();
-      bwd_coef_kernel<<<jobs, NTH, 0, stream>>>(q);
-    }
+    if (jobs > 0) bwd_coef_kernel<<<jobs, NTH, 0, stream>>>(p);
   } else if (stage == 1) {
     launch_chains(p, stream);
   } else if (jobs > 0) {
-    BwdParams q = p;
-    q.touch_ahead = device_cu_count();
-    bwd_grad_kernel<<<jobs, NTH, 0, stream>>>(q);
+    bwd_grad_kernel<<<jobs, NTH, 0, stream>>>(p);
   }
 }
 

@@ -137,40 +137,4 @@ bool shares_qk_fragments(bool per_channel, int H, int H_qk, int n_entries);
 int recur_grid(int n_chains);
 void launch_decode(const DecodeParams& p, int B, bool bf16_state, bool per_channel, bool delta, hipStream_t stream);
 
-// Backward pass, scalar gate, delta rule (kda_bwd.hip).
-constexpr int BREC_BYTES = 104 * 1024;  // per (entry, head): operand fragments of both chains, and T
-struct BwdParams {
-  const uint16_t* q;      // bf16 [tokens, H_qk, 128]
-  const uint16_t* k;
-  const uint16_t* v;      // bf16 [tokens, H, 128]
-  const uint16_t* g_raw;  // bf16 [tokens, H]
-  const float* beta;      // fp32 [tokens, H] (logits)
-  const float* A_log;     // fp32 [H]
-  const uint16_t* dout;   // bf16 [tokens, H, 128]
-  const float* dfinal;    // fp32 [seqs, H, 128, 128] ([V][K]) or null
-  const float* s0;        // fp32 initial state, same layout, or null
-  float scale;
-  int H, H_qk;
-  int dense_T;            // >= 0: B rows of dense_T tokens; -1: read chunks / seqs / order
-  const int4* chunks;
-  const int4* seqs;
-  const int* order;
-  int n_entries, n_chains;
-  uint16_t* states;        // fp16 [entries][H][V][K]: the state entering every chunk
-  uint16_t* dstates;       // fp16 [entries][H][V][K]: the gradient of the state leaving every chunk
-  uint8_t* brec;           // [entries][H][BREC_BYTES]
-  float* dq;              // fp32 [tokens, H_qk, 128]
-  float* dk;
-  float* dv;              // fp32 [tokens, H, 128]
-  float* dg_raw;          // fp32 [tokens, H]
-  float* dbeta;           // fp32 [tokens, H]
-  float* dA_log;          // fp32 [H]
-  float* dinit;           // fp32 [seqs, H, 128, 128] or null
-  int touch_ahead = 0;    // chunk-parallel kernels: prefetch the inputs of job + touch_ahead
-};
-// Stages, in this order: 0 the coefficient records (after clearing dA_log, and dq, dk when value heads
-// share q/k heads; qk_floats: elements of dq), 1 both chains (the chunk states and their gradients),
-// 2 the gradients.
-void launch_bwd(const BwdParams& p, size_t qk_floats, int stage, hipStream_t stream);
-
 }  // namespace kda
