@@ -10,7 +10,10 @@ precision of the forward's own chunk path, whose state error the forward
 tests hold to 1e-3 rel-L2.  Every gradient is bilinear in those states and the
 upstream gradients, so its relative error is of that order times a small
 factor: each gradient is held to GRAD_REL rel-L2 and to GRAD_MAXABS of its
-own largest magnitude.
+own largest magnitude.  dA_log is a sum over every token of a head,
+sum_t dg_t g_t, whose terms have both signs: its error is held to GRAD_REL
+times sum_t |dg_t g_t| (the sum's condition), computed from the oracle's dg_raw
+(dg_t g_t = dg_raw_t softplus(g_raw_t) / sigmoid(g_raw_t)).
 """
 
 import numpy as np
@@ -79,14 +82,26 @@ def run_oracle_bwd(inp, dout, dfinal, heads=None):
                       cu_seqlens=inp.get("cu_seqlens"))
 
 
-def compare(got, ref, label):
+def dA_log_condition(ref, g_raw_bits):
+    """sum over a head's tokens of |dg_t g_t| (the magnitude the dA_log sum is formed from)."""
+    x = oracle.widen(g_raw_bits)                                   # [B, T, H]
+    sp = np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
+    sig = 1.0 / (1.0 + np.exp(-x))
+    return np.abs(ref["dg_raw"] * sp / sig).sum(axis=(0, 1))
+
+
+def compare(got, ref, label, g_raw_bits):
     errs = {}
     for n in NAMES:
         r, x = ref[n], got[n]
         assert x.shape == r.shape, (label, n, x.shape, r.shape)
         assert np.all(np.isfinite(x)), (label, n)
-        rel = rel_l2(x, r)
-        mx = float(np.max(np.abs(x - r)) / max(np.max(np.abs(r)), 1e-30))
+        if n == "dA_log":  # per head, against the condition of the sum
+            rel = float(np.max(np.abs(x - r) / np.maximum(dA_log_condition(ref, g_raw_bits), 1e-30)))
+            mx = rel
+        else:
+            rel = rel_l2(x, r)
+            mx = float(np.max(np.abs(x - r)) / max(np.max(np.abs(r)), 1e-30))
         errs[n] = (rel, mx)
     print(label, " ".join("%s %.1e/%.1e" % (n, *errs[n]) for n in NAMES), flush=True)
     for n, (rel, mx) in errs.items():
@@ -113,7 +128,7 @@ def test_backward_matches_the_oracle(label, kw, dstd):
     dout, dfinal = upstream(inp, kw["seed"] + 500, dstd)
     got = run_gpu_bwd(inp, dout, dfinal)
     ref = run_oracle_bwd(inp, dout, dfinal)
-    compare(got, ref, label)
+    compare(got, ref, label, inp["g_raw"])
 
 
 def test_backward_grouped_heads_long_sequence():
@@ -122,7 +137,7 @@ def test_backward_grouped_heads_long_sequence():
     dout, dfinal = upstream(inp, 579)
     got = run_gpu_bwd(inp, dout, dfinal)
     ref = run_oracle_bwd(inp, dout, dfinal)
-    compare(got, ref, "grouped heads T=4096 H=8 H_qk=4")
+    compare(got, ref, "grouped heads T=4096 H=8 H_qk=4", inp["g_raw"])
 
 
 def test_backward_many_jobs_sampled_heads():
@@ -135,7 +150,7 @@ def test_backward_many_jobs_sampled_heads():
     ref = run_oracle_bwd(inp, dout, dfinal, heads=heads)
     sub = {n: (got[n][heads] if n == "dA_log" else got[n][:, heads] if n == "dinitial_state"
                else got[n][:, :, heads]) for n in NAMES}
-    compare(sub, ref, "T=8192 H=32, heads 0 and 31")
+    compare(sub, ref, "T=8192 H=32, heads 0 and 31", inp["g_raw"][:, :, heads])
 
 
 def test_backward_zero_tokens():
@@ -155,3 +170,47 @@ def test_backward_rejects_the_per_channel_gate():
     x = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16, device="cuda")
     with pytest.raises(ValueError):
         kda.bwd(x, x, x, x, torch.zeros(1, 64, 1, device="cuda"), torch.zeros(1, device="cuda"), x)
+
+
+# ---- seeded random configurations -----------------------------------------------------------------
+REGIMES = {
+    "workload": dict(A_log=(-1.0, 1.0)),
+    "slow decay": dict(A_log=(-6.0, -4.0)),
+    "harsh decay": dict(A_log=(2.0, 3.0)),
+    "correlated keys": dict(A_log=-8.0, k_noise=0.5, b_shift=4.6),
+}
+
+
+def draw_bwd_case(i):
+    """Case i: q/k heads and grouping, dense rows or packed sequences (empty ones allowed), lengths rarely a
+    multiple of 64, initial state and dfinal present or not, and a gate regime, all from seed 1900 + i."""
+    rng = np.random.default_rng(1900 + i)
+    H_qk = int(rng.choice([1, 2, 4]))
+    H = H_qk * int(rng.choice([1, 2, 3]))
+    regime = str(rng.choice(sorted(REGIMES)))
+    kw = dict(REGIMES[regime], gate_per_channel=False, seed=2900 + i)
+    if rng.integers(0, 2):
+        kw["state_std"] = 0.05
+    dstd = 0.1 if rng.integers(0, 2) else None
+    if rng.integers(0, 2):
+        N = int(rng.integers(1, 6))
+        lens = [int(x) for x in rng.integers(0, 300, N)]
+        if sum(lens) == 0:
+            lens[0] = 1
+        inp = make_inputs(1, sum(lens), H, H_qk, N=N, lengths=lens, **kw)
+        shape = "packed %s" % lens
+    else:
+        B, T = int(rng.integers(1, 3)), int(rng.integers(1, 400))
+        inp = make_inputs(B, T, H, H_qk, **kw)
+        shape = "B=%d T=%d" % (B, T)
+    what = "bwd case %d: %s H=%d H_qk=%d, %s, state %s, dfinal %s" % (
+        i, shape, H, H_qk, regime, "none" if inp["initial_state"] is None else "fp32", dstd)
+    return inp, dstd, what
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_backward_random_configuration(i):
+    inp, dstd, what = draw_bwd_case(i)
+    print(what, flush=True)
+    dout, dfinal = upstream(inp, 3900 + i, dstd)
+    compare(run_gpu_bwd(inp, dout, dfinal), run_oracle_bwd(inp, dout, dfinal), what, inp["g_raw"])
