@@ -379,6 +379,55 @@ def run_sweep(steps, warmup):
                       "steps": steps, "warmup": warmup, "rows": rows}), flush=True)
 
 
+# the backward table of the FlashQLA H200 results page: heads x total tokens, split into 8 equal sequences
+BWD_SWEEP_HEADS = (32, 48, 64)
+BWD_SWEEP_TOKENS = (16384, 32768, 65536, 131072, 262144)
+
+
+def run_bwd_sweep(steps, warmup):
+    """Backward sweep: every (heads, tokens) row of the backward table, 8 sequences, scalar decay, one
+    kda.bwd_varlen call per step.  Inputs are drawn on the device from a seeded generator with the
+    workloads' distributions (q, k, v, g_raw, beta logits, dout ~ N(0, 1); A_log = 0): the largest rows hold
+    several GB per tensor.  Prints one JSON line with a row per (heads, tokens)."""
+    import torch
+    from chunked_gated_delta_10_amd import kda
+    rows = []
+    for H in BWD_SWEEP_HEADS:
+        for T in BWD_SWEEP_TOKENS:
+            gen = torch.Generator(device="cuda")
+            gen.manual_seed(3000 + H * 1000 + T // 1024)
+
+            def draw(*shape):
+                return torch.randn(*shape, generator=gen, device="cuda", dtype=torch.float32)
+            q, k, v = (draw(1, T, H, D).to(torch.bfloat16) for _ in range(3))
+            g = draw(1, T, H).to(torch.bfloat16)
+            b = draw(1, T, H)
+            dout = draw(1, T, H, D).to(torch.bfloat16)
+            a = torch.zeros(H, device="cuda")
+            cu = torch.arange(0, T + 1, T // 8, dtype=torch.int32, device="cuda")
+            ws = torch.empty(kda.bwd_workspace_bytes(1, T, H, H, 8), dtype=torch.uint8, device="cuda")
+            print("backward H=%d T=%d" % (H, T), file=sys.stderr, flush=True)
+
+            def step():
+                return kda.bwd_varlen(q, k, v, g, b, a, dout, cu, workspace=ws)
+            for _ in range(warmup):
+                step()
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(steps):
+                step()
+            e1.record()
+            torch.cuda.synchronize()
+            ms = e0.elapsed_time(e1) / steps
+            rows.append({"heads": H, "tokens": T, "sequences": 8, "ms": round(ms, 4),
+                         "tokens_per_s": round(T / (ms * 1e-3), 1)})
+            del q, k, v, g, b, dout, ws
+            torch.cuda.empty_cache()
+    print(json.dumps({"bwd_sweep": "gated delta rule backward, scalar decay, K=V=128, 8 equal sequences, "
+                      "fp32 gradients", "steps": steps, "warmup": warmup, "rows": rows}), flush=True)
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__, formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
@@ -402,6 +451,8 @@ def main():
                          "its per-kernel averages; for profiling runs")
     ap.add_argument("--sweep", action="store_true",
                     help="only run the grouped-value-head sweep (head shapes x sequence patterns)")
+    ap.add_argument("--bwd-sweep", action="store_true",
+                    help="only run the backward sweep (heads 32/48/64 x 16k..256k tokens in 8 sequences)")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(args.traffic_from, args.copy_bytes, args.traffic_workload)
@@ -422,6 +473,9 @@ def main():
     kda.load()
     if args.sweep:
         run_sweep(args.steps, args.warmup)
+        return
+    if args.bwd_sweep:
+        run_bwd_sweep(args.steps, args.warmup)
         return
     if args.only:
         ms, per_kernel, _, w, pct = time_workload(args.only, args.steps, args.warmup)
