@@ -156,3 +156,50 @@ def test_noalloc_validation(lib, over, code):
 
 def test_noalloc_zero_batch_is_a_no_op(lib):
     assert fwd_noalloc(lib, B=0) == 0
+
+
+# ---- backward (scalar gate) ---------------------------------------------------------------------------------
+
+
+def test_bwd_workspace_query(lib):
+    # per (chunk, head): two fp16 state blocks (32 KiB each) and a 104 KiB operator record
+    ws = lib.kda_bwd_workspace_bytes(1, 32768, 32, 32, 8)
+    assert ws >= 512 * 32 * (2 * 32768 + 106496)
+    assert lib.kda_bwd_workspace_bytes(2, 1000, 4, 4, 0) > 0
+    assert lib.kda_bwd_workspace_bytes(2, 100, 4, 4, 3) == 0    # packed needs B == 1
+    assert lib.kda_bwd_workspace_bytes(1, 100, 3, 4, 0) == 0    # H % H_qk != 0
+    assert lib.kda_bwd_workspace_bytes(1, -5, 4, 4, 0) == 0
+
+
+def bwd(lib, **over):
+    a = dict(q=P, k=P, v=P, g=P, beta=P, alog=P, scale=0.088, pc=0, s0=None, dout=P, dfin=None, dq=P, dk=P, dv=P,
+             dg=P, db=P, dal=P, dinit=None, B=1, T=64, Hqk=2, H=2, K=128, V=128, ws=P, wsb=1 << 40)
+    a.update(over)
+    return lib.kda_bwd(a["q"], a["k"], a["v"], a["g"], a["beta"], a["alog"], a["scale"], a["pc"], a["s0"], a["dout"],
+                       a["dfin"], a["dq"], a["dk"], a["dv"], a["dg"], a["db"], a["dal"], a["dinit"], a["B"], a["T"],
+                       a["Hqk"], a["H"], a["K"], a["V"], a["ws"], a["wsb"], None)
+
+
+@pytest.mark.parametrize("over,code", [
+    (dict(pc=1), 2), (dict(K=64), 2), (dict(H=3), 2), (dict(T=-1), 2), (dict(B=-1), 2),
+    (dict(dout=None), 1), (dict(dq=None), 1), (dict(dv=None), 1), (dict(dal=None), 1), (dict(beta=None), 1),
+    (dict(dk=P + 8), 6), (dict(s0=P + 4), 6), (dict(dinit=P + 2), 6), (dict(ws=P + 16), 6),
+    (dict(ws=None), 5), (dict(wsb=4096), 5),
+])
+def test_bwd_validation(lib, over, code):
+    st = bwd(lib, **over)
+    assert st == code, (st, lib.kda_last_error())
+    assert lib.kda_last_error().decode() != ""
+
+
+def test_bwd_empty_batch_is_a_noop(lib):
+    assert bwd(lib, B=0) == 0
+
+
+def test_bwd_varlen_validation(lib):
+    def call(cu, N):
+        return lib.kda_bwd_varlen(P, P, P, P, P, P, 0.088, 0, None, P, None, P, P, P, P, P, P, None, cu, N, 100, 2, 2,
+                                  128, 128, P, 1 << 40, None)
+    assert call(None, 3) == 1
+    assert call(P + 2, 3) == 6
+    assert call(None, 0) == 0
