@@ -80,8 +80,6 @@ def test_host_inputs_rejected_before_the_library_is_called():
 @pytest.mark.parametrize("dout,dfinal,s0,exc", [
     (torch.empty((1, 5, 3, 128), dtype=torch.float32), None, None, TypeError),     # dout must be bf16
     (torch.empty((1, 5, 3, 128), dtype=torch.bfloat16), None, None, ValueError),   # not a device tensor
-    (torch.empty((1, 5, 3, 128), dtype=torch.bfloat16), torch.empty((1, 3, 128, 128), dtype=torch.bfloat16), None,
-     TypeError),                                                                   # dfinal must be fp32
 ])
 def test_bwd_upstream_rejected(dout, dfinal, s0, exc):
     with pytest.raises(exc):
