@@ -361,11 +361,12 @@ kda_status run_decode(const void* q, const void* k, const void* v, const void* g
   return ok();
 }
 
-// ---- backward (scalar gate) ------------------------------------------------
+// ---- backward ----------------------------------------------------------------
 // Workspace: a 256-byte header, the schedule (sequence table, chunk table,
 // order), then the state entering every (chunk, head) and the gradient of
 // the state leaving it (fp16, 32 KiB each), and the chains' operator records
-// (kda::BREC_BYTES each).
+// (sized for the per-channel gate's kda::BREC_PC_BYTES each; the scalar gate
+// uses kda::BREC_BYTES of each slot).
 struct BwdLayout {
   size_t seqs, chunks, order, states, dstates, brec, total;
 };
@@ -379,7 +380,7 @@ BwdLayout bwd_layout(int n_seqs, int n_entries, int H) {
   L.states = L.order + round_up((size_t)n_seqs * sizeof(int));
   L.dstates = L.states + round_up(jobs * kda::HD * kda::HD * sizeof(uint16_t));
   L.brec = L.dstates + round_up(jobs * kda::HD * kda::HD * sizeof(uint16_t));
-  L.total = L.brec + round_up(jobs * kda::BREC_BYTES);
+  L.total = L.brec + round_up(jobs * kda::BREC_PC_BYTES);
   return L;
 }
 
@@ -405,8 +406,6 @@ kda_status run_backward(const BwdArgs& a) {
             a.stream, true};
   kda_status st = validate_common(f);
   if (st != KDA_OK) return st;
-  if (a.gate_per_channel != 0)
-    return fail(KDA_ERR_SHAPE, "the backward pass supports the scalar gate only (gate_per_channel = 0)");
   if (a.n_seqs == 0) return ok();
   const long tokens = (long)a.rows * a.T;
   if (tokens > 0) {
@@ -445,7 +444,8 @@ kda_status run_backward(const BwdArgs& a) {
   }
   kda::BwdParams bp{static_cast<const uint16_t*>(a.q), static_cast<const uint16_t*>(a.k),
                     static_cast<const uint16_t*>(a.v), static_cast<const uint16_t*>(a.g_raw), a.beta, a.A_log,
-                    static_cast<const uint16_t*>(a.dout), a.dfinal, a.s0, a.scale, a.H, a.H_qk, a.cu ? -1 : a.T,
+                    static_cast<const uint16_t*>(a.dout), a.dfinal, a.s0, a.scale, a.gate_per_channel != 0 ? 1 : 0,
+                    a.gate_per_channel != 0 ? kda::BREC_PC_BYTES : kda::BREC_BYTES, a.H, a.H_qk, a.cu ? -1 : a.T,
                     chunks, seqs, order, tokens > 0 ? n_entries : 0, a.n_seqs * a.H,
                     reinterpret_cast<uint16_t*>(ws + L.states), reinterpret_cast<uint16_t*>(ws + L.dstates),
                     ws + L.brec, a.dq, a.dk, a.dv, a.dg_raw, a.dbeta, a.dA_log, a.dinit};

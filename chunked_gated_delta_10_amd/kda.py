@@ -443,10 +443,11 @@ def bwd_workspace_bytes(B: int, T: int, H_qk: int, H: int, N: int = 0) -> int:
     return int(load().kda_bwd_workspace_bytes(B, T, H_qk, H, N))
 
 
-def _grad_buffers(B, T, H_qk, H, K, V, C, dev, want_dinit):
+def _grad_buffers(B, T, H_qk, H, K, V, C, dev, want_dinit, per_channel):
     f = dict(dtype=torch.float32, device=dev)
     return dict(dq=torch.empty((B, T, H_qk, K), **f), dk=torch.empty((B, T, H_qk, K), **f),
-                dv=torch.empty((B, T, H, V), **f), dg_raw=torch.empty((B, T, H), **f),
+                dv=torch.empty((B, T, H, V), **f),
+                dg_raw=torch.empty((B, T, H, K) if per_channel else (B, T, H), **f),
                 dbeta_logits=torch.empty((B, T, H), **f), dA_log=torch.empty((H,), **f),
                 dinitial_state=torch.empty((C, H, V, K), **f) if want_dinit else None)
 
@@ -466,13 +467,13 @@ def _bwd_checks(dout, dfinal, initial_state, B, T, H, V, K, C, dev):
 def bwd(q, k, v, g_raw, beta_logits, A_log, dout, dfinal: Optional[torch.Tensor] = None,
         scale: Optional[float] = None, initial_state: Optional[torch.Tensor] = None,
         workspace: Optional[torch.Tensor] = None, stream=None) -> dict:
-    """Gradients of sum(dout * out) + sum(dfinal * final_state) through fwd (scalar gate, g_raw [B, T, H]).
+    """Gradients of sum(dout * out) + sum(dfinal * final_state) through fwd (g_raw [B, T, H] for one decay
+    per token-head, [B, T, H, K] for one per key channel).
 
-    Returns {dq, dk, dv, dg_raw, dbeta_logits, dA_log, dinitial_state}, all float32."""
+    Returns {dq, dk, dv, dg_raw, dbeta_logits, dA_log, dinitial_state}, all float32 (dg_raw in g_raw's
+    shape)."""
     lib = load()
     B, T, H_qk, H, K, V, per_channel = _prep(q, k, v, g_raw, beta_logits, A_log)
-    if per_channel:
-        raise ValueError("the backward pass supports the scalar gate only (g_raw [B, T, H])")
     scale = K ** -0.5 if scale is None else float(scale)
     dev = q.device
     _bwd_checks(dout, dfinal, initial_state, B, T, H, V, K, B, dev)
@@ -480,8 +481,8 @@ def bwd(q, k, v, g_raw, beta_logits, A_log, dout, dfinal: Optional[torch.Tensor]
     if workspace is None:
         workspace = _workspace(nbytes, dev)
     _check_workspace(workspace, nbytes, dev)
-    g = _grad_buffers(B, T, H_qk, H, K, V, B, dev, True)
-    _check(lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale, 0,
+    g = _grad_buffers(B, T, H_qk, H, K, V, B, dev, True, per_channel)
+    _check(lib.kda_bwd(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale, per_channel,
                        _ptr(initial_state), _ptr(dout), _ptr(dfinal), _ptr(g["dq"]), _ptr(g["dk"]), _ptr(g["dv"]),
                        _ptr(g["dg_raw"]), _ptr(g["dbeta_logits"]), _ptr(g["dA_log"]), _ptr(g["dinitial_state"]),
                        B, T, H_qk, H, K, V, _ptr(workspace), workspace.numel(), _stream(stream)))
@@ -495,8 +496,6 @@ def bwd_varlen(q, k, v, g_raw, beta_logits, A_log, dout, cu_seqlens: torch.Tenso
     """bwd over packed sequences (B = 1); states and dinitial_state are [N, H, V, K]."""
     lib = load()
     B, T, H_qk, H, K, V, per_channel = _prep(q, k, v, g_raw, beta_logits, A_log)
-    if per_channel:
-        raise ValueError("the backward pass supports the scalar gate only (g_raw [1, T, H])")
     if B != 1:
         raise ValueError("packed sequences need B == 1")
     _need(cu_seqlens, "cu_seqlens", torch.int32)
@@ -510,8 +509,9 @@ def bwd_varlen(q, k, v, g_raw, beta_logits, A_log, dout, cu_seqlens: torch.Tenso
     if workspace is None:
         workspace = _workspace(nbytes, dev)
     _check_workspace(workspace, nbytes, dev)
-    g = _grad_buffers(1, T, H_qk, H, K, V, max(N, 0), dev, True)
-    _check(lib.kda_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale, 0,
+    g = _grad_buffers(1, T, H_qk, H, K, V, max(N, 0), dev, True, per_channel)
+    _check(lib.kda_bwd_varlen(_ptr(q), _ptr(k), _ptr(v), _ptr(g_raw), _ptr(beta_logits), _ptr(A_log), scale,
+                              per_channel,
                               _ptr(initial_state), _ptr(dout), _ptr(dfinal), _ptr(g["dq"]), _ptr(g["dk"]),
                               _ptr(g["dv"]), _ptr(g["dg_raw"]), _ptr(g["dbeta_logits"]), _ptr(g["dA_log"]),
                               _ptr(g["dinitial_state"]), _ptr(cu_seqlens), N, T, H_qk, H, K, V, _ptr(workspace),

@@ -200,32 +200,34 @@ kda_status kda_la_decode_step(const void* q, const void* k, const void* v, const
                               int V, void* stream);
 
 /*
- * Backward pass of the scalar-gate forward (gate_per_channel = 0: the gated
- * delta rule with grouped value heads whose backward the FlashQLA H200 page
- * times, "BACKWARD BENCHMARKS" table; the page does not define it, and it is
- * read as the gradient of a scalar loss through kda_fwd).  Returns the
- * gradients of
+ * Backward pass of kda_fwd, for both gate modes: gate_per_channel = 1 (KDA,
+ * one decay per key channel: the method of the cuLA KDA and FlashKDA pages)
+ * and gate_per_channel = 0 (the gated delta rule with grouped value heads
+ * whose backward the FlashQLA H200 page times, "BACKWARD BENCHMARKS" table).
+ * The pages do not define the backward; it is read as the gradient of a
+ * scalar loss through kda_fwd.  Returns the gradients of
  *     L = sum(dout * out) + sum(dfinal * final_state)
  * where (out, final_state) = kda_fwd with the same inputs, with respect to
  * q, k, v, g_raw, beta_logits, A_log and initial_state.
  *
- * Inputs: q, k, v, g_raw (bf16 [B, T, H]), beta_logits, A_log, scale as for
- * kda_fwd; initial_state fp32 [B, H, V, K] or NULL (zero state); dout bf16
- * [B, T, H, 128]; dfinal fp32 [B, H, V, K] or NULL (zero).  Outputs, fp32,
- * caller-allocated, each written whole (no accumulation into what they
- * held): dq, dk [B, T, H_qk, 128] (summed over the value heads of each q/k
- * head); dv [B, T, H, 128]; dg_raw, dbeta_logits [B, T, H]; dA_log [H];
- * dinitial_state [B, H, V, K], or NULL (not written).
+ * Inputs: q, k, v, g_raw (bf16 [B, T, H, 128] or [B, T, H]), beta_logits,
+ * A_log, scale as for kda_fwd; initial_state fp32 [B, H, V, K] or NULL (zero
+ * state); dout bf16 [B, T, H, 128]; dfinal fp32 [B, H, V, K] or NULL (zero).
+ * Outputs, fp32, caller-allocated, each written whole (no accumulation into
+ * what they held): dq, dk [B, T, H_qk, 128] (summed over the value heads of
+ * each q/k head); dv [B, T, H, 128]; dg_raw in g_raw's layout;
+ * dbeta_logits [B, T, H]; dA_log [H]; dinitial_state [B, H, V, K], or NULL
+ * (not written).
  *
  * The forward is recomputed inside the call (the state entering every
  * 64-token chunk is kept in the workspace, fp16), so nothing from an earlier
  * kda_fwd call is needed.  Workspace bytes:
- * kda_bwd_workspace_bytes(B, T, H_qk, H, 0) (N > 0: kda_bwd_varlen), 256-byte
- * aligned, contents garbage before and after.  gate_per_channel = 1 is
- * rejected with KDA_ERR_SHAPE.  dq, dk (when H > H_qk) and dA_log are
- * accumulated with float atomics, so their last bits may differ from run to
- * run.  Other errors and the B/N/T == 0 behaviour follow kda_fwd /
- * kda_fwd_varlen (T == 0: dinitial_state = dfinal, or zero).
+ * kda_bwd_workspace_bytes(B, T, H_qk, H, 0) (N > 0: kda_bwd_varlen), the same
+ * for both gate modes, 256-byte aligned, contents garbage before and after.
+ * dq, dk (when H > H_qk) and dA_log are accumulated with float atomics, so
+ * their last bits may differ from run to run.  Other errors and the B/N/T == 0
+ * behaviour follow kda_fwd / kda_fwd_varlen (T == 0: dinitial_state = dfinal,
+ * or zero).
  */
 size_t kda_bwd_workspace_bytes(int B, int T, int H_qk, int H, int N);
 kda_status kda_bwd(const void* q, const void* k, const void* v, const void* g_raw,

@@ -158,13 +158,14 @@ def test_noalloc_zero_batch_is_a_no_op(lib):
     assert fwd_noalloc(lib, B=0) == 0
 
 
-# ---- backward (scalar gate) ---------------------------------------------------------------------------------
+# ---- backward --------------------------------------------------------------------------------------------------
 
 
 def test_bwd_workspace_query(lib):
-    # per (chunk, head): two fp16 state blocks (32 KiB each) and a 104 KiB operator record
+    # per (chunk, head): two fp16 state blocks (32 KiB each) and a 120 KiB operator record (the per-channel
+    # gate's; the scalar gate uses 104 KiB of it)
     ws = lib.kda_bwd_workspace_bytes(1, 32768, 32, 32, 8)
-    assert ws >= 512 * 32 * (2 * 32768 + 106496)
+    assert ws >= 512 * 32 * (2 * 32768 + 122880)
     assert lib.kda_bwd_workspace_bytes(2, 1000, 4, 4, 0) > 0
     assert lib.kda_bwd_workspace_bytes(2, 100, 4, 4, 3) == 0    # packed needs B == 1
     assert lib.kda_bwd_workspace_bytes(1, 100, 3, 4, 0) == 0    # H % H_qk != 0
@@ -181,7 +182,7 @@ def bwd(lib, **over):
 
 
 @pytest.mark.parametrize("over,code", [
-    (dict(pc=1), 2), (dict(K=64), 2), (dict(H=3), 2), (dict(T=-1), 2), (dict(B=-1), 2),
+    (dict(pc=1, K=64), 2), (dict(K=64), 2), (dict(pc=1, dq=None), 1), (dict(H=3), 2), (dict(T=-1), 2), (dict(B=-1), 2),
     (dict(dout=None), 1), (dict(dq=None), 1), (dict(dv=None), 1), (dict(dal=None), 1), (dict(beta=None), 1),
     (dict(dk=P + 8), 6), (dict(s0=P + 4), 6), (dict(dinit=P + 2), 6), (dict(ws=P + 16), 6),
     (dict(ws=None), 5), (dict(wsb=4096), 5),

@@ -1,5 +1,6 @@
-"""GPU parity of the scalar-gate backward pass (kda.bwd / kda.bwd_varlen, C ABI
-kda_bwd / kda_bwd_varlen) against the fp64 backward oracle.
+"""GPU parity of the backward pass with one decay per token-head (kda.bwd /
+kda.bwd_varlen, C ABI kda_bwd / kda_bwd_varlen) against the fp64 backward
+oracle; the helpers serve the per-channel gate's tests as well.
 
 The oracle (oracle/kda_backward.py) is reverse-mode differentiation of the
 token-by-token forward, pinned on the CPU to complex-step and finite
@@ -64,7 +65,8 @@ def run_gpu_bwd(inp, dout, dfinal):
 
 
 def run_oracle_bwd(inp, dout, dfinal, heads=None):
-    """The oracle on all value heads, or on `heads` only (q/k heads not shared: H == H_qk)."""
+    """The oracle on all value heads, or on `heads` only (q/k heads not shared: H == H_qk).  The gate mode
+    follows g_raw's rank."""
     w = oracle.widen
     q, k, v, g, b, a = w(inp["q"]), w(inp["k"]), w(inp["v"]), w(inp["g_raw"]), inp["b"], inp["A_log"]
     do = w(dout)
@@ -78,16 +80,16 @@ def run_oracle_bwd(inp, dout, dfinal, heads=None):
         q, k, v, g, b, a, do = q[:, :, hs], k[:, :, hs], v[:, :, hs], g[:, :, hs], b[:, :, hs], a[hs], do[:, :, hs]
         s0 = None if s0 is None else s0[:, hs]
         df = df[:, hs]
-    return KB.kda_bwd(q, k, v, g, b, a, inp["scale"], do, df, gate_per_channel=False, initial_state=s0,
+    return KB.kda_bwd(q, k, v, g, b, a, inp["scale"], do, df, gate_per_channel=g.ndim == 4, initial_state=s0,
                       cu_seqlens=inp.get("cu_seqlens"))
 
 
 def dA_log_condition(ref, g_raw_bits):
-    """sum over a head's tokens of |dg_t g_t| (the magnitude the dA_log sum is formed from)."""
-    x = oracle.widen(g_raw_bits)                                   # [B, T, H]
+    """sum over a head's tokens (and key channels) of |dg g| (the magnitude the dA_log sum is formed from)."""
+    x = oracle.widen(g_raw_bits)                                   # [B, T, H] or [B, T, H, K]
     sp = np.maximum(x, 0.0) + np.log1p(np.exp(-np.abs(x)))
     sig = 1.0 / (1.0 + np.exp(-x))
-    return np.abs(ref["dg_raw"] * sp / sig).sum(axis=(0, 1))
+    return np.abs(ref["dg_raw"] * sp / sig).sum(axis=(0, 1) if x.ndim == 3 else (0, 1, 3))
 
 
 def compare(got, ref, label, g_raw_bits):
@@ -164,12 +166,6 @@ def test_backward_zero_tokens():
     torch.cuda.synchronize()
     assert torch.equal(g["dinitial_state"], df)
     assert torch.count_nonzero(g["dA_log"]) == 0
-
-
-def test_backward_rejects_the_per_channel_gate():
-    x = torch.zeros(1, 64, 1, 128, dtype=torch.bfloat16, device="cuda")
-    with pytest.raises(ValueError):
-        kda.bwd(x, x, x, x, torch.zeros(1, 64, 1, device="cuda"), torch.zeros(1, device="cuda"), x)
 
 
 # ---- seeded random configurations -----------------------------------------------------------------
