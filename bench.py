@@ -32,8 +32,9 @@ FLOP_PER_TOKEN_HEAD = 6 * D * D + 5 * C * D   # 139,264 (algorithmic, per token 
 FORWARD_SOURCES = ["chunked_gated_delta_10_amd/csrc/" + f for f in
                    ("kda_chunk.hip", "kda_chunk_job.h", "kda_fused.hip", "kda_recur.hip", "kda_table.hip",
                     "kda_decode.hip", "kda_device.h", "kda_kernels.h")]
-BACKWARD_SOURCES = ["chunked_gated_delta_10_amd/csrc/" + f for f in ("kda_bwd.hip", "kda_bwd.h", "kda_device.h",
-                                                                     "kda_kernels.h")]
+BACKWARD_SOURCES = ["chunked_gated_delta_10_amd/csrc/" + f for f in ("kda_bwd.hip", "kda_bwd_pc.hip",
+                                                                     "kda_bwd_common.h", "kda_bwd.h",
+                                                                     "kda_device.h", "kda_kernels.h")]
 
 
 def algorithmic_bytes(w, with_state=True, state_bytes=4):
@@ -56,13 +57,14 @@ def algorithmic_bytes(w, with_state=True, state_bytes=4):
 
 def backward_bytes(w):
     """The backward operator's own inputs read once and outputs written once (bytes): q, k, v, dout (bf16),
-    g_raw (bf16), beta logits (fp32) in; dq, dk, dv, dg_raw, dbeta (fp32) out.  The gradient kernel touches
-    all of them.  The recomputed forward, the chunk states and the adjoint's records are the method's own
-    intermediates and are not counted."""
+    g_raw (bf16, one or 128 per token-head), beta logits (fp32) in; dq, dk, dv, dg_raw, dbeta (fp32) out.
+    The gradient kernel touches all of them.  The recomputed forward, the chunk states and the adjoint's
+    records are the method's own intermediates and are not counted."""
     tok = w.B * w.T
     C_ = w.N if w.N else w.B
-    reads = 2 * tok * w.H_qk * D * 2 + 2 * tok * w.H * D * 2 + tok * w.H * (2 + 4)
-    writes = 2 * tok * w.H_qk * D * 4 + tok * w.H * D * 4 + 2 * tok * w.H * 4
+    gw = D if w.gate_per_channel else 1
+    reads = 2 * tok * w.H_qk * D * 2 + 2 * tok * w.H * D * 2 + tok * w.H * (2 * gw + 4)
+    writes = 2 * tok * w.H_qk * D * 4 + tok * w.H * D * 4 + tok * w.H * (4 * gw + 4)
     return {"kda_bwd_grad": reads + writes, "total": reads + writes + w.H * 8 + C_ * w.H * D * D * 4}
 
 
@@ -265,9 +267,14 @@ def time_workload(name, steps, warmup, bf16_state=False):
         dout = torch.from_numpy(dout_bits.view("int16")).view(torch.bfloat16).cuda()
         ws = torch.empty(kda.bwd_workspace_bytes(w.B, w.T, w.H_qk, w.H, w.N), dtype=torch.uint8, device="cuda")
 
-        def step():
-            kda.bwd_varlen(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], dout, d["cu_seqlens"],
-                           scale=inp["scale"], workspace=ws)
+        if w.N:
+            def step():
+                kda.bwd_varlen(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], dout, d["cu_seqlens"],
+                               scale=inp["scale"], initial_state=d["initial_state"], workspace=ws)
+        else:
+            def step():
+                kda.bwd(d["q"], d["k"], d["v"], d["g_raw"], d["b"], d["A_log"], dout, scale=inp["scale"],
+                        initial_state=d["initial_state"], workspace=ws)
     elif w.decode:
         st = d["initial_state"]
         out = torch.empty((w.B, w.H, D), dtype=torch.bfloat16, device="cuda")
@@ -446,7 +453,7 @@ def main():
     ap.add_argument("--copy-bytes", type=int, default=1024 * 1024 * 1024,
                     help="size of the calibration copy used with --traffic-from")
     ap.add_argument("--only", metavar="WORKLOAD",
-                    help="only time one workload (kda_tiny, kda_dense, kda_varlen, gdn_gva, kda_decode, la_varlen, la_decode, "
+                    help="only time one workload (kda_tiny, kda_dense, kda_varlen, gdn_gva, kda_decode, la_varlen, la_decode, kda_bwd, "
                          "gdn_bwd) and print "
                          "its per-kernel averages; for profiling runs")
     ap.add_argument("--sweep", action="store_true",
@@ -522,7 +529,7 @@ def main():
         # else runs (measured after the copy probe or the decode runs, both of its kernels ran ~10% slower,
         # the chunk-local one included, which never touches the state)
         for other in ("kda_dense_bf16_state", "kda_varlen", "gdn_gva", "kda_decode", "la_varlen", "la_decode",
-                      "gdn_bwd"):
+                      "gdn_bwd", "kda_bwd"):
             bf16_state = other.endswith("_bf16_state")
             osteps = args.steps if bf16_state else max(10, args.steps // 5)
             oms, opk, _, ow, _ = time_workload(other.replace("_bf16_state", ""), osteps, 10, bf16_state=bf16_state)

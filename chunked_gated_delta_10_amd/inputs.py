@@ -94,6 +94,9 @@ WORKLOADS: Dict[str, Workload] = {
     "gdn_bwd": Workload("gdn_bwd", B=1, T=32768, H=32, H_qk=32, gate_per_channel=False, A_log=(0.0, 0.0), N=8,
                         lengths=(4096,) * 8, seed=1007, backward=True,
                         note="gated delta rule backward, scalar decay, 8 sequences x 4096 tokens, 32 heads"),
+    # the backward of KDA itself (one decay per key channel) on the forward's dense shape
+    "kda_bwd": Workload("kda_bwd", B=2, T=16384, H=16, H_qk=16, state_std=0.02, seed=1008, backward=True,
+                        note="KDA backward, per-channel decay, B=2 T=16384 H=16, fp32 initial state"),
 }
 
 

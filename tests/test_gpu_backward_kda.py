@@ -41,3 +41,70 @@ def test_kda_backward_matches_the_oracle(label, kw, dstd):
     got = run_gpu_bwd(inp, dout, dfinal)
     ref = run_oracle_bwd(inp, dout, dfinal)
     compare(got, ref, label, inp["g_raw"])
+
+
+def test_kda_backward_grouped_heads_long_sequence():
+    # 64 chunks, two value heads on each q/k head
+    inp = make_inputs(1, 4096, 8, 4, gate_per_channel=True, A_log=(-1.0, 1.0), state_std=0.05, seed=181)
+    dout, dfinal = upstream(inp, 681)
+    compare(run_gpu_bwd(inp, dout, dfinal), run_oracle_bwd(inp, dout, dfinal), "kda grouped T=4096 H=8 H_qk=4",
+            inp["g_raw"])
+
+
+def test_kda_backward_benchmark_shape_sampled_heads():
+    # the KDA backward benchmark shape (B=2, T=16384, H=16, fp32 initial state): 8192 (chunk, head) jobs and
+    # chains of 256 chunks; heads 0 and 15 of both rows against the oracle
+    from chunked_gated_delta_10_amd.inputs import WORKLOADS, workload_inputs
+    w = WORKLOADS["kda_bwd"]
+    inp = workload_inputs("kda_bwd")
+    dout, dfinal = upstream(inp, w.seed + 500)
+    got = run_gpu_bwd(inp, dout, dfinal)
+    heads = [0, 15]
+    ref = run_oracle_bwd(inp, dout, dfinal, heads=heads)
+    sub = {n: (got[n][heads] if n == "dA_log" else got[n][:, heads] if n == "dinitial_state"
+               else got[n][:, :, heads]) for n in NAMES}
+    compare(sub, ref, "kda_bwd shape B=2 T=16384 H=16, heads 0 and 15", inp["g_raw"][:, :, heads])
+
+
+# ---- seeded random configurations -----------------------------------------------------------------
+REGIMES = {
+    "workload": dict(A_log=(-1.0, 1.0)),
+    "slow decay": dict(A_log=(-6.0, -4.0)),
+    "harsh decay": dict(A_log=(2.0, 3.0)),
+    "correlated keys": dict(A_log=-8.0, k_noise=0.5, b_shift=4.6),
+}
+
+
+def draw_kda_bwd_case(i):
+    """Case i: q/k heads and grouping, dense rows or packed sequences (empty ones allowed), lengths rarely a
+    multiple of 64, initial state and dfinal present or not, and a gate regime, all from seed 5100 + i."""
+    rng = np.random.default_rng(5100 + i)
+    H_qk = int(rng.choice([1, 2, 4]))
+    H = H_qk * int(rng.choice([1, 2, 3]))
+    regime = str(rng.choice(sorted(REGIMES)))
+    kw = dict(REGIMES[regime], gate_per_channel=True, seed=6100 + i)
+    if rng.integers(0, 2):
+        kw["state_std"] = 0.05
+    dstd = 0.1 if rng.integers(0, 2) else None
+    if rng.integers(0, 2):
+        N = int(rng.integers(1, 6))
+        lens = [int(x) for x in rng.integers(0, 300, N)]
+        if sum(lens) == 0:
+            lens[0] = 1
+        inp = make_inputs(1, sum(lens), H, H_qk, N=N, lengths=lens, **kw)
+        shape = "packed %s" % lens
+    else:
+        B, T = int(rng.integers(1, 3)), int(rng.integers(1, 400))
+        inp = make_inputs(B, T, H, H_qk, **kw)
+        shape = "B=%d T=%d" % (B, T)
+    what = "kda bwd case %d: %s H=%d H_qk=%d, %s, state %s, dfinal %s" % (
+        i, shape, H, H_qk, regime, "none" if inp["initial_state"] is None else "fp32", dstd)
+    return inp, dstd, what
+
+
+@pytest.mark.parametrize("i", range(16))
+def test_kda_backward_random_configuration(i):
+    inp, dstd, what = draw_kda_bwd_case(i)
+    print(what, flush=True)
+    dout, dfinal = upstream(inp, 7100 + i, dstd)
+    compare(run_gpu_bwd(inp, dout, dfinal), run_oracle_bwd(inp, dout, dfinal), what, inp["g_raw"])
