@@ -304,25 +304,32 @@ __global__ __launch_bounds__(NTH) void bwd_coef_pc_kernel(BwdParams p) {
       hq[jl] = sq;
       hk[jl] = sk;
     }
-#pragma unroll
-    for (int jl = 0; jl < 16; ++jl)
-#pragma unroll
-      for (int o = 1; o < 8; o <<= 1) {
-        hq[jl] += __shfl_xor(hq[jl], o);
-        hk[jl] += __shfl_xor(hk[jl], o);
-      }
-    // lane t % 8 writes partners 2 (t % 8) and 2 (t % 8) + 1
+    // sums over the 8 lanes of the row (channel groups), halving the partners at every step: lane
+    // cg = t % 8 ends with the full sums of partners 2 cg and 2 cg + 1
     const int cg = t & 7;
+    float q8[8], k8[8], q4[4], k4[4], q2[2], k2[2];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const bool hi = cg & 4;
+      q8[j] = (hi ? hq[8 + j] : hq[j]) + __shfl_xor(hi ? hq[j] : hq[8 + j], 4);
+      k8[j] = (hi ? hk[8 + j] : hk[j]) + __shfl_xor(hi ? hk[j] : hk[8 + j], 4);
+    }
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const bool hi = cg & 2;
+      q4[j] = (hi ? q8[4 + j] : q8[j]) + __shfl_xor(hi ? q8[j] : q8[4 + j], 2);
+      k4[j] = (hi ? k8[4 + j] : k8[j]) + __shfl_xor(hi ? k8[j] : k8[4 + j], 2);
+    }
+#pragma unroll
+    for (int j = 0; j < 2; ++j) {
+      const bool hi = cg & 1;
+      q2[j] = (hi ? q4[2 + j] : q4[j]) + __shfl_xor(hi ? q4[j] : q4[2 + j], 1);
+      k2[j] = (hi ? k4[2 + j] : k4[j]) + __shfl_xor(hi ? k4[j] : k4[2 + j], 1);
+    }
 #pragma unroll
     for (int u = 0; u < 2; ++u) {
       const int jl = 2 * cg + u, i = b0 + jl;
-      float vq = 0.f, vk = 0.f;
-#pragma unroll
-      for (int x = 0; x < 16; ++x)
-        if (x == jl) {
-          vq = hq[x];
-          vk = hk[x];
-        }
+      const float vq = q2[u], vk = k2[u];
       M16[r * LDN + i] = (f16)(i <= r ? vq : 0.f);
       AF[r * LDF + i] = i < r ? R.b[r] * vk : 0.f;
       HKg[r * CH + i] = (f16)(i < r ? vk : 0.f);
@@ -833,57 +840,63 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
       dgk[ib][jj] -= bfac * Z[jj];
     }
   }
-  // ---- the diagonal blocks, exactly: thread (row r8, channels c0 ..), partners of its block.
-  // With E = exp2(-|LG[r8] - LG[i]|): X, Yq take the partners i <= r8 (dH, dM rows r8 vanish
-  // beyond), Z the partners i >= r8 (columns r8 of dH, dM vanish before).
-  float Xd[16], Yd[16], Zd[16];
+  // ---- the diagonal blocks, exactly: thread -> block bb = t / 128, key channel c = t % 128, every pair
+  // i <= r of the block once (E = exp2(LG[r][c] - LG[i][c]) <= 1), row sums X, Yq for r and column
+  // sums Z for i in registers; then through one fp32 exchange matrix into the C layout:
+  // X + Z -> dkn, Yq -> dqn, X - Z -> dgk
   {
-    float lr[16];
-    load_f32x16(LG + r8 * LGS + c0, lr);
+    const int bb = t >> 7, c = t & (HD - 1), rb0 = 16 * bb;
+    float lgc[16], knc[16], qnc[16], Xd[16], Yd[16], Zd[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) Xd[j] = Yd[j] = Zd[j] = 0.f;
-    const int b0 = r8 & ~15;
-#pragma unroll 2
-    for (int jl = 0; jl < 16; ++jl) {
-      const int i = b0 + jl;
-      float li[16], ki[16], qi[16];
-      load_f32x16(LG + i * LGS + c0, li);
-      load_f16x16(KN + i * LDW + c0, ki);
-      load_f16x16(QN + i * LDW + c0, qi);
-      const float hr = (float)DH[r8 * LDN + i], mr = (float)DMm[r8 * LDN + i];  // row r8, column i
-      const float hc = (float)DH[i * LDN + r8], mcv = (float)DMm[i * LDN + r8];  // row i, column r8
+    for (int j = 0; j < 16; ++j) {
+      lgc[j] = LG[(rb0 + j) * LGS + c];
+      knc[j] = (float)KN[(rb0 + j) * LDW + c];
+      qnc[j] = (float)QN[(rb0 + j) * LDW + c];
+      Xd[j] = Yd[j] = Zd[j] = 0.f;
+    }
 #pragma unroll
-      for (int j = 0; j < 16; ++j) {
-        const float E = exp2f(-fabsf(lr[j] - li[j]));
-        Xd[j] += hr * ki[j] * E;
-        Yd[j] += mr * ki[j] * E;
-        Zd[j] += (hc * ki[j] + mcv * qi[j]) * E;
+    for (int rl = 0; rl < 16; ++rl) {
+      // row rb0 + rl of dH and dM, columns rb0 .. rb0 + 15 (the same for every thread of the block)
+      const f16x8 h0 = *reinterpret_cast<const f16x8*>(DH + (rb0 + rl) * LDN + rb0);
+      const f16x8 h1 = *reinterpret_cast<const f16x8*>(DH + (rb0 + rl) * LDN + rb0 + 8);
+      const f16x8 m0 = *reinterpret_cast<const f16x8*>(DMm + (rb0 + rl) * LDN + rb0);
+      const f16x8 m1 = *reinterpret_cast<const f16x8*>(DMm + (rb0 + rl) * LDN + rb0 + 8);
+#pragma unroll
+      for (int il = 0; il <= rl; ++il) {
+        const float hv = (float)(il < 8 ? h0[il & 7] : h1[il & 7]), mv = (float)(il < 8 ? m0[il & 7] : m1[il & 7]);
+        const float E = exp2f(fminf(lgc[rl] - lgc[il], 0.f));
+        const float ke = knc[il] * E;
+        Xd[rl] += hv * ke;
+        Yd[rl] += mv * ke;
+        Zd[il] += (hv * knc[rl] + mv * qnc[rl]) * E;
       }
     }
-  }
-  // exchange into the C layout: X + Z -> dkn, Yq -> dqn, X - Z -> dgk
 #pragma unroll
-  for (int pass = 0; pass < 3; ++pass) {
-    float o[16];
+    for (int pass = 0; pass < 3; ++pass) {
 #pragma unroll
-    for (int j = 0; j < 16; ++j) o[j] = pass == 0 ? Xd[j] + Zd[j] : (pass == 1 ? Yd[j] : Xd[j] - Zd[j]);
+      for (int j = 0; j < 16; ++j)
+        XB[(rb0 + j) * LGS + c] = pass == 0 ? Xd[j] + Zd[j] : (pass == 1 ? Yd[j] : Xd[j] - Zd[j]);
+      __syncthreads();
 #pragma unroll
-    for (int j = 0; j < 4; ++j)
-      reinterpret_cast<float4*>(XB + r8 * LGS + c0)[j] = make_float4(o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]);
-    __syncthreads();
+      for (int i = 0; i < 4; ++i)
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const float x = XB[(16 * i + 4 * lg + jj) * LGS + vc];
-        if (pass == 0) dkn[i][jj] += x;
-        else if (pass == 1) dqn[i][jj] += x;
-        else dgk[i][jj] += x;
-      }
-    __syncthreads();
+        for (int jj = 0; jj < 4; ++jj) {
+          const float x = XB[(16 * i + 4 * lg + jj) * LGS + vc];
+          if (pass == 0) dkn[i][jj] += x;
+          else if (pass == 1) dqn[i][jj] += x;
+          else dgk[i][jj] += x;
+        }
+      __syncthreads();
+    }
   }
   // ---- row dots qn . dqn, kn . dkn; dGamma; dg (reverse cumulative sum over the chunk's rows)
   float dgm[4][4];
+  uint4 graw[2];  // g_raw of row r8, channels c0 .. c0 + 15 (issued now, used last)
+  {
+    const size_t o = ((size_t)(tok0 + min(r8, len - 1)) * p.H + h) * HD + c0;
+    graw[0] = *reinterpret_cast<const uint4*>(p.g_raw + o);
+    graw[1] = *reinterpret_cast<const uint4*>(p.g_raw + o + 8);
+  }
   {
     const float dglc = red.dgl[vc] + R.el[vc] * red.sdl[vc];
 #pragma unroll
@@ -916,23 +929,11 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
       for (int jj = 0; jj < 4; ++jj) dgm[i][jj] = loc[jj] + after + tot_after;
       tot_after += tile;
     }
-    // dg_raw, and dA_log = sum dg . g
-    const float a = expf(p.A_log[h]);
-    float dal = 0.f;
+    // dg to the exchange matrix: dg_raw and dA_log follow in the row-and-channels mapping
 #pragma unroll
     for (int i = 0; i < 4; ++i)
 #pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int r = 16 * i + 4 * lg + jj;
-        if (r < len) {
-          const size_t o = ((size_t)(tok0 + r) * p.H + h) * HD + vc;
-          const float x = bf(p.g_raw[o]);
-          p.dg_raw[o] = dgm[i][jj] * (-a) * sigmoid_(x);
-          dal += dgm[i][jj] * (-a * softplus_(x));
-        }
-      }
-    dal = sum64(dal);
-    if (lane == 0) atomicAdd(&red.dal, dal);
+      for (int jj = 0; jj < 4; ++jj) XB[(16 * i + 4 * lg + jj) * LGS + vc] = dgm[i][jj];
   }
   __syncthreads();
   // dq, dk through the normalisation: (dxn - xn (xn . dxn)) / |x|
@@ -955,10 +956,35 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
         }
       }
     }
+  {  // dg_raw = dg (-exp(A_log)) sigmoid(g_raw), dA_log = sum dg g: thread -> row r8, channels c0 ..
+    float dg[16], x[16], o[16];
+    load_f32x16(XB + r8 * LGS + c0, dg);
+    unpack_bf16x8(graw[0], x);
+    unpack_bf16x8(graw[1], x + 8);
+    const float a = expf(p.A_log[h]);
+    float dal = 0.f;
+#pragma unroll
+    for (int j = 0; j < 16; ++j) {
+      // sigmoid and softplus from one exponential e = exp(-|x|) <= 1
+      const float ex = __expf(-fabsf(x[j])), inv = 1.f / (1.f + ex);
+      const float sg = x[j] >= 0.f ? inv : ex * inv, sp = fmaxf(x[j], 0.f) + __logf(1.f + ex);
+      o[j] = dg[j] * (-a) * sg;
+      dal += dg[j] * (-a * sp);  // dg = 0 past the chunk's end
+    }
+    if (r8 < len) {
+      f32x4* dst = reinterpret_cast<f32x4*>(p.dg_raw + ((size_t)(tok0 + r8) * p.H + h) * HD + c0);
+#pragma unroll
+      for (int j = 0; j < 4; ++j)
+        __builtin_nontemporal_store(f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]}, dst + j);
+    }
+    dal = sum64(dal);
+    if (lane == 0) atomicAdd(&red.dal, dal);
+  }
   if (t < len) {
     const float b = R.b[t];
     p.dbeta[(size_t)(tok0 + t) * p.H + h] = red.db[t] * b * (1.f - b);
   }
+  __syncthreads();
   if (t == 0) atomicAdd(p.dA_log + h, red.dal);
 }
 
