@@ -32,6 +32,10 @@ pytestmark = pytest.mark.gpu
 
 GRAD_REL = 5e-3
 GRAD_MAXABS = 2e-2  # of max |reference| of the same gradient
+# per (sequence, head): the same error measured on each chain's own slice, so that an error confined to one
+# chain is not diluted by the others; twice the pooled bar (short chains hold few values)
+GRAD_REL_CHAIN = 1e-2
+CHAIN_FLOOR = 1e-2  # of a typical slice's norm; see chain_worst
 NAMES = ("dq", "dk", "dv", "dg_raw", "dbeta_logits", "dA_log", "dinitial_state")
 
 
@@ -92,7 +96,34 @@ def dA_log_condition(ref, g_raw_bits):
     return np.abs(ref["dg_raw"] * sp / sig).sum(axis=(0, 1) if x.ndim == 3 else (0, 1, 3))
 
 
-def compare(got, ref, label, g_raw_bits):
+def chain_worst(got, ref, cu_seqlens=None):
+    """Worst per-(sequence, head) rel-L2 of every gradient with a token axis, and of dinitial_state per
+    (sequence, head).  Each slice's error is taken relative to max(its reference norm, CHAIN_FLOOR times a
+    typical slice's norm): under harsh decays a chain's dinitial_state is a product of many factors near zero
+    (down to 1e-30 and below in the fp64 oracle), and once its entries fall under fp16's normal range
+    (2^-14 ~ 6e-5, against typical entries of 1e-2..1e-1) the fp16 chain operands and stored state
+    gradients keep only a few significant bits; such a slice is held to an absolute error of CHAIN_FLOOR
+    times the typical slice instead of to a relative one."""
+    B, T = got["dv"].shape[:2]
+    spans = ([(b, 0, T) for b in range(B)] if cu_seqlens is None else
+             [(0, int(cu_seqlens[n]), int(cu_seqlens[n + 1])) for n in range(len(cu_seqlens) - 1)])
+    slices = {}
+    for n in ("dq", "dk", "dv", "dg_raw", "dbeta_logits"):
+        slices[n] = [(got[n][b, t0:t1, h], ref[n][b, t0:t1, h])
+                     for b, t0, t1 in spans if t1 > t0 for h in range(got[n].shape[2])]
+    x, r = got["dinitial_state"], ref["dinitial_state"]
+    slices["dinitial_state"] = [(x[c, h], r[c, h]) for c in range(x.shape[0]) for h in range(x.shape[1])]
+    worst = {}
+    for n, sl in slices.items():
+        norms = np.array([np.linalg.norm(rr) for _, rr in sl])
+        if len(sl) == 0 or not np.any(norms > 0):
+            continue
+        floor = CHAIN_FLOOR * np.sqrt(np.mean(norms ** 2))
+        worst[n] = max(float(np.linalg.norm(xx - rr) / max(nr, floor)) for (xx, rr), nr in zip(sl, norms))
+    return worst
+
+
+def compare(got, ref, label, g_raw_bits, cu_seqlens=None):
     errs = {}
     for n in NAMES:
         r, x = ref[n], got[n]
@@ -105,9 +136,13 @@ def compare(got, ref, label, g_raw_bits):
             rel = rel_l2(x, r)
             mx = float(np.max(np.abs(x - r)) / max(np.max(np.abs(r)), 1e-30))
         errs[n] = (rel, mx)
-    print(label, " ".join("%s %.1e/%.1e" % (n, *errs[n]) for n in NAMES), flush=True)
+    worst = chain_worst(got, ref, cu_seqlens)
+    print(label, " ".join("%s %.1e/%.1e" % (n, *errs[n]) for n in NAMES), "| worst chain",
+          " ".join("%s %.1e" % kv for kv in worst.items()), flush=True)
     for n, (rel, mx) in errs.items():
         assert rel <= GRAD_REL and mx <= GRAD_MAXABS, (label, n, rel, mx)
+    for n, e in worst.items():
+        assert e <= GRAD_REL_CHAIN, (label, n, "per chain", e)
 
 
 CASES = [
@@ -130,7 +165,7 @@ def test_backward_matches_the_oracle(label, kw, dstd):
     dout, dfinal = upstream(inp, kw["seed"] + 500, dstd)
     got = run_gpu_bwd(inp, dout, dfinal)
     ref = run_oracle_bwd(inp, dout, dfinal)
-    compare(got, ref, label, inp["g_raw"])
+    compare(got, ref, label, inp["g_raw"], inp.get("cu_seqlens"))
 
 
 def test_backward_grouped_heads_long_sequence():
@@ -209,4 +244,5 @@ def test_backward_random_configuration(i):
     inp, dstd, what = draw_bwd_case(i)
     print(what, flush=True)
     dout, dfinal = upstream(inp, 3900 + i, dstd)
-    compare(run_gpu_bwd(inp, dout, dfinal), run_oracle_bwd(inp, dout, dfinal), what, inp["g_raw"])
+    compare(run_gpu_bwd(inp, dout, dfinal), run_oracle_bwd(inp, dout, dfinal), what, inp["g_raw"],
+            inp.get("cu_seqlens"))

@@ -40,7 +40,7 @@ def test_kda_backward_matches_the_oracle(label, kw, dstd):
     dout, dfinal = upstream(inp, kw["seed"] + 500, dstd)
     got = run_gpu_bwd(inp, dout, dfinal)
     ref = run_oracle_bwd(inp, dout, dfinal)
-    compare(got, ref, label, inp["g_raw"])
+    compare(got, ref, label, inp["g_raw"], inp.get("cu_seqlens"))
 
 
 def test_kda_backward_grouped_heads_long_sequence():
@@ -107,4 +107,5 @@ def test_kda_backward_random_configuration(i):
     inp, dstd, what = draw_kda_bwd_case(i)
     print(what, flush=True)
     dout, dfinal = upstream(inp, 7100 + i, dstd)
-    compare(run_gpu_bwd(inp, dout, dfinal), run_oracle_bwd(inp, dout, dfinal), what, inp["g_raw"])
+    compare(run_gpu_bwd(inp, dout, dfinal), run_oracle_bwd(inp, dout, dfinal), what, inp["g_raw"],
+            inp.get("cu_seqlens"))

@@ -64,3 +64,26 @@ def test_zero_output_fails():
     ref_out, ref_fin = U.run_oracle(inp)
     with pytest.raises(AssertionError):
         U.assert_parity(np.zeros_like(ref_out), ref_fin, ref_out, ref_fin, what="zero output")
+
+
+def test_backward_bars_catch_an_error_confined_to_one_chain():
+    # gradients of 8 rows x 4 heads with rounding-sized noise pass; the same with a 2% error in one
+    # (row, head) of dv passes the pooled bar but fails the per-chain one
+    from test_gpu_backward import compare
+    rng = np.random.default_rng(7)
+    B, T, H, D = 8, 40, 4, 128
+    ref = {"dq": rng.standard_normal((B, T, H, D)), "dk": rng.standard_normal((B, T, H, D)),
+           "dv": rng.standard_normal((B, T, H, D)), "dg_raw": rng.standard_normal((B, T, H)),
+           "dbeta_logits": rng.standard_normal((B, T, H)), "dA_log": rng.standard_normal(H),
+           "dinitial_state": rng.standard_normal((B, H, D, D))}
+    g_raw = np.zeros((B, T, H), dtype=np.uint16)  # bf16 zeros: only dA_log's condition reads it
+    got = {n: v * (1.0 + rng.uniform(-2.0 ** -11, 2.0 ** -11, np.shape(v))) for n, v in ref.items()}
+    ref["dA_log"] = got["dA_log"].copy()
+    compare(got, ref, "noise only", g_raw)
+    bad = dict(got)
+    bad["dv"] = got["dv"].copy()
+    bad["dv"][3, :, 2] *= 1.02
+    pooled = np.linalg.norm(bad["dv"] - ref["dv"]) / np.linalg.norm(ref["dv"])
+    assert pooled < 5e-3
+    with pytest.raises(AssertionError, match="per chain"):
+        compare(bad, ref, "one chain off by 2%", g_raw)
