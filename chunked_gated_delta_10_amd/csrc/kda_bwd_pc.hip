@@ -145,12 +145,10 @@ __device__ void load_pc(const BwdParams& p, int tok0, int len, int h, int hq, f1
 }
 
 // Operand fragment (8 contraction indices k = k0 + 8 (lane / 16) + e over key
-// channels, row r) of exp2(LG[r][k] - LG[p][k]) X[r][k] (sign = +1) or of
-// exp2(LG[p][k] - LG[r][k]) X[r][k] (sign = -1); the exponent is clamped at 0
-// and the fragment is zero unless the row is on the side of p the sign names
-// (live = false).
-__device__ __forceinline__ f16x8 frag_decay_rm(const f16* X, const float* LG, int r, int p, int k0, float sign,
-                                               bool live) {
+// channels, row r) of exp2(LG[r][k] - LG[p][k]) X[r][k] (sign = +1: r after p)
+// or of exp2(LG[p][k] - LG[r][k]) X[r][k] (sign = -1: r at or before p); the
+// exponent is <= 0 on those sides and clamped at 0 against rounding.
+__device__ __forceinline__ f16x8 frag_decay_rm(const f16* X, const float* LG, int r, int p, int k0, float sign) {
   const f16x8 x = *reinterpret_cast<const f16x8*>(X + r * LDW + k0);
   const float4 a0 = *reinterpret_cast<const float4*>(LG + r * LGS + k0);
   const float4 a1 = *reinterpret_cast<const float4*>(LG + r * LGS + k0 + 4);
@@ -158,10 +156,9 @@ __device__ __forceinline__ f16x8 frag_decay_rm(const f16* X, const float* LG, in
   const float4 b1 = *reinterpret_cast<const float4*>(LG + p * LGS + k0 + 4);
   const float la[8] = {a0.x, a0.y, a0.z, a0.w, a1.x, a1.y, a1.z, a1.w};
   const float lb[8] = {b0.x, b0.y, b0.z, b0.w, b1.x, b1.y, b1.z, b1.w};
-  const float m = live ? 1.f : 0.f;
   f16x8 o;
 #pragma unroll
-  for (int e = 0; e < 8; ++e) o[e] = (f16)(m * exp2f(fminf(sign * (la[e] - lb[e]), 0.f)) * (float)x[e]);
+  for (int e = 0; e < 8; ++e) o[e] = (f16)(exp2f(fminf(sign * (la[e] - lb[e]), 0.f)) * (float)x[e]);
   return o;
 }
 // The same along a column: contraction index k = row of X (k0 + 8 (lane / 16) + e), key channel c;
@@ -193,7 +190,7 @@ constexpr int C_QN = 0, C_KN = C_QN + MAT_W, C_LG = C_KN + MAT_W, C_M = C_LG + M
 constexpr int C_TF = C_QN;  // T in fp32 over qn, kn (dead once the operands are formed)
 constexpr int C_YZ = C_LG;  // Y1^T, then Z1^T, over the gates (dead after the Gram products)
 static_assert(MAT_F <= 2 * MAT_W && MAT_NT <= MAT_G, "aliases fit");
-static_assert(2 * HD * 4 * 4 <= MAT_F, "scan scratch fits in A's space");
+static_assert(4 * HD * 4 <= MAT_F, "scan scratch (4 x 128 floats) fits in A's space");
 }  // namespace
 
 __global__ __launch_bounds__(NTH) void bwd_coef_pc_kernel(BwdParams p) {
@@ -257,9 +254,9 @@ __global__ __launch_bounds__(NTH) void bwd_coef_pc_kernel(BwdParams p) {
 #pragma unroll
     for (int s = 0; s < HD / 32; ++s) {
       const int k0 = 32 * s + 8 * lg;
-      const f16x8 bk = frag_decay_rm(KN, LG, 16 * ct + l16, pr, k0, -1.f, true);
-      HQ = mma_f16(frag_decay_rm(QN, LG, 16 * rt + l16, pr, k0, 1.f, true), bk, HQ);
-      HK = mma_f16(frag_decay_rm(KN, LG, 16 * rt + l16, pr, k0, 1.f, true), bk, HK);
+      const f16x8 bk = frag_decay_rm(KN, LG, 16 * ct + l16, pr, k0, -1.f);
+      HQ = mma_f16(frag_decay_rm(QN, LG, 16 * rt + l16, pr, k0, 1.f), bk, HQ);
+      HK = mma_f16(frag_decay_rm(KN, LG, 16 * rt + l16, pr, k0, 1.f), bk, HK);
     }
     const int i = 16 * ct + l16;
 #pragma unroll
