@@ -190,6 +190,22 @@ def test_backward_many_jobs_sampled_heads():
     compare(sub, ref, "T=8192 H=32, heads 0 and 31", inp["g_raw"][:, :, heads])
 
 
+def test_backward_benchmark_shape_sampled_heads():
+    # the scalar-gate backward benchmark configuration (8 packed sequences x 4096 tokens, 32 heads, one
+    # bwd_varlen call; 16,640 (chunk, head) jobs, chains on 128-column tiles); heads 0 and 31 against the
+    # oracle
+    from chunked_gated_delta_10_amd.inputs import WORKLOADS, workload_inputs
+    w = WORKLOADS["gdn_bwd"]
+    inp = workload_inputs("gdn_bwd")
+    dout, dfinal = upstream(inp, w.seed + 500)
+    got = run_gpu_bwd(inp, dout, dfinal)
+    heads = [0, 31]
+    ref = run_oracle_bwd(inp, dout, dfinal, heads=heads)
+    sub = {n: (got[n][heads] if n == "dA_log" else got[n][:, heads] if n == "dinitial_state"
+               else got[n][:, :, heads]) for n in NAMES}
+    compare(sub, ref, "gdn_bwd shape 8 x 4096 H=32, heads 0 and 31", inp["g_raw"][:, :, heads], inp["cu_seqlens"])
+
+
 def test_backward_zero_tokens():
     # T = 0: no token gradients; dinitial_state = dfinal, dA_log = 0
     H = 2
