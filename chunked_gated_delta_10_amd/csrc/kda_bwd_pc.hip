@@ -181,31 +181,37 @@ __device__ __forceinline__ f16x8 frag_decay_cm(const f16* X, const float* LG, in
 // ---------------------------------------------------------------------------
 // coef_pc_kernel: per (chunk, head), the masked Gram matrices M and H, T, and
 // the records of both chains (Phi, Bc, Phi^T, Gc as fp16 A-operand fragments
-// in the chain's contraction order, T, M, H).  One workgroup per CU.
+// in the chain's contraction order, T, M, H).  Two workgroups per CU (72 KB of
+// LDS): qn, kn and the gates live only through the Gram products; A and T in
+// fp32 for the solve, then M and T (fp16), take their space; Khat and Kbar are
+// formed after the solve from registers, over the solve's space; Qhat waits in
+// Bc's record slot until the last product reads it.
 // ---------------------------------------------------------------------------
 namespace {
-constexpr int C_QN = 0, C_KN = C_QN + MAT_W, C_LG = C_KN + MAT_W, C_M = C_LG + MAT_G, C_T = C_M + MAT_N,
-              C_AF = C_T + MAT_N, C_QH = C_AF + MAT_F, C_KH = C_QH + MAT_W, C_KB = C_KH + MAT_W,
-              C_END = C_KB + MAT_W;
-constexpr int C_TF = C_QN;  // T in fp32 over qn, kn (dead once the operands are formed)
-constexpr int C_YZ = C_LG;  // Y1^T, then Z1^T, over the gates (dead after the Gram products)
-static_assert(MAT_F <= 2 * MAT_W && MAT_NT <= MAT_G, "aliases fit");
-static_assert(4 * HD * 4 <= MAT_F, "scan scratch (4 x 128 floats) fits in A's space");
+// Gram products: qn, kn, the gates; the prologue's scan scratch after them
+constexpr int C_QN = 0, C_KN = C_QN + MAT_W, C_LG = C_KN + MAT_W, C_PART = C_LG + MAT_G;
+// solve: A and T in fp32, M and T in fp16
+constexpr int C_AF = 0, C_TF = C_AF + MAT_F, C_M = C_TF + MAT_F, C_T = C_M + MAT_N;
+// operators: Khat, Kbar over A and T (fp32); M, T kept; Y1^T, then Z1^T, after them
+constexpr int C_KH = 0, C_KB = C_KH + MAT_W, C_YZ = C_T + MAT_N, C_END = C_YZ + MAT_NT;
+static_assert(C_PART + 4 * HD * 4 <= C_END, "scan scratch (4 x 128 floats) inside the layout");
+static_assert(C_KB + MAT_W <= C_M, "Khat, Kbar over the fp32 solve");
+static_assert(2 * (C_END + (int)sizeof(PcRows)) <= 160 * 1024, "two workgroups per CU");
 }  // namespace
 
-__global__ __launch_bounds__(NTH) void bwd_coef_pc_kernel(BwdParams p) {
+// two workgroups per CU: at least four waves per SIMD
+__global__ __launch_bounds__(NTH, 4) void bwd_coef_pc_kernel(BwdParams p) {
   __shared__ __attribute__((aligned(16))) uint8_t smem[C_END];
   __shared__ PcRows R;
   f16* QN = reinterpret_cast<f16*>(smem + C_QN);
   f16* KN = reinterpret_cast<f16*>(smem + C_KN);
   float* LG = reinterpret_cast<float*>(smem + C_LG);
+  float* AF = reinterpret_cast<float*>(smem + C_AF);
+  float* TF = reinterpret_cast<float*>(smem + C_TF);
   f16* M16 = reinterpret_cast<f16*>(smem + C_M);
   f16* T16 = reinterpret_cast<f16*>(smem + C_T);
-  float* AF = reinterpret_cast<float*>(smem + C_AF);
-  f16* QH = reinterpret_cast<f16*>(smem + C_QH);
   f16* KH = reinterpret_cast<f16*>(smem + C_KH);
   f16* KB = reinterpret_cast<f16*>(smem + C_KB);
-  float* TF = reinterpret_cast<float*>(smem + C_TF);
   f16* YZt = reinterpret_cast<f16*>(smem + C_YZ);
 
   const int job = blockIdx.x, e = job / p.H, h = job - e * p.H, hq = h / (p.H / p.H_qk);
@@ -215,13 +221,14 @@ __global__ __launch_bounds__(NTH) void bwd_coef_pc_kernel(BwdParams p) {
   const int t = threadIdx.x, w = t >> 6, lane = t & 63, l16 = lane & 15, lg = lane >> 4;
   uint8_t* rec = p.brec + (size_t)job * p.rec_bytes;
   f16* HKg = reinterpret_cast<f16*>(rec + BR_HK);
+  f16* QHg = reinterpret_cast<f16*>(rec + BR_BC);  // Qhat rows until Bc replaces them
 
   uint4 qraw[2];
-  float kv[16];
-  load_pc(p, tok0, len, h, hq, KN, LG, AF, R, qraw, kv);
+  float kv[16], lr[16];
+  load_pc(p, tok0, len, h, hq, KN, LG, reinterpret_cast<float*>(smem + C_PART), R, qraw, kv);
   const int r = t >> 3, c0 = (t & 7) * 16;
-  float qv[16], lr[16];
-  {
+  float qv[16];
+  {  // qn rows to LDS, Qhat rows to the record
     unpack_bf16x8(qraw[0], qv);
     unpack_bf16x8(qraw[1], qv + 8);
     const float iq = r < len ? 1.f / R.nq[r] : 0.f;
@@ -229,65 +236,25 @@ __global__ __launch_bounds__(NTH) void bwd_coef_pc_kernel(BwdParams p) {
     for (int j = 0; j < 16; ++j) qv[j] *= iq;
     *reinterpret_cast<f16x8*>(QN + r * LDW + c0) = to_f16x8(qv);
     *reinterpret_cast<f16x8*>(QN + r * LDW + c0 + 8) = to_f16x8(qv + 8);
-    // Qhat, Khat, Kbar rows
     load_f32x16(LG + r * LGS + c0, lr);
-    float qh[16], kh[16], kb[16];
+    float qh[16];
 #pragma unroll
-    for (int j = 0; j < 16; ++j) {
-      const float ee = exp2f(lr[j]), ff = exp2f(R.lgl[c0 + j] - lr[j]);
-      qh[j] = ee * qv[j];
-      kh[j] = ee * kv[j];
-      kb[j] = ff * kv[j];
-    }
-    *reinterpret_cast<f16x8*>(QH + r * LDW + c0) = to_f16x8(qh);
-    *reinterpret_cast<f16x8*>(QH + r * LDW + c0 + 8) = to_f16x8(qh + 8);
-    *reinterpret_cast<f16x8*>(KH + r * LDW + c0) = to_f16x8(kh);
-    *reinterpret_cast<f16x8*>(KH + r * LDW + c0 + 8) = to_f16x8(kh + 8);
-    *reinterpret_cast<f16x8*>(KB + r * LDW + c0) = to_f16x8(kb);
-    *reinterpret_cast<f16x8*>(KB + r * LDW + c0 + 8) = to_f16x8(kb + 8);
+    for (int j = 0; j < 16; ++j) qh[j] = exp2f(lr[j]) * qv[j];
+    *reinterpret_cast<f16x8*>(QHg + r * HD + c0) = to_f16x8(qh);
+    *reinterpret_cast<f16x8*>(QHg + r * HD + c0 + 8) = to_f16x8(qh + 8);
   }
-  __syncthreads();  // QN complete (the scan scratch in A's space is dead)
-  // ---- off-diagonal 16 x 16 blocks (waves 0..5) and zero blocks above the diagonal (waves 6, 7)
-  if (w < 6) {
-    const int rt = w < 1 ? 1 : (w < 3 ? 2 : 3), ct = w < 1 ? 0 : (w < 3 ? w - 1 : w - 3), pr = 16 * rt - 1;
-    f32x4 HQ = zero4(), HK = zero4();
+  __syncthreads();  // qn complete
+  // ---- diagonal blocks, exactly: thread (r, 16 channels), partners i of r's block in two groups of 8;
+  // the sums over the 8 lanes of the row (channel groups) halve the partners at every step, so lane
+  // cg = t % 8 ends with the full sums of partner 8 g + cg of group g
+  const int b0 = r & ~15, cg = t & 7;
+  float q1[2], k1[2];
 #pragma unroll
-    for (int s = 0; s < HD / 32; ++s) {
-      const int k0 = 32 * s + 8 * lg;
-      const f16x8 bk = frag_decay_rm(KN, LG, 16 * ct + l16, pr, k0, -1.f);
-      HQ = mma_f16(frag_decay_rm(QN, LG, 16 * rt + l16, pr, k0, 1.f), bk, HQ);
-      HK = mma_f16(frag_decay_rm(KN, LG, 16 * rt + l16, pr, k0, 1.f), bk, HK);
-    }
-    const int i = 16 * ct + l16;
+  for (int g = 0; g < 2; ++g) {
+    float hq[8], hk[8];
 #pragma unroll
-    for (int jj = 0; jj < 4; ++jj) {
-      const int rr = 16 * rt + 4 * lg + jj;
-      M16[rr * LDN + i] = (f16)HQ[jj];
-      AF[rr * LDF + i] = R.b[rr] * HK[jj];
-      HKg[rr * CH + i] = (f16)HK[jj];
-    }
-  } else {
-#pragma unroll
-    for (int q2 = 0; q2 < 3; ++q2) {
-      const int blk = 3 * (w - 6) + q2;  // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
-      const int rt = blk < 3 ? 0 : (blk < 5 ? 1 : 2), ct = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
-      const int i = 16 * ct + l16;
-#pragma unroll
-      for (int jj = 0; jj < 4; ++jj) {
-        const int rr = 16 * rt + 4 * lg + jj;
-        M16[rr * LDN + i] = (f16)0.f;
-        AF[rr * LDF + i] = 0.f;
-        HKg[rr * CH + i] = (f16)0.f;
-      }
-    }
-  }
-  // ---- diagonal blocks, exactly: thread (r, 16 channels), partners i of r's block
-  {
-    const int b0 = r & ~15;
-    float hq[16], hk[16];
-#pragma unroll
-    for (int jl = 0; jl < 16; ++jl) {
-      const int i = b0 + jl;
+    for (int jl = 0; jl < 8; ++jl) {
+      const int i = b0 + 8 * g + jl;
       float li[16], ki[16];
       load_f32x16(LG + i * LGS + c0, li);
       load_f16x16(KN + i * LDW + c0, ki);
@@ -301,42 +268,92 @@ __global__ __launch_bounds__(NTH) void bwd_coef_pc_kernel(BwdParams p) {
       hq[jl] = sq;
       hk[jl] = sk;
     }
-    // sums over the 8 lanes of the row (channel groups), halving the partners at every step: lane
-    // cg = t % 8 ends with the full sums of partners 2 cg and 2 cg + 1
-    const int cg = t & 7;
-    float q8[8], k8[8], q4[4], k4[4], q2[2], k2[2];
-#pragma unroll
-    for (int j = 0; j < 8; ++j) {
-      const bool hi = cg & 4;
-      q8[j] = (hi ? hq[8 + j] : hq[j]) + __shfl_xor(hi ? hq[j] : hq[8 + j], 4);
-      k8[j] = (hi ? hk[8 + j] : hk[j]) + __shfl_xor(hi ? hk[j] : hk[8 + j], 4);
-    }
+    float q4[4], k4[4], q2[2], k2[2];
 #pragma unroll
     for (int j = 0; j < 4; ++j) {
-      const bool hi = cg & 2;
-      q4[j] = (hi ? q8[4 + j] : q8[j]) + __shfl_xor(hi ? q8[j] : q8[4 + j], 2);
-      k4[j] = (hi ? k8[4 + j] : k8[j]) + __shfl_xor(hi ? k8[j] : k8[4 + j], 2);
+      const bool hi = cg & 4;
+      q4[j] = (hi ? hq[4 + j] : hq[j]) + __shfl_xor(hi ? hq[j] : hq[4 + j], 4);
+      k4[j] = (hi ? hk[4 + j] : hk[j]) + __shfl_xor(hi ? hk[j] : hk[4 + j], 4);
     }
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
-      const bool hi = cg & 1;
-      q2[j] = (hi ? q4[2 + j] : q4[j]) + __shfl_xor(hi ? q4[j] : q4[2 + j], 1);
-      k2[j] = (hi ? k4[2 + j] : k4[j]) + __shfl_xor(hi ? k4[j] : k4[2 + j], 1);
+      const bool hi = cg & 2;
+      q2[j] = (hi ? q4[2 + j] : q4[j]) + __shfl_xor(hi ? q4[j] : q4[2 + j], 2);
+      k2[j] = (hi ? k4[2 + j] : k4[j]) + __shfl_xor(hi ? k4[j] : k4[2 + j], 2);
     }
+    const bool hi = cg & 1;
+    q1[g] = (hi ? q2[1] : q2[0]) + __shfl_xor(hi ? q2[0] : q2[1], 1);
+    k1[g] = (hi ? k2[1] : k2[0]) + __shfl_xor(hi ? k2[0] : k2[1], 1);
+  }
+  f16x8 khb[4];  // this row's Khat, Kbar entries (fp16), kept until the solve's space is free
+  {
+    float kh[16], kb[16];
 #pragma unroll
-    for (int u = 0; u < 2; ++u) {
-      const int jl = 2 * cg + u, i = b0 + jl;
-      const float vq = q2[u], vk = k2[u];
-      M16[r * LDN + i] = (f16)(i <= r ? vq : 0.f);
-      AF[r * LDF + i] = i < r ? R.b[r] * vk : 0.f;
-      HKg[r * CH + i] = (f16)(i < r ? vk : 0.f);
+    for (int j = 0; j < 16; ++j) {
+      kh[j] = exp2f(lr[j]) * kv[j];
+      kb[j] = exp2f(R.lgl[c0 + j] - lr[j]) * kv[j];
     }
+    khb[0] = to_f16x8(kh);
+    khb[1] = to_f16x8(kh + 8);
+    khb[2] = to_f16x8(kb);
+    khb[3] = to_f16x8(kb + 8);
+  }
+  // ---- off-diagonal 16 x 16 blocks (waves 0..5; in registers until the gates are dead)
+  f32x4 HQ = zero4(), HK = zero4();
+  const int rt = w < 1 ? 1 : (w < 3 ? 2 : 3), ct = w < 1 ? 0 : (w < 3 ? w - 1 : w - 3);
+  if (w < 6) {
+    const int pr = 16 * rt - 1;
+#pragma unroll
+    for (int s = 0; s < HD / 32; ++s) {
+      const int k0 = 32 * s + 8 * lg;
+      const f16x8 bk = frag_decay_rm(KN, LG, 16 * ct + l16, pr, k0, -1.f);
+      HQ = mma_f16(frag_decay_rm(QN, LG, 16 * rt + l16, pr, k0, 1.f), bk, HQ);
+      HK = mma_f16(frag_decay_rm(KN, LG, 16 * rt + l16, pr, k0, 1.f), bk, HK);
+    }
+  }
+  __syncthreads();  // qn, kn and the gates read for the last time: A and M take their space
+  if (w < 6) {
+    const int i = 16 * ct + l16;
+#pragma unroll
+    for (int jj = 0; jj < 4; ++jj) {
+      const int rr = 16 * rt + 4 * lg + jj;
+      M16[rr * LDN + i] = (f16)HQ[jj];
+      AF[rr * LDF + i] = R.b[rr] * HK[jj];
+      HKg[rr * CH + i] = (f16)HK[jj];
+    }
+  } else {  // zero blocks above the diagonal
+#pragma unroll
+    for (int q3 = 0; q3 < 3; ++q3) {
+      const int blk = 3 * (w - 6) + q3;  // (0,1) (0,2) (0,3) (1,2) (1,3) (2,3)
+      const int zr = blk < 3 ? 0 : (blk < 5 ? 1 : 2), zc = blk < 3 ? blk + 1 : (blk < 5 ? blk - 1 : 3);
+      const int i = 16 * zc + l16;
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        const int rr = 16 * zr + 4 * lg + jj;
+        M16[rr * LDN + i] = (f16)0.f;
+        AF[rr * LDF + i] = 0.f;
+        HKg[rr * CH + i] = (f16)0.f;
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 2; ++g) {  // the diagonal blocks' entries of this lane
+    const int i = b0 + 8 * g + cg;
+    M16[r * LDN + i] = (f16)(i <= r ? q1[g] : 0.f);
+    AF[r * LDF + i] = i < r ? R.b[r] * k1[g] : 0.f;
+    HKg[r * CH + i] = (f16)(i < r ? k1[g] : 0.f);
   }
   __syncthreads();  // A, M complete
   solve_T(AF, TF, T16);
   // T and M (fp16 rows) for the gradient kernel: thread -> row t / 8, columns 8 (t % 8) ..
   *reinterpret_cast<f16x8*>(rec + BR_T + t * 16) = *reinterpret_cast<const f16x8*>(T16 + (t >> 3) * LDN + 8 * (t & 7));
   *reinterpret_cast<f16x8*>(rec + BR_M + t * 16) = *reinterpret_cast<const f16x8*>(M16 + (t >> 3) * LDN + 8 * (t & 7));
+  // Khat, Kbar rows over the solve's fp32 space (dead: solve_T ended with a barrier)
+  *reinterpret_cast<f16x8*>(KH + r * LDW + c0) = khb[0];
+  *reinterpret_cast<f16x8*>(KH + r * LDW + c0 + 8) = khb[1];
+  *reinterpret_cast<f16x8*>(KB + r * LDW + c0) = khb[2];
+  *reinterpret_cast<f16x8*>(KB + r * LDW + c0 + 8) = khb[3];
+  __syncthreads();  // Khat, Kbar complete
 
   const int d = 16 * w + l16;  // this lane's key column of the 128-wide results
   // Y1 = T^T Kbar: rows i (4 tiles), columns d (tile w); K = 64
@@ -416,6 +433,15 @@ __global__ __launch_bounds__(NTH) void bwd_coef_pc_kernel(BwdParams p) {
       }
     }
   }
+  // this lane's Qhat entries (rows i = 32 s + 16 hh + 4 lg + jj, column d), read back now and
+  // used after the next product
+  f16 qh[2][2][4];
+#pragma unroll
+  for (int s = 0; s < 2; ++s)
+#pragma unroll
+    for (int hh = 0; hh < 2; ++hh)
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) qh[s][hh][jj] = QHg[(32 * s + 16 * hh + 4 * lg + jj) * HD + d];
   __syncthreads();  // Y1^T read for the last time
   // Z1 = T diag(b) Khat
   {
@@ -433,7 +459,7 @@ __global__ __launch_bounds__(NTH) void bwd_coef_pc_kernel(BwdParams p) {
       *reinterpret_cast<f16x4*>(YZt + d * LDN + 16 * i + 4 * lg) =
           f16x4{(f16)Z1[i][0], (f16)Z1[i][1], (f16)Z1[i][2], (f16)Z1[i][3]};
   }
-  __syncthreads();
+  __syncthreads();  // Z1 complete; every lane's Qhat entries are in registers: Bc may replace them
   // Bc^T = Qhat - M Z1: rows i (4 tiles), columns d (tile w); K = 64
   {
     f32x4 B[4];
@@ -451,10 +477,7 @@ __global__ __launch_bounds__(NTH) void bwd_coef_pc_kernel(BwdParams p) {
 #pragma unroll
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
-        for (int jj = 0; jj < 4; ++jj) {
-          const int i = 32 * s + 16 * hh + 4 * lg + jj;
-          o[4 * hh + jj] = (f16)((float)QH[i * LDW + d] - B[2 * s + hh][jj]);
-        }
+        for (int jj = 0; jj < 4; ++jj) o[4 * hh + jj] = (f16)((float)qh[s][hh][jj] - B[2 * s + hh][jj]);
       *reinterpret_cast<f16x8*>(rec + BR_BC + (w * 2 + s) * FRAG_BYTES + lane * 16) = o;
     }
   }
