@@ -71,7 +71,9 @@ def backward_bytes(w):
 # Algorithmic FLOP per token-head of the backward: the recomputed forward (FLOP_PER_TOKEN_HEAD) plus the
 # chunk form's products per 64-token chunk: seven C x D x D (kn dS', dO' S^T, dV S^T, U dS'^T, kn S, and
 # the adjoint's qn^T dO', kn^T Z), ten C x C x D (M^T dO', T^T dU, U, dO' U^T, dU (bR)^T, dP kn, dGm kn,
-# dP^T qn, qn kn^T, kn kn^T) and two C x C x C (dA = -T^T dT T^T): 548,864 in all.
+# dP^T qn, qn kn^T, kn kn^T) and two C x C x C (dA = -T^T dT T^T): 548,864 in all.  The per-channel gate's
+# backward is counted the same way (its masked Gram products replace the scalar gate's Gram products one for
+# one; the per-block decay factors are elementwise work, not counted).
 BWD_FLOP_PER_TOKEN_HEAD = FLOP_PER_TOKEN_HEAD + 2 * (7 * C * D * D + 10 * C * C * D + 2 * C ** 3) // C
 
 

@@ -109,3 +109,19 @@ def test_kda_backward_random_configuration(i):
     dout, dfinal = upstream(inp, 7100 + i, dstd)
     compare(run_gpu_bwd(inp, dout, dfinal), run_oracle_bwd(inp, dout, dfinal), what, inp["g_raw"],
             inp.get("cu_seqlens"))
+
+
+def test_kda_backward_zero_tokens():
+    # T = 0 with the per-channel gate: no token gradients; dinitial_state = dfinal, dA_log = 0
+    import torch
+    from chunked_gated_delta_10_amd import kda
+    H = 2
+    z = lambda *s: torch.zeros(s, dtype=torch.bfloat16, device="cuda")
+    df = torch.randn(3, H, 128, 128, device="cuda")
+    g = kda.bwd_varlen(z(1, 0, H, 128), z(1, 0, H, 128), z(1, 0, H, 128), z(1, 0, H, 128),
+                       torch.zeros(1, 0, H, device="cuda"), torch.zeros(H, device="cuda"), z(1, 0, H, 128),
+                       torch.zeros(4, dtype=torch.int32, device="cuda"), dfinal=df)
+    torch.cuda.synchronize()
+    assert g["dg_raw"].shape == (1, 0, H, 128)
+    assert torch.equal(g["dinitial_state"], df)
+    assert torch.count_nonzero(g["dA_log"]) == 0
