@@ -804,7 +804,9 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
         const float dm = r >= c ? DM[j][jj] : 0.f;
         const float da = r > c ? -DA[j][jj] : 0.f;
         const float dp = dm * lam, dgm = R.b[r] * da * lam;
-        const float wv = (R.b[r] * da * Gm[j][jj] + dm * P[j][jj]) * lam;
+        // W's diagonal (dM_rr P_rr) enters its row sum and its column sum alike and cancels in dG exactly;
+        // left out, its rounding cannot swamp dG when harsh decays make dG small
+        const float wv = r != c ? (R.b[r] * da * Gm[j][jj] + dm * P[j][jj]) * lam : 0.f;
         DP[r * LDN + c] = (f16)dp;
         DG[r * LDN + c] = (f16)dgm;
         pc[jj] = (f16)dp;

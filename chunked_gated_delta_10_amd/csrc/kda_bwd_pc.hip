@@ -861,9 +861,12 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
     }
   }
   // ---- the diagonal blocks, exactly: thread -> block bb = t / 128, key channel c = t % 128, every pair
-  // i <= r of the block once (E = exp2(LG[r][c] - LG[i][c]) <= 1), row sums X, Yq for r and column
+  // i < r of the block once (E = exp2(LG[r][c] - LG[i][c]) <= 1), row sums X, Yq for r and column
   // sums Z for i in registers; then through one fp32 exchange matrix into the C layout:
-  // X + Z -> dkn, Yq -> dqn, X - Z -> dgk
+  // X + Z -> dkn, Yq -> dqn, X - Z -> dgk.  The pairs i = r (dH's diagonal is zero, E = 1) add
+  // dM_rr kn_r to dqn_r and dM_rr qn_r to dkn_r, and nothing to dGamma: in dGamma's qn . Yq - kn . Z
+  // they cancel exactly, so they are added to dqn, dkn only after dGamma is formed (under harsh decays
+  // their rounding would otherwise swamp dGamma's small true value)
   {
     const int bb = t >> 7, c = t & (HD - 1), rb0 = 16 * bb;
     float lgc[16], knc[16], qnc[16], Xd[16], Yd[16], Zd[16];
@@ -882,7 +885,7 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
       const f16x8 m0 = *reinterpret_cast<const f16x8*>(DMm + (rb0 + rl) * LDN + rb0);
       const f16x8 m1 = *reinterpret_cast<const f16x8*>(DMm + (rb0 + rl) * LDN + rb0 + 8);
 #pragma unroll
-      for (int il = 0; il <= rl; ++il) {
+      for (int il = 0; il < rl; ++il) {
         const float hv = (float)(il < 8 ? h0[il & 7] : h1[il & 7]), mv = (float)(il < 8 ? m0[il & 7] : m1[il & 7]);
         const float E = exp2f(fminf(lgc[rl] - lgc[il], 0.f));
         const float ke = knc[il] * E;
@@ -925,12 +928,15 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
       for (int jj = 0; jj < 4; ++jj) {
         const int r = 16 * i + 4 * lg + jj;
         const float qx = (float)QN[r * LDW + vc], kx = (float)KN[r * LDW + vc];
+        dgm[i][jj] = r < len ? qx * dqn[i][jj] + kx * dgk[i][jj] + (r == len - 1 ? dglc : 0.f) : 0.f;
+        const float dmrr = (float)DMm[r * LDN + r];  // the pair i = r
+        dqn[i][jj] += dmrr * kx;
+        dkn[i][jj] += dmrr * qx;
         const float qd = rowsum16(qx * dqn[i][jj]), kd = rowsum16(kx * dkn[i][jj]);
         if (l16 == 0) {
           atomicAdd(&red.qd[r], qd);
           atomicAdd(&red.kd[r], kd);
         }
-        dgm[i][jj] = r < len ? qx * dqn[i][jj] + kx * dgk[i][jj] + (r == len - 1 ? dglc : 0.f) : 0.f;
       }
     // reverse inclusive sum over rows 16 i + 4 lg + jj of column vc (lanes lg = 0..3 share the column)
     float tot_after = 0.f;

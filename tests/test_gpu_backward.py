@@ -206,6 +206,23 @@ def test_backward_benchmark_shape_sampled_heads():
     compare(sub, ref, "gdn_bwd shape 8 x 4096 H=32, heads 0 and 31", inp["g_raw"][:, :, heads], inp["cu_seqlens"])
 
 
+def test_backward_extreme_decay():
+    # per-token decays of e^-60 and below (A_log = 3, g_raw ~ N(3, 1)): the gate gradients are tiny, formed
+    # from products that are not.  Token gradients at the usual bars; dinitial_state (about e^-60 per token
+    # of the sequence in the fp64 oracle, zero in fp32) to an absolute 1e-6 of dfinal's scale; dA_log, a sum
+    # of tiny terms of both signs, to 0.1 of its condition.
+    inp = make_inputs(1, 150, 2, 2, gate_per_channel=False, A_log=3.0, g_shift=3.0, state_std=0.05, seed=81)
+    dout, dfinal = upstream(inp, 581)
+    got, ref = run_gpu_bwd(inp, dout, dfinal), run_oracle_bwd(inp, dout, dfinal)
+    for n in ("dq", "dk", "dv", "dg_raw", "dbeta_logits"):
+        rel = rel_l2(got[n], ref[n])
+        print("extreme decay", n, "%.1e" % rel, flush=True)
+        assert rel <= GRAD_REL, (n, rel)
+    assert np.max(np.abs(got["dinitial_state"] - ref["dinitial_state"])) <= 1e-6 * np.max(np.abs(dfinal))
+    cond = dA_log_condition(ref, inp["g_raw"])
+    assert np.max(np.abs(got["dA_log"] - ref["dA_log"]) / cond) <= 0.1
+
+
 def test_backward_zero_tokens():
     # T = 0: no token gradients; dinitial_state = dfinal, dA_log = 0
     H = 2

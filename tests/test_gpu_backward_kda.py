@@ -43,6 +43,26 @@ def test_kda_backward_matches_the_oracle(label, kw, dstd):
     compare(got, ref, label, inp["g_raw"], inp.get("cu_seqlens"))
 
 
+def test_kda_backward_extreme_decay():
+    # per-token decays of e^-60 and below (A_log = 3, g_raw ~ N(3, 1)): every cross-block factor and most
+    # in-block ones underflow and the gate gradients are tiny, formed from products that are not.  The
+    # token gradients are held to the usual bars; dinitial_state (about e^-60 per token of the sequence in
+    # the fp64 oracle, zero in fp32) to an absolute 1e-6 of dfinal's scale; dA_log, a sum of 19,200 tiny
+    # terms of both signs, to 0.1 of its condition (measured 0.063: the terms' small relative errors add
+    # up against a sum they nearly cancel in).
+    from test_gpu_backward import dA_log_condition, rel_l2
+    inp = make_inputs(1, 150, 2, 2, gate_per_channel=True, A_log=3.0, g_shift=3.0, state_std=0.05, seed=180)
+    dout, dfinal = upstream(inp, 680)
+    got, ref = run_gpu_bwd(inp, dout, dfinal), run_oracle_bwd(inp, dout, dfinal)
+    for n in ("dq", "dk", "dv", "dg_raw", "dbeta_logits"):
+        rel = rel_l2(got[n], ref[n])
+        print("kda extreme decay", n, "%.1e" % rel, flush=True)
+        assert rel <= 5e-3, (n, rel)
+    assert np.max(np.abs(got["dinitial_state"] - ref["dinitial_state"])) <= 1e-6 * np.max(np.abs(dfinal))
+    cond = dA_log_condition(ref, inp["g_raw"])
+    assert np.max(np.abs(got["dA_log"] - ref["dA_log"]) / cond) <= 0.1
+
+
 def test_kda_backward_grouped_heads_long_sequence():
     # 64 chunks, two value heads on each q/k head
     inp = make_inputs(1, 4096, 8, 4, gate_per_channel=True, A_log=(-1.0, 1.0), state_std=0.05, seed=181)
