@@ -48,10 +48,12 @@ struct __attribute__((aligned(16))) RowsLds {
   float eL;
   int len;
 };
-// per-row sums collected across waves (grad kernel)
+// per-row sums collected across waves (grad kernel); each wave stores its partial sums and they are added
+// up wave by wave after a barrier, so a call's results do not depend on the order in which waves finish
 struct __attribute__((aligned(16))) RedLds {
   float de[CH], df[CH], db[CH], wr[CH], wc[CH], qd[CH], kd[CH];
   float deL[NTH / 64];
+  float part[4][NTH / 64][CH];
 };
 
 // Gate rows and normalised q, k rows (fp16, rows past the chunk's end zero).
@@ -604,7 +606,6 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
     *reinterpret_cast<f16x8*>(DO + r * LDW + c0) = to_f16x8(x);
     *reinterpret_cast<f16x8*>(DO + r * LDW + c0 + 8) = to_f16x8(x + 8);
   }
-  if (t < CH) red.de[t] = red.df[t] = red.db[t] = red.wr[t] = red.wc[t] = red.qd[t] = red.kd[t] = 0.f;
   __syncthreads();
   f32x4 P[2], Gm[2];
   gram_and_T<false>(QN, KN, R, Mt, nullptr, nullptr, nullptr, nullptr, P, Gm);
@@ -698,12 +699,22 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
         DR[r * LDW + vc] = (f16)dv;
         const float db = rowsum16(Y[i][jj] * RR[i][jj]), de = rowsum16(dv * KS[i][jj]);
         if (l16 == 0) {
-          atomicAdd(&red.db[r], db);
-          atomicAdd(&red.de[r], -de);
+          red.part[0][w][r] = db;
+          red.part[1][w][r] = -de;
         }
       }
   }
   __syncthreads();  // dR complete
+  if (t < CH) {
+    float db = 0.f, de = 0.f;
+#pragma unroll
+    for (int q = 0; q < NTH / 64; ++q) {
+      db += red.part[0][q][t];
+      de += red.part[1][q][t];
+    }
+    red.db[t] = db;
+    red.de[t] = de;
+  }
   // ---- [dO'; dR] S^T and U dS'^T (rows r, columns d: tile w) ------------------
   f32x4 dqn[4], dkn[4];
   {
@@ -736,8 +747,8 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
         const float de = rowsum16((float)QN[r * LDW + vc] * SD[i][jj]);
         const float df = rowsum16((float)KN[r * LDW + vc] * UD[i][jj]);
         if (l16 == 0) {
-          atomicAdd(&red.de[r], de);
-          atomicAdd(&red.df[r], df);
+          red.part[2][w][r] = de;
+          red.part[3][w][r] = df;
         }
       }
   }
@@ -758,6 +769,16 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
       }
     }
     __syncthreads();  // last reads of dO', bR, U, dU, dR: their space now holds the 64 x 64 results
+    if (t < CH) {
+      float de = 0.f, df = 0.f;
+#pragma unroll
+      for (int q = 0; q < NTH / 64; ++q) {
+        de += red.part[2][q][t];
+        df += red.part[3][q][t];
+      }
+      red.de[t] += de;
+      red.df[t] = df;
+    }
 #pragma unroll
     for (int j = 0; j < 2; ++j)
 #pragma unroll
@@ -792,6 +813,7 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) DA[j] = mma_f16(a, frag_rm(X1t, LDN, 16 * (ct0 + j), 32 * s, lane), DA[j]);
     }
+    float db2[4] = {0.f, 0.f, 0.f, 0.f}, wr[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int c = 16 * (ct0 + j) + l16;
@@ -812,20 +834,29 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
         pc[jj] = (f16)dp;
         gc[jj] = (f16)dgm;
         wcol += wv;
-        const float db2 = rowsum16(da * Gm[j][jj] * lam), wr = rowsum16(wv);
-        if (l16 == 0) {
-          atomicAdd(&red.db[r], db2);
-          atomicAdd(&red.wr[r], wr);
-        }
+        db2[jj] += rowsum16(da * Gm[j][jj] * lam);
+        wr[jj] += rowsum16(wv);
       }
       *reinterpret_cast<f16x4*>(DPt + c * LDN + 16 * rt + 4 * lg) = pc;
       *reinterpret_cast<f16x4*>(DGt + c * LDN + 16 * rt + 4 * lg) = gc;
       wcol += __shfl_xor(wcol, 16);
       wcol += __shfl_xor(wcol, 32);
-      if (lg == 0) atomicAdd(&red.wc[c], wcol);
+      if (lg == 0) red.part[1][rt][c] = wcol;  // column c's share from row tile rt
+    }
+    if (l16 == 0) {  // row tile rt's two waves: column tiles 0, 1 and 2, 3
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) {
+        red.part[0][w & 1][16 * rt + 4 * lg + jj] = db2[jj];
+        red.part[0][2 + (w & 1)][16 * rt + 4 * lg + jj] = wr[jj];
+      }
     }
   }
   __syncthreads();
+  if (t < CH) {
+    red.db[t] += red.part[0][0][t] + red.part[0][1][t];
+    red.wr[t] = red.part[0][2][t] + red.part[0][3][t];
+    red.wc[t] = (red.part[1][0][t] + red.part[1][1][t]) + (red.part[1][2][t] + red.part[1][3][t]);
+  }
   // ---- dqn += dP kn;  dkn += (dGm + dGm^T) kn + dP^T qn ---------------------
 #pragma unroll
   for (int s = 0; s < 2; ++s) {
@@ -850,10 +881,17 @@ __global__ __launch_bounds__(NTH) void bwd_grad_kernel(BwdParams p) {
       kf[i][jj] = kx;
       const float qd = rowsum16(qx * dqn[i][jj]), kd = rowsum16(kx * dkn[i][jj]);
       if (l16 == 0) {
-        atomicAdd(&red.qd[r], qd);
-        atomicAdd(&red.kd[r], kd);
+        red.part[2][w][r] = qd;
+        red.part[3][w][r] = kd;
       }
     }
+  __syncthreads();
+  if (t < 2 * CH) {  // the row dots, wave by wave
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < NTH / 64; ++q) a += red.part[2 + (t >> 6)][q][t & (CH - 1)];
+    (t < CH ? red.qd : red.kd)[t & (CH - 1)] = a;
+  }
   __syncthreads();
   // dq, dk through the normalisation: (dxn - xn (xn . dxn)) / |x|
 #pragma unroll

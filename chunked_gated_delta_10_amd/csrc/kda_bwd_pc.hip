@@ -505,11 +505,15 @@ constexpr int P_QN = P_MT;  // qn, over M^T and T once dA is formed
 static_assert(P_XB + MAT_G <= P_END && P_X1 + MAT_N <= P_END, "64 x 64 results fit");
 static_assert(MAT_W <= 2 * MAT_N, "qn fits over M^T and T");
 
+// Per-row and per-channel sums over the waves are formed in a fixed order (each wave's partial sum
+// stored, then added up wave by wave), so that a call's results do not depend on the order in which the
+// waves finish.
 struct __attribute__((aligned(16))) PcRed {
   float db[CH], qd[CH], kd[CH];
   float dgl[HD];  // sum_r Kbar . dKbar per key channel
   float sdl[HD];  // sum_v S_c . dS' per key channel
-  float dal;
+  float part[8][CH];  // the waves' partial row sums
+  float dalw[8];      // the waves' partial sums of dA_log
 };
 }  // namespace
 
@@ -590,9 +594,6 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
     *reinterpret_cast<f16x8*>(DO + r * LDW + c0) = to_f16x8(x);
     *reinterpret_cast<f16x8*>(DO + r * LDW + c0 + 8) = to_f16x8(x + 8);
   }
-  if (t < CH) red.db[t] = red.qd[t] = red.kd[t] = 0.f;
-  if (t < HD) red.sdl[t] = 0.f;
-  if (t == 0) red.dal = 0.f;
   uint4 qraw[2];
   float kv[16];
   load_pc(p, tok0, len, h, hq, KN, LG, reinterpret_cast<float*>(smem + P_PART), R, qraw, kv);
@@ -610,15 +611,23 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
     *reinterpret_cast<f16x8*>(KB + r8 * LDW + c0) = to_f16x8(kb);
     *reinterpret_cast<f16x8*>(KB + r8 * LDW + c0 + 8) = to_f16x8(kb + 8);
   }
-  // sum_v S_c . dS' per key channel d = 32 s + 8 lg + e (v = this lane's column)
+  // sum_v S_c . dS' per key channel d = 32 s + 8 lg + e (v = this lane's column); the waves' partial
+  // sums in dR's space (free until dR is formed, several barriers later)
+  float* psdl = reinterpret_cast<float*>(smem + P_DR);
 #pragma unroll
   for (int s = 0; s < 4; ++s)
 #pragma unroll
     for (int e2 = 0; e2 < 8; ++e2) {
       const float x = rowsum16((float)sfr[s][e2] * (float)dsfr[s][e2]);
-      if (l16 == 0) atomicAdd(&red.sdl[32 * s + 8 * lg + e2], x);
+      if (l16 == 0) psdl[w * HD + 32 * s + 8 * lg + e2] = x;
     }
   __syncthreads();  // Khat, Kbar complete
+  if (t < HD) {
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a += psdl[q * HD + t];
+    red.sdl[t] = a;
+  }
   // ---- KS = Khat S (rows r, columns v); R = V - KS; bR;  KD = Kbar dS' ------
   f32x4 RR[4], KD[4];
   {
@@ -690,10 +699,16 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
         if (r < len) __builtin_nontemporal_store(dv, p.dv + (size_t)(tok0 + r) * vrow + (size_t)h * HD + vc);
         DR[r * LDW + vc] = (f16)dv;
         const float db = rowsum16(Y[i][jj] * RR[i][jj]);
-        if (l16 == 0) atomicAdd(&red.db[r], db);
+        if (l16 == 0) red.part[w][r] = db;
       }
   }
   __syncthreads();  // dR complete
+  if (t < CH) {
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a += red.part[q][t];
+    red.db[t] = a;
+  }
   // ---- dQhat = dO' S^T, dKhat = -dR S^T, dKbar = U dS'^T (rows r, key columns: tile w)
   f32x4 dqn[4], dkn[4], dgk[4];
   {
@@ -783,6 +798,7 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
 #pragma unroll
       for (int j = 0; j < 2; ++j) DA[j] = mma_f16(a, frag_rm(X1t, LDN, 16 * (ct0 + j), 32 * s, lane), DA[j]);
     }
+    float db2[4] = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int j = 0; j < 2; ++j) {
       const int c = 16 * (ct0 + j) + l16;
@@ -797,14 +813,18 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
         DH[r * LDN + c] = (f16)dh;
         mc[jj] = (f16)dm;
         hc[jj] = (f16)dh;
-        const float db2 = rowsum16(da * (float)hkv[j][jj]);
-        if (l16 == 0) atomicAdd(&red.db[r], db2);
+        db2[jj] += rowsum16(da * (float)hkv[j][jj]);
       }
       *reinterpret_cast<f16x4*>(DMt + c * LDN + 16 * rt + 4 * lg) = mc;
       *reinterpret_cast<f16x4*>(DHt + c * LDN + 16 * rt + 4 * lg) = hc;
     }
+    if (l16 == 0) {  // this row tile's two waves: column tiles 0, 1 and 2, 3
+#pragma unroll
+      for (int jj = 0; jj < 4; ++jj) red.part[w & 1][16 * rt + 4 * lg + jj] = db2[jj];
+    }
   }
   __syncthreads();  // dM, dH complete; M^T, T, dT, X1^T dead
+  if (t < CH) red.db[t] += red.part[0][t] + red.part[1][t];
   {  // qn rows over M^T and T
     float qv[16];
     unpack_bf16x8(qraw[0], qv);
@@ -914,6 +934,7 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
   }
   // ---- row dots qn . dqn, kn . dkn; dGamma; dg (reverse cumulative sum over the chunk's rows)
   float dgm[4][4];
+  float* pqk = reinterpret_cast<float*>(smem + P_DHT);  // the waves' partial row dots (dH^T, dM^T are dead)
   uint4 graw[2];  // g_raw of row r8, channels c0 .. c0 + 15 (issued now, used last)
   {
     const size_t o = ((size_t)(tok0 + min(r8, len - 1)) * p.H + h) * HD + c0;
@@ -934,8 +955,8 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
         dkn[i][jj] += dmrr * qx;
         const float qd = rowsum16(qx * dqn[i][jj]), kd = rowsum16(kx * dkn[i][jj]);
         if (l16 == 0) {
-          atomicAdd(&red.qd[r], qd);
-          atomicAdd(&red.kd[r], kd);
+          pqk[w * CH + r] = qd;
+          pqk[(8 + w) * CH + r] = kd;
         }
       }
     // reverse inclusive sum over rows 16 i + 4 lg + jj of column vc (lanes lg = 0..3 share the column)
@@ -960,6 +981,13 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
     for (int i = 0; i < 4; ++i)
 #pragma unroll
       for (int jj = 0; jj < 4; ++jj) XB[(16 * i + 4 * lg + jj) * LGS + vc] = dgm[i][jj];
+  }
+  __syncthreads();
+  if (t < 2 * CH) {  // the row dots, wave by wave
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a += pqk[((t >> 6) * 8 + q) * CH + (t & (CH - 1))];
+    (t < CH ? red.qd : red.kd)[t & (CH - 1)] = a;
   }
   __syncthreads();
   // dq, dk through the normalisation: (dxn - xn (xn . dxn)) / |x|
@@ -1004,14 +1032,19 @@ __global__ __launch_bounds__(NTH) void bwd_grad_pc_kernel(BwdParams p) {
         __builtin_nontemporal_store(f32x4{o[4 * j], o[4 * j + 1], o[4 * j + 2], o[4 * j + 3]}, dst + j);
     }
     dal = sum64(dal);
-    if (lane == 0) atomicAdd(&red.dal, dal);
+    if (lane == 0) red.dalw[w] = dal;
   }
   if (t < len) {
     const float b = R.b[t];
     p.dbeta[(size_t)(tok0 + t) * p.H + h] = red.db[t] * b * (1.f - b);
   }
   __syncthreads();
-  if (t == 0) atomicAdd(p.dA_log + h, red.dal);
+  if (t == 0) {
+    float a = 0.f;
+#pragma unroll
+    for (int q = 0; q < 8; ++q) a += red.dalw[q];
+    atomicAdd(p.dA_log + h, a);
+  }
 }
 
 void launch_coef_pc(const BwdParams& p, hipStream_t stream) {

@@ -225,7 +225,9 @@ kda_status kda_la_decode_step(const void* q, const void* k, const void* v, const
  * kda_bwd_workspace_bytes(B, T, H_qk, H, 0) (N > 0: kda_bwd_varlen), the same
  * for both gate modes, 256-byte aligned, contents garbage before and after.
  * dq, dk (when H > H_qk) and dA_log are accumulated with float atomics, so
- * their last bits may differ from run to run.  Other errors and the B/N/T == 0
+ * their last bits may differ from run to run; every other output is the same
+ * bit for bit on every call (sums inside a workgroup are formed in a fixed
+ * order).  Other errors and the B/N/T == 0
  * behaviour follow kda_fwd / kda_fwd_varlen (T == 0: dinitial_state = dfinal,
  * or zero).
  */

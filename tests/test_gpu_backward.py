@@ -223,6 +223,20 @@ def test_backward_extreme_decay():
     assert np.max(np.abs(got["dA_log"] - ref["dA_log"]) / cond) <= 0.1
 
 
+@pytest.mark.parametrize("per_channel", [False, True], ids=["scalar gate", "per-channel gate"])
+def test_backward_deterministic(per_channel):
+    # two calls on the same inputs: every gradient that is not accumulated with float atomics (dA_log always
+    # is; dq, dk only when value heads share q/k heads, not here) is bit for bit the same
+    inp = make_inputs(1, 300, 4, 4, gate_per_channel=per_channel, state_std=0.05, seed=82, N=3,
+                      lengths=[130, 64, 106])
+    dout, dfinal = upstream(inp, 582)
+    a, b = run_gpu_bwd(inp, dout, dfinal), run_gpu_bwd(inp, dout, dfinal)
+    for n in NAMES:
+        if n != "dA_log":
+            assert np.array_equal(a[n], b[n]), n
+    np.testing.assert_allclose(a["dA_log"], b["dA_log"], rtol=1e-5, atol=1e-7)
+
+
 def test_backward_zero_tokens():
     # T = 0: no token gradients; dinitial_state = dfinal, dA_log = 0
     H = 2
