@@ -4,7 +4,8 @@
 A step is one kda_fwd call (schedule, chunk-local and recurrence kernels:
 the whole chunked hot path) over one batch of the dense KDA workload
 B=2, T=16384, H=16, K=V=128 with fp32 initial/final state, inputs already
-resident in HBM.  Prints ONE JSON line (see the design doc for the fields).
+resident in HBM.  Prints ONE JSON line: throughput, per-kernel times, the
+dominant kernel's roofline fraction and the oracle's CPU rate.
 
     python bench.py [--gpus 1] [--steps 100] [--warmup 10]
 
@@ -469,7 +470,7 @@ def main():
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
         print("bench.py runs on exactly one GPU: the KDA path here is built and measured on a single MI355X "
-              "(sharding across GPUs is by batch, sequence and head with no exchange; see DESIGN.md). "
+              "(sharding across GPUs is by batch, sequence and head with no exchange). "
               "Run with --gpus 1.", file=sys.stderr)
         sys.exit(2)
 

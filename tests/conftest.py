@@ -15,7 +15,7 @@ def pytest_configure(config):
 
 def pytest_collection_modifyitems(config, items):
     # GPU tests cannot run without a device; skip them loudly rather than fail
-    # on machines without one (the GPU machine runs them with -m gpu).
+    # on machines without one (a machine with a GPU runs them with -m gpu).
     try:
         import torch
         have_gpu = torch.cuda.is_available()
