@@ -36,6 +36,12 @@ GRAD_MAXABS = 2e-2  # of max |reference| of the same gradient
 # chain is not diluted by the others; twice the pooled bar (short chains hold few values)
 GRAD_REL_CHAIN = 1e-2
 CHAIN_FLOOR = 1e-2  # of a typical slice's norm; see chain_worst
+# dinitial_state entries within this absolute distance of the oracle pass whatever their relative error (the
+# upstream gradients here are of unit scale): the adjoint chain stores and multiplies fp16 values, whose
+# resolution below the normal range (2^-14) is the subnormal spacing 2^-24 ~ 6e-8, so when harsh decays leave
+# every entry of every slice under ~1e-6 (the fp64 oracle's values reach 1e-9 and below) relative bars measure
+# only that rounding; at ordinary magnitudes (1e-2..1e-1) the bound is far below fp16's relative resolution
+DINIT_ABS = 1e-6
 NAMES = ("dq", "dk", "dv", "dg_raw", "dbeta_logits", "dA_log", "dinitial_state")
 
 
@@ -119,7 +125,8 @@ def chain_worst(got, ref, cu_seqlens=None):
         if len(sl) == 0 or not np.any(norms > 0):
             continue
         floor = CHAIN_FLOOR * np.sqrt(np.mean(norms ** 2))
-        worst[n] = max(float(np.linalg.norm(xx - rr) / max(nr, floor)) for (xx, rr), nr in zip(sl, norms))
+        worst[n] = max(0.0 if n == "dinitial_state" and np.max(np.abs(xx - rr)) <= DINIT_ABS else
+                       float(np.linalg.norm(xx - rr) / max(nr, floor)) for (xx, rr), nr in zip(sl, norms))
     return worst
 
 
@@ -140,6 +147,8 @@ def compare(got, ref, label, g_raw_bits, cu_seqlens=None):
     print(label, " ".join("%s %.1e/%.1e" % (n, *errs[n]) for n in NAMES), "| worst chain",
           " ".join("%s %.1e" % kv for kv in worst.items()), flush=True)
     for n, (rel, mx) in errs.items():
+        if n == "dinitial_state" and np.max(np.abs(got[n] - ref[n])) <= DINIT_ABS:
+            continue
         assert rel <= GRAD_REL and mx <= GRAD_MAXABS, (label, n, rel, mx)
     for n, e in worst.items():
         assert e <= GRAD_REL_CHAIN, (label, n, "per chain", e)

@@ -87,3 +87,24 @@ def test_backward_bars_catch_an_error_confined_to_one_chain():
     assert pooled < 5e-3
     with pytest.raises(AssertionError, match="per chain"):
         compare(bad, ref, "one chain off by 2%", g_raw)
+
+
+def test_backward_dinitial_state_absolute_bar():
+    # dinitial_state entries all far under fp16's range (harsh decays): zero from the kernel passes against
+    # 1e-9-sized reference values; at ordinary magnitudes an error of 1e-3 in one slice still fails
+    from test_gpu_backward import compare
+    rng = np.random.default_rng(8)
+    B, T, H, D = 2, 40, 2, 128
+    ref = {"dq": rng.standard_normal((B, T, H, D)), "dk": rng.standard_normal((B, T, H, D)),
+           "dv": rng.standard_normal((B, T, H, D)), "dg_raw": rng.standard_normal((B, T, H)),
+           "dbeta_logits": rng.standard_normal((B, T, H)), "dA_log": np.zeros(H),
+           "dinitial_state": 1e-9 * rng.standard_normal((B, H, D, D))}
+    g_raw = np.zeros((B, T, H), dtype=np.uint16)
+    got = {n: v.copy() for n, v in ref.items()}
+    got["dinitial_state"] = np.zeros_like(ref["dinitial_state"])
+    compare(got, ref, "tiny dinitial_state flushed to zero", g_raw)
+    ref["dinitial_state"] = 1e-2 * rng.standard_normal((B, H, D, D))
+    got["dinitial_state"] = ref["dinitial_state"].copy()
+    got["dinitial_state"][1, 0] += 1e-3 * rng.standard_normal((D, D))
+    with pytest.raises(AssertionError, match="dinitial_state"):
+        compare(got, ref, "one dinitial_state slice off by 1e-3", g_raw)
