@@ -222,8 +222,8 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_kernel(BwdParams p) {
   gram_and_T<true>(QN, KN, R, nullptr, M16, AF, TF, T16, P, Gm);
   uint8_t* rec = p.brec + (size_t)job * p.rec_bytes;
   // T (fp16 rows) for the gradient kernel: thread -> row t / 8, columns 8 (t % 8) ..
-  *reinterpret_cast<f16x8*>(rec + BR_T + t * 16) =
-      *reinterpret_cast<const f16x8*>(T16 + (t >> 3) * LDN + 8 * (t & 7));
+  __builtin_nontemporal_store(*reinterpret_cast<const f16x8*>(T16 + (t >> 3) * LDN + 8 * (t & 7)),
+                              reinterpret_cast<f16x8*>(rec + BR_T + t * 16));
 
   // Y1 = T^T diag(f) kn: rows i (4 tiles), columns d (tile w); K = 64
   {
@@ -249,7 +249,7 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_kernel(BwdParams p) {
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) o[4 * hh + jj] = (f16)(R.b[32 * s + 16 * hh + 4 * lg + jj] * Y1[2 * s + hh][jj]);
-      *reinterpret_cast<f16x8*>(rec + BR_GC + (w * 2 + s) * FRAG_BYTES + lane * 16) = o;
+      __builtin_nontemporal_store(o, reinterpret_cast<f16x8*>(rec + BR_GC + (w * 2 + s) * FRAG_BYTES + lane * 16));
     }
   }
   __syncthreads();
@@ -274,7 +274,7 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_kernel(BwdParams p) {
         o[jj] = (f16)((d0 == d ? eL : 0.f) - A[2 * s][jj]);
         o[4 + jj] = (f16)((d1 == d ? eL : 0.f) - A[2 * s + 1][jj]);
       }
-      *reinterpret_cast<f16x8*>(rec + BR_PHI + (w * 4 + s) * FRAG_BYTES + lane * 16) = o;
+      __builtin_nontemporal_store(o, reinterpret_cast<f16x8*>(rec + BR_PHI + (w * 4 + s) * FRAG_BYTES + lane * 16));
     }
   }
   // Phi = e_L I - (diag(b e) kn)^T Y1: rows d (8 tiles), columns d' (tile w); its C layout is the
@@ -300,7 +300,7 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_kernel(BwdParams p) {
           o[jj] = (f16)((d0 == d ? eL : 0.f) - A[2 * s2][jj]);
           o[4 + jj] = (f16)((d1 == d ? eL : 0.f) - A[2 * s2 + 1][jj]);
         }
-        *reinterpret_cast<f16x8*>(rec + BR_PHIT + (w * 4 + s) * FRAG_BYTES + lane * 16) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<f16x8*>(rec + BR_PHIT + (w * 4 + s) * FRAG_BYTES + lane * 16));
       }
     }
   }
@@ -344,7 +344,7 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_kernel(BwdParams p) {
           const float qn = i < len ? bf(qraw[s][hh][jj]) / R.nq[i] : 0.f;
           o[4 * hh + jj] = (f16)(R.e[i] * qn - B[2 * s + hh][jj]);
         }
-      *reinterpret_cast<f16x8*>(rec + BR_BC + (w * 2 + s) * FRAG_BYTES + lane * 16) = o;
+      __builtin_nontemporal_store(o, reinterpret_cast<f16x8*>(rec + BR_BC + (w * 2 + s) * FRAG_BYTES + lane * 16));
     }
   }
 }

@@ -346,8 +346,8 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_pc_kernel(BwdParams p) {
   __syncthreads();  // A, M complete
   solve_T(AF, TF, T16);
   // T and M (fp16 rows) for the gradient kernel: thread -> row t / 8, columns 8 (t % 8) ..
-  *reinterpret_cast<f16x8*>(rec + BR_T + t * 16) = *reinterpret_cast<const f16x8*>(T16 + (t >> 3) * LDN + 8 * (t & 7));
-  *reinterpret_cast<f16x8*>(rec + BR_M + t * 16) = *reinterpret_cast<const f16x8*>(M16 + (t >> 3) * LDN + 8 * (t & 7));
+  __builtin_nontemporal_store(*reinterpret_cast<const f16x8*>(T16 + (t >> 3) * LDN + 8 * (t & 7)), reinterpret_cast<f16x8*>(rec + BR_T + t * 16));
+  __builtin_nontemporal_store(*reinterpret_cast<const f16x8*>(M16 + (t >> 3) * LDN + 8 * (t & 7)), reinterpret_cast<f16x8*>(rec + BR_M + t * 16));
   // Khat, Kbar rows over the solve's fp32 space (dead: solve_T ended with a barrier)
   *reinterpret_cast<f16x8*>(KH + r * LDW + c0) = khb[0];
   *reinterpret_cast<f16x8*>(KH + r * LDW + c0 + 8) = khb[1];
@@ -379,7 +379,7 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_pc_kernel(BwdParams p) {
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) o[4 * hh + jj] = (f16)(R.b[32 * s + 16 * hh + 4 * lg + jj] * Y1[2 * s + hh][jj]);
-      *reinterpret_cast<f16x8*>(rec + BR_GC + (w * 2 + s) * FRAG_BYTES + lane * 16) = o;
+      __builtin_nontemporal_store(o, reinterpret_cast<f16x8*>(rec + BR_GC + (w * 2 + s) * FRAG_BYTES + lane * 16));
     }
   }
   __syncthreads();
@@ -404,7 +404,7 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_pc_kernel(BwdParams p) {
         o[jj] = (f16)((d0 == d ? eL : 0.f) - A[2 * s][jj]);
         o[4 + jj] = (f16)((d1 == d ? eL : 0.f) - A[2 * s + 1][jj]);
       }
-      *reinterpret_cast<f16x8*>(rec + BR_PHI + (w * 4 + s) * FRAG_BYTES + lane * 16) = o;
+      __builtin_nontemporal_store(o, reinterpret_cast<f16x8*>(rec + BR_PHI + (w * 4 + s) * FRAG_BYTES + lane * 16));
     }
   }
   // Phi = D_L - (diag(b) Khat)^T Y1: rows d (8 tiles), columns d' (tile w); its C layout is the
@@ -429,7 +429,7 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_pc_kernel(BwdParams p) {
           o[jj] = (f16)((d0 == d ? R.el[d0] : 0.f) - A[2 * s2][jj]);
           o[4 + jj] = (f16)((d1 == d ? R.el[d1] : 0.f) - A[2 * s2 + 1][jj]);
         }
-        *reinterpret_cast<f16x8*>(rec + BR_PHIT + (w * 4 + s) * FRAG_BYTES + lane * 16) = o;
+        __builtin_nontemporal_store(o, reinterpret_cast<f16x8*>(rec + BR_PHIT + (w * 4 + s) * FRAG_BYTES + lane * 16));
       }
     }
   }
@@ -478,7 +478,7 @@ __global__ __launch_bounds__(NTH, 4) void bwd_coef_pc_kernel(BwdParams p) {
       for (int hh = 0; hh < 2; ++hh)
 #pragma unroll
         for (int jj = 0; jj < 4; ++jj) o[4 * hh + jj] = (f16)((float)qh[s][hh][jj] - B[2 * s + hh][jj]);
-      *reinterpret_cast<f16x8*>(rec + BR_BC + (w * 2 + s) * FRAG_BYTES + lane * 16) = o;
+      __builtin_nontemporal_store(o, reinterpret_cast<f16x8*>(rec + BR_BC + (w * 2 + s) * FRAG_BYTES + lane * 16));
     }
   }
 }
